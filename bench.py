@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeek-V4 CSA/HCA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
+
+A step is one CSA decode step of the 1M-context workload (4 sequences at position
+1,048,575, 262,144 compressed entries each, 128 query heads, head dim 512, 64 MXFP4
+indexer heads, top-1024, 128-token window, sink):
+  1. compress the block each sequence's newest token completes into its entry record and
+     its MXFP4 indexer key (two batched compressor launches);
+  2. score every entry with the lightning indexer and select the top-1024;
+  3. attend over the selected entries plus the window with the sink, then combine the splits.
+Inputs are seeded synthetic data (N(0,1) before quantisation).  Every input set is cloned
+R times in HBM and step i uses set i mod R, so the 256 MB Infinity Cache cannot hold the
+working set; the inputs are resident in HBM when timing starts.
+
+One JSON line is printed: throughput (tokens/s = sequences decoded per second), the roofline
+of the dominant stage (the indexer + top-k call) measured live with HIP events on the
+stream the kernels run on, the oracle timed on the host cores, a parity check of set 0
+against the oracle, and a secondary figure for the 1M-context HCA decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "CSA/HCA decode tokens/s at 1M ctx; achieved HBM GB/s and indexer MFMA util"
+HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10100.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--rotate", type=int, default=16, help="input copies cycled through (MALL defeat)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the hot path "
+              "is measured on one MI355X; see the design notes for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_sparse_attention_02_amd as v4
+    from workloads import CSA_PRO_1M, HCA_1M, decode_inputs, normal, to_bf16_bits
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = CSA_PRO_1M
+    B, H, D, R, W, k, HI, dI, m = wl.B, wl.H, wl.D, wl.R, wl.W, wl.k, wl.H_I, wl.d_I, wl.m
+    T = wl.T
+    N = wl.n_csa
+    scale = 1.0 / math.sqrt(D)
+    q_pos = [T - 1] * B
+    print(f"[bench] drawing inputs for {wl.name}", file=sys.stderr, flush=True)
+    inp = decode_inputs(wl, threads=16)
+    s = wl.seed
+    # raw streams of the last two blocks (B-block N-2, A-block N-1) of every sequence
+    ntok = 2 * m
+    tok0 = T - ntok
+    raw = {
+        "kv_a": normal(s, "kv_a", (B, ntok, D)), "kv_b": normal(s, "kv_b", (B, ntok, D)),
+        "gate_a": normal(s, "gate_a", (B, ntok, 1)), "gate_b": normal(s, "gate_b", (B, ntok, 1)),
+        "bias_a": normal(s, "bias_a", (m, 1)), "bias_b": normal(s, "bias_b", (m, 1)),
+        "idx_a": normal(s, "idx_a", (B, ntok, dI)), "idx_b": normal(s, "idx_b", (B, ntok, dI)),
+        "idx_gate_a": normal(s, "idx_gate_a", (B, ntok, 1)), "idx_gate_b": normal(s, "idx_gate_b", (B, ntok, 1)),
+        "idx_bias_a": normal(s, "idx_bias_a", (m, 1)), "idx_bias_b": normal(s, "idx_bias_b", (m, 1)),
+    }
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def bf16(a):
+        return torch.from_numpy(to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    print("[bench] quantising set 0 on the GPU", file=sys.stderr, flush=True)
+    kv0 = v4.KV.empty(B, N, D, R)
+    for b in range(B):  # one sequence at a time keeps the fp32 staging buffer at 537 MB
+        v4.v4a_quantize_kv(f32(inp["records"][b]), kv0, b * N)
+    keys0 = v4.Idx.empty(B, N, dI)
+    v4.v4a_quantize_mxfp4(f32(inp["keys"].reshape(-1, dI)), keys0)
+    qi0 = v4.Idx.empty(B, HI, dI)
+    v4.v4a_quantize_mxfp4(f32(inp["q_idx"].reshape(-1, dI)), qi0)
+    set0 = dict(kv=kv0, keys=keys0, qi=qi0, w=f32(inp["w"]), q=bf16(inp["q"]), win=bf16(inp["window"]),
+                sink=f32(inp["sink"]),
+                kv_a=bf16(raw["kv_a"]), kv_b=bf16(raw["kv_b"]), gate_a=f32(raw["gate_a"]), gate_b=f32(raw["gate_b"]),
+                bias_a=f32(raw["bias_a"]), bias_b=f32(raw["bias_b"]),
+                idx_a=bf16(raw["idx_a"]), idx_b=bf16(raw["idx_b"]), idx_gate_a=f32(raw["idx_gate_a"]),
+                idx_gate_b=f32(raw["idx_gate_b"]), idx_bias_a=f32(raw["idx_bias_a"]),
+                idx_bias_b=f32(raw["idx_bias_b"]))
+    rec0 = inp["records"][0].copy()   # sequence 0 stays on the host for the oracle check
+    del inp["records"]
+
+    def clone(st):
+        c = {}
+        for name, v in st.items():
+            if isinstance(v, v4.KV):
+                c[name] = v4.KV(v.fmt, v.D, v.R, v.nope.clone(), v.rope.clone(), v.scale.clone(), v.cap)
+            elif isinstance(v, v4.Idx):
+                c[name] = v4.Idx(v.fmt, v.d, v.codes.clone(), v.scales.clone(), v.cap)
+            else:
+                c[name] = v.clone()
+        return c
+
+    sets = [set0] + [clone(set0) for _ in range(max(1, args.rotate) - 1)]
+    ws = v4.workspace(max(v4.v4a_indexer_topk_workspace(B, 1, N, k), v4.v4a_decode_workspace(B, H, D, k, W)))
+    sel = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    win_len = [W] * B
+
+    def step(i, ev=None):
+        st = sets[i % len(sets)]
+        v4.v4a_compress_csa(st["kv_a"], st["kv_b"], st["gate_a"], st["gate_b"], st["bias_a"], st["bias_b"],
+                            tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_kv=st["kv"])
+        v4.v4a_compress_csa(st["idx_a"], st["idx_b"], st["idx_gate_a"], st["idx_gate_b"], st["idx_bias_a"],
+                            st["idx_bias_b"], tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_idx=st["keys"])
+        if ev is not None:
+            ev[0].record()
+        v4.v4a_indexer_topk(st["keys"], [N] * B, m, st["qi"], st["w"], B, 1, HI, q_pos, k, sel, ws)
+        if ev is not None:
+            ev[1].record()
+        v4.v4a_decode_csa(st["q"], st["kv"], sel.view(B, k), k, st["win"], win_len, W, st["sink"], q_pos,
+                          softmax_scale=scale, out=outs[i % 2], ws=ws)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tok_s = B / (ms_step / 1e3)
+
+    # algorithmic bytes of the indexer + top-k call: keys, indexer queries and weights read,
+    # the top-k list written
+    idx_bytes = B * N * (dI // 2 + dI // 32) + B * HI * (dI // 2 + dI // 32) + B * HI * 4 + B * k * 4
+    idx_flops = 2.0 * B * N * HI * dI
+    achieved = idx_bytes / (idx_ms / 1e3) / 1e9
+    # whole-step algorithmic bytes: keys + gathered records + window + queries + output + raw blocks
+    rec_bytes = (D - R) + 2 * R + 4
+    step_bytes = idx_bytes + B * k * rec_bytes + B * W * D * 2 + B * H * D * 2 * 2 + \
+        B * ntok * (D + dI) * 2 * 2
+    step_flops = idx_flops + 4.0 * B * H * D * (k + W)
+
+    # parity of the last step on set 0 against the oracle (sequence 0, full indexer scan)
+    step(0)
+    torch.cuda.synchronize()
+    gpu_sel = sel.cpu().numpy()[:, 0]
+    gpu_out = outs[0].float().cpu().numpy()
+
+    result = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "context_tokens": T, "csa_entries": N, "heads": H,
+                   "head_dim": D, "rope_dims": R, "indexer_heads": HI, "indexer_dim": dI, "topk": k,
+                   "window": W, "input_copies": len(sets)},
+        "roofline": {"kernel": "v4a_indexer_topk (MXFP4 scoring + top-k select)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "ms_per_launch": idx_ms, "algorithmic_bytes": idx_bytes,
+                     "mfma_util": idx_flops / (idx_ms / 1e3) / (MXFP4_PEAK_TFLOPS * 1e12)},
+        "step": {"algorithmic_bytes": step_bytes, "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9,
+                 "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, "flops": step_flops,
+                 "wall_s": wall},
+    }
+
+    if not args.no_secondary:
+        result["secondary"] = hca_secondary(v4, torch, HCA_1M, args, f32, bf16)
+
+    if not args.no_cpu_baseline:
+        import oracle
+        from workloads import bf16_bits_to_f64
+        print("[bench] oracle on the host", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        b = 0
+        ent = oracle.compress_csa(raw["kv_a"][b], raw["kv_b"][b], raw["gate_a"][b], raw["gate_b"][b], raw["bias_a"],
+                                  raw["bias_b"], tok0=tok0, m=m, first_entry=N - 1, n_entries=1, apply_rope=True, R=R)
+        key = oracle.compress_csa(raw["idx_a"][b], raw["idx_b"][b], raw["idx_gate_a"][b], raw["idx_gate_b"][b],
+                                  raw["idx_bias_a"], raw["idx_bias_b"], tok0=tok0, m=m, first_entry=N - 1,
+                                  n_entries=1, apply_rope=False, R=0)
+        keys_b = inp["keys"][b].copy()
+        keys_b[N - 1] = key[0]
+        kc, ksc = oracle.quant_mxfp4(keys_b)
+        qc, qs = oracle.quant_mxfp4(inp["q_idx"][b])
+        scores, bad = oracle.indexer_scores_mxfp4(qc, qs, inp["w"][b], kc, ksc)
+        ref_sel = oracle.topk(scores, k)
+        rec_rows = rec0
+        rec_rows[N - 1] = ent[0]
+        chosen = ref_sel[ref_sel >= 0]
+        ents = oracle.dequant_kv(*oracle.quant_kv(rec_rows[chosen], R))
+        qd = bf16_bits_to_f64(to_bf16_bits(inp["q"][b]))
+        wd = bf16_bits_to_f64(to_bf16_bits(inp["window"][b]))
+        ref = oracle.attend(qd, ents, wd, inp["sink"], scale, rope_inverse=True, R=R, t_q=T - 1)
+        cpu_s = time.perf_counter() - t0
+        recall = len(np.intersect1d(gpu_sel[b], ref_sel)) / k
+        ref_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        err = np.abs(gpu_out[b] - ref_bf16)
+        result["cpu_baseline"] = {"value": 1.0 / cpu_s, "unit": "tokens/s", "cores": oracle.threads(),
+                                  "kind": "oracle", "seconds": cpu_s,
+                                  "sample": "sequence 0 of the same step: compress its new block, exact MXFP4 "
+                                            "scores of all 262144 entries, full-sort top-1024, double-precision "
+                                            "attention (1 token)"}
+        result["check"] = {"sequence": 0, "topk_equal": bool(np.array_equal(gpu_sel[b], ref_sel)),
+                           "topk_recall": recall, "max_abs": float(err.max()),
+                           "rel_l2": float(np.linalg.norm(gpu_out[b] - ref_bf16) / np.linalg.norm(ref_bf16)),
+                           "inexact_dots": bad}
+    print(json.dumps(result), flush=True)
+
+
+def hca_secondary(v4, torch, wl, args, f32, bf16):
+    """The 1M-context HCA decode step (16 x 8192 entries, 128 heads): dense MQA + window + sink."""
+    from workloads import decode_inputs
+    print(f"[bench] secondary: {wl.name}", file=sys.stderr, flush=True)
+    inp = decode_inputs(wl, threads=16)
+    B, H, D, R, W, N = wl.B, wl.H, wl.D, wl.R, wl.W, inp["N"]
+    kv0 = v4.KV.empty(B, N, D, R)
+    v4.v4a_quantize_kv(f32(inp["records"].reshape(-1, D)), kv0)
+    q, win, sink = bf16(inp["q"]), bf16(inp["window"]), f32(inp["sink"])
+    rot = max(1, min(args.rotate, 8))
+    kvs = [kv0] + [v4.KV(kv0.fmt, D, R, kv0.nope.clone(), kv0.rope.clone(), kv0.scale.clone(), N)
+                   for _ in range(rot - 1)]
+    ws = v4.workspace(v4.v4a_decode_workspace(B, H, D, N, W))
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    q_pos = [wl.T - 1] * B
+
+    def step(i):
+        v4.v4a_decode_hca(q, kvs[i % rot], [N] * B, wl.m_hca, win, [W] * B, W, sink, q_pos,
+                          softmax_scale=1.0 / math.sqrt(D), out=out, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = args.steps
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nbytes = B * N * ((D - R) + 2 * R + 4) + B * W * D * 2 + B * H * D * 2 * 2
+    flops = 4.0 * B * H * D * (N + W)
+    return {"workload": wl.name, "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms,
+            "bound": "mfma", "mfma_tflops": flops / (ms / 1e3) / 1e12,
+            "mfma_frac": flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
+            "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "input_copies": rot}
+
+
+if __name__ == "__main__":
+    main()

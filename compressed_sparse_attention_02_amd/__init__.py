@@ -1,0 +1,256 @@
+"""Python binding of libv4attn (DeepSeek-V4 CSA/HCA attention hot path on MI355X / gfx950).
+
+Argument marshalling only: each function here forwards torch device tensors (as raw
+pointers) and host integers to the C entry point of the same name in ``include/v4attn.h``,
+on the current torch stream, and raises ``V4AError`` with the library's message when the
+call is rejected.  Every step of the path runs in the HIP kernels of ``libv4attn.so``; there
+is no fallback: importing the binding without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libv4attn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "v4attn.h")
+
+# enums (include/v4attn.h)
+V4A_F32, V4A_BF16 = 0, 1
+V4A_KV_F32, V4A_KV_FP8_BF16 = 0, 1
+V4A_IDX_F32, V4A_IDX_MXFP4 = 0, 1
+STATUS = {0: "V4A_OK", 1: "V4A_EINVAL", 2: "V4A_EUNSUPPORTED", 3: "V4A_EWORKSPACE", 4: "V4A_EHIP"}
+
+
+class V4AError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class c_kv(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("nope", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("cap", ctypes.c_int64)]
+
+
+class c_idx(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("d", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("cap", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libv4attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m compressed_sparse_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        KVP, IDXP = ctypes.POINTER(c_kv), ctypes.POINTER(c_idx)
+        sig = {
+            "v4a_quantize_kv": [P, I64, KVP, I64, P],
+            "v4a_quantize_mxfp4": [P, I64, IDXP, I64, P],
+            "v4a_compress_csa": [P, P, ctypes.c_int, I32, P, P, I32, P, P, I64, I64, I32, I64, I64,
+                                 I32, F32, P, KVP, IDXP, I32, I32, P],
+            "v4a_compress_hca": [P, ctypes.c_int, I32, P, I32, P, I64, I64, I32, I64, I64, I32, F32,
+                                 P, KVP, I32, I32, P],
+            "v4a_indexer_topk": [IDXP, P, I32, IDXP, P, I32, I32, I32, P, I32, P, P, SZ, P],
+            "v4a_indexer_scores": [IDXP, P, I32, IDXP, P, I32, I32, I32, P, I64, P, P],
+            "v4a_decode_csa": [P, ctypes.c_int, I32, I32, KVP, P, I32, P, ctypes.c_int, P, I32, P,
+                               P, F32, I32, F32, P, ctypes.c_int, P, SZ, P],
+            "v4a_decode_hca": [P, ctypes.c_int, I32, I32, KVP, P, I32, P, ctypes.c_int, P, I32, P,
+                               P, F32, I32, F32, P, ctypes.c_int, P, SZ, P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.v4a_indexer_topk_workspace.argtypes = [I32, I32, I64, I32]
+        L.v4a_indexer_topk_workspace.restype = SZ
+        L.v4a_decode_workspace.argtypes = [I32, I32, I32, I64, I32]
+        L.v4a_decode_workspace.restype = SZ
+        L.v4a_last_error.restype = ctypes.c_char_p
+        L.v4a_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise V4AError(status, lib().v4a_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libv4attn must be contiguous")
+    return t.data_ptr()
+
+
+def _host_i64(vals):
+    arr = (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def _host_i32(vals):
+    return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ftype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return V4A_BF16
+    if t.dtype == torch.float32:
+        return V4A_F32
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+@dataclass
+class KV:
+    """A batch of entry records (device tensors); see ``v4a_kv`` in include/v4attn.h."""
+    fmt: int
+    D: int
+    R: int
+    nope: torch.Tensor
+    rope: torch.Tensor | None
+    scale: torch.Tensor | None
+    cap: int
+
+    @staticmethod
+    def empty(B: int, cap: int, D: int, R: int, fmt: int = V4A_KV_FP8_BF16, device="cuda"):
+        if fmt == V4A_KV_FP8_BF16:
+            return KV(fmt, D, R, torch.zeros((B, cap, D - R), dtype=torch.uint8, device=device),
+                      torch.zeros((B, cap, R), dtype=torch.int16, device=device),
+                      torch.zeros((B, cap), dtype=torch.float32, device=device), cap)
+        return KV(fmt, D, R, torch.zeros((B, cap, D), dtype=torch.float32, device=device), None, None, cap)
+
+    def c(self) -> c_kv:
+        return c_kv(self.fmt, self.D, self.R, _ptr(self.nope), _ptr(self.rope), _ptr(self.scale), self.cap)
+
+
+@dataclass
+class Idx:
+    """A batch of indexer vectors (device tensors); see ``v4a_idx`` in include/v4attn.h."""
+    fmt: int
+    d: int
+    codes: torch.Tensor
+    scales: torch.Tensor | None
+    cap: int
+
+    @staticmethod
+    def empty(B: int, cap: int, d: int, fmt: int = V4A_IDX_MXFP4, device="cuda"):
+        if fmt == V4A_IDX_MXFP4:
+            return Idx(fmt, d, torch.zeros((B, cap, d // 2), dtype=torch.uint8, device=device),
+                       torch.zeros((B, cap, d // 32), dtype=torch.uint8, device=device), cap)
+        return Idx(fmt, d, torch.zeros((B, cap, d), dtype=torch.float32, device=device), None, cap)
+
+    def c(self) -> c_idx:
+        return c_idx(self.fmt, self.d, _ptr(self.codes), _ptr(self.scales), self.cap)
+
+
+# ------------------------------------------------------------------ entry points ----
+
+def v4a_version() -> str:
+    return lib().v4a_version().decode()
+
+
+def v4a_quantize_kv(x: torch.Tensor, out: KV, row0: int = 0, stream=None):
+    rows = x.numel() // out.D if x.numel() else 0
+    _check(lib().v4a_quantize_kv(_ptr(x), rows, ctypes.byref(out.c()), row0, _stream(stream)))
+
+
+def v4a_quantize_mxfp4(x: torch.Tensor, out: Idx, row0: int = 0, stream=None):
+    rows = x.numel() // out.d if x.numel() else 0
+    _check(lib().v4a_quantize_mxfp4(_ptr(x), rows, ctypes.byref(out.c()), row0, _stream(stream)))
+
+
+def v4a_compress_csa(kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, *, tok0: int, m: int,
+                     first_entry: int, n_entries: int, apply_rope: bool = True,
+                     rope_theta: float = 10000.0, out_kv: KV | None = None,
+                     out_idx: Idx | None = None, b: int = 0, stream=None):
+    """Streams are [n_tok][D] (one sequence, slot b) or [n_seq][n_tok][D] (slots b..b+n_seq-1)."""
+    D = kv_a.shape[-1]
+    G = gate_a.shape[-1]
+    n_tok = kv_a.shape[-2]
+    n_seq = kv_a.shape[0] if kv_a.dim() == 3 else 1
+    _check(lib().v4a_compress_csa(
+        _ptr(kv_a), _ptr(kv_b), _ftype(kv_a), D, _ptr(gate_a), _ptr(gate_b), G, _ptr(bias_a),
+        _ptr(bias_b), tok0, n_tok, m, first_entry, n_entries, int(apply_rope), rope_theta, None,
+        ctypes.byref(out_kv.c()) if out_kv is not None else None,
+        ctypes.byref(out_idx.c()) if out_idx is not None else None, b, n_seq, _stream(stream)))
+
+
+def v4a_compress_hca(kv, gate, bias, *, tok0: int, m: int, first_entry: int, n_entries: int,
+                     apply_rope: bool = True, rope_theta: float = 10000.0, out_kv: KV, b: int = 0,
+                     stream=None):
+    n_seq = kv.shape[0] if kv.dim() == 3 else 1
+    _check(lib().v4a_compress_hca(
+        _ptr(kv), _ftype(kv), kv.shape[-1], _ptr(gate), gate.shape[-1], _ptr(bias), tok0,
+        kv.shape[-2], m, first_entry, n_entries, int(apply_rope), rope_theta, None,
+        ctypes.byref(out_kv.c()), b, n_seq, _stream(stream)))
+
+
+def v4a_indexer_topk_workspace(B: int, Q: int, n_max: int, k: int) -> int:
+    return int(lib().v4a_indexer_topk_workspace(B, Q, n_max, k))
+
+
+def v4a_indexer_topk(keys: Idx, n_entries, m: int, q_idx: Idx, w: torch.Tensor, B: int, Q: int,
+                     H_I: int, q_pos, k: int, out: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().v4a_indexer_topk(
+        ctypes.byref(keys.c()), _host_i64(n_entries), m, ctypes.byref(q_idx.c()), _ptr(w), B, Q,
+        H_I, _host_i64(q_pos), k, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def v4a_indexer_scores(keys: Idx, n_entries, m: int, q_idx: Idx, w: torch.Tensor, B: int, Q: int,
+                       H_I: int, q_pos, n_max: int, out: torch.Tensor, stream=None):
+    _check(lib().v4a_indexer_scores(
+        ctypes.byref(keys.c()), _host_i64(n_entries), m, ctypes.byref(q_idx.c()), _ptr(w), B, Q,
+        H_I, _host_i64(q_pos), n_max, _ptr(out), _stream(stream)))
+
+
+def v4a_decode_workspace(B: int, H: int, D: int, n_keys_max: int, W: int) -> int:
+    return int(lib().v4a_decode_workspace(B, H, D, n_keys_max, W))
+
+
+def v4a_decode_csa(q, kv: KV, topk_idx, k: int, win, win_len, W: int, sink, q_pos, *,
+                   softmax_scale: float, out_rope_inverse: bool = True, rope_theta: float = 10000.0,
+                   out: torch.Tensor, ws: torch.Tensor | None = None, stream=None):
+    B, H = q.shape[0], q.shape[1]
+    _check(lib().v4a_decode_csa(
+        _ptr(q), _ftype(q), B, H, ctypes.byref(kv.c()), _ptr(topk_idx), k, _ptr(win),
+        _ftype(win) if win is not None else V4A_BF16, _host_i32(win_len), W, _ptr(sink),
+        _host_i64(q_pos), softmax_scale, int(out_rope_inverse), rope_theta, _ptr(out), _ftype(out),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def v4a_decode_hca(q, kv: KV, n_entries, m: int, win, win_len, W: int, sink, q_pos, *,
+                   softmax_scale: float, out_rope_inverse: bool = True, rope_theta: float = 10000.0,
+                   out: torch.Tensor, ws: torch.Tensor | None = None, stream=None):
+    B, H = q.shape[0], q.shape[1]
+    _check(lib().v4a_decode_hca(
+        _ptr(q), _ftype(q), B, H, ctypes.byref(kv.c()), _host_i64(n_entries), m, _ptr(win),
+        _ftype(win) if win is not None else V4A_BF16, _host_i32(win_len), W, _ptr(sink),
+        _host_i64(q_pos), softmax_scale, int(out_rope_inverse), rope_theta, _ptr(out), _ftype(out),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A caller-owned workspace buffer (torch allocations are 256-byte aligned)."""
+    return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)

@@ -1,0 +1,522 @@
+// api.hip -- the C ABI of the hot path (declared in include/v4attn.h): host-side argument
+// validation (always before any launch), workspace layout, and kernel dispatch.  No device
+// memory is allocated here; scratch lives in the caller's workspace.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.hpp"
+
+namespace v4a {
+
+static thread_local std::string g_err;
+
+void set_error(const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+static v4a_status fail(v4a_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+static v4a_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return V4A_OK;
+    return fail(V4A_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static v4a_status check_kv(const v4a_kv *kv, const char *name) {
+    if (!kv) return fail(V4A_EINVAL, "%s is NULL", name);
+    if (kv->cap < 1) return fail(V4A_EINVAL, "%s->cap must be >= 1", name);
+    if (kv->D < 2 || kv->D > 512 || kv->R < 0 || kv->R > kv->D || (kv->R & 1))
+        return fail(V4A_EUNSUPPORTED, "%s: D=%d R=%d not supported", name, kv->D, kv->R);
+    if (!kv->nope) return fail(V4A_EINVAL, "%s->nope is NULL", name);
+    if (kv->fmt == V4A_KV_FP8_BF16) {
+        if (!kv->scale || (kv->R > 0 && !kv->rope))
+            return fail(V4A_EINVAL, "%s: FP8 records need rope and scale arrays", name);
+        if (((kv->D - kv->R) % 8) != 0 || (kv->R % 4) != 0)
+            return fail(V4A_EUNSUPPORTED, "%s: D-R must be a multiple of 8 and R of 4", name);
+        if (!aligned(kv->nope, 16) || !aligned(kv->rope, 16) || !aligned(kv->scale, 4))
+            return fail(V4A_EINVAL, "%s: record arrays must be 16-byte aligned", name);
+    } else if (kv->fmt == V4A_KV_F32) {
+        if (!aligned(kv->nope, 16)) return fail(V4A_EINVAL, "%s->nope must be 16-byte aligned", name);
+    } else {
+        return fail(V4A_EUNSUPPORTED, "%s: unknown record format %d", name, (int)kv->fmt);
+    }
+    return V4A_OK;
+}
+
+static v4a_status check_idx(const v4a_idx *x, const char *name) {
+    if (!x) return fail(V4A_EINVAL, "%s is NULL", name);
+    if (x->cap < 1) return fail(V4A_EINVAL, "%s->cap must be >= 1", name);
+    if (!x->codes) return fail(V4A_EINVAL, "%s->codes is NULL", name);
+    if (x->fmt == V4A_IDX_MXFP4) {
+        if (x->d % 32 != 0 || x->d < 32 || x->d > 512)
+            return fail(V4A_EUNSUPPORTED, "%s: MXFP4 needs d a multiple of 32 up to 512", name);
+        if (!x->scales) return fail(V4A_EINVAL, "%s->scales is NULL", name);
+        if (!aligned(x->codes, 16) || !aligned(x->scales, 4))
+            return fail(V4A_EINVAL, "%s: codes must be 16-byte and scales 4-byte aligned", name);
+    } else if (x->fmt == V4A_IDX_F32) {
+        if (x->d < 1 || x->d > 512) return fail(V4A_EUNSUPPORTED, "%s: d=%d", name, x->d);
+        if (!aligned(x->codes, 4)) return fail(V4A_EINVAL, "%s->codes misaligned", name);
+    } else {
+        return fail(V4A_EUNSUPPORTED, "%s: unknown format %d", name, (int)x->fmt);
+    }
+    return V4A_OK;
+}
+
+// ------------------------------------------------------------- indexer workspace ----
+struct TopkWs {
+    size_t keys, hist, counters, cand, sel, total;
+};
+
+static TopkWs topk_layout(int B, int Q, int64_t n_max, int k) {
+    TopkWs L{};
+    const size_t BQ = (size_t)B * (size_t)Q;
+    size_t off = 0;
+    L.keys = off;
+    off = round_up(off + BQ * (size_t)n_max * 4, 256);
+    L.hist = off;
+    off += BQ * 4096 * 4;
+    L.counters = off;
+    off = round_up(off + BQ * 16, 256);
+    L.cand = off;
+    off = round_up(off + BQ * (size_t)n_max * 8, 256);
+    L.sel = off;
+    off = round_up(off + BQ * (size_t)k * 4, 256);
+    L.total = off;
+    return L;
+}
+
+static v4a_status fill_query_pos(QueryPos &qp, int B, int Q, int m, const int64_t *n_entries,
+                                 const int64_t *q_pos, int64_t cap, int64_t *n_max) {
+    if (B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "B=%d exceeds %d sequences per call", B, kMaxSeq);
+    memset(&qp, 0, sizeof qp);
+    qp.Q = Q;
+    qp.m = m;
+    bool consecutive = true;
+    for (int b = 0; b < B; b++) {
+        if (n_entries[b] < 0) return fail(V4A_EINVAL, "n_entries[%d] < 0", b);
+        if (n_entries[b] > cap) return fail(V4A_EINVAL, "n_entries[%d]=%lld exceeds keys->cap", b, (long long)n_entries[b]);
+        qp.n_ent[b] = n_entries[b];
+        for (int j = 0; j < Q; j++) {
+            int64_t p = q_pos[(int64_t)b * Q + j];
+            if (p < 0) return fail(V4A_EINVAL, "q_pos[%d] < 0", b * Q + j);
+            if (p != q_pos[(int64_t)b * Q] + j) consecutive = false;
+        }
+    }
+    if (consecutive) {
+        qp.mode = 1;
+        for (int b = 0; b < B; b++) qp.pos[b] = q_pos[(int64_t)b * Q];
+    } else {
+        if ((int64_t)B * Q > kMaxSeq)
+            return fail(V4A_EUNSUPPORTED, "non-consecutive query positions need B*Q <= %d", kMaxSeq);
+        qp.mode = 0;
+        for (int i = 0; i < B * Q; i++) qp.pos[i] = q_pos[i];
+    }
+    int64_t mx = 0;
+    for (int i = 0; i < B * Q; i++) {
+        int64_t v = visible_keys(qp, i);
+        if (v > mx) mx = v;
+    }
+    *n_max = mx;
+    return V4A_OK;
+}
+
+static v4a_status check_indexer_args(const v4a_idx *keys, const int64_t *n_entries, int32_t m,
+                                     const v4a_idx *q_idx, const float *w, int32_t B, int32_t Q,
+                                     int32_t H_I, const int64_t *q_pos) {
+    v4a_status st;
+    if ((st = check_idx(keys, "keys")) != V4A_OK) return st;
+    if ((st = check_idx(q_idx, "q_idx")) != V4A_OK) return st;
+    if (!n_entries || !q_pos || !w) return fail(V4A_EINVAL, "n_entries, q_pos and w are required");
+    if (keys->fmt != q_idx->fmt || keys->d != q_idx->d)
+        return fail(V4A_EINVAL, "keys and q_idx must share format and d");
+    if (keys->fmt == V4A_IDX_MXFP4 && keys->d != 128)
+        return fail(V4A_EUNSUPPORTED, "the MXFP4 indexer supports d = 128");
+    if (keys->fmt == V4A_IDX_F32 && (keys->d > 128))
+        return fail(V4A_EUNSUPPORTED, "the fp32 indexer supports d <= 128");
+    if (B < 1 || Q < 1) return fail(V4A_EINVAL, "B and Q must be >= 1");
+    if (H_I < 4 || H_I > 64 || (H_I % 4) != 0)
+        return fail(V4A_EUNSUPPORTED, "H_I=%d: need a multiple of 4 in [4, 64]", H_I);
+    if ((int64_t)Q * H_I > q_idx->cap) return fail(V4A_EINVAL, "Q*H_I exceeds q_idx->cap");
+    if (m < 1 || m > 128) return fail(V4A_EUNSUPPORTED, "m=%d not in [1, 128]", m);
+    if (!aligned(w, 4)) return fail(V4A_EINVAL, "w misaligned");
+    return V4A_OK;
+}
+
+}  // namespace v4a
+
+using namespace v4a;
+
+extern "C" {
+
+const char *v4a_last_error(void) { return g_err.c_str(); }
+
+const char *v4a_version(void) { return "v4attn 0.1.0 (gfx950)"; }
+
+v4a_status v4a_quantize_kv(const float *x, int64_t rows, const v4a_kv *out, int64_t row0, void *stream) {
+    v4a_status st = check_kv(out, "out");
+    if (st != V4A_OK) return st;
+    if (rows < 0 || row0 < 0) return fail(V4A_EINVAL, "rows and row0 must be >= 0");
+    if (rows > 0 && !x) return fail(V4A_EINVAL, "x is NULL");
+    if (x && !aligned(x, 16)) return fail(V4A_EINVAL, "x must be 16-byte aligned");
+    if (out->D != 32 && out->D != 64 && out->D != 128 && out->D != 256 && out->D != 512)
+        return fail(V4A_EUNSUPPORTED, "D=%d: need 32, 64, 128, 256 or 512", out->D);
+    const int vpt = out->D >= 64 ? out->D / 64 : 1;
+    if (((out->D - out->R) % vpt) != 0) return fail(V4A_EUNSUPPORTED, "D-R must be a multiple of D/64");
+    g_err.clear();
+    return hip_status(launch_quantize_kv(x, rows, *out, row0, (hipStream_t)stream), "v4a_quantize_kv");
+}
+
+v4a_status v4a_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx *out, int64_t row0, void *stream) {
+    v4a_status st = check_idx(out, "out");
+    if (st != V4A_OK) return st;
+    if (rows < 0 || row0 < 0) return fail(V4A_EINVAL, "rows and row0 must be >= 0");
+    if (rows > 0 && !x) return fail(V4A_EINVAL, "x is NULL");
+    if (out->d != 32 && out->d != 64 && out->d != 128 && out->d != 256 && out->d != 512)
+        return fail(V4A_EUNSUPPORTED, "d=%d: need 32, 64, 128, 256 or 512", out->d);
+    g_err.clear();
+    return hip_status(launch_quantize_mxfp4(x, rows, *out, row0, (hipStream_t)stream), "v4a_quantize_mxfp4");
+}
+
+static v4a_status compress_common(CompressArgs &a, const float *norm_w, void *stream) {
+    if (norm_w) return fail(V4A_EUNSUPPORTED, "norm_w must be NULL");
+    if (a.D != 32 && a.D != 64 && a.D != 128 && a.D != 256 && a.D != 512)
+        return fail(V4A_EUNSUPPORTED, "D=%d: need 32, 64, 128, 256 or 512", a.D);
+    if (a.G != 1 && a.G != a.D) return fail(V4A_EUNSUPPORTED, "G must be 1 or D");
+    if (a.m < 1 || a.m > 128) return fail(V4A_EUNSUPPORTED, "m=%d not in [1, 128]", a.m);
+    if (a.n_entries < 0 || a.first_entry < 0 || a.n_tok < 0) return fail(V4A_EINVAL, "negative size");
+    if (a.tok0 % a.m != 0) return fail(V4A_EINVAL, "tok0 must be a multiple of m");
+    if (a.b0 < 0 || a.n_seq < 0) return fail(V4A_EINVAL, "b0 and n_seq must be >= 0");
+    if (a.n_seq > 65535) return fail(V4A_EUNSUPPORTED, "n_seq > 65535");
+    for (int s = 0; s < a.n_streams; s++)
+        if (a.n_entries > 0 && (!a.x[s] || !a.gate[s] || !a.bias[s]))
+            return fail(V4A_EINVAL, "stream, gate and bias pointers are required");
+    if (a.n_entries > 0) {
+        const int64_t need_lo = a.n_streams == 2 ? (a.first_entry >= 1 ? a.m * (a.first_entry - 1) : 0)
+                                                 : a.m * a.first_entry;
+        const int64_t need_hi = a.m * (a.first_entry + a.n_entries);
+        if (a.tok0 > need_lo || a.tok0 + a.n_tok < need_hi)
+            return fail(V4A_EINVAL, "rows [%lld, %lld) do not cover tokens [%lld, %lld)", (long long)a.tok0,
+                        (long long)(a.tok0 + a.n_tok), (long long)need_lo, (long long)need_hi);
+    }
+    if (a.kv) {
+        v4a_status st = check_kv(a.kv, "out_kv");
+        if (st != V4A_OK) return st;
+        if (a.kv->D != a.D) return fail(V4A_EINVAL, "out_kv->D != D");
+        if (a.first_entry + a.n_entries > a.kv->cap) return fail(V4A_EINVAL, "entries exceed out_kv->cap");
+        if (a.rope && (a.kv->R < 2)) return fail(V4A_EINVAL, "apply_rope needs R >= 2");
+        a.R = a.kv->R;
+        const int vpt = a.D >= 64 ? a.D / 64 : 1;
+        if (((a.D - a.R) % vpt) != 0) return fail(V4A_EUNSUPPORTED, "D-R must be a multiple of D/64");
+    } else {
+        v4a_status st = check_idx(a.idx, "out_idx");
+        if (st != V4A_OK) return st;
+        if (a.idx->d != a.D) return fail(V4A_EINVAL, "out_idx->d != D");
+        if (a.first_entry + a.n_entries > a.idx->cap) return fail(V4A_EINVAL, "entries exceed out_idx->cap");
+        a.rope = false;
+        a.R = 0;
+    }
+    g_err.clear();
+    return hip_status(launch_compress(a, (hipStream_t)stream), "compress");
+}
+
+v4a_status v4a_compress_csa(const void *kv_a, const void *kv_b, v4a_float in_t, int32_t D, const float *gate_a,
+                            const float *gate_b, int32_t G, const float *bias_a, const float *bias_b, int64_t tok0,
+                            int64_t n_tok, int32_t m, int64_t first_entry, int64_t n_entries, int32_t apply_rope,
+                            float rope_theta, const float *norm_w, const v4a_kv *out_kv, const v4a_idx *out_idx,
+                            int32_t b0, int32_t n_seq, void *stream) {
+    if ((out_kv == nullptr) == (out_idx == nullptr))
+        return fail(V4A_EINVAL, "exactly one of out_kv and out_idx must be given");
+    if (in_t != V4A_F32 && in_t != V4A_BF16) return fail(V4A_EINVAL, "in_t");
+    CompressArgs a{};
+    a.x[0] = kv_a;
+    a.x[1] = kv_b;
+    a.gate[0] = gate_a;
+    a.gate[1] = gate_b;
+    a.bias[0] = bias_a;
+    a.bias[1] = bias_b;
+    a.n_streams = 2;
+    a.bf16_in = in_t == V4A_BF16;
+    a.D = D;
+    a.G = G;
+    a.m = m;
+    a.tok0 = tok0;
+    a.n_tok = n_tok;
+    a.first_entry = first_entry;
+    a.n_entries = n_entries;
+    a.rope = apply_rope != 0;
+    a.theta = rope_theta;
+    a.kv = out_kv;
+    a.idx = out_idx;
+    a.b0 = b0;
+    a.n_seq = n_seq;
+    return compress_common(a, norm_w, stream);
+}
+
+v4a_status v4a_compress_hca(const void *kv, v4a_float in_t, int32_t D, const float *gate, int32_t G,
+                            const float *bias, int64_t tok0, int64_t n_tok, int32_t m, int64_t first_entry,
+                            int64_t n_entries, int32_t apply_rope, float rope_theta, const float *norm_w,
+                            const v4a_kv *out_kv, int32_t b0, int32_t n_seq, void *stream) {
+    if (!out_kv) return fail(V4A_EINVAL, "out_kv is NULL");
+    if (in_t != V4A_F32 && in_t != V4A_BF16) return fail(V4A_EINVAL, "in_t");
+    CompressArgs a{};
+    a.x[0] = kv;
+    a.x[1] = kv;
+    a.gate[0] = gate;
+    a.gate[1] = gate;
+    a.bias[0] = bias;
+    a.bias[1] = bias;
+    a.n_streams = 1;
+    a.bf16_in = in_t == V4A_BF16;
+    a.D = D;
+    a.G = G;
+    a.m = m;
+    a.tok0 = tok0;
+    a.n_tok = n_tok;
+    a.first_entry = first_entry;
+    a.n_entries = n_entries;
+    a.rope = apply_rope != 0;
+    a.theta = rope_theta;
+    a.kv = out_kv;
+    a.b0 = b0;
+    a.n_seq = n_seq;
+    return compress_common(a, norm_w, stream);
+}
+
+size_t v4a_indexer_topk_workspace(int32_t B, int32_t Q, int64_t n_max, int32_t k) {
+    if (B < 0 || Q < 0 || n_max < 0 || k < 0) return 0;
+    return topk_layout(B, Q, n_max, k).total;
+}
+
+v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
+                            const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos, int32_t k,
+                            int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    v4a_status st = check_indexer_args(keys, n_entries, m, q_idx, w, B, Q, H_I, q_pos);
+    if (st != V4A_OK) return st;
+    if (k < 1 || k > 2048) return fail(V4A_EUNSUPPORTED, "k=%d not in [1, 2048]", k);
+    if (!out_idx || !aligned(out_idx, 4)) return fail(V4A_EINVAL, "out_idx is NULL or misaligned");
+    QueryPos qp;
+    int64_t n_max = 0;
+    if ((st = fill_query_pos(qp, B, Q, m, n_entries, q_pos, keys->cap, &n_max)) != V4A_OK) return st;
+    const TopkWs L = topk_layout(B, Q, n_max, k);
+    if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+        return fail(V4A_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, ws_bytes);
+    g_err.clear();
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    const size_t BQ = (size_t)B * Q;
+    hipError_t e = launch_zero(base + L.hist, BQ * 4096 * 4 + BQ * 16, s);
+    if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
+    IndexerArgs ia{};
+    ia.keys = keys;
+    ia.q = q_idx;
+    ia.w = w;
+    ia.B = B;
+    ia.Q = Q;
+    ia.H_I = H_I;
+    ia.n_max = n_max;
+    ia.score_keys = (uint32_t *)(base + L.keys);
+    ia.hist = (uint32_t *)(base + L.hist);
+    if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
+    SelectArgs sa{};
+    sa.score_keys = ia.score_keys;
+    sa.hist = ia.hist;
+    sa.n_max = n_max;
+    sa.BQ = (int)BQ;
+    sa.k = k;
+    sa.cand = (uint32_t *)(base + L.cand);
+    sa.cand_cap = n_max > 0 ? n_max : 1;
+    sa.sel = (int32_t *)(base + L.sel);
+    sa.counters = (uint32_t *)(base + L.counters);
+    sa.out = out_idx;
+    return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
+}
+
+v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
+                              const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos,
+                              int64_t n_max, float *out_scores, void *stream) {
+    v4a_status st = check_indexer_args(keys, n_entries, m, q_idx, w, B, Q, H_I, q_pos);
+    if (st != V4A_OK) return st;
+    if (!out_scores) return fail(V4A_EINVAL, "out_scores is NULL");
+    QueryPos qp;
+    int64_t vis_max = 0;
+    if ((st = fill_query_pos(qp, B, Q, m, n_entries, q_pos, keys->cap, &vis_max)) != V4A_OK) return st;
+    if (n_max < vis_max) return fail(V4A_EINVAL, "n_max=%lld is below the visible count %lld", (long long)n_max,
+                                     (long long)vis_max);
+    g_err.clear();
+    IndexerArgs ia{};
+    ia.keys = keys;
+    ia.q = q_idx;
+    ia.w = w;
+    ia.B = B;
+    ia.Q = Q;
+    ia.H_I = H_I;
+    ia.n_max = n_max;
+    ia.scores = out_scores;
+    return hip_status(launch_indexer(ia, qp, (hipStream_t)stream), "v4a_indexer_scores");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------- decode ----------
+namespace v4a {
+
+constexpr int kDecodeSplitTarget = 16;
+
+static int decode_split_cap(int64_t n_keys_max) {
+    int64_t tiles = (n_keys_max + kAttnTile - 1) / kAttnTile;
+    return (int)(tiles < kDecodeSplitTarget ? (tiles < 1 ? 1 : tiles) : kDecodeSplitTarget);
+}
+
+static size_t decode_ws_bytes(int B, int H, int D, int split_cap) {
+    if (split_cap <= 1) return 0;
+    return round_up((size_t)B * split_cap * H * D * 4 + (size_t)B * split_cap * H * 2 * 4, 256);
+}
+
+static v4a_status decode_common(AttnArgs &a, SeqInfo &sq, const int32_t *win_len, const int64_t *q_pos,
+                                v4a_float q_t, v4a_float win_t, v4a_float out_t, void *ws, size_t ws_bytes,
+                                void *stream, const char *name) {
+    if (!a.q || !a.out || !a.sink || !q_pos) return fail(V4A_EINVAL, "%s: q, out, sink and q_pos are required", name);
+    if (a.B < 1 || a.B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "%s: B=%d not in [1, %d]", name, a.B, kMaxSeq);
+    if (a.H < 1 || a.H > 128) return fail(V4A_EUNSUPPORTED, "%s: H=%d not in [1, 128]", name, a.H);
+    if (a.W < 0 || a.W > 128) return fail(V4A_EUNSUPPORTED, "%s: W=%d not in [0, 128]", name, a.W);
+    if (a.W > 0 && (!a.win || !win_len)) return fail(V4A_EINVAL, "%s: win and win_len are required", name);
+    if ((q_t != V4A_F32 && q_t != V4A_BF16) || (win_t != V4A_F32 && win_t != V4A_BF16) ||
+        (out_t != V4A_F32 && out_t != V4A_BF16))
+        return fail(V4A_EINVAL, "%s: bad element type", name);
+    a.q_bf16 = q_t == V4A_BF16;
+    a.win_bf16 = win_t == V4A_BF16;
+    a.out_bf16 = out_t == V4A_BF16;
+    a.D = a.kv->D;
+    a.R = a.kv->R;
+    if (a.D % 2 != 0 || (a.rope_inv && a.R < 2)) return fail(V4A_EUNSUPPORTED, "%s: odd D or no RoPE dims", name);
+    if (!aligned(a.q, 16) || !aligned(a.out, 16) || (a.win && !aligned(a.win, 16)))
+        return fail(V4A_EINVAL, "%s: q, win and out must be 16-byte aligned", name);
+    int64_t n_keys_max = 0;
+    for (int b = 0; b < a.B; b++) {
+        const int wl = a.W > 0 ? win_len[b] : 0;
+        if (wl < 0 || wl > a.W) return fail(V4A_EINVAL, "%s: win_len[%d]=%d not in [0, W]", name, b, wl);
+        if (q_pos[b] < 0) return fail(V4A_EINVAL, "%s: q_pos[%d] < 0", name, b);
+        sq.win_len[b] = wl;
+        sq.q_pos[b] = q_pos[b];
+        if ((int64_t)sq.n_ent[b] + wl > n_keys_max) n_keys_max = (int64_t)sq.n_ent[b] + wl;
+    }
+    const bool mfma = attn_uses_mfma(a);
+    if (!mfma && n_keys_max > 8192 + 2048)
+        return fail(V4A_EUNSUPPORTED, "%s: this format/shape uses the fp32 kernel, limited to %d keys", name, 8192 + 2048);
+    if (mfma) {
+        a.target_splits = kDecodeSplitTarget;
+        int cap = 1;
+        for (int b = 0; b < a.B; b++) {
+            int tps, sp;
+            split_plan_host(sq.n_ent[b] + sq.win_len[b], kDecodeSplitTarget, &tps, &sp);
+            if (sp > cap) cap = sp;
+        }
+        a.split_cap = cap;
+        const size_t need = decode_ws_bytes(a.B, a.H, a.D, cap);
+        if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+            return fail(V4A_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need, ws_bytes);
+        a.partial = need > 0 ? (float *)ws : nullptr;
+    } else {
+        a.target_splits = 1;
+        a.split_cap = 1;
+        a.partial = nullptr;
+    }
+    g_err.clear();
+    return hip_status(launch_attention(a, sq, (hipStream_t)stream), name);
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_keys_max, int32_t W) {
+    if (B < 0 || H < 0 || D < 0 || n_keys_max < 0 || W < 0) return 0;
+    return decode_ws_bytes(B, H, D, decode_split_cap(n_keys_max + W));
+}
+
+v4a_status v4a_decode_csa(const void *q, v4a_float q_t, int32_t B, int32_t H, const v4a_kv *kv,
+                          const int32_t *topk_idx, int32_t k, const void *win, v4a_float win_t,
+                          const int32_t *win_len, int32_t W, const float *sink, const int64_t *q_pos,
+                          float softmax_scale, int32_t out_rope_inverse, float rope_theta, void *out,
+                          v4a_float out_t, void *ws, size_t ws_bytes, void *stream) {
+    v4a_status st = check_kv(kv, "kv");
+    if (st != V4A_OK) return st;
+    if (!topk_idx || !aligned(topk_idx, 4)) return fail(V4A_EINVAL, "v4a_decode_csa: topk_idx is NULL or misaligned");
+    if (k < 1 || k > 2048) return fail(V4A_EUNSUPPORTED, "v4a_decode_csa: k=%d not in [1, 2048]", k);
+    AttnArgs a{};
+    SeqInfo sq;
+    memset(&sq, 0, sizeof sq);
+    a.q = q;
+    a.B = B;
+    a.H = H;
+    a.kv = kv;
+    a.topk = topk_idx;
+    a.k = k;
+    a.win = win;
+    a.W = W;
+    a.sink = sink;
+    a.scale = softmax_scale;
+    a.rope_inv = out_rope_inverse != 0;
+    a.theta = rope_theta;
+    a.out = out;
+    if (B >= 1 && B <= kMaxSeq)
+        for (int b = 0; b < B; b++) sq.n_ent[b] = k;
+    return decode_common(a, sq, win_len, q_pos, q_t, win_t, out_t, ws, ws_bytes, stream, "v4a_decode_csa");
+}
+
+v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32_t H, const v4a_kv *kv,
+                          const int64_t *n_entries, int32_t m, const void *win, v4a_float win_t,
+                          const int32_t *win_len, int32_t W, const float *sink, const int64_t *q_pos,
+                          float softmax_scale, int32_t out_rope_inverse, float rope_theta, void *out,
+                          v4a_float out_t, void *ws, size_t ws_bytes, void *stream) {
+    v4a_status st = check_kv(kv, "kv");
+    if (st != V4A_OK) return st;
+    if (!n_entries || !q_pos) return fail(V4A_EINVAL, "v4a_decode_hca: n_entries and q_pos are required");
+    if (m < 1) return fail(V4A_EINVAL, "v4a_decode_hca: m < 1");
+    if (B < 1 || B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "v4a_decode_hca: B=%d not in [1, %d]", B, kMaxSeq);
+    AttnArgs a{};
+    SeqInfo sq;
+    memset(&sq, 0, sizeof sq);
+    for (int b = 0; b < B; b++) {
+        if (n_entries[b] < 0 || n_entries[b] > kv->cap)
+            return fail(V4A_EINVAL, "v4a_decode_hca: n_entries[%d] not in [0, cap]", b);
+        if (q_pos[b] < 0) return fail(V4A_EINVAL, "v4a_decode_hca: q_pos[%d] < 0", b);
+        int64_t vis = (q_pos[b] + 1) / m;
+        if (vis > n_entries[b]) vis = n_entries[b];
+        if (vis > (1 << 30)) return fail(V4A_EUNSUPPORTED, "v4a_decode_hca: too many entries");
+        sq.n_ent[b] = (int32_t)vis;
+    }
+    a.q = q;
+    a.B = B;
+    a.H = H;
+    a.kv = kv;
+    a.topk = nullptr;
+    a.k = 0;
+    a.win = win;
+    a.W = W;
+    a.sink = sink;
+    a.scale = softmax_scale;
+    a.rope_inv = out_rope_inverse != 0;
+    a.theta = rope_theta;
+    a.out = out;
+    return decode_common(a, sq, win_len, q_pos, q_t, win_t, out_t, ws, ws_bytes, stream, "v4a_decode_hca");
+}
+
+}  // extern "C"

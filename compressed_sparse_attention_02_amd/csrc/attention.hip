@@ -1,0 +1,539 @@
+// attention.hip -- a6/a7: shared-KV multi-query attention over compressed entries plus the
+// sliding window, with the attention sink, split over keys and combined in a fixed order.
+// "DeepSeek V4 technical report explained" (firecat-web.com), item 2 "Hybrid attention":
+// multi-query attention over the selected compressed entries, head dim 512, partial RoPE on
+// the last 64 dims, a 128-token sliding window and a learnable sink logit.
+// "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.2: the window branch joins
+// the core attention and the sink is a learnable extra term of the softmax denominator.
+// "DeepSeek-V4: the engineering answer to million-token context" (mewclaw), "Partial RoPE":
+// the attention output is treated so that values carry no absolute position (here: its RoPE
+// slice is rotated back by the query position).
+//
+// Keys of sequence b, in order: its entries (the top-k indices for CSA, the visible prefix
+// for HCA) then its window tokens; every key is also its own value over all D dims.
+//
+// MFMA kernel (FP8/BF16 records, BF16 queries and window).  A workgroup of four wavefronts
+// owns 64 heads (16 per wavefront) of one sequence and one split of its keys; with 128 heads
+// the two head-group workgroups of a split get linear ids 8 apart, so they land on the same
+// XCD and share its L2 for the key tiles.  Per tile of 32 keys:
+//   staging: every lane converts 4 keys x 4 dims (E4M3 codes are exact in BF16) and writes
+//            them key-major (Er: rows = keys) and dim-major (Ec: rows = dims) into LDS;
+//   scores:  S^T = E Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims from Er,
+//            B = the wavefront's 16 query heads held in registers), accumulating the FP8
+//            dims and the BF16 RoPE dims separately so the per-entry scale folds in as
+//            s = scale_e * (q.codes) + q.rope;
+//   softmax: online, in the exp2 domain, each lane owning one head and 8 keys;
+//   values:  O^T += E^T P^T with A = 16 dims x 32 keys from Ec and B = the lane's own
+//            probabilities (times scale_e for the FP8 dims), whose key order the A reads
+//            follow, so P never leaves registers.
+// A split's (m, l, O) go to the workspace unless the sequence has a single split, in which
+// case the workgroup finishes the output itself (sink, normalisation, inverse RoPE, cast).
+// Split boundaries depend only on the sequence's own key count.
+#include "common.hpp"
+
+namespace v4a {
+
+constexpr int kTile = 32;
+constexpr int kErStride = 520;  // bf16 per key row in Er (512 + 8: staggers LDS banks)
+constexpr int kEcStride = 36;   // bf16 per dim row in Ec (32 keys + 4)
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnParams {
+    const void *q;           // [B][H][D]
+    bool q_bf16;
+    int B, H, D, R;
+    int fmt;                 // v4a_kv_fmt
+    const uint8_t *nope;     // FP8: [B][cap][D-R]; F32: float [B][cap][D]
+    const uint16_t *rope;    // [B][cap][R]
+    const float *kscale;     // [B][cap]
+    int64_t cap;
+    const int32_t *topk;     // [B][k] or NULL
+    int k;
+    const void *win;         // [B][W][D]
+    bool win_bf16;
+    int W;
+    const float *sink;       // [H]
+    float scale2;            // softmax scale * log2(e)
+    bool rope_inv;
+    double theta;
+    void *out;
+    bool out_bf16;
+    float *part_o;           // [B][S][H][D]
+    float *part_ml;          // [B][S][H][2]
+    int S;                   // split capacity per sequence
+    int target;              // splits aimed at per sequence
+    int n_hg;                // head groups (workgroups) per split
+};
+
+__host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int *tps, int *splits) {
+    int tiles = (n_keys + kTile - 1) / kTile;
+    int t = (tiles + target - 1) / target;
+    if (t < 1) t = 1;
+    int s = (tiles + t - 1) / t;
+    if (s < 1) s = 1;
+    *tps = t;
+    *splits = s;
+}
+
+// Factor turning one head's accumulated sum into the output: exp(m - M) / den with
+// M = max(sink, m) and den = exp(sink - M) + l exp(m - M) (exp2 domain; 0 if nothing is left).
+__device__ __forceinline__ float finish_factor(const AttnParams &P, int h, float m2, float l) {
+    const float sink2 = P.sink[h] * kLog2e;
+    const float M = fmaxf(sink2, m2);
+    if (M == -INFINITY) return 0.0f;
+    const float c = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - M);
+    const float den = exp2f(sink2 - M) + l * c;
+    return den > 0.0f ? c / den : 0.0f;
+}
+
+// Inverse rotation (by -pos) of one RoPE pair (x, y) with pair index j.
+__device__ __noinline__ float2 rope_unrotate(double pos, int j, int R, double theta, float x, float y) {
+    float c, s;
+    rope_cs(pos, j, R, theta, &c, &s);
+    return make_float2(x * c + y * s, -x * s + y * c);
+}
+
+template <int NV>
+__device__ __forceinline__ void store_out(const AttnParams &P, int b, int h, int d0, const float (&o)[NV]) {
+    const int64_t base = ((int64_t)b * P.H + h) * P.D + d0;
+    if (P.out_bf16) {
+        uint16_t *dst = (uint16_t *)P.out + base;
+#pragma unroll
+        for (int v = 0; v < NV; v++) dst[v] = f32_to_bf16(o[v]);
+    } else {
+        float *dst = (float *)P.out + base;
+#pragma unroll
+        for (int v = 0; v < NV; v++) dst[v] = o[v];
+    }
+}
+
+// Final output of one head from NV consecutive dims at d0 (NV even, pairs aligned).
+template <int NV>
+__device__ __forceinline__ void finish_head(const AttnParams &P, const SeqInfo &Sq, int b, int h,
+                                            int d0, float m2, float l, float (&o)[NV]) {
+    const float f = finish_factor(P, h, m2, l);
+#pragma unroll
+    for (int v = 0; v < NV; v++) o[v] *= f;
+    const int Dn = P.D - P.R;
+    if (P.rope_inv && d0 >= Dn) {
+#pragma unroll
+        for (int v = 0; v < NV; v += 2) {
+            const float2 r = rope_unrotate((double)Sq.q_pos[b], (d0 + v - Dn) / 2, P.R, P.theta, o[v], o[v + 1]);
+            o[v] = r.x;
+            o[v + 1] = r.y;
+        }
+    }
+    store_out<NV>(P, b, h, d0, o);
+}
+
+// ------------------------------------------------------------------ MFMA kernel -----
+template <int D, int R>
+__global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo Sq) {
+    constexpr int NKS = D / 32;   // k-steps of the score MFMA
+    constexpr int NDT = D / 16;   // dim tiles of the value MFMA
+    constexpr int Dn = D - R;
+    __shared__ __attribute__((aligned(16))) uint16_t Er[kTile * kErStride];
+    __shared__ __attribute__((aligned(16))) uint16_t Ec[D * kEcStride];
+    __shared__ float ksc[kTile];
+    __shared__ int kvalid[kTile];
+
+    // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart
+    int L = blockIdx.x, hg = 0, p = L;
+    if (P.n_hg == 2) {
+        hg = (L >> 3) & 1;
+        p = (L >> 4) * 8 + (L & 7);
+    }
+    const int b = p / P.S, split = p % P.S;
+    if (b >= P.B) return;
+    const int n_ent = Sq.n_ent[b], n_keys = n_ent + Sq.win_len[b];
+    int tps, splits;
+    split_plan(n_keys, P.target, &tps, &splits);
+    if (split >= splits) return;
+    const int kb0 = split * tps * kTile;
+    const int kb1 = min(n_keys, kb0 + tps * kTile);
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int h0 = hg * 64 + wv * 16;
+    const bool wave_on = h0 < P.H;
+    const int h = h0 + col;
+    const int NT = blockDim.x;
+
+    // query heads as the B operand of S^T: lane holds head h, dims 32*ks + 8*grp + j
+    v8bf qT[NKS];
+    {
+        const uint16_t *qr = (const uint16_t *)P.q + ((int64_t)b * P.H + (wave_on ? h : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) {
+            uint4 u = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+            qT[ks] = __builtin_bit_cast(v8bf, u);
+        }
+    }
+    v4f O[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int n_tasks = 8 * (D / 4);
+    for (int tb = kb0; tb < kb1; tb += kTile) {
+        __syncthreads();
+        // ---- staging: task = (key group kg of 4 keys, dim quad dq of 4 dims)
+        for (int task = t; task < n_tasks; task += NT) {
+            const int kg = task & 7, dq = task >> 3;
+            const int dim = 4 * dq;
+            uint32_t v01[4], v23[4];  // 4 keys x (2 packed bf16 pairs)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int key = 4 * kg + j, kidx = tb + key;
+                int64_t e = -1;
+                int wtok = -1;
+                if (kidx < n_ent) {
+                    e = P.topk ? (int64_t)P.topk[(int64_t)b * P.k + kidx] : (int64_t)kidx;
+                    if (e >= P.cap) e = -1;  // out-of-range index: treated as padding
+                } else if (kidx < kb1) {
+                    wtok = kidx - n_ent;
+                }
+                uint32_t lo = 0, hi = 0;
+                if (e >= 0) {
+                    const int64_t row = (int64_t)b * P.cap + e;
+                    if (dim < Dn) {
+                        const uint32_t c4 = *(const uint32_t *)(P.nope + row * Dn + dim);
+                        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, false));
+                        hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, true));
+                    } else {
+                        const uint2 r = *(const uint2 *)(P.rope + row * R + (dim - Dn));
+                        lo = r.x;
+                        hi = r.y;
+                    }
+                    if (dq == 0) { ksc[key] = P.kscale[row]; kvalid[key] = 1; }
+                } else if (wtok >= 0) {
+                    const uint2 r = *(const uint2 *)((const uint16_t *)P.win + ((int64_t)b * P.W + wtok) * D + dim);
+                    lo = r.x;
+                    hi = r.y;
+                    if (dq == 0) { ksc[key] = 1.0f; kvalid[key] = 1; }
+                } else if (dq == 0) {
+                    ksc[key] = 0.0f;
+                    kvalid[key] = 0;
+                }
+                v01[j] = lo;
+                v23[j] = hi;
+                *(uint2 *)(Er + key * kErStride + dim) = make_uint2(lo, hi);
+            }
+            // dim-major: row dim+d holds keys 4kg..4kg+3
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                uint32_t a0, a1;
+                const int sh = (d & 1) ? 16 : 0;
+                if (d < 2) {
+                    a0 = ((v01[0] >> sh) & 0xFFFFu) | (((v01[1] >> sh) & 0xFFFFu) << 16);
+                    a1 = ((v01[2] >> sh) & 0xFFFFu) | (((v01[3] >> sh) & 0xFFFFu) << 16);
+                } else {
+                    a0 = ((v23[0] >> sh) & 0xFFFFu) | (((v23[1] >> sh) & 0xFFFFu) << 16);
+                    a1 = ((v23[2] >> sh) & 0xFFFFu) | (((v23[3] >> sh) & 0xFFFFu) << 16);
+                }
+                *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
+            }
+        }
+        __syncthreads();
+        if (!wave_on) continue;
+
+        // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
+        float s2[8];
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+            v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint16_t *arow = Er + (16 * st + col) * kErStride + 8 * grp;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const v8bf a = __builtin_bit_cast(v8bf, *(const uint4 *)(arow + 32 * ks));
+                if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
+                else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int key = 16 * st + 4 * grp + i;
+                s2[4 * st + i] = kvalid[key] ? P.scale2 * fmaf(ksc[key], an[i], ar[i]) : -INFINITY;
+            }
+        }
+        // ---- online softmax (exp2 domain); lane: head h, keys {4grp+i, 16+4grp+i}
+        float mt = s2[0];
+#pragma unroll
+        for (int i = 1; i < 8; i++) mt = fmaxf(mt, s2[i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        if (m_new > m_run) {  // same decision in all four lanes of a head
+            const float alpha = exp2f(m_run - m_new);  // 0 when m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDT; i++) O[i] *= alpha;
+            m_run = m_new;
+        }
+        float pn[8], pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int key = (i < 4) ? (4 * grp + i) : (16 + 4 * grp + i - 4);
+            const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
+            l_run += pi;
+            pr[i] = pi;
+            pn[i] = pi * ksc[key];
+        }
+        v8bf Pn, Pr;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            Pn[i] = __builtin_bit_cast(__bf16, f32_to_bf16(pn[i]));
+            Pr[i] = __builtin_bit_cast(__bf16, f32_to_bf16(pr[i]));
+        }
+        // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+            const uint16_t *er = Ec + (16 * dt + col) * kEcStride;
+            const uint2 x0 = *(const uint2 *)(er + 4 * grp);
+            const uint2 x1 = *(const uint2 *)(er + 16 + 4 * grp);
+            const v8bf a = __builtin_bit_cast(v8bf, make_uint4(x0.x, x0.y, x1.x, x1.y));
+            O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
+        }
+    }
+    if (!wave_on) return;
+    // l over the four lane groups of each head
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (h >= P.H) return;
+    if (splits == 1) {
+        const float f = finish_factor(P, h, m_run, l_run);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) O[dt] *= f;
+        if (P.rope_inv) {
+#pragma unroll
+            for (int dt = Dn / 16; dt < NDT; dt++) {
+                const int j = (16 * dt + 4 * grp - Dn) / 2;
+                const float2 r0 = rope_unrotate((double)Sq.q_pos[b], j, R, P.theta, O[dt][0], O[dt][1]);
+                const float2 r1 = rope_unrotate((double)Sq.q_pos[b], j + 1, R, P.theta, O[dt][2], O[dt][3]);
+                O[dt] = v4f{r0.x, r0.y, r1.x, r1.y};
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+            const float o[4] = {O[dt][0], O[dt][1], O[dt][2], O[dt][3]};
+            store_out<4>(P, b, h, 16 * dt + 4 * grp, o);
+        }
+    } else {
+        float *po = P.part_o + (((int64_t)b * P.S + split) * P.H + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) *(v4f *)(po + 16 * dt + 4 * grp) = O[dt];
+        if (grp == 0) {
+            float *pm = P.part_ml + (((int64_t)b * P.S + split) * P.H + h) * 2;
+            pm[0] = m_run;
+            pm[1] = l_run;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- combine kernel ----
+// One wavefront per (head, sequence): fixed-order merge of the splits, the sink added once.
+template <int NV>
+__global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int n_keys = Sq.n_ent[b] + Sq.win_len[b];
+    int tps, splits;
+    split_plan(n_keys, P.target, &tps, &splits);
+    if (splits == 1) return;
+    const int d0 = lane * NV;
+    if (d0 >= P.D) return;
+    float M = P.sink[h] * kLog2e;
+    for (int s = 0; s < splits; s++)
+        M = fmaxf(M, P.part_ml[(((int64_t)b * P.S + s) * P.H + h) * 2]);
+    float o[NV];
+#pragma unroll
+    for (int v = 0; v < NV; v++) o[v] = 0.0f;
+    float l = 0.0f;
+    for (int s = 0; s < splits; s++) {
+        const float *pm = P.part_ml + (((int64_t)b * P.S + s) * P.H + h) * 2;
+        const float m2 = pm[0];
+        const float c = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - M);
+        l = fmaf(pm[1], c, l);
+        const float *po = P.part_o + (((int64_t)b * P.S + s) * P.H + h) * P.D + d0;
+#pragma unroll
+        for (int v = 0; v < NV; v++) o[v] = fmaf(po[v], c, o[v]);
+    }
+    // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
+    finish_head<NV>(P, Sq, b, h, d0, M, l, o);
+}
+
+// ---------------------------------------------------------------- fp32 kernel -------
+// Any record format, fp32 or BF16 queries/window: one workgroup per (head, sequence),
+// scores in LDS, fp32 arithmetic throughout (no split).
+constexpr int kF32MaxKeys = 8192 + 2048;
+
+__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_t e, int wtok, int d) {
+    const int Dn = P.D - P.R;
+    if (e >= 0) {
+        const int64_t row = (int64_t)b * P.cap + e;
+        if (P.fmt == V4A_KV_F32) return ((const float *)P.nope)[row * P.D + d];
+        if (d < Dn) {
+            const uint8_t c = P.nope[row * Dn + d];
+            const uint32_t c4 = c;
+            const v2bf pr = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, false);
+            return bf16_to_f32(__builtin_bit_cast(uint16_t, pr[0])) * P.kscale[row];
+        }
+        return bf16_to_f32(P.rope[row * P.R + (d - Dn)]);
+    }
+    const int64_t wi = ((int64_t)b * P.W + wtok) * P.D + d;
+    return P.win_bf16 ? bf16_to_f32(((const uint16_t *)P.win)[wi]) : ((const float *)P.win)[wi];
+}
+
+__global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq) {
+    __shared__ float sc[kF32MaxKeys];
+    __shared__ float qs[512];
+    __shared__ float red[256];
+    __shared__ float osh[512];
+    const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int n_ent = Sq.n_ent[b], n_keys = n_ent + Sq.win_len[b];
+    const int D = P.D;
+    for (int d = t; d < D; d += 256) {
+        const int64_t qi = ((int64_t)b * P.H + h) * D + d;
+        qs[d] = P.q_bf16 ? bf16_to_f32(((const uint16_t *)P.q)[qi]) : ((const float *)P.q)[qi];
+    }
+    __syncthreads();
+    const float scale = P.scale2 / kLog2e;
+    float mx = -INFINITY;
+    for (int j = t; j < n_keys; j += 256) {
+        int64_t e = -1;
+        int wtok = -1;
+        if (j < n_ent) {
+            e = P.topk ? (int64_t)P.topk[(int64_t)b * P.k + j] : (int64_t)j;
+            if (e >= P.cap) e = -1;
+        } else {
+            wtok = j - n_ent;
+        }
+        float s = -INFINITY;
+        if (e >= 0 || wtok >= 0) {
+            float acc = 0.0f;
+            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, e, wtok, d), acc);
+            s = scale * acc;
+        }
+        sc[j] = s;
+        mx = fmaxf(mx, s);
+    }
+    red[t] = mx;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (t < o) red[t] = fmaxf(red[t], red[t + o]);
+        __syncthreads();
+    }
+    const float sink = P.sink[h];
+    const float M = fmaxf(red[0], sink);
+    __syncthreads();
+    float part = 0.0f;
+    for (int j = t; j < n_keys; j += 256) {
+        const float pj = sc[j] == -INFINITY ? 0.0f : expf(sc[j] - M);
+        sc[j] = pj;
+        part += pj;
+    }
+    red[t] = part;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (t < o) red[t] += red[t + o];
+        __syncthreads();
+    }
+    const float den = (M == -INFINITY) ? 0.0f : red[0] + expf(sink - M);
+    for (int d = t; d < D; d += 256) {
+        float acc = 0.0f;
+        for (int j = 0; j < n_keys; j++) {
+            if (sc[j] == 0.0f) continue;
+            int64_t e = -1;
+            int wtok = -1;
+            if (j < n_ent) {
+                e = P.topk ? (int64_t)P.topk[(int64_t)b * P.k + j] : (int64_t)j;
+                if (e >= P.cap) e = -1;
+            } else {
+                wtok = j - n_ent;
+            }
+            if (e < 0 && wtok < 0) continue;
+            acc = fmaf(sc[j], load_key_dim(P, b, e, wtok, d), acc);
+        }
+        osh[d] = den > 0.0f ? acc / den : 0.0f;
+    }
+    __syncthreads();
+    const int Dn = D - P.R;
+    for (int d = 2 * t; d < D; d += 512) {
+        float o[2] = {osh[d], osh[d + 1]};
+        if (P.rope_inv && d >= Dn) {
+            float c, s;
+            rope_cs((double)Sq.q_pos[b], (d - Dn) / 2, P.R, P.theta, &c, &s);
+            const float x = o[0], y = o[1];
+            o[0] = x * c + y * s;
+            o[1] = -x * s + y * c;
+        }
+        const int64_t base = ((int64_t)b * P.H + h) * D + d;
+        if (P.out_bf16) {
+            ((uint16_t *)P.out)[base] = f32_to_bf16(o[0]);
+            ((uint16_t *)P.out)[base + 1] = f32_to_bf16(o[1]);
+        } else {
+            ((float *)P.out)[base] = o[0];
+            ((float *)P.out)[base + 1] = o[1];
+        }
+    }
+}
+
+bool attn_uses_mfma(const AttnArgs &a) {
+    return a.kv->fmt == V4A_KV_FP8_BF16 && a.q_bf16 && a.win_bf16 && (a.H % 16) == 0 && a.H <= 128 &&
+           ((a.D == 512 && a.R == 64) || (a.D == 128 && a.R == 32));
+}
+
+void split_plan_host(int n_keys, int target, int *tps, int *splits) {
+    split_plan(n_keys, target, tps, splits);
+}
+
+hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s) {
+    AttnParams P{};
+    P.q = a.q;
+    P.q_bf16 = a.q_bf16;
+    P.B = a.B;
+    P.H = a.H;
+    P.D = a.D;
+    P.R = a.R;
+    P.fmt = a.kv->fmt;
+    P.nope = (const uint8_t *)a.kv->nope;
+    P.rope = (const uint16_t *)a.kv->rope;
+    P.kscale = a.kv->scale;
+    P.cap = a.kv->cap;
+    P.topk = a.topk;
+    P.k = a.k;
+    P.win = a.win;
+    P.win_bf16 = a.win_bf16;
+    P.W = a.W;
+    P.sink = a.sink;
+    P.scale2 = a.scale * kLog2e;
+    P.rope_inv = a.rope_inv;
+    P.theta = a.theta;
+    P.out = a.out;
+    P.out_bf16 = a.out_bf16;
+    P.part_o = a.partial;
+    P.target = a.target_splits;
+    P.S = a.split_cap;
+    P.part_ml = a.partial ? a.partial + (size_t)a.B * P.S * a.H * a.D : nullptr;
+    if (a.B == 0) return hipSuccess;
+    if (!attn_uses_mfma(a)) {
+        hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);
+        return hipGetLastError();
+    }
+    P.n_hg = (a.H + 63) / 64;
+    const int waves = (a.H >= 64) ? 4 : a.H / 16;
+    int pairs = a.B * P.S;
+    int blocks = pairs;
+    if (P.n_hg == 2) blocks = ((pairs + 7) / 8) * 16;
+    if (a.D == 512)
+        hipLaunchKernelGGL((attn_mfma_kernel<512, 64>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+    else
+        hipLaunchKernelGGL((attn_mfma_kernel<128, 32>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || P.S <= 1) return e;
+    if (a.D == 512)
+        hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(a.H, a.B), dim3(64), 0, s, P, sq);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<2>, dim3(a.H, a.B), dim3(64), 0, s, P, sq);
+    return hipGetLastError();
+}
+
+}  // namespace v4a

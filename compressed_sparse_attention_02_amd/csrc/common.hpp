@@ -1,0 +1,201 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the CSA/HCA hot path:
+// number-format encoders written from the OCP FP8/MX format definitions, bf16 packing,
+// wavefront reductions, and the host-side launch interface of each kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/v4attn.h"
+
+namespace v4a {
+
+constexpr int kWave = 64;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// bf16 <-> f32.  Encoding rounds to nearest even on bit 16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    uint32_t u = fbits(x);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bitsf((uint32_t)b << 16); }
+
+// OCP FP8 E4M3FN encoding of a finite fp32 value: nearest, ties to even, saturating to
+// +-448; the sign bit is kept (a negative value rounding to zero gives 0x80).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t s = (fbits(v) >> 24) & 0x80u;
+    float a = fabsf(v);
+    if (!(a < 448.0f)) return s | 0x7Eu;
+    if (a < 0.015625f) {                        // below 2^-6: grid step 2^-9
+        float n = __builtin_rintf(a * 512.0f);  // exact scaling, then nearest-even; n <= 8
+        return s | (uint32_t)n;                 // n == 8 is the code of 2^-6
+    }
+    uint32_t ua = fbits(a);
+    int e = (int)(ua >> 23) - 127;              // a in [2^e, 2^(e+1)), e in [-6, 8]
+    uint32_t mant = ua & 0x7FFFFFu;
+    uint32_t keep = mant >> 20, rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep++;
+    if (keep == 8u) { keep = 0; e++; }
+    return s | ((uint32_t)(e + 7) << 3) | keep;
+}
+
+// E2M1 (FP4) encoding of a value already divided by its block scale: nearest with ties
+// to the even code, saturating at 6; bit 3 is the sign.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    uint32_t s = (fbits(v) >> 28) & 0x8u;
+    float a = fabsf(v);
+    uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+               : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+    return s | c;
+}
+
+// floor(log2(a)) - 2 for a > 0, clamped to [-127, 127]: the MXFP4 block exponent.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    uint32_t u = fbits(amax);
+    int e = (int)(u >> 23);
+    int fl = e ? e - 127 : -127 - (__builtin_clz(u & 0x7FFFFFu) - 9);  // subnormal: below 2^-126
+    int X = fl - 2;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// Wavefront reductions over all 64 lanes (result in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Orderable key of an fp32 score: larger score -> larger unsigned key (-0 canonical +0).
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = fbits(s);
+    if (u == 0x80000000u) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// RoPE cos/sin of one pair: angle p * theta^(-2j/R) in double, cos and sin in double,
+// rounded to fp32.
+__device__ __forceinline__ void rope_cs(double p, int j, int R, double theta, float *c, float *s) {
+    double inv_freq = pow(theta, -2.0 * (double)j / (double)R);
+    double ang = p * inv_freq;
+    *c = (float)cos(ang);
+    *s = (float)sin(ang);
+}
+
+}  // namespace v4a
+
+// ---------------------------------------------------------------- host side ----------
+namespace v4a {
+
+// Per-sequence / per-query positions travel as kernel arguments (no host-to-device copy,
+// so every call stays asynchronous and capturable).
+constexpr int kMaxSeq = 128;
+
+struct QueryPos {
+    int mode;  // 0: pos[qi] per query (B*Q <= kMaxSeq); 1: pos[b] + j for query j of sequence b
+    int Q, m;
+    int64_t pos[kMaxSeq];
+    int64_t n_ent[kMaxSeq];
+};
+
+__host__ __device__ __forceinline__ int64_t visible_keys(const QueryPos &P, int qi) {
+    int b = qi / P.Q, j = qi % P.Q;
+    int64_t pos = P.mode == 0 ? P.pos[qi] : P.pos[b] + j;
+    int64_t v = (pos + 1) / P.m;
+    int64_t n = P.n_ent[b];
+    v = v < n ? v : n;
+    return v < 0 ? 0 : v;
+}
+
+struct SeqInfo {
+    int32_t n_ent[kMaxSeq];    // entry keys of sequence b (k for CSA, visible entries for HCA)
+    int32_t win_len[kMaxSeq];
+    int64_t q_pos[kMaxSeq];
+};
+
+void set_error(const char *fmt, ...);
+
+hipError_t launch_quantize_kv(const float *x, int64_t rows, const v4a_kv &out, int64_t row0,
+                              hipStream_t s);
+hipError_t launch_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx &out, int64_t row0,
+                                 hipStream_t s);
+
+struct CompressArgs {
+    const void *x[2];        // stream A (or the HCA stream) and stream B (CSA only)
+    const float *gate[2];
+    const float *bias[2];
+    int n_streams;           // 2 for CSA (overlapped), 1 for HCA
+    bool bf16_in;
+    int D, G, m;
+    int64_t tok0, n_tok, first_entry, n_entries;
+    bool rope;
+    int R;
+    double theta;
+    const v4a_kv *kv;        // exactly one of kv / idx
+    const v4a_idx *idx;
+    int b0, n_seq;           // output slots b0 .. b0+n_seq-1; stream s at x + s * n_tok * D
+};
+hipError_t launch_compress(const CompressArgs &a, hipStream_t s);
+
+struct IndexerArgs {
+    const v4a_idx *keys;
+    const v4a_idx *q;
+    const float *w;
+    int B, Q, H_I;
+    int64_t n_max;            // max visible keys over the queries (grid size)
+    uint32_t *score_keys;     // [B*Q][n_max] orderable keys (or NULL)
+    float *scores;            // [B*Q][n_max] raw scores (or NULL)
+    uint32_t *hist;           // [B*Q][4096] histogram of the top 12 key bits (or NULL)
+};
+hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+struct SelectArgs {
+    const uint32_t *score_keys;   // [BQ][n_max]
+    const uint32_t *hist;         // [BQ][4096]
+    int64_t n_max;
+    int BQ, k;
+    uint32_t *cand;               // [BQ][cand_cap][2]: (score key, index)
+    int64_t cand_cap;
+    int32_t *sel;                 // [BQ][k] keys above the threshold bin
+    uint32_t *counters;           // [BQ][4]: selected, candidates, finished workgroups
+    int32_t *out;                 // [BQ][k]
+};
+hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s);
+
+struct AttnArgs {
+    const void *q;
+    bool q_bf16;
+    int B, H, D, R;
+    const v4a_kv *kv;
+    const int32_t *topk;      // [B][k] or NULL (dense)
+    int k;
+    const void *win;
+    bool win_bf16;
+    int W;
+    const float *sink;
+    float scale;
+    bool rope_inv;
+    double theta;
+    void *out;
+    bool out_bf16;
+    float *partial;           // workspace for split partials (or NULL when split_cap == 1)
+    int target_splits;        // splits aimed at per sequence
+    int split_cap;            // max splits of any sequence (partial stride)
+};
+bool attn_uses_mfma(const AttnArgs &a);
+hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s);
+void split_plan_host(int n_keys, int target, int *tps, int *splits);
+constexpr int kAttnTile = 32;
+
+}  // namespace v4a

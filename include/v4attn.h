@@ -1,0 +1,233 @@
+/*
+ * v4attn.h -- C ABI of the MI355X (gfx950) hot path of DeepSeek-V4 hybrid attention
+ * (CSA + HCA) for one layer: KV compressors, lightning indexer with top-k, and
+ * shared-KV multi-query attention with a sliding window and an attention sink.
+ *
+ * The operations follow these pages (cited by site, title and section):
+ *   [cyqw]     "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.2 "Hybrid
+ *              attention CSA+HCA", section 3.4 "FP4 QAT", section 3.5 "KV cache layering".
+ *   [firecat]  "DeepSeek V4 technical report explained" (firecat-web.com), "Core
+ *              architecture upgrades", item 2 "Hybrid attention", and the model table.
+ *   [chooseai] "DeepSeek V4 preview and technical report" (chooseai.net/news/3476),
+ *              section 1 "CSA + HCA hybrid attention".
+ *   [mewclaw]  "DeepSeek-V4: the engineering answer to million-token context"
+ *              (tutorial.mewclaw.fun), "Hybrid Attention", "Partial RoPE", "Attention sink".
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are device memory owned by the caller; pointers marked
+ *     (host) are host memory read before the call returns.  The library allocates no
+ *     device memory: scratch space is the caller's workspace `ws` of `ws_bytes` bytes,
+ *     sized by the matching *_workspace() function, 256-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *     Buffers must stay alive until the stream has executed the call.
+ *   - Every call validates its arguments on the host before launching anything.  On a
+ *     status other than V4A_OK nothing was launched and no output was written;
+ *     v4a_last_error() returns a message for the calling thread.  No C++ exception
+ *     crosses this boundary.  The library keeps no state between calls and may be used
+ *     from several threads and streams at once (calls sharing a workspace must not
+ *     overlap).
+ *   - Results are deterministic and batch invariant: the work split of a sequence depends
+ *     only on its own lengths and the shape constants, never on the batch size or on
+ *     device occupancy, and no floating-point reduction uses atomics.
+ *
+ * Positions: tokens of a sequence sit at positions 0..T-1.  A decode query is the token
+ * at q_pos = T-1.  Compressed entry i of ratio m covers the block of tokens
+ * [m*i, m*i + m - 1] and is visible to a query at position t iff m*(i+1) - 1 <= t.
+ */
+#ifndef V4ATTN_H
+#define V4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define V4A_API __attribute__((visibility("default")))
+#else
+#define V4A_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    V4A_OK = 0,
+    V4A_EINVAL = 1,        /* a pointer, size or position is invalid */
+    V4A_EUNSUPPORTED = 2,  /* a shape or format this build does not implement */
+    V4A_EWORKSPACE = 3,    /* workspace missing, too small or misaligned */
+    V4A_EHIP = 4           /* the HIP runtime reported an error at launch */
+} v4a_status;
+
+/* Element type of raw KV streams, queries, window tokens and outputs. */
+typedef enum { V4A_F32 = 0, V4A_BF16 = 1 } v4a_float;
+
+/* Compressed-entry record formats.
+ * V4A_KV_FP8_BF16 ([chooseai] section 1, [mewclaw] "Low-precision path": RoPE dims in
+ * BF16, the other dims in FP8): per entry, the first D-R dims as OCP FP8 E4M3FN codes
+ * with one fp32 scale per entry (value = code * scale; scale = amax/448 over those dims,
+ * 1 when they are all zero), the last R dims as BF16.
+ * V4A_KV_F32: all D dims in fp32. */
+typedef enum { V4A_KV_F32 = 0, V4A_KV_FP8_BF16 = 1 } v4a_kv_fmt;
+
+/* Indexer key/query formats.  V4A_IDX_MXFP4 ([cyqw] section 3.4: the indexer QK path in
+ * FP4): OCP MXFP4, blocks of 32 E2M1 elements sharing an E8M0 scale byte (2^(byte-127)),
+ * element 2j in the low nibble of byte j.  V4A_IDX_F32: plain fp32 vectors. */
+typedef enum { V4A_IDX_F32 = 0, V4A_IDX_MXFP4 = 1 } v4a_idx_fmt;
+
+/* A batch of entry records: slot b holds entries [0, cap) of sequence b.
+ *   FP8_BF16: nope  u8   [B][cap][D-R]  (device)
+ *             rope  bf16 [B][cap][R]    (device, raw 16-bit words)
+ *             scale f32  [B][cap]       (device)
+ *   F32:      nope  f32  [B][cap][D]    (device); rope and scale unused (NULL). */
+typedef struct {
+    v4a_kv_fmt fmt;
+    int32_t D, R;
+    void *nope;
+    void *rope;
+    float *scale;
+    int64_t cap;
+} v4a_kv;
+
+/* A batch of indexer vectors (keys, or query heads): slot b holds rows [0, cap).
+ *   MXFP4: codes u8 [B][cap][d/2], scales u8 [B][cap][d/32]  (device)
+ *   F32:   codes f32 [B][cap][d] (device); scales unused (NULL). */
+typedef struct {
+    v4a_idx_fmt fmt;
+    int32_t d;
+    void *codes;
+    uint8_t *scales;
+    int64_t cap;
+} v4a_idx;
+
+/* ---------------------------------------------------------------- a3: quantisers ----
+ * Quantise fp32 rows x [rows][D] (device) into records row0 .. row0+rows-1 of `out`,
+ * counting rows across slots (row r lives in slot r / cap).  Encoding: round to nearest
+ * even everywhere; FP8 codes are the E4M3 encoding (saturating at +-448) of the fp32
+ * product x * (448/amax); BF16 is the nearest-even rounding of x.  Requires D-R a multiple
+ * of 8, D <= 512, R even, rows >= 0.  [chooseai] section 1. */
+V4A_API v4a_status v4a_quantize_kv(const float *x, int64_t rows, const v4a_kv *out, int64_t row0,
+                           void *stream);
+
+/* MXFP4 quantisation of fp32 rows x [rows][d] (device) into rows row0.. of `out`:
+ * per 32-element block, X = floor(log2(amax)) - 2 clamped to [-127, 127] (amax = 0 gives
+ * X = -127 and zero codes), codes = E2M1 nearest-even of x * 2^-X, saturating at 6.
+ * Requires d a multiple of 32, d <= 512.  [cyqw] section 3.4. */
+V4A_API v4a_status v4a_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx *out, int64_t row0,
+                              void *stream);
+
+/* ------------------------------------------------------------ a1/a2: compressors ----
+ * CSA compressor ([cyqw] section 2.2: every m tokens become one entry; two independent KV
+ * sequences merged with softmax-normalised gate weights; adjacent compressed blocks share
+ * indices. [chooseai] section 1: softmax with positional bias).
+ * Entry i merges A-block i (tokens m*i .. m*i+m-1 of stream A, logits gate_a[t] +
+ * bias_a[j]) with B-block i-1 (tokens m*(i-1)+j of stream B, logits gate_b[t] +
+ * bias_b[j]); entry 0 merges its A-block alone.  Per gate channel (G == 1: one gate for
+ * all dims; G == D: one per dim) the weights are the softmax over the candidates; the
+ * entry is the weighted sum of the candidate rows.  Then, if apply_rope, the last R dims
+ * are rotated (interleaved pairs, inv_freq_j = theta^(-2j/R)) at position m*i, and the
+ * entry is written in the output's format.
+ *   kv_a, kv_b  [n_seq][n_tok][D] (device, f32 or bf16 per in_t); row r of sequence s is
+ *               its token tok0 + r (all n_seq sequences share tok0 and the entry range)
+ *   gate_a, gate_b [n_seq][n_tok][G] f32 (device); bias_a, bias_b [m][G] f32 (device)
+ *   Writes entries first_entry .. first_entry+n_entries-1 of slots b0 .. b0+n_seq-1 (which
+ *   must exist in the output) of exactly one of
+ *   out_kv (records; D == out_kv->D, R == out_kv->R) or out_idx (indexer keys;
+ *   D == out_idx->d, no RoPE).  The rows must cover every block these entries read:
+ *   tok0 <= m*(first_entry-1) (or tok0 <= 0 when first_entry == 0) and
+ *   m*(first_entry+n_entries) <= tok0 + n_tok; tok0 must be a multiple of m.
+ *   norm_w must be NULL (Q/KV RMSNorm is not part of this build).
+ *   Supports m in [1, 128], G in {1, D}, D in {32, 128, 512}. */
+V4A_API v4a_status v4a_compress_csa(const void *kv_a, const void *kv_b, v4a_float in_t, int32_t D,
+                            const float *gate_a, const float *gate_b, int32_t G,
+                            const float *bias_a, const float *bias_b, int64_t tok0,
+                            int64_t n_tok, int32_t m, int64_t first_entry, int64_t n_entries,
+                            int32_t apply_rope, float rope_theta, const float *norm_w,
+                            const v4a_kv *out_kv, const v4a_idx *out_idx, int32_t b0,
+                            int32_t n_seq, void *stream);
+
+/* HCA compressor ([cyqw] section 2.2, [firecat] item 2: every m' = 128 tokens become one
+ * entry, no overlap, no sparse selection).  Entry i merges tokens m*i .. m*i+m-1 of kv
+ * with logits gate[t] + bias[j]; RoPE at m*i and output as for the CSA compressor.
+ * kv [n_seq][n_tok][D], gate [n_seq][n_tok][G]; writes slots b0 .. b0+n_seq-1.
+ * Requires tok0 <= m*first_entry, m*(first_entry+n_entries) <= tok0 + n_tok. */
+V4A_API v4a_status v4a_compress_hca(const void *kv, v4a_float in_t, int32_t D, const float *gate,
+                            int32_t G, const float *bias, int64_t tok0, int64_t n_tok,
+                            int32_t m, int64_t first_entry, int64_t n_entries,
+                            int32_t apply_rope, float rope_theta, const float *norm_w,
+                            const v4a_kv *out_kv, int32_t b0, int32_t n_seq, void *stream);
+
+/* ------------------------------------------------ a4/a5: lightning indexer + top-k ----
+ * [cyqw] section 2.2 (a low-rank, low-precision multi-head indexer scores compressed
+ * entries; each query keeps its top-k entries; k = 1024 for Pro) and section 3.4 (QK in
+ * FP4); [chooseai] section 1 (k = 512 for Flash).
+ * For query j of sequence b (position q_pos[b*Q+j]) and each visible key i < n_vis with
+ * n_vis = min(n_entries[b], (q_pos+1)/m):
+ *   s_h   = q_h . key_i per head h (MXFP4: the exact dot rounded once to fp32; F32: an
+ *           fp32 fma chain over ascending dims),
+ *   score = sum_h w_h * ReLU(s_h), evaluated as four fp32 fma chains (chain (h>>2)&3,
+ *           ascending h), combined as ((c0+c1)+c2)+c3, with -0 turned into +0.
+ * The selection is the k_eff = min(k, n_vis) best keys under (score descending, index
+ * ascending), written to out_idx[b][j][0..k) in ascending index order, padded with -1.
+ *   keys   [B][cap][..] (device; keys->fmt == q_idx->fmt, keys->d == q_idx->d)
+ *   q_idx  rows [B*Q*H_I] (device; slot stride cap >= Q*H_I, i.e. one slot per sequence)
+ *   w      [B][Q][H_I] f32 (device); n_entries [B], q_pos [B*Q] (host)
+ *   out_idx [B][Q][k] int32 (device)
+ * Supports H_I a multiple of 4 up to 64, d in {32, 128} (MXFP4: d == 128), k <= 2048,
+ * Q*H_I <= q_idx->cap. */
+V4A_API v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32_t m,
+                            const v4a_idx *q_idx, const float *w, int32_t B, int32_t Q,
+                            int32_t H_I, const int64_t *q_pos, int32_t k, int32_t *out_idx,
+                            void *ws, size_t ws_bytes, void *stream);
+V4A_API size_t v4a_indexer_topk_workspace(int32_t B, int32_t Q, int64_t n_max, int32_t k);
+
+/* The scores alone (same definition as above), for inspection: out_scores [B][Q][n_max]
+ * f32 (device), -inf at positions that are not visible. */
+V4A_API v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int32_t m,
+                              const v4a_idx *q_idx, const float *w, int32_t B, int32_t Q,
+                              int32_t H_I, const int64_t *q_pos, int64_t n_max,
+                              float *out_scores, void *stream);
+
+/* ---------------------------------------- a6/a7: shared-KV MQA with window and sink ----
+ * [firecat] item 2 (multi-query attention over the selected compressed entries, head dim
+ * 512, partial RoPE on the last 64 dims, a 128-token sliding window, a learnable sink
+ * logit so the attention mass may be below one); [cyqw] section 2.2 (the window branch
+ * joins the core attention; the sink adds a learnable term to the softmax denominator);
+ * [mewclaw] "Partial RoPE" (the output is treated so values carry no absolute position).
+ * For sequence b and head h, with keys = the selected (CSA) or all visible (HCA) entries
+ * followed by the win_len[b] window tokens, each key also its own value (all D dims):
+ *   z_j = softmax_scale * q_h . key_j,   M = max(sink_h, max_j z_j),
+ *   out_h = sum_j exp(z_j - M) key_j / (exp(sink_h - M) + sum_j exp(z_j - M)),
+ * then, if out_rope_inverse, the last R dims of out_h are rotated by -q_pos[b] (interleaved
+ * pairs, inv_freq_j = theta^(-2j/R)).  Queries and window tokens arrive already rotated.
+ *   q    [B][H][D] (device, q_t);  sink [H] f32 (device)
+ *   win  [B][W][D] (device, win_t): the last win_len[b] <= W tokens, oldest first
+ *   win_len [B], q_pos [B] (host)
+ *   out  [B][H][D] (device, out_t)
+ * decode_csa: topk_idx [B][k] int32 (device), ascending entry indices, -1 padding (the
+ *   output of v4a_indexer_topk with Q = 1); every index must be < kv->cap.
+ * decode_hca: n_entries [B] (host): entries min(n_entries[b], (q_pos+1)/m) are attended.
+ * Supports D in {128, 512}, R even and < D, H a multiple of 16 up to 128 for
+ * V4A_KV_FP8_BF16 (BF16 MFMA) and H <= 128 for V4A_KV_F32, W <= 128, k <= 2048. */
+V4A_API v4a_status v4a_decode_csa(const void *q, v4a_float q_t, int32_t B, int32_t H, const v4a_kv *kv,
+                          const int32_t *topk_idx, int32_t k, const void *win, v4a_float win_t,
+                          const int32_t *win_len, int32_t W, const float *sink,
+                          const int64_t *q_pos, float softmax_scale, int32_t out_rope_inverse,
+                          float rope_theta, void *out, v4a_float out_t, void *ws,
+                          size_t ws_bytes, void *stream);
+V4A_API v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32_t H, const v4a_kv *kv,
+                          const int64_t *n_entries, int32_t m, const void *win,
+                          v4a_float win_t, const int32_t *win_len, int32_t W, const float *sink,
+                          const int64_t *q_pos, float softmax_scale, int32_t out_rope_inverse,
+                          float rope_theta, void *out, v4a_float out_t, void *ws,
+                          size_t ws_bytes, void *stream);
+/* Workspace for either decode call: n_keys_max = k (CSA) or max entries (HCA), plus W. */
+V4A_API size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_keys_max, int32_t W);
+
+/* ---------------------------------------------------------------------- utilities ---- */
+V4A_API const char *v4a_last_error(void);
+V4A_API const char *v4a_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* V4ATTN_H */

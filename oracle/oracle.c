@@ -388,6 +388,12 @@ static float head_combine(const float *s, const float *w, int H) {
  * integer times a power of two) and converted once to fp32 (nearest even).
  * *inexact is incremented when the exact value needs more than 24
  * significant bits, i.e. is not an fp32 number. */
+/* Twice the E2M1 value of each 4-bit code: an integer (E2M1 values are multiples of 1/2). */
+static int twice_e2m1[16];
+static void init_twice_e2m1(void) {
+    for (int c = 0; c < 16; c++) twice_e2m1[c] = (int)lround(2.0 * orc_e2m1_decode((uint8_t)c));
+}
+
 static float mxfp4_dot(const uint8_t *qc, const uint8_t *qs, const uint8_t *kc, const uint8_t *ks,
                        int d, int64_t *inexact) {
     int nb = d / 32;
@@ -401,9 +407,7 @@ static float mxfp4_dot(const uint8_t *qc, const uint8_t *qs, const uint8_t *kc, 
             uint8_t qb = qc[e / 2], kb = kc[e / 2];
             uint8_t qn = (e & 1) ? (qb >> 4) : (qb & 15);
             uint8_t kn = (e & 1) ? (kb >> 4) : (kb & 15);
-            int64_t q2 = (int64_t)llround(2.0 * orc_e2m1_decode(qn));
-            int64_t k2 = (int64_t)llround(2.0 * orc_e2m1_decode(kn));
-            acc += q2 * k2;
+            acc += (int64_t)twice_e2m1[qn] * (int64_t)twice_e2m1[kn];
         }
         P[b] = acc;
         E[b] = ((int)qs[b] - 127) + ((int)ks[b] - 127) - 2;
@@ -450,6 +454,7 @@ ORC_API void orc_indexer_scores_mxfp4(const uint8_t *q_codes, const uint8_t *q_s
                                       int H, int d, const uint8_t *k_codes, const uint8_t *k_scales,
                                       int64_t n_keys, float *scores, int64_t *inexact) {
     int64_t bad = 0;
+    init_twice_e2m1();
 #pragma omp parallel for schedule(static) reduction(+ : bad)
     for (int64_t i = 0; i < n_keys; i++) {
         float s[256];

@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU parity tests: moving seeded inputs to the device, reading HIP
+outputs back, and the tolerance checks the parity bar uses."""
+import sys
+
+import numpy as np
+import torch
+
+import compressed_sparse_attention_02_amd as v4
+
+DEV = "cuda"
+
+# Attention parity bar for BF16/FP8 inputs: max-abs and relative L2 over the whole output.
+MAX_ABS_BF16 = 1e-2
+REL_L2_BF16 = 5e-3
+# fp32 workload bar.
+MAX_ABS_F32 = 1e-5
+
+
+def announce(msg: str):
+    """Print (and flush) what the next GPU step is, so a failing run names its case."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def bf16_from_bits(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """The oracle's final cast to BF16 (nearest even), back as float64."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 numbers at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, max_abs: float, rel_l2: float | None = None, what="",
+                ulps: float = 0.0):
+    """max |got - ref| <= max_abs (+ `ulps` BF16 spacings of |ref| where a case states it) and
+    ||got - ref|| / ||ref|| <= rel_l2 over the whole tensor."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bar = max_abs + ulps * bf16_ulp(ref)
+    ma = float(err.max()) if err.size else 0.0
+    rl = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if err.size else 0.0
+    worst = np.unravel_index(int(np.argmax(err - bar)), err.shape) if err.size else ()
+    msg = f"{what}: max-abs {ma:.3e} (bar {max_abs:.1e}" + (f" + {ulps} bf16 ulp" if ulps else "") + \
+          f"), rel-L2 {rl:.3e}" + (f" (bar {rel_l2:.1e})" if rel_l2 is not None else "")
+    if err.size:
+        msg += f"; worst at {tuple(int(i) for i in worst)}: got {got[worst]:.6g} ref {ref[worst]:.6g}"
+    if got.ndim == 3:
+        per = [f"{float(np.abs(got[b] - ref[b]).max()):.2e}" for b in range(got.shape[0])]
+        msg += f"; per-sequence max-abs {per}"
+    print(msg, flush=True)
+    assert (err <= bar).all(), msg
+    if rel_l2 is not None:
+        assert rl <= rel_l2, msg
+    return ma, rl
+
+
+def kv_from_f32(x: np.ndarray, R: int, fmt=v4.V4A_KV_FP8_BF16) -> v4.KV:
+    """Device entry records of fp32 rows x [B][N][D], quantised by the HIP quantiser."""
+    B, N, D = x.shape
+    kv = v4.KV.empty(B, N, D, R, fmt)
+    v4.v4a_quantize_kv(f32(x.reshape(-1, D)), kv, 0)
+    return kv
+
+
+def idx_from_f32(x: np.ndarray, fmt=v4.V4A_IDX_MXFP4) -> v4.Idx:
+    B, N, d = x.shape
+    ix = v4.Idx.empty(B, N, d, fmt)
+    if fmt == v4.V4A_IDX_MXFP4:
+        v4.v4a_quantize_mxfp4(f32(x.reshape(-1, d)), ix, 0)
+    else:
+        ix.codes.copy_(f32(x))
+    return ix

@@ -1,0 +1,131 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point include/v4attn.h
+declares, sizes workspaces, and rejects bad arguments on the host before any launch (these
+calls never reach the GPU, so they run without one)."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import compressed_sparse_attention_02_amd as v4
+
+FAKE = 0x10000  # an aligned address that host validation never dereferences
+
+
+def declared_symbols():
+    text = open(v4.HEADER).read()
+    return sorted(set(re.findall(r"^V4A_API\s+[\w\s\*]*?\b(v4a_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = v4.lib()
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert v4.v4a_version().startswith("v4attn")
+
+
+def kv(fmt=v4.V4A_KV_FP8_BF16, D=512, R=64, cap=100, nope=FAKE, rope=FAKE, scale=FAKE):
+    return v4.c_kv(fmt, D, R, nope, rope, scale, cap)
+
+
+def idx(fmt=v4.V4A_IDX_MXFP4, d=128, cap=100, codes=FAKE, scales=FAKE):
+    return v4.c_idx(fmt, d, codes, scales, cap)
+
+
+def i64(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def i32(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def status(name, *args):
+    return getattr(v4.lib(), name)(*args)
+
+
+def test_workspace_sizes_are_monotone_and_aligned():
+    a = v4.v4a_indexer_topk_workspace(4, 1, 262144, 1024)
+    b = v4.v4a_indexer_topk_workspace(4, 1, 262145, 1024)
+    assert a > 4 * 262144 * 12 and b >= a and a % 256 == 0
+    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) >= 16 * 16 * 128 * 512 * 4
+    assert v4.v4a_decode_workspace(1, 8, 128, 0, 0) == 0   # a single split needs no partials
+
+
+def test_quantize_rejects():
+    L = v4.lib()
+    assert L.v4a_quantize_kv(FAKE, 10, None, 0, None) == 1
+    assert L.v4a_quantize_kv(FAKE, -1, ctypes.byref(kv()), 0, None) == 1
+    assert L.v4a_quantize_kv(FAKE, 10, ctypes.byref(kv(D=500, R=64)), 0, None) == 2
+    assert L.v4a_quantize_kv(FAKE + 4, 10, ctypes.byref(kv()), 0, None) == 1   # misaligned x
+    assert L.v4a_quantize_mxfp4(FAKE, 10, ctypes.byref(idx(d=100)), 0, None) == 2
+    assert L.v4a_quantize_mxfp4(FAKE, 10, ctypes.byref(idx(scales=0)), 0, None) == 1
+    assert "scales" in v4.lib().v4a_last_error().decode()
+
+
+def test_compress_rejects():
+    L = v4.lib()
+    out = kv(D=512, R=64, cap=1000)
+    args = dict(kv_a=FAKE, kv_b=FAKE, in_t=1, D=512, ga=FAKE, gb=FAKE, G=1, ba=FAKE, bb=FAKE,
+                tok0=0, n_tok=4096, m=4, first=0, n=1024, rope=1)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.v4a_compress_csa(a["kv_a"], a["kv_b"], a["in_t"], a["D"], a["ga"], a["gb"], a["G"],
+                                  a["ba"], a["bb"], a["tok0"], a["n_tok"], a["m"], a["first"], a["n"],
+                                  a["rope"], 10000.0, a.get("norm", None),
+                                  ctypes.byref(a.get("out", out)), a.get("oidx", None), 0, 1, None)
+    assert call(m=0) == 2
+    assert call(m=129) == 2
+    assert call(G=7) == 2
+    assert call(tok0=2) == 1                      # not a multiple of m
+    assert call(n_tok=4095) == 1                  # last block uncovered
+    assert call(first=10, tok0=40) == 1           # B-block of entry 10 starts at 36
+    assert call(norm=FAKE) == 2                   # RMSNorm not built
+    assert call(out=kv(D=512, R=64, cap=1000), n=1001) == 1
+    assert call(oidx=ctypes.byref(idx())) == 1     # both outputs given
+    assert call(kv_a=0) == 1
+
+
+def test_indexer_rejects():
+    L = v4.lib()
+    keys, q = idx(cap=1000), idx(cap=64)
+    n, pos, out = i64(1000), i64(3999), FAKE
+
+    def call(keys=keys, q=q, H_I=64, k=512, B=1, Q=1, m=4, ws=FAKE, wsb=1 << 30, n=n, pos=pos):
+        return L.v4a_indexer_topk(ctypes.byref(keys), n, m, ctypes.byref(q), FAKE, B, Q, H_I, pos, k,
+                                  out, ws, wsb, None)
+    assert call(H_I=6) == 2
+    assert call(H_I=68) == 2
+    assert call(k=0) == 2 and call(k=4096) == 2
+    assert call(q=idx(cap=32)) == 1                  # Q*H_I rows do not fit
+    assert call(keys=idx(d=64, cap=1000)) == 1       # d differs from q
+    assert call(keys=idx(d=64, cap=1000), q=idx(d=64, cap=64)) == 2   # MXFP4 needs d = 128
+    assert call(n=i64(2000)) == 1                    # more entries than capacity
+    assert call(pos=i64(-1)) == 1
+    assert call(wsb=100) == 3
+    assert call(ws=FAKE + 8) == 3
+    assert call(B=200) == 2
+
+
+def test_decode_rejects():
+    L = v4.lib()
+    rec = kv(cap=1000)
+    win_len, pos = i32(128), i64(4095)
+    sink = FAKE
+
+    def call(H=128, W=128, k=1024, wl=win_len, rec=rec, ws=FAKE, wsb=1 << 30, q=FAKE):
+        return L.v4a_decode_csa(q, 1, 1, H, ctypes.byref(rec), FAKE, k, FAKE, 1, wl, W, sink, pos,
+                                0.04, 1, 10000.0, FAKE, 1, ws, wsb, None)
+    assert call(H=0) == 2 and call(H=256) == 2
+    assert call(W=129) == 2
+    assert call(wl=i32(129)) == 1
+    assert call(k=0) == 2
+    assert call(wsb=16) == 3
+    assert call(q=FAKE + 2) == 1
+    assert call(rec=kv(D=512, R=64, cap=0)) == 1
+    assert L.v4a_decode_hca(FAKE, 1, 1, 128, ctypes.byref(rec), i64(2000), 128, FAKE, 1, win_len, 128,
+                            sink, pos, 0.04, 1, 10000.0, FAKE, 1, FAKE, 1 << 30, None) == 1

@@ -1,0 +1,167 @@
+"""GPU parity of the lightning indexer (a4) and the top-k selection (a5).
+
+Scores are compared bit for bit with the oracle (same quantised keys and queries: the HIP
+quantiser is itself bit-exact against the oracle's); the top-k index lists must be equal.
+Cases: the fp32 tiny workload, ragged key counts and causal visibility, padded head counts,
+adversarial ties, k above the visible count, nothing visible, and the full CSA decode sizes
+of the 131072-token (B=8, top-512) and 1M-token (B=4, top-1024) workloads in the launch
+configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_02_amd as v4
+import oracle
+from gpu_util import announce, f32, idx_from_f32
+from workloads import CSA_FLASH, CSA_PRO_1M, TINY, decode_inputs, normal, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+def run_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1):
+    """HIP indexer + top-k; keys_f [B][N][d], q_f [B][Q*H][d], w [B][Q][H]."""
+    B, N, d = keys_f.shape
+    H = w.shape[-1]
+    keys = idx_from_f32(keys_f, fmt)
+    qi = idx_from_f32(q_f, fmt)
+    wt = f32(w)
+    out = torch.full((B, Q, k), -7, dtype=torch.int32, device="cuda")
+    n_max = max(min(int(n), (int(p) + 1) // m) for n, p in zip(np.repeat(n_entries, Q), q_pos))
+    ws = v4.workspace(v4.v4a_indexer_topk_workspace(B, Q, max(n_max, 0), k))
+    v4.v4a_indexer_topk(keys, n_entries, m, qi, wt, B, Q, H, q_pos, k, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), keys, qi
+
+
+def oracle_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1):
+    B, N, d = keys_f.shape
+    H = w.shape[-1]
+    res = np.empty((B, Q, k), np.int32)
+    for b in range(B):
+        if fmt == v4.V4A_IDX_MXFP4:
+            kc, ks = oracle.quant_mxfp4(keys_f[b])
+        for j in range(Q):
+            n_vis = oracle.visible_entries(int(n_entries[b]), m, int(q_pos[b * Q + j]))
+            qrows = q_f[b, j * H:(j + 1) * H]
+            if fmt == v4.V4A_IDX_MXFP4:
+                qc, qs = oracle.quant_mxfp4(qrows)
+                s, bad = oracle.indexer_scores_mxfp4(qc, qs, w[b, j], kc, ks, n_vis)
+                assert bad == 0
+            else:
+                s = oracle.indexer_scores_f32(qrows, w[b, j], keys_f[b], n_vis)
+            res[b, j] = oracle.topk(s, k, n_vis)
+    return res
+
+
+def test_scores_mxfp4_bit_exact():
+    B, N, H = 2, 3000, 64
+    keys = normal(101, "keys", (B, N, 128))
+    q = normal(101, "q_idx", (B, H, 128))
+    w = normal(101, "w", (B, 1, H))
+    n_entries, q_pos = [N, N], [4 * N - 1, 4 * 1000 + 2]
+    announce("indexer scores MXFP4 B=2 N=3000")
+    ki, qi = idx_from_f32(keys), idx_from_f32(q)
+    out = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    v4.v4a_indexer_scores(ki, n_entries, 4, qi, f32(w), B, 1, H, q_pos, N, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        kc, ks = oracle.quant_mxfp4(keys[b])
+        qc, qs = oracle.quant_mxfp4(q[b])
+        n_vis = oracle.visible_entries(N, 4, q_pos[b])
+        ref, bad = oracle.indexer_scores_mxfp4(qc, qs, w[b, 0], kc, ks, n_vis)
+        assert bad == 0
+        assert np.array_equal(got[b, :n_vis].view(np.uint32), ref.view(np.uint32)), b
+        assert np.all(got[b, n_vis:] == -np.inf)
+
+
+def test_scores_f32_bit_exact():
+    w_ = TINY
+    N = w_.n_csa
+    keys = normal(w_.seed, "misc0", (1, N, w_.d_I))
+    q = normal(w_.seed, "q_idx", (1, w_.H_I, w_.d_I))
+    w = normal(w_.seed, "w", (1, 1, w_.H_I))
+    announce("indexer scores fp32 tiny")
+    ki, qi = idx_from_f32(keys, v4.V4A_IDX_F32), idx_from_f32(q, v4.V4A_IDX_F32)
+    out = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    v4.v4a_indexer_scores(ki, [N], 4, qi, f32(w), 1, 1, w_.H_I, [w_.T - 1], N, out)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_scores_f32(q[0], w[0, 0], keys[0])
+    assert np.array_equal(out.cpu().numpy()[0].view(np.uint32), ref.view(np.uint32))
+
+
+CASES = {
+    # name: (B, N list, H, k, q_pos list or None (decode at the end), fmt, d)
+    "tiny_f32": (1, [1024], 4, 64, None, v4.V4A_IDX_F32, 32),
+    "ragged_causal": (3, [5000, 3000, 100], 64, 512, [4 * 5000 - 1, 4 * 2000 + 1, 399], v4.V4A_IDX_MXFP4, 128),
+    "nothing_visible": (2, [100, 100], 64, 16, [2, 399], v4.V4A_IDX_MXFP4, 128),
+    "k_equals_visible": (1, [777], 64, 777, None, v4.V4A_IDX_MXFP4, 128),
+    "heads_4": (2, [2500, 2500], 4, 100, None, v4.V4A_IDX_MXFP4, 128),
+    "heads_36": (2, [2500, 1500], 36, 300, None, v4.V4A_IDX_MXFP4, 128),
+    "k_1": (2, [9000, 17000], 64, 1, None, v4.V4A_IDX_MXFP4, 128),
+    "k_2048": (1, [20000], 64, 2048, None, v4.V4A_IDX_MXFP4, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_topk_bit_exact(name):
+    B, Ns, H, k, q_pos, fmt, d = CASES[name]
+    N = max(Ns)
+    seed = 200 + list(CASES).index(name)
+    keys = normal(seed, "keys", (B, N, d))
+    q = normal(seed, "q_idx", (B, H, d))
+    w = normal(seed, "w", (B, 1, H))
+    if q_pos is None:
+        q_pos = [4 * n - 1 for n in Ns]
+    announce(f"topk {name}")
+    got, _, _ = run_topk(keys, q, w, np.array(Ns), q_pos, k, fmt=fmt)
+    ref = oracle_topk(keys, q, w, np.array(Ns), q_pos, k, fmt=fmt)
+    for b in range(B):
+        assert np.array_equal(got[b, 0], ref[b, 0]), (name, b, np.setdiff1d(got[b, 0], ref[b, 0])[:10])
+
+
+def test_topk_adversarial_ties():
+    """Keys from a handful of distinct vectors make many exactly equal scores: the lowest
+    indices must win at the threshold; identical keys everywhere give indices 0..k-1."""
+    B, N, H, k = 2, 12000, 64, 700
+    g = np.random.default_rng(300)
+    base = normal(300, "keys", (5, 128))
+    choice = g.integers(0, 5, size=(B, N))
+    keys = base[choice]
+    keys[1] = base[0]                           # sequence 1: every key identical
+    q = normal(300, "q_idx", (B, H, 128))
+    w = normal(300, "w", (B, 1, H))
+    announce("topk adversarial ties")
+    got, _, _ = run_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k)
+    ref = oracle_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[1, 0], np.arange(k))
+
+
+def test_topk_prefill_queries():
+    """Several queries per sequence at consecutive positions (the prefill form)."""
+    B, N, H, k, Q = 1, 6000, 64, 512, 24
+    keys = normal(301, "keys", (B, N, 128))
+    q = normal(301, "q_idx", (B, Q * H, 128))
+    w = normal(301, "w", (B, Q, H))
+    pos0 = 4 * 5000
+    q_pos = [pos0 + j for j in range(Q)]
+    announce("topk prefill-form queries")
+    got, _, _ = run_topk(keys, q, w, np.array([N]), q_pos, k, Q=Q)
+    ref = oracle_topk(keys, q, w, np.array([N]), q_pos, k, Q=Q)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wl", [CSA_FLASH, CSA_PRO_1M], ids=lambda w: w.name)
+def test_topk_full_size(wl):
+    """Full decode sizes (every key of every sequence scored), checked bit for bit."""
+    inp = decode_inputs(wl, threads=16)
+    N = inp["N"]
+    announce(f"topk full size {wl.name} B={wl.B} N={N} k={wl.k}")
+    q_pos = [wl.T - 1] * wl.B
+    got, _, _ = run_topk(inp["keys"], inp["q_idx"], inp["w"][:, None, :], np.array([N] * wl.B), q_pos, wl.k)
+    ref = oracle_topk(inp["keys"], inp["q_idx"], inp["w"][:, None, :], np.array([N] * wl.B), q_pos, wl.k)
+    assert np.array_equal(got, ref)
+    # deterministic: a second run gives the same bits
+    got2, _, _ = run_topk(inp["keys"], inp["q_idx"], inp["w"][:, None, :], np.array([N] * wl.B), q_pos, wl.k)
+    assert np.array_equal(got, got2)
