@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--rotate", type=int, default=16, help="input copies cycled through (MALL defeat)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying graphs")
     return p.parse_args()
 
 
@@ -125,19 +126,67 @@ def main():
     outs = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     win_len = [W] * B
 
-    def step(i, ev=None):
-        st = sets[i % len(sets)]
+    def stage_compress(st):
         v4.v4a_compress_csa(st["kv_a"], st["kv_b"], st["gate_a"], st["gate_b"], st["bias_a"], st["bias_b"],
                             tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_kv=st["kv"])
         v4.v4a_compress_csa(st["idx_a"], st["idx_b"], st["idx_gate_a"], st["idx_gate_b"], st["idx_bias_a"],
                             st["idx_bias_b"], tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_idx=st["keys"])
+
+    def stage_indexer(st):
+        v4.v4a_indexer_topk(st["keys"], [N] * B, m, st["qi"], st["w"], B, 1, HI, q_pos, k, sel, ws)
+
+    def stage_attend(st, out):
+        v4.v4a_decode_csa(st["q"], st["kv"], sel.view(B, k), k, st["win"], win_len, W, st["sink"], q_pos,
+                          softmax_scale=scale, out=out, ws=ws)
+
+    def step_eager(i):
+        st = sets[i % len(sets)]
+        stage_compress(st)
+        stage_indexer(st)
+        stage_attend(st, outs[i % 2])
+
+    graphs = None
+    if not args.eager:
+        # each input set's step is captured as three graphs (compress, indexer + top-k,
+        # attention); replaying them between HIP events times the indexer stage live
+        print("[bench] capturing graphs", file=sys.stderr, flush=True)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_eager(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for r, st in enumerate(sets):
+            gs = []
+            for fn in (lambda: stage_compress(st), lambda: stage_indexer(st),
+                       lambda: stage_attend(st, outs[r % 2])):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                gs.append(g)
+            graphs.append(gs)
+        torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if graphs is None:
+            st = sets[i % len(sets)]
+            stage_compress(st)
+            if ev is not None:
+                ev[0].record()
+            stage_indexer(st)
+            if ev is not None:
+                ev[1].record()
+            stage_attend(st, outs[i % 2])
+            return
+        g = graphs[i % len(graphs)]
+        g[0].replay()
         if ev is not None:
             ev[0].record()
-        v4.v4a_indexer_topk(st["keys"], [N] * B, m, st["qi"], st["w"], B, 1, HI, q_pos, k, sel, ws)
+        g[1].replay()
         if ev is not None:
             ev[1].record()
-        v4.v4a_decode_csa(st["q"], st["kv"], sel.view(B, k), k, st["win"], win_len, W, st["sink"], q_pos,
-                          softmax_scale=scale, out=outs[i % 2], ws=ws)
+        g[2].replay()
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -172,6 +221,8 @@ def main():
     # parity of the last step on set 0 against the oracle (sequence 0, full indexer scan)
     step(0)
     torch.cuda.synchronize()
+    used_graphs = graphs is not None
+    graphs = None
     gpu_sel = sel.cpu().numpy()[:, 0]
     gpu_out = outs[0].float().cpu().numpy()
 
@@ -181,7 +232,7 @@ def main():
         "vs_baseline": None, "dtype": "mxfp4+bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "context_tokens": T, "csa_entries": N, "heads": H,
                    "head_dim": D, "rope_dims": R, "indexer_heads": HI, "indexer_dim": dI, "topk": k,
-                   "window": W, "input_copies": len(sets)},
+                   "window": W, "input_copies": len(sets), "hip_graphs": used_graphs},
         "roofline": {"kernel": "v4a_indexer_topk (MXFP4 scoring + top-k select)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "ms_per_launch": idx_ms, "algorithmic_bytes": idx_bytes,

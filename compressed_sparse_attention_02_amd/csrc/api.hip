@@ -81,23 +81,28 @@ static v4a_status check_idx(const v4a_idx *x, const char *name) {
 
 // ------------------------------------------------------------- indexer workspace ----
 struct TopkWs {
-    size_t keys, hist, counters, cand, sel, total;
+    size_t keys, hist, list, counts, meta, total;
 };
 
+// Workspace of the indexer + top-k call: orderable score keys, the per-query histograms
+// (cleared on every call), the per-slice ordered lists of keys at or above the threshold
+// bin, their counts, and the per-query threshold.
 static TopkWs topk_layout(int B, int Q, int64_t n_max, int k) {
+    (void)k;
     TopkWs L{};
     const size_t BQ = (size_t)B * (size_t)Q;
+    const size_t slices = (size_t)select_slices(n_max);
     size_t off = 0;
     L.keys = off;
     off = round_up(off + BQ * (size_t)n_max * 4, 256);
     L.hist = off;
-    off += BQ * 4096 * 4;
-    L.counters = off;
-    off = round_up(off + BQ * 16, 256);
-    L.cand = off;
-    off = round_up(off + BQ * (size_t)n_max * 8, 256);
-    L.sel = off;
-    off = round_up(off + BQ * (size_t)k * 4, 256);
+    off = round_up(off + BQ * kHistCopies * kHistBins * 4, 256);
+    L.list = off;
+    off = round_up(off + BQ * slices * kSelSlice * 8, 256);
+    L.counts = off;
+    off = round_up(off + BQ * slices * 4, 256);
+    L.meta = off;
+    off = round_up(off + BQ * 8, 256);
     L.total = off;
     return L;
 }
@@ -314,6 +319,7 @@ v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32
     QueryPos qp;
     int64_t n_max = 0;
     if ((st = fill_query_pos(qp, B, Q, m, n_entries, q_pos, keys->cap, &n_max)) != V4A_OK) return st;
+    if (n_max > (int64_t)1024 * kSelSlice) return fail(V4A_EUNSUPPORTED, "more than %d visible keys per query", 1024 * kSelSlice);
     const TopkWs L = topk_layout(B, Q, n_max, k);
     if (!ws || ws_bytes < L.total || !aligned(ws, 256))
         return fail(V4A_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, ws_bytes);
@@ -321,7 +327,7 @@ v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32
     hipStream_t s = (hipStream_t)stream;
     char *base = (char *)ws;
     const size_t BQ = (size_t)B * Q;
-    hipError_t e = launch_zero(base + L.hist, BQ * 4096 * 4 + BQ * 16, s);
+    hipError_t e = launch_zero(base + L.hist, BQ * kHistCopies * kHistBins * 4, s);
     if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
     IndexerArgs ia{};
     ia.keys = keys;
@@ -340,10 +346,9 @@ v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32
     sa.n_max = n_max;
     sa.BQ = (int)BQ;
     sa.k = k;
-    sa.cand = (uint32_t *)(base + L.cand);
-    sa.cand_cap = n_max > 0 ? n_max : 1;
-    sa.sel = (int32_t *)(base + L.sel);
-    sa.counters = (uint32_t *)(base + L.counters);
+    sa.list = (uint32_t *)(base + L.list);
+    sa.counts = (uint32_t *)(base + L.counts);
+    sa.meta = (int32_t *)(base + L.meta);
     sa.out = out_idx;
     return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
 }

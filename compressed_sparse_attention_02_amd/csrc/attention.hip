@@ -37,6 +37,7 @@ constexpr int kTile = 32;
 constexpr int kErStride = 520;  // bf16 per key row in Er (512 + 8: staggers LDS banks)
 constexpr int kEcStride = 36;   // bf16 per dim row in Ec (32 keys + 4)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSelKeys = 2048;  // top-k entries per sequence (k <= 2048)
 
 struct AttnParams {
     const void *q;           // [B][H][D]
@@ -136,6 +137,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
     __shared__ __attribute__((aligned(16))) uint16_t Ec[D * kEcStride];
     __shared__ float ksc[kTile];
     __shared__ int kvalid[kTile];
+    __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
 
     // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart
     int L = blockIdx.x, hg = 0, p = L;
@@ -173,64 +175,124 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 #pragma unroll
     for (int i = 0; i < NDT; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
+    // the split's selected entry indices, read once (one load round for all its tiles)
+    if (P.topk) {
+        const int e1 = min(kb1, n_ent);
+        for (int j = kb0 + t; j < e1; j += NT) sidx[j - kb0] = P.topk[(int64_t)b * P.k + j];
+    }
 
-    const int n_tasks = 8 * (D / 4);
+    constexpr int NSEG = D / 8;          // 8-dim segments per key row
+    constexpr int NTASK = 8 * NSEG;      // (4-key group, segment) staging tasks per tile
     for (int tb = kb0; tb < kb1; tb += kTile) {
         __syncthreads();
-        // ---- staging: task = (key group kg of 4 keys, dim quad dq of 4 dims)
-        for (int task = t; task < n_tasks; task += NT) {
-            const int kg = task & 7, dq = task >> 3;
-            const int dim = 4 * dq;
-            uint32_t v01[4], v23[4];  // 4 keys x (2 packed bf16 pairs)
+        // ---- staging.  Task (kg, seg): keys 4kg..4kg+3, dims 8seg..8seg+7.  All loads of a
+        // thread are issued before any is used; padding keys read a valid row and are zeroed.
+        const int kind = (tb + kTile <= n_ent) ? 0 : (tb >= n_ent ? 1 : 2);  // entries / window / mixed
+        for (int task = t; task < NTASK; task += NT) {
+            const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
+            uint4 v[4];
+            bool valid[4];
+            if (kind == 0) {
+                int64_t row[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int kidx = tb + 4 * kg + j;
+                    int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
+                    valid[j] = e >= 0 && e < P.cap;
+                    row[j] = (int64_t)b * P.cap + (valid[j] ? e : 0);
+                }
+                if (dim < Dn) {
+                    uint2 c[4];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) c[j] = *(const uint2 *)(P.nope + row[j] * Dn + dim);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        v[j].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].x, 1.0f, false));
+                        v[j].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].x, 1.0f, true));
+                        v[j].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].y, 1.0f, false));
+                        v[j].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].y, 1.0f, true));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)(P.rope + row[j] * R + (dim - Dn));
+                }
+                if (seg == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        ksc[4 * kg + j] = P.kscale[row[j]];
+                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
+                    }
+                }
+            } else if (kind == 1) {
+                int64_t row[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int wtok = tb + 4 * kg + j - n_ent;
+                    valid[j] = tb + 4 * kg + j < kb1;
+                    row[j] = (int64_t)b * P.W + (valid[j] ? wtok : 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
+                if (seg == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        ksc[4 * kg + j] = 1.0f;
+                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
+                    }
+                }
+            } else {
+                // a tile holding the last entries and the first window tokens: per key
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int kidx = tb + 4 * kg + j;
+                    float scl = 0.0f;
+                    v[j] = make_uint4(0, 0, 0, 0);
+                    valid[j] = false;
+                    if (kidx < n_ent) {
+                        int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
+                        if (e >= 0 && e < P.cap) {
+                            const int64_t row = (int64_t)b * P.cap + e;
+                            valid[j] = true;
+                            scl = P.kscale[row];
+                            if (dim < Dn) {
+                                const uint2 c = *(const uint2 *)(P.nope + row * Dn + dim);
+                                v[j].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
+                                v[j].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
+                                v[j].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
+                                v[j].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
+                            } else {
+                                v[j] = *(const uint4 *)(P.rope + row * R + (dim - Dn));
+                            }
+                        }
+                    } else if (kidx < kb1) {
+                        valid[j] = true;
+                        scl = 1.0f;
+                        v[j] = *(const uint4 *)((const uint16_t *)P.win + ((int64_t)b * P.W + (kidx - n_ent)) * D + dim);
+                    }
+                    if (seg == 0) {
+                        ksc[4 * kg + j] = scl;
+                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int key = 4 * kg + j, kidx = tb + key;
-                int64_t e = -1;
-                int wtok = -1;
-                if (kidx < n_ent) {
-                    e = P.topk ? (int64_t)P.topk[(int64_t)b * P.k + kidx] : (int64_t)kidx;
-                    if (e >= P.cap) e = -1;  // out-of-range index: treated as padding
-                } else if (kidx < kb1) {
-                    wtok = kidx - n_ent;
-                }
-                uint32_t lo = 0, hi = 0;
-                if (e >= 0) {
-                    const int64_t row = (int64_t)b * P.cap + e;
-                    if (dim < Dn) {
-                        const uint32_t c4 = *(const uint32_t *)(P.nope + row * Dn + dim);
-                        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, false));
-                        hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, true));
-                    } else {
-                        const uint2 r = *(const uint2 *)(P.rope + row * R + (dim - Dn));
-                        lo = r.x;
-                        hi = r.y;
-                    }
-                    if (dq == 0) { ksc[key] = P.kscale[row]; kvalid[key] = 1; }
-                } else if (wtok >= 0) {
-                    const uint2 r = *(const uint2 *)((const uint16_t *)P.win + ((int64_t)b * P.W + wtok) * D + dim);
-                    lo = r.x;
-                    hi = r.y;
-                    if (dq == 0) { ksc[key] = 1.0f; kvalid[key] = 1; }
-                } else if (dq == 0) {
-                    ksc[key] = 0.0f;
-                    kvalid[key] = 0;
-                }
-                v01[j] = lo;
-                v23[j] = hi;
-                *(uint2 *)(Er + key * kErStride + dim) = make_uint2(lo, hi);
+                if (!valid[j]) v[j] = make_uint4(0, 0, 0, 0);
+                *(uint4 *)(Er + (4 * kg + j) * kErStride + dim) = v[j];
             }
             // dim-major: row dim+d holds keys 4kg..4kg+3
 #pragma unroll
-            for (int d = 0; d < 4; d++) {
-                uint32_t a0, a1;
+            for (int d = 0; d < 8; d++) {
                 const int sh = (d & 1) ? 16 : 0;
-                if (d < 2) {
-                    a0 = ((v01[0] >> sh) & 0xFFFFu) | (((v01[1] >> sh) & 0xFFFFu) << 16);
-                    a1 = ((v01[2] >> sh) & 0xFFFFu) | (((v01[3] >> sh) & 0xFFFFu) << 16);
-                } else {
-                    a0 = ((v23[0] >> sh) & 0xFFFFu) | (((v23[1] >> sh) & 0xFFFFu) << 16);
-                    a1 = ((v23[2] >> sh) & 0xFFFFu) | (((v23[3] >> sh) & 0xFFFFu) << 16);
+                uint32_t w0, w1, w2, w3;
+                switch (d >> 1) {
+                    case 0: w0 = v[0].x; w1 = v[1].x; w2 = v[2].x; w3 = v[3].x; break;
+                    case 1: w0 = v[0].y; w1 = v[1].y; w2 = v[2].y; w3 = v[3].y; break;
+                    case 2: w0 = v[0].z; w1 = v[1].z; w2 = v[2].z; w3 = v[3].z; break;
+                    default: w0 = v[0].w; w1 = v[1].w; w2 = v[2].w; w3 = v[3].w; break;
                 }
+                const uint32_t a0 = ((w0 >> sh) & 0xFFFFu) | (((w1 >> sh) & 0xFFFFu) << 16);
+                const uint32_t a1 = ((w2 >> sh) & 0xFFFFu) | (((w3 >> sh) & 0xFFFFu) << 16);
                 *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
             }
         }
@@ -340,21 +402,33 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
     if (splits == 1) return;
     const int d0 = lane * NV;
     if (d0 >= P.D) return;
+    // every split's (m, l) and partial output are loaded before the merge (splits <= 16)
+    float m2s[16], ls[16];
+    float po[16][NV];
+#pragma unroll
+    for (int s = 0; s < 16; s++) {
+        const int sc = s < splits ? s : 0;
+        const float *pm = P.part_ml + (((int64_t)b * P.S + sc) * P.H + h) * 2;
+        m2s[s] = pm[0];
+        ls[s] = pm[1];
+        const float *pp = P.part_o + (((int64_t)b * P.S + sc) * P.H + h) * P.D + d0;
+#pragma unroll
+        for (int v = 0; v < NV; v++) po[s][v] = pp[v];
+    }
     float M = P.sink[h] * kLog2e;
-    for (int s = 0; s < splits; s++)
-        M = fmaxf(M, P.part_ml[(((int64_t)b * P.S + s) * P.H + h) * 2]);
+#pragma unroll
+    for (int s = 0; s < 16; s++)
+        if (s < splits) M = fmaxf(M, m2s[s]);
     float o[NV];
 #pragma unroll
     for (int v = 0; v < NV; v++) o[v] = 0.0f;
     float l = 0.0f;
-    for (int s = 0; s < splits; s++) {
-        const float *pm = P.part_ml + (((int64_t)b * P.S + s) * P.H + h) * 2;
-        const float m2 = pm[0];
-        const float c = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - M);
-        l = fmaf(pm[1], c, l);
-        const float *po = P.part_o + (((int64_t)b * P.S + s) * P.H + h) * P.D + d0;
 #pragma unroll
-        for (int v = 0; v < NV; v++) o[v] = fmaf(po[v], c, o[v]);
+    for (int s = 0; s < 16; s++) {
+        const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
+        l = fmaf(ls[s], c, l);
+#pragma unroll
+        for (int v = 0; v < NV; v++) o[v] = fmaf(po[s][v], c, o[v]);
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
     finish_head<NV>(P, Sq, b, h, d0, M, l, o);

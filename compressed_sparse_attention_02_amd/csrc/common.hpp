@@ -16,6 +16,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -100,6 +101,8 @@ namespace v4a {
 // Per-sequence / per-query positions travel as kernel arguments (no host-to-device copy,
 // so every call stays asynchronous and capturable).
 constexpr int kMaxSeq = 128;
+constexpr int kHistBins = 4096;   // top-12-bit histogram of the orderable score keys
+constexpr int kHistCopies = 8;    // copies of each query's histogram (contention spreading)
 
 struct QueryPos {
     int mode;  // 0: pos[qi] per query (B*Q <= kMaxSeq); 1: pos[b] + j for query j of sequence b
@@ -155,22 +158,23 @@ struct IndexerArgs {
     int64_t n_max;            // max visible keys over the queries (grid size)
     uint32_t *score_keys;     // [B*Q][n_max] orderable keys (or NULL)
     float *scores;            // [B*Q][n_max] raw scores (or NULL)
-    uint32_t *hist;           // [B*Q][4096] histogram of the top 12 key bits (or NULL)
+    uint32_t *hist;           // [B*Q][kHistCopies][4096] histogram of the top 12 key bits (or NULL)
 };
 hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 struct SelectArgs {
     const uint32_t *score_keys;   // [BQ][n_max]
-    const uint32_t *hist;         // [BQ][4096]
+    const uint32_t *hist;         // [BQ][kHistCopies][4096]
     int64_t n_max;
     int BQ, k;
-    uint32_t *cand;               // [BQ][cand_cap][2]: (score key, index)
-    int64_t cand_cap;
-    int32_t *sel;                 // [BQ][k] keys above the threshold bin
-    uint32_t *counters;           // [BQ][4]: selected, candidates, finished workgroups
+    uint32_t *list;               // [BQ][slices * kSelSlice][2]: (index, score key) at or above the threshold bin
+    uint32_t *counts;             // [BQ][slices] entries listed per slice
+    int32_t *meta;                // [BQ][2]: threshold bin, count above it
     int32_t *out;                 // [BQ][k]
 };
+int select_slices(int64_t n_max);
+constexpr int kSelSlice = 8192;
 hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s);
 
 struct AttnArgs {

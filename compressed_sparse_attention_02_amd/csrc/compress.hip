@@ -78,6 +78,20 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
     for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
 
     if (P.G == 1) {
+        // candidate rows are loaded in batches of kRowBatch; the first batch is issued before the
+        // gate logits so the two memory round trips overlap
+        constexpr int kRowBatch = 8;
+        float xb[kRowBatch][VPT];
+        auto load_batch = [&](int c0) {
+#pragma unroll
+            for (int u = 0; u < kRowBatch; u++) {
+                const int c = min(c0 + u, n_cand - 1);
+                const int s = c / m, j = c % m;
+                const int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - P.tok0;
+                load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, xb[u], x_off);
+            }
+        };
+        load_batch(0);
         // weights once per wavefront: lane c holds candidate c (and c + 64, ...)
         float zmax = -INFINITY;
         for (int c = lane; c < n_cand; c += 64) {
@@ -98,15 +112,21 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
-        for (int c = 0; c < n_cand; c++) {
-            int s = c / m, j = c % m;
-            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - P.tok0;
-            float x[VPT];
-            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
-            float wgt = wsh[wv][c];
+        for (int c0 = 0; c0 < n_cand; c0 += kRowBatch) {
+            float cur[kRowBatch][VPT];
 #pragma unroll
-            for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, x[v], acc[v]);
+            for (int u = 0; u < kRowBatch; u++)
+#pragma unroll
+                for (int v = 0; v < VPT; v++) cur[u][v] = xb[u][v];
+            if (c0 + kRowBatch < n_cand) load_batch(c0 + kRowBatch);  // next batch in flight
+#pragma unroll
+            for (int u = 0; u < kRowBatch; u++) {
+                if (c0 + u < n_cand) {
+                    const float wgt = wsh[wv][c0 + u];
+#pragma unroll
+                    for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
+                }
+            }
         }
 #pragma unroll
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;

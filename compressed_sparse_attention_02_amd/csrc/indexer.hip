@@ -26,8 +26,7 @@
 
 namespace v4a {
 
-constexpr int kKeysPerWG = 1024;
-constexpr int kHistBins = 4096;
+constexpr int kGroupsPerIter = 8;   // key groups of 16 in flight per wavefront
 struct IndexerParams {
     const uint8_t *kc;   // key codes [B][cap][d/2]
     const uint8_t *ks;   // key scales [B][cap][d/32]
@@ -42,7 +41,8 @@ struct IndexerParams {
     int64_t n_max;
     uint32_t *score_keys;  // [BQ][n_max] or NULL
     float *scores;         // [BQ][n_max] or NULL
-    uint32_t *hist;        // [BQ][4096] or NULL
+    uint32_t *hist;        // [BQ][kHistCopies][4096] or NULL
+    int groups_per_wave;   // key groups of 16 per wavefront (a multiple of kGroupsPerIter)
 };
 
 __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64_t i, float score,
@@ -54,90 +54,107 @@ __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64
     if (lhist) atomicAdd(&lhist[key >> 20], 1u);
 }
 
+// Adds the workgroup's LDS histogram into copy (blockIdx.x % kHistCopies) of the query's
+// global histogram; spreading the copies keeps many workgroups off the same hot bins.
 __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint32_t *lhist) {
     __syncthreads();
     if (!P.hist) return;
+    uint32_t *gh = P.hist + ((int64_t)qi * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins;
     for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
         uint32_t c = lhist[bin];
-        if (c) atomicAdd(&P.hist[(int64_t)qi * kHistBins + bin], c);
+        if (c) atomicAdd(&gh[bin], c);
     }
 }
 
 // MXFP4, d = 128 (one 16x16x128 scaled MFMA per 16 heads and 16 keys), H <= 64.
+// A workgroup scores 64 * groups_per_wave consecutive keys; wavefront wv owns groups_per_wave
+// groups of 16 keys and processes them kGroupsPerIter at a time: every load of an iteration is issued
+// before the first MFMA (out-of-range lanes read a clamped, valid key and are masked after),
+// so kGroupsPerIter * 1 KB per wavefront is in flight.
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
     __shared__ uint32_t lhist[kHistBins];
     const int qi = blockIdx.y;
     const int b = qi / QP.Q;
     const int64_t n_vis = visible_keys(QP, qi);
-    const int64_t k0 = (int64_t)blockIdx.x * kKeysPerWG;
+    const int64_t keys_per_wg = (int64_t)4 * P.groups_per_wave * 16;
+    const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
     if (k0 >= n_vis) return;  // uniform over the workgroup
     for (int bin = threadIdx.x; bin < kHistBins; bin += 256) lhist[bin] = 0;
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;  // col: head/key within 16; grp: MX block / chain
 
-    // query: 4 head groups of 16 heads; lane holds head 16g+col, MX block grp
+    // query: 4 head groups of 16 heads; lane holds head 16g+col, MX block grp.  Heads past H
+    // read head H-1 (all loads issued together) and are zeroed: code 0 and weight 0.
     v8i qa[4];
     int qscale[4];
     float wt[4][4];  // w of heads 16g + 4*grp + i
+    {
+        uint4 qc[4];
+        uint32_t qsb[4];
+        float wr[4][4];
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        const int h = 16 * g + col;
-        const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
-        qa[g] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        qscale[g] = 127;
-        if (h < P.H) {
-            const uint4 c = *(const uint4 *)(P.qc + row * 64 + grp * 16);
-            qa[g][0] = (int)c.x; qa[g][1] = (int)c.y; qa[g][2] = (int)c.z; qa[g][3] = (int)c.w;
-            qscale[g] = P.qs[row * 4 + grp];
+        for (int g = 0; g < 4; g++) {
+            const int h = min(16 * g + col, P.H - 1);
+            const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
+            qc[g] = *(const uint4 *)(P.qc + row * 64 + grp * 16);
+            qsb[g] = P.qs[row * 4 + grp];
+#pragma unroll
+            for (int i = 0; i < 4; i++) wr[g][i] = P.w[(int64_t)qi * P.H + min(16 * g + 4 * grp + i, P.H - 1)];
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int hh = 16 * g + 4 * grp + i;
-            wt[g][i] = hh < P.H ? P.w[(int64_t)qi * P.H + hh] : 0.0f;
+        for (int g = 0; g < 4; g++) {
+            const bool on = 16 * g + col < P.H;
+            qa[g] = v8i{on ? (int)qc[g].x : 0, on ? (int)qc[g].y : 0, on ? (int)qc[g].z : 0, on ? (int)qc[g].w : 0,
+                        0, 0, 0, 0};
+            qscale[g] = on ? (int)qsb[g] : 127;
+#pragma unroll
+            for (int i = 0; i < 4; i++) wt[g][i] = (16 * g + 4 * grp + i < P.H) ? wr[g][i] : 0.0f;
         }
     }
     __syncthreads();
 
     const uint8_t *kc = P.kc + (int64_t)b * P.kcap * 64;
     const uint8_t *ks = P.ks + (int64_t)b * P.kcap * 4;
-    const int64_t kend = k0 + kKeysPerWG < n_vis ? k0 + kKeysPerWG : n_vis;
-    constexpr int kUnroll = 4;
-    // wavefront wv takes key groups wv, wv+4, ... of the chunk, kUnroll at a time
-    for (int64_t g0 = k0 + 16 * wv; g0 < kend; g0 += 16 * 4 * kUnroll) {
-        uint4 kd[kUnroll];
-        uint32_t ksc[kUnroll];
+    const int64_t kend = k0 + keys_per_wg < n_vis ? k0 + keys_per_wg : n_vis;
+    uint32_t *hist = P.hist ? lhist : nullptr;
+    const int64_t wbase = k0 + (int64_t)wv * P.groups_per_wave * 16;
+    for (int it = 0; it < P.groups_per_wave / kGroupsPerIter; it++) {
+        const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
+        if (base >= kend) break;  // uniform over the wavefront
+        uint4 kd[kGroupsPerIter];
+        uint32_t ksc[kGroupsPerIter];
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int64_t key = g0 + (int64_t)u * 64 + col;
-            if (key < kend) {
-                kd[u] = *(const uint4 *)(kc + key * 64 + grp * 16);
-                ksc[u] = (*(const uint32_t *)(ks + key * 4) >> (8 * grp)) & 0xFFu;
-            } else {
-                kd[u] = make_uint4(0, 0, 0, 0);
-                ksc[u] = 127;
-            }
+        for (int u = 0; u < kGroupsPerIter; u++) {
+            int64_t key = base + 16 * u + col;
+            key = key < kend ? key : kend - 1;  // clamped: always a valid key of this query
+            const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16));
+            kd[u] = make_uint4(v.x, v.y, v.z, v.w);
+            ksc[u] = *(const uint32_t *)(ks + key * 4);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int64_t gbase = g0 + (int64_t)u * 64;
+        for (int u = 0; u < kGroupsPerIter; u++) {
+            const int64_t gbase = base + 16 * u;
             if (gbase >= kend) break;  // uniform
             const v8i kb = v8i{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
+            const int sc = (int)((ksc[u] >> (8 * grp)) & 0xFFu);
+            v4f acc[4];
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                                                                          qscale[g], 0, sc);
             float c = 0.0f;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, acc, 4, 4, 0, qscale[g], 0,
-                                                                       (int)ksc[u]);
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float r = acc[i] > 0.0f ? acc[i] : 0.0f;
+                    const float r = acc[g][i] > 0.0f ? acc[g][i] : 0.0f;
                     c = fmaf(wt[g][i], r, c);
                 }
             }
             const float c1 = __shfl_down(c, 16), c2 = __shfl_down(c, 32), c3 = __shfl_down(c, 48);
             const int64_t key = gbase + col;
-            if (grp == 0 && key < kend) emit_score(P, qi, key, ((c + c1) + c2) + c3, P.hist ? lhist : nullptr);
+            if (grp == 0 && key < kend) emit_score(P, qi, key, ((c + c1) + c2) + c3, hist);
         }
     }
     flush_hist(P, qi, lhist);
@@ -217,7 +234,13 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
     if (mx) {
-        dim3 grid((unsigned)((a.n_max + kKeysPerWG - 1) / kKeysPerWG), (unsigned)BQ);
+        // keys per workgroup: the largest power-of-two multiple of 512 that still gives at least
+        // 512 workgroups (two per CU); it changes only the work split, never a result
+        int gpw = kGroupsPerIter;  // keys per workgroup = 4 wavefronts * gpw groups * 16 keys
+        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 1024) gpw *= 2;
+        P.groups_per_wave = gpw;
+        const int64_t kpw = (int64_t)64 * gpw;
+        dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
         hipLaunchKernelGGL(indexer_mxfp4_kernel, grid, dim3(256), 0, s, P, qp);
     } else {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
