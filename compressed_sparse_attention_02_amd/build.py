@@ -19,6 +19,8 @@ SOURCES = ["api.hip", "quant.hip", "compress.hip", "indexer.hip", "topk.hip", "a
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in VGPRs, so the epilogues read them without accumulator-register moves
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-command-line-argument"]
 
 

@@ -447,8 +447,8 @@ __device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_
         if (d < Dn) {
             const uint8_t c = P.nope[row * Dn + d];
             const uint32_t c4 = c;
-            const v2bf pr = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, false);
-            return bf16_to_f32(__builtin_bit_cast(uint16_t, pr[0])) * P.kscale[row];
+            const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4, 1.0f, false));
+            return bf16_to_f32((uint16_t)(pr & 0xFFFFu)) * P.kscale[row];
         }
         return bf16_to_f32(P.rope[row * P.R + (d - Dn)]);
     }

@@ -85,12 +85,25 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 
 // RoPE cos/sin of one pair: angle p * theta^(-2j/R) in double, cos and sin in double,
-// rounded to fp32.
+// rounded to fp32.  Positions reach 2^20, so the angle is first reduced by multiples of pi/2
+// (Cody-Waite with a two-term pi/2 and fused multiply-adds, error ~1e-16 relative to the
+// reduced angle); sin and cos then run on |r| <= pi/4 and the quadrant picks the pair.
 __device__ __forceinline__ void rope_cs(double p, int j, int R, double theta, float *c, float *s) {
-    double inv_freq = pow(theta, -2.0 * (double)j / (double)R);
-    double ang = p * inv_freq;
-    *c = (float)cos(ang);
-    *s = (float)sin(ang);
+    const double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
+    const double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
+    const double kTwoOverPi = 0.6366197723675814;
+    const double inv_freq = pow(theta, -2.0 * (double)j / (double)R);
+    const double ang = p * inv_freq;
+    const double k = rint(ang * kTwoOverPi);
+    double r = fma(-k, kPio2Hi, ang);
+    r = fma(-k, kPio2Lo, r);
+    const double sr = sin(r), cr = cos(r);
+    switch (((long long)k) & 3) {
+        case 0: *c = (float)cr; *s = (float)sr; break;
+        case 1: *c = (float)-sr; *s = (float)cr; break;
+        case 2: *c = (float)-cr; *s = (float)-sr; break;
+        default: *c = (float)sr; *s = (float)-cr; break;
+    }
 }
 
 }  // namespace v4a

@@ -26,7 +26,8 @@
 
 namespace v4a {
 
-constexpr int kGroupsPerIter = 8;   // key groups of 16 in flight per wavefront
+constexpr int kGroupsPerIter = 4;   // key groups of 16 per load batch (two batches in flight)
+constexpr int kMaxKeysPerWG = 4 * 64 * 16;  // 4 wavefronts x at most 64 groups of 16 keys
 struct IndexerParams {
     const uint8_t *kc;   // key codes [B][cap][d/2]
     const uint8_t *ks;   // key scales [B][cap][d/32]
@@ -73,6 +74,7 @@ __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint3
 // so kGroupsPerIter * 1 KB per wavefront is in flight.
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
     __shared__ uint32_t lhist[kHistBins];
+    __shared__ __attribute__((aligned(16))) float sbuf[kMaxKeysPerWG];  // this workgroup's scores
     const int qi = blockIdx.y;
     const int b = qi / QP.Q;
     const int64_t n_vis = visible_keys(QP, qi);
@@ -119,23 +121,26 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     const int64_t kend = k0 + keys_per_wg < n_vis ? k0 + keys_per_wg : n_vis;
     uint32_t *hist = P.hist ? lhist : nullptr;
     const int64_t wbase = k0 + (int64_t)wv * P.groups_per_wave * 16;
-    for (int it = 0; it < P.groups_per_wave / kGroupsPerIter; it++) {
+    const int n_it = P.groups_per_wave / kGroupsPerIter;
+
+    // Double-buffered: the loads of iteration it+1 are issued before iteration it is computed.
+    // Lanes past the end read a clamped, valid key of this query and are masked afterwards.
+    auto load_iter = [&](int it, uint4 (&kd)[kGroupsPerIter], uint32_t (&ksc)[kGroupsPerIter]) {
         const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
-        if (base >= kend) break;  // uniform over the wavefront
-        uint4 kd[kGroupsPerIter];
-        uint32_t ksc[kGroupsPerIter];
 #pragma unroll
         for (int u = 0; u < kGroupsPerIter; u++) {
             int64_t key = base + 16 * u + col;
-            key = key < kend ? key : kend - 1;  // clamped: always a valid key of this query
+            key = key < kend ? key : kend - 1;
             const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16));
             kd[u] = make_uint4(v.x, v.y, v.z, v.w);
             ksc[u] = *(const uint32_t *)(ks + key * 4);
         }
+    };
+    auto compute_iter = [&](int it, const uint4 (&kd)[kGroupsPerIter], const uint32_t (&ksc)[kGroupsPerIter]) {
+        const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
+        float c[kGroupsPerIter];
 #pragma unroll
         for (int u = 0; u < kGroupsPerIter; u++) {
-            const int64_t gbase = base + 16 * u;
-            if (gbase >= kend) break;  // uniform
             const v8i kb = v8i{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
             const int sc = (int)((ksc[u] >> (8 * grp)) & 0xFFu);
             v4f acc[4];
@@ -143,18 +148,78 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
             for (int g = 0; g < 4; g++)
                 acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
                                                                           qscale[g], 0, sc);
-            float c = 0.0f;
+            // ReLU on the bit pattern: a finite float is negative (or -0) exactly when its bits
+            // read as a negative int, so max(int bits, 0) gives s for s > 0 and +0 otherwise
+            float cu = 0.0f;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float r = acc[g][i] > 0.0f ? acc[g][i] : 0.0f;
-                    c = fmaf(wt[g][i], r, c);
+                    const float si = acc[g][i];  // a scalar copy: bit casts read whole objects
+                    const float r = __builtin_bit_cast(float, max(__builtin_bit_cast(int, si), 0));
+                    cu = fmaf(wt[g][i], r, cu);
                 }
             }
-            const float c1 = __shfl_down(c, 16), c2 = __shfl_down(c, 32), c3 = __shfl_down(c, 48);
-            const int64_t key = gbase + col;
-            if (grp == 0 && key < kend) emit_score(P, qi, key, ((c + c1) + c2) + c3, hist);
+            c[u] = cu;
+        }
+        // the four chains of each key sit in lanes col, col+16, col+32, col+48
+        float c1[kGroupsPerIter], c2[kGroupsPerIter], c3[kGroupsPerIter];
+#pragma unroll
+        for (int u = 0; u < kGroupsPerIter; u++) {
+            c1[u] = __shfl_down(c[u], 16);
+            c2[u] = __shfl_down(c[u], 32);
+            c3[u] = __shfl_down(c[u], 48);
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int u = 0; u < kGroupsPerIter; u++) {
+                float sc = ((c[u] + c1[u]) + c2[u]) + c3[u];
+                if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
+                sbuf[base - k0 + 16 * u + col] = sc;  // slots past kend are never read
+            }
+        }
+    };
+    uint4 kdA[kGroupsPerIter], kdB[kGroupsPerIter];
+    uint32_t kscA[kGroupsPerIter], kscB[kGroupsPerIter];
+    if (wbase < kend) load_iter(0, kdA, kscA);
+    for (int it = 0; it < n_it; it += 2) {
+        if (wbase + (int64_t)it * kGroupsPerIter * 16 >= kend) break;  // uniform over the wavefront
+        const bool more1 = it + 1 < n_it && wbase + (int64_t)(it + 1) * kGroupsPerIter * 16 < kend;
+        if (more1) load_iter(it + 1, kdB, kscB);
+        compute_iter(it, kdA, kscA);
+        if (!more1) break;
+        const bool more2 = it + 2 < n_it && wbase + (int64_t)(it + 2) * kGroupsPerIter * 16 < kend;
+        if (more2) load_iter(it + 2, kdA, kscA);
+        compute_iter(it + 1, kdB, kscB);
+    }
+    // the streaming loop touched only registers and LDS; now the scores leave in 16-byte stores
+    // and the histogram is counted from LDS
+    __syncthreads();
+    const int n_here = (int)(kend - k0);
+    float *g_sc = P.scores ? P.scores + (int64_t)qi * P.n_max + k0 : nullptr;
+    uint32_t *g_key = P.score_keys ? P.score_keys + (int64_t)qi * P.n_max + k0 : nullptr;
+    for (int i0 = 4 * threadIdx.x; i0 < n_here; i0 += 4 * 256) {
+        const float4 v = *(const float4 *)(sbuf + i0);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        uint32_t kk[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) kk[j] = score_key(vv[j]);
+        if (i0 + 4 <= n_here && ((k0 + (int64_t)qi * P.n_max) & 3) == 0) {
+            if (g_sc) *(float4 *)(g_sc + i0) = v;
+            if (g_key) *(uint4 *)(g_key + i0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                if (i0 + j < n_here) {
+                    if (g_sc) g_sc[i0 + j] = vv[j];
+                    if (g_key) g_key[i0 + j] = kk[j];
+                }
+            }
+        }
+        if (hist) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                if (i0 + j < n_here) atomicAdd(&lhist[kk[j] >> 20], 1u);
         }
     }
     flush_hist(P, qi, lhist);
@@ -235,9 +300,9 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
     if (mx) {
         // keys per workgroup: the largest power-of-two multiple of 512 that still gives at least
-        // 512 workgroups (two per CU); it changes only the work split, never a result
-        int gpw = kGroupsPerIter;  // keys per workgroup = 4 wavefronts * gpw groups * 16 keys
-        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 1024) gpw *= 2;
+        // 1024 workgroups (four per CU); it changes only the work split, never a result
+        int gpw = 2 * kGroupsPerIter;  // keys per workgroup = 4 wavefronts * gpw groups * 16 keys
+        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 2048) gpw *= 2;
         P.groups_per_wave = gpw;
         const int64_t kpw = (int64_t)64 * gpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
