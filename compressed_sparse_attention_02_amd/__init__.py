@@ -42,6 +42,22 @@ class c_idx(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("cap", ctypes.c_int64)]
 
 
+class c_prefill_args(ctypes.Structure):
+    P = ctypes.c_void_p
+    _fields_ = [("tok0", ctypes.c_int64), ("C", ctypes.c_int32), ("n_prev", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("in_t", ctypes.c_int), ("G", ctypes.c_int32),
+                ("kv_a", P), ("kv_b", P), ("gate_a", P), ("gate_b", P), ("bias_a", P), ("bias_b", P),
+                ("apply_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("kv", ctypes.POINTER(c_kv)), ("slot", ctypes.c_int32), ("idx_G", ctypes.c_int32),
+                ("idx_a", P), ("idx_b", P), ("idx_gate_a", P), ("idx_gate_b", P), ("idx_bias_a", P),
+                ("idx_bias_b", P), ("keys", ctypes.POINTER(c_idx)), ("q_idx", ctypes.POINTER(c_idx)),
+                ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
+                ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("sink", P), ("softmax_scale", ctypes.c_float),
+                ("out_rope_inverse", ctypes.c_int32), ("out", P), ("out_t", ctypes.c_int)]
+
+
+V4A_LAYER_CSA, V4A_LAYER_HCA = 0, 1
+
 _lib = None
 
 
@@ -73,6 +89,11 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        PAP = ctypes.POINTER(c_prefill_args)
+        L.v4a_prefill_chunk.argtypes = [ctypes.c_int, PAP, P, SZ, P]
+        L.v4a_prefill_chunk.restype = ctypes.c_int
+        L.v4a_prefill_workspace.argtypes = [ctypes.c_int, PAP]
+        L.v4a_prefill_workspace.restype = SZ
         L.v4a_indexer_topk_workspace.argtypes = [I32, I32, I64, I32]
         L.v4a_indexer_topk_workspace.restype = SZ
         L.v4a_decode_workspace.argtypes = [I32, I32, I32, I64, I32]
@@ -249,6 +270,49 @@ def v4a_decode_hca(q, kv: KV, n_entries, m: int, win, win_len, W: int, sink, q_p
         _ftype(win) if win is not None else V4A_BF16, _host_i32(win_len), W, _ptr(sink),
         _host_i64(q_pos), softmax_scale, int(out_rope_inverse), rope_theta, _ptr(out), _ftype(out),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class PrefillArgs:
+    """The arguments of one prefill chunk (v4a_prefill_args), holding every tensor it points to.
+
+    Streams hold n_prev + C rows (row r = position tok0 - n_prev + r); q is [C][H][D]; for CSA
+    the indexer streams, key cache, q_idx ([C*H_I] rows), w ([C][H_I]) and k are required.
+    """
+
+    def __init__(self, *, tok0: int, n_prev: int, m: int, kv_a, gate_a, bias_a, kv: KV, q, W: int, sink,
+                 softmax_scale: float, out, kv_b=None, gate_b=None, bias_b=None, slot: int = 0,
+                 apply_rope: bool = True, rope_theta: float = 10000.0, idx_a=None, idx_b=None,
+                 idx_gate_a=None, idx_gate_b=None, idx_bias_a=None, idx_bias_b=None, keys: Idx | None = None,
+                 q_idx: Idx | None = None, w=None, k: int = 0, out_rope_inverse: bool = True):
+        self._kv = kv.c()
+        self._keys = keys.c() if keys is not None else None
+        self._q_idx = q_idx.c() if q_idx is not None else None
+        self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b,
+                      idx_bias_a, idx_bias_b, w, q, sink, out, kv, keys, q_idx)
+        C, H = q.shape[0], q.shape[1]
+        H_I = (w.numel() // C) if (w is not None and C > 0) else 0
+        self.s = c_prefill_args(
+            tok0=tok0, C=C, n_prev=n_prev, m=m, in_t=_ftype(kv_a), G=gate_a.shape[-1],
+            kv_a=_ptr(kv_a), kv_b=_ptr(kv_b), gate_a=_ptr(gate_a), gate_b=_ptr(gate_b), bias_a=_ptr(bias_a),
+            bias_b=_ptr(bias_b), apply_rope=int(apply_rope), rope_theta=rope_theta,
+            kv=ctypes.pointer(self._kv), slot=slot,
+            idx_G=idx_gate_a.shape[-1] if idx_gate_a is not None else 0,
+            idx_a=_ptr(idx_a), idx_b=_ptr(idx_b), idx_gate_a=_ptr(idx_gate_a), idx_gate_b=_ptr(idx_gate_b),
+            idx_bias_a=_ptr(idx_bias_a), idx_bias_b=_ptr(idx_bias_b),
+            keys=ctypes.pointer(self._keys) if self._keys is not None else None,
+            q_idx=ctypes.pointer(self._q_idx) if self._q_idx is not None else None,
+            w=_ptr(w), H_I=H_I, k=k, q=_ptr(q), q_t=_ftype(q), H=H, W=W, sink=_ptr(sink),
+            softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out),
+            out_t=_ftype(out))
+
+
+def v4a_prefill_workspace(kind: int, args: PrefillArgs) -> int:
+    return int(lib().v4a_prefill_workspace(kind, ctypes.byref(args.s)))
+
+
+def v4a_prefill_chunk(kind: int, args: PrefillArgs, ws: torch.Tensor | None = None, stream=None):
+    _check(lib().v4a_prefill_chunk(kind, ctypes.byref(args.s), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

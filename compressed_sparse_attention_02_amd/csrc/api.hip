@@ -96,7 +96,7 @@ static TopkWs topk_layout(int B, int Q, int64_t n_max, int k) {
     L.keys = off;
     off = round_up(off + BQ * (size_t)n_max * 4, 256);
     L.hist = off;
-    off = round_up(off + BQ * kHistCopies * kHistBins * 4, 256);
+    off = round_up(off + BQ * hist_copies((int64_t)BQ) * kHistBins * 4, 256);
     L.list = off;
     off = round_up(off + BQ * slices * kSelSlice * 8, 256);
     L.counts = off;
@@ -199,7 +199,7 @@ v4a_status v4a_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx *out, 
     return hip_status(launch_quantize_mxfp4(x, rows, *out, row0, (hipStream_t)stream), "v4a_quantize_mxfp4");
 }
 
-static v4a_status compress_common(CompressArgs &a, const float *norm_w, void *stream) {
+static v4a_status compress_check(CompressArgs &a, const float *norm_w) {
     if (norm_w) return fail(V4A_EUNSUPPORTED, "norm_w must be NULL");
     if (a.D != 32 && a.D != 64 && a.D != 128 && a.D != 256 && a.D != 512)
         return fail(V4A_EUNSUPPORTED, "D=%d: need 32, 64, 128, 256 or 512", a.D);
@@ -237,6 +237,12 @@ static v4a_status compress_common(CompressArgs &a, const float *norm_w, void *st
         a.rope = false;
         a.R = 0;
     }
+    return V4A_OK;
+}
+
+static v4a_status compress_common(CompressArgs &a, const float *norm_w, void *stream) {
+    v4a_status st = compress_check(a, norm_w);
+    if (st != V4A_OK) return st;
     g_err.clear();
     return hip_status(launch_compress(a, (hipStream_t)stream), "compress");
 }
@@ -309,6 +315,49 @@ size_t v4a_indexer_topk_workspace(int32_t B, int32_t Q, int64_t n_max, int32_t k
     return topk_layout(B, Q, n_max, k).total;
 }
 
+}  // extern "C"
+
+namespace v4a {
+
+// Launches of the indexer + top-k call once every argument has been checked.
+static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, int64_t n_max, const v4a_idx *q_idx,
+                                      const float *w, int32_t B, int32_t Q, int32_t H_I, int32_t k, int32_t *out_idx,
+                                      void *ws, hipStream_t s) {
+    const TopkWs L = topk_layout(B, Q, n_max, k);
+    char *base = (char *)ws;
+    const size_t BQ = (size_t)B * Q;
+    hipError_t e = launch_zero(base + L.hist, BQ * hist_copies((int64_t)BQ) * kHistBins * 4, s);
+    if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
+    IndexerArgs ia{};
+    ia.keys = keys;
+    ia.q = q_idx;
+    ia.w = w;
+    ia.B = B;
+    ia.Q = Q;
+    ia.H_I = H_I;
+    ia.n_max = n_max;
+    ia.score_keys = (uint32_t *)(base + L.keys);
+    ia.hist = (uint32_t *)(base + L.hist);
+    ia.hist_copies = hist_copies((int64_t)BQ);
+    if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
+    SelectArgs sa{};
+    sa.score_keys = ia.score_keys;
+    sa.hist = ia.hist;
+    sa.hist_copies = ia.hist_copies;
+    sa.n_max = n_max;
+    sa.BQ = (int)BQ;
+    sa.k = k;
+    sa.list = (uint32_t *)(base + L.list);
+    sa.counts = (uint32_t *)(base + L.counts);
+    sa.meta = (int32_t *)(base + L.meta);
+    sa.out = out_idx;
+    return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
+}
+
+}  // namespace v4a
+
+extern "C" {
+
 v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
                             const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos, int32_t k,
                             int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
@@ -324,33 +373,7 @@ v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32
     if (!ws || ws_bytes < L.total || !aligned(ws, 256))
         return fail(V4A_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, ws_bytes);
     g_err.clear();
-    hipStream_t s = (hipStream_t)stream;
-    char *base = (char *)ws;
-    const size_t BQ = (size_t)B * Q;
-    hipError_t e = launch_zero(base + L.hist, BQ * kHistCopies * kHistBins * 4, s);
-    if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
-    IndexerArgs ia{};
-    ia.keys = keys;
-    ia.q = q_idx;
-    ia.w = w;
-    ia.B = B;
-    ia.Q = Q;
-    ia.H_I = H_I;
-    ia.n_max = n_max;
-    ia.score_keys = (uint32_t *)(base + L.keys);
-    ia.hist = (uint32_t *)(base + L.hist);
-    if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
-    SelectArgs sa{};
-    sa.score_keys = ia.score_keys;
-    sa.hist = ia.hist;
-    sa.n_max = n_max;
-    sa.BQ = (int)BQ;
-    sa.k = k;
-    sa.list = (uint32_t *)(base + L.list);
-    sa.counts = (uint32_t *)(base + L.counts);
-    sa.meta = (int32_t *)(base + L.meta);
-    sa.out = out_idx;
-    return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
+    return indexer_topk_launch(keys, qp, n_max, q_idx, w, B, Q, H_I, k, out_idx, ws, (hipStream_t)stream);
 }
 
 v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
@@ -472,6 +495,7 @@ v4a_status v4a_decode_csa(const void *q, v4a_float q_t, int32_t B, int32_t H, co
     a.B = B;
     a.H = H;
     a.kv = kv;
+    a.kv_bstride = kv->cap;
     a.topk = topk_idx;
     a.k = k;
     a.win = win;
@@ -512,6 +536,7 @@ v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32_t H, co
     a.B = B;
     a.H = H;
     a.kv = kv;
+    a.kv_bstride = kv->cap;
     a.topk = nullptr;
     a.k = 0;
     a.win = win;
@@ -522,6 +547,227 @@ v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32_t H, co
     a.theta = rope_theta;
     a.out = out;
     return decode_common(a, sq, win_len, q_pos, q_t, win_t, out_t, ws, ws_bytes, stream, "v4a_decode_hca");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------- prefill ---------
+namespace v4a {
+
+struct PrefillPlan {
+    bool csa;
+    int64_t first, n_new, n_total;   // entries written, entries in the cache afterwards
+    CompressArgs ckv, cidx;
+    v4a_kv kv;                       // the sequence's slot (record rows 0 .. cap-1)
+    v4a_idx keys;
+    QueryPos qp;
+    size_t idx_bytes, topk_bytes, ws_total;
+};
+
+static const char *ptr_at(const void *p, int64_t elems, size_t esz) {
+    return p ? (const char *)p + elems * (int64_t)esz : nullptr;
+}
+
+// Checks every argument of a prefill chunk and lays out its launches; launches nothing.
+static v4a_status prefill_plan(v4a_layer kind, const v4a_prefill_args *a, PrefillPlan &pl) {
+    if (!a) return fail(V4A_EINVAL, "v4a_prefill_chunk: args is NULL");
+    if (kind != V4A_LAYER_CSA && kind != V4A_LAYER_HCA) return fail(V4A_EINVAL, "v4a_prefill_chunk: kind=%d", (int)kind);
+    pl = PrefillPlan{};
+    pl.csa = kind == V4A_LAYER_CSA;
+    v4a_status st = check_kv(a->kv, "kv");
+    if (st != V4A_OK) return st;
+    const int D = a->kv->D;
+    if (a->C < 0 || a->C > 65535) return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: C=%d not in [0, 65535]", a->C);
+    if (a->tok0 < 0) return fail(V4A_EINVAL, "v4a_prefill_chunk: tok0 < 0");
+    if (a->m < 1 || a->m > 128) return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: m=%d not in [1, 128]", a->m);
+    if (a->tok0 % a->m != 0) return fail(V4A_EINVAL, "v4a_prefill_chunk: tok0 must be a multiple of m");
+    if (a->W < 0 || a->W > 128) return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: W=%d not in [0, 128]", a->W);
+    if (a->n_prev < 0 || a->n_prev > a->tok0) return fail(V4A_EINVAL, "v4a_prefill_chunk: n_prev not in [0, tok0]");
+    int64_t need_prev = a->W > 0 ? (a->tok0 < a->W - 1 ? a->tok0 : a->W - 1) : 0;
+    if (pl.csa && a->tok0 > 0 && need_prev < a->m) need_prev = a->m;
+    if (a->n_prev < need_prev)
+        return fail(V4A_EINVAL, "v4a_prefill_chunk: n_prev=%d, the window and blocks need %lld rows before tok0",
+                    a->n_prev, (long long)need_prev);
+    if (a->slot < 0) return fail(V4A_EINVAL, "v4a_prefill_chunk: slot < 0");
+    if (a->in_t != V4A_F32 && a->in_t != V4A_BF16) return fail(V4A_EINVAL, "v4a_prefill_chunk: in_t");
+    if ((a->q_t != V4A_F32 && a->q_t != V4A_BF16) || (a->out_t != V4A_F32 && a->out_t != V4A_BF16))
+        return fail(V4A_EINVAL, "v4a_prefill_chunk: q_t / out_t");
+    if (a->H < 1 || a->H > 128) return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: H=%d not in [1, 128]", a->H);
+    if (!a->q || !a->out || !a->sink || !a->kv_a) return fail(V4A_EINVAL, "v4a_prefill_chunk: q, out, sink and kv_a are required");
+    if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->kv_a, 16))
+        return fail(V4A_EINVAL, "v4a_prefill_chunk: q, out and kv_a must be 16-byte aligned");
+    if (D % 2 != 0 || (a->out_rope_inverse && a->kv->R < 2))
+        return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: odd D or no RoPE dims");
+    pl.first = a->tok0 / a->m;
+    pl.n_total = (a->tok0 + a->C) / a->m;
+    pl.n_new = pl.n_total - pl.first;
+    if (pl.n_total > a->kv->cap) return fail(V4A_EINVAL, "v4a_prefill_chunk: %lld entries exceed kv->cap", (long long)pl.n_total);
+    const size_t esz = a->in_t == V4A_BF16 ? 2 : 4;
+    // the compressor reads from row n_prev - mneed: CSA also needs the B-block before tok0
+    const int mneed = (pl.csa && a->tok0 > 0) ? a->m : 0;
+    const int64_t r0 = a->n_prev - mneed;
+    CompressArgs &c = pl.ckv;
+    c.n_streams = pl.csa ? 2 : 1;
+    c.x[0] = ptr_at(a->kv_a, r0 * D, esz);
+    c.x[1] = pl.csa ? ptr_at(a->kv_b, r0 * D, esz) : c.x[0];
+    c.gate[0] = (const float *)ptr_at(a->gate_a, r0 * a->G, 4);
+    c.gate[1] = pl.csa ? (const float *)ptr_at(a->gate_b, r0 * a->G, 4) : c.gate[0];
+    c.bias[0] = a->bias_a;
+    c.bias[1] = pl.csa ? a->bias_b : a->bias_a;
+    c.bf16_in = a->in_t == V4A_BF16;
+    c.D = D;
+    c.G = a->G;
+    c.m = a->m;
+    c.tok0 = a->tok0 - mneed;
+    c.n_tok = mneed + a->C;
+    c.first_entry = pl.first;
+    c.n_entries = pl.n_new;
+    c.rope = a->apply_rope != 0;
+    c.theta = a->rope_theta;
+    c.kv = a->kv;
+    c.b0 = a->slot;
+    c.n_seq = 1;
+    if ((st = compress_check(c, nullptr)) != V4A_OK) return st;
+    if ((int64_t)(a->slot + 1) * a->kv->cap < 0) return fail(V4A_EINVAL, "v4a_prefill_chunk: slot");
+    pl.kv = *a->kv;
+    {
+        const int64_t base = (int64_t)a->slot * a->kv->cap;
+        const int Dn = D - a->kv->R;
+        if (a->kv->fmt == V4A_KV_FP8_BF16) {
+            pl.kv.nope = (char *)a->kv->nope + base * Dn;
+            pl.kv.rope = (char *)a->kv->rope + base * a->kv->R * 2;
+            pl.kv.scale = a->kv->scale + base;
+        } else {
+            pl.kv.nope = (char *)a->kv->nope + base * D * 4;
+        }
+    }
+    AttnArgs probe{};
+    probe.kv = &pl.kv;
+    probe.q_bf16 = a->q_t == V4A_BF16;
+    probe.win_bf16 = a->in_t == V4A_BF16;
+    probe.H = a->H;
+    probe.D = D;
+    probe.R = a->kv->R;
+    const int64_t ent_max = pl.csa ? a->k : pl.n_total;
+    if (!attn_uses_mfma(probe) && ent_max + a->W > 8192 + 2048)
+        return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: this format/shape uses the fp32 kernel, limited to %d keys",
+                    8192 + 2048);
+    pl.ws_total = 0;
+    if (pl.csa) {
+        if (!a->kv_b) return fail(V4A_EINVAL, "v4a_prefill_chunk: kv_b is required for CSA");
+        if ((st = check_idx(a->keys, "keys")) != V4A_OK) return st;
+        if (a->k < 1 || a->k > 2048) return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: k=%d not in [1, 2048]", a->k);
+        const int d = a->keys->d;
+        CompressArgs &ci = pl.cidx;
+        ci.n_streams = 2;
+        ci.x[0] = ptr_at(a->idx_a, r0 * d, esz);
+        ci.x[1] = ptr_at(a->idx_b, r0 * d, esz);
+        ci.gate[0] = (const float *)ptr_at(a->idx_gate_a, r0 * a->idx_G, 4);
+        ci.gate[1] = (const float *)ptr_at(a->idx_gate_b, r0 * a->idx_G, 4);
+        ci.bias[0] = a->idx_bias_a;
+        ci.bias[1] = a->idx_bias_b;
+        ci.bf16_in = c.bf16_in;
+        ci.D = d;
+        ci.G = a->idx_G;
+        ci.m = a->m;
+        ci.tok0 = c.tok0;
+        ci.n_tok = c.n_tok;
+        ci.first_entry = pl.first;
+        ci.n_entries = pl.n_new;
+        ci.idx = a->keys;
+        ci.b0 = a->slot;
+        ci.n_seq = 1;
+        if ((st = compress_check(ci, nullptr)) != V4A_OK) return st;
+        pl.keys = *a->keys;
+        const int64_t base = (int64_t)a->slot * a->keys->cap;
+        if (a->keys->fmt == V4A_IDX_MXFP4) {
+            pl.keys.codes = (char *)a->keys->codes + base * (d / 2);
+            pl.keys.scales = a->keys->scales + base * (d / 32);
+        } else {
+            pl.keys.codes = (char *)a->keys->codes + base * d * 4;
+        }
+        const int64_t n_ent1 = pl.n_total;
+        const int64_t pos0 = a->tok0;
+        if ((st = check_indexer_args(&pl.keys, &n_ent1, a->m, a->q_idx, a->w, 1, a->C > 0 ? a->C : 1, a->H_I, &pos0)) != V4A_OK)
+            return st;
+        if (pl.n_total > (int64_t)1024 * kSelSlice)
+            return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: more than %d entries", 1024 * kSelSlice);
+        memset(&pl.qp, 0, sizeof pl.qp);
+        pl.qp.mode = 1;
+        pl.qp.Q = a->C;
+        pl.qp.m = a->m;
+        pl.qp.pos[0] = a->tok0;
+        pl.qp.n_ent[0] = pl.n_total;
+        pl.idx_bytes = round_up((size_t)a->C * a->k * 4, 256);
+        pl.topk_bytes = topk_layout(1, a->C, pl.n_total, a->k).total;
+        pl.ws_total = pl.idx_bytes + pl.topk_bytes;
+    }
+    return V4A_OK;
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *args) {
+    PrefillPlan pl;
+    if (prefill_plan(kind, args, pl) != V4A_OK) return 0;
+    return pl.ws_total;
+}
+
+v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *a, void *ws, size_t ws_bytes, void *stream) {
+    PrefillPlan pl;
+    v4a_status st = prefill_plan(kind, a, pl);
+    if (st != V4A_OK) return st;
+    if (pl.ws_total > 0 && (!ws || ws_bytes < pl.ws_total || !aligned(ws, 256)))
+        return fail(V4A_EWORKSPACE, "v4a_prefill_chunk: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    pl.ws_total, ws_bytes);
+    g_err.clear();
+    if (a->C == 0) return V4A_OK;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_compress(pl.ckv, s);
+    if (e != hipSuccess) return hip_status(e, "v4a_prefill_chunk: compress");
+    int32_t *sel = nullptr;
+    if (pl.csa) {
+        if ((e = launch_compress(pl.cidx, s)) != hipSuccess) return hip_status(e, "v4a_prefill_chunk: compress keys");
+        sel = (int32_t *)ws;
+        st = indexer_topk_launch(&pl.keys, pl.qp, pl.n_total, a->q_idx, a->w, 1, a->C, a->H_I, a->k, sel,
+                                 (char *)ws + pl.idx_bytes, s);
+        if (st != V4A_OK) return st;
+    }
+    AttnArgs at{};
+    at.q = a->q;
+    at.q_bf16 = a->q_t == V4A_BF16;
+    at.B = a->C;
+    at.H = a->H;
+    at.D = pl.kv.D;
+    at.R = pl.kv.R;
+    at.kv = &pl.kv;
+    at.kv_bstride = 0;
+    at.topk = sel;
+    at.k = pl.csa ? a->k : 0;
+    at.win = a->kv_a;
+    at.win_bf16 = a->in_t == V4A_BF16;
+    at.W = a->W;
+    at.sink = a->sink;
+    at.scale = a->softmax_scale;
+    at.rope_inv = a->out_rope_inverse != 0;
+    at.theta = a->rope_theta;
+    at.out = a->out;
+    at.out_bf16 = a->out_t == V4A_BF16;
+    at.partial = nullptr;
+    at.target_splits = 1;
+    at.split_cap = 1;
+    SeqInfo sq;
+    memset(&sq, 0, sizeof sq);
+    sq.mode = 1;
+    sq.tok0 = a->tok0;
+    sq.n_prev = a->n_prev;
+    sq.W = a->W;
+    sq.m = a->m;
+    sq.fixed_ent = pl.csa ? a->k : 0;
+    sq.n_total = pl.n_total;
+    return hip_status(launch_attention(at, sq, s), "v4a_prefill_chunk: attention");
 }
 
 }  // extern "C"

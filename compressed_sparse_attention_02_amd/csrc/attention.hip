@@ -48,9 +48,10 @@ struct AttnParams {
     const uint16_t *rope;    // [B][cap][R]
     const float *kscale;     // [B][cap]
     int64_t cap;
+    int64_t kv_bstride;      // record rows between consecutive queries' caches (cap, or 0)
     const int32_t *topk;     // [B][k] or NULL
     int k;
-    const void *win;         // [B][W][D]
+    const void *win;         // [B][W][D] (decode) or the prefill stream [n_prev + C][D]
     bool win_bf16;
     int W;
     const float *sink;       // [H]
@@ -119,7 +120,7 @@ __device__ __forceinline__ void finish_head(const AttnParams &P, const SeqInfo &
     if (P.rope_inv && d0 >= Dn) {
 #pragma unroll
         for (int v = 0; v < NV; v += 2) {
-            const float2 r = rope_unrotate((double)Sq.q_pos[b], (d0 + v - Dn) / 2, P.R, P.theta, o[v], o[v + 1]);
+            const float2 r = rope_unrotate((double)sq_pos(Sq, b), (d0 + v - Dn) / 2, P.R, P.theta, o[v], o[v + 1]);
             o[v] = r.x;
             o[v + 1] = r.y;
         }
@@ -147,7 +148,8 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
     }
     const int b = p / P.S, split = p % P.S;
     if (b >= P.B) return;
-    const int n_ent = Sq.n_ent[b], n_keys = n_ent + Sq.win_len[b];
+    const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
+    const int64_t wrow0 = sq_win_row0(Sq, b, P.W);
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
     if (split >= splits) return;
@@ -199,7 +201,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                     const int kidx = tb + 4 * kg + j;
                     int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
                     valid[j] = e >= 0 && e < P.cap;
-                    row[j] = (int64_t)b * P.cap + (valid[j] ? e : 0);
+                    row[j] = (int64_t)b * P.kv_bstride + (valid[j] ? e : 0);
                 }
                 if (dim < Dn) {
                     uint2 c[4];
@@ -229,7 +231,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                 for (int j = 0; j < 4; j++) {
                     const int wtok = tb + 4 * kg + j - n_ent;
                     valid[j] = tb + 4 * kg + j < kb1;
-                    row[j] = (int64_t)b * P.W + (valid[j] ? wtok : 0);
+                    row[j] = wrow0 + (valid[j] ? wtok : 0);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
@@ -251,7 +253,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                     if (kidx < n_ent) {
                         int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
                         if (e >= 0 && e < P.cap) {
-                            const int64_t row = (int64_t)b * P.cap + e;
+                            const int64_t row = (int64_t)b * P.kv_bstride + e;
                             valid[j] = true;
                             scl = P.kscale[row];
                             if (dim < Dn) {
@@ -267,7 +269,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                     } else if (kidx < kb1) {
                         valid[j] = true;
                         scl = 1.0f;
-                        v[j] = *(const uint4 *)((const uint16_t *)P.win + ((int64_t)b * P.W + (kidx - n_ent)) * D + dim);
+                        v[j] = *(const uint4 *)((const uint16_t *)P.win + (wrow0 + (kidx - n_ent)) * D + dim);
                     }
                     if (seg == 0) {
                         ksc[4 * kg + j] = scl;
@@ -369,8 +371,8 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 #pragma unroll
             for (int dt = Dn / 16; dt < NDT; dt++) {
                 const int j = (16 * dt + 4 * grp - Dn) / 2;
-                const float2 r0 = rope_unrotate((double)Sq.q_pos[b], j, R, P.theta, O[dt][0], O[dt][1]);
-                const float2 r1 = rope_unrotate((double)Sq.q_pos[b], j + 1, R, P.theta, O[dt][2], O[dt][3]);
+                const float2 r0 = rope_unrotate((double)sq_pos(Sq, b), j, R, P.theta, O[dt][0], O[dt][1]);
+                const float2 r1 = rope_unrotate((double)sq_pos(Sq, b), j + 1, R, P.theta, O[dt][2], O[dt][3]);
                 O[dt] = v4f{r0.x, r0.y, r1.x, r1.y};
             }
         }
@@ -396,7 +398,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 template <int NV>
 __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int n_keys = Sq.n_ent[b] + Sq.win_len[b];
+    const int n_keys = sq_n_ent(Sq, b) + sq_win_len(Sq, b);
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
     if (splits == 1) return;
@@ -439,10 +441,11 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
 // scores in LDS, fp32 arithmetic throughout (no split).
 constexpr int kF32MaxKeys = 8192 + 2048;
 
-__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_t e, int wtok, int d) {
+__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_t wrow0, int64_t e, int wtok,
+                                              int d) {
     const int Dn = P.D - P.R;
     if (e >= 0) {
-        const int64_t row = (int64_t)b * P.cap + e;
+        const int64_t row = (int64_t)b * P.kv_bstride + e;
         if (P.fmt == V4A_KV_F32) return ((const float *)P.nope)[row * P.D + d];
         if (d < Dn) {
             const uint8_t c = P.nope[row * Dn + d];
@@ -452,7 +455,7 @@ __device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_
         }
         return bf16_to_f32(P.rope[row * P.R + (d - Dn)]);
     }
-    const int64_t wi = ((int64_t)b * P.W + wtok) * P.D + d;
+    const int64_t wi = (wrow0 + wtok) * P.D + d;
     return P.win_bf16 ? bf16_to_f32(((const uint16_t *)P.win)[wi]) : ((const float *)P.win)[wi];
 }
 
@@ -462,7 +465,8 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
     __shared__ float red[256];
     __shared__ float osh[512];
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-    const int n_ent = Sq.n_ent[b], n_keys = n_ent + Sq.win_len[b];
+    const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
+    const int64_t wrow0 = sq_win_row0(Sq, b, P.W);
     const int D = P.D;
     for (int d = t; d < D; d += 256) {
         const int64_t qi = ((int64_t)b * P.H + h) * D + d;
@@ -483,7 +487,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
         float s = -INFINITY;
         if (e >= 0 || wtok >= 0) {
             float acc = 0.0f;
-            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, e, wtok, d), acc);
+            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, wrow0, e, wtok, d), acc);
             s = scale * acc;
         }
         sc[j] = s;
@@ -524,7 +528,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
                 wtok = j - n_ent;
             }
             if (e < 0 && wtok < 0) continue;
-            acc = fmaf(sc[j], load_key_dim(P, b, e, wtok, d), acc);
+            acc = fmaf(sc[j], load_key_dim(P, b, wrow0, e, wtok, d), acc);
         }
         osh[d] = den > 0.0f ? acc / den : 0.0f;
     }
@@ -534,7 +538,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
         float o[2] = {osh[d], osh[d + 1]};
         if (P.rope_inv && d >= Dn) {
             float c, s;
-            rope_cs((double)Sq.q_pos[b], (d - Dn) / 2, P.R, P.theta, &c, &s);
+            rope_cs((double)sq_pos(Sq, b), (d - Dn) / 2, P.R, P.theta, &c, &s);
             const float x = o[0], y = o[1];
             o[0] = x * c + y * s;
             o[1] = -x * s + y * c;
@@ -572,6 +576,7 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     P.rope = (const uint16_t *)a.kv->rope;
     P.kscale = a.kv->scale;
     P.cap = a.kv->cap;
+    P.kv_bstride = a.kv_bstride;
     P.topk = a.topk;
     P.k = a.k;
     P.win = a.win;

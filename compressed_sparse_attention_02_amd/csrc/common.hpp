@@ -117,6 +117,10 @@ constexpr int kMaxSeq = 128;
 constexpr int kHistBins = 4096;   // top-12-bit histogram of the orderable score keys
 constexpr int kHistCopies = 8;    // copies of each query's histogram (contention spreading)
 
+// Histogram copies per query: many workgroups score one decode query and spread their adds
+// over kHistCopies copies; a prefill chunk has few workgroups per query and keeps one copy.
+inline int hist_copies(int64_t BQ) { return BQ <= 32 ? kHistCopies : 1; }
+
 struct QueryPos {
     int mode;  // 0: pos[qi] per query (B*Q <= kMaxSeq); 1: pos[b] + j for query j of sequence b
     int Q, m;
@@ -133,11 +137,39 @@ __host__ __device__ __forceinline__ int64_t visible_keys(const QueryPos &P, int 
     return v < 0 ? 0 : v;
 }
 
+// The queries an attention launch serves.  Mode 0 (decode): query b is the newest token of
+// sequence b, described by the arrays.  Mode 1 (prefill): query b is the token at tok0 + b of
+// one sequence; its window is the W stream rows ending at itself, read from a buffer whose row
+// 0 holds position tok0 - n_prev; it attends over fixed_ent top-k entries (CSA) or, when
+// fixed_ent is 0, over its visible prefix of the n_total cached entries (ratio m).
 struct SeqInfo {
+    int mode;
+    int64_t tok0;
+    int n_prev, W, m, fixed_ent;
+    int64_t n_total;
     int32_t n_ent[kMaxSeq];    // entry keys of sequence b (k for CSA, visible entries for HCA)
     int32_t win_len[kMaxSeq];
     int64_t q_pos[kMaxSeq];
 };
+
+__host__ __device__ __forceinline__ int64_t sq_pos(const SeqInfo &S, int b) {
+    return S.mode ? S.tok0 + b : S.q_pos[b];
+}
+__host__ __device__ __forceinline__ int sq_win_len(const SeqInfo &S, int b) {
+    if (!S.mode) return S.win_len[b];
+    const int64_t t = S.tok0 + b;
+    return (int)(t + 1 < (int64_t)S.W ? t + 1 : (int64_t)S.W);
+}
+__host__ __device__ __forceinline__ int sq_n_ent(const SeqInfo &S, int b) {
+    if (!S.mode) return S.n_ent[b];
+    if (S.fixed_ent) return S.fixed_ent;
+    const int64_t v = (S.tok0 + b + 1) / S.m;
+    return (int)(v < S.n_total ? v : S.n_total);
+}
+// Row of the window buffer holding query b's oldest window token (W rows per sequence in mode 0).
+__host__ __device__ __forceinline__ int64_t sq_win_row0(const SeqInfo &S, int b, int W) {
+    return S.mode ? (int64_t)b + S.n_prev - sq_win_len(S, b) + 1 : (int64_t)b * W;
+}
 
 void set_error(const char *fmt, ...);
 
@@ -171,14 +203,16 @@ struct IndexerArgs {
     int64_t n_max;            // max visible keys over the queries (grid size)
     uint32_t *score_keys;     // [B*Q][n_max] orderable keys (or NULL)
     float *scores;            // [B*Q][n_max] raw scores (or NULL)
-    uint32_t *hist;           // [B*Q][kHistCopies][4096] histogram of the top 12 key bits (or NULL)
+    uint32_t *hist;           // [B*Q][copies][4096] histogram of the top 12 key bits (or NULL)
+    int hist_copies;
 };
 hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 struct SelectArgs {
     const uint32_t *score_keys;   // [BQ][n_max]
-    const uint32_t *hist;         // [BQ][kHistCopies][4096]
+    const uint32_t *hist;         // [BQ][copies][4096]
+    int hist_copies;
     int64_t n_max;
     int BQ, k;
     uint32_t *list;               // [BQ][slices * kSelSlice][2]: (index, score key) at or above the threshold bin
@@ -195,6 +229,7 @@ struct AttnArgs {
     bool q_bf16;
     int B, H, D, R;
     const v4a_kv *kv;
+    int64_t kv_bstride;       // record rows between consecutive queries' caches (cap, or 0)
     const int32_t *topk;      // [B][k] or NULL (dense)
     int k;
     const void *win;

@@ -42,7 +42,8 @@ struct IndexerParams {
     int64_t n_max;
     uint32_t *score_keys;  // [BQ][n_max] or NULL
     float *scores;         // [BQ][n_max] or NULL
-    uint32_t *hist;        // [BQ][kHistCopies][4096] or NULL
+    uint32_t *hist;        // [BQ][hist_copies][4096] or NULL
+    int hist_copies;
     int groups_per_wave;   // key groups of 16 per wavefront (a multiple of kGroupsPerIter)
 };
 
@@ -55,12 +56,12 @@ __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64
     if (lhist) atomicAdd(&lhist[key >> 20], 1u);
 }
 
-// Adds the workgroup's LDS histogram into copy (blockIdx.x % kHistCopies) of the query's
+// Adds the workgroup's LDS histogram into copy (blockIdx.x % hist_copies) of the query's
 // global histogram; spreading the copies keeps many workgroups off the same hot bins.
 __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint32_t *lhist) {
     __syncthreads();
     if (!P.hist) return;
-    uint32_t *gh = P.hist + ((int64_t)qi * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins;
+    uint32_t *gh = P.hist + ((int64_t)qi * P.hist_copies + (int)(blockIdx.x % (unsigned)P.hist_copies)) * kHistBins;
     for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
         uint32_t c = lhist[bin];
         if (c) atomicAdd(&gh[bin], c);
@@ -296,6 +297,7 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     P.score_keys = a.score_keys;
     P.scores = a.scores;
     P.hist = a.hist;
+    P.hist_copies = a.hist_copies > 0 ? a.hist_copies : 1;
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
     if (mx) {

@@ -33,7 +33,8 @@ int select_slices(int64_t n_max) {
 
 struct SelParams {
     const uint32_t *keys;
-    const uint32_t *hist;
+    const uint32_t *hist;    // [BQ][copies][4096]
+    int copies;
     int64_t n_max;
     int k, slices;
     uint32_t *list;
@@ -108,10 +109,12 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
         }
         return;
     }
-    const uint32_t *h = P.hist + (int64_t)qi * kHistCopies * kHistBins;
+    const uint32_t *h = P.hist + (int64_t)qi * P.copies * kHistBins;
+    const bool one_copy = P.copies == 1;
     int T;
     uint32_t above;
     top_down_threshold(kHistBins, k_eff, [&](int bin) {
+        if (one_copy) return h[bin];
         uint32_t c = 0;
 #pragma unroll
         for (int cp = 0; cp < kHistCopies; cp++) c += h[cp * kHistBins + bin];
@@ -289,6 +292,7 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
     SelParams P{};
     P.keys = a.score_keys;
     P.hist = a.hist;
+    P.copies = a.hist_copies > 0 ? a.hist_copies : 1;
     P.n_max = a.n_max;
     P.k = a.k;
     P.slices = select_slices(a.n_max);

@@ -223,6 +223,75 @@ V4A_API v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32
 /* Workspace for either decode call: n_keys_max = k (CSA) or max entries (HCA), plus W. */
 V4A_API size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_keys_max, int32_t W);
 
+/* -------------------------------------------------------------- a8: prefill chunk ----
+ * One chunk of C consecutive tokens of one sequence (positions tok0 .. tok0+C-1) through
+ * one attention layer of either kind, as C causal queries.  [cyqw] section 3.5 "KV cache
+ * layering" and [mewclaw] "State cache" / "Compressed cache": a sequence's state is the
+ * cache of compressed entries plus the raw tail (the 128-token window and the tokens of a
+ * block not yet complete); a chunk appends its complete blocks to the entry cache.
+ * The call
+ *   1. compresses every block that ends inside the chunk (entries tok0/m ..
+ *      (tok0+C)/m - 1) into the entry cache `kv` and, for CSA, the indexer key cache
+ *      `keys` (the compressors above; CSA entry tok0/m also reads the B-block before tok0);
+ *   2. CSA: selects, for every query t, the top-k of its visible entries (i < (t+1)/m)
+ *      exactly as v4a_indexer_topk does with Q = C and q_pos = tok0 + j;
+ *   3. attends, for query t = tok0 + j and every head, over its selected entries (CSA) or
+ *      all its visible entries (HCA) plus the window tokens max(0, t-W+1) .. t (rows of
+ *      stream kv_a), with the sink, exactly as the decode calls define it, and writes
+ *      out[j].
+ * Every query runs as one split, so its output equals the decode output at q_pos = t on
+ * the same cache within rounding (not bitwise: decode splits its keys).
+ * Stream rows: every stream holds n_prev + C rows; row r is position tok0 - n_prev + r.
+ * Requirements: tok0 a multiple of m; entries [0, tok0/m) already in the caches;
+ * n_prev <= tok0 and n_prev >= min(tok0, W-1); CSA with tok0 > 0 also n_prev >= m.
+ * Supports the shapes of the calls it composes, C <= 65535, and for CSA the MXFP4 or fp32
+ * indexer as in v4a_indexer_topk. */
+typedef enum { V4A_LAYER_CSA = 0, V4A_LAYER_HCA = 1 } v4a_layer;
+
+typedef struct {
+    int64_t tok0;            /* position of the chunk's first token                      */
+    int32_t C;               /* tokens (= queries) in the chunk                           */
+    int32_t n_prev;          /* stream rows before tok0 (the raw state)                   */
+    int32_t m;               /* compression ratio of this layer (CSA 4, HCA 128)          */
+    v4a_float in_t;          /* element type of every raw stream                          */
+    int32_t G;               /* gate width of the KV streams (1 or D)                     */
+    const void *kv_a;        /* [n_prev+C][D] (device) CSA stream A or the HCA stream; the
+                                window tokens are its rows                                */
+    const void *kv_b;        /* [n_prev+C][D] (device) CSA stream B; NULL for HCA         */
+    const float *gate_a;     /* [n_prev+C][G] f32 (device)                                */
+    const float *gate_b;     /* CSA only                                                  */
+    const float *bias_a;     /* [m][G] f32 (device)                                       */
+    const float *bias_b;     /* CSA only                                                  */
+    int32_t apply_rope;      /* rotate the entries' last R dims at their block start      */
+    float rope_theta;
+    const v4a_kv *kv;        /* entry cache; the sequence lives in slot `slot`            */
+    int32_t slot;
+    /* CSA indexer */
+    int32_t idx_G;           /* gate width of the indexer streams (1 or d)                */
+    const void *idx_a;       /* [n_prev+C][d] (device, in_t) indexer stream A             */
+    const void *idx_b;       /* [n_prev+C][d] indexer stream B                            */
+    const float *idx_gate_a, *idx_gate_b;   /* [n_prev+C][idx_G] f32 (device)             */
+    const float *idx_bias_a, *idx_bias_b;   /* [m][idx_G] f32 (device)                    */
+    const v4a_idx *keys;     /* indexer key cache, slot `slot`                            */
+    const v4a_idx *q_idx;    /* [C*H_I] rows (device): the chunk queries' indexer heads   */
+    const float *w;          /* [C][H_I] f32 (device)                                     */
+    int32_t H_I, k;
+    /* attention */
+    const void *q;           /* [C][H][D] (device, q_t)                                   */
+    v4a_float q_t;
+    int32_t H, W;
+    const float *sink;       /* [H] f32 (device)                                          */
+    float softmax_scale;
+    int32_t out_rope_inverse;
+    void *out;               /* [C][H][D] (device, out_t)                                 */
+    v4a_float out_t;
+} v4a_prefill_args;
+
+V4A_API v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *args, void *ws,
+                             size_t ws_bytes, void *stream);
+/* Workspace of v4a_prefill_chunk for these arguments (0 for HCA; 0 if they are invalid). */
+V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *args);
+
 /* ---------------------------------------------------------------------- utilities ---- */
 V4A_API const char *v4a_last_error(void);
 V4A_API const char *v4a_version(void);

@@ -302,3 +302,39 @@ def decode_hca(q, records, n_entries, window, sink, scale, *, q_pos, m=128, rope
     n_vis = visible_entries(n_entries, m, q_pos)
     return attend(q, records[:n_vis], window, sink, scale, rope_inverse=rope_inverse, R=R,
                   theta=theta, t_q=q_pos)
+
+
+def prefill_queries(kind, q, records, n_entries, stream, *, n_prev, tok0, queries, W, sink, scale,
+                    m, k=None, idx=None, rope_inverse=True, R=64, theta=10000.0):
+    """Attention of chosen queries of a prefill chunk, each exactly as a decode step.
+
+    The chunk's own compression is the compressor run on the chunk with its state (the
+    caller does it, so ``records`` / ``idx`` already hold the appended entries).  Query j
+    sits at t = tok0 + j: it sees the entries whose block ends at or before t, keeps its
+    top-k of them (CSA) or all of them (HCA), and its window is the raw rows t-W+1 .. t of
+    ``stream`` (row r of ``stream`` is position tok0 - n_prev + r).  "DeepSeek-V4 technical
+    report walkthrough" (cyqw.cn), section 3.5: the state cache keeps the window and the
+    incomplete block; the compressed entries are the classical cache.
+
+    q: [C][H][D] float64; idx (CSA): per-query dicts are made from the chunk arrays
+    dict(q_codes [C][H_I][..], q_scales, w [C][H_I], k_codes, k_scales) or
+    dict(q [C][H_I][d], w, keys).  Returns {j: out [H][D]} and, for CSA, {j: top-k}.
+    """
+    outs, sels = {}, {}
+    row0 = tok0 - n_prev
+    for j in queries:
+        t = tok0 + int(j)
+        lo = max(0, t - W + 1)
+        window = stream[lo - row0:t - row0 + 1] if W > 0 else None
+        if kind == "csa":
+            if "k_codes" in idx:
+                qi = dict(q_codes=idx["q_codes"][j], q_scales=idx["q_scales"][j], w=idx["w"][j],
+                          k_codes=idx["k_codes"], k_scales=idx["k_scales"])
+            else:
+                qi = dict(q=idx["q"][j], w=idx["w"][j], keys=idx["keys"])
+            outs[j], sels[j] = decode_csa(q[j], records, n_entries, k, window, sink, scale, q_pos=t,
+                                          m=m, idx=qi, rope_inverse=rope_inverse, R=R, theta=theta)
+        else:
+            outs[j] = decode_hca(q[j], records, n_entries, window, sink, scale, q_pos=t, m=m,
+                                 rope_inverse=rope_inverse, R=R, theta=theta)
+    return outs, sels

@@ -76,6 +76,15 @@ def check_close(got: np.ndarray, ref: np.ndarray, max_abs: float, rel_l2: float 
     return ma, rl
 
 
+def rel_close(got, ref, tol=1e-5):
+    """|got - ref| <= tol * max(1, |ref|) elementwise (fp32 entries against the double oracle)."""
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    scale = np.maximum(1.0, np.abs(np.asarray(ref, np.float64)))
+    worst = float((err / scale).max()) if err.size else 0.0
+    print(f"max relative error {worst:.3e}", flush=True)
+    assert (err <= tol * scale).all(), worst
+
+
 def kv_from_f32(x: np.ndarray, R: int, fmt=v4.V4A_KV_FP8_BF16) -> v4.KV:
     """Device entry records of fp32 rows x [B][N][D], quantised by the HIP quantiser."""
     B, N, D = x.shape

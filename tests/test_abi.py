@@ -129,3 +129,66 @@ def test_decode_rejects():
     assert call(rec=kv(D=512, R=64, cap=0)) == 1
     assert L.v4a_decode_hca(FAKE, 1, 1, 128, ctypes.byref(rec), i64(2000), 128, FAKE, 1, win_len, 128,
                             sink, pos, 0.04, 1, 10000.0, FAKE, 1, FAKE, 1 << 30, None) == 1
+
+
+def test_prefill_args_layout_matches_the_header(tmp_path):
+    """The binding's v4a_prefill_args has the C struct's size and field offsets (gcc on the header)."""
+    import subprocess
+    fields = [f for f, _ in v4.c_prefill_args._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "v4attn.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(v4a_prefill_args));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(v4a_prefill_args, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    inc = str(v4.HEADER).rsplit("/", 1)[0]
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(v4.c_prefill_args)
+    assert got[1:] == [getattr(v4.c_prefill_args, f).offset for f in fields]
+
+
+def prefill_struct(**kw):
+    """A valid CSA prefill chunk at the long-context prefill shape (fake device pointers)."""
+    rec, keys, q_idx = kv(cap=17408), idx(cap=17408), idx(cap=4096 * 64)
+    a = dict(tok0=65536, C=4096, n_prev=128, m=4, in_t=1, G=1, kv_a=FAKE, kv_b=FAKE, gate_a=FAKE, gate_b=FAKE,
+             bias_a=FAKE, bias_b=FAKE, apply_rope=1, rope_theta=10000.0, kv=ctypes.pointer(rec), slot=0, idx_G=1,
+             idx_a=FAKE, idx_b=FAKE, idx_gate_a=FAKE, idx_gate_b=FAKE, idx_bias_a=FAKE, idx_bias_b=FAKE,
+             keys=ctypes.pointer(keys), q_idx=ctypes.pointer(q_idx), w=FAKE, H_I=64, k=1024, q=FAKE, q_t=1,
+             H=128, W=128, sink=FAKE, softmax_scale=0.044, out_rope_inverse=1, out=FAKE, out_t=1)
+    a.update(kw)
+    s = v4.c_prefill_args(**a)
+    s._keep = (rec, keys, q_idx, a)
+    return s
+
+
+def test_prefill_workspace_and_rejects():
+    L = v4.lib()
+    csa, hca = v4.V4A_LAYER_CSA, v4.V4A_LAYER_HCA
+    s = prefill_struct()
+    need = L.v4a_prefill_workspace(csa, ctypes.byref(s))
+    # the chunk's top-k lists plus the indexer workspace for 4096 queries over 17408 entries
+    assert need >= 4096 * 1024 * 4 + v4.v4a_indexer_topk_workspace(1, 4096, 17408, 1024) - 256
+    assert need % 256 == 0
+
+    def call(kind=csa, ws=FAKE, wsb=1 << 40, **kw):
+        return L.v4a_prefill_chunk(kind, ctypes.byref(prefill_struct(**kw)), ws, wsb, None)
+    assert L.v4a_prefill_chunk(csa, None, FAKE, 1 << 40, None) == 1
+    assert call(kind=7) == 1
+    assert call(tok0=65537) == 1                 # not a multiple of m
+    assert call(n_prev=100) == 1                 # the window needs 127 rows before tok0
+    assert call(n_prev=70000) == 1               # more rows than positions before tok0
+    assert call(tok0=0, n_prev=0, C=70000) == 2
+    assert call(kv=ctypes.pointer(kv(cap=16000))) == 1     # 17408 entries do not fit
+    assert call(k=4096) == 2
+    assert call(H_I=6) == 2
+    assert call(kv_b=0) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=FAKE + 64) == 3
+    assert call(q=FAKE + 2) == 1
+    assert call(W=129) == 2
+    assert call(G=7) == 2
+    # HCA: m' = 128, no indexer, no workspace
+    h = prefill_struct(m=128, kv_b=0, gate_b=0, bias_b=0, keys=None, q_idx=None, w=0, k=0)
+    assert L.v4a_prefill_workspace(hca, ctypes.byref(h)) == 0
+    assert L.v4a_prefill_chunk(hca, ctypes.byref(prefill_struct(m=128, tok0=65600)), None, 0, None) == 1

@@ -176,3 +176,38 @@ def tiny_inputs(w: Workload = TINY) -> dict:
         "w": normal(s, "w", (w.H_I,)),
         "sink": np.zeros((w.H,), np.float32),
     }
+
+
+def prefill_inputs(w: Workload, C: int | None = None, tok0: int | None = None, n_prev: int = 128,
+                   kind: str = "csa", threads: int = 8) -> dict:
+    """fp32 inputs of one prefill chunk of C tokens at positions tok0 .. tok0+C-1.
+
+    The entries cached before tok0 are drawn directly (records [tok0/m][D], and for CSA the
+    indexer keys [tok0/m][d_I]); the chunk's raw streams hold n_prev + C rows (row r is
+    position tok0 - n_prev + r) and are compressed by the call under test.  Queries:
+    q [C][H][D], and for CSA q_idx [C][H_I][d_I], w [C][H_I].
+    """
+    s = w.seed
+    C = w.chunk if C is None else C
+    tok0 = w.T if tok0 is None else tok0
+    rows = n_prev + C
+    m = w.m if kind == "csa" else w.m_hca
+    out = {"C": C, "tok0": tok0, "n_prev": n_prev, "m": m, "N0": tok0 // m,
+           "q": normal(s, "q_chunk", (C, w.H, w.D), threads=threads),
+           "sink": (np.zeros((w.H,), np.float32) if w.sink_zero else normal(s, "sink", (w.H,)))}
+    if kind == "csa":
+        out.update(records=normal(s, "records", (tok0 // m, w.D), threads=threads),
+                   keys=normal(s, "keys", (tok0 // m, w.d_I), threads=threads),
+                   kv_a=normal(s, "kv_a", (rows, w.D)), kv_b=normal(s, "kv_b", (rows, w.D)),
+                   gate_a=normal(s, "gate_a", (rows, 1)), gate_b=normal(s, "gate_b", (rows, 1)),
+                   bias_a=normal(s, "bias_a", (m, 1)), bias_b=normal(s, "bias_b", (m, 1)),
+                   idx_a=normal(s, "idx_a", (rows, w.d_I)), idx_b=normal(s, "idx_b", (rows, w.d_I)),
+                   idx_gate_a=normal(s, "idx_gate_a", (rows, 1)), idx_gate_b=normal(s, "idx_gate_b", (rows, 1)),
+                   idx_bias_a=normal(s, "idx_bias_a", (m, 1)), idx_bias_b=normal(s, "idx_bias_b", (m, 1)),
+                   q_idx=normal(s, "q_idx_chunk", (C, w.H_I, w.d_I), threads=threads),
+                   w=normal(s, "w_chunk", (C, w.H_I)))
+    else:
+        out.update(records=normal(s, "records_h", (tok0 // m, w.D), threads=threads),
+                   kv_a=normal(s, "kv_h", (rows, w.D)), gate_a=normal(s, "gate_h", (rows, 1)),
+                   bias_a=normal(s, "bias_h", (m, 1)))
+    return out
