@@ -2,6 +2,7 @@
 """Benchmark of the DeepSeek-V4 CSA/HCA decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
+                    [--no-secondary] [--graphs] [--copy-probe]
 
 A step is one CSA decode step of the 1M-context workload (4 sequences at position
 1,048,575, 262,144 compressed entries each, 128 query heads, head dim 512, 64 MXFP4
@@ -12,12 +13,18 @@ indexer heads, top-1024, 128-token window, sink):
   3. attend over the selected entries plus the window with the sink, then combine the splits.
 Inputs are seeded synthetic data (N(0,1) before quantisation).  Every input set is cloned
 R times in HBM and step i uses set i mod R, so the 256 MB Infinity Cache cannot hold the
-working set; the inputs are resident in HBM when timing starts.
+working set; the inputs are resident in HBM when timing starts.  Calls are launched
+directly on one stream (--graphs replays captured per-stage HIP graphs instead).
 
 One JSON line is printed: throughput (tokens/s = sequences decoded per second), the roofline
-of the dominant stage (the indexer + top-k call) measured live with HIP events on the
-stream the kernels run on, the oracle timed on the host cores, a parity check of set 0
-against the oracle, and a secondary figure for the 1M-context HCA decode step.
+of the dominant launch (the indexer + top-k call, whose MXFP4 scoring kernel streams the
+keys) measured live with HIP events on the stream the kernels run on, the oracle timed on
+the host cores, a parity check of set 0 against the oracle, and secondary figures: the
+1M-context HCA decode step and one 4096-token prefill chunk per layer kind.
+
+--copy-probe first runs a plain device copy (an elementwise negation of 1 GiB) five times, so
+that a hardware-counter run of this command can scale FETCH_SIZE / WRITE_SIZE by what the
+counters read for a known byte count.
 """
 from __future__ import annotations
 
@@ -35,6 +42,11 @@ import numpy as np  # noqa: E402
 
 METRIC = "CSA/HCA decode tokens/s at 1M ctx; achieved HBM GB/s and indexer MFMA util"
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_BYTES = 1 << 30
+# Counter summary of the indexer + top-k call (FETCH_SIZE / WRITE_SIZE per call, already
+# scaled by the copy probe) and the hash of the kernel sources it was taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_topk_traffic_csa_decode_pro_1m.txt")
+TRAFFIC_SOURCES = ["indexer.hip", "topk.hip", "common.hpp", "api.hip"]
 MXFP4_PEAK_TFLOPS = 10100.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -47,7 +59,8 @@ def parse():
     p.add_argument("--rotate", type=int, default=16, help="input copies cycled through (MALL defeat)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying graphs")
+    p.add_argument("--graphs", action="store_true", help="replay captured per-stage HIP graphs")
+    p.add_argument("--copy-probe", action="store_true", help="run the 1 GiB copy used to scale counters")
     return p.parse_args()
 
 
@@ -145,8 +158,16 @@ def main():
         stage_indexer(st)
         stage_attend(st, outs[i % 2])
 
+    if args.copy_probe:
+        src = torch.randn((COPY_PROBE_BYTES // 4,), device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     graphs = None
-    if not args.eager:
+    if args.graphs:
         # each input set's step is captured as three graphs (compress, indexer + top-k,
         # attention); replaying them between HIP events times the indexer stage live
         print("[bench] capturing graphs", file=sys.stderr, flush=True)
@@ -233,9 +254,10 @@ def main():
         "config": {"workload": wl.name, "batch": B, "context_tokens": T, "csa_entries": N, "heads": H,
                    "head_dim": D, "rope_dims": R, "indexer_heads": HI, "indexer_dim": dI, "topk": k,
                    "window": W, "input_copies": len(sets), "hip_graphs": used_graphs},
-        "roofline": {"kernel": "v4a_indexer_topk (MXFP4 scoring + top-k select)", "bound": "hbm",
+        "roofline": {"kernel": "v4a_indexer_topk call: zero_kernel + indexer_mxfp4_kernel + select_scan_kernel "
+                               "+ select_final_kernel", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "ms_per_launch": idx_ms, "algorithmic_bytes": idx_bytes,
+                     "traffic": measured_traffic(), "ms_per_launch": idx_ms, "algorithmic_bytes": idx_bytes,
                      "mfma_util": idx_flops / (idx_ms / 1e3) / (MXFP4_PEAK_TFLOPS * 1e12)},
         "step": {"algorithmic_bytes": step_bytes, "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9,
                  "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, "flops": step_flops,
@@ -243,7 +265,13 @@ def main():
     }
 
     if not args.no_secondary:
-        result["secondary"] = hca_secondary(v4, torch, HCA_1M, args, f32, bf16)
+        del sets, graphs
+        torch.cuda.empty_cache()
+        result["secondary"] = {"hca_decode_1m": hca_secondary(v4, torch, HCA_1M, args, f32, bf16)}
+        torch.cuda.empty_cache()
+        result["secondary"]["prefill_csa_4k_on_64k"] = prefill_secondary(v4, torch, "csa", args)
+        torch.cuda.empty_cache()
+        result["secondary"]["prefill_hca_4k_on_64k"] = prefill_secondary(v4, torch, "hca", args)
 
     if not args.no_cpu_baseline:
         import oracle
@@ -322,6 +350,101 @@ def hca_secondary(v4, torch, wl, args, f32, bf16):
             "bound": "mfma", "mfma_tflops": flops / (ms / 1e3) / 1e12,
             "mfma_frac": flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "input_copies": rot}
+
+
+def prefill_secondary(v4, torch, kind, args):
+    """One 4096-token prefill chunk at positions 65536..69631 of a sequence whose 65536 earlier
+    tokens are cached (16384 CSA entries + keys, or 512 HCA entries); the chunk's own blocks are
+    compressed and appended by the call.  Throughput = chunk tokens / call time."""
+    from workloads import PREFILL_64K, prefill_inputs, to_bf16_bits
+    wl = PREFILL_64K
+    print(f"[bench] secondary: prefill {kind} {wl.name}", file=sys.stderr, flush=True)
+    x = prefill_inputs(wl, kind=kind, threads=16)
+    C, tok0, n_prev, N0 = x["C"], x["tok0"], x["n_prev"], x["N0"]
+    D, R, H, W = wl.D, wl.R, wl.H, wl.W
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    def bf16(a):
+        return torch.from_numpy(to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q = bf16(x["q"])
+    out = torch.empty((C, H, D), dtype=torch.bfloat16, device="cuda")
+    m = x["m"]
+    n_total = (tok0 + C) // m
+    kv = v4.KV.empty(1, n_total, D, R)
+    v4.v4a_quantize_kv(f32(x["records"]), kv, 0)
+    common = dict(tok0=tok0, n_prev=n_prev, m=m, kv_a=bf16(x["kv_a"]), gate_a=f32(x["gate_a"]),
+                  bias_a=f32(x["bias_a"]), kv=kv, q=q, W=W, sink=f32(x["sink"]), softmax_scale=wl.scale, out=out)
+    if kind == "csa":
+        keys = v4.Idx.empty(1, n_total, wl.d_I)
+        v4.v4a_quantize_mxfp4(f32(x["keys"]), keys, 0)
+        qi = v4.Idx.empty(1, C * wl.H_I, wl.d_I)
+        v4.v4a_quantize_mxfp4(f32(x["q_idx"].reshape(-1, wl.d_I)), qi)
+        a = v4.PrefillArgs(kv_b=bf16(x["kv_b"]), gate_b=f32(x["gate_b"]), bias_b=f32(x["bias_b"]),
+                           idx_a=bf16(x["idx_a"]), idx_b=bf16(x["idx_b"]), idx_gate_a=f32(x["idx_gate_a"]),
+                           idx_gate_b=f32(x["idx_gate_b"]), idx_bias_a=f32(x["idx_bias_a"]),
+                           idx_bias_b=f32(x["idx_bias_b"]), keys=keys, q_idx=qi, w=f32(x["w"]), k=wl.k, **common)
+        layer = v4.V4A_LAYER_CSA
+    else:
+        a = v4.PrefillArgs(**common)
+        layer = v4.V4A_LAYER_HCA
+    ws = v4.workspace(v4.v4a_prefill_workspace(layer, a))
+    del x
+    for _ in range(2):
+        v4.v4a_prefill_chunk(layer, a, ws)
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        v4.v4a_prefill_chunk(layer, a, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # algorithmic flops: every query's indexer dots over its visible entries (MXFP4) and its
+    # attention over its keys (BF16, 4*H*D per key: QK and PV)
+    vis = [min(n_total, (tok0 + j + 1) // m) for j in range(C)]
+    wins = [min(W, tok0 + j + 1) for j in range(C)]
+    attn_keys = sum((wl.k if kind == "csa" else v) + w_ for v, w_ in zip(vis, wins))
+    bf16_flops = 4.0 * H * D * attn_keys
+    mx_flops = 2.0 * wl.H_I * wl.d_I * sum(vis) if kind == "csa" else 0.0
+    t = ms / 1e3
+    res = {"tokens_per_s": C / t, "ms_per_chunk": ms, "bound": "mfma",
+           "bf16_tflops": bf16_flops / t / 1e12, "bf16_mfma_frac": bf16_flops / t / (BF16_PEAK_TFLOPS * 1e12)}
+    if kind == "csa":
+        res.update(mxfp4_tflops=mx_flops / t / 1e12, mxfp4_mfma_frac=mx_flops / t / (MXFP4_PEAK_TFLOPS * 1e12),
+                   mfma_time_frac=(bf16_flops / (BF16_PEAK_TFLOPS * 1e12) + mx_flops / (MXFP4_PEAK_TFLOPS * 1e12)) / t)
+    else:
+        res["mfma_time_frac"] = bf16_flops / (BF16_PEAK_TFLOPS * 1e12) / t
+    return res
+
+
+def source_hash(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "compressed_sparse_attention_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per indexer + top-k call from the committed counter summary, or None when it is
+    missing or was taken with other kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("kernel_sources_sha256") != source_hash(TRAFFIC_SOURCES):
+            return None
+        return float(fields["hbm_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 if __name__ == "__main__":
