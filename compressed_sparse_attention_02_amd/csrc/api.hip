@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of the hot path (declared in include/v4attn.h): host-side argument
 // validation (always before any launch), workspace layout, and kernel dispatch.  No device
 // memory is allocated here; scratch lives in the caller's workspace.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -34,6 +35,11 @@ static v4a_status fail(v4a_status st, const char *fmt, ...) {
 static v4a_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return V4A_OK;
     return fail(V4A_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void fill_rope_table(RopeTable &t, int R, double theta) {
+    for (int j = 0; j < kMaxRopePairs; j++)
+        t.inv_freq[j] = (2 * j < R) ? pow(theta, -2.0 * (double)j / (double)R) : 0.0;
 }
 
 static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -226,6 +232,7 @@ static v4a_status compress_check(CompressArgs &a, const float *norm_w) {
         if (a.kv->D != a.D) return fail(V4A_EINVAL, "out_kv->D != D");
         if (a.first_entry + a.n_entries > a.kv->cap) return fail(V4A_EINVAL, "entries exceed out_kv->cap");
         if (a.rope && (a.kv->R < 2)) return fail(V4A_EINVAL, "apply_rope needs R >= 2");
+        if (a.rope && a.kv->R > 2 * kMaxRopePairs) return fail(V4A_EUNSUPPORTED, "apply_rope supports R <= 64");
         a.R = a.kv->R;
         const int vpt = a.D >= 64 ? a.D / 64 : 1;
         if (((a.D - a.R) % vpt) != 0) return fail(V4A_EUNSUPPORTED, "D-R must be a multiple of D/64");
@@ -433,7 +440,8 @@ static v4a_status decode_common(AttnArgs &a, SeqInfo &sq, const int32_t *win_len
     a.out_bf16 = out_t == V4A_BF16;
     a.D = a.kv->D;
     a.R = a.kv->R;
-    if (a.D % 2 != 0 || (a.rope_inv && a.R < 2)) return fail(V4A_EUNSUPPORTED, "%s: odd D or no RoPE dims", name);
+    if (a.D % 2 != 0 || (a.rope_inv && (a.R < 2 || a.R > 2 * kMaxRopePairs)))
+        return fail(V4A_EUNSUPPORTED, "%s: odd D, or R not in [2, 64] with out_rope_inverse", name);
     if (!aligned(a.q, 16) || !aligned(a.out, 16) || (a.win && !aligned(a.win, 16)))
         return fail(V4A_EINVAL, "%s: q, win and out must be 16-byte aligned", name);
     int64_t n_keys_max = 0;
@@ -596,8 +604,8 @@ static v4a_status prefill_plan(v4a_layer kind, const v4a_prefill_args *a, Prefil
     if (!a->q || !a->out || !a->sink || !a->kv_a) return fail(V4A_EINVAL, "v4a_prefill_chunk: q, out, sink and kv_a are required");
     if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->kv_a, 16))
         return fail(V4A_EINVAL, "v4a_prefill_chunk: q, out and kv_a must be 16-byte aligned");
-    if (D % 2 != 0 || (a->out_rope_inverse && a->kv->R < 2))
-        return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: odd D or no RoPE dims");
+    if (D % 2 != 0 || (a->out_rope_inverse && (a->kv->R < 2 || a->kv->R > 2 * kMaxRopePairs)))
+        return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: odd D, or R not in [2, 64] with out_rope_inverse");
     pl.first = a->tok0 / a->m;
     pl.n_total = (a->tok0 + a->C) / a->m;
     pl.n_new = pl.n_total - pl.first;

@@ -57,7 +57,7 @@ struct AttnParams {
     const float *sink;       // [H]
     float scale2;            // softmax scale * log2(e)
     bool rope_inv;
-    double theta;
+    RopeTable rt;
     void *out;
     bool out_bf16;
     float *part_o;           // [B][S][H][D]
@@ -88,11 +88,9 @@ __device__ __forceinline__ float finish_factor(const AttnParams &P, int h, float
     return den > 0.0f ? c / den : 0.0f;
 }
 
-// Inverse rotation (by -pos) of one RoPE pair (x, y) with pair index j.
-__device__ __noinline__ float2 rope_unrotate(double pos, int j, int R, double theta, float x, float y) {
-    float c, s;
-    rope_cs(pos, j, R, theta, &c, &s);
-    return make_float2(x * c + y * s, -x * s + y * c);
+// Inverse rotation (by -pos) of one RoPE pair (x, y) given its (cos, sin).
+__device__ __forceinline__ float2 rope_unrotate(float2 cs, float x, float y) {
+    return make_float2(x * cs.x + y * cs.y, -x * cs.y + y * cs.x);
 }
 
 template <int NV>
@@ -117,12 +115,17 @@ __device__ __forceinline__ void finish_head(const AttnParams &P, const SeqInfo &
 #pragma unroll
     for (int v = 0; v < NV; v++) o[v] *= f;
     const int Dn = P.D - P.R;
-    if (P.rope_inv && d0 >= Dn) {
+    if (P.rope_inv) {  // reached by the whole wavefront
+        RopeLanes rl;
+        rl.eval(P.rt, P.R / 2, (double)sq_pos(Sq, b));
 #pragma unroll
         for (int v = 0; v < NV; v += 2) {
-            const float2 r = rope_unrotate((double)sq_pos(Sq, b), (d0 + v - Dn) / 2, P.R, P.theta, o[v], o[v + 1]);
-            o[v] = r.x;
-            o[v + 1] = r.y;
+            const float2 cs = rl.get(min(max((d0 + v - Dn) / 2, 0), P.R / 2 - 1));
+            if (d0 >= Dn) {
+                const float2 r = rope_unrotate(cs, o[v], o[v + 1]);
+                o[v] = r.x;
+                o[v + 1] = r.y;
+            }
         }
     }
     store_out<NV>(P, b, h, d0, o);
@@ -367,12 +370,14 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
         const float f = finish_factor(P, h, m_run, l_run);
 #pragma unroll
         for (int dt = 0; dt < NDT; dt++) O[dt] *= f;
-        if (P.rope_inv) {
+        if (P.rope_inv) {  // H is a multiple of 16: the whole wavefront is here
+            RopeLanes rl;
+            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
 #pragma unroll
             for (int dt = Dn / 16; dt < NDT; dt++) {
                 const int j = (16 * dt + 4 * grp - Dn) / 2;
-                const float2 r0 = rope_unrotate((double)sq_pos(Sq, b), j, R, P.theta, O[dt][0], O[dt][1]);
-                const float2 r1 = rope_unrotate((double)sq_pos(Sq, b), j + 1, R, P.theta, O[dt][2], O[dt][3]);
+                const float2 r0 = rope_unrotate(rl.get(j), O[dt][0], O[dt][1]);
+                const float2 r1 = rope_unrotate(rl.get(j + 1), O[dt][2], O[dt][3]);
                 O[dt] = v4f{r0.x, r0.y, r1.x, r1.y};
             }
         }
@@ -538,7 +543,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
         float o[2] = {osh[d], osh[d + 1]};
         if (P.rope_inv && d >= Dn) {
             float c, s;
-            rope_cs((double)sq_pos(Sq, b), (d - Dn) / 2, P.R, P.theta, &c, &s);
+            rope_cs_freq((double)sq_pos(Sq, b), P.rt.inv_freq[(d - Dn) / 2], &c, &s);
             const float x = o[0], y = o[1];
             o[0] = x * c + y * s;
             o[1] = -x * s + y * c;
@@ -585,7 +590,7 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     P.sink = a.sink;
     P.scale2 = a.scale * kLog2e;
     P.rope_inv = a.rope_inv;
-    P.theta = a.theta;
+    if (a.rope_inv) fill_rope_table(P.rt, a.R, a.theta);
     P.out = a.out;
     P.out_bf16 = a.out_bf16;
     P.part_o = a.partial;

@@ -88,12 +88,21 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // rounded to fp32.  Positions reach 2^20, so the angle is first reduced by multiples of pi/2
 // (Cody-Waite with a two-term pi/2 and fused multiply-adds, error ~1e-16 relative to the
 // reduced angle); sin and cos then run on |r| <= pi/4 and the quadrant picks the pair.
-__device__ __forceinline__ void rope_cs(double p, int j, int R, double theta, float *c, float *s) {
+// RoPE frequencies of the R/2 interleaved pairs: inv_freq_j = theta^(-2j/R), computed on the
+// host in double (a kernel argument, so no kernel evaluates pow).
+constexpr int kMaxRopePairs = 32;
+struct RopeTable {
+    double inv_freq[kMaxRopePairs];
+};
+
+// cos and sin of the angle pos * inv_freq (double), each rounded once to fp32.  The angle is
+// first reduced by pi/2 with a two-term constant (Cody-Waite), which keeps the double sin/cos
+// on |r| <= pi/4 for positions up to millions.
+__device__ __forceinline__ void rope_cs_freq(double pos, double inv_freq, float *c, float *s) {
     const double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
     const double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
     const double kTwoOverPi = 0.6366197723675814;
-    const double inv_freq = pow(theta, -2.0 * (double)j / (double)R);
-    const double ang = p * inv_freq;
+    const double ang = pos * inv_freq;
     const double k = rint(ang * kTwoOverPi);
     double r = fma(-k, kPio2Hi, ang);
     r = fma(-k, kPio2Lo, r);
@@ -105,6 +114,22 @@ __device__ __forceinline__ void rope_cs(double p, int j, int R, double theta, fl
         default: *c = (float)sr; *s = (float)-cr; break;
     }
 }
+
+// Every lane of the wavefront gets (cos, sin) of pair `want` (< R/2) at position pos: lane j
+// < R/2 evaluates pair j once and the values travel by cross-lane reads.  Must be reached by
+// the whole wavefront.
+struct RopeLanes {
+    float c, s;
+    __device__ __forceinline__ void eval(const RopeTable &T, int npairs, double pos) {
+        const int lane = threadIdx.x & 63;
+        c = 1.0f;
+        s = 0.0f;
+        if (lane < npairs) rope_cs_freq(pos, T.inv_freq[lane], &c, &s);
+    }
+    __device__ __forceinline__ float2 get(int want) const {
+        return make_float2(__shfl(c, want), __shfl(s, want));
+    }
+};
 
 }  // namespace v4a
 
@@ -172,6 +197,7 @@ __host__ __device__ __forceinline__ int64_t sq_win_row0(const SeqInfo &S, int b,
 }
 
 void set_error(const char *fmt, ...);
+void fill_rope_table(RopeTable &t, int R, double theta);
 
 hipError_t launch_quantize_kv(const float *x, int64_t rows, const v4a_kv &out, int64_t row0,
                               hipStream_t s);

@@ -29,7 +29,7 @@ struct CompressParams {
     int n_streams, D, G, m, R;
     bool bf16_in, rope;
     int64_t tok0, first_entry, n_entries;
-    double theta;
+    RopeTable rt;
     v4a_kv kv;
     v4a_idx idx;
     bool to_idx;
@@ -157,28 +157,31 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
     }
 
-    // partial RoPE on the last R dims at position m*i (interleaved pairs)
+    // partial RoPE on the last R dims at position m*i (interleaved pairs); lane j < R/2
+    // evaluates pair j's cos/sin and the owning lanes read them across the wavefront
     if (P.rope) {
-        const int rs = D - P.R;
+        const int rs = D - P.R, npairs = P.R / 2;
+        RopeLanes rl;
+        rl.eval(P.rt, npairs, (double)(m * i));
         if constexpr (VPT >= 2) {
-            if (active && d0 >= rs) {
 #pragma unroll
-                for (int v = 0; v < VPT; v += 2) {
-                    float c, s;
-                    rope_cs((double)(m * i), (d0 - rs + v) / 2, P.R, P.theta, &c, &s);
-                    float x = acc[v], y = acc[v + 1];
-                    acc[v] = x * c - y * s;
-                    acc[v + 1] = x * s + y * c;
+            for (int v = 0; v < VPT; v += 2) {
+                const int j = min(max((d0 - rs + v) / 2, 0), npairs - 1);
+                const float2 cs = rl.get(j);
+                if (active && d0 >= rs) {
+                    const float x = acc[v], y = acc[v + 1];
+                    acc[v] = x * cs.x - y * cs.y;
+                    acc[v + 1] = x * cs.y + y * cs.x;
                 }
             }
         } else {
-            float partner = __shfl_xor(acc[0], 1);
+            const float partner = __shfl_xor(acc[0], 1);
+            const int j = min(max((d0 - rs) / 2, 0), npairs - 1);
+            const float2 cs = rl.get(j);
             if (active && d0 >= rs) {
-                float c, s;
-                rope_cs((double)(m * i), (d0 - rs) / 2, P.R, P.theta, &c, &s);
-                bool even = ((d0 - rs) & 1) == 0;
-                float x = even ? acc[0] : partner, y = even ? partner : acc[0];
-                acc[0] = even ? (x * c - y * s) : (x * s + y * c);
+                const bool even = ((d0 - rs) & 1) == 0;
+                const float x = even ? acc[0] : partner, y = even ? partner : acc[0];
+                acc[0] = even ? (x * cs.x - y * cs.y) : (x * cs.y + y * cs.x);
             }
         }
     }
@@ -209,7 +212,7 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     P.tok0 = a.tok0;
     P.first_entry = a.first_entry;
     P.n_entries = a.n_entries;
-    P.theta = a.theta;
+    if (a.rope) fill_rope_table(P.rt, a.R, a.theta);
     P.to_idx = a.idx != nullptr;
     if (a.kv) P.kv = *a.kv; else P.kv = v4a_kv{};
     if (a.idx) P.idx = *a.idx; else P.idx = v4a_idx{};
