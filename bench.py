@@ -8,7 +8,8 @@ A step is one CSA decode step of the 1M-context workload (4 sequences at positio
 1,048,575, 262,144 compressed entries each, 128 query heads, head dim 512, 64 MXFP4
 indexer heads, top-1024, 128-token window, sink):
   1. compress the block each sequence's newest token completes into its entry record and
-     its MXFP4 indexer key (two batched compressor launches);
+     its MXFP4 indexer key (two batched compressor launches; the record, read only by
+     attention, is compressed on a second stream while the indexer runs);
   2. score every entry with the lightning indexer and select the top-1024;
   3. attend over the selected entries plus the window with the sink, then combine the splits.
 Inputs are seeded synthetic data (N(0,1) before quantisation).  Every input set is cloned
@@ -152,11 +153,25 @@ def main():
         v4.v4a_decode_csa(st["q"], st["kv"], sel.view(B, k), k, st["win"], win_len, W, st["sink"], q_pos,
                           softmax_scale=scale, out=out, ws=ws)
 
+    def stage_compress_records(st):
+        v4.v4a_compress_csa(st["kv_a"], st["kv_b"], st["gate_a"], st["gate_b"], st["bias_a"], st["bias_b"],
+                            tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_kv=st["kv"])
+
+    def stage_compress_keys(st):
+        v4.v4a_compress_csa(st["idx_a"], st["idx_b"], st["idx_gate_a"], st["idx_gate_b"], st["idx_bias_a"],
+                            st["idx_bias_b"], tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_idx=st["keys"])
+
     def step_eager(i):
         st = sets[i % len(sets)]
         stage_compress(st)
         stage_indexer(st)
         stage_attend(st, outs[i % 2])
+
+    # the new entry record is only read by attention: it is compressed on a second stream
+    # while the key compressor, the indexer and the selection run on the main one
+    side_rec = torch.cuda.Stream()
+    ev_start = [torch.cuda.Event() for _ in range(2)]
+    ev_rec = [torch.cuda.Event() for _ in range(2)]
 
     if args.copy_probe:
         src = torch.randn((COPY_PROBE_BYTES // 4,), device=dev)
@@ -192,12 +207,19 @@ def main():
     def step(i, ev=None):
         if graphs is None:
             st = sets[i % len(sets)]
-            stage_compress(st)
+            main = torch.cuda.current_stream()
+            ev_start[i % 2].record(main)
+            side_rec.wait_event(ev_start[i % 2])
+            with torch.cuda.stream(side_rec):
+                stage_compress_records(st)
+            ev_rec[i % 2].record(side_rec)
+            stage_compress_keys(st)
             if ev is not None:
                 ev[0].record()
             stage_indexer(st)
             if ev is not None:
                 ev[1].record()
+            main.wait_event(ev_rec[i % 2])
             stage_attend(st, outs[i % 2])
             return
         g = graphs[i % len(graphs)]

@@ -100,7 +100,7 @@ static TopkWs topk_layout(int B, int Q, int64_t n_max, int k) {
     const size_t slices = (size_t)select_slices(n_max);
     size_t off = 0;
     L.keys = off;
-    off = round_up(off + BQ * (size_t)n_max * 4, 256);
+    off = round_up(off + BQ * (size_t)score_key_stride(n_max) * 4, 256);
     L.hist = off;
     off = round_up(off + BQ * hist_copies((int64_t)BQ) * kHistBins * 4, 256);
     L.list = off;
@@ -343,12 +343,14 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
     ia.Q = Q;
     ia.H_I = H_I;
     ia.n_max = n_max;
+    ia.key_stride = score_key_stride(n_max);
     ia.score_keys = (uint32_t *)(base + L.keys);
     ia.hist = (uint32_t *)(base + L.hist);
     ia.hist_copies = hist_copies((int64_t)BQ);
     if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
     SelectArgs sa{};
     sa.score_keys = ia.score_keys;
+    sa.key_stride = ia.key_stride;
     sa.hist = ia.hist;
     sa.hist_copies = ia.hist_copies;
     sa.n_max = n_max;
@@ -403,6 +405,7 @@ v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int
     ia.Q = Q;
     ia.H_I = H_I;
     ia.n_max = n_max;
+    ia.key_stride = score_key_stride(n_max);
     ia.scores = out_scores;
     return hip_status(launch_indexer(ia, qp, (hipStream_t)stream), "v4a_indexer_scores");
 }

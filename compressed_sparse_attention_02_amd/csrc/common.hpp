@@ -84,10 +84,6 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// RoPE cos/sin of one pair: angle p * theta^(-2j/R) in double, cos and sin in double,
-// rounded to fp32.  Positions reach 2^20, so the angle is first reduced by multiples of pi/2
-// (Cody-Waite with a two-term pi/2 and fused multiply-adds, error ~1e-16 relative to the
-// reduced angle); sin and cos then run on |r| <= pi/4 and the quadrant picks the pair.
 // RoPE frequencies of the R/2 interleaved pairs: inv_freq_j = theta^(-2j/R), computed on the
 // host in double (a kernel argument, so no kernel evaluates pow).
 constexpr int kMaxRopePairs = 32;
@@ -227,7 +223,8 @@ struct IndexerArgs {
     const float *w;
     int B, Q, H_I;
     int64_t n_max;            // max visible keys over the queries (grid size)
-    uint32_t *score_keys;     // [B*Q][n_max] orderable keys (or NULL)
+    int64_t key_stride;       // score-key row stride (a multiple of 4 >= n_max)
+    uint32_t *score_keys;     // [B*Q][key_stride] orderable keys (or NULL)
     float *scores;            // [B*Q][n_max] raw scores (or NULL)
     uint32_t *hist;           // [B*Q][copies][4096] histogram of the top 12 key bits (or NULL)
     int hist_copies;
@@ -236,7 +233,8 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 struct SelectArgs {
-    const uint32_t *score_keys;   // [BQ][n_max]
+    const uint32_t *score_keys;   // [BQ][key_stride]
+    int64_t key_stride;
     const uint32_t *hist;         // [BQ][copies][4096]
     int hist_copies;
     int64_t n_max;
@@ -248,6 +246,7 @@ struct SelectArgs {
 };
 int select_slices(int64_t n_max);
 constexpr int kSelSlice = 8192;
+inline int64_t score_key_stride(int64_t n_max) { return (n_max + 63) / 64 * 64; }
 hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s);
 
 struct AttnArgs {

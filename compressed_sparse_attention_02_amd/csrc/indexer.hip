@@ -40,7 +40,8 @@ struct IndexerParams {
     const float *w;      // [B*Q][H_I]
     int H, d;
     int64_t n_max;
-    uint32_t *score_keys;  // [BQ][n_max] or NULL
+    int64_t key_stride;
+    uint32_t *score_keys;  // [BQ][key_stride] or NULL
     float *scores;         // [BQ][n_max] or NULL
     uint32_t *hist;        // [BQ][hist_copies][4096] or NULL
     int hist_copies;
@@ -52,7 +53,7 @@ __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64
     if (score == 0.0f) score = 0.0f;  // -0 -> +0
     if (P.scores) P.scores[(int64_t)qi * P.n_max + i] = score;
     uint32_t key = score_key(score);
-    if (P.score_keys) P.score_keys[(int64_t)qi * P.n_max + i] = key;
+    if (P.score_keys) P.score_keys[(int64_t)qi * P.key_stride + i] = key;
     if (lhist) atomicAdd(&lhist[key >> 20], 1u);
 }
 
@@ -198,23 +199,31 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     __syncthreads();
     const int n_here = (int)(kend - k0);
     float *g_sc = P.scores ? P.scores + (int64_t)qi * P.n_max + k0 : nullptr;
-    uint32_t *g_key = P.score_keys ? P.score_keys + (int64_t)qi * P.n_max + k0 : nullptr;
+    uint32_t *g_key = P.score_keys ? P.score_keys + (int64_t)qi * P.key_stride + k0 : nullptr;
+    const bool sc_aligned = ((k0 + (int64_t)qi * P.n_max) & 3) == 0;
     for (int i0 = 4 * threadIdx.x; i0 < n_here; i0 += 4 * 256) {
         const float4 v = *(const float4 *)(sbuf + i0);
         const float vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t kk[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) kk[j] = score_key(vv[j]);
-        if (i0 + 4 <= n_here && ((k0 + (int64_t)qi * P.n_max) & 3) == 0) {
-            if (g_sc) *(float4 *)(g_sc + i0) = v;
-            if (g_key) *(uint4 *)(g_key + i0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
-        } else {
+        const bool whole = i0 + 4 <= n_here;
+        if (g_key) {  // rows are padded to a multiple of 4 keys and k0 is a multiple of 4
+            if (whole) {
+                *(uint4 *)(g_key + i0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if (i0 + j < n_here) {
-                    if (g_sc) g_sc[i0 + j] = vv[j];
-                    if (g_key) g_key[i0 + j] = kk[j];
-                }
+                for (int j = 0; j < 4; j++)
+                    if (i0 + j < n_here) g_key[i0 + j] = kk[j];
+            }
+        }
+        if (g_sc) {
+            if (whole && sc_aligned) {
+                *(float4 *)(g_sc + i0) = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (i0 + j < n_here) g_sc[i0 + j] = vv[j];
             }
         }
         if (hist) {
@@ -294,6 +303,7 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     P.H = a.H_I;
     P.d = a.keys->d;
     P.n_max = a.n_max;
+    P.key_stride = a.key_stride;
     P.score_keys = a.score_keys;
     P.scores = a.scores;
     P.hist = a.hist;

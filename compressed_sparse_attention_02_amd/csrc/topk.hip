@@ -25,6 +25,7 @@ constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kLdsList = 12288;   // listed keys the finalize kernel keeps in LDS
 constexpr int kMaxSlices = 1024;  // n_max <= 8M keys
+constexpr int kSubBins = 1024;    // 10-bit digits of the low 20 score-key bits
 
 int select_slices(int64_t n_max) {
     int64_t s = (n_max + kSelSlice - 1) / kSelSlice;
@@ -32,7 +33,8 @@ int select_slices(int64_t n_max) {
 }
 
 struct SelParams {
-    const uint32_t *keys;
+    const uint32_t *keys;    // [BQ][key_stride]
+    int64_t key_stride;
     const uint32_t *hist;    // [BQ][copies][4096]
     int copies;
     int64_t n_max;
@@ -66,27 +68,28 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *wsum, uint3
     return base + v;
 }
 
-// Walks a histogram from its top bin down, nb bins, in rounds of kSelThreads bins, and finds
-// the bin T where the count from the top first reaches `need`; returns T (or -1) and the
-// count strictly above T.  `bin_count(b)` gives the count of bin b.
-template <class F>
-__device__ __forceinline__ void top_down_threshold(int nb, uint32_t need, F bin_count, uint32_t *wsum,
-                                                   int *sT, uint32_t *sAbove, int *T, uint32_t *above) {
+// Threshold search over a histogram whose bins are held BPT per thread, thread t owning bins
+// BPT*t .. BPT*t+BPT-1 (counts c[]): finds the bin T where the count walking down from the top
+// bin first reaches `need`, and the count strictly above T.  One block scan: thread t's bins
+// sit below everything owned by threads > t.  T = -1 if the histogram holds fewer than need.
+template <int BPT>
+__device__ __forceinline__ void find_threshold(const uint32_t (&c)[BPT], uint32_t need, uint32_t *wsum, int *sT,
+                                               uint32_t *sAbove, int *T, uint32_t *above) {
     const int t = threadIdx.x;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; b++) mine += c[b];
     if (t == 0) { *sT = -1; *sAbove = 0; }
-    uint32_t run = 0;
-    for (int r0 = 0; r0 < nb; r0 += kSelThreads) {
-        const int bin = nb - 1 - (r0 + t);
-        const uint32_t c = bin >= 0 ? bin_count(bin) : 0u;
-        uint32_t tot;
-        const uint32_t incl = block_scan(c, wsum, &tot);
-        if (run + incl >= need && run + incl - c < need) {
-            *sT = bin;
-            *sAbove = run + incl - c;
+    uint32_t tot;
+    const uint32_t incl = block_scan(mine, wsum, &tot);
+    const uint32_t over = tot - incl;  // held by threads above this one
+    if (over < need && need <= over + mine) {
+        uint32_t run = over;
+#pragma unroll
+        for (int b = BPT - 1; b >= 0; b--) {
+            if (run < need && need <= run + c[b]) { *sT = BPT * t + b; *sAbove = run; }
+            run += c[b];
         }
-        run += tot;
-        __syncthreads();
-        if (*sT >= 0 || run >= need) break;  // uniform: every thread reads the same LDS value
     }
     __syncthreads();
     *T = *sT;
@@ -94,11 +97,17 @@ __device__ __forceinline__ void top_down_threshold(int nb, uint32_t need, F bin_
     __syncthreads();
 }
 
+// Scan: one workgroup per (slice of kSelSlice keys, query).  The histogram (all copies) is
+// read with 16-byte loads in one round, the threshold bin T found with one block scan, and the
+// slice's keys whose bin is >= T listed in index order (each thread owns a contiguous run of
+// keys; one block scan places the runs).
 __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, QueryPos QP) {
-    __shared__ uint32_t wsum[2 * kSelWaves];  // double-buffered so one barrier per round suffices
+    constexpr int kBPT = kHistBins / kSelThreads;       // 8 bins per thread
+    constexpr int kPer = kSelSlice / kSelThreads;       // 16 keys per thread
+    __shared__ uint32_t wsum[kSelWaves];
     __shared__ int sT;
     __shared__ uint32_t sAbove;
-    const int qi = blockIdx.y, s = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int qi = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
     const int64_t n_vis = visible_keys(QP, qi);
     const uint32_t k_eff = (uint32_t)(n_vis < P.k ? n_vis : P.k);
     uint32_t *cnt = P.counts + (int64_t)qi * P.slices + s;
@@ -109,65 +118,75 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
         }
         return;
     }
-    const uint32_t *h = P.hist + (int64_t)qi * P.copies * kHistBins;
-    const bool one_copy = P.copies == 1;
+    // this slice's keys are requested first, so their latency overlaps the histogram's
+    const int64_t lo = (int64_t)s * kSelSlice;
+    const int64_t hi = lo + kSelSlice < n_vis ? lo + kSelSlice : n_vis;
+    const int64_t my0 = lo + (int64_t)t * kPer;
+    const uint32_t *keys = P.keys + (int64_t)qi * P.key_stride;
+    uint4 kq[kPer / 4];
+#pragma unroll
+    for (int r = 0; r < kPer / 4; r++) {  // rows are padded to a multiple of 64 keys
+        const int64_t i = my0 + 4 * r;
+        kq[r] = i < hi ? *(const uint4 *)(keys + i) : make_uint4(0, 0, 0, 0);
+    }
+    uint32_t c[kBPT];
+    {
+        const uint32_t *h = P.hist + (int64_t)qi * P.copies * kHistBins + kBPT * t;
+        uint4 a = *(const uint4 *)h, b = *(const uint4 *)(h + 4);
+        if (P.copies > 1) {
+            uint4 ha[kHistCopies - 1], hb[kHistCopies - 1];
+#pragma unroll
+            for (int cp = 1; cp < kHistCopies; cp++) {
+                ha[cp - 1] = *(const uint4 *)(h + cp * kHistBins);
+                hb[cp - 1] = *(const uint4 *)(h + cp * kHistBins + 4);
+            }
+#pragma unroll
+            for (int cp = 0; cp < kHistCopies - 1; cp++) {
+                a.x += ha[cp].x; a.y += ha[cp].y; a.z += ha[cp].z; a.w += ha[cp].w;
+                b.x += hb[cp].x; b.y += hb[cp].y; b.z += hb[cp].z; b.w += hb[cp].w;
+            }
+        }
+        c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
+        c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
+    }
     int T;
     uint32_t above;
-    top_down_threshold(kHistBins, k_eff, [&](int bin) {
-        if (one_copy) return h[bin];
-        uint32_t c = 0;
-#pragma unroll
-        for (int cp = 0; cp < kHistCopies; cp++) c += h[cp * kHistBins + bin];
-        return c;
-    }, wsum, &sT, &sAbove, &T, &above);
+    find_threshold<kBPT>(c, k_eff, wsum, &sT, &sAbove, &T, &above);
     if (s == 0 && t == 0) {
         P.meta[2 * qi] = T;
         P.meta[2 * qi + 1] = (int32_t)above;
     }
-    // list, in index order, the slice's keys whose bin is >= T
-    const int64_t lo = (int64_t)s * kSelSlice;
-    const int64_t hi = lo + kSelSlice < n_vis ? lo + kSelSlice : n_vis;
-    const uint32_t *keys = P.keys + (int64_t)qi * P.n_max;
-    uint32_t *lst = P.list + ((int64_t)qi * P.slices * kSelSlice + lo) * 2;
-    // every key of the slice is loaded before the first is used (kSelSlice / kSelThreads each)
-    constexpr int kPer = kSelSlice / kSelThreads;
     uint32_t kv[kPer];
 #pragma unroll
-    for (int r = 0; r < kPer; r++) {
-        const int64_t i = lo + (int64_t)r * kSelThreads + t;
-        kv[r] = i < hi ? keys[i] : 0u;
+    for (int r = 0; r < kPer / 4; r++) {
+        kv[4 * r] = kq[r].x; kv[4 * r + 1] = kq[r].y; kv[4 * r + 2] = kq[r].z; kv[4 * r + 3] = kq[r].w;
     }
-    uint32_t off = 0;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; r++) mine += (my0 + r < hi && (int)(kv[r] >> 20) >= T) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t pos = block_scan(mine, wsum, &tot) - mine;
+    uint32_t *lst = P.list + ((int64_t)qi * P.slices * kSelSlice + lo) * 2;
 #pragma unroll
     for (int r = 0; r < kPer; r++) {
-        const int64_t i = lo + (int64_t)r * kSelThreads + t;
-        const uint32_t key = kv[r];
-        const bool take = i < hi && (int)(key >> 20) >= T;
-        const uint64_t m = __ballot(take);
-        if (lane == 0) wsum[(r & 1) * kSelWaves + w] = (uint32_t)__popcll(m);
-        __syncthreads();
-        uint32_t base = off, tot = 0;
-#pragma unroll
-        for (int j = 0; j < kSelWaves; j++) {
-            const uint32_t x = wsum[(r & 1) * kSelWaves + j];
-            base += j < w ? x : 0u;
-            tot += x;
+        if (my0 + r < hi && (int)(kv[r] >> 20) >= T) {
+            *(uint2 *)(lst + 2 * pos) = make_uint2((uint32_t)(my0 + r), kv[r]);
+            pos++;
         }
-        if (take) {
-            const uint32_t pos = base + (uint32_t)__popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-            lst[2 * pos] = (uint32_t)i;
-            lst[2 * pos + 1] = key;
-        }
-        off += tot;
     }
-    if (t == 0) *cnt = off;
+    if (t == 0) *cnt = tot;
 }
 
+// Finalize: one workgroup per query.  The listed keys are read in global index order (slice
+// by slice) into LDS.  Inside bin T two 10-bit digit passes find the exact threshold score
+// key S* and how many keys equal to it are still needed (rem); the ordered compaction then
+// keeps every key above S* and the first rem keys equal to S* in index order (the lowest
+// indices win the tie).  One block scan places every kept key.
 __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, QueryPos QP) {
     __shared__ uint32_t wsum[kSelWaves];
     __shared__ int sT;
     __shared__ uint32_t sAbove;
-    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t hist[kSubBins];
     __shared__ uint32_t lidx[kLdsList];
     __shared__ uint32_t lkey[kLdsList];
     __shared__ uint32_t soff[kMaxSlices + 1];
@@ -181,7 +200,7 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     }
     const int T = P.meta[2 * qi];
     const uint32_t above = (uint32_t)P.meta[2 * qi + 1];
-    const uint32_t need = k_eff > above ? k_eff - above : 0u;  // keys still to take from bin T
+    const uint32_t need = k_eff - above;  // >= 1: keys still to take from bin T
     // global order of the listed keys: slice offsets
     const uint32_t *cnts = P.counts + (int64_t)qi * P.slices;
     const int S = P.slices;
@@ -200,35 +219,29 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     const bool in_lds = L <= (uint32_t)kLdsList;
     const uint32_t *lst = P.list + (int64_t)qi * S * kSelSlice * 2;
     // entry j of the global order lives in slice s at position j - soff[s]
-    auto entry = [&](uint32_t j, uint32_t *idx, uint32_t *key) {
-        if (in_lds) { *idx = lidx[j]; *key = lkey[j]; return; }
-        int lo = 0, hi = S;  // find s with soff[s] <= j < soff[s+1]
+    auto fetch = [&](uint32_t j) -> uint2 {
+        int lo = 0, hi = S;  // s with soff[s] <= j < soff[s+1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (soff[mid] <= j) lo = mid; else hi = mid;
         }
-        const uint32_t *e = lst + ((int64_t)lo * kSelSlice + (j - soff[lo])) * 2;
-        *idx = e[0];
-        *key = e[1];
+        return *(const uint2 *)(lst + ((int64_t)lo * kSelSlice + (j - soff[lo])) * 2);
+    };
+    auto entry = [&](uint32_t j, uint32_t *idx, uint32_t *key) {
+        if (in_lds) { *idx = lidx[j]; *key = lkey[j]; return; }
+        const uint2 e = fetch(j);
+        *idx = e.x;
+        *key = e.y;
     };
     if (in_lds) {
-        // each thread loads entries j = t, t + kSelThreads, ... of the global order (its slice by
-        // binary search over the offsets), all loads issued before any LDS store
+        // all loads of a batch are issued before any LDS store
         constexpr int kBatch = 8;
         for (uint32_t j0 = 0; j0 < L; j0 += kBatch * kSelThreads) {
             uint2 e[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; u++) {
                 const uint32_t j = j0 + (uint32_t)u * kSelThreads + t;
-                e[u] = make_uint2(0, 0);
-                if (j < L) {
-                    int lo = 0, hi = S;
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (soff[mid] <= j) lo = mid; else hi = mid;
-                    }
-                    e[u] = *(const uint2 *)(lst + ((int64_t)lo * kSelSlice + (j - soff[lo])) * 2);
-                }
+                e[u] = j < L ? fetch(j) : make_uint2(0, 0);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; u++) {
@@ -239,50 +252,64 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     }
     __syncthreads();
 
-    // radix select of the need-th largest sub-rank (low 20 score bits, inverted index) among
-    // the keys of bin T; digits from the top: 10 + 10 score bits, then 11 + 11 + 10 index bits
-    const int dig_lo[5] = {42, 32, 21, 10, 0};
-    const int dig_w[5] = {10, 10, 11, 11, 10};
-    uint64_t prefix = 0, pmask = 0;
-    uint32_t rem = need;
-    for (int p = 0; p < 5 && need > 0; p++) {
-        const int w = dig_w[p], lo_bit = dig_lo[p];
-        const int nb = 1 << w;
-        for (int i = t; i < nb; i += kSelThreads) hist[i] = 0;
+    // two digit passes over the low 20 bits of the keys in bin T
+    uint32_t rem = need, sub = 0, sub_mask = 0;
+    for (int p = 0; p < 2; p++) {
+        const int shift = p == 0 ? 10 : 0;
+        for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
         __syncthreads();
         for (uint32_t j = t; j < L; j += kSelThreads) {
             uint32_t idx, key;
             entry(j, &idx, &key);
-            if ((int)(key >> 20) != T) continue;
-            const uint64_t v = ((uint64_t)(key & 0xFFFFFu) << 32) | (uint64_t)(~idx);
-            if ((v & pmask) == prefix) atomicAdd(&hist[(v >> lo_bit) & (uint64_t)(nb - 1)], 1u);
+            if ((int)(key >> 20) == T && (key & sub_mask) == sub) atomicAdd(&hist[(key >> shift) & (kSubBins - 1)], 1u);
         }
         __syncthreads();
+        uint32_t c[kSubBins / kSelThreads];
+#pragma unroll
+        for (int b = 0; b < kSubBins / kSelThreads; b++) c[b] = hist[(kSubBins / kSelThreads) * t + b];
         int d;
         uint32_t ab;
-        top_down_threshold(nb, rem, [&](int bin) { return hist[bin]; }, wsum, &sT, &sAbove, &d, &ab);
+        find_threshold<kSubBins / kSelThreads>(c, rem, wsum, &sT, &sAbove, &d, &ab);
         rem -= ab;
-        prefix |= (uint64_t)(d < 0 ? 0 : d) << lo_bit;
-        pmask |= (uint64_t)(nb - 1) << lo_bit;
+        sub |= (uint32_t)d << shift;
+        sub_mask |= (uint32_t)(kSubBins - 1) << shift;
     }
-    // ordered compaction: keep keys above bin T and keys of bin T with sub-rank >= prefix
-    uint32_t written = 0;
-    for (uint32_t j0 = 0; j0 < L; j0 += kSelThreads) {
-        const uint32_t j = j0 + t;
-        bool keep = false;
-        uint32_t idx = 0;
-        if (j < L) {
-            uint32_t key;
-            entry(j, &idx, &key);
-            const int bin = (int)(key >> 20);
-            const uint64_t v = ((uint64_t)(key & 0xFFFFFu) << 32) | (uint64_t)(~idx);
-            keep = bin > T || (bin == T && need > 0 && v >= prefix);
+    const uint32_t tkey = ((uint32_t)T << 20) | sub;  // the k_eff-th best score key
+    // ordered compaction: thread t owns a contiguous run of the global order; keys > tkey are
+    // kept, keys == tkey are kept while fewer than rem of them come earlier
+    const uint32_t per = (L + kSelThreads - 1) / kSelThreads;
+    const uint32_t j0 = per * (uint32_t)t, j1 = min(L, j0 + per);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (uint32_t j = j0; j < j1; j++) {
+        uint32_t idx, key;
+        entry(j, &idx, &key);
+        n_gt += key > tkey ? 1u : 0u;
+        n_eq += key == tkey ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t incl = block_scan((n_eq << 16) | n_gt, wsum, &tot);  // both counts < 2^16 when in LDS
+    uint32_t gt_before, eq_before;
+    if (in_lds) {
+        gt_before = (incl & 0xFFFFu) - n_gt;
+        eq_before = (incl >> 16) - n_eq;
+    } else {
+        // long lists: two separate scans (counts may exceed 16 bits)
+        uint32_t t1, t2;
+        gt_before = block_scan(n_gt, wsum, &t1) - n_gt;
+        eq_before = block_scan(n_eq, wsum, &t2) - n_eq;
+    }
+    for (uint32_t j = j0; j < j1; j++) {
+        uint32_t idx, key;
+        entry(j, &idx, &key);
+        if (key > tkey) {
+            const uint32_t p = gt_before + min(eq_before, rem);
+            if (p < k_eff) out[p] = (int32_t)idx;
+            gt_before++;
+        } else if (key == tkey) {
+            const uint32_t p = gt_before + eq_before;
+            if (eq_before < rem && p < k_eff) out[p] = (int32_t)idx;
+            eq_before++;
         }
-        uint32_t tot;
-        const uint32_t incl = block_scan(keep ? 1u : 0u, wsum, &tot);
-        const uint32_t pos = written + incl - (keep ? 1u : 0u);
-        if (keep && pos < k_eff) out[pos] = (int32_t)idx;
-        written += tot;
     }
     for (int j = (int)k_eff + t; j < P.k; j += kSelThreads) out[j] = -1;
 }
@@ -291,6 +318,7 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
     if (a.BQ == 0) return hipSuccess;
     SelParams P{};
     P.keys = a.score_keys;
+    P.key_stride = a.key_stride;
     P.hist = a.hist;
     P.copies = a.hist_copies > 0 ? a.hist_copies : 1;
     P.n_max = a.n_max;
