@@ -60,7 +60,7 @@ struct AttnParams {
     RopeTable rt;
     void *out;
     bool out_bf16;
-    float *part_o;           // [B][S][H][D]
+    float *part_o;           // [B][S][D/16][H][16]: per dim tile, the heads' 16 dims contiguous
     float *part_ml;          // [B][S][H][2]
     int S;                   // split capacity per sequence
     int target;              // splits aimed at per sequence
@@ -93,33 +93,32 @@ __device__ __forceinline__ float2 rope_unrotate(float2 cs, float x, float y) {
     return make_float2(x * cs.x + y * cs.y, -x * cs.y + y * cs.x);
 }
 
-template <int NV>
-__device__ __forceinline__ void store_out(const AttnParams &P, int b, int h, int d0, const float (&o)[NV]) {
+// Output of head h of query b, dims d0 .. d0+3 (d0 a multiple of 4): one 8- or 16-byte store.
+__device__ __forceinline__ void store_out4(const AttnParams &P, int b, int h, int d0, const float (&o)[4]) {
     const int64_t base = ((int64_t)b * P.H + h) * P.D + d0;
     if (P.out_bf16) {
-        uint16_t *dst = (uint16_t *)P.out + base;
-#pragma unroll
-        for (int v = 0; v < NV; v++) dst[v] = f32_to_bf16(o[v]);
+        const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *(uint2 *)((uint16_t *)P.out + base) = make_uint2(lo, hi);
     } else {
-        float *dst = (float *)P.out + base;
-#pragma unroll
-        for (int v = 0; v < NV; v++) dst[v] = o[v];
+        *(float4 *)((float *)P.out + base) = make_float4(o[0], o[1], o[2], o[3]);
     }
 }
 
-// Final output of one head from NV consecutive dims at d0 (NV even, pairs aligned).
-template <int NV>
-__device__ __forceinline__ void finish_head(const AttnParams &P, const SeqInfo &Sq, int b, int h,
-                                            int d0, float m2, float l, float (&o)[NV]) {
+// Final output of head h, dims d0 .. d0+3: normalisation with the sink, inverse RoPE on the
+// RoPE dims, cast.  Reached by the whole wavefront; rope_wave says whether any of its lanes
+// holds RoPE dims (uniform), so other wavefronts skip the cos/sin.
+__device__ __forceinline__ void finish4(const AttnParams &P, const SeqInfo &Sq, int b, int h, int d0,
+                                        bool rope_wave, float m2, float l, float (&o)[4]) {
     const float f = finish_factor(P, h, m2, l);
 #pragma unroll
-    for (int v = 0; v < NV; v++) o[v] *= f;
+    for (int v = 0; v < 4; v++) o[v] *= f;
     const int Dn = P.D - P.R;
-    if (P.rope_inv) {  // reached by the whole wavefront
+    if (P.rope_inv && rope_wave) {
         RopeLanes rl;
         rl.eval(P.rt, P.R / 2, (double)sq_pos(Sq, b));
 #pragma unroll
-        for (int v = 0; v < NV; v += 2) {
+        for (int v = 0; v < 4; v += 2) {
             const float2 cs = rl.get(min(max((d0 + v - Dn) / 2, 0), P.R / 2 - 1));
             if (d0 >= Dn) {
                 const float2 r = rope_unrotate(cs, o[v], o[v + 1]);
@@ -128,7 +127,7 @@ __device__ __forceinline__ void finish_head(const AttnParams &P, const SeqInfo &
             }
         }
     }
-    store_out<NV>(P, b, h, d0, o);
+    store_out4(P, b, h, d0, o);
 }
 
 // ------------------------------------------------------------------ MFMA kernel -----
@@ -384,12 +383,14 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 #pragma unroll
         for (int dt = 0; dt < NDT; dt++) {
             const float o[4] = {O[dt][0], O[dt][1], O[dt][2], O[dt][3]};
-            store_out<4>(P, b, h, 16 * dt + 4 * grp, o);
+            store_out4(P, b, h, 16 * dt + 4 * grp, o);
         }
     } else {
-        float *po = P.part_o + (((int64_t)b * P.S + split) * P.H + h) * D;
+        // each store writes 1 KB contiguous: the wavefront's 16 heads x 16 dims of one tile
+        // (streaming stores: the combine reads them once)
+        float *po = P.part_o + ((int64_t)(b * P.S + split) * NDT * P.H + h) * 16 + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) *(v4f *)(po + 16 * dt + 4 * grp) = O[dt];
+        for (int dt = 0; dt < NDT; dt++) __builtin_nontemporal_store(O[dt], (v4f *)(po + (int64_t)dt * P.H * 16));
         if (grp == 0) {
             float *pm = P.part_ml + (((int64_t)b * P.S + split) * P.H + h) * 2;
             pm[0] = m_run;
@@ -399,46 +400,55 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 }
 
 // ---------------------------------------------------------------- combine kernel ----
-// One wavefront per (head, sequence): fixed-order merge of the splits, the sink added once.
-template <int NV>
+// One wavefront per (16-dim tile, 16 heads, sequence): lane l holds head 16*hy + l/4 and dims
+// 16*dt + 4*(l%4) .. +3.  All splits' (m, l) are read first for the maximum; the partial tiles
+// (each one contiguous 1 KB read per split) are then merged in split order, eight loads in
+// flight, and the sink is added once (splits <= kMaxSplits).
+constexpr int kMaxSplits = 32;
+
 __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int dt = blockIdx.x, b = blockIdx.z, lane = threadIdx.x;
+    const int h = 16 * blockIdx.y + (lane >> 2);
+    const int d0 = 16 * dt + 4 * (lane & 3);
+    const int ndt = P.D / 16;
     const int n_keys = sq_n_ent(Sq, b) + sq_win_len(Sq, b);
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
-    if (splits == 1) return;
-    const int d0 = lane * NV;
-    if (d0 >= P.D) return;
-    // every split's (m, l) and partial output are loaded before the merge (splits <= 16)
-    float m2s[16], ls[16];
-    float po[16][NV];
+    if (splits == 1) return;  // uniform over the wavefront
+    float m2s[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
-    for (int s = 0; s < 16; s++) {
+    for (int s = 0; s < kMaxSplits; s++) {
         const int sc = s < splits ? s : 0;
-        const float *pm = P.part_ml + (((int64_t)b * P.S + sc) * P.H + h) * 2;
-        m2s[s] = pm[0];
-        ls[s] = pm[1];
-        const float *pp = P.part_o + (((int64_t)b * P.S + sc) * P.H + h) * P.D + d0;
-#pragma unroll
-        for (int v = 0; v < NV; v++) po[s][v] = pp[v];
+        const float2 ml = *(const float2 *)(P.part_ml + ((int64_t)(b * P.S + sc) * P.H + h) * 2);
+        m2s[s] = ml.x;
+        ls[s] = ml.y;
     }
     float M = P.sink[h] * kLog2e;
 #pragma unroll
-    for (int s = 0; s < 16; s++)
+    for (int s = 0; s < kMaxSplits; s++)
         if (s < splits) M = fmaxf(M, m2s[s]);
-    float o[NV];
-#pragma unroll
-    for (int v = 0; v < NV; v++) o[v] = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float l = 0.0f;
+    const float *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
+    const int64_t sstride = (int64_t)ndt * P.H * 16;
 #pragma unroll
-    for (int s = 0; s < 16; s++) {
-        const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
-        l = fmaf(ls[s], c, l);
+    for (int s0 = 0; s0 < kMaxSplits; s0 += 8) {
+        if (s0 >= splits) break;  // uniform
+        v4f po[8];
 #pragma unroll
-        for (int v = 0; v < NV; v++) o[v] = fmaf(po[s][v], c, o[v]);
+        for (int u = 0; u < 8; u++)
+            po[u] = __builtin_nontemporal_load((const v4f *)(pbase + (s0 + u < splits ? s0 + u : 0) * sstride));
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int s = s0 + u;
+            const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
+            l = fmaf(ls[s], c, l);
+#pragma unroll
+            for (int v = 0; v < 4; v++) o[v] = fmaf(po[u][v], c, o[v]);
+        }
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
-    finish_head<NV>(P, Sq, b, h, d0, M, l, o);
+    finish4(P, Sq, b, h, d0, 16 * dt + 16 > P.D - P.R, M, l, o);
 }
 
 // ---------------------------------------------------------------- fp32 kernel -------
@@ -613,10 +623,7 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
         hipLaunchKernelGGL((attn_mfma_kernel<128, 32>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
-    if (a.D == 512)
-        hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(a.H, a.B), dim3(64), 0, s, P, sq);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel<2>, dim3(a.H, a.B), dim3(64), 0, s, P, sq);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.D / 16, a.H / 16, a.B), dim3(64), 0, s, P, sq);
     return hipGetLastError();
 }
 
