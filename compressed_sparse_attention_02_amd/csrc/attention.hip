@@ -37,6 +37,7 @@ constexpr int kTile = 32;
 constexpr int kErStride = 520;  // bf16 per key row in Er (512 + 8: staggers LDS banks)
 constexpr int kEcStride = 36;   // bf16 per dim row in Ec (32 keys + 4)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running maximum may lag the scores
 constexpr int kMaxSelKeys = 2048;  // top-k entries per sequence (k <= 2048)
 
 struct AttnParams {
@@ -138,8 +139,8 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
     constexpr int Dn = D - R;
     __shared__ __attribute__((aligned(16))) uint16_t Er[kTile * kErStride];
     __shared__ __attribute__((aligned(16))) uint16_t Ec[D * kEcStride];
-    __shared__ float ksc[kTile];
-    __shared__ int kvalid[kTile];
+    __shared__ __attribute__((aligned(16))) float ksc[kTile];
+    __shared__ __attribute__((aligned(16))) int kvalid[kTile];
     __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
 
     // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart
@@ -282,7 +283,10 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 if (!valid[j]) v[j] = make_uint4(0, 0, 0, 0);
-                *(uint4 *)(Er + (4 * kg + j) * kErStride + dim) = v[j];
+                // 16-byte chunk seg of key row r sits at chunk seg ^ ((r >> 3) & 3): the eight
+                // rows 4kg + j written together then fall in distinct LDS banks
+                const int r = 4 * kg + j;
+                *(uint4 *)(Er + r * kErStride + 8 * (seg ^ ((r >> 3) & 3))) = v[j];
             }
             // dim-major: row dim+d holds keys 4kg..4kg+3
 #pragma unroll
@@ -295,8 +299,10 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                     case 2: w0 = v[0].z; w1 = v[1].z; w2 = v[2].z; w3 = v[3].z; break;
                     default: w0 = v[0].w; w1 = v[1].w; w2 = v[2].w; w3 = v[3].w; break;
                 }
-                const uint32_t a0 = ((w0 >> sh) & 0xFFFFu) | (((w1 >> sh) & 0xFFFFu) << 16);
-                const uint32_t a1 = ((w2 >> sh) & 0xFFFFu) | (((w3 >> sh) & 0xFFFFu) << 16);
+                // the 16-bit halves (low for even d, high for odd d) of keys 4kg..4kg+3, paired
+                const uint32_t sel = sh ? 0x07060302u : 0x05040100u;
+                const uint32_t a0 = __builtin_amdgcn_perm(w1, w0, sel);
+                const uint32_t a1 = __builtin_amdgcn_perm(w3, w2, sel);
                 *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
             }
         }
@@ -304,21 +310,26 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
         if (!wave_on) continue;
 
         // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
-        float s2[8];
+        float s2[8], ks8[8];
 #pragma unroll
         for (int st = 0; st < 2; st++) {
             v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-            const uint16_t *arow = Er + (16 * st + col) * kErStride + 8 * grp;
+            const int r = 16 * st + col;
+            const uint16_t *arow = Er + r * kErStride + 8 * (grp ^ ((r >> 3) & 3));
 #pragma unroll
             for (int ks = 0; ks < NKS; ks++) {
                 const v8bf a = __builtin_bit_cast(v8bf, *(const uint4 *)(arow + 32 * ks));
                 if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
                 else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
             }
+            const float4 sc4 = *(const float4 *)(ksc + 16 * st + 4 * grp);
+            const int4 kv4 = *(const int4 *)(kvalid + 16 * st + 4 * grp);
+            const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+            const int kvv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int key = 16 * st + 4 * grp + i;
-                s2[4 * st + i] = kvalid[key] ? P.scale2 * fmaf(ksc[key], an[i], ar[i]) : -INFINITY;
+                s2[4 * st + i] = kvv[i] ? P.scale2 * fmaf(scv[i], an[i], ar[i]) : -INFINITY;
+                ks8[4 * st + i] = scv[i];
             }
         }
         // ---- online softmax (exp2 domain); lane: head h, keys {4grp+i, 16+4grp+i}
@@ -327,28 +338,29 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
         for (int i = 1; i < 8; i++) mt = fmaxf(mt, s2[i]);
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        if (m_new > m_run) {  // same decision in all four lanes of a head
-            const float alpha = exp2f(m_run - m_new);  // 0 when m_run = -inf
+        // The running reference moves only when a score exceeds it by more than kRescaleSlack
+        // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
+        // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
+        if (mt > m_run + kRescaleSlack) {
+            const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < NDT; i++) O[i] *= alpha;
-            m_run = m_new;
+            m_run = mt;
         }
         float pn[8], pr[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int key = (i < 4) ? (4 * grp + i) : (16 + 4 * grp + i - 4);
             const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
             l_run += pi;
             pr[i] = pi;
-            pn[i] = pi * ksc[key];
+            pn[i] = pi * ks8[i];
         }
-        v8bf Pn, Pr;
+        v8bf Pn, Pr;  // round to nearest even (v_cvt_pk_bf16_f32)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            Pn[i] = __builtin_bit_cast(__bf16, f32_to_bf16(pn[i]));
-            Pr[i] = __builtin_bit_cast(__bf16, f32_to_bf16(pr[i]));
+            Pn[i] = (__bf16)pn[i];
+            Pr[i] = (__bf16)pr[i];
         }
         // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
 #pragma unroll

@@ -83,10 +83,35 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     const int64_t keys_per_wg = (int64_t)4 * P.groups_per_wave * 16;
     const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
     if (k0 >= n_vis) return;  // uniform over the workgroup
-    for (int bin = threadIdx.x; bin < kHistBins; bin += 256) lhist[bin] = 0;
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;  // col: head/key within 16; grp: MX block / chain
+
+    const uint8_t *kc = P.kc + (int64_t)b * P.kcap * 64;
+    const uint8_t *ks = P.ks + (int64_t)b * P.kcap * 4;
+    const int64_t kend = k0 + keys_per_wg < n_vis ? k0 + keys_per_wg : n_vis;
+    uint32_t *hist = P.hist ? lhist : nullptr;
+    const int64_t wbase = k0 + (int64_t)wv * P.groups_per_wave * 16;
+    const int n_it = P.groups_per_wave / kGroupsPerIter;
+
+    // Double-buffered: the loads of iteration it+1 are issued before iteration it is computed.
+    // Lanes past the end read a clamped, valid key of this query and are masked afterwards.
+    auto load_iter = [&](int it, uint4 (&kd)[kGroupsPerIter], uint32_t (&ksc)[kGroupsPerIter]) {
+        const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
+#pragma unroll
+        for (int u = 0; u < kGroupsPerIter; u++) {
+            int64_t key = base + 16 * u + col;
+            key = key < kend ? key : kend - 1;
+            const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16));
+            kd[u] = make_uint4(v.x, v.y, v.z, v.w);
+            ksc[u] = *(const uint32_t *)(ks + key * 4);
+        }
+    };
+    // the first key batch is requested before the query, so the two latencies overlap
+    uint4 kdA[kGroupsPerIter], kdB[kGroupsPerIter];
+    uint32_t kscA[kGroupsPerIter], kscB[kGroupsPerIter];
+    if (wbase < kend) load_iter(0, kdA, kscA);
+    for (int bin = threadIdx.x; bin < kHistBins; bin += 256) lhist[bin] = 0;
 
     // query: 4 head groups of 16 heads; lane holds head 16g+col, MX block grp.  Heads past H
     // read head H-1 (all loads issued together) and are zeroed: code 0 and weight 0.
@@ -118,26 +143,6 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     }
     __syncthreads();
 
-    const uint8_t *kc = P.kc + (int64_t)b * P.kcap * 64;
-    const uint8_t *ks = P.ks + (int64_t)b * P.kcap * 4;
-    const int64_t kend = k0 + keys_per_wg < n_vis ? k0 + keys_per_wg : n_vis;
-    uint32_t *hist = P.hist ? lhist : nullptr;
-    const int64_t wbase = k0 + (int64_t)wv * P.groups_per_wave * 16;
-    const int n_it = P.groups_per_wave / kGroupsPerIter;
-
-    // Double-buffered: the loads of iteration it+1 are issued before iteration it is computed.
-    // Lanes past the end read a clamped, valid key of this query and are masked afterwards.
-    auto load_iter = [&](int it, uint4 (&kd)[kGroupsPerIter], uint32_t (&ksc)[kGroupsPerIter]) {
-        const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
-#pragma unroll
-        for (int u = 0; u < kGroupsPerIter; u++) {
-            int64_t key = base + 16 * u + col;
-            key = key < kend ? key : kend - 1;
-            const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16));
-            kd[u] = make_uint4(v.x, v.y, v.z, v.w);
-            ksc[u] = *(const uint32_t *)(ks + key * 4);
-        }
-    };
     auto compute_iter = [&](int it, const uint4 (&kd)[kGroupsPerIter], const uint32_t (&ksc)[kGroupsPerIter]) {
         const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
         float c[kGroupsPerIter];
@@ -181,9 +186,6 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
             }
         }
     };
-    uint4 kdA[kGroupsPerIter], kdB[kGroupsPerIter];
-    uint32_t kscA[kGroupsPerIter], kscB[kGroupsPerIter];
-    if (wbase < kend) load_iter(0, kdA, kscA);
     for (int it = 0; it < n_it; it += 2) {
         if (wbase + (int64_t)it * kGroupsPerIter * 16 >= kend) break;  // uniform over the wavefront
         const bool more1 = it + 1 < n_it && wbase + (int64_t)(it + 1) * kGroupsPerIter * 16 < kend;
