@@ -413,9 +413,9 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
 
 // ---------------------------------------------------------------- combine kernel ----
 // One wavefront per (16-dim tile, 16 heads, sequence): lane l holds head 16*hy + l/4 and dims
-// 16*dt + 4*(l%4) .. +3.  All splits' (m, l) are read first for the maximum; the partial tiles
-// (each one contiguous 1 KB read per split) are then merged in split order, eight loads in
-// flight, and the sink is added once (splits <= kMaxSplits).
+// 16*dt + 4*(l%4) .. +3.  The splits' (m, l) and partial tiles (each one contiguous 1 KB read
+// per split) are requested together; the tiles are then merged in split order and the sink
+// is added once (splits <= kMaxSplits).
 constexpr int kMaxSplits = 32;
 
 __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
@@ -427,7 +427,14 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
     if (splits == 1) return;  // uniform over the wavefront
+    // every split's (m, l) and the first 16 partial tiles are requested before any is used
     float m2s[kMaxSplits], ls[kMaxSplits];
+    const float *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
+    const int64_t sstride = (int64_t)ndt * P.H * 16;
+    v4f po[16];
+#pragma unroll
+    for (int s = 0; s < 16; s++)
+        po[s] = __builtin_nontemporal_load((const v4f *)(pbase + (s < splits ? s : 0) * sstride));
 #pragma unroll
     for (int s = 0; s < kMaxSplits; s++) {
         const int sc = s < splits ? s : 0;
@@ -441,22 +448,23 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
         if (s < splits) M = fmaxf(M, m2s[s]);
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float l = 0.0f;
-    const float *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
-    const int64_t sstride = (int64_t)ndt * P.H * 16;
 #pragma unroll
-    for (int s0 = 0; s0 < kMaxSplits; s0 += 8) {
-        if (s0 >= splits) break;  // uniform
-        v4f po[8];
+    for (int s = 0; s < 16; s++) {
+        const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
+        l = fmaf(ls[s], c, l);
 #pragma unroll
-        for (int u = 0; u < 8; u++)
-            po[u] = __builtin_nontemporal_load((const v4f *)(pbase + (s0 + u < splits ? s0 + u : 0) * sstride));
+        for (int v = 0; v < 4; v++) o[v] = fmaf(po[s][v], c, o[v]);
+    }
+    if (splits > 16) {  // uniform over the wavefront
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int s = s0 + u;
+        for (int s = 16; s < kMaxSplits; s++)
+            po[s - 16] = __builtin_nontemporal_load((const v4f *)(pbase + (s < splits ? s : 0) * sstride));
+#pragma unroll
+        for (int s = 16; s < kMaxSplits; s++) {
             const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
             l = fmaf(ls[s], c, l);
 #pragma unroll
-            for (int v = 0; v < 4; v++) o[v] = fmaf(po[u][v], c, o[v]);
+            for (int v = 0; v < 4; v++) o[v] = fmaf(po[s - 16][v], c, o[v]);
         }
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
