@@ -2,7 +2,7 @@
 """Benchmark of the DeepSeek-V4 CSA/HCA decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
-                    [--no-secondary] [--graphs] [--copy-probe]
+                    [--no-secondary] [--copy-probe]
 
 A step is one CSA decode step of the 1M-context workload (4 sequences at position
 1,048,575, 262,144 compressed entries each, 128 query heads, head dim 512, 64 MXFP4
@@ -14,14 +14,16 @@ indexer heads, top-1024, 128-token window, sink):
   3. attend over the selected entries plus the window with the sink, then combine the splits.
 Inputs are seeded synthetic data (N(0,1) before quantisation).  Every input set is cloned
 R times in HBM and step i uses set i mod R, so the 256 MB Infinity Cache cannot hold the
-working set; the inputs are resident in HBM when timing starts.  Calls are launched
-directly on one stream (--graphs replays captured per-stage HIP graphs instead).
+working set; the inputs are resident in HBM when timing starts.  The timed step is one
+v4a_decode_step_csa call, launched directly on one stream.
 
 One JSON line is printed: throughput (tokens/s = sequences decoded per second), the roofline
 of the dominant launch (the indexer + top-k call, whose MXFP4 scoring kernel streams the
-keys) measured live with HIP events on the stream the kernels run on, the oracle timed on
-the host cores, a parity check of set 0 against the oracle, and secondary figures: the
-1M-context HCA decode step and one 4096-token prefill chunk per layer kind.
+keys), timed live with HIP events on the stream the kernels run on in a second timed loop of
+the same step composed of the separate entry points (the fused call offers no boundary to
+place events at), the oracle timed on the host cores, a parity check of set 0 against the
+oracle, and secondary figures: the 1M-context HCA decode step and one 4096-token prefill
+chunk per layer kind.
 
 --copy-probe first runs a plain device copy (an elementwise negation of 1 GiB) five times, so
 that a hardware-counter run of this command can scale FETCH_SIZE / WRITE_SIZE by what the
@@ -60,7 +62,6 @@ def parse():
     p.add_argument("--rotate", type=int, default=16, help="input copies cycled through (MALL defeat)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--graphs", action="store_true", help="replay captured per-stage HIP graphs")
     p.add_argument("--copy-probe", action="store_true", help="run the 1 GiB copy used to scale counters")
     return p.parse_args()
 
@@ -153,25 +154,43 @@ def main():
         v4.v4a_decode_csa(st["q"], st["kv"], sel.view(B, k), k, st["win"], win_len, W, st["sink"], q_pos,
                           softmax_scale=scale, out=out, ws=ws)
 
-    def stage_compress_records(st):
-        v4.v4a_compress_csa(st["kv_a"], st["kv_b"], st["gate_a"], st["gate_b"], st["bias_a"], st["bias_b"],
-                            tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_kv=st["kv"])
+    # the step as one call (compression + histogram clear in one launch, then selection and
+    # attention) on every input set
+    step_args = [[v4.DecodeStepArgs(q_pos=q_pos, n_entries=[N] * B, m=m, kv_a=st["kv_a"], kv_b=st["kv_b"],
+                                     gate_a=st["gate_a"], gate_b=st["gate_b"], bias_a=st["bias_a"],
+                                     bias_b=st["bias_b"], idx_a=st["idx_a"], idx_b=st["idx_b"],
+                                     idx_gate_a=st["idx_gate_a"], idx_gate_b=st["idx_gate_b"],
+                                     idx_bias_a=st["idx_bias_a"], idx_bias_b=st["idx_bias_b"], kv=st["kv"],
+                                     keys=st["keys"], q_idx=st["qi"], w=st["w"], k=k, q=st["q"], win=st["win"],
+                                     win_len=win_len, W=W, sink=st["sink"], softmax_scale=scale, out=outs[j])
+                  for j in range(2)] for st in sets]
+    step_ws = v4.workspace(v4.v4a_decode_step_workspace(step_args[0][0]))
 
-    def stage_compress_keys(st):
+    def step(i):
+        v4.v4a_decode_step_csa(step_args[i % len(sets)][i % 2], step_ws)
+
+    def step_separate(i, ev):
+        # the same step composed of the separate entry points, with HIP events around the
+        # indexer + top-k call (the record compressor, read only by attention, runs on a
+        # second stream meanwhile)
+        st = sets[i % len(sets)]
+        main = torch.cuda.current_stream()
+        ev_start.record(main)
+        side_rec.wait_event(ev_start)
+        with torch.cuda.stream(side_rec):
+            v4.v4a_compress_csa(st["kv_a"], st["kv_b"], st["gate_a"], st["gate_b"], st["bias_a"], st["bias_b"],
+                                tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_kv=st["kv"])
+        ev_rec.record(side_rec)
         v4.v4a_compress_csa(st["idx_a"], st["idx_b"], st["idx_gate_a"], st["idx_gate_b"], st["idx_bias_a"],
                             st["idx_bias_b"], tok0=tok0, m=m, first_entry=N - 1, n_entries=1, out_idx=st["keys"])
-
-    def step_eager(i):
-        st = sets[i % len(sets)]
-        stage_compress(st)
+        ev[0].record()
         stage_indexer(st)
+        ev[1].record()
+        main.wait_event(ev_rec)
         stage_attend(st, outs[i % 2])
 
-    # the new entry record is only read by attention: it is compressed on a second stream
-    # while the key compressor, the indexer and the selection run on the main one
     side_rec = torch.cuda.Stream()
-    ev_start = [torch.cuda.Event() for _ in range(2)]
-    ev_rec = [torch.cuda.Event() for _ in range(2)]
+    ev_start, ev_rec = torch.cuda.Event(), torch.cuda.Event()
 
     if args.copy_probe:
         src = torch.randn((COPY_PROBE_BYTES // 4,), device=dev)
@@ -181,74 +200,37 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    graphs = None
-    if args.graphs:
-        # each input set's step is captured as three graphs (compress, indexer + top-k,
-        # attention); replaying them between HIP events times the indexer stage live
-        print("[bench] capturing graphs", file=sys.stderr, flush=True)
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step_eager(0)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graphs = []
-        for r, st in enumerate(sets):
-            gs = []
-            for fn in (lambda: stage_compress(st), lambda: stage_indexer(st),
-                       lambda: stage_attend(st, outs[r % 2])):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    fn()
-                gs.append(g)
-            graphs.append(gs)
-        torch.cuda.synchronize()
-
-    def step(i, ev=None):
-        if graphs is None:
-            st = sets[i % len(sets)]
-            main = torch.cuda.current_stream()
-            ev_start[i % 2].record(main)
-            side_rec.wait_event(ev_start[i % 2])
-            with torch.cuda.stream(side_rec):
-                stage_compress_records(st)
-            ev_rec[i % 2].record(side_rec)
-            stage_compress_keys(st)
-            if ev is not None:
-                ev[0].record()
-            stage_indexer(st)
-            if ev is not None:
-                ev[1].record()
-            main.wait_event(ev_rec[i % 2])
-            stage_attend(st, outs[i % 2])
-            return
-        g = graphs[i % len(graphs)]
-        g[0].replay()
-        if ev is not None:
-            ev[0].record()
-        g[1].replay()
-        if ev is not None:
-            ev[1].record()
-        g[2].replay()
-
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     tok_s = B / (ms_step / 1e3)
+
+    # the indexer + top-k call timed live inside the composed step
+    n_sep = max(10, args.steps // 2)
+    for i in range(args.warmup):
+        step_separate(i, (torch.cuda.Event(), torch.cuda.Event()))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_sep)]
+    s_start, s_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_start.record()
+    for i in range(n_sep):
+        step_separate(args.warmup + i, evs[i])
+    s_end.record()
+    torch.cuda.synchronize()
+    ms_step_sep = s_start.elapsed_time(s_end) / n_sep
+    idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     # algorithmic bytes of the indexer + top-k call: keys, indexer queries and weights read,
     # the top-k list written
@@ -261,12 +243,15 @@ def main():
         B * ntok * (D + dI) * 2 * 2
     step_flops = idx_flops + 4.0 * B * H * D * (k + W)
 
-    # parity of the last step on set 0 against the oracle (sequence 0, full indexer scan)
+    # parity of the step on set 0 against the oracle (sequence 0, full indexer scan); the
+    # fused call must give bitwise the composed calls' output
+    step_separate(0, (torch.cuda.Event(), torch.cuda.Event()))
+    torch.cuda.synchronize()
+    gpu_sel = sel.cpu().numpy()[:, 0]
+    sep_out = outs[0].clone()
     step(0)
     torch.cuda.synchronize()
-    used_graphs = graphs is not None
-    graphs = None
-    gpu_sel = sel.cpu().numpy()[:, 0]
+    fused_equal = bool(torch.equal(sep_out, outs[0]))
     gpu_out = outs[0].float().cpu().numpy()
 
     result = {
@@ -275,7 +260,7 @@ def main():
         "vs_baseline": None, "dtype": "mxfp4+bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "context_tokens": T, "csa_entries": N, "heads": H,
                    "head_dim": D, "rope_dims": R, "indexer_heads": HI, "indexer_dim": dI, "topk": k,
-                   "window": W, "input_copies": len(sets), "hip_graphs": used_graphs},
+                   "window": W, "input_copies": len(sets), "entry_point": "v4a_decode_step_csa"},
         "roofline": {"kernel": "v4a_indexer_topk call: zero_kernel + indexer_mxfp4_kernel + select_scan_kernel "
                                "+ select_final_kernel", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -283,11 +268,12 @@ def main():
                      "mfma_util": idx_flops / (idx_ms / 1e3) / (MXFP4_PEAK_TFLOPS * 1e12)},
         "step": {"algorithmic_bytes": step_bytes, "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9,
                  "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, "flops": step_flops,
+                 "ms_separate_calls": ms_step_sep,
                  "wall_s": wall},
     }
 
     if not args.no_secondary:
-        del sets, graphs
+        del sets, step_args
         torch.cuda.empty_cache()
         result["secondary"] = {"hca_decode_1m": hca_secondary(v4, torch, HCA_1M, args, f32, bf16)}
         torch.cuda.empty_cache()
@@ -328,7 +314,8 @@ def main():
                                   "sample": "sequence 0 of the same step: compress its new block, exact MXFP4 "
                                             "scores of all 262144 entries, full-sort top-1024, double-precision "
                                             "attention (1 token)"}
-        result["check"] = {"sequence": 0, "topk_equal": bool(np.array_equal(gpu_sel[b], ref_sel)),
+        result["check"] = {"sequence": 0, "fused_equals_separate_calls": fused_equal,
+                           "topk_equal": bool(np.array_equal(gpu_sel[b], ref_sel)),
                            "topk_recall": recall, "max_abs": float(err.max()),
                            "rel_l2": float(np.linalg.norm(gpu_out[b] - ref_bf16) / np.linalg.norm(ref_bf16)),
                            "inexact_dots": bad}

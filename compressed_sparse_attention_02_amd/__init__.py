@@ -58,6 +58,20 @@ class c_prefill_args(ctypes.Structure):
 
 V4A_LAYER_CSA, V4A_LAYER_HCA = 0, 1
 
+
+class c_decode_step_args(ctypes.Structure):
+    P = ctypes.c_void_p
+    _fields_ = [("B", ctypes.c_int32), ("m", ctypes.c_int32), ("q_pos", P), ("n_entries", P),
+                ("in_t", ctypes.c_int), ("G", ctypes.c_int32), ("idx_G", ctypes.c_int32),
+                ("kv_a", P), ("kv_b", P), ("gate_a", P), ("gate_b", P), ("bias_a", P), ("bias_b", P),
+                ("idx_a", P), ("idx_b", P), ("idx_gate_a", P), ("idx_gate_b", P), ("idx_bias_a", P),
+                ("idx_bias_b", P), ("apply_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("kv", ctypes.POINTER(c_kv)), ("keys", ctypes.POINTER(c_idx)), ("q_idx", ctypes.POINTER(c_idx)),
+                ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
+                ("H", ctypes.c_int32), ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32),
+                ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
+                ("out", P), ("out_t", ctypes.c_int)]
+
 _lib = None
 
 
@@ -89,6 +103,11 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        DSP = ctypes.POINTER(c_decode_step_args)
+        L.v4a_decode_step_csa.argtypes = [DSP, P, SZ, P]
+        L.v4a_decode_step_csa.restype = ctypes.c_int
+        L.v4a_decode_step_workspace.argtypes = [DSP]
+        L.v4a_decode_step_workspace.restype = SZ
         PAP = ctypes.POINTER(c_prefill_args)
         L.v4a_prefill_chunk.argtypes = [ctypes.c_int, PAP, P, SZ, P]
         L.v4a_prefill_chunk.restype = ctypes.c_int
@@ -313,6 +332,40 @@ def v4a_prefill_workspace(kind: int, args: PrefillArgs) -> int:
 def v4a_prefill_chunk(kind: int, args: PrefillArgs, ws: torch.Tensor | None = None, stream=None):
     _check(lib().v4a_prefill_chunk(kind, ctypes.byref(args.s), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class DecodeStepArgs:
+    """The arguments of one fused CSA decode step (v4a_decode_step_args), holding every tensor
+    and host array it points to.  Streams hold [B][2m] rows per sequence."""
+
+    def __init__(self, *, q_pos, n_entries, m: int, kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b,
+                 idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
+                 win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
+                 rope_theta: float = 10000.0, out_rope_inverse: bool = True):
+        B, H = q.shape[0], q.shape[1]
+        self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
+        self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
+        self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b, idx_bias_a,
+                      idx_bias_b, kv, keys, q_idx, w, q, win, sink, out)
+        self.s = c_decode_step_args(
+            B=B, m=m, q_pos=ctypes.cast(self._pos, ctypes.c_void_p), n_entries=ctypes.cast(self._nent, ctypes.c_void_p),
+            in_t=_ftype(kv_a), G=gate_a.shape[-1], idx_G=idx_gate_a.shape[-1], kv_a=_ptr(kv_a), kv_b=_ptr(kv_b),
+            gate_a=_ptr(gate_a), gate_b=_ptr(gate_b), bias_a=_ptr(bias_a), bias_b=_ptr(bias_b), idx_a=_ptr(idx_a),
+            idx_b=_ptr(idx_b), idx_gate_a=_ptr(idx_gate_a), idx_gate_b=_ptr(idx_gate_b),
+            idx_bias_a=_ptr(idx_bias_a), idx_bias_b=_ptr(idx_bias_b), apply_rope=int(apply_rope),
+            rope_theta=rope_theta, kv=ctypes.pointer(self._kv), keys=ctypes.pointer(self._keys),
+            q_idx=ctypes.pointer(self._q_idx), w=_ptr(w), H_I=w.numel() // B, k=k, q=_ptr(q), q_t=_ftype(q), H=H,
+            win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
+            softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out))
+
+
+def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:
+    return int(lib().v4a_decode_step_workspace(ctypes.byref(args.s)))
+
+
+def v4a_decode_step_csa(args: DecodeStepArgs, ws: torch.Tensor, stream=None):
+    _check(lib().v4a_decode_step_csa(ctypes.byref(args.s), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

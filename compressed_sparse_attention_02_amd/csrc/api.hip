@@ -329,12 +329,15 @@ namespace v4a {
 // Launches of the indexer + top-k call once every argument has been checked.
 static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, int64_t n_max, const v4a_idx *q_idx,
                                       const float *w, int32_t B, int32_t Q, int32_t H_I, int32_t k, int32_t *out_idx,
-                                      void *ws, hipStream_t s) {
+                                      void *ws, hipStream_t s, bool clear_hist = true) {
     const TopkWs L = topk_layout(B, Q, n_max, k);
     char *base = (char *)ws;
     const size_t BQ = (size_t)B * Q;
-    hipError_t e = launch_zero(base + L.hist, BQ * hist_copies((int64_t)BQ) * kHistBins * 4, s);
-    if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
+    hipError_t e = hipSuccess;
+    if (clear_hist) {
+        e = launch_zero(base + L.hist, BQ * hist_copies((int64_t)BQ) * kHistBins * 4, s);
+        if (e != hipSuccess) return hip_status(e, "v4a_indexer_topk: clear");
+    }
     IndexerArgs ia{};
     ia.keys = keys;
     ia.q = q_idx;
@@ -427,9 +430,11 @@ static size_t decode_ws_bytes(int B, int H, int D, int split_cap) {
     return round_up((size_t)B * split_cap * H * D * 4 + (size_t)B * split_cap * H * 2 * 4, 256);
 }
 
-static v4a_status decode_common(AttnArgs &a, SeqInfo &sq, const int32_t *win_len, const int64_t *q_pos,
-                                v4a_float q_t, v4a_float win_t, v4a_float out_t, void *ws, size_t ws_bytes,
-                                void *stream, const char *name) {
+// Checks a decode call's attention arguments, fills the per-sequence window lengths and
+// positions and the split plan, and returns the workspace it needs; launches nothing.
+static v4a_status decode_prepare(AttnArgs &a, SeqInfo &sq, const int32_t *win_len, const int64_t *q_pos,
+                                 v4a_float q_t, v4a_float win_t, v4a_float out_t, size_t *ws_need,
+                                 const char *name) {
     if (!a.q || !a.out || !a.sink || !q_pos) return fail(V4A_EINVAL, "%s: q, out, sink and q_pos are required", name);
     if (a.B < 1 || a.B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "%s: B=%d not in [1, %d]", name, a.B, kMaxSeq);
     if (a.H < 1 || a.H > 128) return fail(V4A_EUNSUPPORTED, "%s: H=%d not in [1, 128]", name, a.H);
@@ -468,15 +473,25 @@ static v4a_status decode_common(AttnArgs &a, SeqInfo &sq, const int32_t *win_len
             if (sp > cap) cap = sp;
         }
         a.split_cap = cap;
-        const size_t need = decode_ws_bytes(a.B, a.H, a.D, cap);
-        if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
-            return fail(V4A_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need, ws_bytes);
-        a.partial = need > 0 ? (float *)ws : nullptr;
+        *ws_need = decode_ws_bytes(a.B, a.H, a.D, cap);
     } else {
         a.target_splits = 1;
         a.split_cap = 1;
-        a.partial = nullptr;
+        *ws_need = 0;
     }
+    a.partial = nullptr;
+    return V4A_OK;
+}
+
+static v4a_status decode_common(AttnArgs &a, SeqInfo &sq, const int32_t *win_len, const int64_t *q_pos,
+                                v4a_float q_t, v4a_float win_t, v4a_float out_t, void *ws, size_t ws_bytes,
+                                void *stream, const char *name) {
+    size_t need = 0;
+    v4a_status st = decode_prepare(a, sq, win_len, q_pos, q_t, win_t, out_t, &need, name);
+    if (st != V4A_OK) return st;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return fail(V4A_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need, ws_bytes);
+    a.partial = need > 0 ? (float *)ws : nullptr;
     g_err.clear();
     return hip_status(launch_attention(a, sq, (hipStream_t)stream), name);
 }
@@ -779,6 +794,128 @@ v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *a, void *ws
     sq.fixed_ent = pl.csa ? a->k : 0;
     sq.n_total = pl.n_total;
     return hip_status(launch_attention(at, sq, s), "v4a_prefill_chunk: attention");
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------- fused CSA decode step ----
+namespace v4a {
+
+struct StepPlan {
+    CompressArgs rec, key;
+    int64_t entry[kMaxSeq];
+    QueryPos qp;
+    int64_t n_max;
+    AttnArgs at;
+    SeqInfo sq;
+    v4a_kv kv;
+    size_t sel_bytes, topk_bytes, attn_bytes, total;
+};
+
+static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
+    if (!a) return fail(V4A_EINVAL, "v4a_decode_step_csa: args is NULL");
+    pl = StepPlan{};
+    if (a->B < 1 || a->B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: B=%d not in [1, %d]", a->B, kMaxSeq);
+    if (!a->q_pos || !a->n_entries) return fail(V4A_EINVAL, "v4a_decode_step_csa: q_pos and n_entries are required");
+    v4a_status st;
+    if ((st = check_kv(a->kv, "kv")) != V4A_OK) return st;
+    if ((st = check_idx(a->keys, "keys")) != V4A_OK) return st;
+    if (a->in_t != V4A_F32 && a->in_t != V4A_BF16) return fail(V4A_EINVAL, "v4a_decode_step_csa: in_t");
+    const int D = a->kv->D, d = a->keys->d, m = a->m;
+    if (!((D == 512 && d == 128) || (D == 128 && d == 32)))
+        return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs D=512 with d=128 or D=128 with d=32");
+    // compressor arguments, checked as one entry at rows [0, 2m) (the per-sequence entries and
+    // row origins are set at launch)
+    auto fill = [&](CompressArgs &c, const void *xa, const void *xb, const float *ga, const float *gb,
+                     const float *ba, const float *bb, int Dd, int G) {
+        c.x[0] = xa; c.x[1] = xb; c.gate[0] = ga; c.gate[1] = gb; c.bias[0] = ba; c.bias[1] = bb;
+        c.n_streams = 2; c.bf16_in = a->in_t == V4A_BF16; c.D = Dd; c.G = G; c.m = m;
+        c.tok0 = 0; c.n_tok = 2 * m; c.first_entry = 1; c.n_entries = 1;
+        c.theta = a->rope_theta; c.b0 = 0; c.n_seq = a->B;
+    };
+    fill(pl.rec, a->kv_a, a->kv_b, a->gate_a, a->gate_b, a->bias_a, a->bias_b, D, a->G);
+    pl.rec.rope = a->apply_rope != 0;
+    pl.rec.kv = a->kv;
+    if ((st = compress_check(pl.rec, nullptr)) != V4A_OK) return st;
+    fill(pl.key, a->idx_a, a->idx_b, a->idx_gate_a, a->idx_gate_b, a->idx_bias_a, a->idx_bias_b, d, a->idx_G);
+    pl.key.idx = a->keys;
+    if ((st = compress_check(pl.key, nullptr)) != V4A_OK) return st;
+    for (int b = 0; b < a->B; b++) {
+        const int64_t t = a->q_pos[b];
+        if (t < 0) return fail(V4A_EINVAL, "v4a_decode_step_csa: q_pos[%d] < 0", b);
+        const int64_t i = (t + 1) % m == 0 ? (t + 1) / m - 1 : -1;
+        if (i >= a->n_entries[b])
+            return fail(V4A_EINVAL, "v4a_decode_step_csa: n_entries[%d] does not include the entry this step completes", b);
+        if (i >= a->kv->cap || i >= a->keys->cap)
+            return fail(V4A_EINVAL, "v4a_decode_step_csa: entry %lld of sequence %d exceeds the cache", (long long)i, b);
+        pl.entry[b] = i;
+    }
+    // selection
+    if ((st = check_indexer_args(a->keys, a->n_entries, m, a->q_idx, a->w, a->B, 1, a->H_I, a->q_pos)) != V4A_OK)
+        return st;
+    if (a->k < 1 || a->k > 2048) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: k=%d not in [1, 2048]", a->k);
+    if ((st = fill_query_pos(pl.qp, a->B, 1, m, a->n_entries, a->q_pos, a->keys->cap, &pl.n_max)) != V4A_OK) return st;
+    if (pl.n_max > (int64_t)1024 * kSelSlice) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: too many entries");
+    // attention
+    AttnArgs &at = pl.at;
+    at.q = a->q;
+    at.B = a->B;
+    at.H = a->H;
+    at.kv = a->kv;
+    at.kv_bstride = a->kv->cap;
+    at.k = a->k;
+    at.win = a->win;
+    at.W = a->W;
+    at.sink = a->sink;
+    at.scale = a->softmax_scale;
+    at.rope_inv = a->out_rope_inverse != 0;
+    at.theta = a->rope_theta;
+    at.out = a->out;
+    memset(&pl.sq, 0, sizeof pl.sq);
+    for (int b = 0; b < a->B; b++) pl.sq.n_ent[b] = a->k;
+    size_t attn_need = 0;
+    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &attn_need,
+                             "v4a_decode_step_csa")) != V4A_OK)
+        return st;
+    if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs the MFMA attention shapes");
+    pl.sel_bytes = round_up((size_t)a->B * a->k * 4, 256);
+    pl.topk_bytes = topk_layout(a->B, 1, pl.n_max, a->k).total;
+    pl.attn_bytes = round_up(attn_need, 256);
+    pl.total = pl.sel_bytes + pl.topk_bytes + pl.attn_bytes;
+    return V4A_OK;
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+size_t v4a_decode_step_workspace(const v4a_decode_step_args *args) {
+    StepPlan pl;
+    if (step_plan(args, pl) != V4A_OK) return 0;
+    return pl.total;
+}
+
+v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t ws_bytes, void *stream) {
+    StepPlan pl;
+    v4a_status st = step_plan(a, pl);
+    if (st != V4A_OK) return st;
+    if (!ws || ws_bytes < pl.total || !aligned(ws, 256))
+        return fail(V4A_EWORKSPACE, "v4a_decode_step_csa: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    pl.total, ws_bytes);
+    g_err.clear();
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    int32_t *sel = (int32_t *)base;
+    char *tws = base + pl.sel_bytes;
+    const TopkWs L = topk_layout(a->B, 1, pl.n_max, a->k);
+    const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
+    hipError_t e = launch_decode_prologue(pl.rec, pl.key, a->B, pl.entry, tws + L.hist, hist_bytes, s);
+    if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
+    st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false);
+    if (st != V4A_OK) return st;
+    pl.at.topk = sel;
+    pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;
+    return hip_status(launch_attention(pl.at, pl.sq, s), "v4a_decode_step_csa: attention");
 }
 
 }  // extern "C"

@@ -16,6 +16,8 @@
 // are computed once per wavefront (one candidate per lane) and broadcast through LDS; with
 // a gate per dim (G = D) each lane runs an online softmax for its own dims.  All row
 // reads are 64-lane contiguous; the work is HBM-bound.
+#include <algorithm>
+
 #include "encoders.hpp"
 
 
@@ -57,16 +59,14 @@ __device__ __forceinline__ void load_row(const void *base, bool bf16, int64_t ro
     }
 }
 
+// Entry i of sequence seq, computed by one whole wavefront; row 0 of the sequence's streams
+// is position tok0 (its streams and gates start n_tok rows further per sequence); wsh is the
+// wavefront's scratch for the candidate weights.
 template <int VPT>
-__global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
-    __shared__ float wsh[4][kMaxCand];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t e = (int64_t)blockIdx.x * 4 + wv;
-    if (e >= P.n_entries) return;  // the whole wavefront leaves together
-    // sequence blockIdx.y: its streams and gates start n_tok rows further per sequence
-    const int64_t seq = blockIdx.y;
+__device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
+                                               int64_t tok0) {
+    const int lane = threadIdx.x & 63;
     const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
-    const int64_t i = P.first_entry + e;
     const int m = P.m, D = P.D;
     const int d0 = lane * VPT;
     const bool active = d0 < D;
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
             for (int u = 0; u < kRowBatch; u++) {
                 const int c = min(c0 + u, n_cand - 1);
                 const int s = c / m, j = c % m;
-                const int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - P.tok0;
+                const int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
                 load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, xb[u], x_off);
             }
         };
@@ -96,16 +96,16 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         float zmax = -INFINITY;
         for (int c = lane; c < n_cand; c += 64) {
             int s = c / m, j = c % m;
-            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - P.tok0;
+            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
             float z = (s == 0 ? P.g0 : P.g1)[g_off + r] + (s == 0 ? P.b0 : P.b1)[j];
-            wsh[wv][c] = z;
+            wsh[c] = z;
             zmax = fmaxf(zmax, z);
         }
         zmax = wave_max(zmax);
         float den = 0.0f;
         for (int c = lane; c < n_cand; c += 64) {
-            float ex = expf(wsh[wv][c] - zmax);
-            wsh[wv][c] = ex;
+            float ex = expf(wsh[c] - zmax);
+            wsh[c] = ex;
             den += ex;
         }
         den = wave_sum(den);
@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
 #pragma unroll
             for (int u = 0; u < kRowBatch; u++) {
                 if (c0 + u < n_cand) {
-                    const float wgt = wsh[wv][c0 + u];
+                    const float wgt = wsh[c0 + u];
 #pragma unroll
                     for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
                 }
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         for (int v = 0; v < VPT; v++) { mx[v] = -INFINITY; l[v] = 0.0f; }
         for (int c = 0; c < n_cand; c++) {
             int s = c / m, j = c % m;
-            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - P.tok0;
+            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
             float x[VPT];
             load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
             const float *g = (s == 0 ? P.g0 : P.g1) + g_off + r * D + d0;
@@ -193,8 +193,47 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         store_record<VPT>(acc, d0, active, D, P.R, P.kv, orow);
 }
 
-hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
-    if (a.n_entries == 0) return hipSuccess;
+template <int VPT>
+__global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
+    __shared__ float wsh[4][kMaxCand];
+    const int wv = threadIdx.x >> 6;
+    const int64_t e = (int64_t)blockIdx.x * 4 + wv;
+    if (e >= P.n_entries) return;  // the whole wavefront leaves together
+    compress_entry<VPT>(P, wsh[wv], blockIdx.y, P.first_entry + e, P.tok0);
+}
+
+// Decode-step prologue, one launch: row y < B compresses the entry record of sequence y, row
+// B <= y < 2B its indexer key (each where the sequence's newest token completes a block:
+// entry[seq] >= 0, the sequence's 2m stream rows starting at the block before it), and row 2B
+// clears the selection's histogram region.
+struct PrologueParams {
+    CompressParams rec, key;
+    int B;
+    int64_t entry[kMaxSeq];
+    uint4 *zero;
+    size_t zero_n16;
+};
+
+template <int VR, int VK>
+__global__ void __launch_bounds__(256) decode_prologue_kernel(PrologueParams P) {
+    __shared__ float wsh[kMaxCand];
+    const int y = blockIdx.y;
+    if (y == 2 * P.B) {
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < P.zero_n16; i += (size_t)gridDim.x * blockDim.x)
+            P.zero[i] = make_uint4(0, 0, 0, 0);
+        return;
+    }
+    if (blockIdx.x != 0 || threadIdx.x >= 64) return;  // one wavefront per entry
+    const int seq = y < P.B ? y : y - P.B;
+    const int64_t i = P.entry[seq];
+    if (i < 0) return;
+    if (y < P.B)
+        compress_entry<VR>(P.rec, wsh, seq, i, (int64_t)P.rec.m * (i - 1));
+    else
+        compress_entry<VK>(P.key, wsh, seq, i, (int64_t)P.key.m * (i - 1));
+}
+
+static CompressParams compress_params(const CompressArgs &a) {
     CompressParams P;
     P.x0 = a.x[0];
     P.x1 = a.x[1];
@@ -219,7 +258,12 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     P.cap = a.idx ? a.idx->cap : a.kv->cap;
     P.out_row0 = (int64_t)a.b0 * P.cap;
     P.n_tok = a.n_tok;
-    if (a.n_seq == 0) return hipSuccess;
+    return P;
+}
+
+hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
+    if (a.n_entries == 0 || a.n_seq == 0) return hipSuccess;
+    const CompressParams P = compress_params(a);
     dim3 grid((unsigned)((a.n_entries + 3) / 4), (unsigned)a.n_seq), block(256);
     switch (a.D) {
         case 32: case 64: hipLaunchKernelGGL(compress_kernel<1>, grid, block, 0, s, P); break;
@@ -227,6 +271,30 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
         case 256: hipLaunchKernelGGL(compress_kernel<4>, grid, block, 0, s, P); break;
         default: hipLaunchKernelGGL(compress_kernel<8>, grid, block, 0, s, P); break;
     }
+    return hipGetLastError();
+}
+
+}  // namespace v4a
+
+namespace v4a {
+
+hipError_t launch_decode_prologue(const CompressArgs &rec, const CompressArgs &key, int B, const int64_t *entry,
+                                  void *zero, size_t zero_bytes, hipStream_t s) {
+    PrologueParams P;
+    P.rec = compress_params(rec);
+    P.key = compress_params(key);
+    P.B = B;
+    for (int b = 0; b < kMaxSeq; b++) P.entry[b] = b < B ? entry[b] : -1;
+    P.zero = (uint4 *)zero;
+    P.zero_n16 = zero_bytes / 16;
+    const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 255) / 256, 1024);
+    dim3 grid(zx > 0 ? zx : 1, (unsigned)(2 * B + 1));
+    if (rec.D == 512 && key.D == 128)
+        hipLaunchKernelGGL((decode_prologue_kernel<8, 2>), grid, dim3(256), 0, s, P);
+    else if (rec.D == 128 && key.D == 32)
+        hipLaunchKernelGGL((decode_prologue_kernel<2, 1>), grid, dim3(256), 0, s, P);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

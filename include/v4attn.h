@@ -292,6 +292,56 @@ V4A_API v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *arg
 /* Workspace of v4a_prefill_chunk for these arguments (0 for HCA; 0 if they are invalid). */
 V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *args);
 
+/* ------------------------------------------------- fused CSA decode step (one token) ----
+ * One decode step of B sequences in one call, equal to v4a_compress_csa (records, then keys)
+ * + v4a_indexer_topk (Q = 1) + v4a_decode_csa with the same arguments.  For every sequence b
+ * whose newest token t = q_pos[b] completes a block ((t+1) % m == 0), entry (t+1)/m - 1 is
+ * compressed into the record cache and the key cache; then the top-k of its visible entries
+ * (n_entries[b] cached) are selected and attended over with the window and the sink.  The
+ * compression and the selection's histogram clear share one launch.
+ * [cyqw] section 3.5 (the state cache keeps the incomplete block; a completed block becomes a
+ * compressed entry) and the sections cited at the calls it composes.
+ * Stream rows: every stream holds [B][2m] rows per sequence, the B-block before the completed
+ * block and the completed block itself (positions t+1-2m .. t; for the first block only the
+ * last m rows are read).  Sequences whose newest token completes no block read no rows.
+ * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
+ * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
+typedef struct {
+    int32_t B, m;
+    const int64_t *q_pos;        /* host[B]: position of each sequence's newest token         */
+    const int64_t *n_entries;    /* host[B]: entries cached after this step (<= cap)          */
+    v4a_float in_t;              /* element type of the raw streams                            */
+    int32_t G, idx_G;            /* gate widths (1 or D / 1 or d)                              */
+    const void *kv_a, *kv_b;     /* [B][2m][D] (device)                                        */
+    const float *gate_a, *gate_b, *bias_a, *bias_b;      /* [B][2m][G], [m][G]               */
+    const void *idx_a, *idx_b;   /* [B][2m][d] (device)                                        */
+    const float *idx_gate_a, *idx_gate_b, *idx_bias_a, *idx_bias_b;
+    int32_t apply_rope;
+    float rope_theta;
+    const v4a_kv *kv;            /* record cache, slot b = sequence b                          */
+    const v4a_idx *keys;         /* key cache, slot b = sequence b                             */
+    const v4a_idx *q_idx;        /* [B*H_I] rows (device)                                      */
+    const float *w;              /* [B][H_I] f32 (device)                                      */
+    int32_t H_I, k;
+    const void *q;               /* [B][H][D] (device)                                         */
+    v4a_float q_t;
+    int32_t H;
+    const void *win;             /* [B][W][D] (device)                                         */
+    v4a_float win_t;
+    const int32_t *win_len;      /* host[B]                                                    */
+    int32_t W;
+    const float *sink;           /* [H] f32 (device)                                           */
+    float softmax_scale;
+    int32_t out_rope_inverse;
+    void *out;                   /* [B][H][D] (device)                                         */
+    v4a_float out_t;
+} v4a_decode_step_args;
+
+V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,
+                               void *stream);
+/* Workspace of v4a_decode_step_csa for these arguments (0 if they are invalid). */
+V4A_API size_t v4a_decode_step_workspace(const v4a_decode_step_args *args);
+
 /* ---------------------------------------------------------------------- utilities ---- */
 V4A_API const char *v4a_last_error(void);
 V4A_API const char *v4a_version(void);

@@ -192,3 +192,59 @@ def test_prefill_workspace_and_rejects():
     h = prefill_struct(m=128, kv_b=0, gate_b=0, bias_b=0, keys=None, q_idx=None, w=0, k=0)
     assert L.v4a_prefill_workspace(hca, ctypes.byref(h)) == 0
     assert L.v4a_prefill_chunk(hca, ctypes.byref(prefill_struct(m=128, tok0=65600)), None, 0, None) == 1
+
+
+def test_decode_step_args_layout_matches_the_header(tmp_path):
+    import subprocess
+    fields = [f for f, _ in v4.c_decode_step_args._fields_]
+    src = tmp_path / "layout2.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "v4attn.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(v4a_decode_step_args));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(v4a_decode_step_args, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout2"
+    inc = str(v4.HEADER).rsplit("/", 1)[0]
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(v4.c_decode_step_args)
+    assert got[1:] == [getattr(v4.c_decode_step_args, f).offset for f in fields]
+
+
+def step_struct(**kw):
+    """A valid fused CSA decode step at the 1M-context shape (fake device pointers)."""
+    rec, keys, q_idx = kv(cap=262144), idx(cap=262144), idx(cap=64)
+    pos, nent, wl = i64(*[1048575] * 4), i64(*[262144] * 4), i32(*[128] * 4)
+    a = dict(B=4, m=4, q_pos=ctypes.cast(pos, ctypes.c_void_p), n_entries=ctypes.cast(nent, ctypes.c_void_p), in_t=1,
+             G=1, idx_G=1, kv_a=FAKE, kv_b=FAKE, gate_a=FAKE, gate_b=FAKE, bias_a=FAKE, bias_b=FAKE, idx_a=FAKE,
+             idx_b=FAKE, idx_gate_a=FAKE, idx_gate_b=FAKE, idx_bias_a=FAKE, idx_bias_b=FAKE, apply_rope=1,
+             rope_theta=10000.0, kv=ctypes.pointer(rec), keys=ctypes.pointer(keys), q_idx=ctypes.pointer(q_idx),
+             w=FAKE, H_I=64, k=1024, q=FAKE, q_t=1, H=128, win=FAKE, win_t=1, win_len=ctypes.cast(wl, ctypes.c_void_p),
+             W=128, sink=FAKE, softmax_scale=0.044, out_rope_inverse=1, out=FAKE, out_t=1)
+    a.update(kw)
+    s = v4.c_decode_step_args(**a)
+    s._keep = (rec, keys, q_idx, pos, nent, wl, a)
+    return s
+
+
+def test_decode_step_workspace_and_rejects():
+    L = v4.lib()
+    s = step_struct()
+    need = L.v4a_decode_step_workspace(ctypes.byref(s))
+    # the top-k lists, the indexer workspace and the split partials of 1152 keys (12 splits)
+    assert need >= 4 * 1024 * 4 + v4.v4a_indexer_topk_workspace(4, 1, 262144, 1024) + 4 * 12 * 128 * 512 * 4
+    assert need % 256 == 0
+
+    def call(ws=FAKE, wsb=1 << 40, **kw):
+        return L.v4a_decode_step_csa(ctypes.byref(step_struct(**kw)), ws, wsb, None)
+    assert L.v4a_decode_step_csa(None, FAKE, 1 << 40, None) == 1
+    assert call(B=0) == 2 and call(B=200) == 2
+    assert call(k=0) == 2
+    assert call(H_I=6) == 2
+    assert call(H=24) == 2                                   # not a multiple of 16: no MFMA attention
+    assert call(keys=ctypes.pointer(idx(d=64, cap=262144))) == 2
+    assert call(kv_b=0) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=FAKE + 64) == 3
+    pos = i64(*[1048575] * 4)
+    short = i64(262143, 262144, 262144, 262144)   # sequence 0 would not hold the entry it completes
+    assert call(n_entries=ctypes.cast(short, ctypes.c_void_p), q_pos=ctypes.cast(pos, ctypes.c_void_p)) == 1

@@ -1,0 +1,102 @@
+"""GPU check of the fused CSA decode step (v4a_decode_step_csa): one call must give bitwise
+the same caches, selections and outputs as the separate calls it replaces (v4a_compress_csa
+for the entry record and the indexer key of every sequence whose newest token completes a
+block, v4a_indexer_topk, v4a_decode_csa), for a batch mixing sequences that complete a block,
+one that does not, and one that completes its first block.  The separate calls are checked
+against the oracle by the other GPU tests; sequence 0 is also checked against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_02_amd as v4
+import oracle
+from gpu_util import MAX_ABS_BF16, REL_L2_BF16, announce, bf16_from_bits, bf16_round, check_close, f32, out_f64
+from workloads import bf16_bits_to_f64, normal, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def clone_kv(kv):
+    return v4.KV(kv.fmt, kv.D, kv.R, kv.nope.clone(), kv.rope.clone(), kv.scale.clone(), kv.cap)
+
+
+def clone_idx(ix):
+    return v4.Idx(ix.fmt, ix.d, ix.codes.clone(), ix.scales.clone(), ix.cap)
+
+
+def test_fused_step_equals_separate_calls():
+    seed, m, D, R, H, HI, dI, k, W = 4242, 4, 512, 64, 128, 64, 128, 512, 128
+    q_pos = [4003, 4001, 3, 8191]            # completes entry 1000 / none / entry 0 / entry 2047
+    B, cap = len(q_pos), 2304
+    n_ent = [(p + 1) // m for p in q_pos]
+    entry = [(p + 1) // m - 1 if (p + 1) % m == 0 else -1 for p in q_pos]
+    announce(f"fused decode step: q_pos={q_pos}")
+    kv = v4.KV.empty(B, cap, D, R)
+    v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
+    keys = v4.Idx.empty(B, cap, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "keys", (B * cap, dI))), keys, 0)
+    qi = v4.Idx.empty(1, B * HI, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "q_idx", (B * HI, dI))), qi)
+    bits = {n: to_bf16_bits(normal(seed, n, (B, 2 * m, D if n.startswith("kv") else dI)))
+            for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
+    dev = {n: bf16_from_bits(v) for n, v in bits.items()}
+    gates = {n: f32(normal(seed, n, (B, 2 * m, 1))) for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
+    bias = {n: f32(normal(seed, n, (m, 1))) for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
+    w = f32(normal(seed, "w", (B, HI)))
+    q = bf16_from_bits(to_bf16_bits(normal(seed, "q", (B, H, D))))
+    win = bf16_from_bits(to_bf16_bits(normal(seed, "window", (B, W, D))))
+    win_len = [min(W, p + 1) for p in q_pos]
+    sink = f32(normal(seed, "sink", (H,)))
+    scale = 1.0 / math.sqrt(D)
+
+    # the fused call
+    kv1, keys1 = clone_kv(kv), clone_idx(keys)
+    out1 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    args = v4.DecodeStepArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=dev["kv_a"], kv_b=dev["kv_b"],
+                             gate_a=gates["gate_a"], gate_b=gates["gate_b"], bias_a=bias["bias_a"],
+                             bias_b=bias["bias_b"], idx_a=dev["idx_a"], idx_b=dev["idx_b"],
+                             idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
+                             idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv1, keys=keys1,
+                             q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
+                             softmax_scale=scale, out=out1)
+    ws1 = v4.workspace(v4.v4a_decode_step_workspace(args))
+    v4.v4a_decode_step_csa(args, ws1)
+
+    # the separate calls
+    kv2, keys2 = clone_kv(kv), clone_idx(keys)
+    for b, i in enumerate(entry):
+        if i < 0:
+            continue
+        v4.v4a_compress_csa(dev["kv_a"][b], dev["kv_b"][b], gates["gate_a"][b], gates["gate_b"][b], bias["bias_a"],
+                            bias["bias_b"], tok0=m * (i - 1), m=m, first_entry=i, n_entries=1, out_kv=kv2, b=b)
+        v4.v4a_compress_csa(dev["idx_a"][b], dev["idx_b"][b], gates["idx_gate_a"][b], gates["idx_gate_b"][b],
+                            bias["idx_bias_a"], bias["idx_bias_b"], tok0=m * (i - 1), m=m, first_entry=i,
+                            n_entries=1, out_idx=keys2, b=b)
+    sel = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    ws2 = v4.workspace(max(v4.v4a_indexer_topk_workspace(B, 1, max(n_ent), k),
+                           v4.v4a_decode_workspace(B, H, D, k, W)))
+    v4.v4a_indexer_topk(keys2, n_ent, m, qi, w, B, 1, HI, q_pos, k, sel, ws2)
+    out2 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    v4.v4a_decode_csa(q, kv2, sel.view(B, k), k, win, win_len, W, sink, q_pos, softmax_scale=scale, out=out2, ws=ws2)
+    torch.cuda.synchronize()
+
+    for a, c in ((kv1.nope, kv2.nope), (kv1.rope, kv2.rope), (kv1.scale, kv2.scale),
+                 (keys1.codes, keys2.codes), (keys1.scales, keys2.scales)):
+        assert torch.equal(a, c)
+    assert not torch.equal(kv1.nope, kv.nope)   # the completing sequences did write entries
+    assert torch.equal(out1, out2)
+
+    # sequence 0 against the oracle, fed the caches the GPU wrote
+    b = 0
+    recs = oracle.dequant_kv(kv1.nope[b, :n_ent[b]].cpu().numpy(), kv1.rope[b, :n_ent[b]].cpu().numpy().view(np.uint16),
+                             kv1.scale[b, :n_ent[b]].cpu().numpy())
+    idx = dict(q_codes=qi.codes[0, b * HI:(b + 1) * HI].cpu().numpy(), q_scales=qi.scales[0, b * HI:(b + 1) * HI].cpu().numpy(),
+               w=w[b].cpu().numpy(), k_codes=keys1.codes[b, :n_ent[b]].cpu().numpy(),
+               k_scales=keys1.scales[b, :n_ent[b]].cpu().numpy())
+    ref, ref_sel = oracle.decode_csa(bf16_bits_to_f64(q[b].view(torch.int16).cpu().numpy().view(np.uint16)), recs,
+                                     n_ent[b], k, bf16_bits_to_f64(win[b].view(torch.int16).cpu().numpy().view(np.uint16)),
+                                     sink.cpu().numpy(), scale, q_pos=q_pos[b], m=m, idx=idx, R=R)
+    assert np.array_equal(sel[b, 0].cpu().numpy(), ref_sel)
+    check_close(out_f64(out1[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what="fused step vs oracle")
