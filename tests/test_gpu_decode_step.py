@@ -37,7 +37,7 @@ def test_fused_step_equals_separate_calls():
     v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
     keys = v4.Idx.empty(B, cap, dI)
     v4.v4a_quantize_mxfp4(f32(normal(seed, "keys", (B * cap, dI))), keys, 0)
-    qi = v4.Idx.empty(1, B * HI, dI)
+    qi = v4.Idx.empty(B, HI, dI)  # slot b holds sequence b's H_I query rows
     v4.v4a_quantize_mxfp4(f32(normal(seed, "q_idx", (B * HI, dI))), qi)
     bits = {n: to_bf16_bits(normal(seed, n, (B, 2 * m, D if n.startswith("kv") else dI)))
             for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
@@ -92,7 +92,7 @@ def test_fused_step_equals_separate_calls():
     b = 0
     recs = oracle.dequant_kv(kv1.nope[b, :n_ent[b]].cpu().numpy(), kv1.rope[b, :n_ent[b]].cpu().numpy().view(np.uint16),
                              kv1.scale[b, :n_ent[b]].cpu().numpy())
-    idx = dict(q_codes=qi.codes[0, b * HI:(b + 1) * HI].cpu().numpy(), q_scales=qi.scales[0, b * HI:(b + 1) * HI].cpu().numpy(),
+    idx = dict(q_codes=qi.codes[b].cpu().numpy(), q_scales=qi.scales[b].cpu().numpy(),
                w=w[b].cpu().numpy(), k_codes=keys1.codes[b, :n_ent[b]].cpu().numpy(),
                k_scales=keys1.scales[b, :n_ent[b]].cpu().numpy())
     ref, ref_sel = oracle.decode_csa(bf16_bits_to_f64(q[b].view(torch.int16).cpu().numpy().view(np.uint16)), recs,
