@@ -79,6 +79,7 @@ def _declare(L):
     L.orc_indexer_scores_mxfp4.argtypes = [P, P, P, I32, I32, P, P, I64, P, P]
     L.orc_indexer_scores_f32.argtypes = [P, P, I32, I32, P, I64, P]
     L.orc_topk.argtypes = [P, I64, I32, P]
+    L.orc_topk_bf16.argtypes = [P, I64, I32, P]
     L.orc_attend.argtypes = [P, I32, I32, P, I64, P, I64, P, F64, I32, I32, F64, F64, P, P]
 
 
@@ -238,11 +239,13 @@ def indexer_scores_f32(q, w, keys, n_keys=None) -> np.ndarray:
     return scores
 
 
-def topk(scores, k: int, n_vis=None) -> np.ndarray:
+def topk(scores, k: int, n_vis=None, score_bf16: bool = False) -> np.ndarray:
+    """The k best of scores[:n_vis] (lowest index wins ties), ascending, -1 padded; with
+    score_bf16 the scores are first rounded to BF16."""
     scores, ps = _c(scores, np.float32)
     n = scores.size if n_vis is None else int(n_vis)
     out = np.empty((k,), np.int32)
-    lib().orc_topk(ps, n, int(k), out.ctypes.data_as(P))
+    (lib().orc_topk_bf16 if score_bf16 else lib().orc_topk)(ps, n, int(k), out.ctypes.data_as(P))
     return out
 
 
@@ -274,11 +277,12 @@ def visible_entries(n_entries: int, m: int, pos: int) -> int:
 
 
 def decode_csa(q, records, n_entries, k, window, sink, scale, *, q_pos, m=4, idx=None,
-               rope_inverse=True, R=64, theta=10000.0, scores=None):
+               rope_inverse=True, R=64, theta=10000.0, scores=None, score_bf16=False):
     """One CSA decode step for one sequence.
 
     records: float64 [N][D] dequantised entries; idx: dict(q_codes, q_scales, w, k_codes,
-    k_scales) for MXFP4, or dict(q, w, keys) for fp32; scores may be given precomputed.
+    k_scales) for MXFP4, or dict(q, w, keys) for fp32; scores may be given precomputed;
+    score_bf16 selects on the scores rounded to BF16.
     Returns (out [H][D] float64, topk indices [k]).
     """
     n_vis = visible_entries(n_entries, m, q_pos)
@@ -290,7 +294,7 @@ def decode_csa(q, records, n_entries, k, window, sink, scale, *, q_pos, m=4, idx
                 raise AssertionError(f"{bad} indexer dots are not fp32-exact")
         else:
             scores = indexer_scores_f32(idx["q"], idx["w"], idx["keys"], n_vis)
-    sel = topk(scores, k, n_vis)
+    sel = topk(scores, k, n_vis, score_bf16=score_bf16)
     chosen = sel[sel >= 0]
     out = attend(q, records[chosen], window, sink, scale, rope_inverse=rope_inverse, R=R,
                  theta=theta, t_q=q_pos)
@@ -305,7 +309,7 @@ def decode_hca(q, records, n_entries, window, sink, scale, *, q_pos, m=128, rope
 
 
 def prefill_queries(kind, q, records, n_entries, stream, *, n_prev, tok0, queries, W, sink, scale,
-                    m, k=None, idx=None, rope_inverse=True, R=64, theta=10000.0):
+                    m, k=None, idx=None, rope_inverse=True, R=64, theta=10000.0, score_bf16=False):
     """Attention of chosen queries of a prefill chunk, each exactly as a decode step.
 
     The chunk's own compression is the compressor run on the chunk with its state (the
@@ -333,7 +337,8 @@ def prefill_queries(kind, q, records, n_entries, stream, *, n_prev, tok0, querie
             else:
                 qi = dict(q=idx["q"][j], w=idx["w"][j], keys=idx["keys"])
             outs[j], sels[j] = decode_csa(q[j], records, n_entries, k, window, sink, scale, q_pos=t,
-                                          m=m, idx=qi, rope_inverse=rope_inverse, R=R, theta=theta)
+                                          m=m, idx=qi, rope_inverse=rope_inverse, R=R, theta=theta,
+                                          score_bf16=score_bf16)
         else:
             outs[j] = decode_hca(q[j], records, n_entries, window, sink, scale, q_pos=t, m=m,
                                  rope_inverse=rope_inverse, R=R, theta=theta)

@@ -517,6 +517,19 @@ ORC_API void orc_topk(const float *scores, int64_t n_vis, int k, int32_t *out) {
     free(v);
 }
 
+/* The same selection over the scores held in BF16: each score is first rounded
+ * to the nearest BF16 value (ties to the even one), then the k best are chosen
+ * under the same order, so scores that become equal are taken lowest index
+ * first.  Cited: [cyqw] section 3.4 (the index score is stored as BF16 rather
+ * than FP32, which doubles the speed of the top-k selector at 99.7% KV
+ * recall).  Scores must be finite. */
+ORC_API void orc_topk_bf16(const float *scores, int64_t n_vis, int k, int32_t *out) {
+    float *r = malloc(sizeof(float) * (n_vis > 0 ? n_vis : 1));
+    for (int64_t i = 0; i < n_vis; i++) r[i] = (float)orc_bf16_decode(orc_bf16_encode(scores[i]));
+    orc_topk(r, n_vis, k, out);
+    free(r);
+}
+
 /* ------------------------------------------------------------------------ */
 /* a6 / a7: shared-KV MQA with sliding window and sink                        */
 /* ------------------------------------------------------------------------ */

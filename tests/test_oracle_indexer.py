@@ -125,3 +125,47 @@ def test_topk_adversarial_ties(orc):
     # -0 and +0 are the same score
     s = np.array([0.0, -0.0, 0.0, 1.0], np.float32)
     assert np.array_equal(orc.topk(s, 2), np.array([0, 3], np.int32))
+
+
+def bf16_values_torch(s):
+    """Nearest-even BF16 values of fp32 scores by torch's own conversion (an independent
+    implementation of the rounding)."""
+    import torch
+    return torch.from_numpy(np.asarray(s, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def test_topk_bf16_rounding_decides_ties(orc):
+    # "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 3.4: the selector works on
+    # BF16 scores.  BF16 keeps 8 significant bits, so near 1 its spacing is 2^-7.
+    e = 2.0 ** -8
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7 and rounds to the even 1: it then ties with
+    # index 0, which wins
+    s = np.array([1.0, 1.0 + e, 1.0 + 2 * e], np.float32)
+    assert np.array_equal(orc.topk(s, 2), np.array([1, 2], np.int32))
+    assert np.array_equal(orc.topk(s, 2, score_bf16=True), np.array([0, 2], np.int32))
+    # 1 + 3*2^-8 is the midpoint of 1 + 2^-7 and 1 + 2^-6 and rounds up to the even 1 + 2^-6
+    s = np.array([1.0 + 3 * e, 1.0 + 4 * e], np.float32)
+    assert np.array_equal(orc.topk(s, 1), np.array([1], np.int32))
+    assert np.array_equal(orc.topk(s, 1, score_bf16=True), np.array([0], np.int32))
+    # a negative subnormal score rounds to -0, the same score as +0
+    s = np.array([-2.0 ** -149, 0.0], np.float32)
+    assert np.array_equal(orc.topk(s, 1), np.array([1], np.int32))
+    assert np.array_equal(orc.topk(s, 1, score_bf16=True), np.array([0], np.int32))
+    # only the visible prefix competes, -1 padding as before
+    assert np.array_equal(orc.topk(np.ones(8, np.float32), 4, n_vis=2, score_bf16=True),
+                          np.array([0, 1, -1, -1], np.int32))
+
+
+@pytest.mark.parametrize("n,k", [(4000, 64), (3000, 512), (50, 64)])
+def test_topk_bf16_vs_lexsort_of_torch_rounding(orc, n, k):
+    g = np.random.default_rng(7 * n + k)
+    s = (g.standard_normal(n) * 4.0).astype(np.float32)
+    assert np.array_equal(orc.topk(s, k, score_bf16=True), brute_topk(bf16_values_torch(s), k))
+
+
+def test_topk_bf16_equals_f32_on_bf16_scores(orc):
+    # scores that are already BF16 values select identically in both variants
+    g = np.random.default_rng(11)
+    s = bf16_values_torch(g.standard_normal(5000).astype(np.float32))
+    for k in (1, 100, 1024):
+        assert np.array_equal(orc.topk(s, k, score_bf16=True), orc.topk(s, k))
