@@ -242,6 +242,26 @@ def main():
     torch.cuda.synchronize()
     idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    # the BF16-score selector, timed the same way, and the overlap of its selection with the
+    # fp32 one on every sequence of set 0
+    sel_b = torch.empty_like(sel)
+    for i in range(args.warmup):
+        st = sets[i % len(sets)]
+        v4.v4a_indexer_topk_bf16(st["keys"], [N] * B, m, st["qi"], st["w"], B, 1, HI, q_pos, k, sel_b, ws)
+    torch.cuda.synchronize()
+    for i in range(n_idx):
+        st = sets[(args.warmup + i) % len(sets)]
+        evs[i][0].record()
+        v4.v4a_indexer_topk_bf16(st["keys"], [N] * B, m, st["qi"], st["w"], B, 1, HI, q_pos, k, sel_b, ws)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    idx_bf16_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    stage_indexer(sets[0])
+    v4.v4a_indexer_topk_bf16(sets[0]["keys"], [N] * B, m, sets[0]["qi"], sets[0]["w"], B, 1, HI, q_pos, k, sel_b, ws)
+    torch.cuda.synchronize()
+    sf, sb = sel.cpu().numpy()[:, 0], sel_b.cpu().numpy()[:, 0]
+    bf16_recall = float(np.mean([np.intersect1d(sf[b], sb[b]).size / k for b in range(B)]))
+
     # algorithmic bytes of the indexer + top-k call: keys, indexer queries and weights read,
     # the top-k list written
     idx_bytes = B * N * (dI // 2 + dI // 32) + B * HI * (dI // 2 + dI // 32) + B * HI * 4 + B * k * 4
@@ -280,6 +300,9 @@ def main():
                  "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, "flops": step_flops,
                  "ms_separate_calls": ms_step_sep,
                  "wall_s": wall},
+        "variants": {"bf16_scores": {
+            "entry_point": "v4a_indexer_topk_bf16", "ms_per_call": idx_bf16_ms, "ms_per_call_f32_scores": idx_ms,
+            "hbm_gbs": idx_bytes / (idx_bf16_ms / 1e3) / 1e9, "recall_vs_f32_scores": bf16_recall}},
     }
 
     if not args.no_secondary:
@@ -401,27 +424,32 @@ def prefill_secondary(v4, torch, kind, args):
         v4.v4a_quantize_mxfp4(f32(x["keys"]), keys, 0)
         qi = v4.Idx.empty(1, C * wl.H_I, wl.d_I)
         v4.v4a_quantize_mxfp4(f32(x["q_idx"].reshape(-1, wl.d_I)), qi)
-        a = v4.PrefillArgs(kv_b=bf16(x["kv_b"]), gate_b=f32(x["gate_b"]), bias_b=f32(x["bias_b"]),
-                           idx_a=bf16(x["idx_a"]), idx_b=bf16(x["idx_b"]), idx_gate_a=f32(x["idx_gate_a"]),
-                           idx_gate_b=f32(x["idx_gate_b"]), idx_bias_a=f32(x["idx_bias_a"]),
-                           idx_bias_b=f32(x["idx_bias_b"]), keys=keys, q_idx=qi, w=f32(x["w"]), k=wl.k, **common)
+        csa = dict(kv_b=bf16(x["kv_b"]), gate_b=f32(x["gate_b"]), bias_b=f32(x["bias_b"]),
+                   idx_a=bf16(x["idx_a"]), idx_b=bf16(x["idx_b"]), idx_gate_a=f32(x["idx_gate_a"]),
+                   idx_gate_b=f32(x["idx_gate_b"]), idx_bias_a=f32(x["idx_bias_a"]),
+                   idx_bias_b=f32(x["idx_bias_b"]), keys=keys, q_idx=qi, w=f32(x["w"]), k=wl.k)
+        a = v4.PrefillArgs(**csa, **common)
+        a_bf16 = v4.PrefillArgs(**csa, **common, score_bf16=True)
         layer = v4.V4A_LAYER_CSA
     else:
         a = v4.PrefillArgs(**common)
         layer = v4.V4A_LAYER_HCA
     ws = v4.workspace(v4.v4a_prefill_workspace(layer, a))
     del x
-    for _ in range(2):
-        v4.v4a_prefill_chunk(layer, a, ws)
-    torch.cuda.synchronize()
-    reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        v4.v4a_prefill_chunk(layer, a, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+
+    def time_chunk(a, reps=5):
+        for _ in range(2):
+            v4.v4a_prefill_chunk(layer, a, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            v4.v4a_prefill_chunk(layer, a, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = time_chunk(a)
     # algorithmic flops: every query's indexer dots over its visible entries (MXFP4) and its
     # attention over its keys (BF16, 4*H*D per key: QK and PV)
     vis = [min(n_total, (tok0 + j + 1) // m) for j in range(C)]
@@ -435,6 +463,8 @@ def prefill_secondary(v4, torch, kind, args):
     if kind == "csa":
         res.update(mxfp4_tflops=mx_flops / t / 1e12, mxfp4_mfma_frac=mx_flops / t / (MXFP4_PEAK_TFLOPS * 1e12),
                    mfma_time_frac=(bf16_flops / (BF16_PEAK_TFLOPS * 1e12) + mx_flops / (MXFP4_PEAK_TFLOPS * 1e12)) / t)
+        ms_b = time_chunk(a_bf16)
+        res.update(ms_per_chunk_bf16_scores=ms_b, tokens_per_s_bf16_scores=C / (ms_b / 1e3))
     else:
         res["mfma_time_frac"] = bf16_flops / (BF16_PEAK_TFLOPS * 1e12) / t
     return res

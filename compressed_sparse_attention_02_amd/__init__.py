@@ -53,7 +53,8 @@ class c_prefill_args(ctypes.Structure):
                 ("idx_bias_b", P), ("keys", ctypes.POINTER(c_idx)), ("q_idx", ctypes.POINTER(c_idx)),
                 ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("sink", P), ("softmax_scale", ctypes.c_float),
-                ("out_rope_inverse", ctypes.c_int32), ("out", P), ("out_t", ctypes.c_int)]
+                ("out_rope_inverse", ctypes.c_int32), ("out", P), ("out_t", ctypes.c_int),
+                ("score_bf16", ctypes.c_int32)]
 
 
 V4A_LAYER_CSA, V4A_LAYER_HCA = 0, 1
@@ -70,7 +71,7 @@ class c_decode_step_args(ctypes.Structure):
                 ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
                 ("H", ctypes.c_int32), ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32),
                 ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
-                ("out", P), ("out_t", ctypes.c_int)]
+                ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32)]
 
 _lib = None
 
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "v4a_compress_hca": [P, ctypes.c_int, I32, P, I32, P, I64, I64, I32, I64, I64, I32, F32,
                                  P, KVP, I32, I32, P],
             "v4a_indexer_topk": [IDXP, P, I32, IDXP, P, I32, I32, I32, P, I32, P, P, SZ, P],
+            "v4a_indexer_topk_bf16": [IDXP, P, I32, IDXP, P, I32, I32, I32, P, I32, P, P, SZ, P],
             "v4a_indexer_scores": [IDXP, P, I32, IDXP, P, I32, I32, I32, P, I64, P, P],
             "v4a_decode_csa": [P, ctypes.c_int, I32, I32, KVP, P, I32, P, ctypes.c_int, P, I32, P,
                                P, F32, I32, F32, P, ctypes.c_int, P, SZ, P],
@@ -258,6 +260,14 @@ def v4a_indexer_topk(keys: Idx, n_entries, m: int, q_idx: Idx, w: torch.Tensor, 
         _stream(stream)))
 
 
+def v4a_indexer_topk_bf16(keys: Idx, n_entries, m: int, q_idx: Idx, w: torch.Tensor, B: int, Q: int,
+                          H_I: int, q_pos, k: int, out: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().v4a_indexer_topk_bf16(
+        ctypes.byref(keys.c()), _host_i64(n_entries), m, ctypes.byref(q_idx.c()), _ptr(w), B, Q,
+        H_I, _host_i64(q_pos), k, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
 def v4a_indexer_scores(keys: Idx, n_entries, m: int, q_idx: Idx, w: torch.Tensor, B: int, Q: int,
                        H_I: int, q_pos, n_max: int, out: torch.Tensor, stream=None):
     _check(lib().v4a_indexer_scores(
@@ -302,7 +312,8 @@ class PrefillArgs:
                  softmax_scale: float, out, kv_b=None, gate_b=None, bias_b=None, slot: int = 0,
                  apply_rope: bool = True, rope_theta: float = 10000.0, idx_a=None, idx_b=None,
                  idx_gate_a=None, idx_gate_b=None, idx_bias_a=None, idx_bias_b=None, keys: Idx | None = None,
-                 q_idx: Idx | None = None, w=None, k: int = 0, out_rope_inverse: bool = True):
+                 q_idx: Idx | None = None, w=None, k: int = 0, out_rope_inverse: bool = True,
+                 score_bf16: bool = False):
         self._kv = kv.c()
         self._keys = keys.c() if keys is not None else None
         self._q_idx = q_idx.c() if q_idx is not None else None
@@ -322,7 +333,7 @@ class PrefillArgs:
             q_idx=ctypes.pointer(self._q_idx) if self._q_idx is not None else None,
             w=_ptr(w), H_I=H_I, k=k, q=_ptr(q), q_t=_ftype(q), H=H, W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out),
-            out_t=_ftype(out))
+            out_t=_ftype(out), score_bf16=int(score_bf16))
 
 
 def v4a_prefill_workspace(kind: int, args: PrefillArgs) -> int:
@@ -341,7 +352,7 @@ class DecodeStepArgs:
     def __init__(self, *, q_pos, n_entries, m: int, kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b,
                  idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
                  win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
-                 rope_theta: float = 10000.0, out_rope_inverse: bool = True):
+                 rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False):
         B, H = q.shape[0], q.shape[1]
         self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
@@ -356,7 +367,8 @@ class DecodeStepArgs:
             rope_theta=rope_theta, kv=ctypes.pointer(self._kv), keys=ctypes.pointer(self._keys),
             q_idx=ctypes.pointer(self._q_idx), w=_ptr(w), H_I=w.numel() // B, k=k, q=_ptr(q), q_t=_ftype(q), H=H,
             win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
-            softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out))
+            softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out),
+            score_bf16=int(score_bf16))
 
 
 def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:

@@ -329,7 +329,7 @@ namespace v4a {
 // Launches of the indexer + top-k call once every argument has been checked.
 static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, int64_t n_max, const v4a_idx *q_idx,
                                       const float *w, int32_t B, int32_t Q, int32_t H_I, int32_t k, int32_t *out_idx,
-                                      void *ws, hipStream_t s, bool clear_hist = true) {
+                                      void *ws, hipStream_t s, bool clear_hist = true, bool key16 = false) {
     const TopkWs L = topk_layout(B, Q, n_max, k);
     char *base = (char *)ws;
     const size_t BQ = (size_t)B * Q;
@@ -347,13 +347,15 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
     ia.H_I = H_I;
     ia.n_max = n_max;
     ia.key_stride = score_key_stride(n_max);
-    ia.score_keys = (uint32_t *)(base + L.keys);
+    ia.score_keys = base + L.keys;
+    ia.key16 = key16;
     ia.hist = (uint32_t *)(base + L.hist);
     ia.hist_copies = hist_copies((int64_t)BQ);
     if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
     SelectArgs sa{};
     sa.score_keys = ia.score_keys;
     sa.key_stride = ia.key_stride;
+    sa.key16 = key16;
     sa.hist = ia.hist;
     sa.hist_copies = ia.hist_copies;
     sa.n_max = n_max;
@@ -370,9 +372,14 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
 
 extern "C" {
 
-v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
-                            const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos, int32_t k,
-                            int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace v4a {
+
+static v4a_status indexer_topk_entry(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
+                                     const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos,
+                                     int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes, void *stream,
+                                     bool key16) {
     v4a_status st = check_indexer_args(keys, n_entries, m, q_idx, w, B, Q, H_I, q_pos);
     if (st != V4A_OK) return st;
     if (k < 1 || k > 2048) return fail(V4A_EUNSUPPORTED, "k=%d not in [1, 2048]", k);
@@ -385,7 +392,23 @@ v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32
     if (!ws || ws_bytes < L.total || !aligned(ws, 256))
         return fail(V4A_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, ws_bytes);
     g_err.clear();
-    return indexer_topk_launch(keys, qp, n_max, q_idx, w, B, Q, H_I, k, out_idx, ws, (hipStream_t)stream);
+    return indexer_topk_launch(keys, qp, n_max, q_idx, w, B, Q, H_I, k, out_idx, ws, (hipStream_t)stream, true, key16);
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
+                            const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos, int32_t k,
+                            int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    return indexer_topk_entry(keys, n_entries, m, q_idx, w, B, Q, H_I, q_pos, k, out_idx, ws, ws_bytes, stream, false);
+}
+
+v4a_status v4a_indexer_topk_bf16(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
+                                 const float *w, int32_t B, int32_t Q, int32_t H_I, const int64_t *q_pos, int32_t k,
+                                 int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    return indexer_topk_entry(keys, n_entries, m, q_idx, w, B, Q, H_I, q_pos, k, out_idx, ws, ws_bytes, stream, true);
 }
 
 v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int32_t m, const v4a_idx *q_idx,
@@ -758,7 +781,7 @@ v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *a, void *ws
         if ((e = launch_compress(pl.cidx, s)) != hipSuccess) return hip_status(e, "v4a_prefill_chunk: compress keys");
         sel = (int32_t *)ws;
         st = indexer_topk_launch(&pl.keys, pl.qp, pl.n_total, a->q_idx, a->w, 1, a->C, a->H_I, a->k, sel,
-                                 (char *)ws + pl.idx_bytes, s);
+                                 (char *)ws + pl.idx_bytes, s, true, a->score_bf16 != 0);
         if (st != V4A_OK) return st;
     }
     AttnArgs at{};
@@ -911,7 +934,8 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
     hipError_t e = launch_decode_prologue(pl.rec, pl.key, a->B, pl.entry, tws + L.hist, hist_bytes, s);
     if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
-    st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false);
+    st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false,
+                             a->score_bf16 != 0);
     if (st != V4A_OK) return st;
     pl.at.topk = sel;
     pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;

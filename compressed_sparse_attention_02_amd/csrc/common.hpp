@@ -84,6 +84,17 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Orderable 16-bit key of an fp32 score held in BF16: the score is rounded to the nearest
+// BF16 value with ties to the even one (integer rounding of the top 16 bits; scores are
+// finite), a -0 result becomes +0, and the 16 bits are mapped as score_key maps 32.
+// Shifted left by 16 it orders exactly as score_key of that BF16 value.
+__device__ __forceinline__ uint32_t score_key16(float s) {
+    uint32_t u = fbits(s);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    if (u == 0x8000u) u = 0;
+    return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
+}
+
 // RoPE frequencies of the R/2 interleaved pairs: inv_freq_j = theta^(-2j/R), computed on the
 // host in double (a kernel argument, so no kernel evaluates pow).
 constexpr int kMaxRopePairs = 32;
@@ -228,8 +239,10 @@ struct IndexerArgs {
     const float *w;
     int B, Q, H_I;
     int64_t n_max;            // max visible keys over the queries (grid size)
-    int64_t key_stride;       // score-key row stride (a multiple of 4 >= n_max)
-    uint32_t *score_keys;     // [B*Q][key_stride] orderable keys (or NULL)
+    int64_t key_stride;       // score-key row stride (a multiple of 64 >= n_max)
+    void *score_keys;         // [B*Q][key_stride] orderable keys (or NULL): uint32 of the fp32
+                              // scores, or uint16 of the BF16 scores when key16
+    bool key16;
     float *scores;            // [B*Q][n_max] raw scores (or NULL)
     uint32_t *hist;           // [B*Q][copies][4096] histogram of the top 12 key bits (or NULL)
     int hist_copies;
@@ -238,8 +251,9 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 struct SelectArgs {
-    const uint32_t *score_keys;   // [BQ][key_stride]
+    const void *score_keys;       // [BQ][key_stride] uint32, or uint16 when key16
     int64_t key_stride;
+    bool key16;
     const uint32_t *hist;         // [BQ][copies][4096]
     int hist_copies;
     int64_t n_max;

@@ -19,9 +19,10 @@
 // so each lane runs its chain in registers (16 fmas) and three cross-lane reads finish
 // the fixed-order sum.
 //
-// Each score is written as an orderable 32-bit key (larger score -> larger key) and counted
-// in a 4096-bin histogram of its top 12 bits (LDS per workgroup, then one global atomic add
-// per non-empty bin), which the top-k select uses to find the threshold bin.
+// Each score is written as an orderable key (larger score -> larger key): 32 bits of the fp32
+// score, or 16 bits of the score rounded to BF16 for the BF16 selector.  Its top 12 bits are
+// counted in a 4096-bin histogram (LDS per workgroup, then one global atomic add per
+// non-empty bin), which the top-k select uses to find the threshold bin.
 #include "common.hpp"
 
 namespace v4a {
@@ -41,7 +42,8 @@ struct IndexerParams {
     int H, d;
     int64_t n_max;
     int64_t key_stride;
-    uint32_t *score_keys;  // [BQ][key_stride] or NULL
+    void *score_keys;      // [BQ][key_stride] uint32, or uint16 when key16; or NULL
+    bool key16;
     float *scores;         // [BQ][n_max] or NULL
     uint32_t *hist;        // [BQ][hist_copies][4096] or NULL
     int hist_copies;
@@ -52,9 +54,15 @@ __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64
                                            uint32_t *lhist) {
     if (score == 0.0f) score = 0.0f;  // -0 -> +0
     if (P.scores) P.scores[(int64_t)qi * P.n_max + i] = score;
-    uint32_t key = score_key(score);
-    if (P.score_keys) P.score_keys[(int64_t)qi * P.key_stride + i] = key;
-    if (lhist) atomicAdd(&lhist[key >> 20], 1u);
+    if (P.key16) {
+        const uint32_t key = score_key16(score);
+        if (P.score_keys) ((uint16_t *)P.score_keys)[(int64_t)qi * P.key_stride + i] = (uint16_t)key;
+        if (lhist) atomicAdd(&lhist[key >> 4], 1u);
+    } else {
+        const uint32_t key = score_key(score);
+        if (P.score_keys) ((uint32_t *)P.score_keys)[(int64_t)qi * P.key_stride + i] = key;
+        if (lhist) atomicAdd(&lhist[key >> 20], 1u);
+    }
 }
 
 // Adds the workgroup's LDS histogram into copy (blockIdx.x % hist_copies) of the query's
@@ -201,22 +209,34 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     __syncthreads();
     const int n_here = (int)(kend - k0);
     float *g_sc = P.scores ? P.scores + (int64_t)qi * P.n_max + k0 : nullptr;
-    uint32_t *g_key = P.score_keys ? P.score_keys + (int64_t)qi * P.key_stride + k0 : nullptr;
+    uint32_t *g_key = P.score_keys && !P.key16 ? (uint32_t *)P.score_keys + (int64_t)qi * P.key_stride + k0 : nullptr;
+    uint16_t *g_key16 = P.score_keys && P.key16 ? (uint16_t *)P.score_keys + (int64_t)qi * P.key_stride + k0 : nullptr;
+    const int hshift = P.key16 ? 4 : 20;  // the top 12 bits of either key
     const bool sc_aligned = ((k0 + (int64_t)qi * P.n_max) & 3) == 0;
     for (int i0 = 4 * threadIdx.x; i0 < n_here; i0 += 4 * 256) {
         const float4 v = *(const float4 *)(sbuf + i0);
         const float vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t kk[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) kk[j] = score_key(vv[j]);
+        for (int j = 0; j < 4; j++) kk[j] = P.key16 ? score_key16(vv[j]) : score_key(vv[j]);
         const bool whole = i0 + 4 <= n_here;
-        if (g_key) {  // rows are padded to a multiple of 4 keys and k0 is a multiple of 4
+        // rows are padded to a multiple of 64 keys and k0 is a multiple of 4
+        if (g_key) {
             if (whole) {
                 *(uint4 *)(g_key + i0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; j++)
                     if (i0 + j < n_here) g_key[i0 + j] = kk[j];
+            }
+        }
+        if (g_key16) {
+            if (whole) {
+                *(uint2 *)(g_key16 + i0) = make_uint2(kk[0] | (kk[1] << 16), kk[2] | (kk[3] << 16));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (i0 + j < n_here) g_key16[i0 + j] = (uint16_t)kk[j];
             }
         }
         if (g_sc) {
@@ -231,7 +251,7 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         if (hist) {
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                if (i0 + j < n_here) atomicAdd(&lhist[kk[j] >> 20], 1u);
+                if (i0 + j < n_here) atomicAdd(&lhist[kk[j] >> hshift], 1u);
         }
     }
     flush_hist(P, qi, lhist);
@@ -307,6 +327,7 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     P.n_max = a.n_max;
     P.key_stride = a.key_stride;
     P.score_keys = a.score_keys;
+    P.key16 = a.key16;
     P.scores = a.scores;
     P.hist = a.hist;
     P.hist_copies = a.hist_copies > 0 ? a.hist_copies : 1;

@@ -7,6 +7,10 @@
 // is written in ascending index order, padded with -1.  Equivalently each key i carries the
 // distinct 64-bit rank (orderable score key << 32) | ~i and the k largest ranks win.
 //
+// The BF16 selector ("DeepSeek-V4 technical report walkthrough", section 3.4: the index score
+// kept in BF16) reads 16-bit keys of the scores rounded to BF16; the scan widens each to 32
+// bits (key << 16), which orders identically, so everything after the scan is shared.
+//
 // Radix select in two kernels (the kernel boundary orders the stages; no workgroup waits on
 // another and no device-wide fence is needed):
 //   scan:     the indexer counted the top 12 bits of every score key (in kHistCopies copies).
@@ -14,9 +18,10 @@
 //             from the top of that histogram, then lists, in index order, every key of its
 //             slice whose bin is >= T, with its score key.
 //   finalize: one workgroup per query reads the listed keys in global index order (slice by
-//             slice), resolves the keys inside bin T exactly with LDS radix passes over the
-//             remaining 20 score bits and the inverted index, and compacts the winners in
-//             order, so the output is ascending without a sort.
+//             slice), finds the exact k-th best score key inside bin T with LDS radix passes
+//             over the remaining 20 bits, and compacts the winners in index order (keys equal
+//             to the threshold go lowest index first), so the output is ascending without a
+//             sort.
 #include "common.hpp"
 
 namespace v4a {
@@ -33,12 +38,13 @@ int select_slices(int64_t n_max) {
 }
 
 struct SelParams {
-    const uint32_t *keys;    // [BQ][key_stride]
+    const void *keys;        // [BQ][key_stride] uint32, or uint16 (BF16 scores)
     int64_t key_stride;
     const uint32_t *hist;    // [BQ][copies][4096]
     int copies;
     int64_t n_max;
     int k, slices;
+    bool key16;              // 16-bit keys (listed as key << 16): one 4-bit digit pass
     uint32_t *list;
     uint32_t *counts;
     int32_t *meta;
@@ -100,7 +106,9 @@ __device__ __forceinline__ void find_threshold(const uint32_t (&c)[BPT], uint32_
 // Scan: one workgroup per (slice of kSelSlice keys, query).  The histogram (all copies) is
 // read with 16-byte loads in one round, the threshold bin T found with one block scan, and the
 // slice's keys whose bin is >= T listed in index order (each thread owns a contiguous run of
-// keys; one block scan places the runs).
+// keys; one block scan places the runs).  K16: the keys are 16 bits wide and listed as
+// key << 16.
+template <bool K16>
 __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, QueryPos QP) {
     constexpr int kBPT = kHistBins / kSelThreads;       // 8 bins per thread
     constexpr int kPer = kSelSlice / kSelThreads;       // 16 keys per thread
@@ -122,12 +130,14 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
     const int64_t lo = (int64_t)s * kSelSlice;
     const int64_t hi = lo + kSelSlice < n_vis ? lo + kSelSlice : n_vis;
     const int64_t my0 = lo + (int64_t)t * kPer;
-    const uint32_t *keys = P.keys + (int64_t)qi * P.key_stride;
-    uint4 kq[kPer / 4];
+    constexpr int kPerLoad = K16 ? 8 : 4;  // keys per 16-byte load
+    uint4 kq[kPer / kPerLoad];
 #pragma unroll
-    for (int r = 0; r < kPer / 4; r++) {  // rows are padded to a multiple of 64 keys
-        const int64_t i = my0 + 4 * r;
-        kq[r] = i < hi ? *(const uint4 *)(keys + i) : make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < kPer / kPerLoad; r++) {  // rows are padded to a multiple of 64 keys
+        const int64_t i = my0 + kPerLoad * r;
+        const void *src = K16 ? (const void *)((const uint16_t *)P.keys + (int64_t)qi * P.key_stride + i)
+                              : (const void *)((const uint32_t *)P.keys + (int64_t)qi * P.key_stride + i);
+        kq[r] = i < hi ? *(const uint4 *)src : make_uint4(0, 0, 0, 0);
     }
     uint32_t c[kBPT];
     {
@@ -158,8 +168,17 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
     }
     uint32_t kv[kPer];
 #pragma unroll
-    for (int r = 0; r < kPer / 4; r++) {
-        kv[4 * r] = kq[r].x; kv[4 * r + 1] = kq[r].y; kv[4 * r + 2] = kq[r].z; kv[4 * r + 3] = kq[r].w;
+    for (int r = 0; r < kPer / kPerLoad; r++) {
+        const uint32_t w4[4] = {kq[r].x, kq[r].y, kq[r].z, kq[r].w};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            if (K16) {
+                kv[8 * r + 2 * c] = w4[c] << 16;
+                kv[8 * r + 2 * c + 1] = w4[c] & 0xFFFF0000u;
+            } else {
+                kv[4 * r + c] = w4[c];
+            }
+        }
     }
     uint32_t mine = 0;
 #pragma unroll
@@ -252,16 +271,19 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     }
     __syncthreads();
 
-    // two digit passes over the low 20 bits of the keys in bin T
+    // digit passes over the low 20 bits of the keys in bin T: bits 10..19, then 0..9; keys
+    // widened from 16 bits hold only bits 16..19 below the bin, one pass
     uint32_t rem = need, sub = 0, sub_mask = 0;
-    for (int p = 0; p < 2; p++) {
-        const int shift = p == 0 ? 10 : 0;
+    const int n_pass = P.key16 ? 1 : 2;
+    for (int p = 0; p < n_pass; p++) {
+        const int shift = P.key16 ? 16 : (p == 0 ? 10 : 0);
+        const uint32_t dmask = P.key16 ? 15u : (uint32_t)(kSubBins - 1);
         for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
         __syncthreads();
         for (uint32_t j = t; j < L; j += kSelThreads) {
             uint32_t idx, key;
             entry(j, &idx, &key);
-            if ((int)(key >> 20) == T && (key & sub_mask) == sub) atomicAdd(&hist[(key >> shift) & (kSubBins - 1)], 1u);
+            if ((int)(key >> 20) == T && (key & sub_mask) == sub) atomicAdd(&hist[(key >> shift) & dmask], 1u);
         }
         __syncthreads();
         uint32_t c[kSubBins / kSelThreads];
@@ -272,7 +294,7 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         find_threshold<kSubBins / kSelThreads>(c, rem, wsum, &sT, &sAbove, &d, &ab);
         rem -= ab;
         sub |= (uint32_t)d << shift;
-        sub_mask |= (uint32_t)(kSubBins - 1) << shift;
+        sub_mask |= dmask << shift;
     }
     const uint32_t tkey = ((uint32_t)T << 20) | sub;  // the k_eff-th best score key
     // ordered compaction: thread t owns a contiguous run of the global order; keys > tkey are
@@ -323,12 +345,18 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
     P.copies = a.hist_copies > 0 ? a.hist_copies : 1;
     P.n_max = a.n_max;
     P.k = a.k;
+    P.key16 = a.key16;
     P.slices = select_slices(a.n_max);
     P.list = a.list;
     P.counts = a.counts;
     P.meta = a.meta;
     P.out = a.out;
-    hipLaunchKernelGGL(select_scan_kernel, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s, P, qp);
+    if (a.key16)
+        hipLaunchKernelGGL(select_scan_kernel<true>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
+                           P, qp);
+    else
+        hipLaunchKernelGGL(select_scan_kernel<false>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
+                           P, qp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_final_kernel, dim3((unsigned)a.BQ), dim3(kSelThreads), 0, s, P, qp);

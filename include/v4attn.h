@@ -180,6 +180,18 @@ V4A_API v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entrie
                             void *ws, size_t ws_bytes, void *stream);
 V4A_API size_t v4a_indexer_topk_workspace(int32_t B, int32_t Q, int64_t n_max, int32_t k);
 
+/* The same call with the scores held in BF16 for the selection ([cyqw] section 3.4: the
+ * index score is kept in BF16 instead of FP32, which halves the selector's score bytes).
+ * Each fp32 score defined above is rounded to the nearest BF16 value (ties to the even
+ * one; a -0 result counts as +0), and the k_eff best keys are chosen under (BF16 score
+ * descending, index ascending), so scores that round to the same value are taken lowest
+ * index first.  Arguments, layouts, limits, errors and the workspace size
+ * (v4a_indexer_topk_workspace) are those of v4a_indexer_topk. */
+V4A_API v4a_status v4a_indexer_topk_bf16(const v4a_idx *keys, const int64_t *n_entries, int32_t m,
+                                 const v4a_idx *q_idx, const float *w, int32_t B, int32_t Q,
+                                 int32_t H_I, const int64_t *q_pos, int32_t k, int32_t *out_idx,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* The scores alone (same definition as above), for inspection: out_scores [B][Q][n_max]
  * f32 (device), -inf at positions that are not visible. */
 V4A_API v4a_status v4a_indexer_scores(const v4a_idx *keys, const int64_t *n_entries, int32_t m,
@@ -234,7 +246,8 @@ V4A_API size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_k
  *      (tok0+C)/m - 1) into the entry cache `kv` and, for CSA, the indexer key cache
  *      `keys` (the compressors above; CSA entry tok0/m also reads the B-block before tok0);
  *   2. CSA: selects, for every query t, the top-k of its visible entries (i < (t+1)/m)
- *      exactly as v4a_indexer_topk does with Q = C and q_pos = tok0 + j;
+ *      exactly as v4a_indexer_topk (score_bf16: v4a_indexer_topk_bf16) does with Q = C and
+ *      q_pos = tok0 + j;
  *   3. attends, for query t = tok0 + j and every head, over its selected entries (CSA) or
  *      all its visible entries (HCA) plus the window tokens max(0, t-W+1) .. t (rows of
  *      stream kv_a), with the sink, exactly as the decode calls define it, and writes
@@ -285,6 +298,7 @@ typedef struct {
     int32_t out_rope_inverse;
     void *out;               /* [C][H][D] (device, out_t)                                 */
     v4a_float out_t;
+    int32_t score_bf16;      /* CSA: nonzero selects as v4a_indexer_topk_bf16 does         */
 } v4a_prefill_args;
 
 V4A_API v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *args, void *ws,
@@ -335,6 +349,7 @@ typedef struct {
     int32_t out_rope_inverse;
     void *out;                   /* [B][H][D] (device)                                         */
     v4a_float out_t;
+    int32_t score_bf16;          /* nonzero: select as v4a_indexer_topk_bf16 does               */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,

@@ -26,13 +26,14 @@ def clone_idx(ix):
     return v4.Idx(ix.fmt, ix.d, ix.codes.clone(), ix.scales.clone(), ix.cap)
 
 
-def test_fused_step_equals_separate_calls():
+@pytest.mark.parametrize("score_bf16", [False, True], ids=["f32_scores", "bf16_scores"])
+def test_fused_step_equals_separate_calls(score_bf16):
     seed, m, D, R, H, HI, dI, k, W = 4242, 4, 512, 64, 128, 64, 128, 512, 128
     q_pos = [4003, 4001, 3, 8191]            # completes entry 1000 / none / entry 0 / entry 2047
     B, cap = len(q_pos), 2304
     n_ent = [(p + 1) // m for p in q_pos]
     entry = [(p + 1) // m - 1 if (p + 1) % m == 0 else -1 for p in q_pos]
-    announce(f"fused decode step: q_pos={q_pos}")
+    announce(f"fused decode step: q_pos={q_pos} score_bf16={score_bf16}")
     kv = v4.KV.empty(B, cap, D, R)
     v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
     keys = v4.Idx.empty(B, cap, dI)
@@ -60,7 +61,7 @@ def test_fused_step_equals_separate_calls():
                              idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
                              idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv1, keys=keys1,
                              q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
-                             softmax_scale=scale, out=out1)
+                             softmax_scale=scale, out=out1, score_bf16=score_bf16)
     ws1 = v4.workspace(v4.v4a_decode_step_workspace(args))
     v4.v4a_decode_step_csa(args, ws1)
 
@@ -77,7 +78,8 @@ def test_fused_step_equals_separate_calls():
     sel = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
     ws2 = v4.workspace(max(v4.v4a_indexer_topk_workspace(B, 1, max(n_ent), k),
                            v4.v4a_decode_workspace(B, H, D, k, W)))
-    v4.v4a_indexer_topk(keys2, n_ent, m, qi, w, B, 1, HI, q_pos, k, sel, ws2)
+    (v4.v4a_indexer_topk_bf16 if score_bf16 else v4.v4a_indexer_topk)(keys2, n_ent, m, qi, w, B, 1, HI, q_pos, k,
+                                                                        sel, ws2)
     out2 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
     v4.v4a_decode_csa(q, kv2, sel.view(B, k), k, win, win_len, W, sink, q_pos, softmax_scale=scale, out=out2, ws=ws2)
     torch.cuda.synchronize()
@@ -97,6 +99,7 @@ def test_fused_step_equals_separate_calls():
                k_scales=keys1.scales[b, :n_ent[b]].cpu().numpy())
     ref, ref_sel = oracle.decode_csa(bf16_bits_to_f64(q[b].view(torch.int16).cpu().numpy().view(np.uint16)), recs,
                                      n_ent[b], k, bf16_bits_to_f64(win[b].view(torch.int16).cpu().numpy().view(np.uint16)),
-                                     sink.cpu().numpy(), scale, q_pos=q_pos[b], m=m, idx=idx, R=R)
+                                     sink.cpu().numpy(), scale, q_pos=q_pos[b], m=m, idx=idx, R=R,
+                                     score_bf16=score_bf16)
     assert np.array_equal(sel[b, 0].cpu().numpy(), ref_sel)
     check_close(out_f64(out1[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what="fused step vs oracle")

@@ -5,7 +5,8 @@ quantiser is itself bit-exact against the oracle's); the top-k index lists must 
 Cases: the fp32 tiny workload, ragged key counts and causal visibility, padded head counts,
 adversarial ties, k above the visible count, nothing visible, and the full CSA decode sizes
 of the 131072-token (B=8, top-512) and 1M-token (B=4, top-1024) workloads in the launch
-configuration the benchmark times."""
+configuration the benchmark times.  The BF16-score selector (v4a_indexer_topk_bf16) is held to
+the same bar against the oracle's selection over the scores rounded to BF16."""
 import numpy as np
 import pytest
 import torch
@@ -18,8 +19,9 @@ from workloads import CSA_FLASH, CSA_PRO_1M, TINY, decode_inputs, normal, scaled
 pytestmark = pytest.mark.gpu
 
 
-def run_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1):
-    """HIP indexer + top-k; keys_f [B][N][d], q_f [B][Q*H][d], w [B][Q][H]."""
+def run_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1, bf16=False):
+    """HIP indexer + top-k (bf16: the BF16-score selector); keys_f [B][N][d], q_f [B][Q*H][d],
+    w [B][Q][H]."""
     B, N, d = keys_f.shape
     H = w.shape[-1]
     keys = idx_from_f32(keys_f, fmt)
@@ -28,12 +30,13 @@ def run_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1
     out = torch.full((B, Q, k), -7, dtype=torch.int32, device="cuda")
     n_max = max(min(int(n), (int(p) + 1) // m) for n, p in zip(np.repeat(n_entries, Q), q_pos))
     ws = v4.workspace(v4.v4a_indexer_topk_workspace(B, Q, max(n_max, 0), k))
-    v4.v4a_indexer_topk(keys, n_entries, m, qi, wt, B, Q, H, q_pos, k, out, ws)
+    call = v4.v4a_indexer_topk_bf16 if bf16 else v4.v4a_indexer_topk
+    call(keys, n_entries, m, qi, wt, B, Q, H, q_pos, k, out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy(), keys, qi
 
 
-def oracle_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1):
+def oracle_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, Q=1, bf16=False):
     B, N, d = keys_f.shape
     H = w.shape[-1]
     res = np.empty((B, Q, k), np.int32)
@@ -49,7 +52,7 @@ def oracle_topk(keys_f, q_f, w, n_entries, q_pos, k, m=4, fmt=v4.V4A_IDX_MXFP4, 
                 assert bad == 0
             else:
                 s = oracle.indexer_scores_f32(qrows, w[b, j], keys_f[b], n_vis)
-            res[b, j] = oracle.topk(s, k, n_vis)
+            res[b, j] = oracle.topk(s, k, n_vis, score_bf16=bf16)
     return res
 
 
@@ -165,3 +168,78 @@ def test_topk_full_size(wl):
     # deterministic: a second run gives the same bits
     got2, _, _ = run_topk(inp["keys"], inp["q_idx"], inp["w"][:, None, :], np.array([N] * wl.B), q_pos, wl.k)
     assert np.array_equal(got, got2)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_topk_bf16_bit_exact(name):
+    B, Ns, H, k, q_pos, fmt, d = CASES[name]
+    N = max(Ns)
+    seed = 200 + list(CASES).index(name)
+    keys = normal(seed, "keys", (B, N, d))
+    q = normal(seed, "q_idx", (B, H, d))
+    w = normal(seed, "w", (B, 1, H))
+    if q_pos is None:
+        q_pos = [4 * n - 1 for n in Ns]
+    announce(f"topk bf16 {name}")
+    got, _, _ = run_topk(keys, q, w, np.array(Ns), q_pos, k, fmt=fmt, bf16=True)
+    ref = oracle_topk(keys, q, w, np.array(Ns), q_pos, k, fmt=fmt, bf16=True)
+    for b in range(B):
+        assert np.array_equal(got[b, 0], ref[b, 0]), (name, b, np.setdiff1d(got[b, 0], ref[b, 0])[:10])
+
+
+def test_topk_bf16_rounding_ties():
+    """Scores packed into a narrow range, so that BF16 rounding merges many of them: the ties
+    it creates at the threshold must go to the lowest indices, and the selection must differ
+    from the fp32 one (which separates them)."""
+    B, N, H, k = 2, 9000, 64, 600
+    keys = normal(302, "keys", (B, N, 128))
+    keys[:, :, 64:] = 0.0
+    keys += 8.0  # every per-head dot large and positive, the spread small relative to it
+    q = np.abs(normal(302, "q_idx", (B, H, 128)))
+    w = np.abs(normal(302, "w", (B, 1, H)))
+    announce("topk bf16 rounding ties")
+    got, _, _ = run_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=True)
+    ref = oracle_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=True)
+    assert np.array_equal(got, ref)
+    f32_ref = oracle_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k)
+    assert not np.array_equal(ref, f32_ref)
+
+
+def test_topk_bf16_adversarial_ties_and_prefill_queries():
+    B, N, H, k = 2, 12000, 64, 700
+    g = np.random.default_rng(300)
+    base = normal(300, "keys", (5, 128))
+    keys = base[g.integers(0, 5, size=(B, N))]
+    keys[1] = base[0]
+    q = normal(300, "q_idx", (B, H, 128))
+    w = normal(300, "w", (B, 1, H))
+    announce("topk bf16 adversarial ties")
+    got, _, _ = run_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=True)
+    ref = oracle_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=True)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[1, 0], np.arange(k))
+    B, N, H, k, Q = 1, 6000, 64, 512, 24
+    keys = normal(301, "keys", (B, N, 128))
+    q = normal(301, "q_idx", (B, Q * H, 128))
+    w = normal(301, "w", (B, Q, H))
+    q_pos = [4 * 5000 + j for j in range(Q)]
+    announce("topk bf16 prefill-form queries")
+    got, _, _ = run_topk(keys, q, w, np.array([N]), q_pos, k, Q=Q, bf16=True)
+    ref = oracle_topk(keys, q, w, np.array([N]), q_pos, k, Q=Q, bf16=True)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_bf16_full_size():
+    """1M-token CSA decode sizes, bit for bit; prints the recall against the fp32 selection."""
+    wl = CSA_PRO_1M
+    inp = decode_inputs(wl, threads=16)
+    N = inp["N"]
+    announce(f"topk bf16 full size {wl.name} B={wl.B} N={N} k={wl.k}")
+    q_pos = [wl.T - 1] * wl.B
+    args = (inp["keys"], inp["q_idx"], inp["w"][:, None, :], np.array([N] * wl.B), q_pos, wl.k)
+    got, _, _ = run_topk(*args, bf16=True)
+    ref = oracle_topk(*args, bf16=True)
+    assert np.array_equal(got, ref)
+    f32_sel, _, _ = run_topk(*args)
+    recall = np.mean([np.intersect1d(got[b, 0], f32_sel[b, 0]).size / wl.k for b in range(wl.B)])
+    print(f"recall of the BF16 selection against the fp32 one: {recall:.4f}", flush=True)

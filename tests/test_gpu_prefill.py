@@ -163,14 +163,14 @@ def test_tiny_fp32_two_chunks():
 
 # ----------------------------------------------------- BF16 / FP8 / MXFP4 chunks ----
 
-def run_csa_chunk(w, slot=1, n_slots=2):
+def run_csa_chunk(w, slot=1, n_slots=2, score_bf16=False):
     """Cache the drawn entries in `slot`, run one CSA prefill chunk; returns everything a check needs."""
     x = prefill_inputs(w, kind="csa")
     C, tok0, n_prev, N0 = x["C"], x["tok0"], x["n_prev"], x["N0"]
     D, R, H, HI, dI, k, W = w.D, w.R, w.H, w.H_I, w.d_I, w.k, w.W
     n_total = (tok0 + C) // 4
     cap = n_total + 64
-    announce(f"prefill csa: tok0={tok0} C={C} cached={N0} H={H} k={k}")
+    announce(f"prefill csa: tok0={tok0} C={C} cached={N0} H={H} k={k} score_bf16={score_bf16}")
     kv = v4.KV.empty(n_slots, cap, D, R)
     keys = v4.Idx.empty(n_slots, cap, dI)
     v4.v4a_quantize_kv(f32(x["records"]), kv, slot * cap)
@@ -187,12 +187,12 @@ def run_csa_chunk(w, slot=1, n_slots=2):
                        idx_a=dev["idx_a"], idx_b=dev["idx_b"], idx_gate_a=f32(x["idx_gate_a"]),
                        idx_gate_b=f32(x["idx_gate_b"]), idx_bias_a=f32(x["idx_bias_a"]),
                        idx_bias_b=f32(x["idx_bias_b"]), keys=keys, q_idx=qi, w=f32(x["w"]), k=k, q=q_dev, W=W,
-                       sink=f32(x["sink"]), softmax_scale=w.scale, out=out)
+                       sink=f32(x["sink"]), softmax_scale=w.scale, out=out, score_bf16=score_bf16)
     ws = v4.workspace(v4.v4a_prefill_workspace(CSA, a))
     v4.v4a_prefill_chunk(CSA, a, ws)
     torch.cuda.synchronize()
     return dict(x=x, a=a, ws=ws, kv=kv, keys=keys, qi=qi, dev=dev, val=val, q_dev=q_dev, out=out, n_total=n_total,
-                cap=cap, slot=slot)
+                cap=cap, slot=slot, score_bf16=score_bf16)
 
 
 def check_csa_chunk(w, r, queries, decode_queries=()):
@@ -217,7 +217,8 @@ def check_csa_chunk(w, r, queries, decode_queries=()):
     announce("prefill csa: selections through v4a_indexer_topk, oracle on sampled queries")
     sel = torch.empty((1, C, k), dtype=torch.int32, device="cuda")
     ws = v4.workspace(v4.v4a_indexer_topk_workspace(1, C, n_total, k))
-    v4.v4a_indexer_topk(keys1, [n_total], 4, r["qi"], f32(x["w"]), 1, C, HI, [tok0 + j for j in range(C)], k, sel, ws)
+    topk_call = v4.v4a_indexer_topk_bf16 if r["score_bf16"] else v4.v4a_indexer_topk
+    topk_call(keys1, [n_total], 4, r["qi"], f32(x["w"]), 1, C, HI, [tok0 + j for j in range(C)], k, sel, ws)
     torch.cuda.synchronize()
     recs = dequant_slot(kv1, n_total)
     kc = keys1.codes[0, :n_total].cpu().numpy()
@@ -228,7 +229,7 @@ def check_csa_chunk(w, r, queries, decode_queries=()):
     ref, ref_sel = oracle.prefill_queries(
         "csa", q64, recs, n_total, r["val"]["kv_a"], n_prev=n_prev, tok0=tok0, queries=queries, W=W,
         sink=x["sink"], scale=w.scale, m=4, k=k,
-        idx=dict(q_codes=qc, q_scales=qs, w=x["w"], k_codes=kc, k_scales=ks), R=R)
+        idx=dict(q_codes=qc, q_scales=qs, w=x["w"], k_codes=kc, k_scales=ks), R=R, score_bf16=r["score_bf16"])
     gsel = sel[0].cpu().numpy()
     bad = [j for j in queries if not np.array_equal(gsel[j], ref_sel[j])]
     assert not bad, f"top-k differs for chunk queries {bad[:10]}"
@@ -252,6 +253,14 @@ def test_csa_mxfp4_chunk():
     w = scaled(PREFILL_64K, T=8192, chunk=700)
     r = run_csa_chunk(w)
     check_csa_chunk(w, r, sample_queries(700), decode_queries=(0, 349, 699))
+
+
+def test_csa_mxfp4_chunk_bf16_scores():
+    """The chunk with the BF16-score selector: selections equal v4a_indexer_topk_bf16's and the
+    oracle's over BF16-rounded scores."""
+    w = scaled(PREFILL_64K, T=8192, chunk=700)
+    r = run_csa_chunk(w, score_bf16=True)
+    check_csa_chunk(w, r, sample_queries(700), decode_queries=(349,))
 
 
 def run_hca_chunk(w):
