@@ -329,7 +329,8 @@ namespace v4a {
 // Launches of the indexer + top-k call once every argument has been checked.
 static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, int64_t n_max, const v4a_idx *q_idx,
                                       const float *w, int32_t B, int32_t Q, int32_t H_I, int32_t k, int32_t *out_idx,
-                                      void *ws, hipStream_t s, bool clear_hist = true, bool key16 = false) {
+                                      void *ws, hipStream_t s, bool clear_hist = true, bool key16 = false,
+                                      const CompressArgs *rec = nullptr) {
     const TopkWs L = topk_layout(B, Q, n_max, k);
     char *base = (char *)ws;
     const size_t BQ = (size_t)B * Q;
@@ -365,6 +366,7 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
     sa.counts = (uint32_t *)(base + L.counts);
     sa.meta = (int32_t *)(base + L.meta);
     sa.out = out_idx;
+    sa.rec = rec;
     return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
 }
 
@@ -932,10 +934,10 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     char *tws = base + pl.sel_bytes;
     const TopkWs L = topk_layout(a->B, 1, pl.n_max, a->k);
     const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
-    hipError_t e = launch_decode_prologue(pl.rec, pl.key, a->B, pl.entry, tws + L.hist, hist_bytes, s);
+    hipError_t e = launch_decode_prologue(pl.key, a->B, pl.entry, tws + L.hist, hist_bytes, s);
     if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
     st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false,
-                             a->score_bf16 != 0);
+                             a->score_bf16 != 0, &pl.rec);
     if (st != V4A_OK) return st;
     pl.at.topk = sel;
     pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;

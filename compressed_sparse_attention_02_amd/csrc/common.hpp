@@ -227,11 +227,11 @@ struct CompressArgs {
     int b0, n_seq;           // output slots b0 .. b0+n_seq-1; stream s at x + s * n_tok * D
 };
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s);
-// One launch: entry records (rec) and indexer keys (key) of entry[b] for every sequence b with
-// entry[b] >= 0 (each sequence's streams hold the 2m rows from the block before the entry's
-// own), plus clearing zero_bytes at zero.
-hipError_t launch_decode_prologue(const CompressArgs &rec, const CompressArgs &key, int B, const int64_t *entry,
-                                  void *zero, size_t zero_bytes, hipStream_t s);
+// One launch: the indexer keys (key) of entry[b] for every sequence b with entry[b] >= 0 (each
+// sequence's streams hold the 2m rows from the block before the entry's own), plus clearing
+// zero_bytes at zero.
+hipError_t launch_decode_prologue(const CompressArgs &key, int B, const int64_t *entry, void *zero,
+                                  size_t zero_bytes, hipStream_t s);
 
 struct IndexerArgs {
     const v4a_idx *keys;
@@ -262,6 +262,10 @@ struct SelectArgs {
     uint32_t *counts;             // [BQ][slices] entries listed per slice
     int32_t *meta;                // [BQ][2]: threshold bin, count above it
     int32_t *out;                 // [BQ][k]
+    // optional: the decode step's entry records, compressed by B extra workgroups of the final
+    // selection's launch (query b = sequence b, one query each; the entry is the one its
+    // position completes, if any)
+    const CompressArgs *rec;
 };
 int select_slices(int64_t n_max);
 constexpr int kSelSlice = 8192;

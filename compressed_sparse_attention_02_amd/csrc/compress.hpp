@@ -1,0 +1,185 @@
+// compress.hpp -- one compressed entry computed by one wavefront (a1/a2), shared by the
+// compressor kernels and by the decode step's launches that carry a compression alongside
+// other work.  "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.2; "DeepSeek V4
+// preview and technical report" (chooseai.net), section 1.
+#pragma once
+
+#include "encoders.hpp"
+
+namespace v4a {
+
+
+constexpr int kMaxCand = 256;  // 2 * 128 candidates at most
+
+struct CompressParams {
+    const void *x0, *x1;
+    const float *g0, *g1, *b0, *b1;
+    int n_streams, D, G, m, R;
+    bool bf16_in, rope;
+    int64_t tok0, first_entry, n_entries;
+    RopeTable rt;
+    v4a_kv kv;
+    v4a_idx idx;
+    bool to_idx;
+    int64_t out_row0;  // b0 * cap
+    int64_t cap;
+    int64_t n_tok;
+};
+
+template <int VPT>
+__device__ __forceinline__ void load_row(const void *base, bool bf16, int64_t row, int D, int d0,
+                                         bool active, float (&v)[VPT], int64_t off) {
+    if (!active) {
+#pragma unroll
+        for (int i = 0; i < VPT; i++) v[i] = 0.0f;
+        return;
+    }
+    if (bf16) {
+        const uint16_t *p = (const uint16_t *)base + off + row * D + d0;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) v[i] = bf16_to_f32(p[i]);
+    } else {
+        const float *p = (const float *)base + off + row * D + d0;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) v[i] = p[i];
+    }
+}
+
+// Entry i of sequence seq, computed by one whole wavefront; row 0 of the sequence's streams
+// is position tok0 (its streams and gates start n_tok rows further per sequence); wsh is the
+// wavefront's scratch for the candidate weights.
+template <int VPT>
+__device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
+                                               int64_t tok0) {
+    const int lane = threadIdx.x & 63;
+    const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
+    const int m = P.m, D = P.D;
+    const int d0 = lane * VPT;
+    const bool active = d0 < D;
+    // candidate c: stream s = c / m (0: own block i, 1: B-block i-1), position j = c % m
+    const int n_cand = (P.n_streams == 2 && i >= 1) ? 2 * m : m;
+
+    float acc[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
+
+    if (P.G == 1) {
+        // candidate rows are loaded in batches of kRowBatch; the first batch is issued before the
+        // gate logits so the two memory round trips overlap
+        constexpr int kRowBatch = 8;
+        float xb[kRowBatch][VPT];
+        auto load_batch = [&](int c0) {
+#pragma unroll
+            for (int u = 0; u < kRowBatch; u++) {
+                const int c = min(c0 + u, n_cand - 1);
+                const int s = c / m, j = c % m;
+                const int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+                load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, xb[u], x_off);
+            }
+        };
+        load_batch(0);
+        // weights once per wavefront: lane c holds candidate c (and c + 64, ...)
+        float zmax = -INFINITY;
+        for (int c = lane; c < n_cand; c += 64) {
+            int s = c / m, j = c % m;
+            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+            float z = (s == 0 ? P.g0 : P.g1)[g_off + r] + (s == 0 ? P.b0 : P.b1)[j];
+            wsh[c] = z;
+            zmax = fmaxf(zmax, z);
+        }
+        zmax = wave_max(zmax);
+        float den = 0.0f;
+        for (int c = lane; c < n_cand; c += 64) {
+            float ex = expf(wsh[c] - zmax);
+            wsh[c] = ex;
+            den += ex;
+        }
+        den = wave_sum(den);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int c0 = 0; c0 < n_cand; c0 += kRowBatch) {
+            float cur[kRowBatch][VPT];
+#pragma unroll
+            for (int u = 0; u < kRowBatch; u++)
+#pragma unroll
+                for (int v = 0; v < VPT; v++) cur[u][v] = xb[u][v];
+            if (c0 + kRowBatch < n_cand) load_batch(c0 + kRowBatch);  // next batch in flight
+#pragma unroll
+            for (int u = 0; u < kRowBatch; u++) {
+                if (c0 + u < n_cand) {
+                    const float wgt = wsh[c0 + u];
+#pragma unroll
+                    for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
+    } else {
+        // per-channel gates: online softmax over the candidates for each of this lane's dims
+        float mx[VPT], l[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; v++) { mx[v] = -INFINITY; l[v] = 0.0f; }
+        for (int c = 0; c < n_cand; c++) {
+            int s = c / m, j = c % m;
+            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+            float x[VPT];
+            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
+            const float *g = (s == 0 ? P.g0 : P.g1) + g_off + r * D + d0;
+            const float *bb = (s == 0 ? P.b0 : P.b1) + (int64_t)j * D + d0;
+#pragma unroll
+            for (int v = 0; v < VPT; v++) {
+                float z = active ? g[v] + bb[v] : 0.0f;
+                float mn = fmaxf(mx[v], z);
+                float corr = (mx[v] == -INFINITY) ? 0.0f : expf(mx[v] - mn);
+                float ex = (z == -INFINITY) ? 0.0f : expf(z - mn);
+                l[v] = l[v] * corr + ex;
+                acc[v] = acc[v] * corr + ex * x[v];
+                mx[v] = mn;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
+    }
+
+    // partial RoPE on the last R dims at position m*i (interleaved pairs); lane j < R/2
+    // evaluates pair j's cos/sin and the owning lanes read them across the wavefront
+    if (P.rope) {
+        const int rs = D - P.R, npairs = P.R / 2;
+        RopeLanes rl;
+        rl.eval(P.rt, npairs, (double)(m * i));
+        if constexpr (VPT >= 2) {
+#pragma unroll
+            for (int v = 0; v < VPT; v += 2) {
+                const int j = min(max((d0 - rs + v) / 2, 0), npairs - 1);
+                const float2 cs = rl.get(j);
+                if (active && d0 >= rs) {
+                    const float x = acc[v], y = acc[v + 1];
+                    acc[v] = x * cs.x - y * cs.y;
+                    acc[v + 1] = x * cs.y + y * cs.x;
+                }
+            }
+        } else {
+            const float partner = __shfl_xor(acc[0], 1);
+            const int j = min(max((d0 - rs) / 2, 0), npairs - 1);
+            const float2 cs = rl.get(j);
+            if (active && d0 >= rs) {
+                const bool even = ((d0 - rs) & 1) == 0;
+                const float x = even ? acc[0] : partner, y = even ? partner : acc[0];
+                acc[0] = even ? (x * cs.x - y * cs.y) : (x * cs.y + y * cs.x);
+            }
+        }
+    }
+
+    const int64_t orow = P.out_row0 + seq * P.cap + i;
+    if (P.to_idx)
+        store_mxfp4<VPT>(acc, lane, active, D, P.idx, orow);
+    else
+        store_record<VPT>(acc, d0, active, D, P.R, P.kv, orow);
+}
+
+// Kernel parameters of a checked CompressArgs (host).
+CompressParams compress_params(const CompressArgs &a);
+
+}  // namespace v4a

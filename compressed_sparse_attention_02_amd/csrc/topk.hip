@@ -22,7 +22,7 @@
 //             over the remaining 20 bits, and compacts the winners in index order (keys equal
 //             to the threshold go lowest index first), so the output is ascending without a
 //             sort.
-#include "common.hpp"
+#include "compress.hpp"
 
 namespace v4a {
 
@@ -49,6 +49,8 @@ struct SelParams {
     uint32_t *counts;
     int32_t *meta;
     int32_t *out;
+    CompressParams rec;      // entry records of the decode step (n_rec > 0)
+    int n_rec;               // extra workgroups of the final launch: one per sequence
 };
 
 // Block-wide inclusive prefix sum of one value per thread (thread order); `total` gets the
@@ -201,6 +203,11 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
 // key S* and how many keys equal to it are still needed (rem); the ordered compaction then
 // keeps every key above S* and the first rem keys equal to S* in index order (the lowest
 // indices win the tie).  One block scan places every kept key.
+//
+// With n_rec > 0 the launch also carries the decode step's record compression: workgroup
+// BQ + b compresses, with its first wavefront, the entry record that sequence b's newest token
+// completes (one query per sequence), overlapping the selection; attention reads the records
+// after this launch.
 __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, QueryPos QP) {
     __shared__ uint32_t wsum[kSelWaves];
     __shared__ int sT;
@@ -209,6 +216,21 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     __shared__ uint32_t lidx[kLdsList];
     __shared__ uint32_t lkey[kLdsList];
     __shared__ uint32_t soff[kMaxSlices + 1];
+    const int BQ = (int)gridDim.x - P.n_rec;
+    if ((int)blockIdx.x >= BQ) {
+        if (threadIdx.x >= 64) return;  // one wavefront per record
+        const int b = (int)blockIdx.x - BQ;
+        const int64_t pos = QP.pos[b];
+        const int m = P.rec.m;
+        if ((pos + 1) % m != 0) return;  // no block completed
+        const int64_t i = (pos + 1) / m - 1;
+        float *scratch = (float *)hist;  // kMaxCand floats; this workgroup does no selection
+        if (P.rec.D == 512)
+            compress_entry<8>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+        else
+            compress_entry<2>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+        return;
+    }
     const int qi = blockIdx.x, t = threadIdx.x;
     const int64_t n_vis = visible_keys(QP, qi);
     const uint32_t k_eff = (uint32_t)(n_vis < P.k ? n_vis : P.k);
@@ -359,7 +381,12 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
                            P, qp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_final_kernel, dim3((unsigned)a.BQ), dim3(kSelThreads), 0, s, P, qp);
+    if (a.rec) {  // one query per sequence: pos[b] is sequence b's position in either mode
+        if (qp.Q != 1) return hipErrorInvalidValue;
+        P.rec = compress_params(*a.rec);
+        P.n_rec = a.BQ;
+    }
+    hipLaunchKernelGGL(select_final_kernel, dim3((unsigned)(a.BQ + P.n_rec)), dim3(kSelThreads), 0, s, P, qp);
     return hipGetLastError();
 }
 

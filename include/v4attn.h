@@ -312,7 +312,8 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * whose newest token t = q_pos[b] completes a block ((t+1) % m == 0), entry (t+1)/m - 1 is
  * compressed into the record cache and the key cache; then the top-k of its visible entries
  * (n_entries[b] cached) are selected and attended over with the window and the sink.  The
- * compression and the selection's histogram clear share one launch.
+ * key compression and the selection's histogram clear share one launch; the record
+ * compression runs in the final selection's launch.
  * [cyqw] section 3.5 (the state cache keeps the incomplete block; a completed block becomes a
  * compressed entry) and the sections cited at the calls it composes.
  * Stream rows: every stream holds [B][2m] rows per sequence, the B-block before the completed
