@@ -121,6 +121,12 @@ def lib() -> ctypes.CDLL:
         L.v4a_decode_workspace.restype = SZ
         L.v4a_last_error.restype = ctypes.c_char_p
         L.v4a_version.restype = ctypes.c_char_p
+        L.v4a_trace_begin.argtypes = [I32]
+        L.v4a_trace_begin.restype = ctypes.c_int
+        L.v4a_trace_end.argtypes = []
+        L.v4a_trace_end.restype = I32
+        L.v4a_trace_kernel.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F32)]
+        L.v4a_trace_kernel.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -210,6 +216,26 @@ class Idx:
 
 def v4a_version() -> str:
     return lib().v4a_version().decode()
+
+
+def v4a_trace_begin(capacity: int):
+    _check(lib().v4a_trace_begin(capacity))
+
+
+def v4a_trace_end() -> int:
+    return int(lib().v4a_trace_end())
+
+
+def v4a_trace_kernel(i: int) -> tuple[str, float]:
+    """(kernel name, milliseconds) of the i-th kernel timed by the last trace."""
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    _check(lib().v4a_trace_kernel(i, ctypes.byref(name), ctypes.byref(ms)))
+    return name.value.decode(), float(ms.value)
+
+
+def trace_kernels(n: int) -> list[tuple[str, float]]:
+    """Every kernel of the last trace of n kernels (the caller has synchronised its streams)."""
+    return [v4a_trace_kernel(i) for i in range(n)]
 
 
 def v4a_quantize_kv(x: torch.Tensor, out: KV, row0: int = 0, stream=None):

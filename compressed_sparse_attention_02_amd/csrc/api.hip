@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "common.hpp"
 
@@ -35,6 +36,23 @@ static v4a_status fail(v4a_status st, const char *fmt, ...) {
 static v4a_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return V4A_OK;
     return fail(V4A_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Kernel timing: while armed, every kernel launch takes the next start/stop event pair.
+struct KernelTrace {
+    std::vector<hipEvent_t> start, stop;
+    std::vector<const char *> kernel;
+    int n = 0;
+    bool armed = false;
+};
+static KernelTrace g_trace;
+
+bool trace_claim(const char *kernel, hipEvent_t *start, hipEvent_t *stop) {
+    if (!g_trace.armed || g_trace.n >= (int)g_trace.start.size()) return false;
+    *start = g_trace.start[g_trace.n];
+    *stop = g_trace.stop[g_trace.n];
+    g_trace.kernel[g_trace.n++] = kernel;
+    return true;
 }
 
 void fill_rope_table(RopeTable &t, int R, double theta) {
@@ -942,6 +960,47 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     pl.at.topk = sel;
     pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;
     return hip_status(launch_attention(pl.at, pl.sq, s), "v4a_decode_step_csa: attention");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+v4a_status v4a_trace_begin(int32_t capacity) {
+    using namespace v4a;
+    if (capacity < 1 || capacity > (1 << 18)) return fail(V4A_EINVAL, "v4a_trace_begin: capacity=%d", capacity);
+    if (g_trace.armed) return fail(V4A_EINVAL, "v4a_trace_begin: a trace is already armed");
+    while ((int)g_trace.start.size() < capacity) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return fail(V4A_EHIP, "v4a_trace_begin: hipEventCreate failed");
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return fail(V4A_EHIP, "v4a_trace_begin: hipEventCreate failed");
+        }
+        g_trace.start.push_back(a);
+        g_trace.stop.push_back(b);
+        g_trace.kernel.push_back(nullptr);
+    }
+    g_trace.n = 0;
+    g_trace.armed = true;
+    return V4A_OK;
+}
+
+int32_t v4a_trace_end(void) {
+    v4a::g_trace.armed = false;
+    return v4a::g_trace.n;
+}
+
+v4a_status v4a_trace_kernel(int32_t i, const char **kernel, float *ms) {
+    using namespace v4a;
+    if (g_trace.armed) return fail(V4A_EINVAL, "v4a_trace_kernel: the trace is still armed");
+    if (i < 0 || i >= g_trace.n) return fail(V4A_EINVAL, "v4a_trace_kernel: kernel %d of %d", i, g_trace.n);
+    if (kernel) *kernel = g_trace.kernel[i];
+    if (ms) {
+        hipError_t e = hipEventElapsedTime(ms, g_trace.start[i], g_trace.stop[i]);
+        if (e != hipSuccess) return hip_status(e, "v4a_trace_kernel");
+    }
+    return V4A_OK;
 }
 
 }  // extern "C"

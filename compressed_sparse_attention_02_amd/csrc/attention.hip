@@ -629,7 +629,7 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     P.part_ml = a.partial ? a.partial + (size_t)a.B * P.S * a.H * a.D : nullptr;
     if (a.B == 0) return hipSuccess;
     if (!attn_uses_mfma(a)) {
-        hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);
+        V4A_LAUNCH("attn_f32_kernel", attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);
         return hipGetLastError();
     }
     P.n_hg = (a.H + 63) / 64;
@@ -638,12 +638,12 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     int blocks = pairs;
     if (P.n_hg == 2) blocks = ((pairs + 7) / 8) * 16;
     if (a.D == 512)
-        hipLaunchKernelGGL((attn_mfma_kernel<512, 64>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+        V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     else
-        hipLaunchKernelGGL((attn_mfma_kernel<128, 32>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+        V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.D / 16, a.H / 16, a.B), dim3(64), 0, s, P, sq);
+    V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel, dim3(a.D / 16, a.H / 16, a.B), dim3(64), 0, s, P, sq);
     return hipGetLastError();
 }
 

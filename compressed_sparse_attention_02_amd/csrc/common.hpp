@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "../../include/v4attn.h"
@@ -142,6 +143,21 @@ struct RopeLanes {
 
 // ---------------------------------------------------------------- host side ----------
 namespace v4a {
+
+// Kernel timing: while a trace is armed, claims the next pair of the library's timing events
+// for `kernel` and returns true; false otherwise (api.hip).
+bool trace_claim(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
+
+// Every kernel launch of the library: while a trace is armed the launch carries a start and a
+// stop event that time the dispatch itself (hipExtLaunchKernelGGL); otherwise a plain launch.
+#define V4A_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                                      \
+    do {                                                                                               \
+        hipEvent_t v4a_ev0_, v4a_ev1_;                                                                 \
+        if (::v4a::trace_claim(name, &v4a_ev0_, &v4a_ev1_))                                            \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, v4a_ev0_, v4a_ev1_, 0, __VA_ARGS__); \
+        else                                                                                           \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                       \
+    } while (0)
 
 // Per-sequence / per-query positions travel as kernel arguments (no host-to-device copy,
 // so every call stays asynchronous and capturable).

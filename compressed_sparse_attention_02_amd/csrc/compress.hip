@@ -91,10 +91,10 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     const CompressParams P = compress_params(a);
     dim3 grid((unsigned)((a.n_entries + 3) / 4), (unsigned)a.n_seq), block(256);
     switch (a.D) {
-        case 32: case 64: hipLaunchKernelGGL(compress_kernel<1>, grid, block, 0, s, P); break;
-        case 128: hipLaunchKernelGGL(compress_kernel<2>, grid, block, 0, s, P); break;
-        case 256: hipLaunchKernelGGL(compress_kernel<4>, grid, block, 0, s, P); break;
-        default: hipLaunchKernelGGL(compress_kernel<8>, grid, block, 0, s, P); break;
+        case 32: case 64: V4A_LAUNCH("compress_kernel", compress_kernel<1>, grid, block, 0, s, P); break;
+        case 128: V4A_LAUNCH("compress_kernel", compress_kernel<2>, grid, block, 0, s, P); break;
+        case 256: V4A_LAUNCH("compress_kernel", compress_kernel<4>, grid, block, 0, s, P); break;
+        default: V4A_LAUNCH("compress_kernel", compress_kernel<8>, grid, block, 0, s, P); break;
     }
     return hipGetLastError();
 }
@@ -114,9 +114,9 @@ hipError_t launch_decode_prologue(const CompressArgs &key, int B, const int64_t 
     const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 255) / 256, 1024);
     dim3 grid(zx > 0 ? zx : 1, (unsigned)(B + 1));
     if (key.D == 128)
-        hipLaunchKernelGGL(decode_prologue_kernel<2>, grid, dim3(256), 0, s, P);
+        V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(256), 0, s, P);
     else if (key.D == 32)
-        hipLaunchKernelGGL(decode_prologue_kernel<1>, grid, dim3(256), 0, s, P);
+        V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(256), 0, s, P);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

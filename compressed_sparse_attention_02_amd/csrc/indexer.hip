@@ -303,7 +303,7 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
     if (n16 == 0) return hipSuccess;
     size_t blocks = (n16 + 255) / 256;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16);
+    V4A_LAUNCH("zero_kernel", zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16);
     return hipGetLastError();
 }
 
@@ -341,14 +341,14 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
         P.groups_per_wave = gpw;
         const int64_t kpw = (int64_t)64 * gpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
-        hipLaunchKernelGGL(indexer_mxfp4_kernel, grid, dim3(256), 0, s, P, qp);
+        V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel, grid, dim3(256), 0, s, P, qp);
     } else {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
-        hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), 0, s, P, qp);
+        V4A_LAUNCH("indexer_f32_kernel", indexer_f32_kernel, grid, dim3(256), 0, s, P, qp);
     }
     if (a.scores) {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
-        hipLaunchKernelGGL(fill_invisible_kernel, grid, dim3(256), 0, s, a.scores, a.n_max, qp);
+        V4A_LAUNCH("fill_invisible_kernel", fill_invisible_kernel, grid, dim3(256), 0, s, a.scores, a.n_max, qp);
     }
     return hipGetLastError();
 }

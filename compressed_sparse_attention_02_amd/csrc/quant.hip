@@ -44,10 +44,10 @@ hipError_t launch_quantize_kv(const float *x, int64_t rows, const v4a_kv &out, i
     if (rows == 0) return hipSuccess;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     switch (out.D) {
-        case 32: case 64: hipLaunchKernelGGL(quantize_kv_kernel<1>, grid, block, 0, s, x, rows, out, row0); break;
-        case 128: hipLaunchKernelGGL(quantize_kv_kernel<2>, grid, block, 0, s, x, rows, out, row0); break;
-        case 256: hipLaunchKernelGGL(quantize_kv_kernel<4>, grid, block, 0, s, x, rows, out, row0); break;
-        default: hipLaunchKernelGGL(quantize_kv_kernel<8>, grid, block, 0, s, x, rows, out, row0); break;
+        case 32: case 64: V4A_LAUNCH("quantize_kv_kernel", quantize_kv_kernel<1>, grid, block, 0, s, x, rows, out, row0); break;
+        case 128: V4A_LAUNCH("quantize_kv_kernel", quantize_kv_kernel<2>, grid, block, 0, s, x, rows, out, row0); break;
+        case 256: V4A_LAUNCH("quantize_kv_kernel", quantize_kv_kernel<4>, grid, block, 0, s, x, rows, out, row0); break;
+        default: V4A_LAUNCH("quantize_kv_kernel", quantize_kv_kernel<8>, grid, block, 0, s, x, rows, out, row0); break;
     }
     return hipGetLastError();
 }
@@ -57,10 +57,10 @@ hipError_t launch_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx &ou
     if (rows == 0) return hipSuccess;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     switch (out.d) {
-        case 32: case 64: hipLaunchKernelGGL(quantize_mxfp4_kernel<1>, grid, block, 0, s, x, rows, out, row0); break;
-        case 128: hipLaunchKernelGGL(quantize_mxfp4_kernel<2>, grid, block, 0, s, x, rows, out, row0); break;
-        case 256: hipLaunchKernelGGL(quantize_mxfp4_kernel<4>, grid, block, 0, s, x, rows, out, row0); break;
-        default: hipLaunchKernelGGL(quantize_mxfp4_kernel<8>, grid, block, 0, s, x, rows, out, row0); break;
+        case 32: case 64: V4A_LAUNCH("quantize_mxfp4_kernel", quantize_mxfp4_kernel<1>, grid, block, 0, s, x, rows, out, row0); break;
+        case 128: V4A_LAUNCH("quantize_mxfp4_kernel", quantize_mxfp4_kernel<2>, grid, block, 0, s, x, rows, out, row0); break;
+        case 256: V4A_LAUNCH("quantize_mxfp4_kernel", quantize_mxfp4_kernel<4>, grid, block, 0, s, x, rows, out, row0); break;
+        default: V4A_LAUNCH("quantize_mxfp4_kernel", quantize_mxfp4_kernel<8>, grid, block, 0, s, x, rows, out, row0); break;
     }
     return hipGetLastError();
 }

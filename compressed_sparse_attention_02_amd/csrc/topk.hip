@@ -374,10 +374,10 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
     P.meta = a.meta;
     P.out = a.out;
     if (a.key16)
-        hipLaunchKernelGGL(select_scan_kernel<true>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
+        V4A_LAUNCH("select_scan_kernel", select_scan_kernel<true>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
                            P, qp);
     else
-        hipLaunchKernelGGL(select_scan_kernel<false>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
+        V4A_LAUNCH("select_scan_kernel", select_scan_kernel<false>, dim3((unsigned)P.slices, (unsigned)a.BQ), dim3(kSelThreads), 0, s,
                            P, qp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -386,7 +386,7 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
         P.rec = compress_params(*a.rec);
         P.n_rec = a.BQ;
     }
-    hipLaunchKernelGGL(select_final_kernel, dim3((unsigned)(a.BQ + P.n_rec)), dim3(kSelThreads), 0, s, P, qp);
+    V4A_LAUNCH("select_final_kernel", select_final_kernel, dim3((unsigned)(a.BQ + P.n_rec)), dim3(kSelThreads), 0, s, P, qp);
     return hipGetLastError();
 }
 

@@ -358,6 +358,21 @@ V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *w
 /* Workspace of v4a_decode_step_csa for these arguments (0 if they are invalid). */
 V4A_API size_t v4a_decode_step_workspace(const v4a_decode_step_args *args);
 
+/* ------------------------------------------------------------------- kernel timing ----
+ * Instrumentation, off by default: each kernel the library launches can be timed on the GPU.
+ * v4a_trace_begin arms a trace of at most `capacity` kernel launches (1 .. 2^18): until
+ * v4a_trace_end, every kernel launched by any call carries its own start and stop HIP events
+ * (hipExtLaunchKernelGGL), which time the dispatch itself; launches past `capacity` run
+ * untimed.  v4a_trace_end disarms and returns the number of kernels timed.  After the caller
+ * has synchronised the streams, v4a_trace_kernel(i, &kernel, &ms) gives the i-th timed
+ * kernel's name (a static string, e.g. "indexer_mxfp4_kernel") and its duration in
+ * milliseconds.  The events are the library's, created on the current device at the first
+ * v4a_trace_begin and kept until the process ends.  One trace at a time per process; not
+ * thread-safe. */
+V4A_API v4a_status v4a_trace_begin(int32_t capacity);
+V4A_API int32_t v4a_trace_end(void);
+V4A_API v4a_status v4a_trace_kernel(int32_t i, const char **kernel, float *ms);
+
 /* ---------------------------------------------------------------------- utilities ---- */
 V4A_API const char *v4a_last_error(void);
 V4A_API const char *v4a_version(void);

@@ -248,3 +248,10 @@ def test_decode_step_workspace_and_rejects():
     pos = i64(*[1048575] * 4)
     short = i64(262143, 262144, 262144, 262144)   # sequence 0 would not hold the entry it completes
     assert call(n_entries=ctypes.cast(short, ctypes.c_void_p), q_pos=ctypes.cast(pos, ctypes.c_void_p)) == 1
+
+
+def test_trace_without_marks_is_an_error():
+    # no trace has recorded anything in this process: asking for a mark fails before any HIP call
+    assert v4.v4a_trace_end() == 0
+    with pytest.raises(v4.V4AError):
+        v4.v4a_trace_kernel(0)

@@ -63,7 +63,15 @@ def test_fused_step_equals_separate_calls(score_bf16):
                              q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
                              softmax_scale=scale, out=out1, score_bf16=score_bf16)
     ws1 = v4.workspace(v4.v4a_decode_step_workspace(args))
+    # timed: the call's kernels in launch order, each with a positive duration
+    v4.v4a_trace_begin(16)
     v4.v4a_decode_step_csa(args, ws1)
+    n = v4.v4a_trace_end()
+    torch.cuda.synchronize()
+    kernels = v4.trace_kernels(n)
+    assert [name for name, _ in kernels] == ["decode_prologue_kernel", "indexer_mxfp4_kernel", "select_scan_kernel",
+                                             "select_final_kernel", "attn_mfma_kernel", "attn_combine_kernel"], kernels
+    assert all(ms > 0 for _, ms in kernels), kernels
 
     # the separate calls
     kv2, keys2 = clone_kv(kv), clone_idx(keys)
