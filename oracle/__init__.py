@@ -72,9 +72,9 @@ def _declare(L):
     L.orc_dequant_mxfp4.argtypes = [P, P, I64, I32, P]
     L.orc_rope.argtypes = [P, I64, I32, I32, P, F64, I32]
     L.orc_compress_csa.argtypes = [P, P, I32, P, P, I32, P, P, I64, I64, I32, I64, I64, I32, I32,
-                                   F64, P]
+                                   F64, P, F64, P]
     L.orc_compress_csa.restype = I32
-    L.orc_compress_hca.argtypes = [P, I32, P, I32, P, I64, I64, I32, I64, I64, I32, I32, F64, P]
+    L.orc_compress_hca.argtypes = [P, I32, P, I32, P, I64, I64, I32, I64, I64, I32, I32, F64, P, F64, P]
     L.orc_compress_hca.restype = I32
     L.orc_indexer_scores_mxfp4.argtypes = [P, P, P, I32, I32, P, P, I64, P, P]
     L.orc_indexer_scores_f32.argtypes = [P, P, I32, I32, P, I64, P]
@@ -176,8 +176,9 @@ def rope(x: np.ndarray, R: int, pos, theta: float = 10000.0, sign: int = 1) -> n
 # ------------------------------------------------------------- compressors ---
 
 def compress_csa(kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, *, tok0, m, first_entry, n_entries,
-                 apply_rope, R, theta=10000.0) -> np.ndarray:
-    """fp32 CSA entries [n_entries][D] (before quantisation)."""
+                 apply_rope, R, theta=10000.0, norm_w=None, eps=1e-6) -> np.ndarray:
+    """fp32 CSA entries [n_entries][D] (before quantisation); norm_w [D] RMS-normalises each merged
+    entry before RoPE."""
     kv_a, pa = _c(kv_a, np.float32)
     kv_b, pb = _c(kv_b, np.float32)
     gate_a, pga = _c(gate_a, np.float32)
@@ -187,23 +188,26 @@ def compress_csa(kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, *, tok0, m, first_e
     n_tok, D = kv_a.shape
     G = gate_a.shape[1]
     out = np.empty((n_entries, D), np.float32)
+    nw, pnw = _c(norm_w, np.float32) if norm_w is not None else (None, None)
     rc = lib().orc_compress_csa(pa, pb, D, pga, pgb, G, pba, pbb, tok0, n_tok, m, first_entry,
-                                n_entries, int(apply_rope), R, float(theta), out.ctypes.data_as(P))
+                                n_entries, int(apply_rope), R, float(theta), pnw, float(eps),
+                                out.ctypes.data_as(P))
     if rc != 0:
         raise ValueError("rows do not cover the blocks these entries need")
     return out
 
 
 def compress_hca(kv, gate, bias, *, tok0, m, first_entry, n_entries, apply_rope, R,
-                 theta=10000.0) -> np.ndarray:
+                 theta=10000.0, norm_w=None, eps=1e-6) -> np.ndarray:
     kv, pk = _c(kv, np.float32)
     gate, pg = _c(gate, np.float32)
     bias, pbi = _c(bias, np.float32)
     n_tok, D = kv.shape
     G = gate.shape[1]
     out = np.empty((n_entries, D), np.float32)
+    nw, pnw = _c(norm_w, np.float32) if norm_w is not None else (None, None)
     rc = lib().orc_compress_hca(pk, D, pg, G, pbi, tok0, n_tok, m, first_entry, n_entries,
-                                int(apply_rope), R, float(theta), out.ctypes.data_as(P))
+                                int(apply_rope), R, float(theta), pnw, float(eps), out.ctypes.data_as(P))
     if rc != 0:
         raise ValueError("rows do not cover the blocks these entries need")
     return out

@@ -273,6 +273,17 @@ static void gated_merge(int ncand, const float *const *X, const double *logit /*
     }
 }
 
+/* RMSNorm of one merged entry: y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d.
+ * Cited: [cyqw] section 2.3 (V4's attention lets RMSNorm act directly on the
+ * queries and the KV entries, in place of QK-Clip).  Reading: the norm acts on
+ * the merged fp32 entry before RoPE and quantisation; eps is a parameter. */
+static void rms_norm(double *x, int D, const float *w, double eps) {
+    double ss = 0.0;
+    for (int d = 0; d < D; d++) ss += x[d] * x[d];
+    const double r = 1.0 / sqrt(ss / (double)D + eps);
+    for (int d = 0; d < D; d++) x[d] = x[d] * r * (double)w[d];
+}
+
 /* CSA compressor (ratio m, two streams with overlap).  Cited: [cyqw]
  * section 2.2 (every m = 4 tokens become one entry; two independent KV
  * sequences merged with softmax-normalised gate weights; adjacent compressed
@@ -280,8 +291,9 @@ static void gated_merge(int ncand, const float *const *X, const double *logit /*
  * positional bias).  Reading: entry i merges A-block i (tokens m*i .. m*i+m-1
  * of stream A, logits gate_a[t] + bias_a[j]) with B-block i-1 (tokens
  * m*(i-1)+j of stream B, logits gate_b[t] + bias_b[j]); entry 0 has no
- * B-block and merges its A-block alone.  After the merge the RoPE slice is
- * rotated at position m*i (if apply_rope) and the entry is rounded to fp32.
+ * B-block and merges its A-block alone.  After the merge the entry is
+ * RMS-normalised with weights norm_w (if not NULL), the RoPE slice is rotated
+ * at position m*i (if apply_rope) and the entry is rounded to fp32.
  *   kv_a, kv_b [n_tok][D] fp32, row r holds token tok0 + r
  *   gate_a, gate_b [n_tok][G]; bias_a, bias_b [m][G]
  *   writes out [n_entries][D] fp32 for entries first_entry .. first_entry+n_entries-1.
@@ -289,7 +301,8 @@ static void gated_merge(int ncand, const float *const *X, const double *logit /*
 ORC_API int orc_compress_csa(const float *kv_a, const float *kv_b, int D, const float *gate_a,
                              const float *gate_b, int G, const float *bias_a, const float *bias_b,
                              int64_t tok0, int64_t n_tok, int m, int64_t first_entry,
-                             int64_t n_entries, int apply_rope, int R, double theta, float *out) {
+                             int64_t n_entries, int apply_rope, int R, double theta,
+                             const float *norm_w, double eps, float *out) {
     const float **X = malloc(sizeof(float *) * 2 * m);
     double *logit = malloc(sizeof(double) * 2 * m * G);
     double *tmp = malloc(sizeof(double) * D);
@@ -318,6 +331,7 @@ ORC_API int orc_compress_csa(const float *kv_a, const float *kv_b, int D, const 
         }
         if (rc) break;
         gated_merge(nc, X, logit, G, D, tmp);
+        if (norm_w) rms_norm(tmp, D, norm_w, eps);
         if (apply_rope) rope_rotate(tmp + (D - R), R, (double)(m * i), theta, +1);
         for (int d = 0; d < D; d++) out[e * D + d] = (float)tmp[d];
     }
@@ -331,10 +345,11 @@ ORC_API int orc_compress_csa(const float *kv_a, const float *kv_b, int D, const 
  * section 2.2 and [firecat] item 2 (every 128 tokens become one entry, no
  * sparse selection) and [chooseai] section 1 (no overlapped compression).
  * Entry i merges tokens m*i .. m*i+m-1 with logits gate[t] + bias[j]; then
- * RoPE at m*i and rounding to fp32 as for CSA. */
+ * RMSNorm (if norm_w), RoPE at m*i and rounding to fp32 as for CSA. */
 ORC_API int orc_compress_hca(const float *kv, int D, const float *gate, int G, const float *bias,
                              int64_t tok0, int64_t n_tok, int m, int64_t first_entry,
-                             int64_t n_entries, int apply_rope, int R, double theta, float *out) {
+                             int64_t n_entries, int apply_rope, int R, double theta,
+                             const float *norm_w, double eps, float *out) {
     const float **X = malloc(sizeof(float *) * m);
     double *logit = malloc(sizeof(double) * m * G);
     double *tmp = malloc(sizeof(double) * D);
@@ -350,6 +365,7 @@ ORC_API int orc_compress_hca(const float *kv, int D, const float *gate, int G, c
         }
         if (rc) break;
         gated_merge(m, X, logit, G, D, tmp);
+        if (norm_w) rms_norm(tmp, D, norm_w, eps);
         if (apply_rope) rope_rotate(tmp + (D - R), R, (double)(m * i), theta, +1);
         for (int d = 0; d < D; d++) out[e * D + d] = (float)tmp[d];
     }

@@ -156,3 +156,59 @@ def test_p14_chunked_compression_equals_whole_sequence(orc):
                                               first_entry=c // 128, n_entries=2, apply_rope=True,
                                               R=w.R) for c in range(0, T, 256)])
     assert np.array_equal(part_h, whole_h)
+
+
+# ------------------------------------------------------------- RMSNorm of entries ---
+# "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.3: RMSNorm acts directly on
+# the queries and KV entries.  Reading: it normalises each merged entry before RoPE.
+
+def rms_norm_torch(x, w, eps):
+    """torch's own RMSNorm (a library implementation) in float64."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, np.float64))
+    return torch.nn.functional.rms_norm(t, (t.shape[-1],), torch.from_numpy(np.asarray(w, np.float64)),
+                                        eps).numpy()
+
+
+def csa_inputs(seed, T=64, D=64, m=4):
+    g = np.random.default_rng(seed)
+    f = lambda *s: g.standard_normal(s).astype(np.float32)
+    return dict(kv_a=f(T, D), kv_b=f(T, D), gate_a=f(T, 1), gate_b=f(T, 1), bias_a=f(m, 1), bias_b=f(m, 1))
+
+
+def test_entry_rmsnorm_matches_torch_and_precedes_rope(orc):
+    D, R, m, eps = 64, 16, 4, 1e-6
+    x = csa_inputs(41, D=D)
+    g = np.random.default_rng(42)
+    w = (0.5 + g.random(D)).astype(np.float32)  # unequal within RoPE pairs: the orders differ
+    kw = dict(tok0=0, m=m, first_entry=0, n_entries=16, R=R)
+    plain = orc.compress_csa(**x, apply_rope=False, **kw).astype(np.float64)
+    normed = orc.compress_csa(**x, apply_rope=False, norm_w=w, eps=eps, **kw)
+    np.testing.assert_allclose(normed, rms_norm_torch(plain, w, eps), rtol=2e-6, atol=1e-7)
+    # with RoPE: the norm comes first, then the rotation at the entry position
+    full = orc.compress_csa(**x, apply_rope=True, norm_w=w, eps=eps, **kw)
+    pos = m * np.arange(16)
+    expect = orc.rope(rms_norm_torch(plain, w, eps), R, pos)
+    np.testing.assert_allclose(full, expect, rtol=2e-6, atol=1e-7)
+    rotated_first = rms_norm_torch(orc.compress_csa(**x, apply_rope=True, **kw), w, eps)
+    assert np.abs(full - rotated_first).max() > 1e-3
+
+
+def test_entry_rmsnorm_unit_weights_give_unit_mean_square(orc):
+    x = csa_inputs(43, D=128)
+    y = orc.compress_csa(**x, tok0=0, m=4, first_entry=0, n_entries=16, apply_rope=True, R=32,
+                         norm_w=np.ones(128, np.float32), eps=0.0).astype(np.float64)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-6)
+
+
+def test_hca_entry_rmsnorm_matches_torch(orc):
+    g = np.random.default_rng(44)
+    T, D, m = 512, 64, 128
+    kv = g.standard_normal((T, D)).astype(np.float32)
+    gate = g.standard_normal((T, 1)).astype(np.float32)
+    bias = g.standard_normal((m, 1)).astype(np.float32)
+    w = (0.5 + g.random(D)).astype(np.float32)
+    kw = dict(tok0=0, m=m, first_entry=0, n_entries=4, R=16)
+    plain = orc.compress_hca(kv, gate, bias, apply_rope=False, **kw)
+    normed = orc.compress_hca(kv, gate, bias, apply_rope=False, norm_w=w, eps=1e-6, **kw)
+    np.testing.assert_allclose(normed, rms_norm_torch(plain, w, 1e-6), rtol=2e-6, atol=1e-7)
