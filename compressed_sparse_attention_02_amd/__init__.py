@@ -54,7 +54,7 @@ class c_prefill_args(ctypes.Structure):
                 ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("sink", P), ("softmax_scale", ctypes.c_float),
                 ("out_rope_inverse", ctypes.c_int32), ("out", P), ("out_t", ctypes.c_int),
-                ("score_bf16", ctypes.c_int32)]
+                ("score_bf16", ctypes.c_int32), ("norm_w", P), ("idx_norm_w", P)]
 
 
 V4A_LAYER_CSA, V4A_LAYER_HCA = 0, 1
@@ -71,7 +71,8 @@ class c_decode_step_args(ctypes.Structure):
                 ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
                 ("H", ctypes.c_int32), ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32),
                 ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
-                ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32)]
+                ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32), ("norm_w", P),
+                ("idx_norm_w", P)]
 
 _lib = None
 
@@ -251,26 +252,27 @@ def v4a_quantize_mxfp4(x: torch.Tensor, out: Idx, row0: int = 0, stream=None):
 def v4a_compress_csa(kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, *, tok0: int, m: int,
                      first_entry: int, n_entries: int, apply_rope: bool = True,
                      rope_theta: float = 10000.0, out_kv: KV | None = None,
-                     out_idx: Idx | None = None, b: int = 0, stream=None):
-    """Streams are [n_tok][D] (one sequence, slot b) or [n_seq][n_tok][D] (slots b..b+n_seq-1)."""
+                     out_idx: Idx | None = None, b: int = 0, norm_w=None, stream=None):
+    """Streams are [n_tok][D] (one sequence, slot b) or [n_seq][n_tok][D] (slots b..b+n_seq-1);
+    norm_w [D] f32 RMS-normalises each merged entry before RoPE."""
     D = kv_a.shape[-1]
     G = gate_a.shape[-1]
     n_tok = kv_a.shape[-2]
     n_seq = kv_a.shape[0] if kv_a.dim() == 3 else 1
     _check(lib().v4a_compress_csa(
         _ptr(kv_a), _ptr(kv_b), _ftype(kv_a), D, _ptr(gate_a), _ptr(gate_b), G, _ptr(bias_a),
-        _ptr(bias_b), tok0, n_tok, m, first_entry, n_entries, int(apply_rope), rope_theta, None,
+        _ptr(bias_b), tok0, n_tok, m, first_entry, n_entries, int(apply_rope), rope_theta, _ptr(norm_w),
         ctypes.byref(out_kv.c()) if out_kv is not None else None,
         ctypes.byref(out_idx.c()) if out_idx is not None else None, b, n_seq, _stream(stream)))
 
 
 def v4a_compress_hca(kv, gate, bias, *, tok0: int, m: int, first_entry: int, n_entries: int,
                      apply_rope: bool = True, rope_theta: float = 10000.0, out_kv: KV, b: int = 0,
-                     stream=None):
+                     norm_w=None, stream=None):
     n_seq = kv.shape[0] if kv.dim() == 3 else 1
     _check(lib().v4a_compress_hca(
         _ptr(kv), _ftype(kv), kv.shape[-1], _ptr(gate), gate.shape[-1], _ptr(bias), tok0,
-        kv.shape[-2], m, first_entry, n_entries, int(apply_rope), rope_theta, None,
+        kv.shape[-2], m, first_entry, n_entries, int(apply_rope), rope_theta, _ptr(norm_w),
         ctypes.byref(out_kv.c()), b, n_seq, _stream(stream)))
 
 
@@ -339,12 +341,12 @@ class PrefillArgs:
                  apply_rope: bool = True, rope_theta: float = 10000.0, idx_a=None, idx_b=None,
                  idx_gate_a=None, idx_gate_b=None, idx_bias_a=None, idx_bias_b=None, keys: Idx | None = None,
                  q_idx: Idx | None = None, w=None, k: int = 0, out_rope_inverse: bool = True,
-                 score_bf16: bool = False):
+                 score_bf16: bool = False, norm_w=None, idx_norm_w=None):
         self._kv = kv.c()
         self._keys = keys.c() if keys is not None else None
         self._q_idx = q_idx.c() if q_idx is not None else None
         self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b,
-                      idx_bias_a, idx_bias_b, w, q, sink, out, kv, keys, q_idx)
+                      idx_bias_a, idx_bias_b, w, q, sink, out, kv, keys, q_idx, norm_w, idx_norm_w)
         C, H = q.shape[0], q.shape[1]
         H_I = (w.numel() // C) if (w is not None and C > 0) else 0
         self.s = c_prefill_args(
@@ -359,7 +361,7 @@ class PrefillArgs:
             q_idx=ctypes.pointer(self._q_idx) if self._q_idx is not None else None,
             w=_ptr(w), H_I=H_I, k=k, q=_ptr(q), q_t=_ftype(q), H=H, W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out),
-            out_t=_ftype(out), score_bf16=int(score_bf16))
+            out_t=_ftype(out), score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w))
 
 
 def v4a_prefill_workspace(kind: int, args: PrefillArgs) -> int:
@@ -378,12 +380,13 @@ class DecodeStepArgs:
     def __init__(self, *, q_pos, n_entries, m: int, kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b,
                  idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
                  win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
-                 rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False):
+                 rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False,
+                 norm_w=None, idx_norm_w=None):
         B, H = q.shape[0], q.shape[1]
         self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
         self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b, idx_bias_a,
-                      idx_bias_b, kv, keys, q_idx, w, q, win, sink, out)
+                      idx_bias_b, kv, keys, q_idx, w, q, win, sink, out, norm_w, idx_norm_w)
         self.s = c_decode_step_args(
             B=B, m=m, q_pos=ctypes.cast(self._pos, ctypes.c_void_p), n_entries=ctypes.cast(self._nent, ctypes.c_void_p),
             in_t=_ftype(kv_a), G=gate_a.shape[-1], idx_G=idx_gate_a.shape[-1], kv_a=_ptr(kv_a), kv_b=_ptr(kv_b),
@@ -394,7 +397,7 @@ class DecodeStepArgs:
             q_idx=ctypes.pointer(self._q_idx), w=_ptr(w), H_I=w.numel() // B, k=k, q=_ptr(q), q_t=_ftype(q), H=H,
             win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out),
-            score_bf16=int(score_bf16))
+            score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w))
 
 
 def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:

@@ -224,7 +224,8 @@ v4a_status v4a_quantize_mxfp4(const float *x, int64_t rows, const v4a_idx *out, 
 }
 
 static v4a_status compress_check(CompressArgs &a, const float *norm_w) {
-    if (norm_w) return fail(V4A_EUNSUPPORTED, "norm_w must be NULL");
+    if (norm_w && !aligned(norm_w, 4)) return fail(V4A_EINVAL, "norm_w is misaligned");
+    a.norm_w = norm_w;
     if (a.D != 32 && a.D != 64 && a.D != 128 && a.D != 256 && a.D != 512)
         return fail(V4A_EUNSUPPORTED, "D=%d: need 32, 64, 128, 256 or 512", a.D);
     if (a.G != 1 && a.G != a.D) return fail(V4A_EUNSUPPORTED, "G must be 1 or D");
@@ -696,7 +697,7 @@ static v4a_status prefill_plan(v4a_layer kind, const v4a_prefill_args *a, Prefil
     c.kv = a->kv;
     c.b0 = a->slot;
     c.n_seq = 1;
-    if ((st = compress_check(c, nullptr)) != V4A_OK) return st;
+    if ((st = compress_check(c, a->norm_w)) != V4A_OK) return st;
     if ((int64_t)(a->slot + 1) * a->kv->cap < 0) return fail(V4A_EINVAL, "v4a_prefill_chunk: slot");
     pl.kv = *a->kv;
     {
@@ -746,7 +747,7 @@ static v4a_status prefill_plan(v4a_layer kind, const v4a_prefill_args *a, Prefil
         ci.idx = a->keys;
         ci.b0 = a->slot;
         ci.n_seq = 1;
-        if ((st = compress_check(ci, nullptr)) != V4A_OK) return st;
+        if ((st = compress_check(ci, a->idx_norm_w)) != V4A_OK) return st;
         pl.keys = *a->keys;
         const int64_t base = (int64_t)a->slot * a->keys->cap;
         if (a->keys->fmt == V4A_IDX_MXFP4) {
@@ -879,10 +880,10 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     fill(pl.rec, a->kv_a, a->kv_b, a->gate_a, a->gate_b, a->bias_a, a->bias_b, D, a->G);
     pl.rec.rope = a->apply_rope != 0;
     pl.rec.kv = a->kv;
-    if ((st = compress_check(pl.rec, nullptr)) != V4A_OK) return st;
+    if ((st = compress_check(pl.rec, a->norm_w)) != V4A_OK) return st;
     fill(pl.key, a->idx_a, a->idx_b, a->idx_gate_a, a->idx_gate_b, a->idx_bias_a, a->idx_bias_b, d, a->idx_G);
     pl.key.idx = a->keys;
-    if ((st = compress_check(pl.key, nullptr)) != V4A_OK) return st;
+    if ((st = compress_check(pl.key, a->idx_norm_w)) != V4A_OK) return st;
     for (int b = 0; b < a->B; b++) {
         const int64_t t = a->q_pos[b];
         if (t < 0) return fail(V4A_EINVAL, "v4a_decode_step_csa: q_pos[%d] < 0", b);

@@ -241,7 +241,9 @@ struct CompressArgs {
     const v4a_kv *kv;        // exactly one of kv / idx
     const v4a_idx *idx;
     int b0, n_seq;           // output slots b0 .. b0+n_seq-1; stream s at x + s * n_tok * D
+    const float *norm_w;     // [D] RMSNorm weights of the merged entry, or NULL
 };
+constexpr float kNormEps = 1e-6f;  // RMSNorm epsilon of the compressed entries
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s);
 // One launch: the indexer keys (key) of entry[b] for every sequence b with entry[b] >= 0 (each
 // sequence's streams hold the 2m rows from the block before the entry's own), plus clearing

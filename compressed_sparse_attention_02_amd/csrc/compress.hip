@@ -83,6 +83,7 @@ CompressParams compress_params(const CompressArgs &a) {
     P.cap = a.idx ? a.idx->cap : a.kv->cap;
     P.out_row0 = (int64_t)a.b0 * P.cap;
     P.n_tok = a.n_tok;
+    P.norm_w = a.norm_w;
     return P;
 }
 

@@ -24,6 +24,7 @@ struct CompressParams {
     int64_t out_row0;  // b0 * cap
     int64_t cap;
     int64_t n_tok;
+    const float *norm_w;  // [D] or NULL
 };
 
 template <int VPT>
@@ -62,6 +63,12 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
     float acc[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
+    // RMSNorm weights of this lane's dims, requested first so their latency overlaps the rows'
+    float nw[VPT];
+    if (P.norm_w) {
+#pragma unroll
+        for (int v = 0; v < VPT; v++) nw[v] = active ? P.norm_w[d0 + v] : 0.0f;
+    }
 
     if (P.G == 1) {
         // candidate rows are loaded in batches of kRowBatch; the first batch is issued before the
@@ -141,6 +148,20 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
         }
 #pragma unroll
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
+    }
+
+    // RMSNorm of the merged entry ("DeepSeek-V4 technical report walkthrough", section 2.3:
+    // RMSNorm acts directly on the KV entries): x * w / sqrt(mean(x^2) + eps), before RoPE
+    if (P.norm_w) {
+        float ss = 0.0f;
+        if (active) {
+#pragma unroll
+            for (int v = 0; v < VPT; v++) ss = fmaf(acc[v], acc[v], ss);
+        }
+        ss = __shfl(wave_sum(ss), 0);  // one value for every lane
+        const float r = 1.0f / sqrtf(ss / (float)D + kNormEps);
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] * r * nw[v];
     }
 
     // partial RoPE on the last R dims at position m*i (interleaved pairs); lane j < R/2

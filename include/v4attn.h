@@ -135,7 +135,9 @@ V4A_API v4a_status v4a_quantize_mxfp4(const float *x, int64_t rows, const v4a_id
  *   D == out_idx->d, no RoPE).  The rows must cover every block these entries read:
  *   tok0 <= m*(first_entry-1) (or tok0 <= 0 when first_entry == 0) and
  *   m*(first_entry+n_entries) <= tok0 + n_tok; tok0 must be a multiple of m.
- *   norm_w must be NULL (Q/KV RMSNorm is not part of this build).
+ *   norm_w: NULL, or [D] f32 (device) RMSNorm weights: [cyqw] section 2.3 (RMSNorm acts
+ *   directly on the KV entries).  Each merged entry x becomes x_d * norm_w[d] /
+ *   sqrt(mean(x^2) + 1e-6) before RoPE and encoding.
  *   Supports m in [1, 128], G in {1, D}, D in {32, 128, 512}. */
 V4A_API v4a_status v4a_compress_csa(const void *kv_a, const void *kv_b, v4a_float in_t, int32_t D,
                             const float *gate_a, const float *gate_b, int32_t G,
@@ -299,6 +301,8 @@ typedef struct {
     void *out;               /* [C][H][D] (device, out_t)                                 */
     v4a_float out_t;
     int32_t score_bf16;      /* CSA: nonzero selects as v4a_indexer_topk_bf16 does         */
+    const float *norm_w;     /* [D] f32 (device): RMSNorm of the new entries, or NULL      */
+    const float *idx_norm_w; /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL */
 } v4a_prefill_args;
 
 V4A_API v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *args, void *ws,
@@ -351,6 +355,8 @@ typedef struct {
     void *out;                   /* [B][H][D] (device)                                         */
     v4a_float out_t;
     int32_t score_bf16;          /* nonzero: select as v4a_indexer_topk_bf16 does               */
+    const float *norm_w;         /* [D] f32 (device): RMSNorm of the new entries, or NULL       */
+    const float *idx_norm_w;     /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL  */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,

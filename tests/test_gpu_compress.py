@@ -3,8 +3,9 @@
 The HIP compressor merges in fp32 with expf while the oracle merges in double, so fp32
 entries are compared to 1e-5 relative; quantised outputs must hold the same codes except
 where the two fp32 values straddle a rounding boundary, and there the codes must be
-neighbours.  Chunked compression (with the one-block state before each chunk) must give
-bitwise the whole-sequence entries on the GPU."""
+neighbours.  The same holds with the RMSNorm of the merged entries.  Chunked compression
+(with the one-block state before each chunk) must give bitwise the whole-sequence entries on
+the GPU."""
 import numpy as np
 import pytest
 import torch
@@ -83,18 +84,57 @@ def test_hca_f32_records():
     rel_close(out.nope[0].cpu().numpy(), ref)
 
 
-def test_csa_bf16_stream_fp8_records_and_mxfp4_keys():
+def norm_weights(seed, D):
+    """RMSNorm weights in [0.5, 1.5), unequal within RoPE pairs."""
+    return (0.5 + np.random.default_rng(seed).random(D)).astype(np.float32)
+
+
+@pytest.mark.parametrize("G", [1, 128])
+def test_csa_f32_records_rmsnorm(G):
+    w = TINY
+    T, D, R = 2048, w.D, w.R
+    s = streams(w.seed + 7, T, D, G)
+    nw = norm_weights(60 + G, D)
+    announce(f"compress csa f32 rmsnorm G={G}")
+    out = v4.KV.empty(1, T // 4, D, R, fmt=v4.V4A_KV_F32)
+    v4.v4a_compress_csa(*dev_streams(s), tok0=0, m=4, first_entry=0, n_entries=T // 4, out_kv=out, norm_w=f32(nw))
+    torch.cuda.synchronize()
+    ref = oracle.compress_csa(s["kv_a"], s["kv_b"], s["gate_a"], s["gate_b"], s["bias_a"], s["bias_b"],
+                              tok0=0, m=4, first_entry=0, n_entries=T // 4, apply_rope=True, R=R, norm_w=nw)
+    rel_close(out.nope[0].cpu().numpy(), ref)
+
+
+def test_hca_f32_records_rmsnorm():
+    w = TINY
+    T, D, R = 4096, w.D, w.R
+    x, gt, bi = normal(w.seed, "kv_h", (T, D)), normal(w.seed, "gate_h", (T, 1)), normal(w.seed, "bias_h", (128, 1))
+    nw = norm_weights(62, D)
+    announce("compress hca f32 rmsnorm")
+    out = v4.KV.empty(1, T // 128, D, R, fmt=v4.V4A_KV_F32)
+    v4.v4a_compress_hca(f32(x), f32(gt), f32(bi), tok0=0, m=128, first_entry=0, n_entries=T // 128, out_kv=out,
+                        norm_w=f32(nw))
+    torch.cuda.synchronize()
+    ref = oracle.compress_hca(x, gt, bi, tok0=0, m=128, first_entry=0, n_entries=T // 128, apply_rope=True, R=R,
+                              norm_w=nw)
+    rel_close(out.nope[0].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("norm", [False, True], ids=["plain", "rmsnorm"])
+def test_csa_bf16_stream_fp8_records_and_mxfp4_keys(norm):
     T, D, R, dI = 8192, 512, 64, 128
     s = streams(510, T, D, bf16=True)
-    announce("compress csa bf16 -> fp8 records")
+    nw, nwi = (norm_weights(63, D), norm_weights(64, dI)) if norm else (None, None)
+    announce(f"compress csa bf16 -> fp8 records, norm={norm}")
     out = v4.KV.empty(1, T // 4, D, R)
-    v4.v4a_compress_csa(*dev_streams(s, bf16=True), tok0=0, m=4, first_entry=0, n_entries=T // 4, out_kv=out)
+    v4.v4a_compress_csa(*dev_streams(s, bf16=True), tok0=0, m=4, first_entry=0, n_entries=T // 4, out_kv=out,
+                        norm_w=f32(nw) if norm else None)
     si = streams(511, T, dI, bf16=True)
     keys = v4.Idx.empty(1, T // 4, dI)
-    v4.v4a_compress_csa(*dev_streams(si, bf16=True), tok0=0, m=4, first_entry=0, n_entries=T // 4, out_idx=keys)
+    v4.v4a_compress_csa(*dev_streams(si, bf16=True), tok0=0, m=4, first_entry=0, n_entries=T // 4, out_idx=keys,
+                        norm_w=f32(nwi) if norm else None)
     torch.cuda.synchronize()
     ref = oracle.compress_csa(s["kv_a"], s["kv_b"], s["gate_a"], s["gate_b"], s["bias_a"], s["bias_b"], tok0=0,
-                              m=4, first_entry=0, n_entries=T // 4, apply_rope=True, R=R)
+                              m=4, first_entry=0, n_entries=T // 4, apply_rope=True, R=R, norm_w=nw)
     nope, rope, scale = oracle.quant_kv(ref, R)
     got_scale = out.scale[0].cpu().numpy()
     rel_close(got_scale, scale)
@@ -108,7 +148,7 @@ def test_csa_bf16_stream_fp8_records_and_mxfp4_keys():
     print(f"bf16 mismatches: {int((diff > 0).sum())} of {diff.size}", flush=True)
     assert (diff <= spacing + 1e-6).all() and (diff > 0).mean() < 2e-3
     refk = oracle.compress_csa(si["kv_a"], si["kv_b"], si["gate_a"], si["gate_b"], si["bias_a"], si["bias_b"],
-                               tok0=0, m=4, first_entry=0, n_entries=T // 4, apply_rope=False, R=0)
+                               tok0=0, m=4, first_entry=0, n_entries=T // 4, apply_rope=False, R=0, norm_w=nwi)
     kc, ks = oracle.quant_mxfp4(refk)
     gs = keys.scales[0].cpu().numpy()
     assert (gs != ks).mean() < 1e-3

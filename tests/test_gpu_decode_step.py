@@ -26,14 +26,18 @@ def clone_idx(ix):
     return v4.Idx(ix.fmt, ix.d, ix.codes.clone(), ix.scales.clone(), ix.cap)
 
 
-@pytest.mark.parametrize("score_bf16", [False, True], ids=["f32_scores", "bf16_scores"])
-def test_fused_step_equals_separate_calls(score_bf16):
+@pytest.mark.parametrize("score_bf16,norm", [(False, False), (True, False), (False, True)],
+                         ids=["f32_scores", "bf16_scores", "rmsnorm"])
+def test_fused_step_equals_separate_calls(score_bf16, norm):
     seed, m, D, R, H, HI, dI, k, W = 4242, 4, 512, 64, 128, 64, 128, 512, 128
     q_pos = [4003, 4001, 3, 8191]            # completes entry 1000 / none / entry 0 / entry 2047
     B, cap = len(q_pos), 2304
     n_ent = [(p + 1) // m for p in q_pos]
     entry = [(p + 1) // m - 1 if (p + 1) % m == 0 else -1 for p in q_pos]
-    announce(f"fused decode step: q_pos={q_pos} score_bf16={score_bf16}")
+    announce(f"fused decode step: q_pos={q_pos} score_bf16={score_bf16} norm={norm}")
+    gnw = np.random.default_rng(seed + 1)
+    nw = f32(0.5 + gnw.random(D)) if norm else None
+    nwi = f32(0.5 + gnw.random(dI)) if norm else None
     kv = v4.KV.empty(B, cap, D, R)
     v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
     keys = v4.Idx.empty(B, cap, dI)
@@ -61,7 +65,7 @@ def test_fused_step_equals_separate_calls(score_bf16):
                              idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
                              idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv1, keys=keys1,
                              q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
-                             softmax_scale=scale, out=out1, score_bf16=score_bf16)
+                             softmax_scale=scale, out=out1, score_bf16=score_bf16, norm_w=nw, idx_norm_w=nwi)
     ws1 = v4.workspace(v4.v4a_decode_step_workspace(args))
     # timed: the call's kernels in launch order, each with a positive duration
     v4.v4a_trace_begin(16)
@@ -79,10 +83,11 @@ def test_fused_step_equals_separate_calls(score_bf16):
         if i < 0:
             continue
         v4.v4a_compress_csa(dev["kv_a"][b], dev["kv_b"][b], gates["gate_a"][b], gates["gate_b"][b], bias["bias_a"],
-                            bias["bias_b"], tok0=m * (i - 1), m=m, first_entry=i, n_entries=1, out_kv=kv2, b=b)
+                            bias["bias_b"], tok0=m * (i - 1), m=m, first_entry=i, n_entries=1, out_kv=kv2, b=b,
+                            norm_w=nw)
         v4.v4a_compress_csa(dev["idx_a"][b], dev["idx_b"][b], gates["idx_gate_a"][b], gates["idx_gate_b"][b],
                             bias["idx_bias_a"], bias["idx_bias_b"], tok0=m * (i - 1), m=m, first_entry=i,
-                            n_entries=1, out_idx=keys2, b=b)
+                            n_entries=1, out_idx=keys2, b=b, norm_w=nwi)
     sel = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
     ws2 = v4.workspace(max(v4.v4a_indexer_topk_workspace(B, 1, max(n_ent), k),
                            v4.v4a_decode_workspace(B, H, D, k, W)))

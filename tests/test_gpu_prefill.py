@@ -163,7 +163,7 @@ def test_tiny_fp32_two_chunks():
 
 # ----------------------------------------------------- BF16 / FP8 / MXFP4 chunks ----
 
-def run_csa_chunk(w, slot=1, n_slots=2, score_bf16=False):
+def run_csa_chunk(w, slot=1, n_slots=2, score_bf16=False, norm=False):
     """Cache the drawn entries in `slot`, run one CSA prefill chunk; returns everything a check needs."""
     x = prefill_inputs(w, kind="csa")
     C, tok0, n_prev, N0 = x["C"], x["tok0"], x["n_prev"], x["N0"]
@@ -181,18 +181,22 @@ def run_csa_chunk(w, slot=1, n_slots=2, score_bf16=False):
     for name in ("kv_a", "kv_b", "idx_a", "idx_b"):
         dev[name], val[name] = bf16_dev(x[name])
     q_dev, _ = bf16_dev(x["q"])
+    gnw = np.random.default_rng(70)
+    nw = f32(0.5 + gnw.random(D)) if norm else None
+    nwi = f32(0.5 + gnw.random(dI)) if norm else None
     out = torch.empty((C, H, D), dtype=torch.bfloat16, device="cuda")
     a = v4.PrefillArgs(tok0=tok0, n_prev=n_prev, m=4, kv_a=dev["kv_a"], kv_b=dev["kv_b"], gate_a=f32(x["gate_a"]),
                        gate_b=f32(x["gate_b"]), bias_a=f32(x["bias_a"]), bias_b=f32(x["bias_b"]), kv=kv, slot=slot,
                        idx_a=dev["idx_a"], idx_b=dev["idx_b"], idx_gate_a=f32(x["idx_gate_a"]),
                        idx_gate_b=f32(x["idx_gate_b"]), idx_bias_a=f32(x["idx_bias_a"]),
                        idx_bias_b=f32(x["idx_bias_b"]), keys=keys, q_idx=qi, w=f32(x["w"]), k=k, q=q_dev, W=W,
-                       sink=f32(x["sink"]), softmax_scale=w.scale, out=out, score_bf16=score_bf16)
+                       sink=f32(x["sink"]), softmax_scale=w.scale, out=out, score_bf16=score_bf16, norm_w=nw,
+                       idx_norm_w=nwi)
     ws = v4.workspace(v4.v4a_prefill_workspace(CSA, a))
     v4.v4a_prefill_chunk(CSA, a, ws)
     torch.cuda.synchronize()
     return dict(x=x, a=a, ws=ws, kv=kv, keys=keys, qi=qi, dev=dev, val=val, q_dev=q_dev, out=out, n_total=n_total,
-                cap=cap, slot=slot, score_bf16=score_bf16)
+                cap=cap, slot=slot, score_bf16=score_bf16, norm_w=nw, idx_norm_w=nwi)
 
 
 def check_csa_chunk(w, r, queries, decode_queries=()):
@@ -205,10 +209,11 @@ def check_csa_chunk(w, r, queries, decode_queries=()):
     ref_keys = v4.Idx.empty(1, r["cap"], dI)
     n_new = n_total - N0
     v4.v4a_compress_csa(r["dev"]["kv_a"], r["dev"]["kv_b"], f32(x["gate_a"]), f32(x["gate_b"]), f32(x["bias_a"]),
-                        f32(x["bias_b"]), tok0=tok0 - n_prev, m=4, first_entry=N0, n_entries=n_new, out_kv=ref_kv)
+                        f32(x["bias_b"]), tok0=tok0 - n_prev, m=4, first_entry=N0, n_entries=n_new, out_kv=ref_kv,
+                        norm_w=r["norm_w"])
     v4.v4a_compress_csa(r["dev"]["idx_a"], r["dev"]["idx_b"], f32(x["idx_gate_a"]), f32(x["idx_gate_b"]),
                         f32(x["idx_bias_a"]), f32(x["idx_bias_b"]), tok0=tok0 - n_prev, m=4, first_entry=N0,
-                        n_entries=n_new, out_idx=ref_keys)
+                        n_entries=n_new, out_idx=ref_keys, norm_w=r["idx_norm_w"])
     torch.cuda.synchronize()
     for got, ref in ((kv1.nope, ref_kv.nope), (kv1.rope, ref_kv.rope), (kv1.scale, ref_kv.scale),
                      (keys1.codes, ref_keys.codes), (keys1.scales, ref_keys.scales)):
@@ -253,6 +258,15 @@ def test_csa_mxfp4_chunk():
     w = scaled(PREFILL_64K, T=8192, chunk=700)
     r = run_csa_chunk(w)
     check_csa_chunk(w, r, sample_queries(700), decode_queries=(0, 349, 699))
+
+
+def test_csa_mxfp4_chunk_rmsnorm():
+    """The chunk with RMS-normalised new entries and keys: appended entries bitwise equal to one
+    compressor call with the same weights, selections and outputs against the oracle fed the
+    caches the GPU wrote."""
+    w = scaled(PREFILL_64K, T=8192, chunk=700)
+    r = run_csa_chunk(w, norm=True)
+    check_csa_chunk(w, r, sample_queries(700), decode_queries=(349,))
 
 
 def test_csa_mxfp4_chunk_bf16_scores():
