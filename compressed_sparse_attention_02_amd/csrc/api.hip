@@ -878,10 +878,12 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
         c.theta = a->rope_theta; c.b0 = 0; c.n_seq = a->B;
     };
     fill(pl.rec, a->kv_a, a->kv_b, a->gate_a, a->gate_b, a->bias_a, a->bias_b, D, a->G);
+    pl.rec.ring = a->ring != 0;
     pl.rec.rope = a->apply_rope != 0;
     pl.rec.kv = a->kv;
     if ((st = compress_check(pl.rec, a->norm_w)) != V4A_OK) return st;
     fill(pl.key, a->idx_a, a->idx_b, a->idx_gate_a, a->idx_gate_b, a->idx_bias_a, a->idx_bias_b, d, a->idx_G);
+    pl.key.ring = a->ring != 0;
     pl.key.idx = a->keys;
     if ((st = compress_check(pl.key, a->idx_norm_w)) != V4A_OK) return st;
     for (int b = 0; b < a->B; b++) {
@@ -921,6 +923,12 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &attn_need,
                              "v4a_decode_step_csa")) != V4A_OK)
         return st;
+    if (a->ring) {
+        for (int b = 0; b < a->B; b++)
+            if (pl.sq.win_len[b] > a->q_pos[b] + 1)
+                return fail(V4A_EINVAL, "v4a_decode_step_csa: win_len[%d] exceeds the tokens so far", b);
+        pl.sq.ring = 1;
+    }
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs the MFMA attention shapes");
     pl.sel_bytes = round_up((size_t)a->B * a->k * 4, 256);
     pl.topk_bytes = topk_layout(a->B, 1, pl.n_max, a->k).total;

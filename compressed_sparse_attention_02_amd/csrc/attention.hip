@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
     const int b = p / P.S, split = p % P.S;
     if (b >= P.B) return;
     const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
-    const int64_t wrow0 = sq_win_row0(Sq, b, P.W);
+    const WinRows wr = sq_win_rows(Sq, b, P.W);
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
     if (split >= splits) return;
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                 for (int j = 0; j < 4; j++) {
                     const int wtok = tb + 4 * kg + j - n_ent;
                     valid[j] = tb + 4 * kg + j < kb1;
-                    row[j] = wrow0 + (valid[j] ? wtok : 0);
+                    row[j] = wr.row(valid[j] ? wtok : 0);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo
                     } else if (kidx < kb1) {
                         valid[j] = true;
                         scl = 1.0f;
-                        v[j] = *(const uint4 *)((const uint16_t *)P.win + (wrow0 + (kidx - n_ent)) * D + dim);
+                        v[j] = *(const uint4 *)((const uint16_t *)P.win + wr.row(kidx - n_ent) * D + dim);
                     }
                     if (seg == 0) {
                         ksc[4 * kg + j] = scl;
@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
 // scores in LDS, fp32 arithmetic throughout (no split).
 constexpr int kF32MaxKeys = 8192 + 2048;
 
-__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_t wrow0, int64_t e, int wtok,
+__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, const WinRows &wr, int64_t e, int wtok,
                                               int d) {
     const int Dn = P.D - P.R;
     if (e >= 0) {
@@ -490,7 +490,7 @@ __device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, int64_
         }
         return bf16_to_f32(P.rope[row * P.R + (d - Dn)]);
     }
-    const int64_t wi = (wrow0 + wtok) * P.D + d;
+    const int64_t wi = wr.row(wtok) * P.D + d;
     return P.win_bf16 ? bf16_to_f32(((const uint16_t *)P.win)[wi]) : ((const float *)P.win)[wi];
 }
 
@@ -501,7 +501,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
     __shared__ float osh[512];
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
-    const int64_t wrow0 = sq_win_row0(Sq, b, P.W);
+    const WinRows wr = sq_win_rows(Sq, b, P.W);
     const int D = P.D;
     for (int d = t; d < D; d += 256) {
         const int64_t qi = ((int64_t)b * P.H + h) * D + d;
@@ -522,7 +522,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
         float s = -INFINITY;
         if (e >= 0 || wtok >= 0) {
             float acc = 0.0f;
-            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, wrow0, e, wtok, d), acc);
+            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, wr, e, wtok, d), acc);
             s = scale * acc;
         }
         sc[j] = s;
@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
                 wtok = j - n_ent;
             }
             if (e < 0 && wtok < 0) continue;
-            acc = fmaf(sc[j], load_key_dim(P, b, wrow0, e, wtok, d), acc);
+            acc = fmaf(sc[j], load_key_dim(P, b, wr, e, wtok, d), acc);
         }
         osh[d] = den > 0.0f ? acc / den : 0.0f;
     }

@@ -192,6 +192,7 @@ __host__ __device__ __forceinline__ int64_t visible_keys(const QueryPos &P, int 
 // fixed_ent is 0, over its visible prefix of the n_total cached entries (ratio m).
 struct SeqInfo {
     int mode;
+    int ring;                  // mode 0: the window buffer is a ring (position p at row p mod W)
     int64_t tok0;
     int n_prev, W, m, fixed_ent;
     int64_t n_total;
@@ -219,6 +220,33 @@ __host__ __device__ __forceinline__ int64_t sq_win_row0(const SeqInfo &S, int b,
     return S.mode ? (int64_t)b + S.n_prev - sq_win_len(S, b) + 1 : (int64_t)b * W;
 }
 
+// Rows of query b's window tokens, token j = 0 the oldest: consecutive rows from the oldest's,
+// or, for a ring (mode 0), the sequence's W rows with position p at row p mod W.
+struct WinRows {
+    int64_t base;
+    int start, W;
+    bool ring;
+    __host__ __device__ __forceinline__ int64_t row(int j) const {
+        if (!ring) return base + j;
+        const int r = start + j;
+        return base + (r >= W ? r - W : r);
+    }
+};
+__host__ __device__ __forceinline__ WinRows sq_win_rows(const SeqInfo &S, int b, int W) {
+    WinRows w;
+    w.W = W;
+    w.ring = S.ring && !S.mode;
+    w.start = 0;
+    if (w.ring) {
+        w.base = (int64_t)b * W;
+        const int64_t p0 = S.q_pos[b] - S.win_len[b] + 1;  // the oldest window position, >= 0
+        w.start = (int)(p0 % W);
+    } else {
+        w.base = sq_win_row0(S, b, W);
+    }
+    return w;
+}
+
 void set_error(const char *fmt, ...);
 void fill_rope_table(RopeTable &t, int R, double theta);
 
@@ -242,6 +270,7 @@ struct CompressArgs {
     const v4a_idx *idx;
     int b0, n_seq;           // output slots b0 .. b0+n_seq-1; stream s at x + s * n_tok * D
     const float *norm_w;     // [D] RMSNorm weights of the merged entry, or NULL
+    bool ring;               // rows are a ring: position p at row p mod n_tok (else p - tok0)
 };
 constexpr float kNormEps = 1e-6f;  // RMSNorm epsilon of the compressed entries
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s);

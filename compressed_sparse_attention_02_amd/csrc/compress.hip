@@ -84,6 +84,7 @@ CompressParams compress_params(const CompressArgs &a) {
     P.out_row0 = (int64_t)a.b0 * P.cap;
     P.n_tok = a.n_tok;
     P.norm_w = a.norm_w;
+    P.ring = a.ring;
     return P;
 }
 

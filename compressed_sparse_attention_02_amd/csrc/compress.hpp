@@ -25,6 +25,7 @@ struct CompressParams {
     int64_t cap;
     int64_t n_tok;
     const float *norm_w;  // [D] or NULL
+    bool ring;            // stream rows are a ring: position p at row p mod n_tok
 };
 
 template <int VPT>
@@ -57,8 +58,10 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
     const int m = P.m, D = P.D;
     const int d0 = lane * VPT;
     const bool active = d0 < D;
-    // candidate c: stream s = c / m (0: own block i, 1: B-block i-1), position j = c % m
+    // candidate c: stream s = c / m (0: own block i, 1: B-block i-1), position j = c % m; the
+    // stream row of token position p is p - tok0, or p mod n_tok for a ring
     const int n_cand = (P.n_streams == 2 && i >= 1) ? 2 * m : m;
+    auto row_of = [&](int64_t pos) -> int64_t { return P.ring ? pos % P.n_tok : pos - tok0; };
 
     float acc[VPT];
 #pragma unroll
@@ -80,7 +83,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
             for (int u = 0; u < kRowBatch; u++) {
                 const int c = min(c0 + u, n_cand - 1);
                 const int s = c / m, j = c % m;
-                const int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+                const int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
                 load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, xb[u], x_off);
             }
         };
@@ -89,7 +92,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
         float zmax = -INFINITY;
         for (int c = lane; c < n_cand; c += 64) {
             int s = c / m, j = c % m;
-            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+            int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
             float z = (s == 0 ? P.g0 : P.g1)[g_off + r] + (s == 0 ? P.b0 : P.b1)[j];
             wsh[c] = z;
             zmax = fmaxf(zmax, z);
@@ -130,7 +133,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
         for (int v = 0; v < VPT; v++) { mx[v] = -INFINITY; l[v] = 0.0f; }
         for (int c = 0; c < n_cand; c++) {
             int s = c / m, j = c % m;
-            int64_t r = (s == 0 ? m * i : m * (i - 1)) + j - tok0;
+            int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
             float x[VPT];
             load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
             const float *g = (s == 0 ? P.g0 : P.g1) + g_off + r * D + d0;

@@ -323,6 +323,10 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * Stream rows: every stream holds [B][2m] rows per sequence, the B-block before the completed
  * block and the completed block itself (positions t+1-2m .. t; for the first block only the
  * last m rows are read).  Sequences whose newest token completes no block read no rows.
+ * With ring != 0 the per-token state is kept in rings the caller writes each token into
+ * ([cyqw] section 3.5: the state cache holds the window and the incomplete block): each
+ * stream's [B][2m] rows hold position p at row p mod 2m, and win [B][W][D] holds position p
+ * at row p mod W; the window tokens are positions t-win_len[b]+1 .. t (win_len[b] <= t+1).
  * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
  * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
 typedef struct {
@@ -357,6 +361,7 @@ typedef struct {
     int32_t score_bf16;          /* nonzero: select as v4a_indexer_topk_bf16 does               */
     const float *norm_w;         /* [D] f32 (device): RMSNorm of the new entries, or NULL       */
     const float *idx_norm_w;     /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL  */
+    int32_t ring;                /* nonzero: the streams and the window are rings (see above)    */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,

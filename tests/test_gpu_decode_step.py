@@ -116,3 +116,72 @@ def test_fused_step_equals_separate_calls(score_bf16, norm):
                                      score_bf16=score_bf16)
     assert np.array_equal(sel[b, 0].cpu().numpy(), ref_sel)
     check_close(out_f64(out1[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what="fused step vs oracle")
+
+
+def test_fused_step_ring_state_equals_plain_rows():
+    """The same step with the per-token state in rings (stream rows at position mod 2m, window
+    at position mod W) gives bitwise the output and caches of the plain row layout."""
+    seed, m, D, R, H, HI, dI, k, W = 4343, 4, 512, 64, 128, 64, 128, 512, 128
+    q_pos = [4003, 4001, 3, 8191, 130]      # entry 1000 / none / entry 0 / entry 2047 / none
+    B, cap = len(q_pos), 2304
+    n_ent = [(p + 1) // m for p in q_pos]
+    win_len = [min(W, p + 1) for p in q_pos]
+    win_len[4] = 77                           # a shorter window than the tokens so far
+    announce(f"fused decode step, ring state: q_pos={q_pos}")
+    kv = v4.KV.empty(B, cap, D, R)
+    v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
+    keys = v4.Idx.empty(B, cap, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "keys", (B * cap, dI))), keys, 0)
+    qi = v4.Idx.empty(B, HI, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "q_idx", (B * HI, dI))), qi)
+    w = f32(normal(seed, "w", (B, HI)))
+    q = bf16_from_bits(to_bf16_bits(normal(seed, "q", (B, H, D))))
+    sink = f32(normal(seed, "sink", (H,)))
+    bias = {n: f32(normal(seed, n, (m, 1))) for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
+    # token rows by position: row p of each stream, for the positions any step reads
+    T = max(q_pos) + 1
+    tok = {n: normal(seed, n, (B, T, D if n in ("kv_a", "kv_b") else dI)) for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
+    gt = {n: normal(seed, n, (B, T, 1)) for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
+    plain, ring = {}, {}
+    for n, src in list(tok.items()) + list(gt.items()):
+        width = src.shape[-1]
+        pl_rows = np.zeros((B, 2 * m, width), np.float32)
+        rg_rows = np.zeros((B, 2 * m, width), np.float32)
+        for b, t in enumerate(q_pos):
+            for r in range(2 * m):
+                p = t + 1 - 2 * m + r
+                if p >= 0:
+                    pl_rows[b, r] = src[b, p]
+                    rg_rows[b, p % (2 * m)] = src[b, p]
+        conv = bf16_from_bits if n in tok else f32
+        plain[n] = conv(to_bf16_bits(pl_rows)) if n in tok else f32(pl_rows)
+        ring[n] = conv(to_bf16_bits(rg_rows)) if n in tok else f32(rg_rows)
+    win_plain = np.zeros((B, W, D), np.float32)
+    win_ring = np.zeros((B, W, D), np.float32)
+    for b, t in enumerate(q_pos):
+        for j in range(win_len[b]):
+            p = t - win_len[b] + 1 + j
+            win_plain[b, j] = tok["kv_a"][b, p]
+            win_ring[b, p % W] = tok["kv_a"][b, p]
+    scale = 1.0 / math.sqrt(D)
+    results = []
+    for rows, win, is_ring in ((plain, win_plain, False), (ring, win_ring, True)):
+        kv1, keys1 = clone_kv(kv), clone_idx(keys)
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+        args = v4.DecodeStepArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=rows["kv_a"], kv_b=rows["kv_b"],
+                                 gate_a=rows["gate_a"], gate_b=rows["gate_b"], bias_a=bias["bias_a"],
+                                 bias_b=bias["bias_b"], idx_a=rows["idx_a"], idx_b=rows["idx_b"],
+                                 idx_gate_a=rows["idx_gate_a"], idx_gate_b=rows["idx_gate_b"],
+                                 idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv1, keys=keys1,
+                                 q_idx=qi, w=w, k=k, q=q, win=bf16_from_bits(to_bf16_bits(win)), win_len=win_len,
+                                 W=W, sink=sink, softmax_scale=scale, out=out, ring=is_ring)
+        ws = v4.workspace(v4.v4a_decode_step_workspace(args))
+        v4.v4a_decode_step_csa(args, ws)
+        torch.cuda.synchronize()
+        results.append((out, kv1, keys1))
+    (o1, k1, i1), (o2, k2, i2) = results
+    for a, c in ((k1.nope, k2.nope), (k1.rope, k2.rope), (k1.scale, k2.scale), (i1.codes, i2.codes),
+                 (i1.scales, i2.scales)):
+        assert torch.equal(a, c)
+    assert not torch.equal(k1.nope, kv.nope)
+    assert torch.equal(o1, o2)
