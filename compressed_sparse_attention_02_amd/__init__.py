@@ -74,6 +74,19 @@ class c_decode_step_args(ctypes.Structure):
                 ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32), ("norm_w", P),
                 ("idx_norm_w", P), ("ring", ctypes.c_int32)]
 
+
+
+class c_decode_step_hca_args(ctypes.Structure):
+    P = ctypes.c_void_p
+    _fields_ = [("B", ctypes.c_int32), ("m", ctypes.c_int32), ("q_pos", P), ("n_entries", P),
+                ("in_t", ctypes.c_int), ("G", ctypes.c_int32), ("kv_a", P), ("gate_a", P), ("bias_a", P),
+                ("apply_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("norm_w", P),
+                ("kv", ctypes.POINTER(c_kv)), ("q", P), ("q_t", ctypes.c_int), ("H", ctypes.c_int32),
+                ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32), ("sink", P),
+                ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32), ("out", P),
+                ("out_t", ctypes.c_int), ("ring", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -111,6 +124,11 @@ def lib() -> ctypes.CDLL:
         L.v4a_decode_step_csa.restype = ctypes.c_int
         L.v4a_decode_step_workspace.argtypes = [DSP]
         L.v4a_decode_step_workspace.restype = SZ
+        DHP = ctypes.POINTER(c_decode_step_hca_args)
+        L.v4a_decode_step_hca.argtypes = [DHP, P, SZ, P]
+        L.v4a_decode_step_hca.restype = ctypes.c_int
+        L.v4a_decode_step_hca_workspace.argtypes = [DHP]
+        L.v4a_decode_step_hca_workspace.restype = SZ
         PAP = ctypes.POINTER(c_prefill_args)
         L.v4a_prefill_chunk.argtypes = [ctypes.c_int, PAP, P, SZ, P]
         L.v4a_prefill_chunk.restype = ctypes.c_int
@@ -412,3 +430,32 @@ def v4a_decode_step_csa(args: DecodeStepArgs, ws: torch.Tensor, stream=None):
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A caller-owned workspace buffer (torch allocations are 256-byte aligned)."""
     return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+
+
+class DecodeStepHcaArgs:
+    """The arguments of one fused HCA decode step (v4a_decode_step_hca_args), holding every tensor
+    and host array it points to.  The stream holds [B][m] rows per sequence."""
+
+    def __init__(self, *, q_pos, n_entries, m: int, kv_a, gate_a, bias_a, kv: KV, q, win, win_len, W: int, sink,
+                 softmax_scale: float, out, apply_rope: bool = True, rope_theta: float = 10000.0,
+                 out_rope_inverse: bool = True, norm_w=None, ring: bool = False):
+        B, H = q.shape[0], q.shape[1]
+        self._kv = kv.c()
+        self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
+        self._refs = (kv_a, gate_a, bias_a, kv, q, win, sink, out, norm_w)
+        self.s = c_decode_step_hca_args(
+            B=B, m=m, q_pos=ctypes.cast(self._pos, ctypes.c_void_p), n_entries=ctypes.cast(self._nent, ctypes.c_void_p),
+            in_t=_ftype(kv_a), G=gate_a.shape[-1], kv_a=_ptr(kv_a), gate_a=_ptr(gate_a), bias_a=_ptr(bias_a),
+            apply_rope=int(apply_rope), rope_theta=rope_theta, norm_w=_ptr(norm_w), kv=ctypes.pointer(self._kv),
+            q=_ptr(q), q_t=_ftype(q), H=H, win=_ptr(win), win_t=_ftype(win),
+            win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink), softmax_scale=softmax_scale,
+            out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out), ring=int(ring))
+
+
+def v4a_decode_step_hca_workspace(args: DecodeStepHcaArgs) -> int:
+    return int(lib().v4a_decode_step_hca_workspace(ctypes.byref(args.s)))
+
+
+def v4a_decode_step_hca(args: DecodeStepHcaArgs, ws: torch.Tensor | None, stream=None):
+    _check(lib().v4a_decode_step_hca(ctypes.byref(args.s), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)))

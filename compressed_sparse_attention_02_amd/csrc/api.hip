@@ -961,7 +961,7 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     char *tws = base + pl.sel_bytes;
     const TopkWs L = topk_layout(a->B, 1, pl.n_max, a->k);
     const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
-    hipError_t e = launch_decode_prologue(pl.key, a->B, pl.entry, tws + L.hist, hist_bytes, s);
+    hipError_t e = launch_decode_prologue(pl.key, 1, a->B, pl.entry, tws + L.hist, hist_bytes, s);
     if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
     st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false,
                              a->score_bf16 != 0, &pl.rec);
@@ -1010,6 +1010,106 @@ v4a_status v4a_trace_kernel(int32_t i, const char **kernel, float *ms) {
         if (e != hipSuccess) return hip_status(e, "v4a_trace_kernel");
     }
     return V4A_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ fused HCA decode step --------
+namespace v4a {
+
+struct StepHcaPlan {
+    CompressArgs rec;
+    int64_t entry[kMaxSeq];
+    AttnArgs at;
+    SeqInfo sq;
+    size_t attn_bytes;
+};
+
+static v4a_status step_hca_plan(const v4a_decode_step_hca_args *a, StepHcaPlan &pl) {
+    const char *name = "v4a_decode_step_hca";
+    if (!a) return fail(V4A_EINVAL, "%s: args is NULL", name);
+    pl = StepHcaPlan{};
+    if (a->B < 1 || a->B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "%s: B=%d not in [1, %d]", name, a->B, kMaxSeq);
+    if (!a->q_pos || !a->n_entries) return fail(V4A_EINVAL, "%s: q_pos and n_entries are required", name);
+    v4a_status st;
+    if ((st = check_kv(a->kv, "kv")) != V4A_OK) return st;
+    if (a->in_t != V4A_F32 && a->in_t != V4A_BF16) return fail(V4A_EINVAL, "%s: in_t", name);
+    const int D = a->kv->D, m = a->m;
+    // compressor arguments, checked as one entry at rows [0, m) (entries and row origins are set
+    // per sequence at launch)
+    CompressArgs &c = pl.rec;
+    c.x[0] = a->kv_a; c.gate[0] = a->gate_a; c.bias[0] = a->bias_a;
+    c.n_streams = 1; c.bf16_in = a->in_t == V4A_BF16; c.D = D; c.G = a->G; c.m = m;
+    c.tok0 = 0; c.n_tok = m; c.first_entry = 0; c.n_entries = 1;
+    c.rope = a->apply_rope != 0; c.theta = a->rope_theta; c.kv = a->kv; c.b0 = 0; c.n_seq = a->B;
+    c.ring = a->ring != 0;
+    if ((st = compress_check(c, a->norm_w)) != V4A_OK) return st;
+    memset(&pl.sq, 0, sizeof pl.sq);
+    for (int b = 0; b < a->B; b++) {
+        const int64_t t = a->q_pos[b];
+        if (t < 0) return fail(V4A_EINVAL, "%s: q_pos[%d] < 0", name, b);
+        if (a->n_entries[b] < 0 || a->n_entries[b] > a->kv->cap)
+            return fail(V4A_EINVAL, "%s: n_entries[%d] not in [0, cap]", name, b);
+        const int64_t i = (t + 1) % m == 0 ? (t + 1) / m - 1 : -1;
+        if (i >= a->n_entries[b])
+            return fail(V4A_EINVAL, "%s: n_entries[%d] does not include the entry this step completes", name, b);
+        pl.entry[b] = i;
+        int64_t vis = (t + 1) / m;
+        if (vis > a->n_entries[b]) vis = a->n_entries[b];
+        if (vis > (1 << 30)) return fail(V4A_EUNSUPPORTED, "%s: too many entries", name);
+        pl.sq.n_ent[b] = (int32_t)vis;
+    }
+    AttnArgs &at = pl.at;
+    at.q = a->q;
+    at.B = a->B;
+    at.H = a->H;
+    at.kv = a->kv;
+    at.kv_bstride = a->kv->cap;
+    at.win = a->win;
+    at.W = a->W;
+    at.sink = a->sink;
+    at.scale = a->softmax_scale;
+    at.rope_inv = a->out_rope_inverse != 0;
+    at.theta = a->rope_theta;
+    at.out = a->out;
+    size_t need = 0;
+    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &need, name)) != V4A_OK)
+        return st;
+    if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "%s: needs the MFMA attention shapes", name);
+    if (a->ring) {
+        for (int b = 0; b < a->B; b++)
+            if (pl.sq.win_len[b] > a->q_pos[b] + 1)
+                return fail(V4A_EINVAL, "%s: win_len[%d] exceeds the tokens so far", name, b);
+        pl.sq.ring = 1;
+    }
+    pl.attn_bytes = round_up(need, 256);
+    return V4A_OK;
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+size_t v4a_decode_step_hca_workspace(const v4a_decode_step_hca_args *args) {
+    v4a::StepHcaPlan pl;
+    if (v4a::step_hca_plan(args, pl) != V4A_OK) return 0;
+    return pl.attn_bytes;
+}
+
+v4a_status v4a_decode_step_hca(const v4a_decode_step_hca_args *a, void *ws, size_t ws_bytes, void *stream) {
+    using namespace v4a;
+    StepHcaPlan pl;
+    v4a_status st = step_hca_plan(a, pl);
+    if (st != V4A_OK) return st;
+    if (pl.attn_bytes > 0 && (!ws || ws_bytes < pl.attn_bytes || !aligned(ws, 256)))
+        return fail(V4A_EWORKSPACE, "v4a_decode_step_hca: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    pl.attn_bytes, ws_bytes);
+    g_err.clear();
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode_prologue(pl.rec, 0, a->B, pl.entry, nullptr, 0, s);
+    if (e != hipSuccess) return hip_status(e, "v4a_decode_step_hca: compress");
+    pl.at.partial = pl.attn_bytes > 0 ? (float *)ws : nullptr;
+    return hip_status(launch_attention(pl.at, pl.sq, s), "v4a_decode_step_hca: attention");
 }
 
 }  // extern "C"

@@ -274,11 +274,11 @@ struct CompressArgs {
 };
 constexpr float kNormEps = 1e-6f;  // RMSNorm epsilon of the compressed entries
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s);
-// One launch: the indexer keys (key) of entry[b] for every sequence b with entry[b] >= 0 (each
-// sequence's streams hold the 2m rows from the block before the entry's own), plus clearing
-// zero_bytes at zero.
-hipError_t launch_decode_prologue(const CompressArgs &key, int B, const int64_t *entry, void *zero,
-                                  size_t zero_bytes, hipStream_t s);
+// One launch: the entries (key: records or indexer keys) of entry[b] for every sequence b with
+// entry[b] >= 0 (each sequence's streams hold rows from blocks_before blocks before the entry's
+// own, or a ring), plus clearing zero_bytes at zero.
+hipError_t launch_decode_prologue(const CompressArgs &key, int blocks_before, int B, const int64_t *entry,
+                                  void *zero, size_t zero_bytes, hipStream_t s);
 
 struct IndexerArgs {
     const v4a_idx *keys;

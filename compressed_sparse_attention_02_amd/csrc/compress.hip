@@ -31,12 +31,14 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
     compress_entry<VPT>(P, wsh[wv], blockIdx.y, P.first_entry + e, P.tok0);
 }
 
-// Decode-step prologue, one launch: row y < B compresses the indexer key of sequence y (where
-// the sequence's newest token completes a block: entry[seq] >= 0, the sequence's 2m stream
-// rows starting at the block before it), and row B clears the selection's histogram region.
-// The entry records are compressed in a later launch (they are read only by attention).
+// Decode-step prologue, one launch: row y < B compresses one entry of sequence y (where the
+// sequence's newest token completes a block: entry[seq] >= 0; the sequence's stream rows start
+// blocks_before blocks before the entry's own block), and row B clears zero_n16 16-byte words.
+// The CSA step compresses the indexer keys here (its entry records follow in the final
+// selection's launch, since only attention reads them); the HCA step its entry records.
 struct PrologueParams {
     CompressParams key;
+    int blocks_before;
     int B;
     int64_t entry[kMaxSeq];
     uint4 *zero;
@@ -55,7 +57,7 @@ __global__ void __launch_bounds__(256) decode_prologue_kernel(PrologueParams P) 
     if (blockIdx.x != 0 || threadIdx.x >= 64) return;  // one wavefront per entry
     const int64_t i = P.entry[y];
     if (i < 0) return;
-    compress_entry<VK>(P.key, wsh, y, i, (int64_t)P.key.m * (i - 1));
+    compress_entry<VK>(P.key, wsh, y, i, (int64_t)P.key.m * (i - P.blocks_before));
 }
 
 CompressParams compress_params(const CompressArgs &a) {
@@ -105,22 +107,24 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
 
 namespace v4a {
 
-hipError_t launch_decode_prologue(const CompressArgs &key, int B, const int64_t *entry, void *zero,
-                                  size_t zero_bytes, hipStream_t s) {
+hipError_t launch_decode_prologue(const CompressArgs &key, int blocks_before, int B, const int64_t *entry,
+                                  void *zero, size_t zero_bytes, hipStream_t s) {
     PrologueParams P;
     P.key = compress_params(key);
+    P.blocks_before = blocks_before;
     P.B = B;
     for (int b = 0; b < kMaxSeq; b++) P.entry[b] = b < B ? entry[b] : -1;
     P.zero = (uint4 *)zero;
     P.zero_n16 = zero_bytes / 16;
     const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 255) / 256, 1024);
     dim3 grid(zx > 0 ? zx : 1, (unsigned)(B + 1));
-    if (key.D == 128)
-        V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(256), 0, s, P);
-    else if (key.D == 32)
-        V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(256), 0, s, P);
-    else
-        return hipErrorInvalidValue;
+    switch (key.D) {
+        case 32: case 64: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(256), 0, s, P); break;
+        case 128: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(256), 0, s, P); break;
+        case 256: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<4>, grid, dim3(256), 0, s, P); break;
+        case 512: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<8>, grid, dim3(256), 0, s, P); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -369,6 +369,52 @@ V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *w
 /* Workspace of v4a_decode_step_csa for these arguments (0 if they are invalid). */
 V4A_API size_t v4a_decode_step_workspace(const v4a_decode_step_args *args);
 
+/* ------------------------------------------------- fused HCA decode step (one token) ----
+ * One decode step of B sequences of an HCA layer in one call, equal to v4a_compress_hca +
+ * v4a_decode_hca with the same arguments.  For every sequence b whose newest token t = q_pos[b]
+ * completes a block ((t+1) % m == 0), entry (t+1)/m - 1 is compressed into the record cache;
+ * then its min(n_entries[b], (t+1)/m) visible entries and the window tokens are attended over
+ * with the sink.  [cyqw] section 2.2 (HCA: every m' = 128 tokens become one entry, attended
+ * densely) and section 3.5 (the state cache), and the sections cited at the calls it composes.
+ * Stream rows: kv_a and gate_a hold [B][m] rows per sequence, the block ending at t (positions
+ * t+1-m .. t); sequences whose newest token completes no block read no rows.  With ring != 0,
+ * position p sits at row p mod m of its sequence's rows and at row p mod W of the window,
+ * whose tokens are positions t-win_len[b]+1 .. t (win_len[b] <= t+1).
+ * Supports the MFMA attention shapes (FP8/BF16 records with D in {128, 512}, H a multiple of 16
+ * up to 128), m <= 128, B <= 128. */
+typedef struct {
+    int32_t B, m;
+    const int64_t *q_pos;        /* host[B]: position of each sequence's newest token          */
+    const int64_t *n_entries;    /* host[B]: entries cached after this step (<= cap)           */
+    v4a_float in_t;              /* element type of the raw stream                             */
+    int32_t G;                   /* gate width (1 or D)                                        */
+    const void *kv_a;            /* [B][m][D] (device): the HCA stream                         */
+    const float *gate_a;         /* [B][m][G] f32 (device)                                     */
+    const float *bias_a;         /* [m][G] f32 (device)                                        */
+    int32_t apply_rope;
+    float rope_theta;
+    const float *norm_w;         /* [D] f32 (device): RMSNorm of the new entries, or NULL       */
+    const v4a_kv *kv;            /* record cache, slot b = sequence b                          */
+    const void *q;               /* [B][H][D] (device)                                         */
+    v4a_float q_t;
+    int32_t H;
+    const void *win;             /* [B][W][D] (device)                                         */
+    v4a_float win_t;
+    const int32_t *win_len;      /* host[B]                                                    */
+    int32_t W;
+    const float *sink;           /* [H] f32 (device)                                           */
+    float softmax_scale;
+    int32_t out_rope_inverse;
+    void *out;                   /* [B][H][D] (device)                                         */
+    v4a_float out_t;
+    int32_t ring;                /* nonzero: the stream rows and the window are rings          */
+} v4a_decode_step_hca_args;
+
+V4A_API v4a_status v4a_decode_step_hca(const v4a_decode_step_hca_args *args, void *ws, size_t ws_bytes,
+                               void *stream);
+/* Workspace of v4a_decode_step_hca for these arguments (0 if they are invalid or none is needed). */
+V4A_API size_t v4a_decode_step_hca_workspace(const v4a_decode_step_hca_args *args);
+
 /* ------------------------------------------------------------------- kernel timing ----
  * Instrumentation, off by default: each kernel the library launches can be timed on the GPU.
  * v4a_trace_begin arms a trace of at most `capacity` kernel launches (1 .. 2^18): until

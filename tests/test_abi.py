@@ -255,3 +255,55 @@ def test_trace_without_marks_is_an_error():
     assert v4.v4a_trace_end() == 0
     with pytest.raises(v4.V4AError):
         v4.v4a_trace_kernel(0)
+
+
+def test_decode_step_hca_args_layout_matches_the_header(tmp_path):
+    import subprocess
+    fields = [f for f, _ in v4.c_decode_step_hca_args._fields_]
+    src = tmp_path / "layout3.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "v4attn.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(v4a_decode_step_hca_args));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(v4a_decode_step_hca_args, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout3"
+    inc = str(v4.HEADER).rsplit("/", 1)[0]
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(v4.c_decode_step_hca_args)
+    assert got[1:] == [getattr(v4.c_decode_step_hca_args, f).offset for f in fields]
+
+
+def hca_step_struct(**kw):
+    """A valid fused HCA decode step at the 1M-context shape (fake device pointers)."""
+    rec = kv(cap=8192)
+    pos, nent, wl = i64(*[1048575] * 16), i64(*[8192] * 16), i32(*[128] * 16)
+    a = dict(B=16, m=128, q_pos=ctypes.cast(pos, ctypes.c_void_p), n_entries=ctypes.cast(nent, ctypes.c_void_p),
+             in_t=1, G=1, kv_a=FAKE, gate_a=FAKE, bias_a=FAKE, apply_rope=1, rope_theta=10000.0,
+             kv=ctypes.pointer(rec), q=FAKE, q_t=1, H=128, win=FAKE, win_t=1,
+             win_len=ctypes.cast(wl, ctypes.c_void_p), W=128, sink=FAKE, softmax_scale=0.044, out_rope_inverse=1,
+             out=FAKE, out_t=1)
+    a.update(kw)
+    s = v4.c_decode_step_hca_args(**a)
+    s._keep = (rec, pos, nent, wl, a)
+    return s
+
+
+def test_decode_step_hca_workspace_and_rejects():
+    L = v4.lib()
+    need = L.v4a_decode_step_hca_workspace(ctypes.byref(hca_step_struct()))
+    assert need == v4.v4a_decode_workspace(16, 128, 512, 8192, 128)
+    assert need % 256 == 0
+
+    def call(ws=FAKE, wsb=1 << 40, **kw):
+        return L.v4a_decode_step_hca(ctypes.byref(hca_step_struct(**kw)), ws, wsb, None)
+    assert L.v4a_decode_step_hca(None, FAKE, 1 << 40, None) == 1
+    assert call(B=0) == 2 and call(B=200) == 2
+    assert call(m=0) == 2 and call(m=129) == 2
+    assert call(H=24) == 2
+    assert call(kv_a=0) == 1
+    assert call(wsb=need - 1) == 3
+    short = i64(8191, *[8192] * 15)      # sequence 0 would not hold the entry it completes
+    assert call(n_entries=ctypes.cast(short, ctypes.c_void_p)) == 1
+    wl = i32(*[128] * 16)
+    early = i64(99, *[1048575] * 15)     # a ring window longer than the tokens so far
+    assert call(ring=1, win_len=ctypes.cast(wl, ctypes.c_void_p), q_pos=ctypes.cast(early, ctypes.c_void_p)) == 1

@@ -185,3 +185,75 @@ def test_fused_step_ring_state_equals_plain_rows():
         assert torch.equal(a, c)
     assert not torch.equal(k1.nope, kv.nope)
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("ring", [False, True], ids=["rows", "ring"])
+def test_fused_hca_step_equals_separate_calls(ring):
+    """v4a_decode_step_hca against v4a_compress_hca + v4a_decode_hca (bitwise), for sequences that
+    complete a 128-token block and one that does not; sequence 0 also against the oracle."""
+    seed, m, D, R, H, W = 4444, 128, 512, 64, 128, 128
+    q_pos = [128 * 40 - 1, 128 * 40 + 5, 127, 128 * 64 - 1]   # entry 39 / none / entry 0 / entry 63
+    B, cap = len(q_pos), 80
+    n_ent = [(p + 1) // m for p in q_pos]
+    entry = [(p + 1) // m - 1 if (p + 1) % m == 0 else -1 for p in q_pos]
+    win_len = [min(W, p + 1) for p in q_pos]
+    announce(f"fused hca decode step: q_pos={q_pos} ring={ring}")
+    kv = v4.KV.empty(B, cap, D, R)
+    v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
+    T = max(q_pos) + 1
+    tok = normal(seed, "kv_h", (B, T, D))
+    gt = normal(seed, "gate_h", (B, T, 1))
+    bias = f32(normal(seed, "bias_h", (m, 1)))
+    rows = np.zeros((B, m, D), np.float32)
+    grows = np.zeros((B, m, 1), np.float32)
+    win = np.zeros((B, W, D), np.float32)
+    for b, t in enumerate(q_pos):
+        for r in range(m):
+            p = t + 1 - m + r
+            if p >= 0:
+                rr = p % m if ring else r
+                rows[b, rr], grows[b, rr] = tok[b, p], gt[b, p]
+        for j in range(win_len[b]):
+            p = t - win_len[b] + 1 + j
+            win[b, p % W if ring else j] = tok[b, p]
+    rows_dev, win_dev = bf16_from_bits(to_bf16_bits(rows)), bf16_from_bits(to_bf16_bits(win))
+    q = bf16_from_bits(to_bf16_bits(normal(seed, "q", (B, H, D))))
+    sink = f32(normal(seed, "sink", (H,)))
+    scale = 1.0 / math.sqrt(D)
+
+    kv1 = clone_kv(kv)
+    out1 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    args = v4.DecodeStepHcaArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=rows_dev, gate_a=f32(grows), bias_a=bias,
+                                kv=kv1, q=q, win=win_dev, win_len=win_len, W=W, sink=sink, softmax_scale=scale,
+                                out=out1, ring=ring)
+    ws1 = v4.workspace(v4.v4a_decode_step_hca_workspace(args))
+    v4.v4a_decode_step_hca(args, ws1)
+
+    # the separate calls on the plain layout
+    kv2 = clone_kv(kv)
+    for b, i in enumerate(entry):
+        if i < 0:
+            continue
+        blk = bf16_from_bits(to_bf16_bits(tok[b, m * i:m * i + m]))
+        v4.v4a_compress_hca(blk, f32(gt[b, m * i:m * i + m]), bias, tok0=m * i, m=m, first_entry=i, n_entries=1,
+                            out_kv=kv2, b=b)
+    win_plain = np.zeros((B, W, D), np.float32)
+    for b, t in enumerate(q_pos):
+        win_plain[b, :win_len[b]] = tok[b, t - win_len[b] + 1:t + 1]
+    wp = bf16_from_bits(to_bf16_bits(win_plain))
+    out2 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    ws2 = v4.workspace(v4.v4a_decode_workspace(B, H, D, cap, W))
+    v4.v4a_decode_hca(q, kv2, n_ent, m, wp, win_len, W, sink, q_pos, softmax_scale=scale, out=out2, ws=ws2)
+    torch.cuda.synchronize()
+    for a, c in ((kv1.nope, kv2.nope), (kv1.rope, kv2.rope), (kv1.scale, kv2.scale)):
+        assert torch.equal(a, c)
+    assert not torch.equal(kv1.nope, kv.nope)
+    assert torch.equal(out1, out2)
+
+    b = 0
+    recs = oracle.dequant_kv(kv1.nope[b, :n_ent[b]].cpu().numpy(), kv1.rope[b, :n_ent[b]].cpu().numpy().view(np.uint16),
+                             kv1.scale[b, :n_ent[b]].cpu().numpy())
+    ref = oracle.decode_hca(bf16_bits_to_f64(q[b].view(torch.int16).cpu().numpy().view(np.uint16)), recs, n_ent[b],
+                            bf16_bits_to_f64(wp[b, :win_len[b]].view(torch.int16).cpu().numpy().view(np.uint16)),
+                            sink.cpu().numpy(), scale, q_pos=q_pos[b], m=m, R=R)
+    check_close(out_f64(out1[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what="fused hca step vs oracle")
