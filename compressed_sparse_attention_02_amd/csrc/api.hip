@@ -882,6 +882,8 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     pl.rec.rope = a->apply_rope != 0;
     pl.rec.kv = a->kv;
     if ((st = compress_check(pl.rec, a->norm_w)) != V4A_OK) return st;
+    if (a->G == 1 && m >= 64)  // the records are compressed one wavefront per entry here
+        return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: m=%d with one gate per token", m);
     fill(pl.key, a->idx_a, a->idx_b, a->idx_gate_a, a->idx_gate_b, a->idx_bias_a, a->idx_bias_b, d, a->idx_G);
     pl.key.ring = a->ring != 0;
     pl.key.idx = a->keys;

@@ -22,9 +22,18 @@
 
 namespace v4a {
 
+// Four entries per workgroup, one per wavefront; or, for the long gate-per-token blocks (HCA),
+// one entry per workgroup shared by its four wavefronts.
 template <int VPT>
 __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
-    __shared__ float wsh[4][kMaxCand];
+    __shared__ float wsh[kEntryWaves][kMaxCand];
+    __shared__ float red[kEntryWaves * 64 * VPT];
+    if (entry_uses_workgroup(P)) {
+        const int64_t e = blockIdx.x;
+        if (e >= P.n_entries) return;  // the whole workgroup leaves together
+        compress_entry_wg<VPT>(P, &wsh[0][0], red, blockIdx.y, P.first_entry + e, P.tok0);
+        return;
+    }
     const int wv = threadIdx.x >> 6;
     const int64_t e = (int64_t)blockIdx.x * 4 + wv;
     if (e >= P.n_entries) return;  // the whole wavefront leaves together
@@ -47,17 +56,24 @@ struct PrologueParams {
 
 template <int VK>
 __global__ void __launch_bounds__(256) decode_prologue_kernel(PrologueParams P) {
-    __shared__ float wsh[kMaxCand];
+    __shared__ float wsh[kEntryWaves * kMaxCand];
+    __shared__ float red[kEntryWaves * 64 * VK];
     const int y = blockIdx.y;
     if (y == P.B) {
         for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < P.zero_n16; i += (size_t)gridDim.x * blockDim.x)
             P.zero[i] = make_uint4(0, 0, 0, 0);
         return;
     }
-    if (blockIdx.x != 0 || threadIdx.x >= 64) return;  // one wavefront per entry
+    if (blockIdx.x != 0) return;
     const int64_t i = P.entry[y];
-    if (i < 0) return;
-    compress_entry<VK>(P.key, wsh, y, i, (int64_t)P.key.m * (i - P.blocks_before));
+    if (i < 0) return;  // the whole workgroup leaves together
+    const int64_t tok0 = (int64_t)P.key.m * (i - P.blocks_before);
+    if (entry_uses_workgroup(P.key)) {
+        compress_entry_wg<VK>(P.key, wsh, red, y, i, tok0);
+        return;
+    }
+    if (threadIdx.x >= 64) return;  // one wavefront per entry
+    compress_entry<VK>(P.key, wsh, y, i, tok0);
 }
 
 CompressParams compress_params(const CompressArgs &a) {
@@ -93,7 +109,8 @@ CompressParams compress_params(const CompressArgs &a) {
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     if (a.n_entries == 0 || a.n_seq == 0) return hipSuccess;
     const CompressParams P = compress_params(a);
-    dim3 grid((unsigned)((a.n_entries + 3) / 4), (unsigned)a.n_seq), block(256);
+    const int64_t per_wg = entry_uses_workgroup(P) ? 1 : 4;
+    dim3 grid((unsigned)((a.n_entries + per_wg - 1) / per_wg), (unsigned)a.n_seq), block(256);
     switch (a.D) {
         case 32: case 64: V4A_LAUNCH("compress_kernel", compress_kernel<1>, grid, block, 0, s, P); break;
         case 128: V4A_LAUNCH("compress_kernel", compress_kernel<2>, grid, block, 0, s, P); break;

@@ -47,112 +47,89 @@ __device__ __forceinline__ void load_row(const void *base, bool bf16, int64_t ro
     }
 }
 
-// Entry i of sequence seq, computed by one whole wavefront; row 0 of the sequence's streams
-// is position tok0 (its streams and gates start n_tok rows further per sequence); wsh is the
-// wavefront's scratch for the candidate weights.
+// Candidates of entry i: stream s = c / m (0: own block i, 1: B-block i-1), position j = c % m;
+// the stream row of token position p is p - tok0, or p mod n_tok for a ring.
+__device__ __forceinline__ int entry_candidates(const CompressParams &P, int64_t i) {
+    return (P.n_streams == 2 && i >= 1) ? 2 * P.m : P.m;
+}
+__device__ __forceinline__ int64_t candidate_row(const CompressParams &P, int64_t i, int c, int64_t tok0) {
+    const int m = P.m, s = c / m, j = c % m;
+    const int64_t pos = (s == 0 ? (int64_t)m * i : (int64_t)m * (i - 1)) + j;
+    return P.ring ? pos % P.n_tok : pos - tok0;
+}
+
+// Gate-per-token merge (G = 1) by one wavefront: the softmax weights of all candidates of entry i
+// go to wsh (exp(z - max), computed once per wavefront: lane c holds candidate c, c + 64, ...)
+// and their sum is returned; candidates [c_begin, c_end) are accumulated into acc in order.
+// Candidate rows are loaded in batches of kRowBatch, the first batch issued before the gate
+// logits so the two memory round trips overlap.
 template <int VPT>
-__device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
-                                               int64_t tok0) {
+__device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
+                                             int64_t tok0, int c_begin, int c_end, float (&acc)[VPT]) {
     const int lane = threadIdx.x & 63;
     const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
     const int m = P.m, D = P.D;
     const int d0 = lane * VPT;
     const bool active = d0 < D;
-    // candidate c: stream s = c / m (0: own block i, 1: B-block i-1), position j = c % m; the
-    // stream row of token position p is p - tok0, or p mod n_tok for a ring
-    const int n_cand = (P.n_streams == 2 && i >= 1) ? 2 * m : m;
-    auto row_of = [&](int64_t pos) -> int64_t { return P.ring ? pos % P.n_tok : pos - tok0; };
-
-    float acc[VPT];
+    const int n_cand = entry_candidates(P, i);
+    constexpr int kRowBatch = 8;
+    float xb[kRowBatch][VPT];
+    auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
-    // RMSNorm weights of this lane's dims, requested first so their latency overlaps the rows'
-    float nw[VPT];
-    if (P.norm_w) {
-#pragma unroll
-        for (int v = 0; v < VPT; v++) nw[v] = active ? P.norm_w[d0 + v] : 0.0f;
+        for (int u = 0; u < kRowBatch; u++) {
+            const int c = min(c0 + u, c_end - 1);
+            const int s = c / m;
+            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, candidate_row(P, i, c, tok0), D, d0, active, xb[u],
+                          x_off);
+        }
+    };
+    if (c_begin < c_end) load_batch(c_begin);
+    float zmax = -INFINITY;
+    for (int c = lane; c < n_cand; c += 64) {
+        const int s = c / m, j = c % m;
+        const float z = (s == 0 ? P.g0 : P.g1)[g_off + candidate_row(P, i, c, tok0)] + (s == 0 ? P.b0 : P.b1)[j];
+        wsh[c] = z;
+        zmax = fmaxf(zmax, z);
     }
-
-    if (P.G == 1) {
-        // candidate rows are loaded in batches of kRowBatch; the first batch is issued before the
-        // gate logits so the two memory round trips overlap
-        constexpr int kRowBatch = 8;
-        float xb[kRowBatch][VPT];
-        auto load_batch = [&](int c0) {
-#pragma unroll
-            for (int u = 0; u < kRowBatch; u++) {
-                const int c = min(c0 + u, n_cand - 1);
-                const int s = c / m, j = c % m;
-                const int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
-                load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, xb[u], x_off);
-            }
-        };
-        load_batch(0);
-        // weights once per wavefront: lane c holds candidate c (and c + 64, ...)
-        float zmax = -INFINITY;
-        for (int c = lane; c < n_cand; c += 64) {
-            int s = c / m, j = c % m;
-            int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
-            float z = (s == 0 ? P.g0 : P.g1)[g_off + r] + (s == 0 ? P.b0 : P.b1)[j];
-            wsh[c] = z;
-            zmax = fmaxf(zmax, z);
-        }
-        zmax = wave_max(zmax);
-        float den = 0.0f;
-        for (int c = lane; c < n_cand; c += 64) {
-            float ex = expf(wsh[c] - zmax);
-            wsh[c] = ex;
-            den += ex;
-        }
-        den = wave_sum(den);
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int c0 = 0; c0 < n_cand; c0 += kRowBatch) {
-            float cur[kRowBatch][VPT];
-#pragma unroll
-            for (int u = 0; u < kRowBatch; u++)
-#pragma unroll
-                for (int v = 0; v < VPT; v++) cur[u][v] = xb[u][v];
-            if (c0 + kRowBatch < n_cand) load_batch(c0 + kRowBatch);  // next batch in flight
-#pragma unroll
-            for (int u = 0; u < kRowBatch; u++) {
-                if (c0 + u < n_cand) {
-                    const float wgt = wsh[c0 + u];
-#pragma unroll
-                    for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
-    } else {
-        // per-channel gates: online softmax over the candidates for each of this lane's dims
-        float mx[VPT], l[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; v++) { mx[v] = -INFINITY; l[v] = 0.0f; }
-        for (int c = 0; c < n_cand; c++) {
-            int s = c / m, j = c % m;
-            int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
-            float x[VPT];
-            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
-            const float *g = (s == 0 ? P.g0 : P.g1) + g_off + r * D + d0;
-            const float *bb = (s == 0 ? P.b0 : P.b1) + (int64_t)j * D + d0;
-#pragma unroll
-            for (int v = 0; v < VPT; v++) {
-                float z = active ? g[v] + bb[v] : 0.0f;
-                float mn = fmaxf(mx[v], z);
-                float corr = (mx[v] == -INFINITY) ? 0.0f : expf(mx[v] - mn);
-                float ex = (z == -INFINITY) ? 0.0f : expf(z - mn);
-                l[v] = l[v] * corr + ex;
-                acc[v] = acc[v] * corr + ex * x[v];
-                mx[v] = mn;
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
+    zmax = wave_max(zmax);
+    float den = 0.0f;
+    for (int c = lane; c < n_cand; c += 64) {
+        const float ex = expf(wsh[c] - zmax);
+        wsh[c] = ex;
+        den += ex;
     }
+    den = wave_sum(den);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int c0 = c_begin; c0 < c_end; c0 += kRowBatch) {
+        float cur[kRowBatch][VPT];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; u++)
+#pragma unroll
+            for (int v = 0; v < VPT; v++) cur[u][v] = xb[u][v];
+        if (c0 + kRowBatch < c_end) load_batch(c0 + kRowBatch);  // next batch in flight
+#pragma unroll
+        for (int u = 0; u < kRowBatch; u++) {
+            if (c0 + u < c_end) {
+                const float wgt = wsh[c0 + u];
+#pragma unroll
+                for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
+            }
+        }
+    }
+    return den;
+}
 
+// The merged entry acc (one wavefront) is normalised, rotated and written as entry i of sequence
+// seq: RMSNorm with the lane's weights nw, RoPE at position m*i, the record or key encoder.
+template <int VPT>
+__device__ __forceinline__ void finish_entry(const CompressParams &P, float (&acc)[VPT], const float (&nw)[VPT],
+                                             int64_t seq, int64_t i) {
+    const int lane = threadIdx.x & 63;
+    const int m = P.m, D = P.D;
+    const int d0 = lane * VPT;
+    const bool active = d0 < D;
     // RMSNorm of the merged entry ("DeepSeek-V4 technical report walkthrough", section 2.3:
     // RMSNorm acts directly on the KV entries): x * w / sqrt(mean(x^2) + eps), before RoPE
     if (P.norm_w) {
@@ -201,6 +178,110 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
         store_mxfp4<VPT>(acc, lane, active, D, P.idx, orow);
     else
         store_record<VPT>(acc, d0, active, D, P.R, P.kv, orow);
+}
+
+// RMSNorm weights of this lane's dims (requested early so their latency overlaps the rows').
+template <int VPT>
+__device__ __forceinline__ void load_norm_weights(const CompressParams &P, float (&nw)[VPT]) {
+    const int d0 = (threadIdx.x & 63) * VPT;
+#pragma unroll
+    for (int v = 0; v < VPT; v++) nw[v] = (P.norm_w && d0 < P.D) ? P.norm_w[d0 + v] : 0.0f;
+}
+
+// Entries whose candidates a whole workgroup of kEntryWaves wavefronts shares (gate per token,
+// blocks of at least 64 tokens: the HCA blocks); every caller decides with this one rule.
+constexpr int kEntryWaves = 4;
+__host__ __device__ __forceinline__ bool entry_uses_workgroup(const CompressParams &P) {
+    return P.G == 1 && P.m >= 64;
+}
+
+// Entry i of sequence seq, computed by one whole wavefront; row 0 of the sequence's streams
+// is position tok0 (its streams and gates start n_tok rows further per sequence); wsh is the
+// wavefront's scratch for the candidate weights.
+template <int VPT>
+__device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
+                                               int64_t tok0) {
+    const int lane = threadIdx.x & 63;
+    const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
+    const int m = P.m, D = P.D;
+    const int d0 = lane * VPT;
+    const bool active = d0 < D;
+    const int n_cand = entry_candidates(P, i);
+    auto row_of = [&](int64_t pos) -> int64_t { return P.ring ? pos % P.n_tok : pos - tok0; };
+    float acc[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
+    float nw[VPT];
+    load_norm_weights<VPT>(P, nw);
+    if (P.G == 1) {
+        const float den = merge_gate1<VPT>(P, wsh, seq, i, tok0, 0, n_cand, acc);
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
+    } else {
+        // per-channel gates: online softmax over the candidates for each of this lane's dims
+        float mx[VPT], l[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; v++) { mx[v] = -INFINITY; l[v] = 0.0f; }
+        for (int c = 0; c < n_cand; c++) {
+            int s = c / m, j = c % m;
+            int64_t r = row_of((s == 0 ? m * i : m * (i - 1)) + j);
+            float x[VPT];
+            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, r, D, d0, active, x, x_off);
+            const float *g = (s == 0 ? P.g0 : P.g1) + g_off + r * D + d0;
+            const float *bb = (s == 0 ? P.b0 : P.b1) + (int64_t)j * D + d0;
+#pragma unroll
+            for (int v = 0; v < VPT; v++) {
+                float z = active ? g[v] + bb[v] : 0.0f;
+                float mn = fmaxf(mx[v], z);
+                float corr = (mx[v] == -INFINITY) ? 0.0f : expf(mx[v] - mn);
+                float ex = (z == -INFINITY) ? 0.0f : expf(z - mn);
+                l[v] = l[v] * corr + ex;
+                acc[v] = acc[v] * corr + ex * x[v];
+                mx[v] = mn;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
+    }
+    finish_entry<VPT>(P, acc, nw, seq, i);
+}
+
+// Entry i of sequence seq computed by all kEntryWaves wavefronts of the workgroup (gate per
+// token): wavefront w accumulates its contiguous share of the candidates, the partial sums meet
+// in LDS (red: kEntryWaves x D floats) and wavefront 0 adds them in wavefront order, divides by
+// the weight sum and finishes the entry.  wsh: kEntryWaves x kMaxCand floats.  Every thread of
+// the workgroup must call it.
+template <int VPT>
+__device__ __forceinline__ void compress_entry_wg(const CompressParams &P, float *wsh, float *red, int64_t seq,
+                                                  int64_t i, int64_t tok0) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int d0 = lane * VPT;
+    const bool active = d0 < P.D;
+    const int n_cand = entry_candidates(P, i);
+    const int per = (n_cand + kEntryWaves - 1) / kEntryWaves;
+    const int c0 = min(n_cand, wv * per), c1 = min(n_cand, c0 + per);
+    float acc[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
+    float nw[VPT];
+    if (wv == 0) load_norm_weights<VPT>(P, nw);
+    const float den = merge_gate1<VPT>(P, wsh + wv * kMaxCand, seq, i, tok0, c0, c1, acc);
+    if (active) {
+#pragma unroll
+        for (int v = 0; v < VPT; v++) red[wv * P.D + d0 + v] = acc[v];
+    }
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int v = 0; v < VPT; v++) {
+        float sum = 0.0f;
+        if (active) {
+            sum = red[d0 + v];
+            for (int w = 1; w < kEntryWaves; w++) sum += red[w * P.D + d0 + v];
+        }
+        acc[v] = sum / den;
+    }
+    finish_entry<VPT>(P, acc, nw, seq, i);
 }
 
 // Kernel parameters of a checked CompressArgs (host).
