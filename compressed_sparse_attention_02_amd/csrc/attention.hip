@@ -12,8 +12,9 @@
 // Keys of sequence b, in order: its entries (the top-k indices for CSA, the visible prefix
 // for HCA) then its window tokens; every key is also its own value over all D dims.
 //
-// MFMA kernel (FP8/BF16 records, BF16 queries and window).  A workgroup of four wavefronts
-// owns 64 heads (16 per wavefront) of one sequence and one split of its keys; with 128 heads
+// MFMA kernel (FP8/BF16 records, BF16 queries and window).  A workgroup owns one sequence and
+// one split of its keys, 16 heads per wavefront: either all heads (up to 8 wavefronts, for
+// grids that fill the chip) or 64 of them (4 wavefronts); in the latter case with 128 heads
 // the two head-group workgroups of a split get linear ids 8 apart, so they land on the same
 // XCD and share its L2 for the key tiles.  Per tile of 32 keys:
 //   staging: every lane converts 4 keys x 4 dims (E4M3 codes are exact in BF16) and writes
@@ -132,8 +133,8 @@ __device__ __forceinline__ void finish4(const AttnParams &P, const SeqInfo &Sq, 
 }
 
 // ------------------------------------------------------------------ MFMA kernel -----
-template <int D, int R>
-__global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnParams P, SeqInfo Sq) {
+template <int D, int R, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnParams P, SeqInfo Sq) {
     constexpr int NKS = D / 32;   // k-steps of the score MFMA
     constexpr int NDT = D / 16;   // dim tiles of the value MFMA
     constexpr int Dn = D - R;
@@ -632,15 +633,28 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
         V4A_LAUNCH("attn_f32_kernel", attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);
         return hipGetLastError();
     }
-    P.n_hg = (a.H + 63) / 64;
-    const int waves = (a.H >= 64) ? 4 : a.H / 16;
-    int pairs = a.B * P.S;
+    // Workgroup shape: with enough (query, split) pairs to fill the chip, one workgroup of up to
+    // 8 wavefronts covers all heads, so each staged key tile serves every head (half the
+    // staging per head); with few pairs (latency-bound decode) two 4-wavefront head groups per
+    // split double the workgroups instead.  Every wavefront computes the same keys in the same
+    // order for its 16 heads either way, so the choice never changes a result.
+    const int pairs = a.B * P.S;
+    const bool wide = a.H > 64 && pairs >= 256;
+    P.n_hg = wide ? 1 : (a.H + 63) / 64;
+    const int waves = wide ? a.H / 16 : (a.H >= 64 ? 4 : a.H / 16);
     int blocks = pairs;
     if (P.n_hg == 2) blocks = ((pairs + 7) / 8) * 16;
-    if (a.D == 512)
-        V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
-    else
-        V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+    if (a.D == 512) {
+        if (wide)
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+        else
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+    } else {
+        if (wide)
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+        else
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
     V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel, dim3(a.D / 16, a.H / 16, a.B), dim3(64), 0, s, P, sq);
