@@ -334,10 +334,12 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
     if (mx) {
-        // keys per workgroup: the largest power-of-two multiple of 512 that still gives at least
-        // 1024 workgroups (four per CU); it changes only the work split, never a result
+        // keys per workgroup: doubled from 512 while the grid keeps at least 1024 workgroups, so
+        // a large scan runs as 512-1024 workgroups (two to four per CU) of up to 4096 keys; it
+        // changes only the work split, never a result.  (At the 1M-context decode, 2048-key
+        // workgroups, two per CU, measured 20-21 us on every device tried; 1024-key ones 19-24.)
         int gpw = 2 * kGroupsPerIter;  // keys per workgroup = 4 wavefronts * gpw groups * 16 keys
-        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 2048) gpw *= 2;
+        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 1024) gpw *= 2;
         P.groups_per_wave = gpw;
         const int64_t kpw = (int64_t)64 * gpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
