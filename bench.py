@@ -156,14 +156,13 @@ def main():
 
     # the step as one call (compression + histogram clear in one launch, then selection and
     # attention) on every input set
-    step_args = [[v4.DecodeStepArgs(q_pos=q_pos, n_entries=[N] * B, m=m, kv_a=st["kv_a"], kv_b=st["kv_b"],
-                                     gate_a=st["gate_a"], gate_b=st["gate_b"], bias_a=st["bias_a"],
-                                     bias_b=st["bias_b"], idx_a=st["idx_a"], idx_b=st["idx_b"],
-                                     idx_gate_a=st["idx_gate_a"], idx_gate_b=st["idx_gate_b"],
-                                     idx_bias_a=st["idx_bias_a"], idx_bias_b=st["idx_bias_b"], kv=st["kv"],
-                                     keys=st["keys"], q_idx=st["qi"], w=st["w"], k=k, q=st["q"], win=st["win"],
-                                     win_len=win_len, W=W, sink=st["sink"], softmax_scale=scale, out=outs[j])
-                  for j in range(2)] for st in sets]
+    step_kwargs = [dict(q_pos=q_pos, n_entries=[N] * B, m=m, kv_a=st["kv_a"], kv_b=st["kv_b"], gate_a=st["gate_a"],
+                        gate_b=st["gate_b"], bias_a=st["bias_a"], bias_b=st["bias_b"], idx_a=st["idx_a"],
+                        idx_b=st["idx_b"], idx_gate_a=st["idx_gate_a"], idx_gate_b=st["idx_gate_b"],
+                        idx_bias_a=st["idx_bias_a"], idx_bias_b=st["idx_bias_b"], kv=st["kv"], keys=st["keys"],
+                        q_idx=st["qi"], w=st["w"], k=k, q=st["q"], win=st["win"], win_len=win_len, W=W,
+                        sink=st["sink"], softmax_scale=scale) for st in sets]
+    step_args = [[v4.DecodeStepArgs(**kw, out=outs[j]) for j in range(2)] for kw in step_kwargs]
     step_ws = v4.workspace(v4.v4a_decode_step_workspace(step_args[0][0]))
 
     def step(i):
@@ -333,7 +332,23 @@ def main():
     if bf16_variant is not None:
         result["variants"] = {"bf16_scores": bf16_variant}
     if not args.no_secondary:
-        del sets, step_args
+        # the same fused step with split-free attention (bitwise equal to prefill, no split-K)
+        ns_args = [v4.DecodeStepArgs(**{**sa_kw, "out": outs[0]}, no_split=True) for sa_kw in step_kwargs]
+        ns_ws = v4.workspace(v4.v4a_decode_step_workspace(ns_args[0]))
+        for i in range(args.warmup):
+            v4.v4a_decode_step_csa(ns_args[i % len(ns_args)], ns_ws)
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(n_sep):
+            v4.v4a_decode_step_csa(ns_args[(args.warmup + i) % len(ns_args)], ns_ws)
+        t_end.record()
+        torch.cuda.synchronize()
+        ms_ns = t_start.elapsed_time(t_end) / n_sep
+        result.setdefault("variants", {})["split_free_attention"] = {
+            "entry_point": "v4a_decode_step_csa (no_split)", "ms_per_step": ms_ns, "tokens_per_s": B / (ms_ns / 1e3),
+            "ms_per_step_split_k": ms_step}
+    if not args.no_secondary:
+        del sets, step_args, step_kwargs, ns_args
         torch.cuda.empty_cache()
         result["secondary"] = {"hca_decode_1m": hca_secondary(v4, torch, HCA_1M, args, f32, bf16)}
         torch.cuda.empty_cache()
@@ -433,6 +448,19 @@ def hca_secondary(v4, torch, wl, args, f32, bf16):
     b.record()
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / steps
+    ns_args = [v4.DecodeStepHcaArgs(q_pos=q_pos, n_entries=[N] * B, m=wl.m_hca, kv_a=rows, gate_a=gates,
+                                    bias_a=hbias, kv=kvs[r], q=q, win=win, win_len=[W] * B, W=W, sink=sink,
+                                    softmax_scale=1.0 / math.sqrt(D), out=out, ring=True, no_split=True)
+               for r in range(rot)]
+    for i in range(args.warmup):
+        v4.v4a_decode_step_hca(ns_args[i % rot], None)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(steps):
+        v4.v4a_decode_step_hca(ns_args[i % rot], None)
+    b.record()
+    torch.cuda.synchronize()
+    ms_ns = a.elapsed_time(b) / steps
 
     nbytes = B * N * ((D - R) + 2 * R + 4) + B * W * D * 2 + B * H * D * 2 * 2
     flops = 4.0 * B * H * D * (N + W)
@@ -442,7 +470,8 @@ def hca_secondary(v4, torch, wl, args, f32, bf16):
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "input_copies": rot,
             "fused_step": {"entry_point": "v4a_decode_step_hca", "ms_per_step": ms_step,
                            "tokens_per_s": B / (ms_step / 1e3),
-                           "note": "block compression of every sequence's newest 128 tokens + attention, ring window"}}
+                           "note": "block compression of every sequence's newest 128 tokens + attention, ring window",
+                           "ms_per_step_split_free": ms_ns}}
 
 
 def prefill_secondary(v4, torch, kind, args):

@@ -478,7 +478,7 @@ static size_t decode_ws_bytes(int B, int H, int D, int split_cap) {
 // positions and the split plan, and returns the workspace it needs; launches nothing.
 static v4a_status decode_prepare(AttnArgs &a, SeqInfo &sq, const int32_t *win_len, const int64_t *q_pos,
                                  v4a_float q_t, v4a_float win_t, v4a_float out_t, size_t *ws_need,
-                                 const char *name) {
+                                 const char *name, bool no_split = false) {
     if (!a.q || !a.out || !a.sink || !q_pos) return fail(V4A_EINVAL, "%s: q, out, sink and q_pos are required", name);
     if (a.B < 1 || a.B > kMaxSeq) return fail(V4A_EUNSUPPORTED, "%s: B=%d not in [1, %d]", name, a.B, kMaxSeq);
     if (a.H < 1 || a.H > 128) return fail(V4A_EUNSUPPORTED, "%s: H=%d not in [1, 128]", name, a.H);
@@ -508,7 +508,13 @@ static v4a_status decode_prepare(AttnArgs &a, SeqInfo &sq, const int32_t *win_le
     const bool mfma = attn_uses_mfma(a);
     if (!mfma && n_keys_max > 8192 + 2048)
         return fail(V4A_EUNSUPPORTED, "%s: this format/shape uses the fp32 kernel, limited to %d keys", name, 8192 + 2048);
-    if (mfma) {
+    a.no_split = mfma && no_split;
+    if (mfma && no_split) {
+        if (a.H % 16 != 0) return fail(V4A_EUNSUPPORTED, "%s: the split-free attention needs H a multiple of 16", name);
+        a.target_splits = 1;
+        a.split_cap = 1;
+        *ws_need = 0;
+    } else if (mfma) {
         a.target_splits = kDecodeSplitTarget;
         int cap = 1;
         for (int b = 0; b < a.B; b++) {
@@ -923,7 +929,7 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     for (int b = 0; b < a->B; b++) pl.sq.n_ent[b] = a->k;
     size_t attn_need = 0;
     if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &attn_need,
-                             "v4a_decode_step_csa")) != V4A_OK)
+                             "v4a_decode_step_csa", a->no_split != 0)) != V4A_OK)
         return st;
     if (a->ring) {
         for (int b = 0; b < a->B; b++)
@@ -1075,7 +1081,8 @@ static v4a_status step_hca_plan(const v4a_decode_step_hca_args *a, StepHcaPlan &
     at.theta = a->rope_theta;
     at.out = a->out;
     size_t need = 0;
-    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &need, name)) != V4A_OK)
+    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &need, name,
+                             a->no_split != 0)) != V4A_OK)
         return st;
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "%s: needs the MFMA attention shapes", name);
     if (a->ring) {

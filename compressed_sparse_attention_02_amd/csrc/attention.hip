@@ -67,6 +67,8 @@ struct AttnParams {
     int S;                   // split capacity per sequence
     int target;              // splits aimed at per sequence
     int n_hg;                // head groups (workgroups) per split
+    int hpw;                 // split-free launches: heads per workgroup (0: split layout)
+    int item0;               // split-free launches: first (query, head group) item
 };
 
 __host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int *tps, int *splits) {
@@ -144,9 +146,14 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     __shared__ __attribute__((aligned(16))) int kvalid[kTile];
     __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
 
-    // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart
+    // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart.  A
+    // split-free launch numbers (query, group of hpw heads) items from item0 instead.
     int L = blockIdx.x, hg = 0, p = L;
-    if (P.n_hg == 2) {
+    if (P.hpw) {
+        const int item = P.item0 + L, groups = P.H / P.hpw;
+        hg = item % groups;
+        p = (item / groups) * P.S;  // split 0 of its query (S = 1)
+    } else if (P.n_hg == 2) {
         hg = (L >> 3) & 1;
         p = (L >> 4) * 8 + (L & 7);
     }
@@ -162,7 +169,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int h0 = hg * 64 + wv * 16;
+    const int h0 = hg * (P.hpw ? P.hpw : 64) + wv * 16;
     const bool wave_on = h0 < P.H;
     const int h = h0 + col;
     const int NT = blockDim.x;
@@ -599,6 +606,19 @@ void split_plan_host(int n_keys, int target, int *tps, int *splits) {
     split_plan(n_keys, target, tps, splits);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s) {
     AttnParams P{};
     P.q = a.q;
@@ -631,6 +651,36 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     if (a.B == 0) return hipSuccess;
     if (!attn_uses_mfma(a)) {
         V4A_LAUNCH("attn_f32_kernel", attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);
+        return hipGetLastError();
+    }
+    if (a.no_split) {
+        // Split-free: each (query, head group) attends over all its keys in one workgroup, so a
+        // head's result is the same whatever the batch and equals the prefill path's.  Full
+        // waves of 64-head workgroups first; the last partial wave runs as 16-head workgroups,
+        // which spread it over more CUs without changing any head's order of accumulation.
+        if (P.S != 1) return hipErrorInvalidValue;
+        const int cus = device_cu_count();
+        int full = 0;  // 64-head items of the full waves
+        if (a.H % 64 == 0 && cus > 0) full = (a.B * (a.H / 64) / cus) * cus;
+        const int units = a.B * (a.H / 16) - 4 * full;  // remaining 16-head items
+        if (full > 0) {
+            P.hpw = 64;
+            P.item0 = 0;
+            if (a.D == 512)
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(full), dim3(256), 0, s, P, sq);
+            else
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(full), dim3(256), 0, s, P, sq);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (units > 0) {
+            P.hpw = 16;
+            P.item0 = 4 * full;
+            if (a.D == 512)
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(units), dim3(64), 0, s, P, sq);
+            else
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(units), dim3(64), 0, s, P, sq);
+        }
         return hipGetLastError();
     }
     // Workgroup shape: with enough (query, split) pairs to fill the chip, one workgroup of up to

@@ -339,6 +339,8 @@ struct AttnArgs {
     float *partial;           // workspace for split partials (or NULL when split_cap == 1)
     int target_splits;        // splits aimed at per sequence
     int split_cap;            // max splits of any sequence (partial stride)
+    bool no_split;            // every (query, head group) attends over all its keys in one
+                              // workgroup: full waves of 64-head workgroups, then 16-head ones
 };
 bool attn_uses_mfma(const AttnArgs &a);
 hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s);

@@ -327,6 +327,12 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * ([cyqw] section 3.5: the state cache holds the window and the incomplete block): each
  * stream's [B][2m] rows hold position p at row p mod 2m, and win [B][W][D] holds position p
  * at row p mod W; the window tokens are positions t-win_len[b]+1 .. t (win_len[b] <= t+1).
+ * Split-free attention (no_split != 0; [cyqw] section 3.3: the attention kernels drop
+ * split-KV so that results are bitwise identical whatever the batch, and spread the last
+ * partial wave over more compute units in the same order of accumulation): every (sequence,
+ * head group) attends over all its keys in one workgroup, full waves of the chip as 64-head
+ * workgroups and the rest as 16-head ones, so each head's output is bit for bit the prefill
+ * chunk's for the same query and caches.  No workspace is needed for attention then.
  * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
  * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
 typedef struct {
@@ -362,6 +368,7 @@ typedef struct {
     const float *norm_w;         /* [D] f32 (device): RMSNorm of the new entries, or NULL       */
     const float *idx_norm_w;     /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL  */
     int32_t ring;                /* nonzero: the streams and the window are rings (see above)    */
+    int32_t no_split;            /* nonzero: split-free attention (see below)                   */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,
@@ -380,6 +387,7 @@ V4A_API size_t v4a_decode_step_workspace(const v4a_decode_step_args *args);
  * t+1-m .. t); sequences whose newest token completes no block read no rows.  With ring != 0,
  * position p sits at row p mod m of its sequence's rows and at row p mod W of the window,
  * whose tokens are positions t-win_len[b]+1 .. t (win_len[b] <= t+1).
+ * no_split: the split-free attention of v4a_decode_step_csa.
  * Supports the MFMA attention shapes (FP8/BF16 records with D in {128, 512}, H a multiple of 16
  * up to 128), m <= 128, B <= 128. */
 typedef struct {
@@ -408,6 +416,7 @@ typedef struct {
     void *out;                   /* [B][H][D] (device)                                         */
     v4a_float out_t;
     int32_t ring;                /* nonzero: the stream rows and the window are rings          */
+    int32_t no_split;            /* nonzero: split-free attention (see below)                  */
 } v4a_decode_step_hca_args;
 
 V4A_API v4a_status v4a_decode_step_hca(const v4a_decode_step_hca_args *args, void *ws, size_t ws_bytes,

@@ -345,3 +345,64 @@ def test_hca_chunk_full_size():
     w = PREFILL_64K
     r = run_hca_chunk(w)
     check_hca_chunk(w, r, [0, 1, 2047, 4093, 4094, 4095], decode_queries=(4095,))
+
+
+# ------------------------------------------- prefill == split-free decode, bit for bit ---
+# "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 3.3: attention without
+# split-KV keeps results bitwise identical; the split-free decode step then equals the prefill
+# chunk for the same query and caches.
+
+def decode_positions(tok0, C, m, n=6):
+    """Chunk queries spread over the chunk whose token completes no block (the step compresses
+    nothing, so it reads the caches the chunk left)."""
+    js = [j for j in np.linspace(0, C - 1, 3 * n).astype(int) if (tok0 + j + 1) % m != 0]
+    return js[:n]
+
+
+def test_hca_prefill_equals_split_free_decode():
+    w = scaled(PREFILL_64K, T=8192, chunk=700)
+    r = run_hca_chunk(w)
+    x, kv = r["x"], r["kv"]
+    tok0, n_prev, D, H, W = x["tok0"], x["n_prev"], w.D, w.H, w.W
+    rows = torch.zeros((1, 128, D), dtype=torch.bfloat16, device="cuda")  # read only when a block completes
+    gates = torch.zeros((1, 128, 1), dtype=torch.float32, device="cuda")
+    for j in decode_positions(tok0, x["C"], 128):
+        t = tok0 + j
+        announce(f"hca prefill == split-free decode at t={t}")
+        win = r["kv_dev"][n_prev + j - W + 1:n_prev + j + 1][None].contiguous()
+        out = torch.empty((1, H, D), dtype=torch.bfloat16, device="cuda")
+        args = v4.DecodeStepHcaArgs(q_pos=[t], n_entries=[r["n_total"]], m=128, kv_a=rows, gate_a=gates,
+                                    bias_a=f32(x["bias_a"]), kv=kv, q=r["q_dev"][j][None].contiguous(), win=win,
+                                    win_len=[W], W=W, sink=f32(x["sink"]), softmax_scale=w.scale, out=out,
+                                    no_split=True)
+        assert v4.v4a_decode_step_hca_workspace(args) == 0
+        v4.v4a_decode_step_hca(args, None)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], r["out"][j]), f"hca t={t}"
+
+
+def test_csa_prefill_equals_split_free_decode():
+    w = scaled(PREFILL_64K, T=8192, chunk=700)
+    r = run_csa_chunk(w)
+    x = r["x"]
+    tok0, n_prev, C, D, dI, H, HI, k, W = x["tok0"], x["n_prev"], x["C"], w.D, w.d_I, w.H, w.H_I, w.k, w.W
+    kv1, keys1 = kv_slot(r["kv"], r["slot"]), idx_slot(r["keys"], r["slot"])
+    z = lambda *shape, dt=torch.bfloat16: torch.zeros(shape, dtype=dt, device="cuda")  # rows read only on completion
+    zf = lambda *shape: z(*shape, dt=torch.float32)
+    for j in decode_positions(tok0, C, 4):
+        t = tok0 + j
+        announce(f"csa prefill == split-free decode at t={t}")
+        qi = v4.Idx(r["qi"].fmt, dI, r["qi"].codes[:, j * HI:(j + 1) * HI], r["qi"].scales[:, j * HI:(j + 1) * HI], HI)
+        win = r["dev"]["kv_a"][n_prev + j - W + 1:n_prev + j + 1][None].contiguous()
+        out = torch.empty((1, H, D), dtype=torch.bfloat16, device="cuda")
+        args = v4.DecodeStepArgs(q_pos=[t], n_entries=[r["n_total"]], m=4, kv_a=z(1, 8, D), kv_b=z(1, 8, D),
+                                 gate_a=zf(1, 8, 1), gate_b=zf(1, 8, 1), bias_a=zf(4, 1), bias_b=zf(4, 1),
+                                 idx_a=z(1, 8, dI), idx_b=z(1, 8, dI), idx_gate_a=zf(1, 8, 1), idx_gate_b=zf(1, 8, 1),
+                                 idx_bias_a=zf(4, 1), idx_bias_b=zf(4, 1), kv=kv1, keys=keys1, q_idx=qi,
+                                 w=f32(x["w"][j][None]), k=k, q=r["q_dev"][j][None].contiguous(), win=win,
+                                 win_len=[W], W=W, sink=f32(x["sink"]), softmax_scale=w.scale, out=out,
+                                 no_split=True)
+        ws = v4.workspace(v4.v4a_decode_step_workspace(args))
+        v4.v4a_decode_step_csa(args, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], r["out"][j]), f"csa t={t}"
