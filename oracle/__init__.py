@@ -80,6 +80,7 @@ def _declare(L):
     L.orc_indexer_scores_f32.argtypes = [P, P, I32, I32, P, I64, P]
     L.orc_topk.argtypes = [P, I64, I32, P]
     L.orc_topk_bf16.argtypes = [P, I64, I32, P]
+    L.orc_query_prologue.argtypes = [P, I32, I32, P, F64, I32, F64, F64, P]
     L.orc_attend.argtypes = [P, I32, I32, P, I64, P, I64, P, F64, I32, I32, F64, F64, P, P]
 
 
@@ -254,6 +255,16 @@ def topk(scores, k: int, n_vis=None, score_bf16: bool = False) -> np.ndarray:
 
 
 # --------------------------------------------------------------- attention ---
+
+def query_prologue(q_bits, norm_w, *, pos, R, eps=1e-6, theta=10000.0) -> np.ndarray:
+    """BF16 bits [H][D] of the queries after RMSNorm (weights norm_w [D]) and RoPE at pos."""
+    q_bits, pq = _c(q_bits, np.uint16)
+    H, D = q_bits.shape
+    w, pw = _c(norm_w, np.float32)
+    out = np.empty((H, D), np.uint16)
+    lib().orc_query_prologue(pq, H, D, pw, float(eps), int(R), float(pos), float(theta), out.ctypes.data_as(P))
+    return out
+
 
 def attend(q, E, Wn, sink, scale, *, rope_inverse=False, R=0, theta=10000.0, t_q=0.0,
            with_mass=False):

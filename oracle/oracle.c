@@ -284,6 +284,25 @@ static void rms_norm(double *x, int D, const float *w, double eps) {
     for (int d = 0; d < D; d++) x[d] = x[d] * r * (double)w[d];
 }
 
+/* Query prologue for queries that arrive projected but not normalised or
+ * rotated: each head's D-vector q (BF16 values) becomes RMSNorm(q) with the
+ * weights w (shared by the heads), then its last R dims are rotated at
+ * position pos, and the result is rounded to BF16 (nearest even), the
+ * precision the queries enter the products in.  Cited: [cyqw] section 2.3
+ * (RMSNorm acts directly on the queries) and [mewclaw] "Partial RoPE".
+ *   q [H][D] BF16 bits -> out [H][D] BF16 bits */
+ORC_API void orc_query_prologue(const uint16_t *q, int H, int D, const float *w, double eps, int R,
+                                double pos, double theta, uint16_t *out) {
+    double *x = malloc(sizeof(double) * D);
+    for (int h = 0; h < H; h++) {
+        for (int d = 0; d < D; d++) x[d] = orc_bf16_decode(q[h * D + d]);
+        rms_norm(x, D, w, eps);
+        if (R > 0) rope_rotate(x + (D - R), R, pos, theta, +1);
+        for (int d = 0; d < D; d++) out[h * D + d] = orc_bf16_encode((float)x[d]);
+    }
+    free(x);
+}
+
 /* CSA compressor (ratio m, two streams with overlap).  Cited: [cyqw]
  * section 2.2 (every m = 4 tokens become one entry; two independent KV
  * sequences merged with softmax-normalised gate weights; adjacent compressed

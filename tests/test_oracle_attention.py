@@ -150,3 +150,43 @@ def test_output_rope_inverse_is_applied_at_query_position(orc):
     plain = orc.attend(q, K, None, sink, 0.1)
     rot = orc.attend(q, K, None, sink, 0.1, rope_inverse=True, R=R, t_q=777.0)
     np.testing.assert_allclose(rot, orc.rope(plain, R, 777.0, sign=-1), rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------------ query prologue ---
+# "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.3: RMSNorm acts directly on
+# the queries; the rotation of the last R dims follows at the query position.
+
+def _bf16_bits_of(x64):
+    import torch
+    t = torch.from_numpy(np.asarray(x64, np.float64)).to(torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_query_prologue_matches_torch_norm_then_rope(orc):
+    import torch
+    g = np.random.default_rng(91)
+    H, D, R, pos = 8, 128, 32, 12345
+    q = _bf16_bits_of(g.standard_normal((H, D)))
+    w = (0.5 + g.random(D)).astype(np.float32)
+    got = orc.query_prologue(q, w, pos=pos, R=R)
+    x = torch.from_numpy(orc_bf16_values(q))
+    normed = torch.nn.functional.rms_norm(x, (D,), torch.from_numpy(w.astype(np.float64)), 1e-6).numpy()
+    expect = _bf16_bits_of(orc.rope(normed, R, np.full(H, pos)))
+    assert np.array_equal(got, expect)
+    # rotating first and normalising after gives another result (w differs within pairs)
+    other = _bf16_bits_of(torch.nn.functional.rms_norm(torch.from_numpy(orc.rope(orc_bf16_values(q), R, np.full(H, pos))),
+                                                       (D,), torch.from_numpy(w.astype(np.float64)), 1e-6).numpy())
+    assert not np.array_equal(got, other)
+
+
+def test_query_prologue_unit_weights_unit_rms(orc):
+    g = np.random.default_rng(92)
+    H, D = 4, 512
+    q = _bf16_bits_of(3.0 * g.standard_normal((H, D)))
+    got = orc_bf16_values(orc.query_prologue(q, np.ones(D, np.float32), pos=7, R=64, eps=0.0))
+    np.testing.assert_allclose(np.sqrt((got * got).mean(axis=1)), 1.0, atol=4e-3)
+
+
+def orc_bf16_values(bits):
+    from workloads import bf16_bits_to_f64
+    return bf16_bits_to_f64(np.asarray(bits, np.uint16))
