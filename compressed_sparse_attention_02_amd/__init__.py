@@ -54,7 +54,7 @@ class c_prefill_args(ctypes.Structure):
                 ("w", P), ("H_I", ctypes.c_int32), ("k", ctypes.c_int32), ("q", P), ("q_t", ctypes.c_int),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("sink", P), ("softmax_scale", ctypes.c_float),
                 ("out_rope_inverse", ctypes.c_int32), ("out", P), ("out_t", ctypes.c_int),
-                ("score_bf16", ctypes.c_int32), ("norm_w", P), ("idx_norm_w", P)]
+                ("score_bf16", ctypes.c_int32), ("norm_w", P), ("idx_norm_w", P), ("q_norm_w", P)]
 
 
 V4A_LAYER_CSA, V4A_LAYER_HCA = 0, 1
@@ -72,7 +72,7 @@ class c_decode_step_args(ctypes.Structure):
                 ("H", ctypes.c_int32), ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32),
                 ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
                 ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32), ("norm_w", P),
-                ("idx_norm_w", P), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32)]
+                ("idx_norm_w", P), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P)]
 
 
 
@@ -84,7 +84,7 @@ class c_decode_step_hca_args(ctypes.Structure):
                 ("kv", ctypes.POINTER(c_kv)), ("q", P), ("q_t", ctypes.c_int), ("H", ctypes.c_int32),
                 ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32), ("sink", P),
                 ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32), ("out", P),
-                ("out_t", ctypes.c_int), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32)]
+                ("out_t", ctypes.c_int), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P)]
 
 
 _lib = None
@@ -359,12 +359,12 @@ class PrefillArgs:
                  apply_rope: bool = True, rope_theta: float = 10000.0, idx_a=None, idx_b=None,
                  idx_gate_a=None, idx_gate_b=None, idx_bias_a=None, idx_bias_b=None, keys: Idx | None = None,
                  q_idx: Idx | None = None, w=None, k: int = 0, out_rope_inverse: bool = True,
-                 score_bf16: bool = False, norm_w=None, idx_norm_w=None):
+                 score_bf16: bool = False, norm_w=None, idx_norm_w=None, q_norm_w=None):
         self._kv = kv.c()
         self._keys = keys.c() if keys is not None else None
         self._q_idx = q_idx.c() if q_idx is not None else None
         self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b,
-                      idx_bias_a, idx_bias_b, w, q, sink, out, kv, keys, q_idx, norm_w, idx_norm_w)
+                      idx_bias_a, idx_bias_b, w, q, sink, out, kv, keys, q_idx, norm_w, idx_norm_w, q_norm_w)
         C, H = q.shape[0], q.shape[1]
         H_I = (w.numel() // C) if (w is not None and C > 0) else 0
         self.s = c_prefill_args(
@@ -379,7 +379,8 @@ class PrefillArgs:
             q_idx=ctypes.pointer(self._q_idx) if self._q_idx is not None else None,
             w=_ptr(w), H_I=H_I, k=k, q=_ptr(q), q_t=_ftype(q), H=H, W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out),
-            out_t=_ftype(out), score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w))
+            out_t=_ftype(out), score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w),
+            q_norm_w=_ptr(q_norm_w))
 
 
 def v4a_prefill_workspace(kind: int, args: PrefillArgs) -> int:
@@ -399,12 +400,12 @@ class DecodeStepArgs:
                  idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
                  win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
                  rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False,
-                 norm_w=None, idx_norm_w=None, ring: bool = False, no_split: bool = False):
+                 norm_w=None, idx_norm_w=None, ring: bool = False, no_split: bool = False, q_norm_w=None):
         B, H = q.shape[0], q.shape[1]
         self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
         self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b, idx_bias_a,
-                      idx_bias_b, kv, keys, q_idx, w, q, win, sink, out, norm_w, idx_norm_w)
+                      idx_bias_b, kv, keys, q_idx, w, q, win, sink, out, norm_w, idx_norm_w, q_norm_w)
         self.s = c_decode_step_args(
             B=B, m=m, q_pos=ctypes.cast(self._pos, ctypes.c_void_p), n_entries=ctypes.cast(self._nent, ctypes.c_void_p),
             in_t=_ftype(kv_a), G=gate_a.shape[-1], idx_G=idx_gate_a.shape[-1], kv_a=_ptr(kv_a), kv_b=_ptr(kv_b),
@@ -416,7 +417,7 @@ class DecodeStepArgs:
             win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out),
             score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w), ring=int(ring),
-            no_split=int(no_split))
+            no_split=int(no_split), q_norm_w=_ptr(q_norm_w))
 
 
 def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:
@@ -439,11 +440,12 @@ class DecodeStepHcaArgs:
 
     def __init__(self, *, q_pos, n_entries, m: int, kv_a, gate_a, bias_a, kv: KV, q, win, win_len, W: int, sink,
                  softmax_scale: float, out, apply_rope: bool = True, rope_theta: float = 10000.0,
-                 out_rope_inverse: bool = True, norm_w=None, ring: bool = False, no_split: bool = False):
+                 out_rope_inverse: bool = True, norm_w=None, ring: bool = False, no_split: bool = False,
+                 q_norm_w=None):
         B, H = q.shape[0], q.shape[1]
         self._kv = kv.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
-        self._refs = (kv_a, gate_a, bias_a, kv, q, win, sink, out, norm_w)
+        self._refs = (kv_a, gate_a, bias_a, kv, q, win, sink, out, norm_w, q_norm_w)
         self.s = c_decode_step_hca_args(
             B=B, m=m, q_pos=ctypes.cast(self._pos, ctypes.c_void_p), n_entries=ctypes.cast(self._nent, ctypes.c_void_p),
             in_t=_ftype(kv_a), G=gate_a.shape[-1], kv_a=_ptr(kv_a), gate_a=_ptr(gate_a), bias_a=_ptr(bias_a),
@@ -451,7 +453,7 @@ class DecodeStepHcaArgs:
             q=_ptr(q), q_t=_ftype(q), H=H, win=_ptr(win), win_t=_ftype(win),
             win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink), softmax_scale=softmax_scale,
             out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out), ring=int(ring),
-            no_split=int(no_split))
+            no_split=int(no_split), q_norm_w=_ptr(q_norm_w))
 
 
 def v4a_decode_step_hca_workspace(args: DecodeStepHcaArgs) -> int:

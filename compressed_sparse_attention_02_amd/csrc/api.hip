@@ -728,6 +728,8 @@ static v4a_status prefill_plan(v4a_layer kind, const v4a_prefill_args *a, Prefil
     if (!attn_uses_mfma(probe) && ent_max + a->W > 8192 + 2048)
         return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: this format/shape uses the fp32 kernel, limited to %d keys",
                     8192 + 2048);
+    if (a->q_norm_w && (!attn_uses_mfma(probe) || !aligned(a->q_norm_w, 16)))
+        return fail(V4A_EUNSUPPORTED, "v4a_prefill_chunk: q_norm_w needs the MFMA attention shapes and 16-byte alignment");
     pl.ws_total = 0;
     if (pl.csa) {
         if (!a->kv_b) return fail(V4A_EINVAL, "v4a_prefill_chunk: kv_b is required for CSA");
@@ -828,6 +830,7 @@ v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *a, void *ws
     at.sink = a->sink;
     at.scale = a->softmax_scale;
     at.rope_inv = a->out_rope_inverse != 0;
+    at.q_norm_w = a->q_norm_w;
     at.theta = a->rope_theta;
     at.out = a->out;
     at.out_bf16 = a->out_t == V4A_BF16;
@@ -938,6 +941,9 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
         pl.sq.ring = 1;
     }
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs the MFMA attention shapes");
+    if (a->q_norm_w && !aligned(a->q_norm_w, 16))
+        return fail(V4A_EINVAL, "v4a_decode_step_csa: q_norm_w must be 16-byte aligned");
+    pl.at.q_norm_w = a->q_norm_w;
     pl.sel_bytes = round_up((size_t)a->B * a->k * 4, 256);
     pl.topk_bytes = topk_layout(a->B, 1, pl.n_max, a->k).total;
     pl.attn_bytes = round_up(attn_need, 256);
@@ -1085,6 +1091,8 @@ static v4a_status step_hca_plan(const v4a_decode_step_hca_args *a, StepHcaPlan &
                              a->no_split != 0)) != V4A_OK)
         return st;
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "%s: needs the MFMA attention shapes", name);
+    if (a->q_norm_w && !aligned(a->q_norm_w, 16)) return fail(V4A_EINVAL, "%s: q_norm_w must be 16-byte aligned", name);
+    at.q_norm_w = a->q_norm_w;
     if (a->ring) {
         for (int b = 0; b < a->B; b++)
             if (pl.sq.win_len[b] > a->q_pos[b] + 1)

@@ -59,6 +59,7 @@ struct AttnParams {
     const float *sink;       // [H]
     float scale2;            // softmax scale * log2(e)
     bool rope_inv;
+    const float *q_norm_w;   // [D] or NULL: queries arrive projected only (RMSNorm + RoPE here)
     RopeTable rt;
     void *out;
     bool out_bf16;
@@ -178,10 +179,62 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     v8bf qT[NKS];
     {
         const uint16_t *qr = (const uint16_t *)P.q + ((int64_t)b * P.H + (wave_on ? h : 0)) * D;
+        uint4 qu[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++) {
-            uint4 u = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
-            qT[ks] = __builtin_bit_cast(v8bf, u);
+        for (int ks = 0; ks < NKS; ks++)
+            qu[ks] = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+        if (P.q_norm_w) {
+            // Query prologue ("DeepSeek-V4 technical report walkthrough", section 2.3: RMSNorm acts
+            // directly on the queries): RMSNorm of the head over its D dims (a head's dims sit in
+            // lanes col, col+16, col+32, col+48), RoPE at the query position on the last R dims
+            // (pairs inside a lane's 8 consecutive dims; Dn is a multiple of 32, so a k-step is
+            // all RoPE dims or none), then BF16 (nearest even) as the MFMA operand.
+            float ss = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float lo = __builtin_bit_cast(float, w4[j] << 16);
+                    const float hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
+                    ss = fmaf(lo, lo, ss);
+                    ss = fmaf(hi, hi, ss);
+                }
+            }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float rn = 1.0f / sqrtf(ss / (float)D + kNormEps);
+            RopeLanes rl;
+            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+                const float4 wa = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp);
+                const float4 wb = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp + 4);
+                const float wv8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+                float y[8];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    y[2 * j] = __builtin_bit_cast(float, w4[j] << 16) * rn * wv8[2 * j];
+                    y[2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u) * rn * wv8[2 * j + 1];
+                }
+                if (32 * ks >= Dn) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float2 cs = rl.get(16 * (ks - Dn / 32) + 4 * grp + i);
+                        const float x0 = y[2 * i], x1 = y[2 * i + 1];
+                        y[2 * i] = x0 * cs.x - x1 * cs.y;
+                        y[2 * i + 1] = x0 * cs.y + x1 * cs.x;
+                    }
+                }
+                v8bf qv;
+#pragma unroll
+                for (int j = 0; j < 8; j++) qv[j] = (__bf16)y[j];
+                qT[ks] = qv;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) qT[ks] = __builtin_bit_cast(v8bf, qu[ks]);
         }
     }
     v4f O[NDT];
@@ -641,7 +694,8 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     P.sink = a.sink;
     P.scale2 = a.scale * kLog2e;
     P.rope_inv = a.rope_inv;
-    if (a.rope_inv) fill_rope_table(P.rt, a.R, a.theta);
+    P.q_norm_w = a.q_norm_w;
+    if (a.rope_inv || a.q_norm_w) fill_rope_table(P.rt, a.R, a.theta);
     P.out = a.out;
     P.out_bf16 = a.out_bf16;
     P.part_o = a.partial;

@@ -339,6 +339,7 @@ struct AttnArgs {
     float *partial;           // workspace for split partials (or NULL when split_cap == 1)
     int target_splits;        // splits aimed at per sequence
     int split_cap;            // max splits of any sequence (partial stride)
+    const float *q_norm_w;    // [D]: queries arrive projected only; RMSNorm + RoPE in the kernel
     bool no_split;            // every (query, head group) attends over all its keys in one
                               // workgroup: full waves of 64-head workgroups, then 16-head ones
 };

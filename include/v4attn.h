@@ -303,6 +303,8 @@ typedef struct {
     int32_t score_bf16;      /* CSA: nonzero selects as v4a_indexer_topk_bf16 does         */
     const float *norm_w;     /* [D] f32 (device): RMSNorm of the new entries, or NULL      */
     const float *idx_norm_w; /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL */
+    const float *q_norm_w;   /* [D] f32 (device, 16-byte aligned) or NULL: queries arrive
+                                projected only, as in v4a_decode_step_csa                 */
 } v4a_prefill_args;
 
 V4A_API v4a_status v4a_prefill_chunk(v4a_layer kind, const v4a_prefill_args *args, void *ws,
@@ -333,6 +335,11 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * head group) attends over all its keys in one workgroup, full waves of the chip as 64-head
  * workgroups and the rest as 16-head ones, so each head's output is bit for bit the prefill
  * chunk's for the same query and caches.  No workspace is needed for attention then.
+ * Query prologue (q_norm_w != NULL; [cyqw] section 2.3: RMSNorm acts directly on the queries):
+ * q holds the projected queries before normalisation and rotation; each head's D-vector x
+ * becomes x_d * q_norm_w[d] / sqrt(mean(x^2) + 1e-6), its last R dims are rotated at the
+ * query position (interleaved pairs, as the entries are), and the result enters the products
+ * rounded to BF16 (nearest even).  Without it q arrives normalised and rotated.
  * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
  * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
 typedef struct {
@@ -369,6 +376,7 @@ typedef struct {
     const float *idx_norm_w;     /* [d] f32 (device): RMSNorm of the new indexer keys, or NULL  */
     int32_t ring;                /* nonzero: the streams and the window are rings (see above)    */
     int32_t no_split;            /* nonzero: split-free attention (see below)                   */
+    const float *q_norm_w;       /* [D] f32 (device, 16-byte aligned) or NULL: see below         */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,
@@ -417,6 +425,7 @@ typedef struct {
     v4a_float out_t;
     int32_t ring;                /* nonzero: the stream rows and the window are rings          */
     int32_t no_split;            /* nonzero: split-free attention (see below)                  */
+    const float *q_norm_w;       /* [D] f32 (device, 16-byte aligned) or NULL: as for CSA       */
 } v4a_decode_step_hca_args;
 
 V4A_API v4a_status v4a_decode_step_hca(const v4a_decode_step_hca_args *args, void *ws, size_t ws_bytes,

@@ -257,3 +257,51 @@ def test_fused_hca_step_equals_separate_calls(ring):
                             bf16_bits_to_f64(wp[b, :win_len[b]].view(torch.int16).cpu().numpy().view(np.uint16)),
                             sink.cpu().numpy(), scale, q_pos=q_pos[b], m=m, R=R)
     check_close(out_f64(out1[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what="fused hca step vs oracle")
+
+
+
+def test_fused_step_query_prologue():
+    """The fused CSA step with the query prologue (RMSNorm + RoPE of projected queries) against
+    the oracle fed the oracle's own prologue of the same queries, on every sequence."""
+    seed, m, D, R, H, HI, dI, k, W = 4545, 4, 512, 64, 128, 64, 128, 512, 128
+    q_pos = [4003, 2001, 8191]
+    B, cap = len(q_pos), 2304
+    n_ent = [(p + 1) // m for p in q_pos]
+    announce(f"fused decode step with query prologue: q_pos={q_pos}")
+    kv = v4.KV.empty(B, cap, D, R)
+    v4.v4a_quantize_kv(f32(normal(seed, "records", (B * cap, D))), kv, 0)
+    keys = v4.Idx.empty(B, cap, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "keys", (B * cap, dI))), keys, 0)
+    qi = v4.Idx.empty(B, HI, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(seed, "q_idx", (B * HI, dI))), qi)
+    rows = {n: bf16_from_bits(to_bf16_bits(normal(seed, n, (B, 2 * m, D if n.startswith("kv") else dI))))
+            for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
+    gates = {n: f32(normal(seed, n, (B, 2 * m, 1))) for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
+    bias = {n: f32(normal(seed, n, (m, 1))) for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
+    w = f32(normal(seed, "w", (B, HI)))
+    q_bits = to_bf16_bits(2.0 * normal(seed, "q", (B, H, D)))
+    win_bits = to_bf16_bits(normal(seed, "window", (B, W, D)))
+    win_len = [W] * B
+    sink = normal(seed, "sink", (H,))
+    qw = (0.5 + np.random.default_rng(seed).random(D)).astype(np.float32)
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    args = v4.DecodeStepArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=rows["kv_a"], kv_b=rows["kv_b"],
+                             gate_a=gates["gate_a"], gate_b=gates["gate_b"], bias_a=bias["bias_a"],
+                             bias_b=bias["bias_b"], idx_a=rows["idx_a"], idx_b=rows["idx_b"],
+                             idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
+                             idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv, keys=keys,
+                             q_idx=qi, w=w, k=k, q=bf16_from_bits(q_bits), win=bf16_from_bits(win_bits),
+                             win_len=win_len, W=W, sink=f32(sink), softmax_scale=scale, out=out, q_norm_w=f32(qw))
+    ws = v4.workspace(v4.v4a_decode_step_workspace(args))
+    v4.v4a_decode_step_csa(args, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        recs = oracle.dequant_kv(kv.nope[b, :n_ent[b]].cpu().numpy(),
+                                 kv.rope[b, :n_ent[b]].cpu().numpy().view(np.uint16), kv.scale[b, :n_ent[b]].cpu().numpy())
+        idx = dict(q_codes=qi.codes[b].cpu().numpy(), q_scales=qi.scales[b].cpu().numpy(), w=w[b].cpu().numpy(),
+                   k_codes=keys.codes[b, :n_ent[b]].cpu().numpy(), k_scales=keys.scales[b, :n_ent[b]].cpu().numpy())
+        qp = bf16_bits_to_f64(oracle.query_prologue(q_bits[b], qw, pos=q_pos[b], R=R))
+        ref, _ = oracle.decode_csa(qp, recs, n_ent[b], k, bf16_bits_to_f64(win_bits[b]), sink, scale, q_pos=q_pos[b],
+                                   m=m, idx=idx, R=R)
+        check_close(out_f64(out[b]), bf16_round(ref), MAX_ABS_BF16, REL_L2_BF16, what=f"query prologue, sequence {b}")

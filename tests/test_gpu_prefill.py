@@ -277,7 +277,7 @@ def test_csa_mxfp4_chunk_bf16_scores():
     check_csa_chunk(w, r, sample_queries(700), decode_queries=(349,))
 
 
-def run_hca_chunk(w):
+def run_hca_chunk(w, q_norm_w=None):
     x = prefill_inputs(w, kind="hca")
     C, tok0, n_prev, N0 = x["C"], x["tok0"], x["n_prev"], x["N0"]
     D, R, H, W = w.D, w.R, w.H, w.W
@@ -290,7 +290,8 @@ def run_hca_chunk(w):
     q_dev, _ = bf16_dev(x["q"])
     out = torch.empty((C, H, D), dtype=torch.bfloat16, device="cuda")
     a = v4.PrefillArgs(tok0=tok0, n_prev=n_prev, m=128, kv_a=kv_dev, gate_a=f32(x["gate_a"]), bias_a=f32(x["bias_a"]),
-                       kv=kv, q=q_dev, W=W, sink=f32(x["sink"]), softmax_scale=w.scale, out=out)
+                       kv=kv, q=q_dev, W=W, sink=f32(x["sink"]), softmax_scale=w.scale, out=out,
+                       q_norm_w=None if q_norm_w is None else f32(q_norm_w))
     v4.v4a_prefill_chunk(HCA, a, None)
     torch.cuda.synchronize()
     return dict(x=x, a=a, kv=kv, kv_dev=kv_dev, kv_val=kv_val, q_dev=q_dev, out=out, n_total=n_total, cap=cap)
@@ -406,3 +407,43 @@ def test_csa_prefill_equals_split_free_decode():
         v4.v4a_decode_step_csa(args, ws)
         torch.cuda.synchronize()
         assert torch.equal(out[0], r["out"][j]), f"csa t={t}"
+
+
+
+# --------------------------------------------------------------- query prologue ---
+# "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.3: RMSNorm acts directly on the
+# queries; with q_norm_w the queries arrive projected only and are normalised and rotated here.
+
+def test_hca_chunk_query_prologue_and_split_free_decode():
+    w = scaled(PREFILL_64K, T=8192, chunk=700)
+    D, R, H, W = w.D, w.R, w.H, w.W
+    qw = (0.5 + np.random.default_rng(80).random(D)).astype(np.float32)
+    r = run_hca_chunk(w, q_norm_w=qw)
+    x, kv = r["x"], r["kv"]
+    tok0, n_prev, C, n_total = x["tok0"], x["n_prev"], x["C"], r["n_total"]
+    queries = sample_queries(C)
+    announce("hca prefill with query prologue: oracle on sampled queries")
+    q_bits = to_bf16_bits(x["q"])
+    q64 = np.zeros((C, H, D))
+    for j in queries:
+        q64[j] = bf16_bits_to_f64(oracle.query_prologue(q_bits[j], qw, pos=tok0 + j, R=R))
+    recs = dequant_slot(kv, n_total)
+    ref, _ = oracle.prefill_queries("hca", q64, recs, n_total, r["kv_val"], n_prev=n_prev, tok0=tok0, queries=queries,
+                                    W=W, sink=x["sink"], scale=w.scale, m=128, R=R)
+    got = out_f64(r["out"])
+    check_close(got[queries], bf16_round(np.stack([ref[j] for j in queries])), MAX_ABS_BF16, REL_L2_BF16,
+                what="hca prefill with query prologue vs oracle")
+    rows = torch.zeros((1, 128, D), dtype=torch.bfloat16, device="cuda")
+    gates = torch.zeros((1, 128, 1), dtype=torch.float32, device="cuda")
+    for j in decode_positions(tok0, C, 128, n=3):
+        t = tok0 + j
+        announce(f"hca prefill == split-free decode with query prologue at t={t}")
+        win = r["kv_dev"][n_prev + j - W + 1:n_prev + j + 1][None].contiguous()
+        out = torch.empty((1, H, D), dtype=torch.bfloat16, device="cuda")
+        args = v4.DecodeStepHcaArgs(q_pos=[t], n_entries=[n_total], m=128, kv_a=rows, gate_a=gates,
+                                    bias_a=f32(x["bias_a"]), kv=kv, q=r["q_dev"][j][None].contiguous(), win=win,
+                                    win_len=[W], W=W, sink=f32(x["sink"]), softmax_scale=w.scale, out=out,
+                                    no_split=True, q_norm_w=f32(qw))
+        v4.v4a_decode_step_hca(args, None)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], r["out"][j]), f"t={t}"
