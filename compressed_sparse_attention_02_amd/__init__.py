@@ -72,7 +72,8 @@ class c_decode_step_args(ctypes.Structure):
                 ("H", ctypes.c_int32), ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32),
                 ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
                 ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32), ("norm_w", P),
-                ("idx_norm_w", P), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P)]
+                ("idx_norm_w", P), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P),
+                ("ws_clean", ctypes.c_int32)]
 
 
 
@@ -400,7 +401,8 @@ class DecodeStepArgs:
                  idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
                  win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
                  rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False,
-                 norm_w=None, idx_norm_w=None, ring: bool = False, no_split: bool = False, q_norm_w=None):
+                 norm_w=None, idx_norm_w=None, ring: bool = False, no_split: bool = False, q_norm_w=None,
+                 ws_clean: bool = False):
         B, H = q.shape[0], q.shape[1]
         self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
@@ -417,7 +419,7 @@ class DecodeStepArgs:
             win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out),
             score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w), ring=int(ring),
-            no_split=int(no_split), q_norm_w=_ptr(q_norm_w))
+            no_split=int(no_split), q_norm_w=_ptr(q_norm_w), ws_clean=int(ws_clean))
 
 
 def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:

@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "common.hpp"
+#include "compress.hpp"
 
 namespace v4a {
 
@@ -108,19 +108,19 @@ struct TopkWs {
     size_t keys, hist, list, counts, meta, total;
 };
 
-// Workspace of the indexer + top-k call: orderable score keys, the per-query histograms
-// (cleared on every call), the per-slice ordered lists of keys at or above the threshold
-// bin, their counts, and the per-query threshold.
+// Workspace of the indexer + top-k call: the per-query histograms (first, so that their place
+// depends on B and Q only), orderable score keys, the per-slice ordered lists of keys at or
+// above the threshold bin, their counts, and the per-query threshold.
 static TopkWs topk_layout(int B, int Q, int64_t n_max, int k) {
     (void)k;
     TopkWs L{};
     const size_t BQ = (size_t)B * (size_t)Q;
     const size_t slices = (size_t)select_slices(n_max);
     size_t off = 0;
-    L.keys = off;
-    off = round_up(off + BQ * (size_t)score_key_stride(n_max) * 4, 256);
     L.hist = off;
     off = round_up(off + BQ * hist_copies((int64_t)BQ) * kHistBins * 4, 256);
+    L.keys = off;
+    off = round_up(off + BQ * (size_t)score_key_stride(n_max) * 4, 256);
     L.list = off;
     off = round_up(off + BQ * slices * kSelSlice * 8, 256);
     L.counts = off;
@@ -349,7 +349,8 @@ namespace v4a {
 static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, int64_t n_max, const v4a_idx *q_idx,
                                       const float *w, int32_t B, int32_t Q, int32_t H_I, int32_t k, int32_t *out_idx,
                                       void *ws, hipStream_t s, bool clear_hist = true, bool key16 = false,
-                                      const CompressArgs *rec = nullptr) {
+                                      const CompressArgs *rec = nullptr, const CompressArgs *key_rec = nullptr,
+                                      bool clear_after = false) {
     const TopkWs L = topk_layout(B, Q, n_max, k);
     char *base = (char *)ws;
     const size_t BQ = (size_t)B * Q;
@@ -371,6 +372,7 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
     ia.key16 = key16;
     ia.hist = (uint32_t *)(base + L.hist);
     ia.hist_copies = hist_copies((int64_t)BQ);
+    ia.key_rec = key_rec;
     if ((e = launch_indexer(ia, qp, s)) != hipSuccess) return hip_status(e, "v4a_indexer_topk: scores");
     SelectArgs sa{};
     sa.score_keys = ia.score_keys;
@@ -386,6 +388,7 @@ static v4a_status indexer_topk_launch(const v4a_idx *keys, const QueryPos &qp, i
     sa.meta = (int32_t *)(base + L.meta);
     sa.out = out_idx;
     sa.rec = rec;
+    sa.hist_clear = clear_after ? ia.hist : nullptr;
     return hip_status(launch_select(sa, qp, s), "v4a_indexer_topk: select");
 }
 
@@ -975,10 +978,21 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     char *tws = base + pl.sel_bytes;
     const TopkWs L = topk_layout(a->B, 1, pl.n_max, a->k);
     const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
-    hipError_t e = launch_decode_prologue(pl.key, 1, a->B, pl.entry, tws + L.hist, hist_bytes, s);
+    // MXFP4 keys of d = 128 from short gate-per-token blocks are compressed inside the scoring
+    // kernel (its latency hidden behind the scan); otherwise the prologue compresses them
+    const bool key_in_scoring = a->keys->fmt == V4A_IDX_MXFP4 && a->keys->d == 128 &&
+                                entry_two_phase(compress_params(pl.key));
+    // the histograms: cleared here unless the caller vouches that the previous call left them
+    // clear (the final selection's launch clears them for the next call)
+    const size_t clear_bytes = a->ws_clean ? 0 : hist_bytes;
+    hipError_t e = hipSuccess;
+    if (!key_in_scoring)
+        e = launch_decode_prologue(pl.key, 1, a->B, pl.entry, tws + L.hist, clear_bytes, s);
+    else if (clear_bytes)
+        e = launch_zero(tws + L.hist, clear_bytes, s);
     if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
     st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false,
-                             a->score_bf16 != 0, &pl.rec);
+                             a->score_bf16 != 0, &pl.rec, key_in_scoring ? &pl.key : nullptr, true);
     if (st != V4A_OK) return st;
     pl.at.topk = sel;
     pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;

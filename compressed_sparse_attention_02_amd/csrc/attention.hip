@@ -150,13 +150,14 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart.  A
     // split-free launch numbers (query, group of hpw heads) items from item0 instead.
     int L = blockIdx.x, hg = 0, p = L;
+    const int hpg = P.hpw ? P.hpw : 16 * (int)(blockDim.x >> 6);  // heads per workgroup
     if (P.hpw) {
         const int item = P.item0 + L, groups = P.H / P.hpw;
         hg = item % groups;
         p = (item / groups) * P.S;  // split 0 of its query (S = 1)
-    } else if (P.n_hg == 2) {
-        hg = (L >> 3) & 1;
-        p = (L >> 4) * 8 + (L & 7);
+    } else if (P.n_hg > 1) {  // n_hg a power of two
+        hg = (L >> 3) & (P.n_hg - 1);
+        p = (L >> (3 + __builtin_ctz((unsigned)P.n_hg))) * 8 + (L & 7);
     }
     const int b = p / P.S, split = p % P.S;
     if (b >= P.B) return;
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int h0 = hg * (P.hpw ? P.hpw : 64) + wv * 16;
+    const int h0 = hg * hpg + wv * 16;
     const bool wave_on = h0 < P.H;
     const int h = h0 + col;
     const int NT = blockDim.x;
@@ -744,10 +745,12 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     // order for its 16 heads either way, so the choice never changes a result.
     const int pairs = a.B * P.S;
     const bool wide = a.H > 64 && pairs >= 256;
-    P.n_hg = wide ? 1 : (a.H + 63) / 64;
-    const int waves = wide ? a.H / 16 : (a.H >= 64 ? 4 : a.H / 16);
+    const int hpg = wide ? a.H : (a.H >= 64 ? 64 : a.H);  // heads per workgroup
+    P.n_hg = 1;  // head groups per split: a power of two (groups past H have no heads)
+    while (P.n_hg * hpg < a.H) P.n_hg *= 2;
+    const int waves = hpg / 16;
     int blocks = pairs;
-    if (P.n_hg == 2) blocks = ((pairs + 7) / 8) * 16;
+    if (P.n_hg > 1) blocks = ((pairs + 7) / 8) * 8 * P.n_hg;
     if (a.D == 512) {
         if (wide)
             V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);

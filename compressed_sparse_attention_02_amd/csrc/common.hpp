@@ -293,6 +293,8 @@ struct IndexerArgs {
     float *scores;            // [B*Q][n_max] raw scores (or NULL)
     uint32_t *hist;           // [B*Q][copies][4096] histogram of the top 12 key bits (or NULL)
     int hist_copies;
+    const CompressArgs *key_rec;  // decode step: compress each query's new key (MXFP4,
+                                  // d = 128, Q = 1, two-phase entries) in the scoring kernel
 };
 hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
@@ -313,6 +315,9 @@ struct SelectArgs {
     // selection's launch (query b = sequence b, one query each; the entry is the one its
     // position completes, if any)
     const CompressArgs *rec;
+    // optional, with rec: the histograms (hist, writable), which the same extra workgroups
+    // clear after the scan, their only reader, has finished (left clear for the next call)
+    uint32_t *hist_clear;
 };
 int select_slices(int64_t n_max);
 constexpr int kSelSlice = 8192;

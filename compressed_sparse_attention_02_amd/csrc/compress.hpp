@@ -125,7 +125,7 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
 // seq: RMSNorm with the lane's weights nw, RoPE at position m*i, the record or key encoder.
 template <int VPT>
 __device__ __forceinline__ void finish_entry(const CompressParams &P, float (&acc)[VPT], const float (&nw)[VPT],
-                                             int64_t seq, int64_t i) {
+                                             int64_t seq, int64_t i, uint8_t *idx_mirror = nullptr) {
     const int lane = threadIdx.x & 63;
     const int m = P.m, D = P.D;
     const int d0 = lane * VPT;
@@ -175,7 +175,7 @@ __device__ __forceinline__ void finish_entry(const CompressParams &P, float (&ac
 
     const int64_t orow = P.out_row0 + seq * P.cap + i;
     if (P.to_idx)
-        store_mxfp4<VPT>(acc, lane, active, D, P.idx, orow);
+        store_mxfp4<VPT>(acc, lane, active, D, P.idx, orow, idx_mirror);
     else
         store_record<VPT>(acc, d0, active, D, P.R, P.kv, orow);
 }
@@ -282,6 +282,102 @@ __device__ __forceinline__ void compress_entry_wg(const CompressParams &P, float
         acc[v] = sum / den;
     }
     finish_entry<VPT>(P, acc, nw, seq, i);
+}
+
+// Two-phase form of compress_entry for short gate-per-token entries of BF16 streams (G = 1, at
+// most kRowBatchMax candidates; a ring holds exactly 2m rows), for a wavefront that has other
+// work between the two phases.  key_prefetch only issues loads (row words, gate logits, biases,
+// norm weights; no branch on a loaded value, so nothing waits for them); key_finish (the same
+// wavefront, later) merges and finishes the entry.  The arithmetic is that of compress_entry
+// step for step (same maxima, exponentials, wavefront sums and fma order), so the entry is
+// bitwise the same.
+constexpr int kRowBatchMax = 8;
+__host__ __device__ __forceinline__ bool entry_two_phase(const CompressParams &P) {
+    return P.G == 1 && P.bf16_in && (P.n_streams == 2 ? 2 * P.m : P.m) <= kRowBatchMax &&
+           (!P.ring || P.n_tok == 2 * P.m);
+}
+
+template <int VPT>
+struct KeyPrefetch {
+    uint32_t raw[kRowBatchMax][(VPT + 1) / 2];  // BF16 pairs of this lane's dims, per candidate
+    float gl, bl;                                 // gate logit and positional bias of candidate lane
+    float nw[VPT];                                // RMSNorm weights of this lane's dims
+};
+
+// Stream row of candidate c of entry i (c / m: 0 own block, 1 the B-block i - 1); a ring of 2m
+// rows holds position p at p mod 2m, which for these positions needs no division.
+__device__ __forceinline__ int64_t candidate_row2(const CompressParams &P, int64_t i, int c, int64_t tok0) {
+    const int m = P.m, s = c / m, j = c - s * m;
+    const int64_t blk = s == 0 ? i : i - 1;
+    return P.ring ? (int64_t)m * (blk & 1) + j : (int64_t)m * blk + j - tok0;
+}
+
+template <int VPT>
+__device__ __forceinline__ void key_prefetch(const CompressParams &P, int64_t seq, int64_t i, int64_t tok0,
+                                             KeyPrefetch<VPT> &kp) {
+    static_assert(VPT % 2 == 0, "BF16 pairs");
+    const int lane = threadIdx.x & 63;
+    const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
+    const int d0 = lane * VPT;  // D = 64 * VPT: every lane is active
+    const int n_cand = entry_candidates(P, i);
+#pragma unroll
+    for (int u = 0; u < kRowBatchMax; u++) {
+        const int c = min(u, n_cand - 1);
+        const uint16_t *x = (const uint16_t *)(c < P.m ? P.x0 : P.x1);
+        const uint32_t *src = (const uint32_t *)(x + x_off + candidate_row2(P, i, c, tok0) * P.D + d0);
+#pragma unroll
+        for (int w = 0; w < VPT / 2; w++) kp.raw[u][w] = src[w];
+    }
+    const int c = min(lane, n_cand - 1);
+    kp.gl = (c < P.m ? P.g0 : P.g1)[g_off + candidate_row2(P, i, c, tok0)];
+    kp.bl = (c < P.m ? P.b0 : P.b1)[c % P.m];
+#pragma unroll
+    for (int v = 0; v < VPT; v++) kp.nw[v] = 0.0f;
+    if (P.norm_w) {
+#pragma unroll
+        for (int v = 0; v < VPT; v++) kp.nw[v] = P.norm_w[d0 + v];
+    }
+}
+
+// Lane l's float, read by the whole wavefront (l a constant).
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// The candidates' weights are read lane by lane instead of with wavefront reductions: lanes
+// past the candidates hold -inf and 0, so the maximum is the candidates' maximum, and the
+// butterfly sum over 64 lanes (xor 32, 16, 8 add zeros exactly) is ((e0 + e4) + (e2 + e6)) +
+// ((e1 + e5) + (e3 + e7)), written here in that order.
+template <int VPT>
+__device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t seq, int64_t i,
+                                           uint8_t *idx_mirror) {
+    const int lane = threadIdx.x & 63;
+    const int n_cand = entry_candidates(P, i);
+    const float z = lane < n_cand ? kp.gl + kp.bl : -INFINITY;
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kRowBatchMax; u++) zmax = fmaxf(zmax, lane_value(z, u));
+    const float ex = lane < n_cand ? expf(z - zmax) : 0.0f;
+    float e[kRowBatchMax];
+#pragma unroll
+    for (int u = 0; u < kRowBatchMax; u++) e[u] = lane_value(ex, u);
+    const float den = ((e[0] + e[4]) + (e[2] + e[6])) + ((e[1] + e[5]) + (e[3] + e[7]));
+    float acc[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kRowBatchMax; u++) {
+        if (u < n_cand) {
+#pragma unroll
+            for (int v = 0; v < VPT; v++) {
+                const uint32_t w2 = kp.raw[u][v / 2];
+                acc[v] = fmaf(e[u], bf16_to_f32((uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xFFFFu))), acc[v]);
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
+    finish_entry<VPT>(P, acc, kp.nw, seq, i, idx_mirror);
 }
 
 // Kernel parameters of a checked CompressArgs (host).

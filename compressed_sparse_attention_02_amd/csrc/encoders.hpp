@@ -58,9 +58,11 @@ __device__ __forceinline__ void store_record(const float (&x)[VPT], int lane_dim
 }
 
 // MXFP4 encoding of one row held VPT values per lane (d = 64*VPT, or d = 32 with VPT = 1).
+// With `mirror` (LDS) the row's d/2 code bytes and d/32 scale bytes are also written there,
+// in the same order as in the cache row.
 template <int VPT>
 __device__ __forceinline__ void store_mxfp4(const float (&x)[VPT], int lane, bool active, int d,
-                                            const v4a_idx &out, int64_t row) {
+                                            const v4a_idx &out, int64_t row, uint8_t *mirror = nullptr) {
     if (out.fmt == V4A_IDX_F32) {
         if (active) {
             float *dst = (float *)out.codes + row * d + lane * VPT;
@@ -90,10 +92,16 @@ __device__ __forceinline__ void store_mxfp4(const float (&x)[VPT], int lane, boo
     } else {
         if (active) {
 #pragma unroll
-            for (int i = 0; i < VPT / 2; i++) dst[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
+            for (int i = 0; i < VPT / 2; i++) {
+                dst[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
+                if (mirror) mirror[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
+            }
         }
     }
-    if (active && (lane % group) == 0) out.scales[row * (d / 32) + lane / group] = (uint8_t)(X + 127);
+    if (active && (lane % group) == 0) {
+        out.scales[row * (d / 32) + lane / group] = (uint8_t)(X + 127);
+        if (mirror) mirror[d / 2 + lane / group] = (uint8_t)(X + 127);
+    }
 }
 
 }  // namespace v4a

@@ -23,7 +23,7 @@
 // score, or 16 bits of the score rounded to BF16 for the BF16 selector.  Its top 12 bits are
 // counted in a 4096-bin histogram (LDS per workgroup, then one global atomic add per
 // non-empty bin), which the top-k select uses to find the threshold bin.
-#include "common.hpp"
+#include "compress.hpp"
 
 namespace v4a {
 
@@ -48,7 +48,10 @@ struct IndexerParams {
     uint32_t *hist;        // [BQ][hist_copies][4096] or NULL
     int hist_copies;
     int groups_per_wave;   // key groups of 16 per wavefront (a multiple of kGroupsPerIter)
+    bool key_rec;          // decode step (one query per sequence, d = 128): the key that the
+    CompressParams key;    // query's newest token completes is compressed here (see below)
 };
+static_assert(sizeof(IndexerParams) + sizeof(QueryPos) <= 4096, "kernel arguments");
 
 __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64_t i, float score,
                                            uint32_t *lhist) {
@@ -82,9 +85,18 @@ __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint3
 // groups of 16 keys and processes them kGroupsPerIter at a time: every load of an iteration is issued
 // before the first MFMA (out-of-range lanes read a clamped, valid key and are masked after),
 // so kGroupsPerIter * 1 KB per wavefront is in flight.
+//
+// With key_rec (the decode step), the wavefront whose keys include the entry that the query's
+// newest token completes also compresses that entry's indexer key: it requests the candidate
+// rows before its first key batch, scores its range as usual (reading that entry's stale cache
+// row), then merges and encodes the key, writes it to the cache and, through LDS, scores it
+// with the same arithmetic, replacing the stale score before any score leaves the workgroup.
+// The key is bitwise the one the compressor kernel would write, so is its score.
+template <bool KEYREC>
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(16))) float sbuf[kMaxKeysPerWG];  // this workgroup's scores
+    __shared__ __attribute__((aligned(16))) uint8_t knew[80];           // the new key's codes + scales
     const int qi = blockIdx.y;
     const int b = qi / QP.Q;
     const int64_t n_vis = visible_keys(QP, qi);
@@ -101,6 +113,17 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     uint32_t *hist = P.hist ? lhist : nullptr;
     const int64_t wbase = k0 + (int64_t)wv * P.groups_per_wave * 16;
     const int n_it = P.groups_per_wave / kGroupsPerIter;
+
+    // the new key of this query (decode step), owned by the wavefront whose range holds it
+    int64_t i_new = -1;
+    if (KEYREC) {
+        const int64_t pos = QP.pos[qi];
+        if ((pos + 1) % P.key.m == 0) i_new = (pos + 1) / P.key.m - 1;
+    }
+    const int64_t wend = wbase + (int64_t)P.groups_per_wave * 16;
+    const bool own = KEYREC && i_new >= wbase && i_new < (wend < kend ? wend : kend);  // uniform over the wavefront
+    KeyPrefetch<2> kp;
+    if (own) key_prefetch<2>(P.key, qi, i_new, (int64_t)P.key.m * (i_new - 1), kp);
 
     // Double-buffered: the loads of iteration it+1 are issued before iteration it is computed.
     // Lanes past the end read a clamped, valid key of this query and are masked afterwards.
@@ -151,32 +174,34 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     }
     __syncthreads();
 
+    // fma chain grp of key col of a group (codes kdu, the key's four scale bytes kscu)
+    auto key_chain = [&](const uint4 &kdu, uint32_t kscu) -> float {
+        const v8i kb = v8i{(int)kdu.x, (int)kdu.y, (int)kdu.z, (int)kdu.w, 0, 0, 0, 0};
+        const int sc = (int)((kscu >> (8 * grp)) & 0xFFu);
+        v4f acc[4];
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+            acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                                                                      qscale[g], 0, sc);
+        // ReLU on the bit pattern: a finite float is negative (or -0) exactly when its bits
+        // read as a negative int, so max(int bits, 0) gives s for s > 0 and +0 otherwise
+        float cu = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float si = acc[g][i];  // a scalar copy: bit casts read whole objects
+                const float r = __builtin_bit_cast(float, max(__builtin_bit_cast(int, si), 0));
+                cu = fmaf(wt[g][i], r, cu);
+            }
+        }
+        return cu;
+    };
     auto compute_iter = [&](int it, const uint4 (&kd)[kGroupsPerIter], const uint32_t (&ksc)[kGroupsPerIter]) {
         const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
         float c[kGroupsPerIter];
 #pragma unroll
-        for (int u = 0; u < kGroupsPerIter; u++) {
-            const v8i kb = v8i{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
-            const int sc = (int)((ksc[u] >> (8 * grp)) & 0xFFu);
-            v4f acc[4];
-#pragma unroll
-            for (int g = 0; g < 4; g++)
-                acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
-                                                                          qscale[g], 0, sc);
-            // ReLU on the bit pattern: a finite float is negative (or -0) exactly when its bits
-            // read as a negative int, so max(int bits, 0) gives s for s > 0 and +0 otherwise
-            float cu = 0.0f;
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const float si = acc[g][i];  // a scalar copy: bit casts read whole objects
-                    const float r = __builtin_bit_cast(float, max(__builtin_bit_cast(int, si), 0));
-                    cu = fmaf(wt[g][i], r, cu);
-                }
-            }
-            c[u] = cu;
-        }
+        for (int u = 0; u < kGroupsPerIter; u++) c[u] = key_chain(kd[u], ksc[u]);
         // the four chains of each key sit in lanes col, col+16, col+32, col+48
         float c1[kGroupsPerIter], c2[kGroupsPerIter], c3[kGroupsPerIter];
 #pragma unroll
@@ -203,6 +228,17 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         const bool more2 = it + 2 < n_it && wbase + (int64_t)(it + 2) * kGroupsPerIter * 16 < kend;
         if (more2) load_iter(it + 2, kdA, kscA);
         compute_iter(it + 1, kdB, kscB);
+    }
+    if (own) {
+        key_finish<2>(P.key, kp, qi, i_new, knew);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // every key column of the group holds the new key; the chains meet as in compute_iter
+        const float c = key_chain(*(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64));
+        float sc = ((lane_value(c, 0) + lane_value(c, 16)) + lane_value(c, 32)) + lane_value(c, 48);
+        if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
+        if (lane == 0) sbuf[i_new - k0] = sc;
     }
     // the streaming loop touched only registers and LDS; now the scores leave in 16-byte stores
     // and the histogram is counted from LDS
@@ -331,6 +367,11 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     P.scores = a.scores;
     P.hist = a.hist;
     P.hist_copies = a.hist_copies > 0 ? a.hist_copies : 1;
+    P.key_rec = a.key_rec != nullptr;
+    if (a.key_rec) {
+        P.key = compress_params(*a.key_rec);
+        if (!mx || P.d != 128 || a.Q != 1 || !entry_two_phase(P.key)) return hipErrorInvalidValue;
+    }
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
     if (mx) {
@@ -343,7 +384,10 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
         P.groups_per_wave = gpw;
         const int64_t kpw = (int64_t)64 * gpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
-        V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel, grid, dim3(256), 0, s, P, qp);
+        if (P.key_rec)
+            V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel<true>, grid, dim3(256), 0, s, P, qp);
+        else
+            V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel<false>, grid, dim3(256), 0, s, P, qp);
     } else {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
         V4A_LAUNCH("indexer_f32_kernel", indexer_f32_kernel, grid, dim3(256), 0, s, P, qp);

@@ -51,6 +51,8 @@ struct SelParams {
     int32_t *out;
     CompressParams rec;      // entry records of the decode step (n_rec > 0)
     int n_rec;               // extra workgroups of the final launch: one per sequence
+    uint4 *hist_clear;       // with n_rec: the histograms, cleared by those workgroups
+    int hist_n16;            // 16-byte words of one query's histograms
 };
 
 // Block-wide inclusive prefix sum of one value per thread (thread order); `total` gets the
@@ -207,7 +209,8 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
 // With n_rec > 0 the launch also carries the decode step's record compression: workgroup
 // BQ + b compresses, with its first wavefront, the entry record that sequence b's newest token
 // completes (one query per sequence), overlapping the selection; attention reads the records
-// after this launch.
+// after this launch.  Its other wavefronts clear query b's histograms (hist_clear): the scan
+// kernel, their only reader, has finished, and the next call finds them clear.
 __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, QueryPos QP) {
     __shared__ uint32_t wsum[kSelWaves];
     __shared__ int sT;
@@ -218,8 +221,14 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     __shared__ uint32_t soff[kMaxSlices + 1];
     const int BQ = (int)gridDim.x - P.n_rec;
     if ((int)blockIdx.x >= BQ) {
-        if (threadIdx.x >= 64) return;  // one wavefront per record
         const int b = (int)blockIdx.x - BQ;
+        if (threadIdx.x >= 64) {  // one wavefront per record; the others clear the histograms
+            if (P.hist_clear) {
+                uint4 *h = P.hist_clear + (int64_t)b * P.hist_n16;
+                for (int j = (int)threadIdx.x - 64; j < P.hist_n16; j += kSelThreads - 64) h[j] = make_uint4(0, 0, 0, 0);
+            }
+            return;
+        }
         const int64_t pos = QP.pos[b];
         const int m = P.rec.m;
         if ((pos + 1) % m != 0) return;  // no block completed
@@ -385,6 +394,10 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
         if (qp.Q != 1) return hipErrorInvalidValue;
         P.rec = compress_params(*a.rec);
         P.n_rec = a.BQ;
+        P.hist_clear = (uint4 *)a.hist_clear;
+        P.hist_n16 = P.copies * kHistBins / 4;
+    } else if (a.hist_clear) {
+        return hipErrorInvalidValue;
     }
     V4A_LAUNCH("select_final_kernel", select_final_kernel, dim3((unsigned)(a.BQ + P.n_rec)), dim3(kSelThreads), 0, s, P, qp);
     return hipGetLastError();

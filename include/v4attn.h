@@ -317,9 +317,11 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * + v4a_indexer_topk (Q = 1) + v4a_decode_csa with the same arguments.  For every sequence b
  * whose newest token t = q_pos[b] completes a block ((t+1) % m == 0), entry (t+1)/m - 1 is
  * compressed into the record cache and the key cache; then the top-k of its visible entries
- * (n_entries[b] cached) are selected and attended over with the window and the sink.  The
- * key compression and the selection's histogram clear share one launch; the record
- * compression runs in the final selection's launch.
+ * (n_entries[b] cached) are selected and attended over with the window and the sink.  MXFP4
+ * keys of d = 128 from BF16 streams with one gate per token and 2m <= 8 are compressed by the
+ * scoring kernel itself (bitwise the key v4a_compress_csa writes); other keys by a first
+ * launch.  The record compression runs in the final selection's launch, which also clears the
+ * selection's histograms for the next call (see ws_clean).
  * [cyqw] section 3.5 (the state cache keeps the incomplete block; a completed block becomes a
  * compressed entry) and the sections cited at the calls it composes.
  * Stream rows: every stream holds [B][2m] rows per sequence, the B-block before the completed
@@ -340,6 +342,11 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * becomes x_d * q_norm_w[d] / sqrt(mean(x^2) + 1e-6), its last R dims are rotated at the
  * query position (interleaved pairs, as the entries are), and the result enters the products
  * rounded to BF16 (nearest even).  Without it q arrives normalised and rotated.
+ * ws_clean != 0 promises that the workspace's selection histograms are already clear: the
+ * workspace was last used by a v4a_decode_step_csa call with the same B and k, and nothing
+ * has written it since.  The call then skips clearing them (one launch fewer).  Every call
+ * leaves them clear, so a caller that keeps one workspace per (B, k) for its decode loop may
+ * pass ws_clean = 1 from the second step on.  With ws_clean = 0 the call clears them itself.
  * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
  * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
 typedef struct {
@@ -377,6 +384,7 @@ typedef struct {
     int32_t ring;                /* nonzero: the streams and the window are rings (see above)    */
     int32_t no_split;            /* nonzero: split-free attention (see below)                   */
     const float *q_norm_w;       /* [D] f32 (device, 16-byte aligned) or NULL: see below         */
+    int32_t ws_clean;            /* nonzero: the workspace's histograms are clear (see above)   */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,

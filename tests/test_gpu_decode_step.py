@@ -26,15 +26,18 @@ def clone_idx(ix):
     return v4.Idx(ix.fmt, ix.d, ix.codes.clone(), ix.scales.clone(), ix.cap)
 
 
-@pytest.mark.parametrize("score_bf16,norm", [(False, False), (True, False), (False, True)],
-                         ids=["f32_scores", "bf16_scores", "rmsnorm"])
-def test_fused_step_equals_separate_calls(score_bf16, norm):
+@pytest.mark.parametrize("score_bf16,norm,key_gate_dim", [(False, False, False), (True, False, False),
+                                                          (False, True, False), (False, False, True)],
+                         ids=["f32_scores", "bf16_scores", "rmsnorm", "key_gate_per_dim"])
+def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
+    """With one gate per token the new indexer keys are compressed inside the scoring kernel
+    (the step starts with a histogram clear); with a gate per dim the prologue compresses them."""
     seed, m, D, R, H, HI, dI, k, W = 4242, 4, 512, 64, 128, 64, 128, 512, 128
     q_pos = [4003, 4001, 3, 8191]            # completes entry 1000 / none / entry 0 / entry 2047
     B, cap = len(q_pos), 2304
     n_ent = [(p + 1) // m for p in q_pos]
     entry = [(p + 1) // m - 1 if (p + 1) % m == 0 else -1 for p in q_pos]
-    announce(f"fused decode step: q_pos={q_pos} score_bf16={score_bf16} norm={norm}")
+    announce(f"fused decode step: q_pos={q_pos} score_bf16={score_bf16} norm={norm} key_gate_dim={key_gate_dim}")
     gnw = np.random.default_rng(seed + 1)
     nw = f32(0.5 + gnw.random(D)) if norm else None
     nwi = f32(0.5 + gnw.random(dI)) if norm else None
@@ -47,8 +50,11 @@ def test_fused_step_equals_separate_calls(score_bf16, norm):
     bits = {n: to_bf16_bits(normal(seed, n, (B, 2 * m, D if n.startswith("kv") else dI)))
             for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
     dev = {n: bf16_from_bits(v) for n, v in bits.items()}
-    gates = {n: f32(normal(seed, n, (B, 2 * m, 1))) for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
-    bias = {n: f32(normal(seed, n, (m, 1))) for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
+    gi = dI if key_gate_dim else 1
+    gates = {n: f32(normal(seed, n, (B, 2 * m, gi if n.startswith("idx") else 1)))
+             for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
+    bias = {n: f32(normal(seed, n, (m, gi if n.startswith("idx") else 1)))
+            for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
     w = f32(normal(seed, "w", (B, HI)))
     q = bf16_from_bits(to_bf16_bits(normal(seed, "q", (B, H, D))))
     win = bf16_from_bits(to_bf16_bits(normal(seed, "window", (B, W, D))))
@@ -57,23 +63,29 @@ def test_fused_step_equals_separate_calls(score_bf16, norm):
     scale = 1.0 / math.sqrt(D)
 
     # the fused call
+    def step_args(kv_, keys_, out_, ws_clean=False):
+        return v4.DecodeStepArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=dev["kv_a"], kv_b=dev["kv_b"],
+                                 gate_a=gates["gate_a"], gate_b=gates["gate_b"], bias_a=bias["bias_a"],
+                                 bias_b=bias["bias_b"], idx_a=dev["idx_a"], idx_b=dev["idx_b"],
+                                 idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
+                                 idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv_, keys=keys_,
+                                 q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
+                                 softmax_scale=scale, out=out_, score_bf16=score_bf16, norm_w=nw, idx_norm_w=nwi,
+                                 ws_clean=ws_clean)
+
     kv1, keys1 = clone_kv(kv), clone_idx(keys)
     out1 = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
-    args = v4.DecodeStepArgs(q_pos=q_pos, n_entries=n_ent, m=m, kv_a=dev["kv_a"], kv_b=dev["kv_b"],
-                             gate_a=gates["gate_a"], gate_b=gates["gate_b"], bias_a=bias["bias_a"],
-                             bias_b=bias["bias_b"], idx_a=dev["idx_a"], idx_b=dev["idx_b"],
-                             idx_gate_a=gates["idx_gate_a"], idx_gate_b=gates["idx_gate_b"],
-                             idx_bias_a=bias["idx_bias_a"], idx_bias_b=bias["idx_bias_b"], kv=kv1, keys=keys1,
-                             q_idx=qi, w=w, k=k, q=q, win=win, win_len=win_len, W=W, sink=sink,
-                             softmax_scale=scale, out=out1, score_bf16=score_bf16, norm_w=nw, idx_norm_w=nwi)
+    args = step_args(kv1, keys1, out1)
     ws1 = v4.workspace(v4.v4a_decode_step_workspace(args))
+    ws1.fill_(0x55)  # without ws_clean the call clears what it needs
     # timed: the call's kernels in launch order, each with a positive duration
     v4.v4a_trace_begin(16)
     v4.v4a_decode_step_csa(args, ws1)
     n = v4.v4a_trace_end()
     torch.cuda.synchronize()
     kernels = v4.trace_kernels(n)
-    assert [name for name, _ in kernels] == ["decode_prologue_kernel", "indexer_mxfp4_kernel", "select_scan_kernel",
+    first = "decode_prologue_kernel" if key_gate_dim else "zero_kernel"
+    assert [name for name, _ in kernels] == [first, "indexer_mxfp4_kernel", "select_scan_kernel",
                                              "select_final_kernel", "attn_mfma_kernel", "attn_combine_kernel"], kernels
     assert all(ms > 0 for _, ms in kernels), kernels
 
@@ -102,6 +114,21 @@ def test_fused_step_equals_separate_calls(score_bf16, norm):
         assert torch.equal(a, c)
     assert not torch.equal(kv1.nope, kv.nope)   # the completing sequences did write entries
     assert torch.equal(out1, out2)
+    # the fused call keeps its selection at the start of its workspace: the same top-k
+    assert torch.equal(ws1[:B * k * 4].view(torch.int32).view(B, k), sel.view(B, k))
+    # and its histograms right after, which it leaves clear; a second call that relies on that
+    # (ws_clean) writes the same caches and output with one launch fewer
+    h0 = (B * k * 4 + 255) // 256 * 256
+    assert not ws1[h0:h0 + B * 8 * 4096 * 4].any()
+    kv3, keys3 = clone_kv(kv), clone_idx(keys)
+    out3 = torch.empty_like(out1)
+    v4.v4a_trace_begin(16)
+    v4.v4a_decode_step_csa(step_args(kv3, keys3, out3, ws_clean=True), ws1)
+    n3 = v4.v4a_trace_end()
+    torch.cuda.synchronize()
+    assert [name for name, _ in v4.trace_kernels(n3)] == [name for name, _ in kernels][(0 if key_gate_dim else 1):]
+    assert torch.equal(out3, out1) and torch.equal(keys3.codes, keys1.codes) and torch.equal(kv3.nope, kv1.nope)
+    assert not ws1[h0:h0 + B * 8 * 4096 * 4].any()
 
     # sequence 0 against the oracle, fed the caches the GPU wrote
     b = 0
