@@ -103,6 +103,10 @@ CompressParams compress_params(const CompressArgs &a) {
     P.n_tok = a.n_tok;
     P.norm_w = a.norm_w;
     P.ring = a.ring;
+    // one vector load per lane and row needs the streams aligned to the lane's VPT values
+    const int vpt = a.D >= 64 ? a.D / 64 : 1;
+    const uintptr_t need = (uintptr_t)std::min(16, vpt * (a.bf16_in ? 2 : 4));
+    P.vec_in = ((uintptr_t)a.x[0] % need) == 0 && (a.n_streams < 2 || ((uintptr_t)a.x[1] % need) == 0);
     return P;
 }
 

@@ -26,6 +26,7 @@ struct CompressParams {
     int64_t n_tok;
     const float *norm_w;  // [D] or NULL
     bool ring;            // stream rows are a ring: position p at row p mod n_tok
+    bool vec_in;          // the streams are aligned for one vector load per lane and row
 };
 
 template <int VPT>
@@ -58,38 +59,140 @@ __device__ __forceinline__ int64_t candidate_row(const CompressParams &P, int64_
     return P.ring ? pos % P.n_tok : pos - tok0;
 }
 
+// A uniform pointer held in scalar registers (read lane by lane), so that choosing between two
+// kernel-argument pointers stays a choice of register values instead of becoming a load of
+// the argument block at a computed address ahead of every row load.
+template <typename T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return (const T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The streams of one entry's candidates: per stream (0: block i, 1: B-block i-1) the first
+// element of this sequence's rows, its gates and biases, and the stream row of the block's
+// first token; candidate c = s*m + j sits at row base[s] + j (wrapped once in a ring, whose
+// n_tok >= m rows hold a block).
+struct EntryStreams {
+    const char *x[2];
+    const float *g[2], *b[2];
+    int64_t base[2];
+    int m;
+    int64_t n_tok;
+    bool ring;
+    __device__ __forceinline__ EntryStreams(const CompressParams &P, int64_t seq, int64_t i, int64_t tok0) {
+        const int esz = P.bf16_in ? 2 : 4;
+        x[0] = uniform_ptr((const char *)P.x0) + seq * P.n_tok * P.D * esz;
+        x[1] = P.n_streams == 2 ? uniform_ptr((const char *)P.x1) + seq * P.n_tok * P.D * esz : x[0];
+        g[0] = uniform_ptr(P.g0) + seq * P.n_tok * P.G;
+        g[1] = P.n_streams == 2 ? uniform_ptr(P.g1) + seq * P.n_tok * P.G : g[0];
+        b[0] = uniform_ptr(P.b0);
+        b[1] = P.n_streams == 2 ? uniform_ptr(P.b1) : b[0];
+        m = P.m;
+        n_tok = P.n_tok;
+        ring = P.ring;
+        for (int st = 0; st < 2; st++) {
+            const int64_t pos = (int64_t)m * (st == 0 ? i : i - 1);
+            base[st] = ring ? (pos >= 0 ? pos % n_tok : 0) : pos - tok0;
+        }
+    }
+    __device__ __forceinline__ int64_t row(int c) const {
+        const int s = c >= m ? 1 : 0, j = c - s * m;
+        int64_t r = base[s] + j;
+        if (ring && r >= n_tok) r -= n_tok;
+        return r;
+    }
+};
+
+// One candidate row's VPT values of this lane as raw words: BF16 pairs (VPT/2 words, or one
+// zero-extended value for VPT = 1) or fp32 bits; converted at use, so the loads of a batch
+// of rows are all in flight before the first value is needed.
+template <int VPT>
+__device__ __forceinline__ void load_raw(const char *p, bool bf16, bool vec, uint32_t (&w)[VPT]) {
+    if (bf16) {
+        if constexpr (VPT == 1) {
+            w[0] = *(const uint16_t *)p;
+        } else if (vec) {
+            if constexpr (VPT == 8) {
+                const uint4 q = *(const uint4 *)p;
+                w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+            } else if constexpr (VPT == 4) {
+                const uint2 q = *(const uint2 *)p;
+                w[0] = q.x; w[1] = q.y;
+            } else {
+                w[0] = *(const uint32_t *)p;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < VPT; v += 2)
+                w[v / 2] = (uint32_t)((const uint16_t *)p)[v] | ((uint32_t)((const uint16_t *)p)[v + 1] << 16);
+        }
+    } else {
+        if (vec && VPT % 4 == 0) {
+#pragma unroll
+            for (int v = 0; v < VPT; v += 4) {
+                const uint4 q = *(const uint4 *)(p + 4 * v);
+                w[v] = q.x; w[v + 1] = q.y; w[v + 2] = q.z; w[v + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < VPT; v++) w[v] = ((const uint32_t *)p)[v];
+        }
+    }
+}
+template <int VPT>
+__device__ __forceinline__ float raw_value(const uint32_t (&w)[VPT], bool bf16, int v) {
+    if (!bf16) return bitsf(w[v]);
+    if constexpr (VPT == 1) return bf16_to_f32((uint16_t)w[0]);
+    return bf16_to_f32((uint16_t)((v & 1) ? (w[v / 2] >> 16) : (w[v / 2] & 0xFFFFu)));
+}
+
 // Gate-per-token merge (G = 1) by one wavefront: the softmax weights of all candidates of entry i
 // go to wsh (exp(z - max), computed once per wavefront: lane c holds candidate c, c + 64, ...)
 // and their sum is returned; candidates [c_begin, c_end) are accumulated into acc in order.
-// Candidate rows are loaded in batches of kRowBatch, the first batch issued before the gate
-// logits so the two memory round trips overlap.
+// Candidate rows are loaded in batches of kRowBatch as raw words, the first batch issued
+// before the gate logits and each next batch before the current one is accumulated.
 template <int VPT>
 __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
                                              int64_t tok0, int c_begin, int c_end, float (&acc)[VPT]) {
     const int lane = threadIdx.x & 63;
-    const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
-    const int m = P.m, D = P.D;
+    const int D = P.D;
     const int d0 = lane * VPT;
     const bool active = d0 < D;
+    const int esz = P.bf16_in ? 2 : 4;
+    const int64_t lane_off = (int64_t)(active ? d0 : 0) * esz;  // inactive lanes read dim 0
     const int n_cand = entry_candidates(P, i);
+    const EntryStreams es(P, seq, i, tok0);
     constexpr int kRowBatch = 8;
-    float xb[kRowBatch][VPT];
+    uint32_t xb[kRowBatch][VPT];
     auto load_batch = [&](int c0) {
 #pragma unroll
         for (int u = 0; u < kRowBatch; u++) {
             const int c = min(c0 + u, c_end - 1);
-            const int s = c / m;
-            load_row<VPT>(s == 0 ? P.x0 : P.x1, P.bf16_in, candidate_row(P, i, c, tok0), D, d0, active, xb[u],
-                          x_off);
+            load_raw<VPT>(es.x[c >= es.m ? 1 : 0] + es.row(c) * D * esz + lane_off, P.bf16_in, P.vec_in, xb[u]);
         }
     };
     if (c_begin < c_end) load_batch(c_begin);
+    // gate logits of this lane's candidates (up to kMaxCand / 64), all requested before use
+    constexpr int kPerLane = kMaxCand / 64;
+    float gl[kPerLane], bl[kPerLane];
+#pragma unroll
+    for (int r = 0; r < kPerLane; r++) {
+        const int c = min(lane + 64 * r, n_cand - 1);
+        const int s = c >= es.m ? 1 : 0;
+        gl[r] = es.g[s][es.row(c)];
+        bl[r] = es.b[s][c - s * es.m];
+    }
     float zmax = -INFINITY;
-    for (int c = lane; c < n_cand; c += 64) {
-        const int s = c / m, j = c % m;
-        const float z = (s == 0 ? P.g0 : P.g1)[g_off + candidate_row(P, i, c, tok0)] + (s == 0 ? P.b0 : P.b1)[j];
-        wsh[c] = z;
-        zmax = fmaxf(zmax, z);
+#pragma unroll
+    for (int r = 0; r < kPerLane; r++) {
+        const int c = lane + 64 * r;
+        if (c < n_cand) {
+            const float z = gl[r] + bl[r];
+            wsh[c] = z;
+            zmax = fmaxf(zmax, z);
+        }
     }
     zmax = wave_max(zmax);
     float den = 0.0f;
@@ -103,7 +206,7 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int c0 = c_begin; c0 < c_end; c0 += kRowBatch) {
-        float cur[kRowBatch][VPT];
+        uint32_t cur[kRowBatch][VPT];
 #pragma unroll
         for (int u = 0; u < kRowBatch; u++)
 #pragma unroll
@@ -114,7 +217,7 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
             if (c0 + u < c_end) {
                 const float wgt = wsh[c0 + u];
 #pragma unroll
-                for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, cur[u][v], acc[v]);
+                for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, active ? raw_value<VPT>(cur[u], P.bf16_in, v) : 0.0f, acc[v]);
             }
         }
     }
@@ -293,7 +396,7 @@ __device__ __forceinline__ void compress_entry_wg(const CompressParams &P, float
 // bitwise the same.
 constexpr int kRowBatchMax = 8;
 __host__ __device__ __forceinline__ bool entry_two_phase(const CompressParams &P) {
-    return P.G == 1 && P.bf16_in && (P.n_streams == 2 ? 2 * P.m : P.m) <= kRowBatchMax &&
+    return P.G == 1 && P.bf16_in && P.vec_in && (P.n_streams == 2 ? 2 * P.m : P.m) <= kRowBatchMax &&
            (!P.ring || P.n_tok == 2 * P.m);
 }
 
