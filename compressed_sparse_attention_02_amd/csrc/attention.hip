@@ -250,6 +250,51 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 
     constexpr int NSEG = D / 8;          // 8-dim segments per key row
     constexpr int NTASK = 8 * NSEG;      // (4-key group, segment) staging tasks per tile
+    // LDS writes of one staging task: keys 4kg..4kg+3 as BF16 (v), key-major into Er and
+    // dim-major into Ec; the task of segment 0 also writes the keys' scales and validity
+    auto store_task = [&](int task, uint4 (&v)[4], const bool (&valid)[4], const float (&scl)[4]) {
+        const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
+        if (seg == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                ksc[4 * kg + j] = scl[j];
+                kvalid[4 * kg + j] = valid[j] ? 1 : 0;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (!valid[j]) v[j] = make_uint4(0, 0, 0, 0);
+            // 16-byte chunk seg of key row r sits at chunk seg ^ ((r >> 3) & 3): the eight
+            // rows 4kg + j written together then fall in distinct LDS banks
+            const int r = 4 * kg + j;
+            *(uint4 *)(Er + r * kErStride + 8 * (seg ^ ((r >> 3) & 3))) = v[j];
+        }
+        // dim-major: row dim+d holds keys 4kg..4kg+3
+#pragma unroll
+        for (int d = 0; d < 8; d++) {
+            const int sh = (d & 1) ? 16 : 0;
+            uint32_t w0, w1, w2, w3;
+            switch (d >> 1) {
+                case 0: w0 = v[0].x; w1 = v[1].x; w2 = v[2].x; w3 = v[3].x; break;
+                case 1: w0 = v[0].y; w1 = v[1].y; w2 = v[2].y; w3 = v[3].y; break;
+                case 2: w0 = v[0].z; w1 = v[1].z; w2 = v[2].z; w3 = v[3].z; break;
+                default: w0 = v[0].w; w1 = v[1].w; w2 = v[2].w; w3 = v[3].w; break;
+            }
+            // the 16-bit halves (low for even d, high for odd d) of keys 4kg..4kg+3, paired
+            const uint32_t sel = sh ? 0x07060302u : 0x05040100u;
+            const uint32_t a0 = __builtin_amdgcn_perm(w1, w0, sel);
+            const uint32_t a1 = __builtin_amdgcn_perm(w3, w2, sel);
+            *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
+        }
+    };
+    auto fp8x8_to_bf16 = [](uint2 c) -> uint4 {  // E4M3 codes are exact in BF16
+        uint4 v;
+        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
+        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
+        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
+        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
+        return v;
+    };
     for (int tb = kb0; tb < kb1; tb += kTile) {
         __syncthreads();
         // ---- staging.  Task (kg, seg): keys 4kg..4kg+3, dims 8seg..8seg+7.  All loads of a
@@ -259,6 +304,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
             const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
             uint4 v[4];
             bool valid[4];
+            float scl[4];
             if (kind == 0) {
                 int64_t row[4];
 #pragma unroll
@@ -273,23 +319,13 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 #pragma unroll
                     for (int j = 0; j < 4; j++) c[j] = *(const uint2 *)(P.nope + row[j] * Dn + dim);
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        v[j].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].x, 1.0f, false));
-                        v[j].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].x, 1.0f, true));
-                        v[j].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].y, 1.0f, false));
-                        v[j].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j].y, 1.0f, true));
-                    }
+                    for (int j = 0; j < 4; j++) v[j] = fp8x8_to_bf16(c[j]);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)(P.rope + row[j] * R + (dim - Dn));
                 }
-                if (seg == 0) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        ksc[4 * kg + j] = P.kscale[row[j]];
-                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
-                    }
-                }
+                for (int j = 0; j < 4; j++) scl[j] = seg == 0 ? P.kscale[row[j]] : 0.0f;
             } else if (kind == 1) {
                 int64_t row[4];
 #pragma unroll
@@ -300,19 +336,14 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 }
 #pragma unroll
                 for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
-                if (seg == 0) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        ksc[4 * kg + j] = 1.0f;
-                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
-                    }
-                }
+                for (int j = 0; j < 4; j++) scl[j] = 1.0f;
             } else {
                 // a tile holding the last entries and the first window tokens: per key
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const int kidx = tb + 4 * kg + j;
-                    float scl = 0.0f;
+                    scl[j] = 0.0f;
                     v[j] = make_uint4(0, 0, 0, 0);
                     valid[j] = false;
                     if (kidx < n_ent) {
@@ -320,53 +351,20 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                         if (e >= 0 && e < P.cap) {
                             const int64_t row = (int64_t)b * P.kv_bstride + e;
                             valid[j] = true;
-                            scl = P.kscale[row];
-                            if (dim < Dn) {
-                                const uint2 c = *(const uint2 *)(P.nope + row * Dn + dim);
-                                v[j].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
-                                v[j].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
-                                v[j].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
-                                v[j].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
-                            } else {
+                            scl[j] = P.kscale[row];
+                            if (dim < Dn)
+                                v[j] = fp8x8_to_bf16(*(const uint2 *)(P.nope + row * Dn + dim));
+                            else
                                 v[j] = *(const uint4 *)(P.rope + row * R + (dim - Dn));
-                            }
                         }
                     } else if (kidx < kb1) {
                         valid[j] = true;
-                        scl = 1.0f;
+                        scl[j] = 1.0f;
                         v[j] = *(const uint4 *)((const uint16_t *)P.win + wr.row(kidx - n_ent) * D + dim);
                     }
-                    if (seg == 0) {
-                        ksc[4 * kg + j] = scl;
-                        kvalid[4 * kg + j] = valid[j] ? 1 : 0;
-                    }
                 }
             }
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if (!valid[j]) v[j] = make_uint4(0, 0, 0, 0);
-                // 16-byte chunk seg of key row r sits at chunk seg ^ ((r >> 3) & 3): the eight
-                // rows 4kg + j written together then fall in distinct LDS banks
-                const int r = 4 * kg + j;
-                *(uint4 *)(Er + r * kErStride + 8 * (seg ^ ((r >> 3) & 3))) = v[j];
-            }
-            // dim-major: row dim+d holds keys 4kg..4kg+3
-#pragma unroll
-            for (int d = 0; d < 8; d++) {
-                const int sh = (d & 1) ? 16 : 0;
-                uint32_t w0, w1, w2, w3;
-                switch (d >> 1) {
-                    case 0: w0 = v[0].x; w1 = v[1].x; w2 = v[2].x; w3 = v[3].x; break;
-                    case 1: w0 = v[0].y; w1 = v[1].y; w2 = v[2].y; w3 = v[3].y; break;
-                    case 2: w0 = v[0].z; w1 = v[1].z; w2 = v[2].z; w3 = v[3].z; break;
-                    default: w0 = v[0].w; w1 = v[1].w; w2 = v[2].w; w3 = v[3].w; break;
-                }
-                // the 16-bit halves (low for even d, high for odd d) of keys 4kg..4kg+3, paired
-                const uint32_t sel = sh ? 0x07060302u : 0x05040100u;
-                const uint32_t a0 = __builtin_amdgcn_perm(w1, w0, sel);
-                const uint32_t a1 = __builtin_amdgcn_perm(w3, w2, sel);
-                *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
-            }
+            store_task(task, v, valid, scl);
         }
         __syncthreads();
         if (!wave_on) continue;

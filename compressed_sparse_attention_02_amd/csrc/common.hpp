@@ -163,7 +163,7 @@ bool trace_claim(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
 // so every call stays asynchronous and capturable).
 constexpr int kMaxSeq = 128;
 constexpr int kHistBins = 4096;   // top-12-bit histogram of the orderable score keys
-constexpr int kHistCopies = 8;    // copies of each query's histogram (contention spreading)
+constexpr int kHistCopies = 2;    // copies of each query's histogram (contention spreading)
 
 // Histogram copies per query: many workgroups score one decode query and spread their adds
 // over kHistCopies copies; a prefill chunk has few workgroups per query and keeps one copy.

@@ -147,8 +147,8 @@ __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, Q
     {
         const uint32_t *h = P.hist + (int64_t)qi * P.copies * kHistBins + kBPT * t;
         uint4 a = *(const uint4 *)h, b = *(const uint4 *)(h + 4);
-        if (P.copies > 1) {
-            uint4 ha[kHistCopies - 1], hb[kHistCopies - 1];
+        if (kHistCopies > 1 && P.copies > 1) {
+            uint4 ha[kHistCopies > 1 ? kHistCopies - 1 : 1], hb[kHistCopies > 1 ? kHistCopies - 1 : 1];
 #pragma unroll
             for (int cp = 1; cp < kHistCopies; cp++) {
                 ha[cp - 1] = *(const uint4 *)(h + cp * kHistBins);

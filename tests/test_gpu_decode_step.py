@@ -17,6 +17,8 @@ from workloads import bf16_bits_to_f64, normal, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
+HIST_COPIES = 2  # histogram copies per decode query in the step's workspace (kHistCopies)
+
 
 def clone_kv(kv):
     return v4.KV(kv.fmt, kv.D, kv.R, kv.nope.clone(), kv.rope.clone(), kv.scale.clone(), kv.cap)
@@ -119,7 +121,7 @@ def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
     # and its histograms right after, which it leaves clear; a second call that relies on that
     # (ws_clean) writes the same caches and output with one launch fewer
     h0 = (B * k * 4 + 255) // 256 * 256
-    assert not ws1[h0:h0 + B * 8 * 4096 * 4].any()
+    assert not ws1[h0:h0 + B * HIST_COPIES * 4096 * 4].any()
     kv3, keys3 = clone_kv(kv), clone_idx(keys)
     out3 = torch.empty_like(out1)
     v4.v4a_trace_begin(16)
@@ -128,7 +130,7 @@ def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
     torch.cuda.synchronize()
     assert [name for name, _ in v4.trace_kernels(n3)] == [name for name, _ in kernels][(0 if key_gate_dim else 1):]
     assert torch.equal(out3, out1) and torch.equal(keys3.codes, keys1.codes) and torch.equal(kv3.nope, kv1.nope)
-    assert not ws1[h0:h0 + B * 8 * 4096 * 4].any()
+    assert not ws1[h0:h0 + B * HIST_COPIES * 4096 * 4].any()
 
     # sequence 0 against the oracle, fed the caches the GPU wrote
     b = 0
