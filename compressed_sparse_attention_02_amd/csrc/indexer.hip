@@ -68,10 +68,17 @@ __device__ __forceinline__ void emit_score(const IndexerParams &P, int qi, int64
     }
 }
 
+// Workgroup barrier that orders LDS only: each wavefront waits for its own LDS operations, not
+// for its global stores, whose latency then overlaps what follows.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Adds the workgroup's LDS histogram into copy (blockIdx.x % hist_copies) of the query's
-// global histogram; spreading the copies keeps many workgroups off the same hot bins.
+// global histogram; spreading the copies keeps many workgroups off the same hot bins.  The
+// score stores before it need not have completed.
 __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint32_t *lhist) {
-    __syncthreads();
+    lds_barrier();
     if (!P.hist) return;
     uint32_t *gh = P.hist + ((int64_t)qi * P.hist_copies + (int)(blockIdx.x % (unsigned)P.hist_copies)) * kHistBins;
     for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
