@@ -480,7 +480,18 @@ __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<
     }
 #pragma unroll
     for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
-    finish_entry<VPT>(P, acc, kp.nw, seq, i, idx_mirror);
+    // finish_entry's steps for an indexer key (RMSNorm if any, no RoPE, MXFP4), without its
+    // other branches: this runs once per query in a kernel whose other wavefronts never do
+    if (P.norm_w) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; v++) ss = fmaf(acc[v], acc[v], ss);
+        ss = __shfl(wave_sum(ss), 0);
+        const float r = 1.0f / sqrtf(ss / (float)P.D + kNormEps);
+#pragma unroll
+        for (int v = 0; v < VPT; v++) acc[v] = acc[v] * r * kp.nw[v];
+    }
+    store_mxfp4<VPT>(acc, lane, true, P.D, P.idx, P.out_row0 + seq * P.cap + i, idx_mirror);
 }
 
 // Kernel parameters of a checked CompressArgs (host).

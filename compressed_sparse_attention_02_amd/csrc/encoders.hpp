@@ -5,6 +5,8 @@
 // "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 3.4 (MXFP4 indexer QK).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace v4a {
@@ -77,7 +79,20 @@ __device__ __forceinline__ void store_mxfp4(const float (&x)[VPT], int lane, boo
 #pragma unroll
         for (int v = 0; v < VPT; v++) amax = fmaxf(amax, fabsf(x[v]));
     }
-    for (int o = group / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if constexpr (group == 16) {
+        // a block is one 16-lane row: its maximum by row rotations of 8, 4, 2, 1 lanes
+        // (exact in any order)
+        auto ror_max = [](float a, auto ctrl) {
+            return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, a), decltype(ctrl)::value, 0xF, 0xF, false)));
+        };
+        amax = ror_max(amax, std::integral_constant<int, 0x128>{});
+        amax = ror_max(amax, std::integral_constant<int, 0x124>{});
+        amax = ror_max(amax, std::integral_constant<int, 0x122>{});
+        amax = ror_max(amax, std::integral_constant<int, 0x121>{});
+    } else {
+        for (int o = group / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    }
     int X = mx_block_exp(amax);
     uint32_t codes = 0;  // VPT nibbles, element order = nibble order
 #pragma unroll
