@@ -49,7 +49,7 @@ COPY_PROBE_BYTES = 1 << 30
 # Counter summary of the indexer + top-k call (FETCH_SIZE / WRITE_SIZE per call, already
 # scaled by the copy probe) and the hash of the kernel sources it was taken with.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mxfp4_kernel_traffic_csa_decode_pro_1m.txt")
-TRAFFIC_SOURCES = ["indexer.hip", "common.hpp"]
+TRAFFIC_SOURCES = ["indexer.hip", "common.hpp", "compress.hpp", "encoders.hpp"]
 MXFP4_PEAK_TFLOPS = 10100.0
 BF16_PEAK_TFLOPS = 2500.0
 
