@@ -472,33 +472,35 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 }
 
 // ---------------------------------------------------------------- combine kernel ----
-// One wavefront per (16-dim tile, 16 heads, sequence): lane l holds head 16*hy + l/4 and dims
-// 16*dt + 4*(l%4) .. +3.  The splits' (m, l) and partial tiles (each one contiguous 1 KB read
-// per split) are requested together; the tiles are then merged in split order and the sink
-// is added once (splits <= kMaxSplits).
+// One wavefront per (16-dim tile, 16 heads, sequence), four wavefronts (four consecutive dim
+// tiles) per workgroup: lane l holds head 16*hy + l/4 and dims 16*dt + 4*(l%4) .. +3.  The
+// splits' (m, l) and partial tiles (each one contiguous 1 KB read per split) are requested
+// together, only for the splits the sequence has; the tiles are then merged in split order
+// and the sink is added once (splits <= kMaxSplits).
 constexpr int kMaxSplits = 32;
+constexpr int kCombineWaves = 4;
 
-__global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
-    const int dt = blockIdx.x, b = blockIdx.z, lane = threadIdx.x;
+__global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
+    const int dt = blockIdx.x * kCombineWaves + (threadIdx.x >> 6), b = blockIdx.z, lane = threadIdx.x & 63;
     const int h = 16 * blockIdx.y + (lane >> 2);
     const int d0 = 16 * dt + 4 * (lane & 3);
     const int ndt = P.D / 16;
     const int n_keys = sq_n_ent(Sq, b) + sq_win_len(Sq, b);
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
-    if (splits == 1) return;  // uniform over the wavefront
-    // every split's (m, l) and the first 16 partial tiles are requested before any is used
+    if (splits == 1) return;  // uniform over the workgroup
+    // the (m, l) and the first 16 partial tiles of the splits are requested before any is used
     float m2s[kMaxSplits], ls[kMaxSplits];
     const float *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
     const int64_t sstride = (int64_t)ndt * P.H * 16;
     v4f po[16];
 #pragma unroll
     for (int s = 0; s < 16; s++)
-        po[s] = __builtin_nontemporal_load((const v4f *)(pbase + (s < splits ? s : 0) * sstride));
+        po[s] = s < splits ? __builtin_nontemporal_load((const v4f *)(pbase + s * sstride)) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < kMaxSplits; s++) {
-        const int sc = s < splits ? s : 0;
-        const float2 ml = *(const float2 *)(P.part_ml + ((int64_t)(b * P.S + sc) * P.H + h) * 2);
+        float2 ml = make_float2(-INFINITY, 0.0f);
+        if (s < splits) ml = *(const float2 *)(P.part_ml + ((int64_t)(b * P.S + s) * P.H + h) * 2);
         m2s[s] = ml.x;
         ls[s] = ml.y;
     }
@@ -515,10 +517,11 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnParams P, SeqInfo 
 #pragma unroll
         for (int v = 0; v < 4; v++) o[v] = fmaf(po[s][v], c, o[v]);
     }
-    if (splits > 16) {  // uniform over the wavefront
+    if (splits > 16) {  // uniform over the workgroup
 #pragma unroll
         for (int s = 16; s < kMaxSplits; s++)
-            po[s - 16] = __builtin_nontemporal_load((const v4f *)(pbase + (s < splits ? s : 0) * sstride));
+            po[s - 16] = s < splits ? __builtin_nontemporal_load((const v4f *)(pbase + s * sstride))
+                                    : v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 16; s < kMaxSplits; s++) {
             const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
@@ -762,7 +765,8 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
-    V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel, dim3(a.D / 16, a.H / 16, a.B), dim3(64), 0, s, P, sq);
+    V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel, dim3(a.D / 16 / kCombineWaves, a.H / 16, a.B),
+               dim3(64 * kCombineWaves), 0, s, P, sq);
     return hipGetLastError();
 }
 
