@@ -181,3 +181,43 @@ def test_chunked_equals_whole_on_gpu():
     torch.cuda.synchronize()
     for a, b in ((whole, parts), (hw, hp)):
         assert torch.equal(a.nope, b.nope) and torch.equal(a.rope, b.rope) and torch.equal(a.scale, b.scale)
+
+
+def test_unaligned_bf16_streams_equal_aligned():
+    """Streams that start 2 bytes past an aligned address take the element-wise load path;
+    the entries (CSA records and keys, HCA records) are bitwise those of aligned streams."""
+    T, D, R, dI = 1024, 512, 64, 128
+    announce("compress with unaligned bf16 streams")
+
+    def shifted(t):  # the same values, starting one BF16 element past a 256-byte boundary
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        out = buf[1:].view(t.shape)
+        out.copy_(t)
+        return out
+
+    for d, to_idx in ((D, False), (dI, True)):
+        s = streams(530 + d, T, d, bf16=True)
+        a, b, ga, gb, ba, bb = dev_streams(s, bf16=True)
+        res = []
+        for xa, xb in ((a, b), (shifted(a), shifted(b))):
+            assert (xa.data_ptr() % 16 == 0) == (xa is a)
+            out = v4.Idx.empty(1, T // 4, d) if to_idx else v4.KV.empty(1, T // 4, d, R)
+            v4.v4a_compress_csa(xa, xb, ga, gb, ba, bb, tok0=0, m=4, first_entry=0, n_entries=T // 4,
+                                **({"out_idx": out} if to_idx else {"out_kv": out}))
+            res.append(out)
+        torch.cuda.synchronize()
+        if to_idx:
+            assert torch.equal(res[0].codes, res[1].codes) and torch.equal(res[0].scales, res[1].scales)
+        else:
+            assert torch.equal(res[0].nope, res[1].nope) and torch.equal(res[0].rope, res[1].rope)
+            assert torch.equal(res[0].scale, res[1].scale)
+    x = bf16_from_bits(to_bf16_bits(normal(532, "kv_h", (T, D))))
+    gt, bi = f32(normal(532, "gate_h", (T, 1))), f32(normal(532, "bias_h", (128, 1)))
+    res = []
+    for xs in (x, shifted(x)):
+        out = v4.KV.empty(1, T // 128, D, R)
+        v4.v4a_compress_hca(xs, gt, bi, tok0=0, m=128, first_entry=0, n_entries=T // 128, out_kv=out)
+        res.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(res[0].nope, res[1].nope) and torch.equal(res[0].rope, res[1].rope)
+    assert torch.equal(res[0].scale, res[1].scale)

@@ -28,12 +28,14 @@ def clone_idx(ix):
     return v4.Idx(ix.fmt, ix.d, ix.codes.clone(), ix.scales.clone(), ix.cap)
 
 
-@pytest.mark.parametrize("score_bf16,norm,key_gate_dim", [(False, False, False), (True, False, False),
-                                                          (False, True, False), (False, False, True)],
-                         ids=["f32_scores", "bf16_scores", "rmsnorm", "key_gate_per_dim"])
-def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
+@pytest.mark.parametrize("score_bf16,norm,key_gate_dim,unaligned",
+                         [(False, False, False, False), (True, False, False, False), (False, True, False, False),
+                          (False, False, True, False), (False, False, False, True)],
+                         ids=["f32_scores", "bf16_scores", "rmsnorm", "key_gate_per_dim", "unaligned_streams"])
+def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim, unaligned):
     """With one gate per token the new indexer keys are compressed inside the scoring kernel
-    (the step starts with a histogram clear); with a gate per dim the prologue compresses them."""
+    (the step starts with a histogram clear); with a gate per dim, or streams not aligned for
+    vector loads, a first launch compresses them."""
     seed, m, D, R, H, HI, dI, k, W = 4242, 4, 512, 64, 128, 64, 128, 512, 128
     q_pos = [4003, 4001, 3, 8191]            # completes entry 1000 / none / entry 0 / entry 2047
     B, cap = len(q_pos), 2304
@@ -52,6 +54,11 @@ def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
     bits = {n: to_bf16_bits(normal(seed, n, (B, 2 * m, D if n.startswith("kv") else dI)))
             for n in ("kv_a", "kv_b", "idx_a", "idx_b")}
     dev = {n: bf16_from_bits(v) for n, v in bits.items()}
+    if unaligned:  # the same values one BF16 element past an aligned address
+        for n, t in list(dev.items()):
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+            dev[n] = buf[1:].view(t.shape)
+            dev[n].copy_(t)
     gi = dI if key_gate_dim else 1
     gates = {n: f32(normal(seed, n, (B, 2 * m, gi if n.startswith("idx") else 1)))
              for n in ("gate_a", "gate_b", "idx_gate_a", "idx_gate_b")}
@@ -86,7 +93,7 @@ def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
     n = v4.v4a_trace_end()
     torch.cuda.synchronize()
     kernels = v4.trace_kernels(n)
-    first = "decode_prologue_kernel" if key_gate_dim else "zero_kernel"
+    first = "decode_prologue_kernel" if key_gate_dim or unaligned else "zero_kernel"
     assert [name for name, _ in kernels] == [first, "indexer_mxfp4_kernel", "select_scan_kernel",
                                              "select_final_kernel", "attn_mfma_kernel", "attn_combine_kernel"], kernels
     assert all(ms > 0 for _, ms in kernels), kernels
@@ -128,7 +135,7 @@ def test_fused_step_equals_separate_calls(score_bf16, norm, key_gate_dim):
     v4.v4a_decode_step_csa(step_args(kv3, keys3, out3, ws_clean=True), ws1)
     n3 = v4.v4a_trace_end()
     torch.cuda.synchronize()
-    assert [name for name, _ in v4.trace_kernels(n3)] == [name for name, _ in kernels][(0 if key_gate_dim else 1):]
+    assert [name for name, _ in v4.trace_kernels(n3)] == [name for name, _ in kernels][(0 if first != "zero_kernel" else 1):]
     assert torch.equal(out3, out1) and torch.equal(keys3.codes, keys1.codes) and torch.equal(kv3.nope, kv1.nope)
     assert not ws1[h0:h0 + B * HIST_COPIES * 4096 * 4].any()
 
