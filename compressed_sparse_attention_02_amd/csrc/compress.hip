@@ -22,10 +22,10 @@
 
 namespace v4a {
 
-// Four entries per workgroup, one per wavefront; or, for the long gate-per-token blocks (HCA),
-// one entry per workgroup shared by its four wavefronts.
+// kEntryWaves entries per workgroup, one per wavefront; or, for the long gate-per-token blocks
+// (HCA), one entry per workgroup shared by its kEntryWaves wavefronts.
 template <int VPT>
-__global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
+__global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressParams P) {
     __shared__ float wsh[kEntryWaves][kMaxCand];
     __shared__ float red[kEntryWaves * 64 * VPT];
     if (entry_uses_workgroup(P)) {
@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressParams P) {
         return;
     }
     const int wv = threadIdx.x >> 6;
-    const int64_t e = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t e = (int64_t)blockIdx.x * kEntryWaves + wv;
     if (e >= P.n_entries) return;  // the whole wavefront leaves together
     compress_entry<VPT>(P, wsh[wv], blockIdx.y, P.first_entry + e, P.tok0);
 }
@@ -55,7 +55,7 @@ struct PrologueParams {
 };
 
 template <int VK>
-__global__ void __launch_bounds__(256) decode_prologue_kernel(PrologueParams P) {
+__global__ void __launch_bounds__(64 * kEntryWaves) decode_prologue_kernel(PrologueParams P) {
     __shared__ float wsh[kEntryWaves * kMaxCand];
     __shared__ float red[kEntryWaves * 64 * VK];
     const int y = blockIdx.y;
@@ -113,8 +113,8 @@ CompressParams compress_params(const CompressArgs &a) {
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     if (a.n_entries == 0 || a.n_seq == 0) return hipSuccess;
     const CompressParams P = compress_params(a);
-    const int64_t per_wg = entry_uses_workgroup(P) ? 1 : 4;
-    dim3 grid((unsigned)((a.n_entries + per_wg - 1) / per_wg), (unsigned)a.n_seq), block(256);
+    const int64_t per_wg = entry_uses_workgroup(P) ? 1 : kEntryWaves;
+    dim3 grid((unsigned)((a.n_entries + per_wg - 1) / per_wg), (unsigned)a.n_seq), block(64 * kEntryWaves);
     switch (a.D) {
         case 32: case 64: V4A_LAUNCH("compress_kernel", compress_kernel<1>, grid, block, 0, s, P); break;
         case 128: V4A_LAUNCH("compress_kernel", compress_kernel<2>, grid, block, 0, s, P); break;
@@ -137,13 +137,13 @@ hipError_t launch_decode_prologue(const CompressArgs &key, int blocks_before, in
     for (int b = 0; b < kMaxSeq; b++) P.entry[b] = b < B ? entry[b] : -1;
     P.zero = (uint4 *)zero;
     P.zero_n16 = zero_bytes / 16;
-    const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 255) / 256, 1024);
+    const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 64 * kEntryWaves - 1) / (64 * kEntryWaves), 1024);
     dim3 grid(zx > 0 ? zx : 1, (unsigned)(B + 1));
     switch (key.D) {
-        case 32: case 64: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(256), 0, s, P); break;
-        case 128: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(256), 0, s, P); break;
-        case 256: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<4>, grid, dim3(256), 0, s, P); break;
-        case 512: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<8>, grid, dim3(256), 0, s, P); break;
+        case 32: case 64: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
+        case 128: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
+        case 256: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<4>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
+        case 512: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<8>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

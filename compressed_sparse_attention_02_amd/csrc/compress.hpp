@@ -293,7 +293,7 @@ __device__ __forceinline__ void load_norm_weights(const CompressParams &P, float
 
 // Entries whose candidates a whole workgroup of kEntryWaves wavefronts shares (gate per token,
 // blocks of at least 64 tokens: the HCA blocks); every caller decides with this one rule.
-constexpr int kEntryWaves = 4;
+constexpr int kEntryWaves = 8;
 __host__ __device__ __forceinline__ bool entry_uses_workgroup(const CompressParams &P) {
     return P.G == 1 && P.m >= 64;
 }
