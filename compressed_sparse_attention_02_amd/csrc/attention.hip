@@ -30,6 +30,8 @@
 // A split's (m, l, O) go to the workspace unless the sequence has a single split, in which
 // case the workgroup finishes the output itself (sink, normalisation, inverse RoPE, cast).
 // Split boundaries depend only on the sequence's own key count.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace v4a {
@@ -471,6 +473,473 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     }
 }
 
+// ------------------------------------------------------------------ tile kernel -----
+// The same attention as attn_mfma_kernel (every head's arithmetic identical, so results are
+// bitwise equal), with the key tile kept in LDS in its storage layout instead of converted and
+// copied twice:
+//   entry tiles: the 32 records' bytes (FP8 codes, then BF16 RoPE dims) are copied row by row
+//     from the cache straight into LDS by direct-to-LDS loads, one tile ahead, without holding
+//     registers (invalid keys copy a zero row);
+//   window and mixed tiles: converted to BF16 rows by the wavefronts, as before;
+//   scores:  the A operand (16 keys x 32 dims) is read key-major; FP8 codes are converted to
+//            BF16 (exactly) in registers;
+//   values:  the A operand (16 dims x 32 keys, the keys in the order of the lane's
+//            probabilities) is read transposed with ds_read_b64_tr_b8 (FP8 codes) or two
+//            ds_read_b64_tr_b16 (BF16 dims): within each group of 16 lanes, lane i receives
+//            byte i%8 of the 8-byte chunks of lanes 2j + i/8 (tr_b8), or element i%4 of
+//            the chunks of lanes 4j + i/4 (tr_b16), j = 0..7 (0..3); so source lane s of
+//            group g addresses key k(g, s/2) at dims 16dt + 8(s%2) (FP8) or key k(g, s/4)
+//            at dims 16dt + 4(s%4) (BF16), and lane i gets dim 16dt + i of those keys.
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *glb_ptr_t;
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+__device__ __align__(16) uint8_t g_zero_row[1024];  // source of the rows of invalid keys
+
+// k(g, j): key j of the value operand's k-block g, in the order the lanes' probabilities
+// follow (keys 4g..4g+3, then 16+4g..16+4g+3)
+__device__ __forceinline__ int pv_key(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+__device__ __forceinline__ v8bf fp8x8_bf16(uint32_t lo, uint32_t hi) {
+    uint4 v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return __builtin_bit_cast(v8bf, v);
+}
+
+template <int D, int R, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_tile_kernel(AttnParams P, SeqInfo Sq) {
+    constexpr int NKS = D / 32;   // k-steps of the score MFMA
+    constexpr int NDT = D / 16;   // dim tiles of the value MFMA
+    constexpr int Dn = D - R;
+    constexpr int RB8 = Dn + 2 * R;        // bytes of one record (FP8 codes, BF16 RoPE dims)
+    constexpr int RC8 = RB8 / 16 + 1;      // 16-byte chunks per LDS row (one of padding)
+    constexpr int RS8 = 16 * RC8;          // LDS row stride of an entry tile
+    constexpr int RS16 = D + 8;            // LDS row stride of a BF16 tile (in BF16)
+    constexpr int NCH8 = kTile * RC8;      // chunks of an entry tile
+    static_assert(Dn % 32 == 0 && R % 32 == 0, "k-steps are all FP8 or all BF16 dims");
+    __shared__ __attribute__((aligned(16))) uint8_t E8[2][kTile * RS8];   // entry tiles (two)
+    __shared__ __attribute__((aligned(16))) float ksc8[2][kTile];
+    __shared__ int kval8[2][kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t E16[kTile * RS16];    // window / mixed tile
+    __shared__ __attribute__((aligned(16))) float ksc16[kTile];
+    __shared__ int kval16[kTile];
+    __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
+
+    // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart.  A
+    // split-free launch numbers (query, group of hpw heads) items from item0 instead.
+    int L = blockIdx.x, hg = 0, p = L;
+    const int hpg = P.hpw ? P.hpw : 16 * (int)(blockDim.x >> 6);  // heads per workgroup
+    if (P.hpw) {
+        const int item = P.item0 + L, groups = P.H / P.hpw;
+        hg = item % groups;
+        p = (item / groups) * P.S;  // split 0 of its query (S = 1)
+    } else if (P.n_hg > 1) {  // n_hg a power of two
+        hg = (L >> 3) & (P.n_hg - 1);
+        p = (L >> (3 + __builtin_ctz((unsigned)P.n_hg))) * 8 + (L & 7);
+    }
+    const int b = p / P.S, split = p % P.S;
+    if (b >= P.B) return;
+    const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
+    const WinRows wr = sq_win_rows(Sq, b, P.W);
+    int tps, splits;
+    split_plan(n_keys, P.target, &tps, &splits);
+    if (split >= splits) return;
+    const int kb0 = split * tps * kTile;
+    const int kb1 = min(n_keys, kb0 + tps * kTile);
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int h0 = hg * hpg + wv * 16;
+    const bool wave_on = h0 < P.H;
+    const int h = h0 + col;
+    const int NT = blockDim.x;
+
+    // query heads as the B operand of S^T: lane holds head h, dims 32*ks + 8*grp + j
+    v8bf qT[NKS];
+    {
+        const uint16_t *qr = (const uint16_t *)P.q + ((int64_t)b * P.H + (wave_on ? h : 0)) * D;
+        uint4 qu[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++)
+            qu[ks] = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
+        if (P.q_norm_w) {
+            // Query prologue ("DeepSeek-V4 technical report walkthrough", section 2.3: RMSNorm acts
+            // directly on the queries): RMSNorm of the head over its D dims (a head's dims sit in
+            // lanes col, col+16, col+32, col+48), RoPE at the query position on the last R dims
+            // (pairs inside a lane's 8 consecutive dims; Dn is a multiple of 32, so a k-step is
+            // all RoPE dims or none), then BF16 (nearest even) as the MFMA operand.
+            float ss = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float lo = __builtin_bit_cast(float, w4[j] << 16);
+                    const float hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
+                    ss = fmaf(lo, lo, ss);
+                    ss = fmaf(hi, hi, ss);
+                }
+            }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float rn = 1.0f / sqrtf(ss / (float)D + kNormEps);
+            RopeLanes rl;
+            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+                const float4 wa = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp);
+                const float4 wb = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp + 4);
+                const float wv8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+                float y[8];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    y[2 * j] = __builtin_bit_cast(float, w4[j] << 16) * rn * wv8[2 * j];
+                    y[2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u) * rn * wv8[2 * j + 1];
+                }
+                if (32 * ks >= Dn) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float2 cs = rl.get(16 * (ks - Dn / 32) + 4 * grp + i);
+                        const float x0 = y[2 * i], x1 = y[2 * i + 1];
+                        y[2 * i] = x0 * cs.x - x1 * cs.y;
+                        y[2 * i + 1] = x0 * cs.y + x1 * cs.x;
+                    }
+                }
+                v8bf qv;
+#pragma unroll
+                for (int j = 0; j < 8; j++) qv[j] = (__bf16)y[j];
+                qT[ks] = qv;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) qT[ks] = __builtin_bit_cast(v8bf, qu[ks]);
+        }
+    }
+    v4f O[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    // the split's selected entry indices, read once (one load round for all its tiles)
+    if (P.topk) {
+        const int e1 = min(kb1, n_ent);
+        for (int j = kb0 + t; j < e1; j += NT) sidx[j - kb0] = P.topk[(int64_t)b * P.k + j];
+    }
+
+    const int NW = NT >> 6;
+    // ---- entry tile tb -> E8[q]: wavefront w issues the direct-to-LDS loads w, w + NW, ...
+    // (64 chunks each; chunk c of LDS row r is chunk c of key r's record, the last is padding)
+    auto issue_entries = [&](int tb, int q) {
+        for (int inst = wv; inst * 64 < NCH8; inst += NW) {
+            const int qq = inst * 64 + lane;
+            if (qq < NCH8) {
+                const int r = qq / RC8, c = qq - r * RC8;
+                const int64_t e = P.topk ? (int64_t)sidx[tb + r - kb0] : (int64_t)(tb + r);
+                const bool ok = e >= 0 && e < P.cap && c < RC8 - 1;
+                const int64_t row = (int64_t)b * P.kv_bstride + (ok ? e : 0);
+                const uint8_t *src = !ok ? g_zero_row
+                                         : (16 * c < Dn ? P.nope + row * Dn + 16 * c
+                                                        : (const uint8_t *)P.rope + row * (2 * R) + (16 * c - Dn));
+                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&E8[q][inst * 1024], 16, 0, 0);
+            }
+        }
+        if (wv == NW - 1 && lane < kTile) {
+            const int64_t e = P.topk ? (int64_t)sidx[tb + lane - kb0] : (int64_t)(tb + lane);
+            const bool ok = e >= 0 && e < P.cap;
+            const float *src = ok ? P.kscale + (int64_t)b * P.kv_bstride + e : (const float *)g_zero_row;
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc8[q][0], 4, 0, 0);
+            kval8[q][lane] = ok ? 1 : 0;
+        }
+    };
+    // ---- window / mixed tile -> E16 (BF16 rows), by the wavefronts: task (kg, seg) = keys
+    // 4kg..4kg+3, dims 8seg..8seg+7; all loads of a task are issued before any is used
+    constexpr int NSEG = D / 8;
+    constexpr int NTASK = 8 * NSEG;
+    auto stage_bf16 = [&](int tb) {
+        const bool win_only = tb >= n_ent;
+        for (int task = t; task < NTASK; task += NT) {
+            const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
+            uint4 v[4];
+            bool valid[4];
+            float scl[4];
+            if (win_only) {
+                int64_t row[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    valid[j] = tb + 4 * kg + j < kb1;
+                    row[j] = wr.row(valid[j] ? tb + 4 * kg + j - n_ent : 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
+#pragma unroll
+                for (int j = 0; j < 4; j++) scl[j] = 1.0f;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int kidx = tb + 4 * kg + j;
+                    scl[j] = 0.0f;
+                    v[j] = make_uint4(0, 0, 0, 0);
+                    valid[j] = false;
+                    if (kidx < n_ent) {
+                        const int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
+                        if (e >= 0 && e < P.cap) {
+                            const int64_t row = (int64_t)b * P.kv_bstride + e;
+                            valid[j] = true;
+                            scl[j] = P.kscale[row];
+                            if (dim < Dn) {
+                                const uint2 c = *(const uint2 *)(P.nope + row * Dn + dim);
+                                v[j] = __builtin_bit_cast(uint4, fp8x8_bf16(c.x, c.y));
+                            } else {
+                                v[j] = *(const uint4 *)(P.rope + row * R + (dim - Dn));
+                            }
+                        }
+                    } else if (kidx < kb1) {
+                        valid[j] = true;
+                        scl[j] = 1.0f;
+                        v[j] = *(const uint4 *)((const uint16_t *)P.win + wr.row(kidx - n_ent) * D + dim);
+                    }
+                }
+            }
+            if (seg == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    ksc16[4 * kg + j] = scl[j];
+                    kval16[4 * kg + j] = valid[j] ? 1 : 0;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) *(uint4 *)(E16 + (4 * kg + j) * RS16 + dim) = valid[j] ? v[j] : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    const float *tksc = ksc8[0];
+    const int *tkval = kval8[0];
+    const uint8_t *e8 = E8[0];
+    // A operand of the scores: key r, dims 32ks + 8grp .. +7
+    auto qk_operand = [&](auto f8, int r, int ks) -> v8bf {
+        if constexpr (decltype(f8)::value) {
+            if (32 * ks < Dn) {
+                const uint2 c = *(const uint2 *)(e8 + r * RS8 + 32 * ks + 8 * grp);
+                return fp8x8_bf16(c.x, c.y);
+            }
+            return __builtin_bit_cast(v8bf, *(const uint4 *)(e8 + r * RS8 + Dn + 2 * (32 * ks - Dn + 8 * grp)));
+        } else {
+            return __builtin_bit_cast(v8bf, *(const uint4 *)(E16 + r * RS16 + 32 * ks + 8 * grp));
+        }
+    };
+    // A operand of the values: dims 16dt + col, keys k(grp, 0..7)
+    auto pv_operand = [&](auto f8, int dt) -> v8bf {
+        if constexpr (decltype(f8)::value) {
+            if (16 * dt < Dn) {
+                const v2i_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i_t *)(e8 + pv_key(grp, col >> 1) * RS8 + 16 * dt + 8 * (col & 1)));
+                return fp8x8_bf16((uint32_t)c.x, (uint32_t)c.y);
+            }
+            const int off = Dn + 2 * (16 * dt - Dn + 4 * (col & 3));
+            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)(e8 + pv_key(grp, col >> 2) * RS8 + off));
+            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)(e8 + pv_key(grp, 4 + (col >> 2)) * RS8 + off));
+            return __builtin_bit_cast(v8bf, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
+        } else {
+            const int off = 16 * dt + 4 * (col & 3);
+            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)(E16 + pv_key(grp, col >> 2) * RS16 + off));
+            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)(E16 + pv_key(grp, 4 + (col >> 2)) * RS16 + off));
+            return __builtin_bit_cast(v8bf, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
+        }
+    };
+
+    // the split's indices are in LDS before the first tile's loads
+    __syncthreads();
+    int q = 0;
+    if (kb0 < kb1 && kb0 + kTile <= n_ent) issue_entries(kb0, 0);
+    for (int tb = kb0; tb < kb1; tb += kTile) {
+        const bool f8 = tb + kTile <= n_ent;  // an entry tile (uniform)
+        if (!f8) {
+            __syncthreads();  // the previous tile's readers are done with E16
+            stage_bf16(tb);
+        }
+        // this tile is in LDS: each wavefront waits for its own direct loads, then the barrier
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // the next entry tile travels while this one is computed
+        const int tn = tb + kTile;
+        if (tn < kb1 && tn + kTile <= n_ent) issue_entries(tn, q ^ 1);
+        if (wave_on && f8) {
+            tksc = ksc8[q];
+            tkval = kval8[q];
+            e8 = E8[q];
+                // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
+                float s2[8], ks8[8];
+#pragma unroll
+                for (int st = 0; st < 2; st++) {
+                    v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const int r = 16 * st + col;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ks++) {
+                        const v8bf a = qk_operand(std::true_type{}, r, ks);
+                        if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
+                        else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
+                    }
+                    const float4 sc4 = *(const float4 *)(tksc + 16 * st + 4 * grp);
+                    const int4 kv4 = *(const int4 *)(tkval + 16 * st + 4 * grp);
+                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                    const int kvv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        s2[4 * st + i] = kvv[i] ? P.scale2 * fmaf(scv[i], an[i], ar[i]) : -INFINITY;
+                        ks8[4 * st + i] = scv[i];
+                    }
+                }
+                // ---- online softmax (exp2 domain); lane: head h, keys {4grp+i, 16+4grp+i}
+                float mt = s2[0];
+#pragma unroll
+                for (int i = 1; i < 8; i++) mt = fmaxf(mt, s2[i]);
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                // The running reference moves only when a score exceeds it by more than kRescaleSlack
+                // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
+                // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
+                if (mt > m_run + kRescaleSlack) {
+                    const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NDT; i++) O[i] *= alpha;
+                    m_run = mt;
+                }
+                float pn[8], pr[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
+                    l_run += pi;
+                    pr[i] = pi;
+                    pn[i] = pi * ks8[i];
+                }
+                v8bf Pn, Pr;  // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    Pn[i] = (__bf16)pn[i];
+                    Pr[i] = (__bf16)pr[i];
+                }
+                // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
+#pragma unroll
+                for (int dt = 0; dt < NDT; dt++) {
+                    const v8bf a = pv_operand(std::true_type{}, dt);
+                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
+                }
+        } else if (wave_on) {
+            tksc = ksc16;
+            tkval = kval16;
+                // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
+                float s2[8], ks8[8];
+#pragma unroll
+                for (int st = 0; st < 2; st++) {
+                    v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const int r = 16 * st + col;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ks++) {
+                        const v8bf a = qk_operand(std::false_type{}, r, ks);
+                        if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
+                        else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
+                    }
+                    const float4 sc4 = *(const float4 *)(tksc + 16 * st + 4 * grp);
+                    const int4 kv4 = *(const int4 *)(tkval + 16 * st + 4 * grp);
+                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                    const int kvv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        s2[4 * st + i] = kvv[i] ? P.scale2 * fmaf(scv[i], an[i], ar[i]) : -INFINITY;
+                        ks8[4 * st + i] = scv[i];
+                    }
+                }
+                // ---- online softmax (exp2 domain); lane: head h, keys {4grp+i, 16+4grp+i}
+                float mt = s2[0];
+#pragma unroll
+                for (int i = 1; i < 8; i++) mt = fmaxf(mt, s2[i]);
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                // The running reference moves only when a score exceeds it by more than kRescaleSlack
+                // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
+                // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
+                if (mt > m_run + kRescaleSlack) {
+                    const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NDT; i++) O[i] *= alpha;
+                    m_run = mt;
+                }
+                float pn[8], pr[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
+                    l_run += pi;
+                    pr[i] = pi;
+                    pn[i] = pi * ks8[i];
+                }
+                v8bf Pn, Pr;  // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    Pn[i] = (__bf16)pn[i];
+                    Pr[i] = (__bf16)pr[i];
+                }
+                // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
+#pragma unroll
+                for (int dt = 0; dt < NDT; dt++) {
+                    const v8bf a = pv_operand(std::false_type{}, dt);
+                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
+                }
+        }
+        if (f8) q ^= 1;
+        __syncthreads();      // readers of this tile's buffer are done before it is refilled
+    }
+    if (!wave_on) return;
+    // l over the four lane groups of each head
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (h >= P.H) return;
+    if (splits == 1) {
+        const float f = finish_factor(P, h, m_run, l_run);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) O[dt] *= f;
+        if (P.rope_inv) {  // H is a multiple of 16: the whole wavefront is here
+            RopeLanes rl;
+            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
+#pragma unroll
+            for (int dt = Dn / 16; dt < NDT; dt++) {
+                const int j = (16 * dt + 4 * grp - Dn) / 2;
+                const float2 r0 = rope_unrotate(rl.get(j), O[dt][0], O[dt][1]);
+                const float2 r1 = rope_unrotate(rl.get(j + 1), O[dt][2], O[dt][3]);
+                O[dt] = v4f{r0.x, r0.y, r1.x, r1.y};
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+            const float o[4] = {O[dt][0], O[dt][1], O[dt][2], O[dt][3]};
+            store_out4(P, b, h, 16 * dt + 4 * grp, o);
+        }
+    } else {
+        // each store writes 1 KB contiguous: the wavefront's 16 heads x 16 dims of one tile
+        // (streaming stores: the combine reads them once)
+        float *po = P.part_o + ((int64_t)(b * P.S + split) * NDT * P.H + h) * 16 + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) __builtin_nontemporal_store(O[dt], (v4f *)(po + (int64_t)dt * P.H * 16));
+        if (grp == 0) {
+            float *pm = P.part_ml + (((int64_t)b * P.S + split) * P.H + h) * 2;
+            pm[0] = m_run;
+            pm[1] = l_run;
+        }
+    }
+}
+
+
 // ---------------------------------------------------------------- combine kernel ----
 // One wavefront per (16-dim tile, 16 heads, sequence), four wavefronts (four consecutive dim
 // tiles) per workgroup: lane l holds head 16*hy + l/4 and dims 16*dt + 4*(l%4) .. +3.  The
@@ -723,9 +1192,9 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
             P.hpw = 64;
             P.item0 = 0;
             if (a.D == 512)
-                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(full), dim3(256), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(full), dim3(256), 0, s, P, sq);
             else
-                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(full), dim3(256), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(full), dim3(256), 0, s, P, sq);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -733,9 +1202,9 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
             P.hpw = 16;
             P.item0 = 4 * full;
             if (a.D == 512)
-                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(units), dim3(64), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(units), dim3(64), 0, s, P, sq);
             else
-                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(units), dim3(64), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(units), dim3(64), 0, s, P, sq);
         }
         return hipGetLastError();
     }
@@ -754,14 +1223,14 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     if (P.n_hg > 1) blocks = ((pairs + 7) / 8) * 8 * P.n_hg;
     if (a.D == 512) {
         if (wide)
-            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
         else
-            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     } else {
         if (wide)
-            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
         else
-            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
