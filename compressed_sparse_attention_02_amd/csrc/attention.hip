@@ -17,16 +17,18 @@
 // grids that fill the chip) or 64 of them (4 wavefronts); in the latter case with 128 heads
 // the two head-group workgroups of a split get linear ids 8 apart, so they land on the same
 // XCD and share its L2 for the key tiles.  Per tile of 32 keys:
-//   staging: every lane converts 4 keys x 4 dims (E4M3 codes are exact in BF16) and writes
-//            them key-major (Er: rows = keys) and dim-major (Ec: rows = dims) into LDS;
-//   scores:  S^T = E Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims from Er,
-//            B = the wavefront's 16 query heads held in registers), accumulating the FP8
-//            dims and the BF16 RoPE dims separately so the per-entry scale folds in as
-//            s = scale_e * (q.codes) + q.rope;
+//   staging: an entry tile is its 32 records copied byte for byte into LDS rows (FP8 codes,
+//            then BF16 RoPE dims) by direct-to-LDS loads issued one tile ahead; a tile
+//            holding window tokens is written as BF16 rows by the wavefronts;
+//   scores:  S^T = E Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims read key-major,
+//            FP8 codes converted exactly to BF16 in registers; B = the wavefront's 16 query
+//            heads held in registers), accumulating the FP8 dims and the BF16 RoPE dims
+//            separately so the per-entry scale folds in as s = scale_e * (q.codes) + q.rope;
 //   softmax: online, in the exp2 domain, each lane owning one head and 8 keys;
-//   values:  O^T += E^T P^T with A = 16 dims x 32 keys from Ec and B = the lane's own
-//            probabilities (times scale_e for the FP8 dims), whose key order the A reads
-//            follow, so P never leaves registers.
+//   values:  O^T += E^T P^T with A = 16 dims x 32 keys read transposed from the same rows
+//            (gfx950 transpose LDS reads) and B = the lane's own probabilities (times scale_e
+//            for the FP8 dims), whose key order the A reads follow, so P never leaves
+//            registers.
 // A split's (m, l, O) go to the workspace unless the sequence has a single split, in which
 // case the workgroup finishes the output itself (sink, normalisation, inverse RoPE, cast).
 // Split boundaries depend only on the sequence's own key count.
@@ -37,8 +39,6 @@
 namespace v4a {
 
 constexpr int kTile = 32;
-constexpr int kErStride = 520;  // bf16 per key row in Er (512 + 8: staggers LDS banks)
-constexpr int kEcStride = 36;   // bf16 per dim row in Ec (32 keys + 4)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running maximum may lag the scores
 constexpr int kMaxSelKeys = 2048;  // top-k entries per sequence (k <= 2048)
@@ -138,345 +138,8 @@ __device__ __forceinline__ void finish4(const AttnParams &P, const SeqInfo &Sq, 
 }
 
 // ------------------------------------------------------------------ MFMA kernel -----
-template <int D, int R, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnParams P, SeqInfo Sq) {
-    constexpr int NKS = D / 32;   // k-steps of the score MFMA
-    constexpr int NDT = D / 16;   // dim tiles of the value MFMA
-    constexpr int Dn = D - R;
-    __shared__ __attribute__((aligned(16))) uint16_t Er[kTile * kErStride];
-    __shared__ __attribute__((aligned(16))) uint16_t Ec[D * kEcStride];
-    __shared__ __attribute__((aligned(16))) float ksc[kTile];
-    __shared__ __attribute__((aligned(16))) int kvalid[kTile];
-    __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
-
-    // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart.  A
-    // split-free launch numbers (query, group of hpw heads) items from item0 instead.
-    int L = blockIdx.x, hg = 0, p = L;
-    const int hpg = P.hpw ? P.hpw : 16 * (int)(blockDim.x >> 6);  // heads per workgroup
-    if (P.hpw) {
-        const int item = P.item0 + L, groups = P.H / P.hpw;
-        hg = item % groups;
-        p = (item / groups) * P.S;  // split 0 of its query (S = 1)
-    } else if (P.n_hg > 1) {  // n_hg a power of two
-        hg = (L >> 3) & (P.n_hg - 1);
-        p = (L >> (3 + __builtin_ctz((unsigned)P.n_hg))) * 8 + (L & 7);
-    }
-    const int b = p / P.S, split = p % P.S;
-    if (b >= P.B) return;
-    const int n_ent = sq_n_ent(Sq, b), n_keys = n_ent + sq_win_len(Sq, b);
-    const WinRows wr = sq_win_rows(Sq, b, P.W);
-    int tps, splits;
-    split_plan(n_keys, P.target, &tps, &splits);
-    if (split >= splits) return;
-    const int kb0 = split * tps * kTile;
-    const int kb1 = min(n_keys, kb0 + tps * kTile);
-
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int h0 = hg * hpg + wv * 16;
-    const bool wave_on = h0 < P.H;
-    const int h = h0 + col;
-    const int NT = blockDim.x;
-
-    // query heads as the B operand of S^T: lane holds head h, dims 32*ks + 8*grp + j
-    v8bf qT[NKS];
-    {
-        const uint16_t *qr = (const uint16_t *)P.q + ((int64_t)b * P.H + (wave_on ? h : 0)) * D;
-        uint4 qu[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ks++)
-            qu[ks] = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
-        if (P.q_norm_w) {
-            // Query prologue ("DeepSeek-V4 technical report walkthrough", section 2.3: RMSNorm acts
-            // directly on the queries): RMSNorm of the head over its D dims (a head's dims sit in
-            // lanes col, col+16, col+32, col+48), RoPE at the query position on the last R dims
-            // (pairs inside a lane's 8 consecutive dims; Dn is a multiple of 32, so a k-step is
-            // all RoPE dims or none), then BF16 (nearest even) as the MFMA operand.
-            float ss = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float lo = __builtin_bit_cast(float, w4[j] << 16);
-                    const float hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
-                    ss = fmaf(lo, lo, ss);
-                    ss = fmaf(hi, hi, ss);
-                }
-            }
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            const float rn = 1.0f / sqrtf(ss / (float)D + kNormEps);
-            RopeLanes rl;
-            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
-                const float4 wa = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp);
-                const float4 wb = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp + 4);
-                const float wv8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-                float y[8];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    y[2 * j] = __builtin_bit_cast(float, w4[j] << 16) * rn * wv8[2 * j];
-                    y[2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u) * rn * wv8[2 * j + 1];
-                }
-                if (32 * ks >= Dn) {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float2 cs = rl.get(16 * (ks - Dn / 32) + 4 * grp + i);
-                        const float x0 = y[2 * i], x1 = y[2 * i + 1];
-                        y[2 * i] = x0 * cs.x - x1 * cs.y;
-                        y[2 * i + 1] = x0 * cs.y + x1 * cs.x;
-                    }
-                }
-                v8bf qv;
-#pragma unroll
-                for (int j = 0; j < 8; j++) qv[j] = (__bf16)y[j];
-                qT[ks] = qv;
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) qT[ks] = __builtin_bit_cast(v8bf, qu[ks]);
-        }
-    }
-    v4f O[NDT];
-#pragma unroll
-    for (int i = 0; i < NDT; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
-    // the split's selected entry indices, read once (one load round for all its tiles)
-    if (P.topk) {
-        const int e1 = min(kb1, n_ent);
-        for (int j = kb0 + t; j < e1; j += NT) sidx[j - kb0] = P.topk[(int64_t)b * P.k + j];
-    }
-
-    constexpr int NSEG = D / 8;          // 8-dim segments per key row
-    constexpr int NTASK = 8 * NSEG;      // (4-key group, segment) staging tasks per tile
-    // LDS writes of one staging task: keys 4kg..4kg+3 as BF16 (v), key-major into Er and
-    // dim-major into Ec; the task of segment 0 also writes the keys' scales and validity
-    auto store_task = [&](int task, uint4 (&v)[4], const bool (&valid)[4], const float (&scl)[4]) {
-        const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
-        if (seg == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                ksc[4 * kg + j] = scl[j];
-                kvalid[4 * kg + j] = valid[j] ? 1 : 0;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            if (!valid[j]) v[j] = make_uint4(0, 0, 0, 0);
-            // 16-byte chunk seg of key row r sits at chunk seg ^ ((r >> 3) & 3): the eight
-            // rows 4kg + j written together then fall in distinct LDS banks
-            const int r = 4 * kg + j;
-            *(uint4 *)(Er + r * kErStride + 8 * (seg ^ ((r >> 3) & 3))) = v[j];
-        }
-        // dim-major: row dim+d holds keys 4kg..4kg+3
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-            const int sh = (d & 1) ? 16 : 0;
-            uint32_t w0, w1, w2, w3;
-            switch (d >> 1) {
-                case 0: w0 = v[0].x; w1 = v[1].x; w2 = v[2].x; w3 = v[3].x; break;
-                case 1: w0 = v[0].y; w1 = v[1].y; w2 = v[2].y; w3 = v[3].y; break;
-                case 2: w0 = v[0].z; w1 = v[1].z; w2 = v[2].z; w3 = v[3].z; break;
-                default: w0 = v[0].w; w1 = v[1].w; w2 = v[2].w; w3 = v[3].w; break;
-            }
-            // the 16-bit halves (low for even d, high for odd d) of keys 4kg..4kg+3, paired
-            const uint32_t sel = sh ? 0x07060302u : 0x05040100u;
-            const uint32_t a0 = __builtin_amdgcn_perm(w1, w0, sel);
-            const uint32_t a1 = __builtin_amdgcn_perm(w3, w2, sel);
-            *(uint2 *)(Ec + (dim + d) * kEcStride + 4 * kg) = make_uint2(a0, a1);
-        }
-    };
-    auto fp8x8_to_bf16 = [](uint2 c) -> uint4 {  // E4M3 codes are exact in BF16
-        uint4 v;
-        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
-        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
-        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
-        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
-        return v;
-    };
-    for (int tb = kb0; tb < kb1; tb += kTile) {
-        __syncthreads();
-        // ---- staging.  Task (kg, seg): keys 4kg..4kg+3, dims 8seg..8seg+7.  All loads of a
-        // thread are issued before any is used; padding keys read a valid row and are zeroed.
-        const int kind = (tb + kTile <= n_ent) ? 0 : (tb >= n_ent ? 1 : 2);  // entries / window / mixed
-        for (int task = t; task < NTASK; task += NT) {
-            const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
-            uint4 v[4];
-            bool valid[4];
-            float scl[4];
-            if (kind == 0) {
-                int64_t row[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int kidx = tb + 4 * kg + j;
-                    int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
-                    valid[j] = e >= 0 && e < P.cap;
-                    row[j] = (int64_t)b * P.kv_bstride + (valid[j] ? e : 0);
-                }
-                if (dim < Dn) {
-                    uint2 c[4];
-#pragma unroll
-                    for (int j = 0; j < 4; j++) c[j] = *(const uint2 *)(P.nope + row[j] * Dn + dim);
-#pragma unroll
-                    for (int j = 0; j < 4; j++) v[j] = fp8x8_to_bf16(c[j]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)(P.rope + row[j] * R + (dim - Dn));
-                }
-#pragma unroll
-                for (int j = 0; j < 4; j++) scl[j] = seg == 0 ? P.kscale[row[j]] : 0.0f;
-            } else if (kind == 1) {
-                int64_t row[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int wtok = tb + 4 * kg + j - n_ent;
-                    valid[j] = tb + 4 * kg + j < kb1;
-                    row[j] = wr.row(valid[j] ? wtok : 0);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; j++) v[j] = *(const uint4 *)((const uint16_t *)P.win + row[j] * D + dim);
-#pragma unroll
-                for (int j = 0; j < 4; j++) scl[j] = 1.0f;
-            } else {
-                // a tile holding the last entries and the first window tokens: per key
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int kidx = tb + 4 * kg + j;
-                    scl[j] = 0.0f;
-                    v[j] = make_uint4(0, 0, 0, 0);
-                    valid[j] = false;
-                    if (kidx < n_ent) {
-                        int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
-                        if (e >= 0 && e < P.cap) {
-                            const int64_t row = (int64_t)b * P.kv_bstride + e;
-                            valid[j] = true;
-                            scl[j] = P.kscale[row];
-                            if (dim < Dn)
-                                v[j] = fp8x8_to_bf16(*(const uint2 *)(P.nope + row * Dn + dim));
-                            else
-                                v[j] = *(const uint4 *)(P.rope + row * R + (dim - Dn));
-                        }
-                    } else if (kidx < kb1) {
-                        valid[j] = true;
-                        scl[j] = 1.0f;
-                        v[j] = *(const uint4 *)((const uint16_t *)P.win + wr.row(kidx - n_ent) * D + dim);
-                    }
-                }
-            }
-            store_task(task, v, valid, scl);
-        }
-        __syncthreads();
-        if (!wave_on) continue;
-
-        // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
-        float s2[8], ks8[8];
-#pragma unroll
-        for (int st = 0; st < 2; st++) {
-            v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int r = 16 * st + col;
-            const uint16_t *arow = Er + r * kErStride + 8 * (grp ^ ((r >> 3) & 3));
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                const v8bf a = __builtin_bit_cast(v8bf, *(const uint4 *)(arow + 32 * ks));
-                if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
-                else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
-            }
-            const float4 sc4 = *(const float4 *)(ksc + 16 * st + 4 * grp);
-            const int4 kv4 = *(const int4 *)(kvalid + 16 * st + 4 * grp);
-            const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-            const int kvv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                s2[4 * st + i] = kvv[i] ? P.scale2 * fmaf(scv[i], an[i], ar[i]) : -INFINITY;
-                ks8[4 * st + i] = scv[i];
-            }
-        }
-        // ---- online softmax (exp2 domain); lane: head h, keys {4grp+i, 16+4grp+i}
-        float mt = s2[0];
-#pragma unroll
-        for (int i = 1; i < 8; i++) mt = fmaxf(mt, s2[i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // The running reference moves only when a score exceeds it by more than kRescaleSlack
-        // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
-        // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
-        if (mt > m_run + kRescaleSlack) {
-            const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NDT; i++) O[i] *= alpha;
-            m_run = mt;
-        }
-        float pn[8], pr[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
-            l_run += pi;
-            pr[i] = pi;
-            pn[i] = pi * ks8[i];
-        }
-        v8bf Pn, Pr;  // round to nearest even (v_cvt_pk_bf16_f32)
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            Pn[i] = (__bf16)pn[i];
-            Pr[i] = (__bf16)pr[i];
-        }
-        // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-            const uint16_t *er = Ec + (16 * dt + col) * kEcStride;
-            const uint2 x0 = *(const uint2 *)(er + 4 * grp);
-            const uint2 x1 = *(const uint2 *)(er + 16 + 4 * grp);
-            const v8bf a = __builtin_bit_cast(v8bf, make_uint4(x0.x, x0.y, x1.x, x1.y));
-            O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
-        }
-    }
-    if (!wave_on) return;
-    // l over the four lane groups of each head
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (h >= P.H) return;
-    if (splits == 1) {
-        const float f = finish_factor(P, h, m_run, l_run);
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) O[dt] *= f;
-        if (P.rope_inv) {  // H is a multiple of 16: the whole wavefront is here
-            RopeLanes rl;
-            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
-#pragma unroll
-            for (int dt = Dn / 16; dt < NDT; dt++) {
-                const int j = (16 * dt + 4 * grp - Dn) / 2;
-                const float2 r0 = rope_unrotate(rl.get(j), O[dt][0], O[dt][1]);
-                const float2 r1 = rope_unrotate(rl.get(j + 1), O[dt][2], O[dt][3]);
-                O[dt] = v4f{r0.x, r0.y, r1.x, r1.y};
-            }
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-            const float o[4] = {O[dt][0], O[dt][1], O[dt][2], O[dt][3]};
-            store_out4(P, b, h, 16 * dt + 4 * grp, o);
-        }
-    } else {
-        // each store writes 1 KB contiguous: the wavefront's 16 heads x 16 dims of one tile
-        // (streaming stores: the combine reads them once)
-        float *po = P.part_o + ((int64_t)(b * P.S + split) * NDT * P.H + h) * 16 + 4 * grp;
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) __builtin_nontemporal_store(O[dt], (v4f *)(po + (int64_t)dt * P.H * 16));
-        if (grp == 0) {
-            float *pm = P.part_ml + (((int64_t)b * P.S + split) * P.H + h) * 2;
-            pm[0] = m_run;
-            pm[1] = l_run;
-        }
-    }
-}
-
-// ------------------------------------------------------------------ tile kernel -----
-// The same attention as attn_mfma_kernel (every head's arithmetic identical, so results are
-// bitwise equal), with the key tile kept in LDS in its storage layout instead of converted and
-// copied twice:
+// Every head's arithmetic is the same whatever the workgroup shape, so results do not depend
+// on it.  The key tile stays in LDS in its storage layout:
 //   entry tiles: the 32 records' bytes (FP8 codes, then BF16 RoPE dims) are copied row by row
 //     from the cache straight into LDS by direct-to-LDS loads, one tile ahead, without holding
 //     registers (invalid keys copy a zero row);
@@ -511,7 +174,7 @@ __device__ __forceinline__ v8bf fp8x8_bf16(uint32_t lo, uint32_t hi) {
 }
 
 template <int D, int R, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_tile_kernel(AttnParams P, SeqInfo Sq) {
+__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnParams P, SeqInfo Sq) {
     constexpr int NKS = D / 32;   // k-steps of the score MFMA
     constexpr int NDT = D / 16;   // dim tiles of the value MFMA
     constexpr int Dn = D - R;
@@ -1192,9 +855,9 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
             P.hpw = 64;
             P.item0 = 0;
             if (a.D == 512)
-                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(full), dim3(256), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(full), dim3(256), 0, s, P, sq);
             else
-                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(full), dim3(256), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(full), dim3(256), 0, s, P, sq);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1202,9 +865,9 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
             P.hpw = 16;
             P.item0 = 4 * full;
             if (a.D == 512)
-                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(units), dim3(64), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(units), dim3(64), 0, s, P, sq);
             else
-                V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(units), dim3(64), 0, s, P, sq);
+                V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(units), dim3(64), 0, s, P, sq);
         }
         return hipGetLastError();
     }
@@ -1223,14 +886,14 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     if (P.n_hg > 1) blocks = ((pairs + 7) / 8) * 8 * P.n_hg;
     if (a.D == 512) {
         if (wide)
-            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
         else
-            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<512, 64, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<512, 64, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     } else {
         if (wide)
-            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 8>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
         else
-            V4A_LAUNCH("attn_mfma_kernel", (attn_tile_kernel<128, 32, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
+            V4A_LAUNCH("attn_mfma_kernel", (attn_mfma_kernel<128, 32, 4>), dim3(blocks), dim3(64 * waves), 0, s, P, sq);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
