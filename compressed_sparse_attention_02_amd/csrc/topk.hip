@@ -31,6 +31,8 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kLdsList = 12288;   // listed keys the finalize kernel keeps in LDS
 constexpr int kMaxSlices = 1024;  // n_max <= 8M keys
 constexpr int kSubBins = 1024;    // 10-bit digits of the low 20 score-key bits
+constexpr int kSelTPS = 16;       // finalize: threads per slice placing its listed keys
+constexpr int kSelSpec = 8;       // finalize: listed keys per thread requested with the counts
 
 int select_slices(int64_t n_max) {
     int64_t s = (n_max + kSelSlice - 1) / kSelSlice;
@@ -251,23 +253,66 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     const int T = P.meta[2 * qi];
     const uint32_t above = (uint32_t)P.meta[2 * qi + 1];
     const uint32_t need = k_eff - above;  // >= 1: keys still to take from bin T
-    // global order of the listed keys: slice offsets
+    // global order of the listed keys: slice offsets, then the keys themselves into LDS
     const uint32_t *cnts = P.counts + (int64_t)qi * P.slices;
     const int S = P.slices;
-    if (t == 0) soff[0] = 0;
-    uint32_t run = 0;
-    for (int r0 = 0; r0 < S; r0 += kSelThreads) {
-        const int sidx = r0 + t;
-        const uint32_t c = sidx < S ? cnts[sidx] : 0u;
-        uint32_t tot;
-        const uint32_t incl = block_scan(c, wsum, &tot);
-        if (sidx < S) soff[sidx + 1] = run + incl;
-        run += tot;
-    }
-    __syncthreads();
-    const uint32_t L = soff[S];
-    const bool in_lds = L <= (uint32_t)kLdsList;
     const uint32_t *lst = P.list + (int64_t)qi * S * kSelSlice * 2;
+    // the first digit pass: bits 10..19 of the keys in bin T (bits 16..19 of widened 16-bit keys)
+    const int shift0 = P.key16 ? 16 : 10;
+    const uint32_t dmask0 = P.key16 ? 15u : (uint32_t)(kSubBins - 1);
+    bool hist0 = false;  // the first pass's histogram was counted while the keys were placed
+    uint32_t L;
+    if (S <= kSelThreads / kSelTPS) {
+        // kSelTPS threads per slice request its count and its first kSelTPS * kSelSpec listed
+        // keys at once (slots past the count lie inside the slice's list region and are
+        // dropped), so counts and keys take one memory round trip; one block scan of the
+        // counts then places every key
+        const int sl = t / kSelTPS, p0 = t % kSelTPS;
+        const bool live = sl < S;
+        const uint32_t c = live ? cnts[sl] : 0u;
+        const uint32_t *ls = lst + (int64_t)(live ? sl : 0) * kSelSlice * 2;
+        uint2 e[kSelSpec];
+#pragma unroll
+        for (int u = 0; u < kSelSpec; u++) e[u] = live ? *(const uint2 *)(ls + 2 * (p0 + kSelTPS * u)) : make_uint2(0, 0);
+        for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
+        uint32_t tot;
+        const uint32_t mine = (live && p0 == 0) ? c : 0u;
+        const uint32_t off = block_scan(mine, wsum, &tot) - c;  // the slice's first position (its barriers also order the clear)
+        if (live && p0 == 0) soff[sl] = off;
+        if (t == 0) soff[S] = tot;
+        L = tot;
+        if (L <= (uint32_t)kLdsList) {
+            hist0 = true;
+            auto put = [&](uint32_t pos, uint2 v) {
+                lidx[off + pos] = v.x;
+                lkey[off + pos] = v.y;
+                if ((int)(v.y >> 20) == T) atomicAdd(&hist[(v.y >> shift0) & dmask0], 1u);
+            };
+#pragma unroll
+            for (int u = 0; u < kSelSpec; u++) {
+                const uint32_t pos = (uint32_t)(p0 + kSelTPS * u);
+                if (live && pos < c) put(pos, e[u]);
+            }
+            // a slice that listed more keys than were requested
+            for (uint32_t pos = (uint32_t)(p0 + kSelTPS * kSelSpec); live && pos < c; pos += kSelTPS)
+                put(pos, *(const uint2 *)(ls + 2 * pos));
+        }
+        __syncthreads();
+    } else {
+        if (t == 0) soff[0] = 0;
+        uint32_t run = 0;
+        for (int r0 = 0; r0 < S; r0 += kSelThreads) {
+            const int sidx = r0 + t;
+            const uint32_t c = sidx < S ? cnts[sidx] : 0u;
+            uint32_t tot;
+            const uint32_t incl = block_scan(c, wsum, &tot);
+            if (sidx < S) soff[sidx + 1] = run + incl;
+            run += tot;
+        }
+        __syncthreads();
+        L = soff[S];
+    }
+    const bool in_lds = L <= (uint32_t)kLdsList;
     // entry j of the global order lives in slice s at position j - soff[s]
     auto fetch = [&](uint32_t j) -> uint2 {
         int lo = 0, hi = S;  // s with soff[s] <= j < soff[s+1]
@@ -283,7 +328,7 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         *idx = e.x;
         *key = e.y;
     };
-    if (in_lds) {
+    if (in_lds && !hist0) {
         // all loads of a batch are issued before any LDS store
         constexpr int kBatch = 8;
         for (uint32_t j0 = 0; j0 < L; j0 += kBatch * kSelThreads) {
@@ -299,8 +344,8 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
                 if (j < L) { lidx[j] = e[u].x; lkey[j] = e[u].y; }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // digit passes over the low 20 bits of the keys in bin T: bits 10..19, then 0..9; keys
     // widened from 16 bits hold only bits 16..19 below the bin, one pass
@@ -309,14 +354,16 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     for (int p = 0; p < n_pass; p++) {
         const int shift = P.key16 ? 16 : (p == 0 ? 10 : 0);
         const uint32_t dmask = P.key16 ? 15u : (uint32_t)(kSubBins - 1);
-        for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-        for (uint32_t j = t; j < L; j += kSelThreads) {
-            uint32_t idx, key;
-            entry(j, &idx, &key);
-            if ((int)(key >> 20) == T && (key & sub_mask) == sub) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        if (p > 0 || !hist0) {
+            for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+            for (uint32_t j = t; j < L; j += kSelThreads) {
+                uint32_t idx, key;
+                entry(j, &idx, &key);
+                if ((int)(key >> 20) == T && (key & sub_mask) == sub) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+            }
+            __syncthreads();
         }
-        __syncthreads();
         uint32_t c[kSubBins / kSelThreads];
 #pragma unroll
         for (int b = 0; b < kSubBins / kSelThreads; b++) c[b] = hist[(kSubBins / kSelThreads) * t + b];

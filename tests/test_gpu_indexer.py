@@ -141,6 +141,33 @@ def test_topk_adversarial_ties():
     assert np.array_equal(got[1, 0], np.arange(k))
 
 
+def test_topk_list_longer_than_lds():
+    """Every key identical: the threshold bin lists all 30000 keys, more than the final
+    selection keeps in LDS, so it reads them from the list in global memory."""
+    B, N, H, k = 1, 30000, 64, 900
+    keys = np.repeat(normal(310, "keys", (1, 1, 128)), N, axis=1)
+    q = normal(310, "q_idx", (B, H, 128))
+    w = normal(310, "w", (B, 1, H))
+    announce("topk list longer than LDS")
+    got, _, _ = run_topk(keys, q, w, np.array([N]), [4 * N - 1], k)
+    ref = oracle_topk(keys, q, w, np.array([N]), [4 * N - 1], k)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[0, 0], np.arange(k))
+
+
+def test_topk_more_than_32_slices():
+    """270000 keys make 33 slices of 8192: the final selection places the listed keys with
+    the slice-offset scan instead of 16 threads per slice."""
+    B, N, H, k = 1, 270000, 64, 1024
+    keys = normal(311, "keys", (B, N, 128))
+    q = normal(311, "q_idx", (B, H, 128))
+    w = normal(311, "w", (B, 1, H))
+    announce("topk 33 slices")
+    got, _, _ = run_topk(keys, q, w, np.array([N]), [4 * N - 1], k)
+    ref = oracle_topk(keys, q, w, np.array([N]), [4 * N - 1], k)
+    assert np.array_equal(got, ref)
+
+
 def test_topk_prefill_queries():
     """Several queries per sequence at consecutive positions (the prefill form)."""
     B, N, H, k, Q = 1, 6000, 64, 512, 24
