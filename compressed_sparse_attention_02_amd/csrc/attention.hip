@@ -18,8 +18,9 @@
 // the two head-group workgroups of a split get linear ids 8 apart, so they land on the same
 // XCD and share its L2 for the key tiles.  Per tile of 32 keys:
 //   staging: an entry tile is its 32 records copied byte for byte into LDS rows (FP8 codes,
-//            then BF16 RoPE dims) by direct-to-LDS loads issued one tile ahead; a tile
-//            holding window tokens is written as BF16 rows by the wavefronts;
+//            then BF16 RoPE dims) by direct-to-LDS loads issued one tile ahead; a window tile
+//            (BF16 window) is copied the same way as BF16 rows; a tile mixing entries and
+//            window tokens, or an fp32 window, is written as BF16 rows by the wavefronts;
 //   scores:  S^T = E Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims read key-major,
 //            FP8 codes converted exactly to BF16 in registers; B = the wavefront's 16 query
 //            heads held in registers), accumulating the FP8 dims and the BF16 RoPE dims
@@ -42,6 +43,8 @@ constexpr int kTile = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running maximum may lag the scores
 constexpr int kMaxSelKeys = 2048;  // top-k entries per sequence (k <= 2048)
+constexpr int kQkAhead = 1;        // score k-steps whose operands are requested ahead of use
+constexpr int kPvAhead = 2;        // value dim tiles whose operands are requested ahead of use
 
 struct AttnParams {
     const void *q;           // [B][H][D]
@@ -184,12 +187,13 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     constexpr int RS16 = D + 8;            // LDS row stride of a BF16 tile (in BF16)
     constexpr int NCH8 = kTile * RC8;      // chunks of an entry tile
     static_assert(Dn % 32 == 0 && R % 32 == 0, "k-steps are all FP8 or all BF16 dims");
-    __shared__ __attribute__((aligned(16))) uint8_t E8[2][kTile * RS8];   // entry tiles (two)
-    __shared__ __attribute__((aligned(16))) float ksc8[2][kTile];
-    __shared__ int kval8[2][kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t E16[kTile * RS16];    // window / mixed tile
-    __shared__ __attribute__((aligned(16))) float ksc16[kTile];
-    __shared__ int kval16[kTile];
+    constexpr int RC16 = D / 8 + 1;        // 16-byte chunks per BF16 LDS row (one of padding)
+    constexpr int NCH16 = kTile * RC16;    // chunks of a BF16 tile
+    constexpr int TBYTES = kTile * RS8 > 2 * kTile * RS16 ? kTile * RS8 : 2 * kTile * RS16;
+    // two tile buffers: an entry tile in its storage layout or a BF16 tile (window rows)
+    __shared__ __attribute__((aligned(16))) uint8_t TB[2][TBYTES];
+    __shared__ __attribute__((aligned(16))) float ksc[2][kTile];
+    __shared__ int kval[2][kTile];
     __shared__ int32_t sidx[kMaxSelKeys];  // this split's top-k entry indices (CSA)
 
     // workgroup -> (sequence, split, head group); head groups of one split 8 ids apart.  A
@@ -294,7 +298,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     }
 
     const int NW = NT >> 6;
-    // ---- entry tile tb -> E8[q]: wavefront w issues the direct-to-LDS loads w, w + NW, ...
+    // ---- entry tile tb -> TB[q]: wavefront w issues the direct-to-LDS loads w, w + NW, ...
     // (64 chunks each; chunk c of LDS row r is chunk c of key r's record, the last is padding)
     auto issue_entries = [&](int tb, int q) {
         for (int inst = wv; inst * 64 < NCH8; inst += NW) {
@@ -307,22 +311,44 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 const uint8_t *src = !ok ? g_zero_row
                                          : (16 * c < Dn ? P.nope + row * Dn + 16 * c
                                                         : (const uint8_t *)P.rope + row * (2 * R) + (16 * c - Dn));
-                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&E8[q][inst * 1024], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][inst * 1024], 16, 0, 0);
             }
         }
         if (wv == NW - 1 && lane < kTile) {
             const int64_t e = P.topk ? (int64_t)sidx[tb + lane - kb0] : (int64_t)(tb + lane);
             const bool ok = e >= 0 && e < P.cap;
             const float *src = ok ? P.kscale + (int64_t)b * P.kv_bstride + e : (const float *)g_zero_row;
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc8[q][0], 4, 0, 0);
-            kval8[q][lane] = ok ? 1 : 0;
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc[q][0], 4, 0, 0);
+            kval[q][lane] = ok ? 1 : 0;
         }
     };
-    // ---- window / mixed tile -> E16 (BF16 rows), by the wavefronts: task (kg, seg) = keys
+    // ---- window tile tb (BF16 rows, 16-byte aligned) -> TB[q] as BF16 LDS rows, by direct-to-LDS
+    // loads like the entry tiles; keys past the split read zeros and are masked
+    const bool win_dma = P.win_bf16 && ((uintptr_t)P.win & 15) == 0;
+    auto issue_window = [&](int tb, int q) {
+        for (int inst = wv; inst * 64 < NCH16; inst += NW) {
+            const int qq = inst * 64 + lane;
+            if (qq < NCH16) {
+                const int r = qq / RC16, c = qq - r * RC16;
+                const bool ok = tb + r < kb1 && c < RC16 - 1;
+                const uint8_t *src = ok ? (const uint8_t *)P.win + wr.row(tb + r - n_ent) * (2 * D) + 16 * c : g_zero_row;
+                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][inst * 1024], 16, 0, 0);
+            }
+        }
+        if (wv == NW - 1 && lane < kTile) {
+            ksc[q][lane] = 1.0f;
+            kval[q][lane] = tb + lane < kb1 ? 1 : 0;
+        }
+    };
+    // 0: entry tile (direct loads); 1: window tile (direct loads); 2: staged by the wavefronts
+    // (entries and window rows mixed, or an fp32 window)
+    auto tile_kind = [&](int tb) { return tb + kTile <= n_ent ? 0 : (tb >= n_ent && win_dma ? 1 : 2); };
+    // ---- mixed tile (or fp32 window) -> TB[q] as BF16 rows, by the wavefronts: task (kg, seg) = keys
     // 4kg..4kg+3, dims 8seg..8seg+7; all loads of a task are issued before any is used
     constexpr int NSEG = D / 8;
     constexpr int NTASK = 8 * NSEG;
-    auto stage_bf16 = [&](int tb) {
+    auto stage_bf16 = [&](int tb, int q) {
+        uint16_t *E16 = (uint16_t *)TB[q];
         const bool win_only = tb >= n_ent;
         for (int task = t; task < NTASK; task += NT) {
             const int kg = task & 7, seg = task >> 3, dim = 8 * seg;
@@ -370,8 +396,8 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
             if (seg == 0) {
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    ksc16[4 * kg + j] = scl[j];
-                    kval16[4 * kg + j] = valid[j] ? 1 : 0;
+                    ksc[q][4 * kg + j] = scl[j];
+                    kval[q][4 * kg + j] = valid[j] ? 1 : 0;
                 }
             }
 #pragma unroll
@@ -379,9 +405,10 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         }
     };
 
-    const float *tksc = ksc8[0];
-    const int *tkval = kval8[0];
-    const uint8_t *e8 = E8[0];
+    const float *tksc = ksc[0];
+    const int *tkval = kval[0];
+    const uint8_t *e8 = TB[0];
+    const uint16_t *e16 = (const uint16_t *)TB[0];
     // A operand of the scores: key r, dims 32ks + 8grp .. +7
     auto qk_operand = [&](auto f8, int r, int ks) -> v8bf {
         if constexpr (decltype(f8)::value) {
@@ -391,7 +418,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
             }
             return __builtin_bit_cast(v8bf, *(const uint4 *)(e8 + r * RS8 + Dn + 2 * (32 * ks - Dn + 8 * grp)));
         } else {
-            return __builtin_bit_cast(v8bf, *(const uint4 *)(E16 + r * RS16 + 32 * ks + 8 * grp));
+            return __builtin_bit_cast(v8bf, *(const uint4 *)(e16 + r * RS16 + 32 * ks + 8 * grp));
         }
     };
     // A operand of the values: dims 16dt + col, keys k(grp, 0..7)
@@ -412,9 +439,9 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         } else {
             const int off = 16 * dt + 4 * (col & 3);
             const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_t *)(E16 + pv_key(grp, col >> 2) * RS16 + off));
+                (__attribute__((address_space(3))) v4s_t *)(e16 + pv_key(grp, col >> 2) * RS16 + off));
             const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_t *)(E16 + pv_key(grp, 4 + (col >> 2)) * RS16 + off));
+                (__attribute__((address_space(3))) v4s_t *)(e16 + pv_key(grp, 4 + (col >> 2)) * RS16 + off));
             return __builtin_bit_cast(v8bf, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
                                                        __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
         }
@@ -423,35 +450,65 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     // the split's indices are in LDS before the first tile's loads
     __syncthreads();
     int q = 0;
-    if (kb0 < kb1 && kb0 + kTile <= n_ent) issue_entries(kb0, 0);
+    auto issue = [&](int tb, int q) {
+        const int kind = tile_kind(tb);
+        if (kind == 0) issue_entries(tb, q);
+        else if (kind == 1) issue_window(tb, q);
+    };
+    if (kb0 < kb1) issue(kb0, 0);
     for (int tb = kb0; tb < kb1; tb += kTile) {
-        const bool f8 = tb + kTile <= n_ent;  // an entry tile (uniform)
-        if (!f8) {
-            __syncthreads();  // the previous tile's readers are done with E16
-            stage_bf16(tb);
-        }
+        const int kind = tile_kind(tb);  // uniform
+        if (kind == 2) stage_bf16(tb, q);
         // this tile is in LDS: each wavefront waits for its own direct loads, then the barrier
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // the next entry tile travels while this one is computed
+        // the next tile travels while this one is computed
         const int tn = tb + kTile;
-        if (tn < kb1 && tn + kTile <= n_ent) issue_entries(tn, q ^ 1);
-        if (wave_on && f8) {
-            tksc = ksc8[q];
-            tkval = kval8[q];
-            e8 = E8[q];
+        if (tn < kb1) issue(tn, q ^ 1);
+        tksc = ksc[q];
+        tkval = kval[q];
+        if (wave_on && kind == 0) {
+            e8 = TB[q];
                 // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
                 float s2[8], ks8[8];
+                // both halves' chains advance together, the raw operands of k-step ks + kQkAhead
+                // requested before k-step ks is converted and multiplied
+                v4f an2[2], ar2[2];
+                {
+                    uint2 raw8[NKS][2];
+                    uint4 raw16[NKS][2];
+                    auto request = [&](int ks) {
 #pragma unroll
-                for (int st = 0; st < 2; st++) {
-                    v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const int r = 16 * st + col;
+                        for (int st = 0; st < 2; st++) {
+                            const uint8_t *row = e8 + (16 * st + col) * RS8;
+                            if (32 * ks < Dn) raw8[ks][st] = *(const uint2 *)(row + 32 * ks + 8 * grp);
+                            else raw16[ks][st] = *(const uint4 *)(row + Dn + 2 * (32 * ks - Dn + 8 * grp));
+                        }
+                    };
+#pragma unroll
+                    for (int st = 0; st < 2; st++) {
+                        an2[st] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                        ar2[st] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < kQkAhead; ks++) request(ks);
 #pragma unroll
                     for (int ks = 0; ks < NKS; ks++) {
-                        const v8bf a = qk_operand(std::true_type{}, r, ks);
-                        if (32 * ks < Dn) an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], an, 0, 0, 0);
-                        else ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[ks], ar, 0, 0, 0);
+                        if (ks + kQkAhead < NKS) request(ks + kQkAhead);
+#pragma unroll
+                        for (int st = 0; st < 2; st++) {
+                            if (32 * ks < Dn)
+                                an2[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_bf16(raw8[ks][st].x, raw8[ks][st].y),
+                                                                                 qT[ks], an2[st], 0, 0, 0);
+                            else
+                                ar2[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, raw16[ks][st]),
+                                                                                 qT[ks], ar2[st], 0, 0, 0);
+                        }
                     }
+                }
+#pragma unroll
+                for (int st = 0; st < 2; st++) {
+                    const v4f an = an2[st], ar = ar2[st];
                     const float4 sc4 = *(const float4 *)(tksc + 16 * st + 4 * grp);
                     const int4 kv4 = *(const int4 *)(tkval + 16 * st + 4 * grp);
                     const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
@@ -493,14 +550,39 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                     Pr[i] = (__bf16)pr[i];
                 }
                 // ---- values O^T += E^T P^T; A row = dim 16*dt + col, keys {4grp..+3, 16+4grp..+3}
+                {
+                    // raw operands of dim tile dt + kPvAhead requested before tile dt is used
+                    v2i_t rv8[NDT];
+                    v4s_t rlo[NDT], rhi[NDT];
+                    auto request = [&](int dt) {
+                        if (16 * dt < Dn) {
+                            rv8[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (__attribute__((address_space(3))) v2i_t *)(e8 + pv_key(grp, col >> 1) * RS8 + 16 * dt + 8 * (col & 1)));
+                        } else {
+                            const int off = Dn + 2 * (16 * dt - Dn + 4 * (col & 3));
+                            rlo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) v4s_t *)(e8 + pv_key(grp, col >> 2) * RS8 + off));
+                            rhi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) v4s_t *)(e8 + pv_key(grp, 4 + (col >> 2)) * RS8 + off));
+                        }
+                    };
 #pragma unroll
-                for (int dt = 0; dt < NDT; dt++) {
-                    const v8bf a = pv_operand(std::true_type{}, dt);
-                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
+                    for (int dt = 0; dt < kPvAhead; dt++) request(dt);
+#pragma unroll
+                    for (int dt = 0; dt < NDT; dt++) {
+                        if (dt + kPvAhead < NDT) request(dt + kPvAhead);
+                        v8bf a;
+                        if (16 * dt < Dn) {
+                            a = fp8x8_bf16((uint32_t)rv8[dt].x, (uint32_t)rv8[dt].y);
+                        } else {
+                            const uint2 lo = __builtin_bit_cast(uint2, rlo[dt]), hi = __builtin_bit_cast(uint2, rhi[dt]);
+                            a = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                        }
+                        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
+                    }
                 }
         } else if (wave_on) {
-            tksc = ksc16;
-            tkval = kval16;
+            e16 = (const uint16_t *)TB[q];
                 // ---- scores S^T for keys 0-15 (st = 0) and 16-31 (st = 1)
                 float s2[8], ks8[8];
 #pragma unroll
@@ -560,7 +642,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                     O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, (16 * dt < Dn) ? Pn : Pr, O[dt], 0, 0, 0);
                 }
         }
-        if (f8) q ^= 1;
+        q ^= 1;
         __syncthreads();      // readers of this tile's buffer are done before it is refilled
     }
     if (!wave_on) return;
