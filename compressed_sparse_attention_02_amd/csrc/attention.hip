@@ -226,76 +226,24 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     const int NT = blockDim.x;
 
     // query heads as the B operand of S^T: lane holds head h, dims 32*ks + 8*grp + j
-    v8bf qT[NKS];
+    uint4 qu[NKS];  // the raw query rows: unconditional loads (a wavefront without heads reads head 0 and never uses it)
     {
+        // the split's selected entry indices (read once for all its tiles) are requested before
+        // the queries and stored to LDS as soon as they arrive, so the first tile's loads leave
+        // while the queries are still in flight
+        const int e1 = P.topk ? min(kb1, n_ent) : kb0;
+        const bool has0 = kb0 + t < e1;
+        const int sidx0 = has0 ? P.topk[(int64_t)b * P.k + kb0 + t] : 0;
         const uint16_t *qr = (const uint16_t *)P.q + ((int64_t)b * P.H + (wave_on ? h : 0)) * D;
-        uint4 qu[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++)
-            qu[ks] = wave_on ? *(const uint4 *)(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0);
-        if (P.q_norm_w) {
-            // Query prologue ("DeepSeek-V4 technical report walkthrough", section 2.3: RMSNorm acts
-            // directly on the queries): RMSNorm of the head over its D dims (a head's dims sit in
-            // lanes col, col+16, col+32, col+48), RoPE at the query position on the last R dims
-            // (pairs inside a lane's 8 consecutive dims; Dn is a multiple of 32, so a k-step is
-            // all RoPE dims or none), then BF16 (nearest even) as the MFMA operand.
-            float ss = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float lo = __builtin_bit_cast(float, w4[j] << 16);
-                    const float hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
-                    ss = fmaf(lo, lo, ss);
-                    ss = fmaf(hi, hi, ss);
-                }
-            }
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            const float rn = 1.0f / sqrtf(ss / (float)D + kNormEps);
-            RopeLanes rl;
-            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
-                const float4 wa = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp);
-                const float4 wb = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp + 4);
-                const float wv8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-                float y[8];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    y[2 * j] = __builtin_bit_cast(float, w4[j] << 16) * rn * wv8[2 * j];
-                    y[2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u) * rn * wv8[2 * j + 1];
-                }
-                if (32 * ks >= Dn) {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float2 cs = rl.get(16 * (ks - Dn / 32) + 4 * grp + i);
-                        const float x0 = y[2 * i], x1 = y[2 * i + 1];
-                        y[2 * i] = x0 * cs.x - x1 * cs.y;
-                        y[2 * i + 1] = x0 * cs.y + x1 * cs.x;
-                    }
-                }
-                v8bf qv;
-#pragma unroll
-                for (int j = 0; j < 8; j++) qv[j] = (__bf16)y[j];
-                qT[ks] = qv;
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks++) qT[ks] = __builtin_bit_cast(v8bf, qu[ks]);
-        }
+        for (int ks = 0; ks < NKS; ks++) qu[ks] = *(const uint4 *)(qr + 32 * ks + 8 * grp);
+        if (has0) sidx[t] = sidx0;
+        for (int j = kb0 + t + NT; j < e1; j += NT) sidx[j - kb0] = P.topk[(int64_t)b * P.k + j];
     }
     v4f O[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
-    // the split's selected entry indices, read once (one load round for all its tiles)
-    if (P.topk) {
-        const int e1 = min(kb1, n_ent);
-        for (int j = kb0 + t; j < e1; j += NT) sidx[j - kb0] = P.topk[(int64_t)b * P.k + j];
-    }
 
     const int NW = NT >> 6;
     // ---- entry tile tb -> TB[q]: wavefront w issues the direct-to-LDS loads w, w + NW, ...
@@ -447,8 +395,9 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         }
     };
 
-    // the split's indices are in LDS before the first tile's loads
-    __syncthreads();
+    // the split's indices are in LDS before the first tile's loads (an LDS-only barrier: the
+    // query loads may still be in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     int q = 0;
     auto issue = [&](int tb, int q) {
         const int kind = tile_kind(tb);
@@ -456,6 +405,64 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         else if (kind == 1) issue_window(tb, q);
     };
     if (kb0 < kb1) issue(kb0, 0);
+    // the queries as MFMA operands (after the first tile's loads left: the wait for the query
+    // rows falls here)
+    v8bf qT[NKS];
+    {
+        if (P.q_norm_w) {
+            // Query prologue ("DeepSeek-V4 technical report walkthrough", section 2.3: RMSNorm acts
+            // directly on the queries): RMSNorm of the head over its D dims (a head's dims sit in
+            // lanes col, col+16, col+32, col+48), RoPE at the query position on the last R dims
+            // (pairs inside a lane's 8 consecutive dims; Dn is a multiple of 32, so a k-step is
+            // all RoPE dims or none), then BF16 (nearest even) as the MFMA operand.
+            float ss = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float lo = __builtin_bit_cast(float, w4[j] << 16);
+                    const float hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
+                    ss = fmaf(lo, lo, ss);
+                    ss = fmaf(hi, hi, ss);
+                }
+            }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float rn = 1.0f / sqrtf(ss / (float)D + kNormEps);
+            RopeLanes rl;
+            rl.eval(P.rt, R / 2, (double)sq_pos(Sq, b));
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const uint32_t w4[4] = {qu[ks].x, qu[ks].y, qu[ks].z, qu[ks].w};
+                const float4 wa = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp);
+                const float4 wb = *(const float4 *)(P.q_norm_w + 32 * ks + 8 * grp + 4);
+                const float wv8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+                float y[8];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    y[2 * j] = __builtin_bit_cast(float, w4[j] << 16) * rn * wv8[2 * j];
+                    y[2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u) * rn * wv8[2 * j + 1];
+                }
+                if (32 * ks >= Dn) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float2 cs = rl.get(16 * (ks - Dn / 32) + 4 * grp + i);
+                        const float x0 = y[2 * i], x1 = y[2 * i + 1];
+                        y[2 * i] = x0 * cs.x - x1 * cs.y;
+                        y[2 * i + 1] = x0 * cs.y + x1 * cs.x;
+                    }
+                }
+                v8bf qv;
+#pragma unroll
+                for (int j = 0; j < 8; j++) qv[j] = (__bf16)y[j];
+                qT[ks] = qv;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) qT[ks] = __builtin_bit_cast(v8bf, qu[ks]);
+        }
+    }
     for (int tb = kb0; tb < kb1; tb += kTile) {
         const int kind = tile_kind(tb);  // uniform
         if (kind == 2) stage_bf16(tb, q);
