@@ -453,7 +453,7 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // ((e1 + e5) + (e3 + e7)), written here in that order.
 template <int VPT>
 __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t seq, int64_t i,
-                                           uint8_t *idx_mirror) {
+                                           uint8_t *idx_mirror, bool to_global = true) {
     const int lane = threadIdx.x & 63;
     const int n_cand = entry_candidates(P, i);
     const float z = lane < n_cand ? kp.gl + kp.bl : -INFINITY;
@@ -491,7 +491,7 @@ __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<
 #pragma unroll
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] * r * kp.nw[v];
     }
-    store_mxfp4<VPT>(acc, lane, true, P.D, P.idx, P.out_row0 + seq * P.cap + i, idx_mirror);
+    store_mxfp4<VPT>(acc, lane, true, P.D, P.idx, P.out_row0 + seq * P.cap + i, idx_mirror, to_global);
 }
 
 // Kernel parameters of a checked CompressArgs (host).

@@ -64,7 +64,8 @@ __device__ __forceinline__ void store_record(const float (&x)[VPT], int lane_dim
 // in the same order as in the cache row.
 template <int VPT>
 __device__ __forceinline__ void store_mxfp4(const float (&x)[VPT], int lane, bool active, int d,
-                                            const v4a_idx &out, int64_t row, uint8_t *mirror = nullptr) {
+                                            const v4a_idx &out, int64_t row, uint8_t *mirror = nullptr,
+                                            bool to_global = true) {
     if (out.fmt == V4A_IDX_F32) {
         if (active) {
             float *dst = (float *)out.codes + row * d + lane * VPT;
@@ -108,13 +109,13 @@ __device__ __forceinline__ void store_mxfp4(const float (&x)[VPT], int lane, boo
         if (active) {
 #pragma unroll
             for (int i = 0; i < VPT / 2; i++) {
-                dst[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
+                if (to_global) dst[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
                 if (mirror) mirror[lane * VPT / 2 + i] = (uint8_t)(codes >> (8 * i));
             }
         }
     }
     if (active && (lane % group) == 0) {
-        out.scales[row * (d / 32) + lane / group] = (uint8_t)(X + 127);
+        if (to_global) out.scales[row * (d / 32) + lane / group] = (uint8_t)(X + 127);
         if (mirror) mirror[d / 2 + lane / group] = (uint8_t)(X + 127);
     }
 }

@@ -81,6 +81,18 @@ __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint3
     lds_barrier();
     if (!P.hist) return;
     uint32_t *gh = P.hist + ((int64_t)qi * P.hist_copies + (int)(blockIdx.x % (unsigned)P.hist_copies)) * kHistBins;
+    // consecutive bins in consecutive lanes, so the few hot bins of a query leave in one wide
+    // atomic instruction per cache line; all LDS reads are issued before the first atomic
+    constexpr int kPer = 16;  // bins per thread with 256 threads
+    if (blockDim.x * kPer == kHistBins) {
+        uint32_t c[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; i++) c[i] = lhist[threadIdx.x + i * 256];
+#pragma unroll
+        for (int i = 0; i < kPer; i++)
+            if (c[i]) atomicAdd(&gh[threadIdx.x + i * 256], c[i]);
+        return;
+    }
     for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
         uint32_t c = lhist[bin];
         if (c) atomicAdd(&gh[bin], c);
@@ -226,18 +238,11 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
             }
         }
     };
-    for (int it = 0; it < n_it; it += 2) {
-        if (wbase + (int64_t)it * kGroupsPerIter * 16 >= kend) break;  // uniform over the wavefront
-        const bool more1 = it + 1 < n_it && wbase + (int64_t)(it + 1) * kGroupsPerIter * 16 < kend;
-        if (more1) load_iter(it + 1, kdB, kscB);
-        compute_iter(it, kdA, kscA);
-        if (!more1) break;
-        const bool more2 = it + 2 < n_it && wbase + (int64_t)(it + 2) * kGroupsPerIter * 16 < kend;
-        if (more2) load_iter(it + 2, kdA, kscA);
-        compute_iter(it + 1, kdB, kscB);
-    }
-    if (own) {
-        key_finish<2>(P.key, kp, qi, i_new, knew);
+    // the new key: merged, encoded (into LDS) and scored right after the first iteration, while
+    // the rest of the stream is in flight; its score replaces the stale one after the stream
+    float sc_new = 0.0f;
+    auto new_key = [&]() {
+        key_finish<2>(P.key, kp, qi, i_new, knew, false);
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -245,7 +250,26 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         const float c = key_chain(*(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64));
         float sc = ((lane_value(c, 0) + lane_value(c, 16)) + lane_value(c, 32)) + lane_value(c, 48);
         if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
-        if (lane == 0) sbuf[i_new - k0] = sc;
+        sc_new = sc;
+    };
+    for (int it = 0; it < n_it; it += 2) {
+        if (wbase + (int64_t)it * kGroupsPerIter * 16 >= kend) break;  // uniform over the wavefront
+        const bool more1 = it + 1 < n_it && wbase + (int64_t)(it + 1) * kGroupsPerIter * 16 < kend;
+        if (more1) load_iter(it + 1, kdB, kscB);
+        compute_iter(it, kdA, kscA);
+        if (own && it == 0) new_key();
+        if (!more1) break;
+        const bool more2 = it + 2 < n_it && wbase + (int64_t)(it + 2) * kGroupsPerIter * 16 < kend;
+        if (more2) load_iter(it + 2, kdA, kscA);
+        compute_iter(it + 1, kdB, kscB);
+    }
+    if (own) {
+        if (lane == 0) sbuf[i_new - k0] = sc_new;
+        // the key's cache row (64 code bytes, 4 scale bytes) from its LDS copy; global stores
+        // wait until here since they would hold up the stream's loads (one shared counter)
+        const int64_t row = P.key.out_row0 + (int64_t)qi * P.key.cap + i_new;
+        if (lane < 16) ((uint32_t *)((uint8_t *)P.key.idx.codes + row * 64))[lane] = ((const uint32_t *)knew)[lane];
+        if (lane == 16) *(uint32_t *)(P.key.idx.scales + row * 4) = *(const uint32_t *)(knew + 64);
     }
     // the streaming loop touched only registers and LDS; now the scores leave in 16-byte stores
     // and the histogram is counted from LDS
