@@ -185,10 +185,8 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     constexpr int RC8 = RB8 / 16 + 1;      // 16-byte chunks per LDS row (one of padding)
     constexpr int RS8 = 16 * RC8;          // LDS row stride of an entry tile
     constexpr int RS16 = D + 8;            // LDS row stride of a BF16 tile (in BF16)
-    constexpr int NCH8 = kTile * RC8;      // chunks of an entry tile
     static_assert(Dn % 32 == 0 && R % 32 == 0, "k-steps are all FP8 or all BF16 dims");
-    constexpr int RC16 = D / 8 + 1;        // 16-byte chunks per BF16 LDS row (one of padding)
-    constexpr int NCH16 = kTile * RC16;    // chunks of a BF16 tile
+    static_assert(RB8 % 16 == 0 && RB8 / 16 <= 64 && 2 * D / 16 <= 64, "one direct-load instruction covers an LDS row");
     constexpr int TBYTES = kTile * RS8 > 2 * kTile * RS16 ? kTile * RS8 : 2 * kTile * RS16;
     // two tile buffers: an entry tile in its storage layout or a BF16 tile (window rows)
     __shared__ __attribute__((aligned(16))) uint8_t TB[2][TBYTES];
@@ -246,47 +244,39 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     float m_run = -INFINITY, l_run = 0.0f;
 
     const int NW = NT >> 6;
-    // ---- entry tile tb -> TB[q]: wavefront w issues the direct-to-LDS loads w, w + NW, ...
-    // (64 chunks each; chunk c of LDS row r is chunk c of key r's record, the last is padding)
+    // ---- entry tile tb -> TB[q]: one direct-to-LDS load instruction per LDS row, wavefront w
+    // taking rows w, w + NW, ...: M0 at the row's start, lane c copying 16-byte chunk c of the
+    // key's record (FP8 codes, then BF16 RoPE dims).  A row's entry index is uniform: lane r of
+    // every wavefront reads row r's index once per tile and readlane hands it over.
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
     auto issue_entries = [&](int tb, int q) {
-        for (int inst = wv; inst * 64 < NCH8; inst += NW) {
-            const int qq = inst * 64 + lane;
-            if (qq < NCH8) {
-                const int r = qq / RC8, c = qq - r * RC8;
-                const int64_t e = P.topk ? (int64_t)sidx[tb + r - kb0] : (int64_t)(tb + r);
-                const bool ok = e >= 0 && e < P.cap && c < RC8 - 1;
-                const int64_t row = (int64_t)b * P.kv_bstride + (ok ? e : 0);
-                const uint8_t *src = !ok ? g_zero_row
-                                         : (16 * c < Dn ? P.nope + row * Dn + 16 * c
-                                                        : (const uint8_t *)P.rope + row * (2 * R) + (16 * c - Dn));
-                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][inst * 1024], 16, 0, 0);
-            }
+        const int my_e = P.topk ? (lane < kTile ? sidx[tb + lane - kb0] : 0) : tb + lane;
+        for (int r = wvu; r < kTile; r += NW) {
+            const int e = __builtin_amdgcn_readlane(my_e, r);
+            const bool ok = e >= 0 && (int64_t)e < P.cap;
+            const int64_t row = (int64_t)b * P.kv_bstride + (ok ? e : 0);
+            const uint8_t *src = !ok ? g_zero_row
+                                     : (16 * lane < Dn ? P.nope + row * Dn + 16 * lane
+                                                       : (const uint8_t *)P.rope + row * (2 * R) + (16 * lane - Dn));
+            if (lane < RB8 / 16) __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][r * RS8], 16, 0, 0);
         }
         if (wv == NW - 1 && lane < kTile) {
-            const int64_t e = P.topk ? (int64_t)sidx[tb + lane - kb0] : (int64_t)(tb + lane);
-            const bool ok = e >= 0 && e < P.cap;
-            const float *src = ok ? P.kscale + (int64_t)b * P.kv_bstride + e : (const float *)g_zero_row;
+            const bool ok = my_e >= 0 && (int64_t)my_e < P.cap;
+            const float *src = ok ? P.kscale + (int64_t)b * P.kv_bstride + my_e : (const float *)g_zero_row;
             __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc[q][0], 4, 0, 0);
             kval[q][lane] = ok ? 1 : 0;
         }
     };
-    // ---- window tile tb (BF16 rows, 16-byte aligned) -> TB[q] as BF16 LDS rows, by direct-to-LDS
-    // loads like the entry tiles; keys past the split read zeros and are masked
+    // ---- window tile tb (BF16 rows, 16-byte aligned) -> TB[q] as BF16 LDS rows, one direct load
+    // instruction per row as for the entry tiles; keys past the split read zeros and are masked
     const bool win_dma = P.win_bf16 && ((uintptr_t)P.win & 15) == 0;
     auto issue_window = [&](int tb, int q) {
-        for (int inst = wv; inst * 64 < NCH16; inst += NW) {
-            const int qq = inst * 64 + lane;
-            if (qq < NCH16) {
-                const int r = qq / RC16, c = qq - r * RC16;
-                const bool ok = tb + r < kb1 && c < RC16 - 1;
-                const uint8_t *src = ok ? (const uint8_t *)P.win + wr.row(tb + r - n_ent) * (2 * D) + 16 * c : g_zero_row;
-                __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][inst * 1024], 16, 0, 0);
-            }
+        for (int r = wvu; r < kTile; r += NW) {
+            const bool ok = tb + r < kb1;
+            const uint8_t *src = ok ? (const uint8_t *)P.win + wr.row(tb + r - n_ent) * (2 * D) + 16 * lane : g_zero_row;
+            if (lane < 2 * D / 16) __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][r * 2 * RS16], 16, 0, 0);
         }
-        if (wv == NW - 1 && lane < kTile) {
-            ksc[q][lane] = 1.0f;
-            kval[q][lane] = tb + lane < kb1 ? 1 : 0;
-        }
+        // a window tile's scales (1) and validity (key < kb1) are derived where they are used
     };
     // 0: entry tile (direct loads); 1: window tile (direct loads); 2: staged by the wavefronts
     // (entries and window rows mixed, or an fp32 window)
@@ -604,8 +594,11 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                     }
                     const float4 sc4 = *(const float4 *)(tksc + 16 * st + 4 * grp);
                     const int4 kv4 = *(const int4 *)(tkval + 16 * st + 4 * grp);
-                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-                    const int kvv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+                    const bool wt = kind == 1;  // a window tile: scale 1, keys below kb1 valid
+                    const int kr = tb + 16 * st + 4 * grp;
+                    const float scv[4] = {wt ? 1.0f : sc4.x, wt ? 1.0f : sc4.y, wt ? 1.0f : sc4.z, wt ? 1.0f : sc4.w};
+                    const int kvv[4] = {wt ? (int)(kr < kb1) : kv4.x, wt ? (int)(kr + 1 < kb1) : kv4.y,
+                                        wt ? (int)(kr + 2 < kb1) : kv4.z, wt ? (int)(kr + 3 < kb1) : kv4.w};
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         s2[4 * st + i] = kvv[i] ? P.scale2 * fmaf(scv[i], an[i], ar[i]) : -INFINITY;
