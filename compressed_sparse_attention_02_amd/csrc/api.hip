@@ -467,9 +467,17 @@ namespace v4a {
 
 constexpr int kDecodeSplitTarget = 16;
 
+// The most splits any sequence of at most n_keys_max keys gets (the plan is not monotonic in the
+// key count: short lists take at most two tiles per split).
 static int decode_split_cap(int64_t n_keys_max) {
-    int64_t tiles = (n_keys_max + kAttnTile - 1) / kAttnTile;
-    return (int)(tiles < kDecodeSplitTarget ? (tiles < 1 ? 1 : tiles) : kDecodeSplitTarget);
+    int cap = 1;
+    const int64_t n = n_keys_max < (int64_t)kAttnTile * 4096 ? n_keys_max : (int64_t)kAttnTile * 4096;
+    for (int64_t tiles = 1; tiles * kAttnTile <= n + kAttnTile - 1; tiles++) {
+        int tps, sp;
+        split_plan_host((int)(tiles * kAttnTile), kDecodeSplitTarget, &tps, &sp);
+        if (sp > cap) cap = sp;
+    }
+    return cap;
 }
 
 static size_t decode_ws_bytes(int B, int H, int D, int split_cap) {

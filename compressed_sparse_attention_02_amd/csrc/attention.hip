@@ -77,10 +77,15 @@ struct AttnParams {
     int item0;               // split-free launches: first (query, head group) item
 };
 
+constexpr int kShortTiles = 48;  // key lists of at most this many tiles take <= 2 tiles per split
+
 __host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int *tps, int *splits) {
     int tiles = (n_keys + kTile - 1) / kTile;
     int t = (tiles + target - 1) / target;
     if (t < 1) t = 1;
+    // a short key list (a top-k selection and its window) is latency-bound: at most two tiles
+    // per split, so each workgroup's serial chain is short (a function of the key count only)
+    if (target > 1 && tiles <= kShortTiles && t > 2) t = 2;
     int s = (tiles + t - 1) / t;
     if (s < 1) s = 1;
     *tps = t;
