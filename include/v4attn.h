@@ -234,7 +234,9 @@ V4A_API v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32
                           const int64_t *q_pos, float softmax_scale, int32_t out_rope_inverse,
                           float rope_theta, void *out, v4a_float out_t, void *ws,
                           size_t ws_bytes, void *stream);
-/* Workspace for either decode call: n_keys_max = k (CSA) or max entries (HCA), plus W. */
+/* Workspace for either decode call: n_keys_max = k (CSA) or max entries (HCA), plus W.  It
+ * bounds every sequence of at most n_keys_max keys (a short key list takes more, smaller
+ * splits than a long one, so the bound can exceed what one long sequence needs). */
 V4A_API size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_keys_max, int32_t W);
 
 /* -------------------------------------------------------------- a8: prefill chunk ----

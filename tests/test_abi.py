@@ -291,7 +291,12 @@ def hca_step_struct(**kw):
 def test_decode_step_hca_workspace_and_rejects():
     L = v4.lib()
     need = L.v4a_decode_step_hca_workspace(ctypes.byref(hca_step_struct()))
-    assert need == v4.v4a_decode_workspace(16, 128, 512, 8192, 128)
+    # the step sizes for its own sequences (8192 entries + 128 window = 260 tiles: 16 splits of
+    # fp32 partials plus (m, l)); the generic query bounds any sequence up to that many keys,
+    # shorter lists included (up to 24 splits of two tiles)
+    assert need == 16 * 16 * 128 * (512 + 2) * 4
+    assert need <= v4.v4a_decode_workspace(16, 128, 512, 8192, 128)
+    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) == 16 * 24 * 128 * (512 + 2) * 4
     assert need % 256 == 0
 
     def call(ws=FAKE, wsb=1 << 40, **kw):
