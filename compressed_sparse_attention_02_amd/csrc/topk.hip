@@ -31,7 +31,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kLdsList = 12288;   // listed keys the finalize kernel keeps in LDS
 constexpr int kMaxSlices = 1024;  // n_max <= 8M keys
 constexpr int kSubBins = 1024;    // 10-bit digits of the low 20 score-key bits
-constexpr int kSelTPS = 16;       // finalize: threads per slice placing its listed keys
+constexpr int kSelTPS = 16;       // finalize: fewest threads per slice placing its listed keys
 constexpr int kSelSpec = 8;       // finalize: listed keys per thread requested with the counts
 
 int select_slices(int64_t n_max) {
@@ -263,17 +263,22 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     bool hist0 = false;  // the first pass's histogram was counted while the keys were placed
     uint32_t L;
     if (S <= kSelThreads / kSelTPS) {
-        // kSelTPS threads per slice request its count and its first kSelTPS * kSelSpec listed
-        // keys at once (slots past the count lie inside the slice's list region and are
-        // dropped), so counts and keys take one memory round trip; one block scan of the
-        // counts then places every key
-        const int sl = t / kSelTPS, p0 = t % kSelTPS;
+        // tps threads per slice (512 over the slice count rounded up to a power of two, at
+        // least kSelTPS) request its count and its first tps * kSelSpec listed keys at once
+        // (slots past the count lie inside the slice's list region and are dropped), so counts
+        // and keys take one memory round trip; one block scan of the counts then places every key
+        int tps = kSelThreads;
+        while (tps > kSelTPS && tps * S > kSelThreads) tps >>= 1;
+        const int sl = t / tps, p0 = t % tps;
         const bool live = sl < S;
         const uint32_t c = live ? cnts[sl] : 0u;
         const uint32_t *ls = lst + (int64_t)(live ? sl : 0) * kSelSlice * 2;
         uint2 e[kSelSpec];
 #pragma unroll
-        for (int u = 0; u < kSelSpec; u++) e[u] = live ? *(const uint2 *)(ls + 2 * (p0 + kSelTPS * u)) : make_uint2(0, 0);
+        for (int u = 0; u < kSelSpec; u++) {
+            const int pos = p0 + tps * u;  // < kSelSlice: inside the slice's list region
+            e[u] = live ? *(const uint2 *)(ls + 2 * pos) : make_uint2(0, 0);
+        }
         for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
         uint32_t tot;
         const uint32_t mine = (live && p0 == 0) ? c : 0u;
@@ -290,12 +295,24 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
             };
 #pragma unroll
             for (int u = 0; u < kSelSpec; u++) {
-                const uint32_t pos = (uint32_t)(p0 + kSelTPS * u);
+                const uint32_t pos = (uint32_t)(p0 + tps * u);
                 if (live && pos < c) put(pos, e[u]);
             }
-            // a slice that listed more keys than were requested
-            for (uint32_t pos = (uint32_t)(p0 + kSelTPS * kSelSpec); live && pos < c; pos += kSelTPS)
-                put(pos, *(const uint2 *)(ls + 2 * pos));
+            // a slice that listed more keys than were requested: further rounds of kSelSpec
+            // loads per thread, all issued before any is placed
+            for (uint32_t pos0 = (uint32_t)(p0 + tps * kSelSpec); live && pos0 < c; pos0 += (uint32_t)(tps * kSelSpec)) {
+                uint2 e2[kSelSpec];
+#pragma unroll
+                for (int u = 0; u < kSelSpec; u++) {
+                    const uint32_t pos = pos0 + (uint32_t)(tps * u);
+                    e2[u] = pos < c ? *(const uint2 *)(ls + 2 * pos) : make_uint2(0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < kSelSpec; u++) {
+                    const uint32_t pos = pos0 + (uint32_t)(tps * u);
+                    if (pos < c) put(pos, e2[u]);
+                }
+            }
         }
         __syncthreads();
     } else {
