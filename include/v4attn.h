@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     V4A_OK = 0,
     V4A_EINVAL = 1,        /* a pointer, size or position is invalid */
-    V4A_EUNSUPPORTED = 2,  /* a shape or format this build does not implement */
+    V4A_EUNSUPPORTED = 2,  /* a shape or format the library does not implement */
     V4A_EWORKSPACE = 3,    /* workspace missing, too small or misaligned */
     V4A_EHIP = 4           /* the HIP runtime reported an error at launch */
 } v4a_status;
