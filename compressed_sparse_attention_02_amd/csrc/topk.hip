@@ -118,6 +118,7 @@ template <bool K16>
 __global__ void __launch_bounds__(kSelThreads) select_scan_kernel(SelParams P, QueryPos QP) {
     constexpr int kBPT = kHistBins / kSelThreads;       // 8 bins per thread
     constexpr int kPer = kSelSlice / kSelThreads;       // 16 keys per thread
+    static_assert(kBPT == 8, "each thread reads its histogram bins as two 16-byte loads per copy");
     __shared__ uint32_t wsum[kSelWaves];
     __shared__ int sT;
     __shared__ uint32_t sAbove;
