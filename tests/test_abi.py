@@ -288,6 +288,20 @@ def hca_step_struct(**kw):
     return s
 
 
+def test_decode_workspace_follows_the_split_plan():
+    """The decode workspace holds B x splits x H x (D + 2) fp32 partials, where the split count
+    is the most any sequence up to the given key count takes: target 16 splits, at most two
+    32-key tiles per split for lists of at most 48 tiles."""
+    per = 128 * (512 + 2) * 4
+    # top-1024 + 128 window = 36 tiles: 18 splits of 2 tiles (33..36 tiles give 17..18)
+    assert v4.v4a_decode_workspace(4, 128, 512, 1024, 128) == 4 * 18 * per
+    # top-512 + 128 window = 20 tiles: lists of up to 16 tiles take one tile per split (16)
+    assert v4.v4a_decode_workspace(4, 128, 512, 512, 128) == 4 * 16 * per
+    # 48 tiles still take two per split (24); longer lists fall back to 16 splits
+    assert v4.v4a_decode_workspace(1, 128, 512, 48 * 32 - 128, 128) == 24 * per
+    assert v4.v4a_decode_workspace(1, 128, 512, 8192, 128) == 24 * per
+
+
 def test_decode_step_hca_workspace_and_rejects():
     L = v4.lib()
     need = L.v4a_decode_step_hca_workspace(ctypes.byref(hca_step_struct()))
