@@ -23,6 +23,7 @@
 //             to the threshold go lowest index first), so the output is ascending without a
 //             sort.
 #include "compress.hpp"
+#include "select_logic.hpp"
 
 namespace v4a {
 
@@ -95,13 +96,11 @@ __device__ __forceinline__ void find_threshold(const uint32_t (&c)[BPT], uint32_
     uint32_t tot;
     const uint32_t incl = block_scan(mine, wsum, &tot);
     const uint32_t over = tot - incl;  // held by threads above this one
-    if (over < need && need <= over + mine) {
-        uint32_t run = over;
-#pragma unroll
-        for (int b = BPT - 1; b >= 0; b--) {
-            if (run < need && need <= run + c[b]) { *sT = BPT * t + b; *sAbove = run; }
-            run += c[b];
-        }
+    int b;
+    uint32_t ab;
+    if (sel_threshold_in_run<BPT>(c, over, need, &b, &ab)) {
+        *sT = BPT * t + b;
+        *sAbove = ab;
     }
     __syncthreads();
     *T = *sT;
@@ -253,6 +252,12 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     }
     const int T = P.meta[2 * qi];
     const uint32_t above = (uint32_t)P.meta[2 * qi + 1];
+    // the scan's result is trusted only if it is consistent (a threshold bin, fewer than k_eff
+    // keys above it); otherwise nothing is selected rather than reading past a list
+    if (!sel_meta_consistent(T, above, k_eff)) {  // uniform over the workgroup
+        for (int j = t; j < P.k; j += kSelThreads) out[j] = -1;
+        return;
+    }
     const uint32_t need = k_eff - above;  // >= 1: keys still to take from bin T
     // global order of the listed keys: slice offsets, then the keys themselves into LDS
     const uint32_t *cnts = P.counts + (int64_t)qi * P.slices;
@@ -272,7 +277,7 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         while (tps > kSelTPS && tps * S > kSelThreads) tps >>= 1;
         const int sl = t / tps, p0 = t % tps;
         const bool live = sl < S;
-        const uint32_t c = live ? cnts[sl] : 0u;
+        const uint32_t c = live ? sel_clamp_count(cnts[sl], (uint32_t)kSelSlice) : 0u;
         const uint32_t *ls = lst + (int64_t)(live ? sl : 0) * kSelSlice * 2;
         uint2 e[kSelSpec];
 #pragma unroll
@@ -321,7 +326,7 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         uint32_t run = 0;
         for (int r0 = 0; r0 < S; r0 += kSelThreads) {
             const int sidx = r0 + t;
-            const uint32_t c = sidx < S ? cnts[sidx] : 0u;
+            const uint32_t c = sidx < S ? sel_clamp_count(cnts[sidx], (uint32_t)kSelSlice) : 0u;
             uint32_t tot;
             const uint32_t incl = block_scan(c, wsum, &tot);
             if (sidx < S) soff[sidx + 1] = run + incl;
@@ -388,6 +393,10 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         int d;
         uint32_t ab;
         find_threshold<kSubBins / kSelThreads>(c, rem, wsum, &sT, &sAbove, &d, &ab);
+        if (d < 0) {  // fewer listed keys in bin T than the scan promised: select nothing (uniform)
+            for (int j = t; j < P.k; j += kSelThreads) out[j] = -1;
+            return;
+        }
         rem -= ab;
         sub |= (uint32_t)d << shift;
         sub_mask |= dmask << shift;
@@ -419,15 +428,8 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     for (uint32_t j = j0; j < j1; j++) {
         uint32_t idx, key;
         entry(j, &idx, &key);
-        if (key > tkey) {
-            const uint32_t p = gt_before + min(eq_before, rem);
-            if (p < k_eff) out[p] = (int32_t)idx;
-            gt_before++;
-        } else if (key == tkey) {
-            const uint32_t p = gt_before + eq_before;
-            if (eq_before < rem && p < k_eff) out[p] = (int32_t)idx;
-            eq_before++;
-        }
+        const int p = sel_place(key, tkey, rem, k_eff, &gt_before, &eq_before);
+        if (p >= 0) out[p] = (int32_t)idx;
     }
     for (int j = (int)k_eff + t; j < P.k; j += kSelThreads) out[j] = -1;
 }

@@ -23,9 +23,13 @@
  *   - Every call validates its arguments on the host before launching anything.  On a
  *     status other than V4A_OK nothing was launched and no output was written;
  *     v4a_last_error() returns a message for the calling thread.  No C++ exception
- *     crosses this boundary.  The library keeps no state between calls and may be used
- *     from several threads and streams at once (calls sharing a workspace must not
- *     overlap).
+ *     crosses this boundary.
+ *   - State between calls: the library keeps none of its own except (a) the kernel-timing
+ *     trace (v4a_trace_*: process-global events and records, off unless armed) and (b) the
+ *     per-device scratch array of v4a_decode_step_csa_noalloc (see there).  A workspace's
+ *     contents can carry over between calls where a call says so: v4a_decode_step_csa leaves
+ *     its selection histograms clear and, with ws_clean, relies on that.  Calls may run from
+ *     several threads and streams at once; calls sharing a workspace must not overlap.
  *   - Results are deterministic and batch invariant: the work split of a sequence depends
  *     only on its own lengths and the shape constants, never on the batch size or on
  *     device occupancy, and no floating-point reduction uses atomics.

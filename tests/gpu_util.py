@@ -50,19 +50,33 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_close(got: np.ndarray, ref: np.ndarray, max_abs: float, rel_l2: float | None = None, what="",
-                ulps: float = 0.0):
-    """max |got - ref| <= max_abs (+ `ulps` BF16 spacings of |ref| where a case states it) and
-    ||got - ref|| / ||ref|| <= rel_l2 over the whole tensor."""
+                ulp_seqs=()):
+    """max |got - ref| <= max_abs and ||got - ref|| / ||ref|| <= rel_l2 over the whole tensor.
+
+    ulp_seqs: indices along the first axis (sequences) whose max-abs bar also allows one BF16
+    spacing of |ref|, or "all" for a tensor that is one such sequence.  Only sequences attending
+    over at most FEW_KEYS keys qualify (few_key_seqs): their outputs are near copies of a few
+    N(0,1) key values and reach |o| >= 2, where one BF16 spacing (1/64) exceeds the 1e-2 bar by
+    itself, so rounding the same value on the other side of a BF16 midpoint fails it.  Every
+    other sequence keeps the plain bar."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref)
-    bar = max_abs + ulps * bf16_ulp(ref)
+    bar = np.full(err.shape, max_abs)
+    if isinstance(ulp_seqs, str):
+        assert ulp_seqs == "all"
+        bar = max_abs + bf16_ulp(ref)
+        ulp_seqs = ["all"]
+    else:
+        for s in ulp_seqs:
+            bar[s] = max_abs + bf16_ulp(ref[s])
+    ulps = len(ulp_seqs)
     ma = float(err.max()) if err.size else 0.0
     rl = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if err.size else 0.0
     worst = np.unravel_index(int(np.argmax(err - bar)), err.shape) if err.size else ()
-    msg = f"{what}: max-abs {ma:.3e} (bar {max_abs:.1e}" + (f" + {ulps} bf16 ulp" if ulps else "") + \
+    msg = f"{what}: max-abs {ma:.3e} (bar {max_abs:.1e}" + (f"; + 1 bf16 ulp on sequences {list(ulp_seqs)}" if ulps else "") + \
           f"), rel-L2 {rl:.3e}" + (f" (bar {rel_l2:.1e})" if rel_l2 is not None else "")
     if err.size:
         msg += f"; worst at {tuple(int(i) for i in worst)}: got {got[worst]:.6g} ref {ref[worst]:.6g}"
@@ -74,6 +88,16 @@ def check_close(got: np.ndarray, ref: np.ndarray, max_abs: float, rel_l2: float 
     if rel_l2 is not None:
         assert rl <= rel_l2, msg
     return ma, rl
+
+
+# Sequences attending over at most this many keys (entries plus window tokens) may differ from the
+# oracle's BF16 value by one BF16 spacing (see check_close).
+FEW_KEYS = 8
+
+
+def few_key_seqs(n_keys):
+    """Indices of the sequences with at most FEW_KEYS keys."""
+    return [b for b, n in enumerate(n_keys) if n <= FEW_KEYS]
 
 
 def rel_close(got, ref, tol=1e-5):

@@ -367,7 +367,9 @@ def test_hca_prefill_equals_split_free_decode():
     tok0, n_prev, D, H, W = x["tok0"], x["n_prev"], w.D, w.H, w.W
     rows = torch.zeros((1, 128, D), dtype=torch.bfloat16, device="cuda")  # read only when a block completes
     gates = torch.zeros((1, 128, 1), dtype=torch.float32, device="cuda")
-    for j in decode_positions(tok0, x["C"], 128):
+    js = decode_positions(tok0, x["C"], 128)
+    got = {}
+    for j in js:
         t = tok0 + j
         announce(f"hca prefill == split-free decode at t={t}")
         win = r["kv_dev"][n_prev + j - W + 1:n_prev + j + 1][None].contiguous()
@@ -380,6 +382,15 @@ def test_hca_prefill_equals_split_free_decode():
         v4.v4a_decode_step_hca(args, None)
         torch.cuda.synchronize()
         assert torch.equal(out[0], r["out"][j]), f"hca t={t}"
+        got[j] = out_f64(out[0])
+    # the split-free decode outputs against the oracle directly
+    announce("hca split-free decode vs oracle")
+    q64 = bf16_bits_to_f64(to_bf16_bits(x["q"]))
+    ref, _ = oracle.prefill_queries("hca", q64, dequant_slot(kv, r["n_total"]), r["n_total"], r["kv_val"],
+                                    n_prev=n_prev, tok0=tok0, queries=js, W=W, sink=x["sink"], scale=w.scale, m=128,
+                                    R=w.R)
+    check_close(np.stack([got[j] for j in js]), bf16_round(np.stack([ref[j] for j in js])), MAX_ABS_BF16, REL_L2_BF16,
+                what="hca split-free decode vs oracle")
 
 
 def test_csa_prefill_equals_split_free_decode():
@@ -390,7 +401,9 @@ def test_csa_prefill_equals_split_free_decode():
     kv1, keys1 = kv_slot(r["kv"], r["slot"]), idx_slot(r["keys"], r["slot"])
     z = lambda *shape, dt=torch.bfloat16: torch.zeros(shape, dtype=dt, device="cuda")  # rows read only on completion
     zf = lambda *shape: z(*shape, dt=torch.float32)
-    for j in decode_positions(tok0, C, 4):
+    js = decode_positions(tok0, C, 4)
+    got, got_sel = {}, {}
+    for j in js:
         t = tok0 + j
         announce(f"csa prefill == split-free decode at t={t}")
         qi = v4.Idx(r["qi"].fmt, dI, r["qi"].codes[:, j * HI:(j + 1) * HI], r["qi"].scales[:, j * HI:(j + 1) * HI], HI)
@@ -407,6 +420,23 @@ def test_csa_prefill_equals_split_free_decode():
         v4.v4a_decode_step_csa(args, ws)
         torch.cuda.synchronize()
         assert torch.equal(out[0], r["out"][j]), f"csa t={t}"
+        got[j] = out_f64(out[0])
+        got_sel[j] = ws[:4 * k].view(torch.int32).cpu().numpy()  # the step's selection heads its workspace
+    # the split-free decode outputs and selections against the oracle directly
+    announce("csa split-free decode vs oracle")
+    n_total = r["n_total"]
+    qc = r["qi"].codes[0].cpu().numpy().reshape(C, HI, dI // 2)
+    qs = r["qi"].scales[0].cpu().numpy().reshape(C, HI, dI // 32)
+    idx = dict(q_codes=qc, q_scales=qs, w=x["w"], k_codes=keys1.codes[0, :n_total].cpu().numpy(),
+               k_scales=keys1.scales[0, :n_total].cpu().numpy())
+    q64 = bf16_bits_to_f64(to_bf16_bits(x["q"]))
+    ref, ref_sel = oracle.prefill_queries("csa", q64, dequant_slot(kv1, n_total), n_total, r["val"]["kv_a"],
+                                          n_prev=n_prev, tok0=tok0, queries=js, W=W, sink=x["sink"], scale=w.scale,
+                                          m=4, k=k, idx=idx, R=w.R)
+    for j in js:
+        assert np.array_equal(got_sel[j], ref_sel[j]), j
+    check_close(np.stack([got[j] for j in js]), bf16_round(np.stack([ref[j] for j in js])), MAX_ABS_BF16, REL_L2_BF16,
+                what="csa split-free decode vs oracle")
 
 
 

@@ -170,6 +170,28 @@ def test_quant_kv_record(orc):
     assert np.array_equal(rope, ref_rope)
 
 
+def test_dequant_kv_layout(orc):
+    """dequant_kv puts dims 0..D-R-1 back as FP8 code x scale and dims D-R..D-1 as the BF16
+    values of x, each in its own position (the record layout: non-RoPE dims first, RoPE dims
+    last).  Both halves are checked against torch's own conversions, so a swapped or shifted
+    half fails."""
+    g = np.random.default_rng(5)
+    for D, R in ((128, 32), (512, 64)):
+        x = g.standard_normal((40, D)).astype(np.float32)
+        x[7, :D - R] = 0.0
+        nope, rope, scale = orc.quant_kv(x, R)
+        back = orc.dequant_kv(nope, rope, scale)
+        assert back.shape == (40, D)
+        bf = torch.from_numpy(np.ascontiguousarray(x[:, D - R:])).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(back[:, D - R:], bf)
+        fp8 = torch.from_numpy(np.ascontiguousarray(nope)).view(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(back[:, :D - R], fp8 * scale.astype(np.float64)[:, None])
+        # the non-RoPE half approximates x (FP8 keeps 3 mantissa bits), the RoPE half is not x's
+        # non-RoPE part: a swap would break one of these
+        assert np.abs(back[:, :D - R] - x[:, :D - R]).max() <= np.abs(x[:, :D - R]).max() * 2.0 ** -3
+        assert not back[7, :D - R].any() and scale[7] == 1.0
+
+
 def test_fp4_to_fp8_lossless(orc):
     """Every E2M1 value times 2^k that lies in E4M3's normal range survives an E4M3 round
     trip: E4M3 has two more exponent bits and two more mantissa bits than E2M1, so only the
