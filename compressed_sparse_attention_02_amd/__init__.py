@@ -125,6 +125,8 @@ def lib() -> ctypes.CDLL:
         L.v4a_decode_step_csa.restype = ctypes.c_int
         L.v4a_decode_step_workspace.argtypes = [DSP]
         L.v4a_decode_step_workspace.restype = SZ
+        L.v4a_decode_step_csa_noalloc.argtypes = [DSP, P]
+        L.v4a_decode_step_csa_noalloc.restype = ctypes.c_int
         DHP = ctypes.POINTER(c_decode_step_hca_args)
         L.v4a_decode_step_hca.argtypes = [DHP, P, SZ, P]
         L.v4a_decode_step_hca.restype = ctypes.c_int
@@ -429,6 +431,14 @@ def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:
 def v4a_decode_step_csa(args: DecodeStepArgs, ws: torch.Tensor, stream=None):
     _check(lib().v4a_decode_step_csa(ctypes.byref(args.s), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+V4A_NOALLOC_SCRATCH_BYTES = 64 << 20  # the library's per-device scratch (include/v4attn.h)
+
+
+def v4a_decode_step_csa_noalloc(args: DecodeStepArgs, stream=None):
+    """The fused CSA decode step on the library's own per-device scratch (no workspace)."""
+    _check(lib().v4a_decode_step_csa_noalloc(ctypes.byref(args.s), _stream(stream)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

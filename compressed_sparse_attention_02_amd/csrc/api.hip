@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -972,15 +973,13 @@ size_t v4a_decode_step_workspace(const v4a_decode_step_args *args) {
     return pl.total;
 }
 
-v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t ws_bytes, void *stream) {
-    StepPlan pl;
-    v4a_status st = step_plan(a, pl);
-    if (st != V4A_OK) return st;
-    if (!ws || ws_bytes < pl.total || !aligned(ws, 256))
-        return fail(V4A_EWORKSPACE, "v4a_decode_step_csa: workspace needs %zu bytes, 256-byte aligned (got %zu)",
-                    pl.total, ws_bytes);
-    g_err.clear();
-    hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+namespace v4a {
+
+// The launches of one fused CSA decode step on a checked plan and a workspace of pl.total bytes.
+static v4a_status decode_step_run(const v4a_decode_step_args *a, StepPlan &pl, void *ws, hipStream_t s) {
+    v4a_status st;
     char *base = (char *)ws;
     int32_t *sel = (int32_t *)base;
     char *tws = base + pl.sel_bytes;
@@ -1005,6 +1004,78 @@ v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t w
     pl.at.topk = sel;
     pl.at.partial = pl.attn_bytes > 0 ? (float *)(tws + pl.topk_bytes) : nullptr;
     return hip_status(launch_attention(pl.at, pl.sq, s), "v4a_decode_step_csa: attention");
+}
+
+// Scratch of the entry point that allocates nothing: one array per device (each device that
+// loads the library holds its own copy until the process ends).  Host code must not pass the
+// array's name to a kernel (in host code it is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = V4A_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array; checks that `stream` belongs to that
+// device.
+static v4a_status scratch_address(hipStream_t s, void **out, const char *name) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, name);
+    if (dev < 0 || dev >= kMaxDevices) return fail(V4A_EUNSUPPORTED, "%s: device %d", name, dev);
+    if (s) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(s, &sdev);
+        if (e != hipSuccess) return hip_status(e, name);
+        if ((int)sdev != dev)
+            return fail(V4A_EINVAL, "%s: the stream belongs to device %d, the current device is %d", name, (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, name);
+        if (!p || !aligned(p, 256)) return fail(V4A_EHIP, "%s: scratch address not 256-byte aligned", name);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return V4A_OK;
+}
+
+}  // namespace v4a
+
+extern "C" {
+
+v4a_status v4a_decode_step_csa(const v4a_decode_step_args *a, void *ws, size_t ws_bytes, void *stream) {
+    StepPlan pl;
+    v4a_status st = step_plan(a, pl);
+    if (st != V4A_OK) return st;
+    if (!ws || ws_bytes < pl.total || !aligned(ws, 256))
+        return fail(V4A_EWORKSPACE, "v4a_decode_step_csa: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    pl.total, ws_bytes);
+    g_err.clear();
+    return decode_step_run(a, pl, ws, (hipStream_t)stream);
+}
+
+v4a_status v4a_decode_step_csa_noalloc(const v4a_decode_step_args *args, void *stream) {
+    const char *name = "v4a_decode_step_csa_noalloc";
+    if (!args) return fail(V4A_EINVAL, "%s: args is NULL", name);
+    // the scratch keeps whatever the last call on this device left: the histograms are always
+    // cleared by this call (a fill kernel, no runtime memset)
+    v4a_decode_step_args a = *args;
+    a.ws_clean = 0;
+    StepPlan pl;
+    v4a_status st = step_plan(&a, pl);
+    if (st != V4A_OK) return st;
+    if (pl.total > kNoAllocScratchBytes)
+        return fail(V4A_EWORKSPACE, "%s: these arguments need %zu bytes of scratch, more than the %zu the library holds",
+                    name, pl.total, (size_t)kNoAllocScratchBytes);
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if ((st = scratch_address(s, &ws, name)) != V4A_OK) return st;
+    g_err.clear();
+    return decode_step_run(&a, pl, ws, s);
 }
 
 }  // extern "C"

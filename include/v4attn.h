@@ -398,6 +398,21 @@ V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *w
 /* Workspace of v4a_decode_step_csa for these arguments (0 if they are invalid). */
 V4A_API size_t v4a_decode_step_workspace(const v4a_decode_step_args *args);
 
+/* The same step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): no workspace argument, and the call
+ * allocates nothing.  Its scratch is one array of V4A_NOALLOC_SCRATCH_BYTES (64 MiB) per device,
+ * a static device variable of the library that each device loading it holds until the process
+ * ends; its address is looked up once per device (the stream must belong to the current
+ * device).  Arguments needing more scratch than that (v4a_decode_step_workspace(args) >
+ * V4A_NOALLOC_SCRATCH_BYTES) are rejected with V4A_EWORKSPACE before any launch; the 1M-context
+ * step of 4 sequences with k = 1024 needs about 38 MB.  Every call on a device shares that
+ * device's array and finds the previous call's contents: the call clears what must start at
+ * zero (the selection histograms) with a fill kernel, and ignores ws_clean.  Calls that overlap
+ * on one device (several streams or threads) race on the array and must be serialised by the
+ * caller.  Results are bitwise those of v4a_decode_step_csa with the same arguments. */
+#define V4A_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+V4A_API v4a_status v4a_decode_step_csa_noalloc(const v4a_decode_step_args *args, void *stream);
+
 /* ------------------------------------------------- fused HCA decode step (one token) ----
  * One decode step of B sequences of an HCA layer in one call, equal to v4a_compress_hca +
  * v4a_decode_hca with the same arguments.  For every sequence b whose newest token t = q_pos[b]

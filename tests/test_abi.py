@@ -250,6 +250,26 @@ def test_decode_step_workspace_and_rejects():
     assert call(n_entries=ctypes.cast(short, ctypes.c_void_p), q_pos=ctypes.cast(pos, ctypes.c_void_p)) == 1
 
 
+def test_decode_step_noalloc_rejects_before_any_hip_call():
+    """The entry point without a workspace validates like v4a_decode_step_csa and refuses
+    arguments whose scratch exceeds the library's per-device array, before touching the device."""
+    L = v4.lib()
+    assert L.v4a_decode_step_csa_noalloc(None, None) == 1
+    assert L.v4a_decode_step_csa_noalloc(ctypes.byref(step_struct(k=0)), None) == 2
+    assert L.v4a_decode_step_csa_noalloc(ctypes.byref(step_struct(kv_b=0)), None) == 1
+    # 128 sequences at the 1M-context shape need far more than 64 MiB of scratch
+    B = 128
+    pos, nent, wl = i64(*[1048575] * B), i64(*[262144] * B), i32(*[128] * B)
+    big = step_struct(B=B, q_pos=ctypes.cast(pos, ctypes.c_void_p), n_entries=ctypes.cast(nent, ctypes.c_void_p),
+                      win_len=ctypes.cast(wl, ctypes.c_void_p), q_idx=ctypes.pointer(idx(cap=64)))
+    big._keep2 = (pos, nent, wl)
+    assert L.v4a_decode_step_workspace(ctypes.byref(big)) > v4.V4A_NOALLOC_SCRATCH_BYTES
+    assert L.v4a_decode_step_csa_noalloc(ctypes.byref(big), None) == 3
+    assert b"scratch" in L.v4a_last_error()
+    # the 1M-context step of 4 sequences fits
+    assert L.v4a_decode_step_workspace(ctypes.byref(step_struct())) <= v4.V4A_NOALLOC_SCRATCH_BYTES
+
+
 def test_trace_without_marks_is_an_error():
     # no trace has recorded anything in this process: asking for a mark fails before any HIP call
     assert v4.v4a_trace_end() == 0
