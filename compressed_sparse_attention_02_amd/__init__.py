@@ -73,7 +73,7 @@ class c_decode_step_args(ctypes.Structure):
                 ("sink", P), ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32),
                 ("out", P), ("out_t", ctypes.c_int), ("score_bf16", ctypes.c_int32), ("norm_w", P),
                 ("idx_norm_w", P), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P),
-                ("ws_clean", ctypes.c_int32)]
+                ("ws_clean", ctypes.c_int32), ("Q", ctypes.c_int32)]
 
 
 
@@ -85,7 +85,8 @@ class c_decode_step_hca_args(ctypes.Structure):
                 ("kv", ctypes.POINTER(c_kv)), ("q", P), ("q_t", ctypes.c_int), ("H", ctypes.c_int32),
                 ("win", P), ("win_t", ctypes.c_int), ("win_len", P), ("W", ctypes.c_int32), ("sink", P),
                 ("softmax_scale", ctypes.c_float), ("out_rope_inverse", ctypes.c_int32), ("out", P),
-                ("out_t", ctypes.c_int), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P)]
+                ("out_t", ctypes.c_int), ("ring", ctypes.c_int32), ("no_split", ctypes.c_int32), ("q_norm_w", P),
+                ("Q", ctypes.c_int32)]
 
 
 _lib = None
@@ -397,15 +398,17 @@ def v4a_prefill_chunk(kind: int, args: PrefillArgs, ws: torch.Tensor | None = No
 
 class DecodeStepArgs:
     """The arguments of one fused CSA decode step (v4a_decode_step_args), holding every tensor
-    and host array it points to.  Streams hold [B][2m] rows per sequence."""
+    and host array it points to.  Streams hold [B][2m] rows per sequence (a ring [B][2m+Q-1]).
+    With Q new tokens per sequence q and out are [B][Q][H][D] and w is [B][Q][H_I]."""
 
     def __init__(self, *, q_pos, n_entries, m: int, kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b,
                  idx_gate_a, idx_gate_b, idx_bias_a, idx_bias_b, kv: KV, keys: Idx, q_idx: Idx, w, k: int, q,
                  win, win_len, W: int, sink, softmax_scale: float, out, apply_rope: bool = True,
                  rope_theta: float = 10000.0, out_rope_inverse: bool = True, score_bf16: bool = False,
                  norm_w=None, idx_norm_w=None, ring: bool = False, no_split: bool = False, q_norm_w=None,
-                 ws_clean: bool = False):
-        B, H = q.shape[0], q.shape[1]
+                 ws_clean: bool = False, Q: int = 1):
+        B, H = q.shape[0], q.shape[-2]
+        assert q.dim() == (4 if Q > 1 else 3), "q is [B][H][D], or [B][Q][H][D] with Q > 1"
         self._kv, self._keys, self._q_idx = kv.c(), keys.c(), q_idx.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
         self._refs = (kv_a, kv_b, gate_a, gate_b, bias_a, bias_b, idx_a, idx_b, idx_gate_a, idx_gate_b, idx_bias_a,
@@ -417,11 +420,11 @@ class DecodeStepArgs:
             idx_b=_ptr(idx_b), idx_gate_a=_ptr(idx_gate_a), idx_gate_b=_ptr(idx_gate_b),
             idx_bias_a=_ptr(idx_bias_a), idx_bias_b=_ptr(idx_bias_b), apply_rope=int(apply_rope),
             rope_theta=rope_theta, kv=ctypes.pointer(self._kv), keys=ctypes.pointer(self._keys),
-            q_idx=ctypes.pointer(self._q_idx), w=_ptr(w), H_I=w.numel() // B, k=k, q=_ptr(q), q_t=_ftype(q), H=H,
+            q_idx=ctypes.pointer(self._q_idx), w=_ptr(w), H_I=w.numel() // (B * Q), k=k, q=_ptr(q), q_t=_ftype(q), H=H,
             win=_ptr(win), win_t=_ftype(win), win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink),
             softmax_scale=softmax_scale, out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out),
             score_bf16=int(score_bf16), norm_w=_ptr(norm_w), idx_norm_w=_ptr(idx_norm_w), ring=int(ring),
-            no_split=int(no_split), q_norm_w=_ptr(q_norm_w), ws_clean=int(ws_clean))
+            no_split=int(no_split), q_norm_w=_ptr(q_norm_w), ws_clean=int(ws_clean), Q=Q)
 
 
 def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:
@@ -448,13 +451,15 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 class DecodeStepHcaArgs:
     """The arguments of one fused HCA decode step (v4a_decode_step_hca_args), holding every tensor
-    and host array it points to.  The stream holds [B][m] rows per sequence."""
+    and host array it points to.  The stream holds [B][m] rows per sequence (a ring [B][m+Q-1]).
+    With Q new tokens per sequence q and out are [B][Q][H][D]."""
 
     def __init__(self, *, q_pos, n_entries, m: int, kv_a, gate_a, bias_a, kv: KV, q, win, win_len, W: int, sink,
                  softmax_scale: float, out, apply_rope: bool = True, rope_theta: float = 10000.0,
                  out_rope_inverse: bool = True, norm_w=None, ring: bool = False, no_split: bool = False,
-                 q_norm_w=None):
-        B, H = q.shape[0], q.shape[1]
+                 q_norm_w=None, Q: int = 1):
+        B, H = q.shape[0], q.shape[-2]
+        assert q.dim() == (4 if Q > 1 else 3), "q is [B][H][D], or [B][Q][H][D] with Q > 1"
         self._kv = kv.c()
         self._pos, self._nent, self._wl = _host_i64(q_pos), _host_i64(n_entries), _host_i32(win_len)
         self._refs = (kv_a, gate_a, bias_a, kv, q, win, sink, out, norm_w, q_norm_w)
@@ -465,7 +470,7 @@ class DecodeStepHcaArgs:
             q=_ptr(q), q_t=_ftype(q), H=H, win=_ptr(win), win_t=_ftype(win),
             win_len=ctypes.cast(self._wl, ctypes.c_void_p), W=W, sink=_ptr(sink), softmax_scale=softmax_scale,
             out_rope_inverse=int(out_rope_inverse), out=_ptr(out), out_t=_ftype(out), ring=int(ring),
-            no_split=int(no_split), q_norm_w=_ptr(q_norm_w))
+            no_split=int(no_split), q_norm_w=_ptr(q_norm_w), Q=Q)
 
 
 def v4a_decode_step_hca_workspace(args: DecodeStepHcaArgs) -> int:

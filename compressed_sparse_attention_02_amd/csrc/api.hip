@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of the hot path (declared in include/v4attn.h): host-side argument
 // validation (always before any launch), workspace layout, and kernel dispatch.  No device
 // memory is allocated here; scratch lives in the caller's workspace.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -874,8 +875,39 @@ struct StepPlan {
     AttnArgs at;
     SeqInfo sq;
     v4a_kv kv;
+    int Q;
     size_t sel_bytes, topk_bytes, attn_bytes, total;
 };
+
+// The queries of a decode step with Q new tokens per sequence (the newest at q_pos[b]): query
+// b*Q + j is the token at t_j = q_pos[b] - Q + 1 + j.  Fills their positions (qpos), window
+// lengths (wl: win_len[b], and for Q > 1 at most t_j + 1), the window rows of the plain layout
+// (the buffer's W + Q - 1 rows per sequence hold the tokens ending at q_pos[b], oldest first)
+// and the entry each sequence's tokens complete (at most one, since Q <= m).
+static v4a_status step_queries(int B, int Q, int m, int W, const int64_t *q_pos, const int32_t *win_len, bool ring,
+                               int64_t *qpos, int32_t *wl, int64_t *entry, SeqInfo &sq, const char *name) {
+    if (W > 0 && !win_len) return fail(V4A_EINVAL, "%s: win_len is required", name);
+    for (int b = 0; b < B; b++) {
+        const int64_t t = q_pos[b];
+        if (t < Q - 1) return fail(V4A_EINVAL, "%s: q_pos[%d]=%lld is before the step's first token", name, b, (long long)t);
+        const int wlb = W > 0 ? win_len[b] : 0;
+        if (wlb < 0 || wlb > W) return fail(V4A_EINVAL, "%s: win_len[%d]=%d not in [0, W]", name, b, wlb);
+        const int64_t p_lo = std::max<int64_t>(0, t - wlb - Q + 2);  // the plain buffer's row 0
+        entry[b] = -1;
+        for (int j = 0; j < Q; j++) {
+            const int64_t tj = t - Q + 1 + j;
+            const int qi = b * Q + j;
+            const int w = Q > 1 ? (int)std::min<int64_t>(wlb, tj + 1) : wlb;
+            qpos[qi] = tj;
+            wl[qi] = w;
+            sq.win_off[qi] = (Q > 1 && !ring) ? (int32_t)(tj - w + 1 - p_lo) : 0;
+            if ((tj + 1) % m == 0) entry[b] = (tj + 1) / m - 1;
+        }
+    }
+    sq.qps = Q;
+    sq.win_stride = Q > 1 ? W + Q - 1 : 0;
+    return V4A_OK;
+}
 
 static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     if (!a) return fail(V4A_EINVAL, "v4a_decode_step_csa: args is NULL");
@@ -889,13 +921,17 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     const int D = a->kv->D, d = a->keys->d, m = a->m;
     if (!((D == 512 && d == 128) || (D == 128 && d == 32)))
         return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs D=512 with d=128 or D=128 with d=32");
+    const int Q = a->Q > 0 ? a->Q : 1;
+    if (Q > 4 || Q > m || a->B * Q > kMaxSeq)
+        return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: Q=%d needs Q <= 4, Q <= m and B*Q <= %d", Q, kMaxSeq);
+    pl.Q = Q;
     // compressor arguments, checked as one entry at rows [0, 2m) (the per-sequence entries and
     // row origins are set at launch)
     auto fill = [&](CompressArgs &c, const void *xa, const void *xb, const float *ga, const float *gb,
                      const float *ba, const float *bb, int Dd, int G) {
         c.x[0] = xa; c.x[1] = xb; c.gate[0] = ga; c.gate[1] = gb; c.bias[0] = ba; c.bias[1] = bb;
         c.n_streams = 2; c.bf16_in = a->in_t == V4A_BF16; c.D = Dd; c.G = G; c.m = m;
-        c.tok0 = 0; c.n_tok = 2 * m; c.first_entry = 1; c.n_entries = 1;
+        c.tok0 = 0; c.n_tok = 2 * m + (a->ring ? Q - 1 : 0); c.first_entry = 1; c.n_entries = 1;
         c.theta = a->rope_theta; c.b0 = 0; c.n_seq = a->B;
     };
     fill(pl.rec, a->kv_a, a->kv_b, a->gate_a, a->gate_b, a->bias_a, a->bias_b, D, a->G);
@@ -909,26 +945,30 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     pl.key.ring = a->ring != 0;
     pl.key.idx = a->keys;
     if ((st = compress_check(pl.key, a->idx_norm_w)) != V4A_OK) return st;
+    memset(&pl.sq, 0, sizeof pl.sq);
+    int64_t qpos[kMaxSeq];
+    int32_t wl[kMaxSeq];
+    if ((st = step_queries(a->B, Q, m, a->W, a->q_pos, a->win_len, a->ring != 0, qpos, wl, pl.entry, pl.sq,
+                           "v4a_decode_step_csa")) != V4A_OK)
+        return st;
     for (int b = 0; b < a->B; b++) {
-        const int64_t t = a->q_pos[b];
-        if (t < 0) return fail(V4A_EINVAL, "v4a_decode_step_csa: q_pos[%d] < 0", b);
-        const int64_t i = (t + 1) % m == 0 ? (t + 1) / m - 1 : -1;
+        const int64_t i = pl.entry[b];
         if (i >= a->n_entries[b])
             return fail(V4A_EINVAL, "v4a_decode_step_csa: n_entries[%d] does not include the entry this step completes", b);
         if (i >= a->kv->cap || i >= a->keys->cap)
             return fail(V4A_EINVAL, "v4a_decode_step_csa: entry %lld of sequence %d exceeds the cache", (long long)i, b);
-        pl.entry[b] = i;
     }
     // selection
-    if ((st = check_indexer_args(a->keys, a->n_entries, m, a->q_idx, a->w, a->B, 1, a->H_I, a->q_pos)) != V4A_OK)
+    if ((st = check_indexer_args(a->keys, a->n_entries, m, a->q_idx, a->w, a->B, Q, a->H_I, qpos)) != V4A_OK)
         return st;
     if (a->k < 1 || a->k > 2048) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: k=%d not in [1, 2048]", a->k);
-    if ((st = fill_query_pos(pl.qp, a->B, 1, m, a->n_entries, a->q_pos, a->keys->cap, &pl.n_max)) != V4A_OK) return st;
+    if ((st = fill_query_pos(pl.qp, a->B, Q, m, a->n_entries, qpos, a->keys->cap, &pl.n_max)) != V4A_OK) return st;
     if (pl.n_max > (int64_t)1024 * kSelSlice) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: too many entries");
     // attention
     AttnArgs &at = pl.at;
+    const int BQ = a->B * Q;
     at.q = a->q;
-    at.B = a->B;
+    at.B = BQ;
     at.H = a->H;
     at.kv = a->kv;
     at.kv_bstride = a->kv->cap;
@@ -940,24 +980,23 @@ static v4a_status step_plan(const v4a_decode_step_args *a, StepPlan &pl) {
     at.rope_inv = a->out_rope_inverse != 0;
     at.theta = a->rope_theta;
     at.out = a->out;
-    memset(&pl.sq, 0, sizeof pl.sq);
-    for (int b = 0; b < a->B; b++) pl.sq.n_ent[b] = a->k;
+    for (int qi = 0; qi < BQ; qi++) pl.sq.n_ent[qi] = a->k;
     size_t attn_need = 0;
-    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &attn_need,
+    if ((st = decode_prepare(at, pl.sq, wl, qpos, a->q_t, a->win_t, a->out_t, &attn_need,
                              "v4a_decode_step_csa", a->no_split != 0)) != V4A_OK)
         return st;
     if (a->ring) {
-        for (int b = 0; b < a->B; b++)
-            if (pl.sq.win_len[b] > a->q_pos[b] + 1)
-                return fail(V4A_EINVAL, "v4a_decode_step_csa: win_len[%d] exceeds the tokens so far", b);
+        for (int qi = 0; qi < BQ; qi++)
+            if (pl.sq.win_len[qi] > pl.sq.q_pos[qi] + 1)
+                return fail(V4A_EINVAL, "v4a_decode_step_csa: win_len[%d] exceeds the tokens so far", qi / Q);
         pl.sq.ring = 1;
     }
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "v4a_decode_step_csa: needs the MFMA attention shapes");
     if (a->q_norm_w && !aligned(a->q_norm_w, 16))
         return fail(V4A_EINVAL, "v4a_decode_step_csa: q_norm_w must be 16-byte aligned");
     pl.at.q_norm_w = a->q_norm_w;
-    pl.sel_bytes = round_up((size_t)a->B * a->k * 4, 256);
-    pl.topk_bytes = topk_layout(a->B, 1, pl.n_max, a->k).total;
+    pl.sel_bytes = round_up((size_t)BQ * a->k * 4, 256);
+    pl.topk_bytes = topk_layout(a->B, Q, pl.n_max, a->k).total;
     pl.attn_bytes = round_up(attn_need, 256);
     pl.total = pl.sel_bytes + pl.topk_bytes + pl.attn_bytes;
     return V4A_OK;
@@ -983,11 +1022,13 @@ static v4a_status decode_step_run(const v4a_decode_step_args *a, StepPlan &pl, v
     char *base = (char *)ws;
     int32_t *sel = (int32_t *)base;
     char *tws = base + pl.sel_bytes;
-    const TopkWs L = topk_layout(a->B, 1, pl.n_max, a->k);
-    const size_t hist_bytes = (size_t)a->B * hist_copies(a->B) * kHistBins * 4;
+    const int Q = pl.Q, BQ = a->B * pl.Q;
+    const TopkWs L = topk_layout(a->B, Q, pl.n_max, a->k);
+    const size_t hist_bytes = (size_t)BQ * hist_copies(BQ) * kHistBins * 4;
     // MXFP4 keys of d = 128 from short gate-per-token blocks are compressed inside the scoring
-    // kernel (its latency hidden behind the scan); otherwise the prologue compresses them
-    const bool key_in_scoring = a->keys->fmt == V4A_IDX_MXFP4 && a->keys->d == 128 &&
+    // kernel (its latency hidden behind the scan; one query per sequence); otherwise the
+    // prologue compresses them
+    const bool key_in_scoring = Q == 1 && a->keys->fmt == V4A_IDX_MXFP4 && a->keys->d == 128 &&
                                 entry_two_phase(compress_params(pl.key));
     // the histograms: cleared here unless the caller vouches that the previous call left them
     // clear (the final selection's launch clears them for the next call)
@@ -998,7 +1039,7 @@ static v4a_status decode_step_run(const v4a_decode_step_args *a, StepPlan &pl, v
     else if (clear_bytes)
         e = launch_zero(tws + L.hist, clear_bytes, s);
     if (e != hipSuccess) return hip_status(e, "v4a_decode_step_csa: compress");
-    st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, 1, a->H_I, a->k, sel, tws, s, false,
+    st = indexer_topk_launch(a->keys, pl.qp, pl.n_max, a->q_idx, a->w, a->B, Q, a->H_I, a->k, sel, tws, s, false,
                              a->score_bf16 != 0, &pl.rec, key_in_scoring ? &pl.key : nullptr, true);
     if (st != V4A_OK) return st;
     pl.at.topk = sel;
@@ -1142,33 +1183,40 @@ static v4a_status step_hca_plan(const v4a_decode_step_hca_args *a, StepHcaPlan &
     if ((st = check_kv(a->kv, "kv")) != V4A_OK) return st;
     if (a->in_t != V4A_F32 && a->in_t != V4A_BF16) return fail(V4A_EINVAL, "%s: in_t", name);
     const int D = a->kv->D, m = a->m;
+    const int Q = a->Q > 0 ? a->Q : 1;
+    if (m < 1 || Q > 4 || Q > m || a->B * Q > kMaxSeq)
+        return fail(V4A_EUNSUPPORTED, "%s: Q=%d needs Q <= 4, Q <= m and B*Q <= %d", name, Q, kMaxSeq);
     // compressor arguments, checked as one entry at rows [0, m) (entries and row origins are set
     // per sequence at launch)
     CompressArgs &c = pl.rec;
     c.x[0] = a->kv_a; c.gate[0] = a->gate_a; c.bias[0] = a->bias_a;
     c.n_streams = 1; c.bf16_in = a->in_t == V4A_BF16; c.D = D; c.G = a->G; c.m = m;
-    c.tok0 = 0; c.n_tok = m; c.first_entry = 0; c.n_entries = 1;
+    c.tok0 = 0; c.n_tok = m + (a->ring ? Q - 1 : 0); c.first_entry = 0; c.n_entries = 1;
     c.rope = a->apply_rope != 0; c.theta = a->rope_theta; c.kv = a->kv; c.b0 = 0; c.n_seq = a->B;
     c.ring = a->ring != 0;
     if ((st = compress_check(c, a->norm_w)) != V4A_OK) return st;
     memset(&pl.sq, 0, sizeof pl.sq);
+    int64_t qpos[kMaxSeq];
+    int32_t wl[kMaxSeq];
+    if ((st = step_queries(a->B, Q, m, a->W, a->q_pos, a->win_len, a->ring != 0, qpos, wl, pl.entry, pl.sq, name)) !=
+        V4A_OK)
+        return st;
     for (int b = 0; b < a->B; b++) {
-        const int64_t t = a->q_pos[b];
-        if (t < 0) return fail(V4A_EINVAL, "%s: q_pos[%d] < 0", name, b);
         if (a->n_entries[b] < 0 || a->n_entries[b] > a->kv->cap)
             return fail(V4A_EINVAL, "%s: n_entries[%d] not in [0, cap]", name, b);
-        const int64_t i = (t + 1) % m == 0 ? (t + 1) / m - 1 : -1;
-        if (i >= a->n_entries[b])
+        if (pl.entry[b] >= a->n_entries[b])
             return fail(V4A_EINVAL, "%s: n_entries[%d] does not include the entry this step completes", name, b);
-        pl.entry[b] = i;
-        int64_t vis = (t + 1) / m;
-        if (vis > a->n_entries[b]) vis = a->n_entries[b];
-        if (vis > (1 << 30)) return fail(V4A_EUNSUPPORTED, "%s: too many entries", name);
-        pl.sq.n_ent[b] = (int32_t)vis;
+        for (int j = 0; j < Q; j++) {
+            int64_t vis = (qpos[b * Q + j] + 1) / m;
+            if (vis > a->n_entries[b]) vis = a->n_entries[b];
+            if (vis > (1 << 30)) return fail(V4A_EUNSUPPORTED, "%s: too many entries", name);
+            pl.sq.n_ent[b * Q + j] = (int32_t)vis;
+        }
     }
+    const int BQ = a->B * Q;
     AttnArgs &at = pl.at;
     at.q = a->q;
-    at.B = a->B;
+    at.B = BQ;
     at.H = a->H;
     at.kv = a->kv;
     at.kv_bstride = a->kv->cap;
@@ -1180,16 +1228,15 @@ static v4a_status step_hca_plan(const v4a_decode_step_hca_args *a, StepHcaPlan &
     at.theta = a->rope_theta;
     at.out = a->out;
     size_t need = 0;
-    if ((st = decode_prepare(at, pl.sq, a->win_len, a->q_pos, a->q_t, a->win_t, a->out_t, &need, name,
-                             a->no_split != 0)) != V4A_OK)
+    if ((st = decode_prepare(at, pl.sq, wl, qpos, a->q_t, a->win_t, a->out_t, &need, name, a->no_split != 0)) != V4A_OK)
         return st;
     if (!attn_uses_mfma(at)) return fail(V4A_EUNSUPPORTED, "%s: needs the MFMA attention shapes", name);
     if (a->q_norm_w && !aligned(a->q_norm_w, 16)) return fail(V4A_EINVAL, "%s: q_norm_w must be 16-byte aligned", name);
     at.q_norm_w = a->q_norm_w;
     if (a->ring) {
-        for (int b = 0; b < a->B; b++)
-            if (pl.sq.win_len[b] > a->q_pos[b] + 1)
-                return fail(V4A_EINVAL, "%s: win_len[%d] exceeds the tokens so far", name, b);
+        for (int qi = 0; qi < BQ; qi++)
+            if (pl.sq.win_len[qi] > pl.sq.q_pos[qi] + 1)
+                return fail(V4A_EINVAL, "%s: win_len[%d] exceeds the tokens so far", name, qi / Q);
         pl.sq.ring = 1;
     }
     pl.attn_bytes = round_up(need, 256);

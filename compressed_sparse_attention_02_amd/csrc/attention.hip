@@ -77,6 +77,8 @@ struct AttnParams {
     int item0;               // split-free launches: first (query, head group) item
 };
 
+static_assert(sizeof(AttnParams) + sizeof(SeqInfo) <= 4096, "kernel arguments");
+
 constexpr int kShortTiles = 48;  // key lists of at most this many tiles take <= 2 tiles per split
 
 __host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int *tps, int *splits) {
@@ -259,7 +261,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         for (int r = wvu; r < kTile; r += NW) {
             const int e = __builtin_amdgcn_readlane(my_e, r);
             const bool ok = e >= 0 && (int64_t)e < P.cap;
-            const int64_t row = (int64_t)b * P.kv_bstride + (ok ? e : 0);
+            const int64_t row = (int64_t)sq_slot(Sq, b) * P.kv_bstride + (ok ? e : 0);
             const uint8_t *src = !ok ? g_zero_row
                                      : (16 * lane < Dn ? P.nope + row * Dn + 16 * lane
                                                        : (const uint8_t *)P.rope + row * (2 * R) + (16 * lane - Dn));
@@ -267,7 +269,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         }
         if (wv == NW - 1 && lane < kTile) {
             const bool ok = my_e >= 0 && (int64_t)my_e < P.cap;
-            const float *src = ok ? P.kscale + (int64_t)b * P.kv_bstride + my_e : (const float *)g_zero_row;
+            const float *src = ok ? P.kscale + (int64_t)sq_slot(Sq, b) * P.kv_bstride + my_e : (const float *)g_zero_row;
             __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc[q][0], 4, 0, 0);
             kval[q][lane] = ok ? 1 : 0;
         }
@@ -319,7 +321,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                     if (kidx < n_ent) {
                         const int64_t e = P.topk ? (int64_t)sidx[kidx - kb0] : (int64_t)kidx;
                         if (e >= 0 && e < P.cap) {
-                            const int64_t row = (int64_t)b * P.kv_bstride + e;
+                            const int64_t row = (int64_t)sq_slot(Sq, b) * P.kv_bstride + e;
                             valid[j] = true;
                             scl[j] = P.kscale[row];
                             if (dim < Dn) {
@@ -758,11 +760,11 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
 // scores in LDS, fp32 arithmetic throughout (no split).
 constexpr int kF32MaxKeys = 8192 + 2048;
 
-__device__ __forceinline__ float load_key_dim(const AttnParams &P, int b, const WinRows &wr, int64_t e, int wtok,
+__device__ __forceinline__ float load_key_dim(const AttnParams &P, int64_t kvb, const WinRows &wr, int64_t e, int wtok,
                                               int d) {
     const int Dn = P.D - P.R;
     if (e >= 0) {
-        const int64_t row = (int64_t)b * P.kv_bstride + e;
+        const int64_t row = kvb + e;
         if (P.fmt == V4A_KV_F32) return ((const float *)P.nope)[row * P.D + d];
         if (d < Dn) {
             const uint8_t c = P.nope[row * Dn + d];
@@ -804,7 +806,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
         float s = -INFINITY;
         if (e >= 0 || wtok >= 0) {
             float acc = 0.0f;
-            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, b, wr, e, wtok, d), acc);
+            for (int d = 0; d < D; d++) acc = fmaf(qs[d], load_key_dim(P, (int64_t)sq_slot(Sq, b) * P.kv_bstride, wr, e, wtok, d), acc);
             s = scale * acc;
         }
         sc[j] = s;
@@ -845,7 +847,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams P, SeqInfo Sq)
                 wtok = j - n_ent;
             }
             if (e < 0 && wtok < 0) continue;
-            acc = fmaf(sc[j], load_key_dim(P, b, wr, e, wtok, d), acc);
+            acc = fmaf(sc[j], load_key_dim(P, (int64_t)sq_slot(Sq, b) * P.kv_bstride, wr, e, wtok, d), acc);
         }
         osh[d] = den > 0.0f ? acc / den : 0.0f;
     }

@@ -176,30 +176,44 @@ struct QueryPos {
     int64_t n_ent[kMaxSeq];
 };
 
+__host__ __device__ __forceinline__ int64_t query_pos(const QueryPos &P, int qi) {
+    const int b = qi / P.Q, j = qi % P.Q;
+    return P.mode == 0 ? P.pos[qi] : P.pos[b] + j;
+}
+
 __host__ __device__ __forceinline__ int64_t visible_keys(const QueryPos &P, int qi) {
-    int b = qi / P.Q, j = qi % P.Q;
-    int64_t pos = P.mode == 0 ? P.pos[qi] : P.pos[b] + j;
+    int b = qi / P.Q;
+    int64_t pos = query_pos(P, qi);
     int64_t v = (pos + 1) / P.m;
     int64_t n = P.n_ent[b];
     v = v < n ? v : n;
     return v < 0 ? 0 : v;
 }
 
-// The queries an attention launch serves.  Mode 0 (decode): query b is the newest token of
-// sequence b, described by the arrays.  Mode 1 (prefill): query b is the token at tok0 + b of
-// one sequence; its window is the W stream rows ending at itself, read from a buffer whose row
-// 0 holds position tok0 - n_prev; it attends over fixed_ent top-k entries (CSA) or, when
-// fixed_ent is 0, over its visible prefix of the n_total cached entries (ratio m).
+// The queries an attention launch serves.  Mode 0 (decode): query b is a new token of sequence
+// b / qps (qps consecutive tokens per sequence, one unless a multi-token step), described by the
+// arrays; the window buffer holds win_stride rows per sequence.  Mode 1 (prefill): query b is
+// the token at tok0 + b of one sequence; its window is the W stream rows ending at itself, read
+// from a buffer whose row 0 holds position tok0 - n_prev; it attends over fixed_ent top-k entries
+// (CSA) or, when fixed_ent is 0, over its visible prefix of the n_total cached entries (ratio m).
 struct SeqInfo {
     int mode;
-    int ring;                  // mode 0: the window buffer is a ring (position p at row p mod W)
+    int ring;                  // mode 0: the window buffer is a ring (position p at row p mod win_stride)
     int64_t tok0;
     int n_prev, W, m, fixed_ent;
     int64_t n_total;
-    int32_t n_ent[kMaxSeq];    // entry keys of sequence b (k for CSA, visible entries for HCA)
+    int qps;                   // mode 0: queries per sequence (0 or 1: one)
+    int win_stride;            // mode 0: window rows per sequence (0: W)
+    int32_t n_ent[kMaxSeq];    // entry keys of query b (k for CSA, visible entries for HCA)
     int32_t win_len[kMaxSeq];
+    int32_t win_off[kMaxSeq];  // mode 0, rows: query b's oldest window row within its sequence's rows
     int64_t q_pos[kMaxSeq];
 };
+
+// Cache slot (sequence) of query b.
+__host__ __device__ __forceinline__ int sq_slot(const SeqInfo &S, int b) {
+    return (!S.mode && S.qps > 1) ? b / S.qps : b;
+}
 
 __host__ __device__ __forceinline__ int64_t sq_pos(const SeqInfo &S, int b) {
     return S.mode ? S.tok0 + b : S.q_pos[b];
@@ -215,13 +229,18 @@ __host__ __device__ __forceinline__ int sq_n_ent(const SeqInfo &S, int b) {
     const int64_t v = (S.tok0 + b + 1) / S.m;
     return (int)(v < S.n_total ? v : S.n_total);
 }
-// Row of the window buffer holding query b's oldest window token (W rows per sequence in mode 0).
+// Window rows per sequence in mode 0.
+__host__ __device__ __forceinline__ int sq_win_stride(const SeqInfo &S, int W) {
+    return S.win_stride > 0 ? S.win_stride : W;
+}
+// Row of the window buffer holding query b's oldest window token.
 __host__ __device__ __forceinline__ int64_t sq_win_row0(const SeqInfo &S, int b, int W) {
-    return S.mode ? (int64_t)b + S.n_prev - sq_win_len(S, b) + 1 : (int64_t)b * W;
+    return S.mode ? (int64_t)b + S.n_prev - sq_win_len(S, b) + 1
+                  : (int64_t)sq_slot(S, b) * sq_win_stride(S, W) + S.win_off[b];
 }
 
 // Rows of query b's window tokens, token j = 0 the oldest: consecutive rows from the oldest's,
-// or, for a ring (mode 0), the sequence's W rows with position p at row p mod W.
+// or, for a ring (mode 0), the sequence's win_stride rows with position p at row p mod win_stride.
 struct WinRows {
     int64_t base;
     int start, W;
@@ -238,9 +257,11 @@ __host__ __device__ __forceinline__ WinRows sq_win_rows(const SeqInfo &S, int b,
     w.ring = S.ring && !S.mode;
     w.start = 0;
     if (w.ring) {
-        w.base = (int64_t)b * W;
+        const int stride = sq_win_stride(S, W);
+        w.W = stride;
+        w.base = (int64_t)sq_slot(S, b) * stride;
         const int64_t p0 = S.q_pos[b] - S.win_len[b] + 1;  // the oldest window position, >= 0
-        w.start = (int)(p0 % W);
+        w.start = (int)(p0 % stride);
     } else {
         w.base = sq_win_row0(S, b, W);
     }

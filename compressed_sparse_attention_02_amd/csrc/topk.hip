@@ -223,23 +223,26 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     __shared__ uint32_t soff[kMaxSlices + 1];
     const int BQ = (int)gridDim.x - P.n_rec;
     if ((int)blockIdx.x >= BQ) {
-        const int b = (int)blockIdx.x - BQ;
+        // sequence b, whose QP.Q queries (its new tokens) are queries b*Q .. b*Q+Q-1
+        const int b = (int)blockIdx.x - BQ, Q = QP.Q;
         if (threadIdx.x >= 64) {  // one wavefront per record; the others clear the histograms
             if (P.hist_clear) {
-                uint4 *h = P.hist_clear + (int64_t)b * P.hist_n16;
-                for (int j = (int)threadIdx.x - 64; j < P.hist_n16; j += kSelThreads - 64) h[j] = make_uint4(0, 0, 0, 0);
+                uint4 *h = P.hist_clear + (int64_t)b * Q * P.hist_n16;
+                for (int j = (int)threadIdx.x - 64; j < Q * P.hist_n16; j += kSelThreads - 64) h[j] = make_uint4(0, 0, 0, 0);
             }
             return;
         }
-        const int64_t pos = QP.pos[b];
         const int m = P.rec.m;
-        if ((pos + 1) % m != 0) return;  // no block completed
-        const int64_t i = (pos + 1) / m - 1;
         float *scratch = (float *)hist;  // kMaxCand floats; this workgroup does no selection
-        if (P.rec.D == 512)
-            compress_entry<8>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
-        else
-            compress_entry<2>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+        for (int j = 0; j < Q; j++) {  // Q <= m: at most one of the tokens completes a block
+            const int64_t pos = query_pos(QP, b * Q + j);
+            if ((pos + 1) % m != 0) continue;  // no block completed by this token
+            const int64_t i = (pos + 1) / m - 1;
+            if (P.rec.D == 512)
+                compress_entry<8>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+            else
+                compress_entry<2>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+        }
         return;
     }
     const int qi = blockIdx.x, t = threadIdx.x;
@@ -457,12 +460,12 @@ hipError_t launch_select(const SelectArgs &a, const QueryPos &qp, hipStream_t s)
                            P, qp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.rec) {  // one query per sequence: pos[b] is sequence b's position in either mode
-        if (qp.Q != 1) return hipErrorInvalidValue;
+    if (a.rec) {  // one workgroup per sequence, whose Q queries are its new tokens
+        if (qp.Q < 1 || a.BQ % qp.Q != 0 || qp.Q > a.rec->m) return hipErrorInvalidValue;
         P.rec = compress_params(*a.rec);
-        P.n_rec = a.BQ;
+        P.n_rec = a.BQ / qp.Q;
         P.hist_clear = (uint4 *)a.hist_clear;
-        P.hist_n16 = P.copies * kHistBins / 4;
+        P.hist_n16 = P.copies * kHistBins / 4;  // one query's histograms
     } else if (a.hist_clear) {
         return hipErrorInvalidValue;
     }

@@ -353,6 +353,22 @@ V4A_API size_t v4a_prefill_workspace(v4a_layer kind, const v4a_prefill_args *arg
  * has written it since.  The call then skips clearing them (one launch fewer).  Every call
  * leaves them clear, so a caller that keeps one workspace per (B, k) for its decode loop may
  * pass ws_clean = 1 from the second step on.  With ws_clean = 0 the call clears them itself.
+ * Multi-token step (Q > 1; [cyqw] section 2 and the model table of [cyqw] section 4.2 and
+ * [firecat]: V4 keeps multi-token prediction at depth 1, so a step may verify Q consecutive
+ * tokens per sequence): sequence b's new tokens sit at positions t-Q+1 .. t with t = q_pos[b];
+ * query j (0-based) is the token at t_j = t-Q+1+j.  The Q queries are evaluated together and
+ * causally, exactly as Q steps of one token taken in order: query j sees the entries whose block
+ * ends at or before t_j (so an entry completed by a later token of the step is not visible to
+ * it, one completed by an earlier token is) and the window tokens ending at t_j.  At most one
+ * block completes per step (Q <= m).  Shapes per sequence: q [B][Q][H][D], q_idx rows
+ * [B][Q*H_I] (slot b holds its queries' heads in query order), w [B][Q][H_I], out [B][Q][H][D].
+ * Stream rows: the plain layout holds [B][2m] rows, the B-block and the block completed by a
+ * token of the step (positions m*(i-1) .. m*(i+1)-1 for entry i); a ring holds [B][2m+Q-1] rows
+ * with position p at row p mod (2m+Q-1).  Window: query j's window is the
+ * min(win_len[b], t_j+1) tokens ending at t_j; the buffer holds W+Q-1 rows per sequence
+ * ([B][W+Q-1][D]): in the plain layout the tokens ending at t from row 0 (positions
+ * max(0, t-win_len[b]-Q+2) .. t), in a ring position p at row p mod (W+Q-1).  Q = 1 is the
+ * one-token step described above, with its layouts unchanged.  B*Q <= 128.
  * Supports the MFMA shapes: D = 512 records with d_I = 128 MXFP4 keys, or D = 128 with
  * d_I = 32; H a multiple of 16 up to 128; B <= 128; k <= 2048. */
 typedef struct {
@@ -391,6 +407,7 @@ typedef struct {
     int32_t no_split;            /* nonzero: split-free attention (see below)                   */
     const float *q_norm_w;       /* [D] f32 (device, 16-byte aligned) or NULL: see below         */
     int32_t ws_clean;            /* nonzero: the workspace's histograms are clear (see above)   */
+    int32_t Q;                   /* new tokens (queries) per sequence, 1..4 (0 means 1): see below */
 } v4a_decode_step_args;
 
 V4A_API v4a_status v4a_decode_step_csa(const v4a_decode_step_args *args, void *ws, size_t ws_bytes,
@@ -425,6 +442,10 @@ V4A_API v4a_status v4a_decode_step_csa_noalloc(const v4a_decode_step_args *args,
  * position p sits at row p mod m of its sequence's rows and at row p mod W of the window,
  * whose tokens are positions t-win_len[b]+1 .. t (win_len[b] <= t+1).
  * no_split: the split-free attention of v4a_decode_step_csa.
+ * Q > 1: the multi-token step of v4a_decode_step_csa (queries at t-Q+1 .. t, each seeing the
+ * entries whose block ends at or before it and the window ending at it).  Stream rows: the
+ * plain layout holds the block completed by a token of the step ([B][m] rows, positions m*i ..
+ * m*i+m-1), a ring [B][m+Q-1] rows with position p at row p mod (m+Q-1); the window as for CSA.
  * Supports the MFMA attention shapes (FP8/BF16 records with D in {128, 512}, H a multiple of 16
  * up to 128), m <= 128, B <= 128. */
 typedef struct {
@@ -455,6 +476,7 @@ typedef struct {
     int32_t ring;                /* nonzero: the stream rows and the window are rings          */
     int32_t no_split;            /* nonzero: split-free attention (see below)                  */
     const float *q_norm_w;       /* [D] f32 (device, 16-byte aligned) or NULL: as for CSA       */
+    int32_t Q;                   /* new tokens (queries) per sequence, 1..4 (0 means 1)         */
 } v4a_decode_step_hca_args;
 
 V4A_API v4a_status v4a_decode_step_hca(const v4a_decode_step_hca_args *args, void *ws, size_t ws_bytes,

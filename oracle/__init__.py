@@ -358,3 +358,23 @@ def prefill_queries(kind, q, records, n_entries, stream, *, n_prev, tok0, querie
             outs[j] = decode_hca(q[j], records, n_entries, window, sink, scale, q_pos=t, m=m,
                                  rope_inverse=rope_inverse, R=R, theta=theta)
     return outs, sels
+
+
+def decode_tokens(kind, q, records, n_entries, stream, *, t_last, Q, win_len, sink, scale, m, k=None, idx=None,
+                  rope_inverse=True, R=64, theta=10000.0, score_bf16=False):
+    """A multi-token decode step of one sequence: its Q new tokens at positions t_last-Q+1 .. t_last
+    evaluated together.  "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2 and the
+    model table of section 4.2: V4 keeps multi-token prediction with depth 1, so a step can verify a
+    drafted token together with the new one.  Each query is the decode step at its own position:
+    ``records`` (and, for CSA, the keys in ``idx``) hold every entry cached after the step,
+    including one that a token of the step completes, and query j, at t_j = t_last-Q+1+j, sees only
+    the entries whose block ends at or before t_j (causal visibility by block end) and the
+    min(win_len, t_j+1) raw tokens ending at t_j.  stream: raw rows by position 0 .. t_last.
+    q [Q][H][D]; idx per query as in prefill_queries.  Returns (out [Q][H][D], selections [Q][k]
+    for CSA or None)."""
+    tok0 = t_last - Q + 1
+    outs, sels = prefill_queries(kind, q, records, n_entries, stream, n_prev=tok0, tok0=tok0, queries=range(Q),
+                                 W=win_len, sink=sink, scale=scale, m=m, k=k, idx=idx, rope_inverse=rope_inverse,
+                                 R=R, theta=theta, score_bf16=score_bf16)
+    out = np.stack([outs[j] for j in range(Q)])
+    return out, (np.stack([sels[j] for j in range(Q)]) if kind == "csa" else None)
