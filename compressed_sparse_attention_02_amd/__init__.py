@@ -126,6 +126,10 @@ def lib() -> ctypes.CDLL:
         L.v4a_decode_step_csa.restype = ctypes.c_int
         L.v4a_decode_step_workspace.argtypes = [DSP]
         L.v4a_decode_step_workspace.restype = SZ
+        L.v4a_output_projection.argtypes = [P, I32, I32, I32, I32, I32, P, P, I32, P, ctypes.c_int, P, SZ, P]
+        L.v4a_output_projection.restype = ctypes.c_int
+        L.v4a_output_projection_workspace.argtypes = [I32, I32, I32]
+        L.v4a_output_projection_workspace.restype = SZ
         L.v4a_decode_step_csa_noalloc.argtypes = [DSP, P]
         L.v4a_decode_step_csa_noalloc.restype = ctypes.c_int
         DHP = ctypes.POINTER(c_decode_step_hca_args)
@@ -434,6 +438,20 @@ def v4a_decode_step_workspace(args: DecodeStepArgs) -> int:
 def v4a_decode_step_csa(args: DecodeStepArgs, ws: torch.Tensor, stream=None):
     _check(lib().v4a_decode_step_csa(ctypes.byref(args.s), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def v4a_output_projection_workspace(T: int, G: int, r: int) -> int:
+    return int(lib().v4a_output_projection_workspace(T, G, r))
+
+
+def v4a_output_projection(o: torch.Tensor, G: int, r: int, wg: torch.Tensor, wf: torch.Tensor, out: torch.Tensor,
+                          ws: torch.Tensor, stream=None):
+    """Grouped output projection of the attention output o [T][H][D] (bf16): group weights wg
+    [G][r][H*D/G], final weights wf [d][G*r] (bf16), out [T][d]; ws holds the reduced groups y
+    [T][G*r] (bf16)."""
+    T, H, D = o.shape
+    _check(lib().v4a_output_projection(_ptr(o), T, H, D, G, r, _ptr(wg), _ptr(wf), wf.shape[0], _ptr(out),
+                                       _ftype(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 V4A_NOALLOC_SCRATCH_BYTES = 64 << 20  # the library's per-device scratch (include/v4attn.h)

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libv4attn.so")
-SOURCES = ["api.hip", "quant.hip", "compress.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "quant.hip", "compress.hip", "indexer.hip", "topk.hip", "attention.hip", "projection.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -196,6 +196,37 @@ using namespace v4a;
 
 extern "C" {
 
+size_t v4a_output_projection_workspace(int32_t T, int32_t G, int32_t r) {
+    if (T < 0 || G < 1 || r < 1) return 0;
+    return round_up((size_t)T * G * r * 2, 256);
+}
+
+v4a_status v4a_output_projection(const void *o, int32_t T, int32_t H, int32_t D, int32_t G, int32_t r,
+                                 const void *wg, const void *wf, int32_t d, void *out, v4a_float out_t,
+                                 void *ws, size_t ws_bytes, void *stream) {
+    const char *name = "v4a_output_projection";
+    if (T < 0) return fail(V4A_EINVAL, "%s: T < 0", name);
+    if (H < 1 || D < 1 || G < 1 || r < 1 || d < 1 || H % G != 0)
+        return fail(V4A_EUNSUPPORTED, "%s: H=%d D=%d G=%d r=%d d=%d (G must divide H)", name, H, D, G, r, d);
+    const int64_t Kg = (int64_t)H * D / G;
+    if (Kg % 128 != 0 || ((int64_t)G * r) % 128 != 0 || r % 16 != 0 || d % 16 != 0)
+        return fail(V4A_EUNSUPPORTED, "%s: H*D/G and G*r must be multiples of 128, r and d of 16", name);
+    if (Kg > (1 << 30) || (int64_t)G * r > (1 << 30)) return fail(V4A_EUNSUPPORTED, "%s: too large", name);
+    if (out_t != V4A_F32 && out_t != V4A_BF16) return fail(V4A_EINVAL, "%s: bad out_t", name);
+    if (T == 0) return V4A_OK;
+    if (!o || !wg || !wf || !out) return fail(V4A_EINVAL, "%s: o, wg, wf and out are required", name);
+    if (!aligned(o, 16) || !aligned(wg, 16) || !aligned(wf, 16) || !aligned(out, 16))
+        return fail(V4A_EINVAL, "%s: o, wg, wf and out must be 16-byte aligned", name);
+    const size_t need = v4a_output_projection_workspace(T, G, r);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(V4A_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need, ws_bytes);
+    OutProjArgs a{};
+    a.o = o; a.T = T; a.H = H; a.D = D; a.G = G; a.r = r; a.d = d;
+    a.wg = wg; a.wf = wf; a.y = ws; a.out = out; a.out_bf16 = out_t == V4A_BF16;
+    g_err.clear();
+    return hip_status(launch_output_projection(a, (hipStream_t)stream), name);
+}
+
 const char *v4a_last_error(void) { return g_err.c_str(); }
 
 const char *v4a_version(void) { return "v4attn 0.1.0 (gfx950)"; }

@@ -370,6 +370,17 @@ struct AttnArgs {
                               // workgroup: full waves of 64-head workgroups, then 16-head ones
 };
 bool attn_uses_mfma(const AttnArgs &a);
+
+struct OutProjArgs {
+    const void *o;            // [T][H*D] bf16: the attention output, heads in order
+    int T, H, D, G, r, d;
+    const void *wg;           // [G][r][H*D/G] bf16
+    const void *wf;           // [d][G*r] bf16
+    void *y;                  // [T][G*r] bf16 (workspace): the reduced groups, concatenated
+    void *out;                // [T][d]
+    bool out_bf16;
+};
+hipError_t launch_output_projection(const OutProjArgs &a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s);
 void split_plan_host(int n_keys, int target, int *tps, int *splits);
 constexpr int kAttnTile = 32;

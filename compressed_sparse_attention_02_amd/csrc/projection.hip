@@ -1,0 +1,259 @@
+// projection.hip -- the grouped output projection after the attention.
+// "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.2, "Grouped Output Projection":
+// with many query heads (128 for V4-Pro) the head outputs are first reduced group by group, then
+// the reduced groups are concatenated and projected, which cuts the output projection's
+// parameters and FLOPs; "DeepSeek V4 technical report explained" (firecat-web.com), item 2: head
+// dim 512 with a grouped projection to lower the cost.
+//
+// Two BF16 GEMMs with fp32 accumulation, both of the form C[M][N] = A[M][K] . W[N][K]^T (rows of
+// activations times the rows of a weight matrix stored out-feature major):
+//   grouped: for group g, y[t][g*r .. g*r+r) = bf16(o[t][g*Kg .. g*Kg+Kg) . wg[g]^T), Kg = H*D/G;
+//   final:   out[t] = y[t] . wf^T.
+// On the MFMA unit the weight rows are the A operand (its rows are output features) and the
+// tokens the B operand, so each lane ends up holding 4 consecutive output features of one token
+// and writes them with one store.
+//   skinny kernel (M <= 64, decode): one workgroup per 16 output features; its four wavefronts
+//     stream disjoint quarters of K (the weights are read once, straight from HBM, in 16-byte
+//     loads, eight k-steps in flight), each holding every token as MFMA B operands, and add
+//     their partial sums in a fixed order through LDS;
+//   tiled kernel (large M, prefill): 128 x 128 output tiles, K in chunks of 64 staged in LDS
+//     (double-buffered, the next chunk's loads in flight during the current chunk's MFMAs),
+//     four wavefronts of 64 x 64 each on v_mfma_f32_32x32x16_bf16.
+#include "common.hpp"
+
+namespace v4a {
+
+struct GemmParams {
+    const uint16_t *A;   // [batch][M][lda] bf16 (activations)
+    const uint16_t *W;   // [batch][N][ldw] bf16 (weights, out-feature major)
+    void *C;             // [batch][M][ldc] bf16 or fp32
+    int M, N, K;
+    int64_t lda, ldw, ldc;
+    int64_t sa, sw, sc;  // batch strides (elements)
+    bool c_bf16;
+};
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+// A streamed (read-once) 16-byte weight load.
+__device__ __forceinline__ uint4 load_nt16(const uint16_t *p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Stores 4 consecutive output features n0..n0+3 of token m (n0 a multiple of 4).
+__device__ __forceinline__ void store4(const GemmParams &P, int64_t cbase, int m, int n0, float a, float b, float c,
+                                       float d) {
+    const int64_t off = cbase + (int64_t)m * P.ldc + n0;
+    if (P.c_bf16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+        *(uint2 *)((uint16_t *)P.C + off) = make_uint2(lo, hi);
+    } else {
+        *(float4 *)((float *)P.C + off) = make_float4(a, b, c, d);
+    }
+}
+
+// ---------------------------------------------------------------- skinny kernel ----
+constexpr int kSkinnyTokens = 64;  // M limit of the skinny kernel (four 16-token MFMA columns)
+constexpr int kSkinnyUnroll = 8;   // k-steps of 32 whose weight loads are in flight together
+
+template <int MT>  // 16-token column tiles held per wavefront (M <= 16 * MT)
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams P) {
+    __shared__ float red[3][MT][64][4];  // partial sums of wavefronts 1..3
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int n0 = blockIdx.x * 16, bt = blockIdx.y;
+    const uint16_t *A = P.A + (int64_t)bt * P.sa;
+    const uint16_t *W = P.W + (int64_t)bt * P.sw + (int64_t)(n0 + col) * P.ldw;  // the lane's weight row
+    const int kq = P.K / 4;                     // this wavefront's quarter of K (a multiple of 32)
+    const int kb = wv * kq;
+    v4f acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; t++) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // token rows of the B operand: lane holds token 16t + col (rows past M read row 0, masked
+    // at the store)
+    int64_t arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; t++) arow[t] = (int64_t)(16 * t + col < P.M ? 16 * t + col : 0) * P.lda;
+    for (int k0 = kb; k0 < kb + kq; k0 += 32 * kSkinnyUnroll) {
+        const int nk = min(kSkinnyUnroll, (kb + kq - k0) / 32);  // uniform
+        uint4 wr[kSkinnyUnroll];
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; u++)
+            if (u < nk) wr[u] = load_nt16(W + k0 + 32 * u + 8 * grp);
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; u++) {
+            if (u >= nk) break;
+            uint4 ar[MT];
+#pragma unroll
+            for (int t = 0; t < MT; t++) ar[t] = *(const uint4 *)(A + arow[t] + k0 + 32 * u + 8 * grp);
+#pragma unroll
+            for (int t = 0; t < MT; t++)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(wr[u]), as_bf(ar[t]), acc[t], 0, 0, 0);
+        }
+    }
+    // fixed-order sum over the four K quarters: ((w0 + w1) + w2) + w3
+    if (wv > 0) {
+#pragma unroll
+        for (int t = 0; t < MT; t++) *(v4f *)red[wv - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    const int64_t cbase = (int64_t)bt * P.sc;
+#pragma unroll
+    for (int t = 0; t < MT; t++) {
+        v4f s = acc[t];
+#pragma unroll
+        for (int w = 0; w < 3; w++) s += *(const v4f *)red[w][t][lane];
+        const int m = 16 * t + col;
+        if (m < P.M) store4(P, cbase, m, n0 + 4 * grp, s[0], s[1], s[2], s[3]);
+    }
+}
+
+// ----------------------------------------------------------------- tiled kernel ----
+constexpr int kTB = 128;        // tile rows (output features) and columns (tokens)
+constexpr int kTK = 64;         // K per LDS chunk
+constexpr int kTRow = kTK + 8;  // LDS row stride (bf16): 16 bytes of padding against bank conflicts
+
+__global__ void __launch_bounds__(256, 2) gemm_tiled_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(16))) uint16_t sW[2][kTB * kTRow];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTB * kTRow];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int n0 = blockIdx.x * kTB, m0 = blockIdx.y * kTB, bt = blockIdx.z;
+    const uint16_t *W = P.W + (int64_t)bt * P.sw;
+    const uint16_t *A = P.A + (int64_t)bt * P.sa;
+    // loads of one chunk: 128 rows x 64 bf16 = 1024 chunks of 16 bytes per operand, 4 per thread;
+    // thread t takes row (t / 8) + 32 i, 16-byte column t % 8
+    const int lr = t >> 3, lc = (t & 7) * 8;
+    int64_t wrow[4], arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = n0 + lr + 32 * i, m = m0 + lr + 32 * i;
+        wrow[i] = (int64_t)(n < P.N ? n : P.N - 1) * P.ldw + lc;
+        arow[i] = (int64_t)(m < P.M ? m : P.M - 1) * P.lda + lc;  // rows past M: a valid row, never stored
+    }
+    uint4 gw[4], ga[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            gw[i] = *(const uint4 *)(W + wrow[i] + k0);  // each weight tile serves every token tile
+            ga[i] = *(const uint4 *)(A + arow[i] + k0);
+        }
+    };
+    auto stash = [&](int q) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            *(uint4 *)&sW[q][(lr + 32 * i) * kTRow + lc] = gw[i];
+            *(uint4 *)&sA[q][(lr + 32 * i) * kTRow + lc] = ga[i];
+        }
+    };
+    // wavefront (wn, wm) computes features 64 wn .. +63 and tokens 64 wm .. +63 of the tile as
+    // 2 x 2 MFMA tiles of 32 x 32; lane: A row (feature) / B column (token) lane % 32, K half lane / 32
+    const int wn = wv & 1, wm = wv >> 1;
+    const int r32 = lane & 31, kh = lane >> 5;
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+    const int nch = P.K / kTK;
+    load(0);
+    stash(0);
+    __syncthreads();
+    for (int c = 0; c < nch; c++) {
+        const int q = c & 1;
+        if (c + 1 < nch) load((c + 1) * kTK);  // in flight during this chunk's MFMAs
+#pragma unroll
+        for (int ks = 0; ks < kTK / 16; ks++) {
+            v8bf wa[2], ab[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                wa[i] = as_bf(*(const uint4 *)&sW[q][(64 * wn + 32 * i + r32) * kTRow + 16 * ks + 8 * kh]);
+                ab[i] = as_bf(*(const uint4 *)&sA[q][(64 * wm + 32 * i + r32) * kTRow + 16 * ks + 8 * kh]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], ab[j], acc[i][j], 0, 0, 0);
+        }
+        if (c + 1 < nch) {
+            stash(q ^ 1);  // the other buffer: its readers finished before the last barrier
+            __syncthreads();
+        }
+    }
+    // lane holds token 64 wm + 32 j + r32 and, per register e, feature 64 wn + 32 i + 8 (e / 4) + 4 kh + e % 4
+    const int64_t cbase = (int64_t)bt * P.sc;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int m = m0 + 64 * wm + 32 * j + r32;
+        if (m >= P.M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * kh;
+                if (n < P.N)
+                    store4(P, cbase, m, n, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]);
+            }
+    }
+}
+
+// C = A . W^T over `batch` independent problems: the skinny kernel for a few tokens, else the tiled one.
+hipError_t launch_gemm(const GemmParams &P, int batch, hipStream_t s) {
+    if (P.M <= 0 || P.N <= 0 || batch <= 0) return hipSuccess;
+    if (P.K % 128 != 0 || P.N % 16 != 0) return hipErrorInvalidValue;
+    if (P.M <= kSkinnyTokens) {
+        dim3 grid((unsigned)(P.N / 16), (unsigned)batch);
+        if (P.M <= 16)
+            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<1>, grid, dim3(256), 0, s, P);
+        else if (P.M <= 32)
+            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<2>, grid, dim3(256), 0, s, P);
+        else
+            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<4>, grid, dim3(256), 0, s, P);
+    } else {
+        if (P.K % kTK != 0 || P.N % 8 != 0) return hipErrorInvalidValue;
+        dim3 grid((unsigned)((P.N + kTB - 1) / kTB), (unsigned)((P.M + kTB - 1) / kTB), (unsigned)batch);
+        V4A_LAUNCH("gemm_tiled_kernel", gemm_tiled_kernel, grid, dim3(256), 0, s, P);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_output_projection(const OutProjArgs &a, hipStream_t s) {
+    const int Kg = a.H * a.D / a.G;
+    GemmParams g{};
+    g.A = (const uint16_t *)a.o;
+    g.W = (const uint16_t *)a.wg;
+    g.C = a.y;
+    g.M = a.T;
+    g.N = a.r;
+    g.K = Kg;
+    g.lda = (int64_t)a.H * a.D;
+    g.ldw = Kg;
+    g.ldc = (int64_t)a.G * a.r;
+    g.sa = Kg;                   // group g reads columns g*Kg .. of every token row
+    g.sw = (int64_t)a.r * Kg;
+    g.sc = a.r;                  // and writes columns g*r .. of y
+    g.c_bf16 = true;
+    hipError_t e = launch_gemm(g, a.G, s);
+    if (e != hipSuccess) return e;
+    GemmParams f{};
+    f.A = (const uint16_t *)a.y;
+    f.W = (const uint16_t *)a.wf;
+    f.C = a.out;
+    f.M = a.T;
+    f.N = a.d;
+    f.K = a.G * a.r;
+    f.lda = (int64_t)a.G * a.r;
+    f.ldw = (int64_t)a.G * a.r;
+    f.ldc = a.d;
+    f.c_bf16 = a.out_bf16;
+    return launch_gemm(f, 1, s);
+}
+
+}  // namespace v4a

@@ -243,6 +243,26 @@ V4A_API v4a_status v4a_decode_hca(const void *q, v4a_float q_t, int32_t B, int32
  * splits than a long one, so the bound can exceed what one long sequence needs). */
 V4A_API size_t v4a_decode_workspace(int32_t B, int32_t H, int32_t D, int64_t n_keys_max, int32_t W);
 
+/* ------------------------------------------------------ grouped output projection ----
+ * [cyqw] section 2.2 "Grouped Output Projection" (with many query heads, 128 for V4-Pro, the
+ * head outputs are first reduced per group, then concatenated and projected, which cuts the
+ * output projection's parameters and FLOPs) and [firecat] item 2 (head dim 512 with a grouped
+ * projection).  For every token t (a row of the attention output o) and group g of H/G
+ * consecutive heads (Kg = H*D/G values):
+ *   y[t][g*r + j] = bf16( sum_{c < Kg} o[t][g*Kg + c] * wg[g][j][c] )   (fp32 accumulation, RNE)
+ *   out[t][n]     = sum_{c < G*r} y[t][c] * wf[n][c]                    (fp32, then out_t)
+ *   o   [T][H][D] bf16 (device), e.g. the output of the decode or prefill calls
+ *   wg  [G][r][Kg] bf16 (device): the group weights, out-feature major
+ *   wf  [d][G*r] bf16 (device): the final weights, out-feature major
+ *   out [T][d] (device, out_t)
+ *   ws: y [T][G*r] bf16, v4a_output_projection_workspace(T, G, r) bytes, 256-byte aligned.
+ * Supports G dividing H, Kg and G*r multiples of 128, r and d multiples of 16, 16-byte aligned
+ * pointers; T >= 0. */
+V4A_API v4a_status v4a_output_projection(const void *o, int32_t T, int32_t H, int32_t D, int32_t G, int32_t r,
+                                 const void *wg, const void *wf, int32_t d, void *out, v4a_float out_t,
+                                 void *ws, size_t ws_bytes, void *stream);
+V4A_API size_t v4a_output_projection_workspace(int32_t T, int32_t G, int32_t r);
+
 /* -------------------------------------------------------------- a8: prefill chunk ----
  * One chunk of C consecutive tokens of one sequence (positions tok0 .. tok0+C-1) through
  * one attention layer of either kind, as C causal queries.  [cyqw] section 3.5 "KV cache

@@ -82,6 +82,10 @@ def _declare(L):
     L.orc_topk_bf16.argtypes = [P, I64, I32, P]
     L.orc_query_prologue.argtypes = [P, I32, I32, P, F64, I32, F64, F64, P]
     L.orc_attend.argtypes = [P, I32, I32, P, I64, P, I64, P, F64, I32, I32, F64, F64, P, P]
+    L.orc_round_bf16.argtypes = [F64]
+    L.orc_round_bf16.restype = F64
+    L.orc_group_reduce.argtypes = [P, I64, I32, I32, I32, I32, P, P]
+    L.orc_project.argtypes = [P, I64, I64, P, I64, P]
 
 
 def _c(a, dtype):
@@ -378,3 +382,40 @@ def decode_tokens(kind, q, records, n_entries, stream, *, t_last, Q, win_len, si
                                  R=R, theta=theta, score_bf16=score_bf16)
     out = np.stack([outs[j] for j in range(Q)])
     return out, (np.stack([sels[j] for j in range(Q)]) if kind == "csa" else None)
+
+
+# ------------------------------------------------------ grouped output projection ---
+
+def round_bf16(x: float) -> float:
+    """x rounded to the nearest BF16 value, ties to even, from double directly."""
+    return float(lib().orc_round_bf16(float(x)))
+
+
+def group_reduce(o_bits, G: int, r: int, wg_bits) -> np.ndarray:
+    """The reduced groups y [T][G*r] (BF16 values as float64) of the attention output o_bits
+    [T][H][D] (BF16 bits) with the group weights wg_bits [G][r][H*D/G] (BF16 bits).
+    "DeepSeek-V4 technical report walkthrough" (cyqw.cn), section 2.2, Grouped Output Projection."""
+    o_bits, po = _c(o_bits, np.uint16)
+    T, H, D = o_bits.shape
+    wg_bits, pw = _c(wg_bits, np.uint16)
+    assert wg_bits.shape == (G, r, H * D // G)
+    y = np.empty((T, G * r), np.float64)
+    lib().orc_group_reduce(po, T, H, D, G, r, pw, y.ctypes.data_as(P))
+    return y
+
+
+def project(x, w_bits) -> np.ndarray:
+    """x [T][K] (float64 values) times the rows of w_bits [N][K] (BF16 bits): [T][N] float64."""
+    x, px = _c(x, np.float64)
+    w_bits, pw = _c(w_bits, np.uint16)
+    T, K = x.shape
+    N = w_bits.shape[0]
+    assert w_bits.shape == (N, K)
+    out = np.empty((T, N), np.float64)
+    lib().orc_project(px, T, K, pw, N, out.ctypes.data_as(P))
+    return out
+
+
+def grouped_projection(o_bits, G: int, r: int, wg_bits, wf_bits) -> np.ndarray:
+    """The grouped output projection [T][d] (float64, before the output cast)."""
+    return project(group_reduce(o_bits, G, r, wg_bits), wf_bits)

@@ -615,3 +615,52 @@ ORC_API void orc_attend(const double *q, int H, int D, const double *E, int64_t 
         free(z);
     }
 }
+
+/* Grouped output projection: [cyqw] section 2.2 "Grouped Output Projection" (the head outputs
+ * are reduced group by group, then concatenated and projected) and [firecat] item 2.  Reading:
+ * G groups of H/G consecutive heads; each group's Kg = H*D/G values are projected to r values
+ * by its own weights, the result is held as BF16 (the precision of activations), the G*r
+ * values are concatenated and projected to d values by the final weights.  Double precision,
+ * products and sums in plain loops. */
+
+/* x rounded to the nearest BF16 value (8 significant bits), ties to even, from double directly
+ * (no intermediate fp32 rounding); finite, normal-range inputs. */
+ORC_API double orc_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    const double m = frexp(x, &e);             /* x = m * 2^e, 0.5 <= |m| < 1 */
+    const double r = nearbyint(ldexp(m, 8));   /* 8 significant bits, ties to even */
+    return ldexp(r, e - 8);
+}
+
+/* y [T][G*r] (BF16 values, as double) of the attention output o [T][H*D] (BF16 bits) and the
+ * group weights wg [G][r][Kg] (BF16 bits). */
+ORC_API void orc_group_reduce(const uint16_t *o, int64_t T, int H, int D, int G, int r, const uint16_t *wg,
+                              double *y) {
+    const int64_t Kg = (int64_t)H * D / G;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        for (int g = 0; g < G; g++) {
+            const uint16_t *x = o + t * (int64_t)H * D + g * Kg;
+            for (int j = 0; j < r; j++) {
+                const uint16_t *w = wg + ((int64_t)g * r + j) * Kg;
+                double acc = 0.0;
+                for (int64_t c = 0; c < Kg; c++) acc += orc_bf16_decode(x[c]) * orc_bf16_decode(w[c]);
+                y[t * (int64_t)G * r + (int64_t)g * r + j] = orc_round_bf16(acc);
+            }
+        }
+    }
+}
+
+/* out [T][N] = x [T][K] (double values) times the rows of w [N][K] (BF16 bits). */
+ORC_API void orc_project(const double *x, int64_t T, int64_t K, const uint16_t *w, int64_t N, double *out) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        for (int64_t n = 0; n < N; n++) {
+            const uint16_t *wn = w + n * K;
+            double acc = 0.0;
+            for (int64_t c = 0; c < K; c++) acc += x[t * K + c] * orc_bf16_decode(wn[c]);
+            out[t * N + n] = acc;
+        }
+    }
+}

@@ -30,6 +30,7 @@ TID = {name: i for i, name in enumerate([
     "q", "q_idx", "w", "sink", "window", "window_h", "records", "keys", "records_h",
     "cache_raw", "cache_b_tail", "q_chunk", "q_idx_chunk", "w_chunk",
     "misc0", "misc1", "misc2", "misc3",
+    "o_attn", "w_group", "w_final",
 ])}
 
 
