@@ -114,89 +114,144 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams P) {
 }
 
 // ----------------------------------------------------------------- tiled kernel ----
-constexpr int kTB = 128;        // tile rows (output features) and columns (tokens)
-constexpr int kTK = 64;         // K per LDS chunk
-constexpr int kTRow = kTK + 8;  // LDS row stride (bf16): 16 bytes of padding against bank conflicts
+// Output tile: 256 features x 128 tokens; wavefront (wn, wm) of four owns 128 features x 64 tokens
+// (4 x 2 MFMA tiles of 32 x 32).  K runs in chunks of 64 through a ring of three LDS stages,
+// filled by direct-to-LDS loads two chunks ahead (no register staging).  An LDS row is one
+// feature's (or token's) 64 K values, 128 bytes in eight 16-byte slots; slot c of row r holds K
+// chunk c ^ ((r >> 1) & 7), so the 16 rows read by one quarter-wavefront hit 16 different
+// 4-bank groups.  Tiles are numbered so that the workgroups resident on one XCD (linear ids
+// congruent mod 8) take consecutive tile numbers, which cover blocks of 4 feature tiles by 8 token
+// tiles and share their operands through that XCD's L2.
+constexpr int kTN = 256;            // tile features
+constexpr int kTM = 128;            // tile tokens
+constexpr int kTK = 64;             // K per stage
+constexpr int kGroupM = 8;          // token tiles per tile group
+constexpr int kStageW = kTN * kTK;  // bf16 elements of one stage's weight tile
+constexpr int kStageA = kTM * kTK;
+constexpr int kStage = kStageW + kStageA;
 
-__global__ void __launch_bounds__(256, 2) gemm_tiled_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(16))) uint16_t sW[2][kTB * kTRow];
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTB * kTRow];
+typedef __attribute__((address_space(3))) void *gemm_lds_ptr_t;
+typedef __attribute__((address_space(1))) void *gemm_glb_ptr_t;
+
+struct TiledMap {
+    int nN, nM, per_batch, batch, per_xcd;
+};
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// One chunk: the direct loads of chunk k_next into stage `next` (when issue), then the MFMAs of the
+// chunk held in stage `cur`.  The two stages are distinct restrict pointers: the loads into one
+// never hold up the operand reads of the other.
+__device__ __forceinline__ void tiled_chunk(const uint16_t *__restrict__ cur, uint16_t *__restrict__ next, bool issue,
+                                            int k_next, const uint16_t *const (&wsrc)[8],
+                                            const uint16_t *const (&asrc)[4], int wv_u, const int (&wrow)[4],
+                                            const int (&arow)[2], int kh, v16f (&acc)[4][2]) {
+    if (issue) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(wsrc[i] + k_next),
+                                             (gemm_lds_ptr_t)(next + (64 * wv_u + 8 * i) * kTK), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(asrc[i] + k_next),
+                                             (gemm_lds_ptr_t)(next + kStageW + (32 * wv_u + 8 * i) * kTK), 16, 0, 0);
+    }
+    const uint16_t *__restrict__ sa = cur + kStageW;
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ks++) {
+        const int ch = 2 * ks + kh;  // this lane's 16-byte K chunk
+        v8bf wa[4], ab[2];
+#pragma unroll
+        for (int i = 0; i < 4; i++) wa[i] = as_bf(*(const uint4 *)(cur + wrow[i] * kTK + 8 * swz(wrow[i], ch)));
+#pragma unroll
+        for (int j = 0; j < 2; j++) ab[j] = as_bf(*(const uint4 *)(sa + arow[j] * kTK + 8 * swz(arow[j], ch)));
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], ab[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+__global__ void __launch_bounds__(256, 1) gemm_tiled_kernel(GemmParams P, TiledMap TM) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kStage];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int n0 = blockIdx.x * kTB, m0 = blockIdx.y * kTB, bt = blockIdx.z;
+    // tile of this workgroup: XCD-contiguous numbering, then (batch, group of kGroupM token tiles)
+    const int L = blockIdx.x;
+    const int T = (L & 7) * TM.per_xcd + (L >> 3);
+    if (T >= TM.per_batch * TM.batch) return;  // uniform
+    const int bt = T / TM.per_batch, loc = T % TM.per_batch;
+    const int gsz = kGroupM * TM.nN, grp = loc / gsz, in = loc % gsz;
+    const int gm = min(kGroupM, TM.nM - grp * kGroupM);  // token tiles in this (last) group
+    const int tn = in / gm, tm = grp * kGroupM + in % gm;
+    const int n0 = tn * kTN, m0 = tm * kTM;
     const uint16_t *W = P.W + (int64_t)bt * P.sw;
     const uint16_t *A = P.A + (int64_t)bt * P.sa;
-    // loads of one chunk: 128 rows x 64 bf16 = 1024 chunks of 16 bytes per operand, 4 per thread;
-    // thread t takes row (t / 8) + 32 i, 16-byte column t % 8
-    const int lr = t >> 3, lc = (t & 7) * 8;
-    int64_t wrow[4], arow[4];
+
+    // direct loads: one instruction moves 8 rows x 128 bytes (lane l -> row l / 8, slot l % 8, which
+    // holds K chunk swz(row, l % 8)); wavefront w takes weight rows 64 w .. 64 w + 63 and token
+    // rows 32 w .. 32 w + 31
+    const int lrow = lane >> 3, slot = lane & 7;
+    const uint16_t *wsrc[8];
+    const uint16_t *asrc[4];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int r = 64 * wv + 8 * i + lrow;
+        wsrc[i] = W + (int64_t)min(n0 + r, P.N - 1) * P.ldw + 8 * swz(r, slot);
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int n = n0 + lr + 32 * i, m = m0 + lr + 32 * i;
-        wrow[i] = (int64_t)(n < P.N ? n : P.N - 1) * P.ldw + lc;
-        arow[i] = (int64_t)(m < P.M ? m : P.M - 1) * P.lda + lc;  // rows past M: a valid row, never stored
+        const int r = 32 * wv + 8 * i + lrow;
+        asrc[i] = A + (int64_t)min(m0 + r, P.M - 1) * P.lda + 8 * swz(r, slot);  // rows past M: valid, never stored
     }
-    uint4 gw[4], ga[4];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            gw[i] = *(const uint4 *)(W + wrow[i] + k0);  // each weight tile serves every token tile
-            ga[i] = *(const uint4 *)(A + arow[i] + k0);
-        }
-    };
-    auto stash = [&](int q) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            *(uint4 *)&sW[q][(lr + 32 * i) * kTRow + lc] = gw[i];
-            *(uint4 *)&sA[q][(lr + 32 * i) * kTRow + lc] = ga[i];
-        }
-    };
-    // wavefront (wn, wm) computes features 64 wn .. +63 and tokens 64 wm .. +63 of the tile as
-    // 2 x 2 MFMA tiles of 32 x 32; lane: A row (feature) / B column (token) lane % 32, K half lane / 32
+    const int wv_u = __builtin_amdgcn_readfirstlane(wv);
     const int wn = wv & 1, wm = wv >> 1;
     const int r32 = lane & 31, kh = lane >> 5;
-    v16f acc[2][2];
+    v16f acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+    int wrow[4], arow[2];
+#pragma unroll
+    for (int i = 0; i < 4; i++) wrow[i] = 128 * wn + 32 * i + r32;
+#pragma unroll
+    for (int j = 0; j < 2; j++) arow[j] = 64 * wm + 32 * j + r32;
+
     const int nch = P.K / kTK;
-    load(0);
-    stash(0);
-    __syncthreads();
-    for (int c = 0; c < nch; c++) {
-        const int q = c & 1;
-        if (c + 1 < nch) load((c + 1) * kTK);  // in flight during this chunk's MFMAs
+    // chunks 0 and 1 travel first; chunk c is computed from stage c % 3 while chunk c+1 (issued
+    // earlier) and c+2 (issued at its start, into the stage chunk c-1 used) travel
+    for (int c = 0; c < 2 && c < nch; c++) {
 #pragma unroll
-        for (int ks = 0; ks < kTK / 16; ks++) {
-            v8bf wa[2], ab[2];
+        for (int i = 0; i < 8; i++)
+            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(wsrc[i] + c * kTK),
+                                             (gemm_lds_ptr_t)(smem + c * kStage + (64 * wv_u + 8 * i) * kTK), 16, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                wa[i] = as_bf(*(const uint4 *)&sW[q][(64 * wn + 32 * i + r32) * kTRow + 16 * ks + 8 * kh]);
-                ab[i] = as_bf(*(const uint4 *)&sA[q][(64 * wm + 32 * i + r32) * kTRow + 16 * ks + 8 * kh]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], ab[j], acc[i][j], 0, 0, 0);
-        }
-        if (c + 1 < nch) {
-            stash(q ^ 1);  // the other buffer: its readers finished before the last barrier
-            __syncthreads();
-        }
+        for (int i = 0; i < 4; i++)
+            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(asrc[i] + c * kTK),
+                                             (gemm_lds_ptr_t)(smem + c * kStage + kStageW + (32 * wv_u + 8 * i) * kTK), 16, 0, 0);
     }
-    // lane holds token 64 wm + 32 j + r32 and, per register e, feature 64 wn + 32 i + 8 (e / 4) + 4 kh + e % 4
+    for (int c = 0; c < nch; c++) {
+        // this wavefront's loads of chunk c have landed (chunk c+1's may still travel); after the
+        // barrier every wavefront's have, and chunk c-1's readers are done with its stage
+        if (c + 1 < nch) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        tiled_chunk(smem + (c % 3) * kStage, smem + ((c + 2) % 3) * kStage, c + 2 < nch, (c + 2) * kTK, wsrc, asrc, wv_u,
+                    wrow, arow, kh, acc);
+    }
+    // lane holds token 64 wm + 32 j + r32 and, per register e, feature 128 wn + 32 i + 8 (e / 4) + 4 kh + e % 4
     const int64_t cbase = (int64_t)bt * P.sc;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int m = m0 + 64 * wm + 32 * j + r32;
         if (m >= P.M) continue;
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * kh;
+                const int n = n0 + 128 * wn + 32 * i + 8 * g + 4 * kh;
                 if (n < P.N)
                     store4(P, cbase, m, n, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                            acc[i][j][4 * g + 3]);
@@ -218,8 +273,13 @@ hipError_t launch_gemm(const GemmParams &P, int batch, hipStream_t s) {
             V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<4>, grid, dim3(256), 0, s, P);
     } else {
         if (P.K % kTK != 0 || P.N % 8 != 0) return hipErrorInvalidValue;
-        dim3 grid((unsigned)((P.N + kTB - 1) / kTB), (unsigned)((P.M + kTB - 1) / kTB), (unsigned)batch);
-        V4A_LAUNCH("gemm_tiled_kernel", gemm_tiled_kernel, grid, dim3(256), 0, s, P);
+        TiledMap TM;
+        TM.nN = (P.N + kTN - 1) / kTN;
+        TM.nM = (P.M + kTM - 1) / kTM;
+        TM.per_batch = TM.nN * TM.nM;
+        TM.batch = batch;
+        TM.per_xcd = (TM.per_batch * batch + 7) / 8;
+        V4A_LAUNCH("gemm_tiled_kernel", gemm_tiled_kernel, dim3((unsigned)(8 * TM.per_xcd)), dim3(256), 0, s, P, TM);
     }
     return hipGetLastError();
 }
