@@ -75,7 +75,7 @@ def main():
 
     import torch
     import compressed_sparse_attention_02_amd as v4
-    from workloads import CSA_PRO_1M, HCA_1M, decode_inputs, normal, to_bf16_bits
+    from workloads import CSA_FLASH, CSA_PRO_1M, HCA_1M, decode_inputs, normal, to_bf16_bits
 
     torch.cuda.set_device(0)
     dev = "cuda"
@@ -218,6 +218,16 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     tok_s = B / (ms_step / 1e3)
+    # the same steps again, each between its own pair of events on the step's stream (the host
+    # enqueues faster than the GPU drains, so each interval is that step's GPU time): percentiles
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        step(args.warmup + i)
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
+    step_pct = percentiles([a.elapsed_time(b) for a, b in step_ev])
 
     # the fused step again with the library's kernel timing: each kernel launch carries its own
     # start and stop HIP events (on the step's stream), so every kernel's live duration is known;
@@ -320,7 +330,9 @@ def main():
         "config": {"workload": wl.name, "batch": B, "context_tokens": T, "csa_entries": N, "heads": H,
                    "head_dim": D, "rope_dims": R, "indexer_heads": HI, "indexer_dim": dI, "topk": k,
                    "window": W, "input_copies": len(sets), "entry_point": "v4a_decode_step_csa"},
-        "roofline": {"kernel": "indexer_mxfp4_kernel (the MXFP4 scoring launch of the fused step)", "bound": "hbm",
+        "roofline": {"kernel": "indexer_mxfp4_kernel (the MXFP4 scoring launch of the fused step)",
+                     "scope": "the dominant kernel alone; the whole step's HBM fraction is step.hbm_frac",
+                     "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(), "ms_per_launch": score_ms, "algorithmic_bytes": score_bytes,
                      "mfma_util": idx_flops / (score_ms / 1e3) / (MXFP4_PEAK_TFLOPS * 1e12),
@@ -330,6 +342,7 @@ def main():
                               "frac": idx_bytes / (idx_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "step": {"algorithmic_bytes": step_bytes, "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9,
                  "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, "flops": step_flops,
+                 "ms_per_step_pct": step_pct,
                  "ms_separate_calls": ms_step_sep,
                  "kernel_ms": kernel_ms,
                  "wall_s": wall},
@@ -353,6 +366,8 @@ def main():
         result.setdefault("variants", {})["split_free_attention"] = {
             "entry_point": "v4a_decode_step_csa (no_split)", "ms_per_step": ms_ns, "tokens_per_s": B / (ms_ns / 1e3),
             "ms_per_step_split_k": ms_step}
+        result["variants"]["multi_token_q2"] = mtp_variant(v4, torch, args, sets, step_kwargs, inp, bf16, f32, B, H,
+                                                           D, W, HI, dI, N)
     if not args.no_secondary:
         del sets, step_args, step_kwargs, ns_args
         torch.cuda.empty_cache()
@@ -361,6 +376,12 @@ def main():
         result["secondary"]["prefill_csa_4k_on_64k"] = prefill_secondary(v4, torch, "csa", args)
         torch.cuda.empty_cache()
         result["secondary"]["prefill_hca_4k_on_64k"] = prefill_secondary(v4, torch, "hca", args)
+        torch.cuda.empty_cache()
+        result["secondary"]["csa_decode_flash_131k"] = csa_step_secondary(v4, torch, CSA_FLASH, args, f32, bf16)
+        torch.cuda.empty_cache()
+        result["secondary"]["compress_1m"] = compress_secondary(v4, torch, args)
+        torch.cuda.empty_cache()
+        result["secondary"]["output_projection"] = projection_secondary(v4, torch, args)
 
     if not args.no_cpu_baseline:
         import oracle
@@ -436,6 +457,13 @@ def hca_secondary(v4, torch, wl, args, f32, bf16):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    pct = percentiles([x.elapsed_time(y) for x, y in ev])
 
     # the whole per-token step in one call (v4a_decode_step_hca): the newest token completes a
     # 128-token block, which is compressed into entry N-1 first; the window is a ring
@@ -472,7 +500,7 @@ def hca_secondary(v4, torch, wl, args, f32, bf16):
 
     nbytes = B * N * ((D - R) + 2 * R + 4) + B * W * D * 2 + B * H * D * 2 * 2
     flops = 4.0 * B * H * D * (N + W)
-    return {"workload": wl.name, "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms,
+    return {"workload": wl.name, "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms, "ms_per_step_pct": pct,
             "bound": "mfma", "mfma_tflops": flops / (ms / 1e3) / 1e12,
             "mfma_frac": flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "input_copies": rot,
@@ -538,6 +566,15 @@ def prefill_secondary(v4, torch, kind, args):
         return e0.elapsed_time(e1) / reps
 
     ms = time_chunk(a)
+    # each kernel of the chunk, timed by the library's per-launch events
+    v4.v4a_trace_begin(64)
+    for _ in range(3):
+        v4.v4a_prefill_chunk(layer, a, ws)
+    n_tr = v4.v4a_trace_end()
+    torch.cuda.synchronize()
+    kms = {}
+    for name, kt in v4.trace_kernels(n_tr):
+        kms[name] = kms.get(name, 0.0) + kt / 3
     # algorithmic flops: every query's indexer dots over its visible entries (MXFP4) and its
     # attention over its keys (BF16, 4*H*D per key: QK and PV)
     vis = [min(n_total, (tok0 + j + 1) // m) for j in range(C)]
@@ -546,15 +583,184 @@ def prefill_secondary(v4, torch, kind, args):
     bf16_flops = 4.0 * H * D * attn_keys
     mx_flops = 2.0 * wl.H_I * wl.d_I * sum(vis) if kind == "csa" else 0.0
     t = ms / 1e3
-    res = {"tokens_per_s": C / t, "ms_per_chunk": ms, "bound": "mfma",
-           "bf16_tflops": bf16_flops / t / 1e12, "bf16_mfma_frac": bf16_flops / t / (BF16_PEAK_TFLOPS * 1e12)}
+    res = {"tokens_per_s": C / t, "ms_per_chunk": ms, "bound": "mfma", "kernel_ms": kms,
+           "bf16_tflops": bf16_flops / t / 1e12, "bf16_mfma_frac": bf16_flops / t / (BF16_PEAK_TFLOPS * 1e12),
+           "attention_kernel_bf16_mfma_frac": bf16_flops / (kms["attn_mfma_kernel"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12)}
     if kind == "csa":
-        res.update(mxfp4_tflops=mx_flops / t / 1e12, mxfp4_mfma_frac=mx_flops / t / (MXFP4_PEAK_TFLOPS * 1e12),
+        res.update(scoring_kernel_mxfp4_mfma_frac=mx_flops / (kms["indexer_mxfp4_kernel"] / 1e3) /
+                   (MXFP4_PEAK_TFLOPS * 1e12),
+                   mxfp4_tflops=mx_flops / t / 1e12, mxfp4_mfma_frac=mx_flops / t / (MXFP4_PEAK_TFLOPS * 1e12),
                    mfma_time_frac=(bf16_flops / (BF16_PEAK_TFLOPS * 1e12) + mx_flops / (MXFP4_PEAK_TFLOPS * 1e12)) / t)
         ms_b = time_chunk(a_bf16)
         res.update(ms_per_chunk_bf16_scores=ms_b, tokens_per_s_bf16_scores=C / (ms_b / 1e3))
     else:
         res["mfma_time_frac"] = bf16_flops / (BF16_PEAK_TFLOPS * 1e12) / t
+    return res
+
+
+def percentiles(ms):
+    """Median and 10th / 90th percentiles of per-step times (ms)."""
+    v = np.asarray(ms, np.float64)
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90)),
+            "mean": float(v.mean()), "n": int(v.size)}
+
+
+def timed(torch, fn, steps, warmup):
+    """Mean GPU time (ms) of fn(i) over `steps` back-to-back calls, and its per-call percentiles."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(warmup + i)
+    b.record()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, percentiles([x.elapsed_time(y) for x, y in ev])
+
+
+def mtp_variant(v4, torch, args, sets, step_kwargs, inp, bf16, f32, B, H, D, W, HI, dI, N):
+    """The headline step verifying two tokens per sequence (multi-token prediction with depth 1):
+    queries at positions T-2 and T-1 of every sequence, evaluated together in one call."""
+    from workloads import CSA_PRO_1M, normal
+    wl = CSA_PRO_1M
+    s = wl.seed
+    Q = 2
+    q2 = bf16(normal(s, "q", (B, Q, H, D)))
+    qi2 = v4.Idx.empty(B, Q * HI, dI)
+    v4.v4a_quantize_mxfp4(f32(normal(s, "q_idx", (B * Q * HI, dI))), qi2)
+    w2 = f32(normal(s, "w", (B, Q, HI)))
+    win2 = bf16(normal(s, "window", (B, W + Q - 1, D)))
+    out2 = torch.empty((B, Q, H, D), dtype=torch.bfloat16, device="cuda")
+    margs = []
+    for kw in step_kwargs:
+        kw2 = dict(kw)
+        kw2.update(q=q2, q_idx=qi2, w=w2, win=win2, out=out2, Q=Q)
+        margs.append(v4.DecodeStepArgs(**kw2))
+    mws = v4.workspace(v4.v4a_decode_step_workspace(margs[0]))
+    ms, pct = timed(torch, lambda i: v4.v4a_decode_step_csa(margs[i % len(margs)], mws), args.steps, args.warmup)
+    return {"entry_point": "v4a_decode_step_csa (Q = 2)", "queries_per_sequence": Q, "ms_per_step": ms,
+            "ms_per_step_pct": pct, "tokens_per_s": B * Q / (ms / 1e3)}
+
+
+def csa_step_secondary(v4, torch, wl, args, f32, bf16):
+    """The fused CSA decode step of a second workload (the Flash-like 131K-context batch): tokens/s
+    and the step's algorithmic HBM bytes over its time."""
+    from workloads import decode_inputs, normal
+    print(f"[bench] secondary: {wl.name}", file=sys.stderr, flush=True)
+    inp = decode_inputs(wl, threads=16)
+    B, H, D, R, W, k, HI, dI, m, N = wl.B, wl.H, wl.D, wl.R, wl.W, wl.k, wl.H_I, wl.d_I, wl.m, inp["N"]
+    T = wl.T
+    s = wl.seed
+    kv0 = v4.KV.empty(B, N, D, R)
+    v4.v4a_quantize_kv(f32(inp.pop("records").reshape(-1, D)), kv0)
+    keys0 = v4.Idx.empty(B, N, dI)
+    v4.v4a_quantize_mxfp4(f32(inp.pop("keys").reshape(-1, dI)), keys0)
+    qi = v4.Idx.empty(B, HI, dI)
+    v4.v4a_quantize_mxfp4(f32(inp["q_idx"].reshape(-1, dI)), qi)
+    raw = {n: (bf16 if n in ("kv_a", "kv_b", "idx_a", "idx_b") else f32)(
+        normal(s, n, (B, 2 * m, D if n in ("kv_a", "kv_b") else (dI if n.startswith("idx_") and "gate" not in n else 1))))
+        for n in ("kv_a", "kv_b", "gate_a", "gate_b", "idx_a", "idx_b", "idx_gate_a", "idx_gate_b")}
+    bias = {n: f32(normal(s, n, (m, 1))) for n in ("bias_a", "bias_b", "idx_bias_a", "idx_bias_b")}
+    # input copies rotated so that the keys and records do not stay in the 256 MB Infinity Cache
+    rot = max(1, min(args.rotate, 8))
+    copies = [(kv0, keys0)] + [(v4.KV(kv0.fmt, D, R, kv0.nope.clone(), kv0.rope.clone(), kv0.scale.clone(), N),
+                                v4.Idx(keys0.fmt, dI, keys0.codes.clone(), keys0.scales.clone(), N))
+                               for _ in range(rot - 1)]
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    q_pos = [T - 1] * B
+    sargs = [v4.DecodeStepArgs(q_pos=q_pos, n_entries=[N] * B, m=m, kv=kv, keys=keys, q_idx=qi, w=f32(inp["w"]), k=k,
+                               q=bf16(inp["q"]), win=bf16(inp["window"]), win_len=[W] * B, W=W,
+                               sink=f32(inp["sink"]), softmax_scale=wl.scale, out=out, **raw, **bias)
+             for kv, keys in copies]
+    sws = v4.workspace(v4.v4a_decode_step_workspace(sargs[0]))
+    v4.v4a_decode_step_csa(sargs[0], sws)
+    cargs = [v4.DecodeStepArgs(q_pos=q_pos, n_entries=[N] * B, m=m, kv=kv, keys=keys, q_idx=qi, w=f32(inp["w"]),
+                               k=k, q=bf16(inp["q"]), win=bf16(inp["window"]), win_len=[W] * B, W=W,
+                               sink=f32(inp["sink"]), softmax_scale=wl.scale, out=out, ws_clean=True, **raw, **bias)
+             for kv, keys in copies]
+    ms, pct = timed(torch, lambda i: v4.v4a_decode_step_csa(cargs[i % rot], sws), args.steps, args.warmup)
+    nbytes = B * N * (dI // 2 + dI // 32) + B * HI * (dI // 2 + dI // 32 + 4) + B * k * ((D - R) + 2 * R + 4) + \
+        B * W * D * 2 + B * H * D * 2 * 2 + B * 2 * m * (D + dI) * 2 * 2
+    return {"workload": wl.name, "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms, "ms_per_step_pct": pct,
+            "bound": "hbm", "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "input_copies": rot,
+            "entry_point": "v4a_decode_step_csa"}
+
+
+def compress_secondary(v4, torch, args):
+    """The standalone compressors over 1,048,576 raw BF16 tokens of one sequence: HCA (m' = 128,
+    8192 records) and CSA (m = 4, overlapped, 262,144 records plus 262,144 MXFP4 indexer keys).
+    Inputs are seeded draws on the device (torch's generator); the figure is algorithmic bytes
+    (every raw row read once, records and keys written) over the call's time."""
+    print("[bench] secondary: compressors over 1M tokens", file=sys.stderr, flush=True)
+    T, D, R, dI = 1 << 20, 512, 64, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260425 + 5)
+
+    def bf16n(*shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def f32n(*shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+
+    res = {}
+    kv_h, gate_h, bias_h = bf16n(T, D), f32n(T, 1), f32n(128, 1)
+    rec_h = v4.KV.empty(1, T // 128, D, R)
+    ms, pct = timed(torch, lambda i: v4.v4a_compress_hca(kv_h, gate_h, bias_h, tok0=0, m=128, first_entry=0,
+                                                         n_entries=T // 128, out_kv=rec_h), 10, 2)
+    nb = T * D * 2 + T * 4 + (T // 128) * ((D - R) + 2 * R + 4)
+    res["hca"] = {"tokens": T, "entries": T // 128, "ms": ms, "ms_pct": pct, "algorithmic_bytes": nb,
+                  "hbm_gbs": nb / (ms / 1e3) / 1e9, "hbm_frac": nb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    del kv_h, gate_h
+    kv_a, kv_b, ga, gb = bf16n(T, D), bf16n(T, D), f32n(T, 1), f32n(T, 1)
+    ba, bb = f32n(4, 1), f32n(4, 1)
+    rec = v4.KV.empty(1, T // 4, D, R)
+    ms_r, pct_r = timed(torch, lambda i: v4.v4a_compress_csa(kv_a, kv_b, ga, gb, ba, bb, tok0=0, m=4, first_entry=0,
+                                                             n_entries=T // 4, out_kv=rec), 10, 2)
+    del kv_a, kv_b
+    ia, ib = bf16n(T, dI), bf16n(T, dI)
+    keys = v4.Idx.empty(1, T // 4, dI)
+    ms_k, pct_k = timed(torch, lambda i: v4.v4a_compress_csa(ia, ib, ga, gb, ba, bb, tok0=0, m=4, first_entry=0,
+                                                             n_entries=T // 4, out_idx=keys), 10, 2)
+    nb_r = 2 * T * D * 2 + 2 * T * 4 + (T // 4) * ((D - R) + 2 * R + 4)
+    nb_k = 2 * T * dI * 2 + 2 * T * 4 + (T // 4) * (dI // 2 + dI // 32)
+    res["csa_records"] = {"tokens": T, "entries": T // 4, "ms": ms_r, "ms_pct": pct_r, "algorithmic_bytes": nb_r,
+                          "hbm_gbs": nb_r / (ms_r / 1e3) / 1e9, "hbm_frac": nb_r / (ms_r / 1e3) / 1e9 / HBM_PEAK_GBS}
+    res["csa_keys"] = {"tokens": T, "entries": T // 4, "ms": ms_k, "ms_pct": pct_k, "algorithmic_bytes": nb_k,
+                       "hbm_gbs": nb_k / (ms_k / 1e3) / 1e9, "hbm_frac": nb_k / (ms_k / 1e3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
+def projection_secondary(v4, torch, args):
+    """The grouped output projection (128 heads of 512 in 16 groups, each reduced to 1024, then
+    projected to 7168) for the decode batch of the headline workload (4 tokens: weight-streaming,
+    HBM-bound) and a 4096-token prefill chunk (MFMA-bound).  Synthetic seeded weights."""
+    print("[bench] secondary: grouped output projection", file=sys.stderr, flush=True)
+    H, D, G, r, d = 128, 512, 16, 1024, 7168
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260425 + 6)
+    Kg = H * D // G
+    wg = (torch.randn((G, r, Kg), generator=g, device="cuda") / math.sqrt(Kg)).to(torch.bfloat16)
+    wf = (torch.randn((d, G * r), generator=g, device="cuda") / math.sqrt(G * r)).to(torch.bfloat16)
+    res = {}
+    for name, T in (("decode_4_tokens", 4), ("prefill_4096_tokens", 4096)):
+        o = (0.3 * torch.randn((T, H, D), generator=g, device="cuda")).to(torch.bfloat16)
+        out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        ws = v4.workspace(v4.v4a_output_projection_workspace(T, G, r))
+        ms, pct = timed(torch, lambda i: v4.v4a_output_projection(o, G, r, wg, wf, out, ws), 20, 3)
+        flops = 2.0 * T * (G * r * Kg + d * G * r)
+        nbytes = 2 * (G * r * Kg + d * G * r) + 2 * T * (H * D + 2 * G * r + d)
+        res[name] = {"tokens": T, "ms": ms, "ms_pct": pct, "flops": flops, "algorithmic_bytes": nbytes,
+                     "mfma_tflops": flops / (ms / 1e3) / 1e12, "mfma_frac": flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12),
+                     "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "bound": "hbm" if T <= 64 else "mfma"}
     return res
 
 

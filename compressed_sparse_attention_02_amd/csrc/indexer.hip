@@ -111,7 +111,10 @@ __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint3
 // row), then merges and encodes the key, writes it to the cache and, through LDS, scores it
 // with the same arithmetic, replacing the stale score before any score leaves the workgroup.
 // The key is bitwise the one the compressor kernel would write, so is its score.
-template <bool KEYREC>
+// STREAM: the keys are read once per launch (decode: one query per sequence), so they are
+// loaded non-temporally; otherwise (a prefill chunk: every query of the chunk reads the same
+// keys) they are loaded through the caches, which serve the other queries' re-reads.
+template <bool KEYREC, bool STREAM>
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(16))) float sbuf[kMaxKeysPerWG];  // this workgroup's scores
@@ -152,7 +155,8 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         for (int u = 0; u < kGroupsPerIter; u++) {
             int64_t key = base + 16 * u + col;
             key = key < kend ? key : kend - 1;
-            const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16));
+            const u32x4 v = STREAM ? __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16))
+                                   : *(const u32x4 *)(kc + key * 64 + grp * 16);
             kd[u] = make_uint4(v.x, v.y, v.z, v.w);
             ksc[u] = *(const uint32_t *)(ks + key * 4);
         }
@@ -416,9 +420,11 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
         const int64_t kpw = (int64_t)64 * gpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
         if (P.key_rec)
-            V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel<true>, grid, dim3(256), 0, s, P, qp);
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<true, true>), grid, dim3(256), 0, s, P, qp);
+        else if (a.Q == 1)
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<false, true>), grid, dim3(256), 0, s, P, qp);
         else
-            V4A_LAUNCH("indexer_mxfp4_kernel", indexer_mxfp4_kernel<false>, grid, dim3(256), 0, s, P, qp);
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<false, false>), grid, dim3(256), 0, s, P, qp);
     } else {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
         V4A_LAUNCH("indexer_f32_kernel", indexer_f32_kernel, grid, dim3(256), 0, s, P, qp);
