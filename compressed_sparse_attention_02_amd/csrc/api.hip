@@ -515,7 +515,8 @@ static int decode_split_cap(int64_t n_keys_max) {
 
 static size_t decode_ws_bytes(int B, int H, int D, int split_cap) {
     if (split_cap <= 1) return 0;
-    return round_up((size_t)B * split_cap * H * D * 4 + (size_t)B * split_cap * H * 2 * 4, 256);
+    // BF16 partial sums, then fp32 (m, l) per head
+    return round_up((size_t)B * split_cap * H * D * 2 + (size_t)B * split_cap * H * 2 * 4, 256);
 }
 
 // Checks a decode call's attention arguments, fills the per-sequence window lengths and

@@ -68,7 +68,7 @@ struct AttnParams {
     RopeTable rt;
     void *out;
     bool out_bf16;
-    float *part_o;           // [B][S][D/16][H][16]: per dim tile, the heads' 16 dims contiguous
+    uint16_t *part_o;        // BF16 [B][S][D/16][H][16]: per dim tile, the heads' 16 dims contiguous
     float *part_ml;          // [B][S][H][2]
     int S;                   // split capacity per sequence
     int target;              // splits aimed at per sequence
@@ -92,6 +92,12 @@ __host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int 
     if (s < 1) s = 1;
     *tps = t;
     *splits = s;
+}
+
+// Element v (0..3) of four BF16 values packed in two words, as fp32.
+__device__ __forceinline__ float bf16_half(const u32x2 &w, int v) {
+    const uint32_t x = w[v >> 1];
+    return bitsf((v & 1) ? (x & 0xFFFF0000u) : (x << 16));
 }
 
 // Factor turning one head's accumulated sum into the output: exp(m - M) / den with
@@ -678,11 +684,17 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
             store_out4(P, b, h, 16 * dt + 4 * grp, o);
         }
     } else {
-        // each store writes 1 KB contiguous: the wavefront's 16 heads x 16 dims of one tile
+        // the unnormalised sums leave rounded to BF16 (fp32's exponent range, so no scaling;
+        // relative error 2^-9 per element), halving the round trip through the combine; each
+        // store writes 512 bytes contiguous: the wavefront's 16 heads x 16 dims of one tile
         // (streaming stores: the combine reads them once)
-        float *po = P.part_o + ((int64_t)(b * P.S + split) * NDT * P.H + h) * 16 + 4 * grp;
+        uint16_t *po = P.part_o + ((int64_t)(b * P.S + split) * NDT * P.H + h) * 16 + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) __builtin_nontemporal_store(O[dt], (v4f *)(po + (int64_t)dt * P.H * 16));
+        for (int dt = 0; dt < NDT; dt++) {
+            const v2bf lo = {(__bf16)O[dt][0], (__bf16)O[dt][1]}, hi = {(__bf16)O[dt][2], (__bf16)O[dt][3]};
+            const u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            __builtin_nontemporal_store(w, (u32x2 *)(po + (int64_t)dt * P.H * 16));
+        }
         if (grp == 0) {
             float *pm = P.part_ml + (((int64_t)b * P.S + split) * P.H + h) * 2;
             pm[0] = m_run;
@@ -712,12 +724,12 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
     if (splits == 1) return;  // uniform over the workgroup
     // the (m, l) and the first 16 partial tiles of the splits are requested before any is used
     float m2s[kMaxSplits], ls[kMaxSplits];
-    const float *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
+    const uint16_t *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
     const int64_t sstride = (int64_t)ndt * P.H * 16;
-    v4f po[16];
+    u32x2 po[16];  // four BF16 partial sums of split s
 #pragma unroll
     for (int s = 0; s < 16; s++)
-        po[s] = s < splits ? __builtin_nontemporal_load((const v4f *)(pbase + s * sstride)) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        po[s] = s < splits ? __builtin_nontemporal_load((const u32x2 *)(pbase + s * sstride)) : u32x2{0u, 0u};
 #pragma unroll
     for (int s = 0; s < kMaxSplits; s++) {
         float2 ml = make_float2(-INFINITY, 0.0f);
@@ -736,19 +748,18 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
         const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
         l = fmaf(ls[s], c, l);
 #pragma unroll
-        for (int v = 0; v < 4; v++) o[v] = fmaf(po[s][v], c, o[v]);
+        for (int v = 0; v < 4; v++) o[v] = fmaf(bf16_half(po[s], v), c, o[v]);
     }
     if (splits > 16) {  // uniform over the workgroup
 #pragma unroll
         for (int s = 16; s < kMaxSplits; s++)
-            po[s - 16] = s < splits ? __builtin_nontemporal_load((const v4f *)(pbase + s * sstride))
-                                    : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            po[s - 16] = s < splits ? __builtin_nontemporal_load((const u32x2 *)(pbase + s * sstride)) : u32x2{0u, 0u};
 #pragma unroll
         for (int s = 16; s < kMaxSplits; s++) {
             const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
             l = fmaf(ls[s], c, l);
 #pragma unroll
-            for (int v = 0; v < 4; v++) o[v] = fmaf(po[s - 16][v], c, o[v]);
+            for (int v = 0; v < 4; v++) o[v] = fmaf(bf16_half(po[s - 16], v), c, o[v]);
         }
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
@@ -921,10 +932,10 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     if (a.rope_inv || a.q_norm_w) fill_rope_table(P.rt, a.R, a.theta);
     P.out = a.out;
     P.out_bf16 = a.out_bf16;
-    P.part_o = a.partial;
+    P.part_o = (uint16_t *)a.partial;
     P.target = a.target_splits;
     P.S = a.split_cap;
-    P.part_ml = a.partial ? a.partial + (size_t)a.B * P.S * a.H * a.D : nullptr;
+    P.part_ml = a.partial ? (float *)((uint16_t *)a.partial + (size_t)a.B * P.S * a.H * a.D) : nullptr;
     if (a.B == 0) return hipSuccess;
     if (!attn_uses_mfma(a)) {
         V4A_LAUNCH("attn_f32_kernel", attn_f32_kernel, dim3(a.H, a.B), dim3(256), 0, s, P, sq);

@@ -50,7 +50,8 @@ def test_workspace_sizes_are_monotone_and_aligned():
     a = v4.v4a_indexer_topk_workspace(4, 1, 262144, 1024)
     b = v4.v4a_indexer_topk_workspace(4, 1, 262145, 1024)
     assert a > 4 * 262144 * 12 and b >= a and a % 256 == 0
-    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) >= 16 * 16 * 128 * 512 * 4
+    # BF16 partial sums of 16 splits plus their fp32 (m, l)
+    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) >= 16 * 16 * 128 * (512 * 2 + 8)
     assert v4.v4a_decode_workspace(1, 8, 128, 0, 0) == 0   # a single split needs no partials
 
 
@@ -230,8 +231,8 @@ def test_decode_step_workspace_and_rejects():
     L = v4.lib()
     s = step_struct()
     need = L.v4a_decode_step_workspace(ctypes.byref(s))
-    # the top-k lists, the indexer workspace and the split partials of 1152 keys (12 splits)
-    assert need >= 4 * 1024 * 4 + v4.v4a_indexer_topk_workspace(4, 1, 262144, 1024) + 4 * 12 * 128 * 512 * 4
+    # the top-k lists, the indexer workspace and the BF16 split partials of 1152 keys (18 splits)
+    assert need >= 4 * 1024 * 4 + v4.v4a_indexer_topk_workspace(4, 1, 262144, 1024) + 4 * 18 * 128 * (512 * 2 + 8)
     assert need % 256 == 0
 
     def call(ws=FAKE, wsb=1 << 40, **kw):
@@ -309,10 +310,10 @@ def hca_step_struct(**kw):
 
 
 def test_decode_workspace_follows_the_split_plan():
-    """The decode workspace holds B x splits x H x (D + 2) fp32 partials, where the split count
-    is the most any sequence up to the given key count takes: target 16 splits, at most two
-    32-key tiles per split for lists of at most 48 tiles."""
-    per = 128 * (512 + 2) * 4
+    """The decode workspace holds, per sequence and split, H x D BF16 partial sums and H fp32
+    (m, l) pairs, where the split count is the most any sequence up to the given key count takes:
+    target 16 splits, at most two 32-key tiles per split for lists of at most 48 tiles."""
+    per = 128 * (512 * 2 + 2 * 4)
     # top-1024 + 128 window = 36 tiles: 18 splits of 2 tiles (33..36 tiles give 17..18)
     assert v4.v4a_decode_workspace(4, 128, 512, 1024, 128) == 4 * 18 * per
     # top-512 + 128 window = 20 tiles: lists of up to 16 tiles take one tile per split (16)
@@ -326,11 +327,11 @@ def test_decode_step_hca_workspace_and_rejects():
     L = v4.lib()
     need = L.v4a_decode_step_hca_workspace(ctypes.byref(hca_step_struct()))
     # the step sizes for its own sequences (8192 entries + 128 window = 260 tiles: 16 splits of
-    # fp32 partials plus (m, l)); the generic query bounds any sequence up to that many keys,
-    # shorter lists included (up to 24 splits of two tiles)
-    assert need == 16 * 16 * 128 * (512 + 2) * 4
+    # BF16 partial sums plus fp32 (m, l)); the generic query bounds any sequence up to that many
+    # keys, shorter lists included (up to 24 splits of two tiles)
+    assert need == 16 * 16 * 128 * (512 * 2 + 2 * 4)
     assert need <= v4.v4a_decode_workspace(16, 128, 512, 8192, 128)
-    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) == 16 * 24 * 128 * (512 + 2) * 4
+    assert v4.v4a_decode_workspace(16, 128, 512, 8192, 128) == 16 * 24 * 128 * (512 * 2 + 2 * 4)
     assert need % 256 == 0
 
     def call(ws=FAKE, wsb=1 << 40, **kw):
