@@ -91,6 +91,8 @@ static v4a_status check_idx(const v4a_idx *x, const char *name) {
     if (x->cap < 1) return fail(V4A_EINVAL, "%s->cap must be >= 1", name);
     if (!x->codes) return fail(V4A_EINVAL, "%s->codes is NULL", name);
     if (x->fmt == V4A_IDX_MXFP4) {
+        // the scoring kernel addresses one slot's rows with 32-bit byte offsets
+        if (x->cap > ((int64_t)1 << 26)) return fail(V4A_EUNSUPPORTED, "%s->cap: at most 2^26 MXFP4 rows per slot", name);
         if (x->d % 32 != 0 || x->d < 32 || x->d > 512)
             return fail(V4A_EUNSUPPORTED, "%s: MXFP4 needs d a multiple of 32 up to 512", name);
         if (!x->scales) return fail(V4A_EINVAL, "%s->scales is NULL", name);

@@ -126,7 +126,9 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
     if (k0 >= n_vis) return;  // uniform over the workgroup
 
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // the wavefront index read as a uniform value, so that everything derived from it (the
+    // wavefront's key range, whole-iteration tests) stays in scalar registers and branches
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;  // col: head/key within 16; grp: MX block / chain
 
     const uint8_t *kc = P.kc + (int64_t)b * P.kcap * 64;
@@ -148,17 +150,19 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     if (own) key_prefetch<2>(P.key, qi, i_new, (int64_t)P.key.m * (i_new - 1), kp);
 
     // Double-buffered: the loads of iteration it+1 are issued before iteration it is computed.
-    // Lanes past the end read a clamped, valid key of this query and are masked afterwards.
+    // Keys are addressed as the sequence's (uniform) base plus a 32-bit offset per lane (a
+    // sequence's key rows span less than 4 GiB); lanes past the end read a clamped, valid key of
+    // this query and are masked afterwards.
+    const uint32_t lane_key0 = (uint32_t)(wbase + col);
+    const uint32_t key_last = (uint32_t)(kend - 1);
     auto load_iter = [&](int it, uint4 (&kd)[kGroupsPerIter], uint32_t (&ksc)[kGroupsPerIter]) {
-        const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
 #pragma unroll
         for (int u = 0; u < kGroupsPerIter; u++) {
-            int64_t key = base + 16 * u + col;
-            key = key < kend ? key : kend - 1;
-            const u32x4 v = STREAM ? __builtin_nontemporal_load((const u32x4 *)(kc + key * 64 + grp * 16))
-                                   : *(const u32x4 *)(kc + key * 64 + grp * 16);
+            const uint32_t key = min(lane_key0 + (uint32_t)(it * kGroupsPerIter * 16 + 16 * u), key_last);
+            const u32x4 *pc = (const u32x4 *)(kc + (key * 64u + (uint32_t)grp * 16u));
+            const u32x4 v = STREAM ? __builtin_nontemporal_load(pc) : *pc;
             kd[u] = make_uint4(v.x, v.y, v.z, v.w);
-            ksc[u] = *(const uint32_t *)(ks + key * 4);
+            ksc[u] = *(const uint32_t *)(ks + key * 4u);
         }
     };
     // the first key batch is requested before the query, so the two latencies overlap
@@ -220,27 +224,23 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         }
         return cu;
     };
+    static_assert(kGroupsPerIter == 4, "the chain transpose below pairs four groups with four lane groups");
     auto compute_iter = [&](int it, const uint4 (&kd)[kGroupsPerIter], const uint32_t (&ksc)[kGroupsPerIter]) {
         const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
-        float c[kGroupsPerIter];
+        uint32_t c[kGroupsPerIter];
 #pragma unroll
-        for (int u = 0; u < kGroupsPerIter; u++) c[u] = key_chain(kd[u], ksc[u]);
-        // the four chains of each key sit in lanes col, col+16, col+32, col+48
-        float c1[kGroupsPerIter], c2[kGroupsPerIter], c3[kGroupsPerIter];
-#pragma unroll
-        for (int u = 0; u < kGroupsPerIter; u++) {
-            c1[u] = __shfl_down(c[u], 16);
-            c2[u] = __shfl_down(c[u], 32);
-            c3[u] = __shfl_down(c[u], 48);
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int u = 0; u < kGroupsPerIter; u++) {
-                float sc = ((c[u] + c1[u]) + c2[u]) + c3[u];
-                if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
-                sbuf[base - k0 + 16 * u + col] = sc;  // slots past kend are never read
-            }
-        }
+        for (int u = 0; u < kGroupsPerIter; u++) c[u] = fbits(key_chain(kd[u], ksc[u]));
+        // Lane group q holds chain q of key col of every group u.  A 4 x 4 transpose across the
+        // lane groups (swap the upper half of c0/c1 with the lower half of c2/c3, then the odd
+        // rows of those with the even rows) leaves lane group q holding chains 0..3 of key col of
+        // group q, so every lane finishes one key with the fixed-order sum.
+        const auto a02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+        const auto a13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+        const auto t01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+        const auto t23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+        float sc = ((bitsf(t01[0]) + bitsf(t01[1])) + bitsf(t23[0])) + bitsf(t23[1]);
+        if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
+        sbuf[base - k0 + 16 * grp + col] = sc;  // slots past kend are never read
     };
     // the new key: merged, encoded (into LDS) and scored right after the first iteration, while
     // the rest of the stream is in flight; its score replaces the stale one after the stream

@@ -93,7 +93,7 @@ typedef struct {
 } v4a_kv;
 
 /* A batch of indexer vectors (keys, or query heads): slot b holds rows [0, cap).
- *   MXFP4: codes u8 [B][cap][d/2], scales u8 [B][cap][d/32]  (device)
+ *   MXFP4: codes u8 [B][cap][d/2], scales u8 [B][cap][d/32]  (device; cap <= 2^26)
  *   F32:   codes f32 [B][cap][d] (device); scales unused (NULL). */
 typedef struct {
     v4a_idx_fmt fmt;
