@@ -94,6 +94,11 @@ __host__ __device__ __forceinline__ void split_plan(int n_keys, int target, int 
     *splits = s;
 }
 
+// 2^x for a softmax weight or a rescale factor (x <= kRescaleSlack): the hardware v_exp_f32
+// alone.  Results below 2^-126 come out as zero instead of subnormal; such a weight is below
+// every rounding of the sums it enters (the running sum is at least 1).
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Element v (0..3) of four BF16 values packed in two words, as fp32.
 __device__ __forceinline__ float bf16_half(const u32x2 &w, int v) {
     const uint32_t x = w[v >> 1];
@@ -539,7 +544,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
                 // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
                 if (mt > m_run + kRescaleSlack) {
-                    const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
+                    const float alpha = exp2_weight(m_run - mt);  // 0 when m_run = -inf
                     l_run *= alpha;
 #pragma unroll
                     for (int i = 0; i < NDT; i++) O[i] *= alpha;
@@ -548,7 +553,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 float pn[8], pr[8];
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
+                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2_weight(s2[i] - m_run);
                     l_run += pi;
                     pr[i] = pi;
                     pn[i] = pi * ks8[i];
@@ -628,7 +633,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 // (log2 units): until then the weights, at most 2^kRescaleSlack, stay exact in fp32 and
                 // BF16 range, and O and l need no rescaling.  Same decision in all four lanes of a head.
                 if (mt > m_run + kRescaleSlack) {
-                    const float alpha = exp2f(m_run - mt);  // 0 when m_run = -inf
+                    const float alpha = exp2_weight(m_run - mt);  // 0 when m_run = -inf
                     l_run *= alpha;
 #pragma unroll
                     for (int i = 0; i < NDT; i++) O[i] *= alpha;
@@ -637,7 +642,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 float pn[8], pr[8];
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2f(s2[i] - m_run);
+                    const float pi = (s2[i] == -INFINITY) ? 0.0f : exp2_weight(s2[i] - m_run);
                     l_run += pi;
                     pr[i] = pi;
                     pn[i] = pi * ks8[i];
