@@ -30,23 +30,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bitsf((uint32_t)b << 16); }
 
-// OCP FP8 E4M3FN encoding of a finite fp32 value: nearest, ties to even, saturating to
-// +-448; the sign bit is kept (a negative value rounding to zero gives 0x80).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    uint32_t s = (fbits(v) >> 24) & 0x80u;
-    float a = fabsf(v);
-    if (!(a < 448.0f)) return s | 0x7Eu;
-    if (a < 0.015625f) {                        // below 2^-6: grid step 2^-9
-        float n = __builtin_rintf(a * 512.0f);  // exact scaling, then nearest-even; n <= 8
-        return s | (uint32_t)n;                 // n == 8 is the code of 2^-6
-    }
-    uint32_t ua = fbits(a);
-    int e = (int)(ua >> 23) - 127;              // a in [2^e, 2^(e+1)), e in [-6, 8]
-    uint32_t mant = ua & 0x7FFFFFu;
-    uint32_t keep = mant >> 20, rem = mant & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep++;
-    if (keep == 8u) { keep = 0; e++; }
-    return s | ((uint32_t)(e + 7) << 3) | keep;
+// OCP FP8 E4M3FN codes (nearest, ties to even, the sign kept: a negative value rounding to zero
+// gives 0x80) of two or four fp32 values, byte v holding the code of the v-th, from the hardware
+// conversion v_cvt_pk_fp8_f32.  For every finite |x| <= 449 its code equals the plain nearest-
+// even E4M3 encoding saturating at 448 (checked exhaustively, all 2.28e9 such fp32 values, on
+// gfx950); callers pass values of magnitude at most 448 (1 + 2^-23).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // E2M1 (FP4) encoding of a value already divided by its block scale: nearest with ties
@@ -134,6 +128,14 @@ struct RopeLanes {
         c = 1.0f;
         s = 0.0f;
         if (lane < npairs) rope_cs_freq(pos, T.inv_freq[lane], &c, &s);
+    }
+    // Two positions in one pass (npairs <= 32): lane j < 32 evaluates pair j at pos0, lane
+    // 32 + j pair j at pos1; get(j) and get(32 + j) then serve them.
+    __device__ __forceinline__ void eval2(const RopeTable &T, int npairs, double pos0, double pos1) {
+        const int lane = threadIdx.x & 63, j = lane & 31;
+        c = 1.0f;
+        s = 0.0f;
+        if (j < npairs) rope_cs_freq(lane < 32 ? pos0 : pos1, T.inv_freq[j], &c, &s);
     }
     __device__ __forceinline__ float2 get(int want) const {
         return make_float2(__shfl(c, want), __shfl(s, want));

@@ -22,8 +22,9 @@
 
 namespace v4a {
 
-// kEntryWaves entries per workgroup, one per wavefront; or, for the long gate-per-token blocks
-// (HCA), one entry per workgroup shared by its kEntryWaves wavefronts.
+// 2 * kEntryWaves entries per workgroup, two consecutive ones per wavefront, whose RoPE cos/sin
+// (R/2 <= 32 pairs each) one pass of the wavefront's 64 lanes evaluates; or, for the long
+// gate-per-token blocks (HCA), one entry per workgroup shared by its kEntryWaves wavefronts.
 template <int VPT>
 __global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressParams P) {
     __shared__ float wsh[kEntryWaves][kMaxCand];
@@ -35,9 +36,19 @@ __global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressPara
         return;
     }
     const int wv = threadIdx.x >> 6;
-    const int64_t e = (int64_t)blockIdx.x * kEntryWaves + wv;
+    const int64_t e = ((int64_t)blockIdx.x * kEntryWaves + wv) * 2;
     if (e >= P.n_entries) return;  // the whole wavefront leaves together
-    compress_entry<VPT>(P, wsh[wv], blockIdx.y, P.first_entry + e, P.tok0);
+    const int64_t i0 = P.first_entry + e;
+    const bool two = e + 1 < P.n_entries;  // uniform
+    if (P.rope && P.R / 2 <= 32) {
+        RopeLanes rl;
+        rl.eval2(P.rt, P.R / 2, (double)(P.m * i0), (double)(P.m * (two ? i0 + 1 : i0)));
+        compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0, P.tok0, &rl, 0);
+        if (two) compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0, &rl, 32);
+    } else {
+        compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0, P.tok0);
+        if (two) compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0);
+    }
 }
 
 // Decode-step prologue, one launch: row y < B compresses one entry of sequence y (where the
@@ -113,7 +124,7 @@ CompressParams compress_params(const CompressArgs &a) {
 hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     if (a.n_entries == 0 || a.n_seq == 0) return hipSuccess;
     const CompressParams P = compress_params(a);
-    const int64_t per_wg = entry_uses_workgroup(P) ? 1 : kEntryWaves;
+    const int64_t per_wg = entry_uses_workgroup(P) ? 1 : 2 * kEntryWaves;
     dim3 grid((unsigned)((a.n_entries + per_wg - 1) / per_wg), (unsigned)a.n_seq), block(64 * kEntryWaves);
     switch (a.D) {
         case 32: case 64: V4A_LAUNCH("compress_kernel", compress_kernel<1>, grid, block, 0, s, P); break;

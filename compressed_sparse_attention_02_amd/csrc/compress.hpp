@@ -226,9 +226,11 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
 
 // The merged entry acc (one wavefront) is normalised, rotated and written as entry i of sequence
 // seq: RMSNorm with the lane's weights nw, RoPE at position m*i, the record or key encoder.
+// rl_pre (uniform): the cos/sin of position m*i already evaluated, pair j in lane rl_lane0 + j.
 template <int VPT>
 __device__ __forceinline__ void finish_entry(const CompressParams &P, float (&acc)[VPT], const float (&nw)[VPT],
-                                             int64_t seq, int64_t i, uint8_t *idx_mirror = nullptr) {
+                                             int64_t seq, int64_t i, uint8_t *idx_mirror = nullptr,
+                                             const RopeLanes *rl_pre = nullptr, int rl_lane0 = 0) {
     const int lane = threadIdx.x & 63;
     const int m = P.m, D = P.D;
     const int d0 = lane * VPT;
@@ -251,13 +253,14 @@ __device__ __forceinline__ void finish_entry(const CompressParams &P, float (&ac
     // evaluates pair j's cos/sin and the owning lanes read them across the wavefront
     if (P.rope) {
         const int rs = D - P.R, npairs = P.R / 2;
-        RopeLanes rl;
-        rl.eval(P.rt, npairs, (double)(m * i));
+        RopeLanes rl_own;
+        if (!rl_pre) rl_own.eval(P.rt, npairs, (double)(m * i));
+        const RopeLanes &rl = rl_pre ? *rl_pre : rl_own;
         if constexpr (VPT >= 2) {
 #pragma unroll
             for (int v = 0; v < VPT; v += 2) {
                 const int j = min(max((d0 - rs + v) / 2, 0), npairs - 1);
-                const float2 cs = rl.get(j);
+                const float2 cs = rl.get(rl_lane0 + j);
                 if (active && d0 >= rs) {
                     const float x = acc[v], y = acc[v + 1];
                     acc[v] = x * cs.x - y * cs.y;
@@ -267,7 +270,7 @@ __device__ __forceinline__ void finish_entry(const CompressParams &P, float (&ac
         } else {
             const float partner = __shfl_xor(acc[0], 1);
             const int j = min(max((d0 - rs) / 2, 0), npairs - 1);
-            const float2 cs = rl.get(j);
+            const float2 cs = rl.get(rl_lane0 + j);
             if (active && d0 >= rs) {
                 const bool even = ((d0 - rs) & 1) == 0;
                 const float x = even ? acc[0] : partner, y = even ? partner : acc[0];
@@ -303,7 +306,7 @@ __host__ __device__ __forceinline__ bool entry_uses_workgroup(const CompressPara
 // wavefront's scratch for the candidate weights.
 template <int VPT>
 __device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
-                                               int64_t tok0) {
+                                               int64_t tok0, const RopeLanes *rl_pre = nullptr, int rl_lane0 = 0) {
     const int lane = threadIdx.x & 63;
     const int64_t x_off = seq * P.n_tok * P.D, g_off = seq * P.n_tok * P.G;
     const int m = P.m, D = P.D;
@@ -346,7 +349,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
 #pragma unroll
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] / l[v];
     }
-    finish_entry<VPT>(P, acc, nw, seq, i);
+    finish_entry<VPT>(P, acc, nw, seq, i, nullptr, rl_pre, rl_lane0);
 }
 
 // Entry i of sequence seq computed by all kEntryWaves wavefronts of the workgroup (gate per

@@ -41,8 +41,15 @@ __device__ __forceinline__ void store_record(const float (&x)[VPT], int lane_dim
         } else {
             float inv = __fdiv_rn(448.0f, amax);
             uint32_t packed[(VPT + 3) / 4] = {};
+            if constexpr (VPT % 4 == 0) {
 #pragma unroll
-            for (int v = 0; v < VPT; v++) packed[v / 4] |= e4m3_encode(x[v] * inv) << (8 * (v % 4));
+                for (int i = 0; i < VPT / 4; i++)
+                    packed[i] = e4m3_encode4(x[4 * i] * inv, x[4 * i + 1] * inv, x[4 * i + 2] * inv, x[4 * i + 3] * inv);
+            } else if constexpr (VPT == 2) {
+                packed[0] = e4m3_encode2(x[0] * inv, x[1] * inv);
+            } else {
+                packed[0] = e4m3_encode2(x[0] * inv, 0.0f) & 0xFFu;
+            }
             if constexpr (VPT % 4 == 0) {
 #pragma unroll
                 for (int i = 0; i < VPT / 4; i++) ((uint32_t *)dst)[i] = packed[i];

@@ -58,9 +58,10 @@ __device__ __forceinline__ void store4(const GemmParams &P, int64_t cbase, int m
 
 // ---------------------------------------------------------------- skinny kernel ----
 constexpr int kSkinnyTokens = 64;  // M limit of the skinny kernel (four 16-token MFMA columns)
-constexpr int kSkinnyUnroll = 8;   // k-steps of 32 whose weight loads are in flight together
 
-template <int MT>  // 16-token column tiles held per wavefront (M <= 16 * MT)
+// MT: 16-token column tiles held per wavefront (M <= 16 * MT); UNROLL: k-steps of 32 whose
+// weight loads are in flight together (16 with one token tile measured 3-4% faster than 8).
+template <int MT, int UNROLL>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams P) {
     __shared__ float red[3][MT][64][4];  // partial sums of wavefronts 1..3
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -78,15 +79,15 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams P) {
     int64_t arow[MT];
 #pragma unroll
     for (int t = 0; t < MT; t++) arow[t] = (int64_t)(16 * t + col < P.M ? 16 * t + col : 0) * P.lda;
-    for (int k0 = kb; k0 < kb + kq; k0 += 32 * kSkinnyUnroll) {
-        const int nk = min(kSkinnyUnroll, (kb + kq - k0) / 32);  // uniform
-        uint4 wr[kSkinnyUnroll];
+    for (int k0 = kb; k0 < kb + kq; k0 += 32 * UNROLL) {
+        const int nk = min(UNROLL, (kb + kq - k0) / 32);  // uniform
+        uint4 wr[UNROLL];
 #pragma unroll
-        for (int u = 0; u < kSkinnyUnroll; u++)
+        for (int u = 0; u < UNROLL; u++)
             if (u < nk) wr[u] = load_nt16(W + k0 + 32 * u + 8 * grp);
 #pragma unroll
-        for (int u = 0; u < kSkinnyUnroll; u++) {
-            if (u >= nk) break;
+        for (int u = 0; u < UNROLL; u++) {
+            if (u >= nk) continue;  // uniform; a predicated step keeps the loop unrolled
             uint4 ar[MT];
 #pragma unroll
             for (int t = 0; t < MT; t++) ar[t] = *(const uint4 *)(A + arow[t] + k0 + 32 * u + 8 * grp);
@@ -266,11 +267,11 @@ hipError_t launch_gemm(const GemmParams &P, int batch, hipStream_t s) {
     if (P.M <= kSkinnyTokens) {
         dim3 grid((unsigned)(P.N / 16), (unsigned)batch);
         if (P.M <= 16)
-            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<1>, grid, dim3(256), 0, s, P);
+            V4A_LAUNCH("gemm_skinny_kernel", (gemm_skinny_kernel<1, 16>), grid, dim3(256), 0, s, P);
         else if (P.M <= 32)
-            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<2>, grid, dim3(256), 0, s, P);
+            V4A_LAUNCH("gemm_skinny_kernel", (gemm_skinny_kernel<2, 8>), grid, dim3(256), 0, s, P);
         else
-            V4A_LAUNCH("gemm_skinny_kernel", gemm_skinny_kernel<4>, grid, dim3(256), 0, s, P);
+            V4A_LAUNCH("gemm_skinny_kernel", (gemm_skinny_kernel<4, 8>), grid, dim3(256), 0, s, P);
     } else {
         if (P.K % kTK != 0 || P.N % 8 != 0) return hipErrorInvalidValue;
         TiledMap TM;
