@@ -40,6 +40,20 @@ __global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressPara
     if (e >= P.n_entries) return;  // the whole wavefront leaves together
     const int64_t i0 = P.first_entry + e;
     const bool two = e + 1 < P.n_entries;  // uniform
+    if constexpr (VPT % 2 == 0) {
+        if (entry_two_phase(P) && P.D == 64 * VPT) {
+            // both entries' rows, gate logits and biases requested before either is merged
+            KeyPrefetch<VPT> ka, kb;
+            key_prefetch<VPT>(P, blockIdx.y, i0, P.tok0, ka);
+            if (two) key_prefetch<VPT>(P, blockIdx.y, i0 + 1, P.tok0, kb);
+            RopeLanes rl;
+            const bool shared = P.rope && P.R / 2 <= 32;
+            if (shared) rl.eval2(P.rt, P.R / 2, (double)(P.m * i0), (double)(P.m * (two ? i0 + 1 : i0)));
+            prefetched_entry_finish<VPT>(P, ka, blockIdx.y, i0, shared ? &rl : nullptr, 0);
+            if (two) prefetched_entry_finish<VPT>(P, kb, blockIdx.y, i0 + 1, shared ? &rl : nullptr, 32);
+            return;
+        }
+    }
     if (P.rope && P.R / 2 <= 32) {
         RopeLanes rl;
         rl.eval2(P.rt, P.R / 2, (double)(P.m * i0), (double)(P.m * (two ? i0 + 1 : i0)));

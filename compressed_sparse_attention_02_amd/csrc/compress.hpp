@@ -431,8 +431,13 @@ __device__ __forceinline__ void key_prefetch(const CompressParams &P, int64_t se
         const int c = min(u, n_cand - 1);
         const uint16_t *x = (const uint16_t *)(c < P.m ? P.x0 : P.x1);
         const uint32_t *src = (const uint32_t *)(x + x_off + candidate_row2(P, i, c, tok0) * P.D + d0);
+        if constexpr (VPT == 8) {  // vec_in: the lane's 16 bytes in one load
+            const uint4 q = *(const uint4 *)src;
+            kp.raw[u][0] = q.x; kp.raw[u][1] = q.y; kp.raw[u][2] = q.z; kp.raw[u][3] = q.w;
+        } else {
 #pragma unroll
-        for (int w = 0; w < VPT / 2; w++) kp.raw[u][w] = src[w];
+            for (int w = 0; w < VPT / 2; w++) kp.raw[u][w] = src[w];
+        }
     }
     const int c = min(lane, n_cand - 1);
     kp.gl = (c < P.m ? P.g0 : P.g1)[g_off + candidate_row2(P, i, c, tok0)];
@@ -454,9 +459,11 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // past the candidates hold -inf and 0, so the maximum is the candidates' maximum, and the
 // butterfly sum over 64 lanes (xor 32, 16, 8 add zeros exactly) is ((e0 + e4) + (e2 + e6)) +
 // ((e1 + e5) + (e3 + e7)), written here in that order.
+// The merge of a prefetched entry into acc (divided by the weight sum): compress_entry's
+// arithmetic step for step.
 template <int VPT>
-__device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t seq, int64_t i,
-                                           uint8_t *idx_mirror, bool to_global = true) {
+__device__ __forceinline__ void key_merge(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t i,
+                                          float (&acc)[VPT]) {
     const int lane = threadIdx.x & 63;
     const int n_cand = entry_candidates(P, i);
     const float z = lane < n_cand ? kp.gl + kp.bl : -INFINITY;
@@ -468,7 +475,6 @@ __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<
 #pragma unroll
     for (int u = 0; u < kRowBatchMax; u++) e[u] = lane_value(ex, u);
     const float den = ((e[0] + e[4]) + (e[2] + e[6])) + ((e[1] + e[5]) + (e[3] + e[7]));
-    float acc[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
 #pragma unroll
@@ -483,6 +489,14 @@ __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<
     }
 #pragma unroll
     for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
+}
+
+template <int VPT>
+__device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t seq, int64_t i,
+                                           uint8_t *idx_mirror, bool to_global = true) {
+    const int lane = threadIdx.x & 63;
+    float acc[VPT];
+    key_merge<VPT>(P, kp, i, acc);
     // finish_entry's steps for an indexer key (RMSNorm if any, no RoPE, MXFP4), without its
     // other branches: this runs once per query in a kernel whose other wavefronts never do
     if (P.norm_w) {
@@ -495,6 +509,15 @@ __device__ __forceinline__ void key_finish(const CompressParams &P, KeyPrefetch<
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] * r * kp.nw[v];
     }
     store_mxfp4<VPT>(acc, lane, true, P.D, P.idx, P.out_row0 + seq * P.cap + i, idx_mirror, to_global);
+}
+
+// A prefetched entry merged and finished as compress_entry would (RoPE from rl_pre when given).
+template <int VPT>
+__device__ __forceinline__ void prefetched_entry_finish(const CompressParams &P, KeyPrefetch<VPT> &kp, int64_t seq,
+                                                        int64_t i, const RopeLanes *rl_pre, int rl_lane0) {
+    float acc[VPT];
+    key_merge<VPT>(P, kp, i, acc);
+    finish_entry<VPT>(P, acc, kp.nw, seq, i, nullptr, rl_pre, rl_lane0);
 }
 
 // Kernel parameters of a checked CompressArgs (host).
