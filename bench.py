@@ -389,7 +389,8 @@ def main():
         print("[bench] oracle on the host", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
         chk = {"topk_equal": True, "topk_recall": 1.0, "max_abs": 0.0, "rel_l2": 0.0, "inexact_dots": 0}
-        for b in range(B):   # the whole step: every sequence's token
+        reps = 3  # passes of the whole step (about 10 s of host work); the check uses the first
+        for rep, b in [(r, bb) for r in range(reps) for bb in range(B)]:   # every sequence's token
             ent = oracle.compress_csa(raw["kv_a"][b], raw["kv_b"][b], raw["gate_a"][b], raw["gate_b"][b],
                                       raw["bias_a"], raw["bias_b"], tok0=tok0, m=m, first_entry=N - 1,
                                       n_entries=1, apply_rope=True, R=R)
@@ -409,6 +410,8 @@ def main():
             qd = bf16_bits_to_f64(to_bf16_bits(inp["q"][b]))
             wd = bf16_bits_to_f64(to_bf16_bits(inp["window"][b]))
             ref = oracle.attend(qd, ents, wd, inp["sink"], scale, rope_inverse=True, R=R, t_q=T - 1)
+            if rep > 0:
+                continue
             ref_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
             chk["topk_equal"] &= bool(np.array_equal(gpu_sel[b], ref_sel))
             chk["topk_recall"] = min(chk["topk_recall"], len(np.intersect1d(gpu_sel[b], ref_sel)) / k)
@@ -417,11 +420,11 @@ def main():
                                 float(np.linalg.norm(gpu_out[b] - ref_bf16) / np.linalg.norm(ref_bf16)))
             chk["inexact_dots"] += bad
         cpu_s = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": B / cpu_s, "unit": "tokens/s", "cores": oracle.threads(),
+        result["cpu_baseline"] = {"value": reps * B / cpu_s, "unit": "tokens/s", "cores": oracle.threads(),
                                   "kind": "oracle", "seconds": cpu_s,
-                                  "sample": f"the whole step ({B} sequences, one token each): compress each new "
-                                            f"block, exact MXFP4 scores of all {N} entries, full-sort top-{k}, "
-                                            "double-precision attention"}
+                                  "sample": f"{reps} passes of the whole step ({B} sequences, one token each): "
+                                            f"compress each new block, exact MXFP4 scores of all {N} entries, "
+                                            f"full-sort top-{k}, double-precision attention"}
         result["check"] = {"sequences": B, "fused_equals_separate_calls": fused_equal, **chk}
     print(json.dumps(result), flush=True)
 
