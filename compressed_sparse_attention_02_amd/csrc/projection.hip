@@ -12,13 +12,15 @@
 // On the MFMA unit the weight rows are the A operand (its rows are output features) and the
 // tokens the B operand, so each lane ends up holding 4 consecutive output features of one token
 // and writes them with one store.
+//   GEMV kernel (M <= 8, decode): as the skinny kernel below, but the weight and token rows
+//     travel through LDS by direct loads of 256 contiguous bytes per row;
 //   skinny kernel (M <= 64, decode): one workgroup per 16 output features; its four wavefronts
 //     stream disjoint quarters of K (the weights are read once, straight from HBM, in 16-byte
-//     loads, eight k-steps in flight), each holding every token as MFMA B operands, and add
+//     loads, 8 or 16 k-steps in flight), each holding every token as MFMA B operands, and add
 //     their partial sums in a fixed order through LDS;
-//   tiled kernel (large M, prefill): 128 x 128 output tiles, K in chunks of 64 staged in LDS
-//     (double-buffered, the next chunk's loads in flight during the current chunk's MFMAs),
-//     four wavefronts of 64 x 64 each on v_mfma_f32_32x32x16_bf16.
+//   tiled kernel (large M, prefill): 256 x 128 output tiles, K in chunks of 64 through three LDS
+//     stages filled by direct loads two chunks ahead, four wavefronts of 128 x 64 each on
+//     v_mfma_f32_32x32x16_bf16.
 #include "common.hpp"
 
 namespace v4a {
@@ -261,12 +263,92 @@ __global__ void __launch_bounds__(256, 1) gemm_tiled_kernel(GemmParams P, TiledM
 }
 
 // C = A . W^T over `batch` independent problems: the skinny kernel for a few tokens, else the tiled one.
+// ------------------------------------------------------------------- GEMV kernel ----
+// M <= 8 tokens (decode): one workgroup per 16 output features, its four wavefronts each
+// streaming a quarter of K.  A wavefront moves its 16 weight rows and the 8 token rows through
+// its own ring of three LDS stages in chunks of 128 K, two chunks ahead of the MFMAs, with
+// direct-to-LDS loads only (one instruction carries four rows x 256 contiguous bytes).  In a
+// row, 16-byte slot s holds K chunk s ^ (row & 15), so the A-operand reads of 16 weight rows
+// hit 16 different 4-bank groups (token rows past M repeat row M-1 and are never stored).
+constexpr int kGvK = 128;                 // K per chunk
+constexpr int kGvRow = 2 * kGvK;          // bytes of one row's chunk
+constexpr int kGvTok = 8;                 // token rows per stage (M limit of this kernel)
+constexpr int kGvStage = (16 + kGvTok) * kGvRow;
+constexpr int kGvLoads = (16 + kGvTok) / 4;  // direct loads per chunk
+
+// The MFMAs of one chunk held in stage `cur` (a restrict pointer: its reads are ordered after
+// the chunk's direct loads by the caller's explicit wait, not by the compiler's).
+__device__ __forceinline__ void gemv_compute(const uint8_t *__restrict__ cur, int col, int grp, v4f &acc) {
+    const int tr = 16 + (col & (kGvTok - 1));  // this lane's token row
+#pragma unroll
+    for (int ks = 0; ks < kGvK / 32; ks++) {
+        const int ch = 4 * ks + grp;
+        const uint4 w = *(const uint4 *)(cur + col * kGvRow + 16 * (ch ^ col));
+        const uint4 a = *(const uint4 *)(cur + tr * kGvRow + 16 * (ch ^ (tr & 15)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(w), as_bf(a), acc, 0, 0, 0);
+    }
+}
+
+__global__ void __launch_bounds__(256) gemm_gemv_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(16))) uint8_t buf[4][3][kGvStage];
+    __shared__ float red[3][64][4];  // partial sums of wavefronts 1..3
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int col = lane & 15, grp = lane >> 4;
+    const int n0 = blockIdx.x * 16, bt = blockIdx.y;
+    const uint16_t *A = P.A + (int64_t)bt * P.sa;
+    const uint16_t *W = P.W + (int64_t)bt * P.sw;
+    const int kq = P.K / 4, kb = wvu * kq;  // this wavefront's quarter of K
+    const int nch = kq / kGvK;
+    // direct load i carries rows 4i .. 4i+3 of the stage: lane l -> row 4i + l/16, slot l%16
+    // (K chunk slot ^ (row & 15)); rows 0..15 are weight rows, 16.. token rows
+    const int qr = lane >> 4, slot = lane & 15;
+    const uint16_t *src[kGvLoads];
+#pragma unroll
+    for (int i = 0; i < kGvLoads; i++) {
+        const int r = 4 * i + qr;
+        const int ks = slot ^ (r & 15);
+        src[i] = r < 16 ? W + (int64_t)(n0 + r) * P.ldw + kb + 8 * ks
+                        : A + (int64_t)min(r - 16, P.M - 1) * P.lda + kb + 8 * ks;
+    }
+    uint8_t *const base = &buf[wvu][0][0];  // stage j at base + j * kGvStage (kept in LDS arithmetic)
+    v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // step c loads chunk c + 2 (past the end the last chunk again, into a stage nobody reads, so
+    // every step issues the same loads and the wait needs no branch) and, for c >= 0, computes
+    // chunk c once its loads have landed (the next two chunks' may travel)
+#pragma clang loop unroll(disable)
+    for (int c = -2; c < nch; c++) {
+        uint8_t *next = base + ((c + 2) % 3) * kGvStage;
+#pragma unroll
+        for (int i = 0; i < kGvLoads; i++)
+            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)src[i], (gemm_lds_ptr_t)(next + 4 * i * kGvRow), 16, 0, 0);
+        if (c + 3 < nch) {  // uniform
+#pragma unroll
+            for (int i = 0; i < kGvLoads; i++) src[i] += kGvK;
+        }
+        if (c >= 0) {  // uniform
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGvLoads) : "memory");
+            gemv_compute(base + (c % 3) * kGvStage, col, grp, acc);
+        }
+    }
+    // fixed-order sum over the four K quarters: ((w0 + w1) + w2) + w3
+    if (wv > 0) *(v4f *)red[wv - 1][lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+    v4f s4 = acc;
+#pragma unroll
+    for (int w = 0; w < 3; w++) s4 += *(const v4f *)red[w][lane];
+    if (col < P.M) store4(P, (int64_t)bt * P.sc, col, n0 + 4 * grp, s4[0], s4[1], s4[2], s4[3]);
+}
+
 hipError_t launch_gemm(const GemmParams &P, int batch, hipStream_t s) {
     if (P.M <= 0 || P.N <= 0 || batch <= 0) return hipSuccess;
     if (P.K % 128 != 0 || P.N % 16 != 0) return hipErrorInvalidValue;
     if (P.M <= kSkinnyTokens) {
         dim3 grid((unsigned)(P.N / 16), (unsigned)batch);
-        if (P.M <= 16)
+        if (P.M <= kGvTok && P.K % (4 * kGvK) == 0)
+            V4A_LAUNCH("gemm_gemv_kernel", gemm_gemv_kernel, grid, dim3(256), 0, s, P);
+        else if (P.M <= 16)
             V4A_LAUNCH("gemm_skinny_kernel", (gemm_skinny_kernel<1, 16>), grid, dim3(256), 0, s, P);
         else if (P.M <= 32)
             V4A_LAUNCH("gemm_skinny_kernel", (gemm_skinny_kernel<2, 8>), grid, dim3(256), 0, s, P);

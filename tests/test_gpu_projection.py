@@ -9,9 +9,10 @@ either side of a rounding midpoint) plus the fp32 accumulation error, taken as
 rounding errors add up like a random walk over the K terms).  Near zero the second term is the
 larger one.  At most 1% of the y elements may differ at all; BF16 outputs also keep relative
 L2 <= 5e-3, fp32 outputs relative L2 <= 1e-4.  Shapes: the decode workload (4 tokens, 128 heads of 512, 16
-groups reduced to 1024, projected to 7168), ragged token counts on both kernels (1 .. 64 tokens
-on the skinny one, 65 .. 300 with partial tiles on the tiled one), and the 4096-token prefill
-chunk on sampled tokens."""
+groups reduced to 1024, projected to 7168), ragged token counts on all three kernels (1 .. 8
+tokens on the LDS-staged GEMV, 9 .. 64 on the skinny one, 65 .. 300 with partial tiles on the
+tiled one), a final stage whose K (384) is not a multiple of 512 (the GEMV's limit, so the
+skinny kernel takes it), and the 4096-token prefill chunk on sampled tokens."""
 import numpy as np
 import pytest
 import torch
@@ -88,20 +89,34 @@ def check(o, wg, wf, G, r, y_gpu, out_gpu, rows, bf16_out=True, what=""):
 def test_decode_shape():
     T, H, D, G, r, d = 4, 128, 512, 16, 1024, 7168
     o, wg, wf = make(810, T, H, D, G, r, d)
-    announce("output projection, decode shape (skinny kernel)")
+    announce("output projection, decode shape (GEMV kernel)")
     y, out = run(o, wg, wf, G, r)
     check(o, wg, wf, G, r, y, out, np.arange(T), what="decode")
     _, out32 = run(o, wg, wf, G, r, torch.float32)
     check(o, wg, wf, G, r, y, out32, np.arange(T), bf16_out=False, what="decode fp32 out")
 
 
-@pytest.mark.parametrize("T", [1, 17, 33, 64, 65, 200, 300])
+def kernel_name(T):
+    return "gemv" if T <= 8 else "skinny" if T <= 64 else "tiled"
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 9, 17, 33, 64, 65, 200, 300])
 def test_ragged_tokens(T):
     H, D, G, r, d = 16, 512, 4, 256, 400
     o, wg, wf = make(820 + T, T, H, D, G, r, d)
-    announce(f"output projection, T={T} ({'skinny' if T <= 64 else 'tiled'} kernel)")
+    announce(f"output projection, T={T} ({kernel_name(T)} kernel)")
     y, out = run(o, wg, wf, G, r)
     check(o, wg, wf, G, r, y, out, np.arange(T), what=f"T={T}")
+
+
+@pytest.mark.parametrize("T", [3, 8])
+def test_final_k_not_multiple_of_512(T):
+    # group stage K = 2048 (GEMV), final stage K = G*r = 384 (skinny kernel)
+    H, D, G, r, d = 16, 512, 4, 96, 272
+    o, wg, wf = make(840 + T, T, H, D, G, r, d)
+    announce(f"output projection, T={T}, final K=384")
+    y, out = run(o, wg, wf, G, r)
+    check(o, wg, wf, G, r, y, out, np.arange(T), what=f"T={T} K=384")
 
 
 def test_prefill_shape_sampled():
