@@ -264,23 +264,28 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
     const int NW = NT >> 6;
     // ---- entry tile tb -> TB[q]: one direct-to-LDS load instruction per LDS row, wavefront w
     // taking rows w, w + NW, ...: M0 at the row's start, lane c copying 16-byte chunk c of the
-    // key's record (FP8 codes, then BF16 RoPE dims).  A row's entry index is uniform: lane r of
-    // every wavefront reads row r's index once per tile and readlane hands it over.
+    // key's record (FP8 codes, then BF16 RoPE dims).  The row's address arithmetic is scalar
+    // except for the lane's choice of codes or RoPE dims; the row's entry index is uniform (the tile's position for a visible prefix; for a top-k
+    // list lane r of every wavefront reads row r's index once per tile and readlane hands it over).
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int64_t krow0 = (int64_t)sq_slot(Sq, b) * P.kv_bstride;  // this sequence's first record row
+    const uint8_t *const kbase_n = P.nope + krow0 * Dn;  // uniform
+    const uint8_t *const kbase_r = (const uint8_t *)P.rope + krow0 * (2 * R);
+    const int cap32 = (int)min(P.cap, (int64_t)INT32_MAX);
     auto issue_entries = [&](int tb, int q) {
         const int my_e = P.topk ? (lane < kTile ? sidx[tb + lane - kb0] : 0) : tb + lane;
         for (int r = wvu; r < kTile; r += NW) {
-            const int e = __builtin_amdgcn_readlane(my_e, r);
-            const bool ok = e >= 0 && (int64_t)e < P.cap;
-            const int64_t row = (int64_t)sq_slot(Sq, b) * P.kv_bstride + (ok ? e : 0);
+            const int e = P.topk ? __builtin_amdgcn_readlane(my_e, r) : tb + r;  // uniform
+            const bool ok = e >= 0 && e < cap32;
+            const bool lane_rope = 16 * lane >= Dn;
             const uint8_t *src = !ok ? g_zero_row
-                                     : (16 * lane < Dn ? P.nope + row * Dn + 16 * lane
-                                                       : (const uint8_t *)P.rope + row * (2 * R) + (16 * lane - Dn));
+                                     : (lane_rope ? kbase_r + (uint64_t)(uint32_t)e * (2 * R) + (16 * lane - Dn)
+                                                  : kbase_n + (uint64_t)(uint32_t)e * Dn + 16 * lane);
             if (lane < RB8 / 16) __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][r * RS8], 16, 0, 0);
         }
         if (wv == NW - 1 && lane < kTile) {
-            const bool ok = my_e >= 0 && (int64_t)my_e < P.cap;
-            const float *src = ok ? P.kscale + (int64_t)sq_slot(Sq, b) * P.kv_bstride + my_e : (const float *)g_zero_row;
+            const bool ok = my_e >= 0 && my_e < cap32;
+            const float *src = ok ? P.kscale + krow0 + my_e : (const float *)g_zero_row;
             __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc[q][0], 4, 0, 0);
             kval[q][lane] = ok ? 1 : 0;
         }
@@ -718,6 +723,9 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
 constexpr int kMaxSplits = 32;
 constexpr int kCombineWaves = 4;
 
+// NS: splits per sequence the launch provides for (16 or kMaxSplits), so launches with few splits
+// keep the register count (and occupancy) of a 16-entry array.
+template <int NS>
 __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnParams P, SeqInfo Sq) {
     const int dt = blockIdx.x * kCombineWaves + (threadIdx.x >> 6), b = blockIdx.z, lane = threadIdx.x & 63;
     const int h = 16 * blockIdx.y + (lane >> 2);
@@ -727,16 +735,16 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
     int tps, splits;
     split_plan(n_keys, P.target, &tps, &splits);
     if (splits == 1) return;  // uniform over the workgroup
-    // the (m, l) and the first 16 partial tiles of the splits are requested before any is used
-    float m2s[kMaxSplits], ls[kMaxSplits];
+    // every split's (m, l) and partial tile are requested before any is used (one memory round trip)
+    float m2s[NS], ls[NS];
     const uint16_t *pbase = P.part_o + ((int64_t)b * P.S * ndt + dt) * P.H * 16 + (int64_t)h * 16 + 4 * (lane & 3);
     const int64_t sstride = (int64_t)ndt * P.H * 16;
-    u32x2 po[16];  // four BF16 partial sums of split s
+    u32x2 po[NS];  // four BF16 partial sums of split s
 #pragma unroll
-    for (int s = 0; s < 16; s++)
+    for (int s = 0; s < NS; s++)
         po[s] = s < splits ? __builtin_nontemporal_load((const u32x2 *)(pbase + s * sstride)) : u32x2{0u, 0u};
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; s++) {
+    for (int s = 0; s < NS; s++) {
         float2 ml = make_float2(-INFINITY, 0.0f);
         if (s < splits) ml = *(const float2 *)(P.part_ml + ((int64_t)(b * P.S + s) * P.H + h) * 2);
         m2s[s] = ml.x;
@@ -744,28 +752,16 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
     }
     float M = P.sink[h] * kLog2e;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; s++)
+    for (int s = 0; s < NS; s++)
         if (s < splits) M = fmaxf(M, m2s[s]);
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float l = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 16; s++) {
+    for (int s = 0; s < NS; s++) {
         const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
         l = fmaf(ls[s], c, l);
 #pragma unroll
         for (int v = 0; v < 4; v++) o[v] = fmaf(bf16_half(po[s], v), c, o[v]);
-    }
-    if (splits > 16) {  // uniform over the workgroup
-#pragma unroll
-        for (int s = 16; s < kMaxSplits; s++)
-            po[s - 16] = s < splits ? __builtin_nontemporal_load((const u32x2 *)(pbase + s * sstride)) : u32x2{0u, 0u};
-#pragma unroll
-        for (int s = 16; s < kMaxSplits; s++) {
-            const float c = (s >= splits || m2s[s] == -INFINITY) ? 0.0f : exp2f(m2s[s] - M);
-            l = fmaf(ls[s], c, l);
-#pragma unroll
-            for (int v = 0; v < 4; v++) o[v] = fmaf(bf16_half(po[s - 16], v), c, o[v]);
-        }
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
     finish4(P, Sq, b, h, d0, 16 * dt + 16 > P.D - P.R, M, l, o);
@@ -1002,8 +998,11 @@ hipError_t launch_attention(const AttnArgs &a, const SeqInfo &sq, hipStream_t s)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P.S <= 1) return e;
-    V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel, dim3(a.D / 16 / kCombineWaves, a.H / 16, a.B),
-               dim3(64 * kCombineWaves), 0, s, P, sq);
+    const dim3 cgrid(a.D / 16 / kCombineWaves, a.H / 16, a.B);
+    if (P.S <= 16)
+        V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel<16>, cgrid, dim3(64 * kCombineWaves), 0, s, P, sq);
+    else
+        V4A_LAUNCH("attn_combine_kernel", attn_combine_kernel<kMaxSplits>, cgrid, dim3(64 * kCombineWaves), 0, s, P, sq);
     return hipGetLastError();
 }
 
