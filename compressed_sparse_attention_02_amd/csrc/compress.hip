@@ -25,14 +25,15 @@ namespace v4a {
 // 2 * kEntryWaves entries per workgroup, two consecutive ones per wavefront, whose RoPE cos/sin
 // (R/2 <= 32 pairs each) one pass of the wavefront's 64 lanes evaluates; or, for the long
 // gate-per-token blocks (HCA), one entry per workgroup shared by its kEntryWaves wavefronts.
-template <int VPT>
+// PK: BF16 streams read with one vector load per lane and row (rows kept as packed pairs).
+template <int VPT, bool PK>
 __global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressParams P) {
     __shared__ float wsh[kEntryWaves][kMaxCand];
     __shared__ float red[kEntryWaves * 64 * VPT];
     if (entry_uses_workgroup(P)) {
         const int64_t e = blockIdx.x;
         if (e >= P.n_entries) return;  // the whole workgroup leaves together
-        compress_entry_wg<VPT>(P, &wsh[0][0], red, blockIdx.y, P.first_entry + e, P.tok0);
+        compress_entry_wg<VPT, PK>(P, &wsh[0][0], red, blockIdx.y, P.first_entry + e, P.tok0);
         return;
     }
     const int wv = threadIdx.x >> 6;
@@ -57,11 +58,11 @@ __global__ void __launch_bounds__(64 * kEntryWaves) compress_kernel(CompressPara
     if (P.rope && P.R / 2 <= 32) {
         RopeLanes rl;
         rl.eval2(P.rt, P.R / 2, (double)(P.m * i0), (double)(P.m * (two ? i0 + 1 : i0)));
-        compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0, P.tok0, &rl, 0);
-        if (two) compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0, &rl, 32);
+        compress_entry<VPT, PK>(P, wsh[wv], blockIdx.y, i0, P.tok0, &rl, 0);
+        if (two) compress_entry<VPT, PK>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0, &rl, 32);
     } else {
-        compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0, P.tok0);
-        if (two) compress_entry<VPT>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0);
+        compress_entry<VPT, PK>(P, wsh[wv], blockIdx.y, i0, P.tok0);
+        if (two) compress_entry<VPT, PK>(P, wsh[wv], blockIdx.y, i0 + 1, P.tok0);
     }
 }
 
@@ -79,7 +80,7 @@ struct PrologueParams {
     size_t zero_n16;
 };
 
-template <int VK>
+template <int VK, bool PK>
 __global__ void __launch_bounds__(64 * kEntryWaves) decode_prologue_kernel(PrologueParams P) {
     __shared__ float wsh[kEntryWaves * kMaxCand];
     __shared__ float red[kEntryWaves * 64 * VK];
@@ -94,11 +95,11 @@ __global__ void __launch_bounds__(64 * kEntryWaves) decode_prologue_kernel(Prolo
     if (i < 0) return;  // the whole workgroup leaves together
     const int64_t tok0 = (int64_t)P.key.m * (i - P.blocks_before);
     if (entry_uses_workgroup(P.key)) {
-        compress_entry_wg<VK>(P.key, wsh, red, y, i, tok0);
+        compress_entry_wg<VK, PK>(P.key, wsh, red, y, i, tok0);
         return;
     }
     if (threadIdx.x >= 64) return;  // one wavefront per entry
-    compress_entry<VK>(P.key, wsh, y, i, tok0);
+    compress_entry<VK, PK>(P.key, wsh, y, i, tok0);
 }
 
 CompressParams compress_params(const CompressArgs &a) {
@@ -140,11 +141,21 @@ hipError_t launch_compress(const CompressArgs &a, hipStream_t s) {
     const CompressParams P = compress_params(a);
     const int64_t per_wg = entry_uses_workgroup(P) ? 1 : 2 * kEntryWaves;
     dim3 grid((unsigned)((a.n_entries + per_wg - 1) / per_wg), (unsigned)a.n_seq), block(64 * kEntryWaves);
+    const bool pk = P.bf16_in && P.vec_in;
     switch (a.D) {
-        case 32: case 64: V4A_LAUNCH("compress_kernel", compress_kernel<1>, grid, block, 0, s, P); break;
-        case 128: V4A_LAUNCH("compress_kernel", compress_kernel<2>, grid, block, 0, s, P); break;
-        case 256: V4A_LAUNCH("compress_kernel", compress_kernel<4>, grid, block, 0, s, P); break;
-        default: V4A_LAUNCH("compress_kernel", compress_kernel<8>, grid, block, 0, s, P); break;
+        case 32: case 64: V4A_LAUNCH("compress_kernel", (compress_kernel<1, false>), grid, block, 0, s, P); break;
+        case 128:
+            if (pk) V4A_LAUNCH("compress_kernel", (compress_kernel<2, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("compress_kernel", (compress_kernel<2, false>), grid, block, 0, s, P);
+            break;
+        case 256:
+            if (pk) V4A_LAUNCH("compress_kernel", (compress_kernel<4, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("compress_kernel", (compress_kernel<4, false>), grid, block, 0, s, P);
+            break;
+        default:
+            if (pk) V4A_LAUNCH("compress_kernel", (compress_kernel<8, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("compress_kernel", (compress_kernel<8, false>), grid, block, 0, s, P);
+            break;
     }
     return hipGetLastError();
 }
@@ -164,11 +175,22 @@ hipError_t launch_decode_prologue(const CompressArgs &key, int blocks_before, in
     P.zero_n16 = zero_bytes / 16;
     const unsigned zx = (unsigned)std::min<size_t>((P.zero_n16 + 64 * kEntryWaves - 1) / (64 * kEntryWaves), 1024);
     dim3 grid(zx > 0 ? zx : 1, (unsigned)(B + 1));
+    const bool pk = P.key.bf16_in && P.key.vec_in;
+    const dim3 block(64 * kEntryWaves);
     switch (key.D) {
-        case 32: case 64: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<1>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
-        case 128: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<2>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
-        case 256: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<4>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
-        case 512: V4A_LAUNCH("decode_prologue_kernel", decode_prologue_kernel<8>, grid, dim3(64 * kEntryWaves), 0, s, P); break;
+        case 32: case 64: V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<1, false>), grid, block, 0, s, P); break;
+        case 128:
+            if (pk) V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<2, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<2, false>), grid, block, 0, s, P);
+            break;
+        case 256:
+            if (pk) V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<4, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<4, false>), grid, block, 0, s, P);
+            break;
+        case 512:
+            if (pk) V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<8, true>), grid, block, 0, s, P);
+            else V4A_LAUNCH("decode_prologue_kernel", (decode_prologue_kernel<8, false>), grid, block, 0, s, P);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

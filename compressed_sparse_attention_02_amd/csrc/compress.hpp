@@ -151,11 +151,15 @@ __device__ __forceinline__ float raw_value(const uint32_t (&w)[VPT], bool bf16, 
 // Gate-per-token merge (G = 1) by one wavefront: the softmax weights of all candidates of entry i
 // go to wsh (exp(z - max), computed once per wavefront: lane c holds candidate c, c + 64, ...)
 // and their sum is returned; candidates [c_begin, c_end) are accumulated into acc in order.
-// Candidate rows are loaded in batches of kRowBatch as raw words, the first batch issued
-// before the gate logits and each next batch before the current one is accumulated.
-template <int VPT>
+// Candidate rows are loaded in batches of kRowBatch as raw words, the first two batches issued
+// before the gate logits and each batch refilled once it has been accumulated.
+// PK: the streams are BF16 with one vector load per lane and row (bf16_in and vec_in), whose
+// rows are kept as packed BF16 pairs (VPT / 2 words) instead of VPT words.
+template <int VPT, bool PK>
 __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
                                              int64_t tok0, int c_begin, int c_end, float (&acc)[VPT]) {
+    static_assert(!PK || VPT % 2 == 0, "packed rows hold BF16 pairs");
+    constexpr int W = PK ? VPT / 2 : VPT;  // raw words per row
     const int lane = threadIdx.x & 63;
     const int D = P.D;
     const int d0 = lane * VPT;
@@ -164,16 +168,36 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
     const int64_t lane_off = (int64_t)(active ? d0 : 0) * esz;  // inactive lanes read dim 0
     const int n_cand = entry_candidates(P, i);
     const EntryStreams es(P, seq, i, tok0);
+    // two batches of rows in flight from the start (a wavefront's share of an HCA block is 16
+    // candidates: all of its rows are requested before the gate logits are used)
     constexpr int kRowBatch = 8;
-    uint32_t xb[kRowBatch][VPT];
-    auto load_batch = [&](int c0) {
+    uint32_t xa[kRowBatch][W], xb[kRowBatch][W];
+    auto load_batch = [&](uint32_t (&dst)[kRowBatch][W], int c0) {
 #pragma unroll
         for (int u = 0; u < kRowBatch; u++) {
             const int c = min(c0 + u, c_end - 1);
-            load_raw<VPT>(es.x[c >= es.m ? 1 : 0] + es.row(c) * D * esz + lane_off, P.bf16_in, P.vec_in, xb[u]);
+            const char *src = es.x[c >= es.m ? 1 : 0] + es.row(c) * D * esz + lane_off;
+            if constexpr (PK) {
+                if constexpr (VPT == 8) {
+                    const uint4 q = *(const uint4 *)src;
+                    dst[u][0] = q.x; dst[u][1] = q.y; dst[u][2] = q.z; dst[u][3] = q.w;
+                } else if constexpr (VPT == 4) {
+                    const uint2 q = *(const uint2 *)src;
+                    dst[u][0] = q.x; dst[u][1] = q.y;
+                } else {
+                    dst[u][0] = *(const uint32_t *)src;
+                }
+            } else {
+                load_raw<VPT>(src, P.bf16_in, P.vec_in, dst[u]);
+            }
         }
     };
-    if (c_begin < c_end) load_batch(c_begin);
+    auto value = [&](const uint32_t (&w)[W], int v) -> float {
+        if constexpr (PK) return bf16_to_f32((uint16_t)((v & 1) ? (w[v / 2] >> 16) : (w[v / 2] & 0xFFFFu)));
+        else return raw_value<VPT>(w, P.bf16_in, v);
+    };
+    if (c_begin < c_end) load_batch(xa, c_begin);
+    if (c_begin + kRowBatch < c_end) load_batch(xb, c_begin + kRowBatch);
     // gate logits of this lane's candidates (up to kMaxCand / 64), all requested before use
     constexpr int kPerLane = kMaxCand / 64;
     float gl[kPerLane], bl[kPerLane];
@@ -205,20 +229,24 @@ __device__ __forceinline__ float merge_gate1(const CompressParams &P, float *wsh
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int c0 = c_begin; c0 < c_end; c0 += kRowBatch) {
-        uint32_t cur[kRowBatch][VPT];
-#pragma unroll
-        for (int u = 0; u < kRowBatch; u++)
-#pragma unroll
-            for (int v = 0; v < VPT; v++) cur[u][v] = xb[u][v];
-        if (c0 + kRowBatch < c_end) load_batch(c0 + kRowBatch);  // next batch in flight
+    // candidates in ascending order: batch xa holds c0 .. c0+7, batch xb c0+8 .. c0+15; each is
+    // refilled with the candidates 16 further once it has been added
+    auto merge_batch = [&](const uint32_t (&x)[kRowBatch][W], int c0) {
 #pragma unroll
         for (int u = 0; u < kRowBatch; u++) {
             if (c0 + u < c_end) {
                 const float wgt = wsh[c0 + u];
 #pragma unroll
-                for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, active ? raw_value<VPT>(cur[u], P.bf16_in, v) : 0.0f, acc[v]);
+                for (int v = 0; v < VPT; v++) acc[v] = fmaf(wgt, active ? value(x[u], v) : 0.0f, acc[v]);
             }
+        }
+    };
+    for (int c0 = c_begin; c0 < c_end; c0 += 2 * kRowBatch) {
+        merge_batch(xa, c0);
+        if (c0 + 2 * kRowBatch < c_end) load_batch(xa, c0 + 2 * kRowBatch);
+        if (c0 + kRowBatch < c_end) {
+            merge_batch(xb, c0 + kRowBatch);
+            if (c0 + 3 * kRowBatch < c_end) load_batch(xb, c0 + 3 * kRowBatch);
         }
     }
     return den;
@@ -304,7 +332,7 @@ __host__ __device__ __forceinline__ bool entry_uses_workgroup(const CompressPara
 // Entry i of sequence seq, computed by one whole wavefront; row 0 of the sequence's streams
 // is position tok0 (its streams and gates start n_tok rows further per sequence); wsh is the
 // wavefront's scratch for the candidate weights.
-template <int VPT>
+template <int VPT, bool PK = false>
 __device__ __forceinline__ void compress_entry(const CompressParams &P, float *wsh, int64_t seq, int64_t i,
                                                int64_t tok0, const RopeLanes *rl_pre = nullptr, int rl_lane0 = 0) {
     const int lane = threadIdx.x & 63;
@@ -320,7 +348,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
     float nw[VPT];
     load_norm_weights<VPT>(P, nw);
     if (P.G == 1) {
-        const float den = merge_gate1<VPT>(P, wsh, seq, i, tok0, 0, n_cand, acc);
+        const float den = merge_gate1<VPT, PK>(P, wsh, seq, i, tok0, 0, n_cand, acc);
 #pragma unroll
         for (int v = 0; v < VPT; v++) acc[v] = acc[v] / den;
     } else {
@@ -357,7 +385,7 @@ __device__ __forceinline__ void compress_entry(const CompressParams &P, float *w
 // in LDS (red: kEntryWaves x D floats) and wavefront 0 adds them in wavefront order, divides by
 // the weight sum and finishes the entry.  wsh: kEntryWaves x kMaxCand floats.  Every thread of
 // the workgroup must call it.
-template <int VPT>
+template <int VPT, bool PK = false>
 __device__ __forceinline__ void compress_entry_wg(const CompressParams &P, float *wsh, float *red, int64_t seq,
                                                   int64_t i, int64_t tok0) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -371,7 +399,7 @@ __device__ __forceinline__ void compress_entry_wg(const CompressParams &P, float
     for (int v = 0; v < VPT; v++) acc[v] = 0.0f;
     float nw[VPT];
     if (wv == 0) load_norm_weights<VPT>(P, nw);
-    const float den = merge_gate1<VPT>(P, wsh + wv * kMaxCand, seq, i, tok0, c0, c1, acc);
+    const float den = merge_gate1<VPT, PK>(P, wsh + wv * kMaxCand, seq, i, tok0, c0, c1, acc);
     if (active) {
 #pragma unroll
         for (int v = 0; v < VPT; v++) red[wv * P.D + d0 + v] = acc[v];
