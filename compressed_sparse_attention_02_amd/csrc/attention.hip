@@ -281,12 +281,12 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
             const uint8_t *src = !ok ? g_zero_row
                                      : (lane_rope ? kbase_r + (uint64_t)(uint32_t)e * (2 * R) + (16 * lane - Dn)
                                                   : kbase_n + (uint64_t)(uint32_t)e * Dn + 16 * lane);
-            if (lane < RB8 / 16) __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][r * RS8], 16, 0, 0);
+            if (lane < RB8 / 16) lds_copy16(src, lds_addr(&TB[q][r * RS8]));
         }
         if (wv == NW - 1 && lane < kTile) {
             const bool ok = my_e >= 0 && my_e < cap32;
             const float *src = ok ? P.kscale + krow0 + my_e : (const float *)g_zero_row;
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&ksc[q][0], 4, 0, 0);
+            lds_copy4(src, lds_addr(&ksc[q][0]));
             kval[q][lane] = ok ? 1 : 0;
         }
     };
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
         for (int r = wvu; r < kTile; r += NW) {
             const bool ok = tb + r < kb1;
             const uint8_t *src = ok ? (const uint8_t *)P.win + wr.row(tb + r - n_ent) * (2 * D) + 16 * lane : g_zero_row;
-            if (lane < 2 * D / 16) __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)&TB[q][r * 2 * RS16], 16, 0, 0);
+            if (lane < 2 * D / 16) lds_copy16(src, lds_addr(&TB[q][r * 2 * RS16]));
         }
         // a window tile's scales (1) and validity (key < kb1) are derived where they are used
     };

@@ -23,6 +23,27 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// Direct-to-LDS copies (global_load_lds), written out as instructions: lane l's 16 (or 4)
+// bytes from gsrc land at LDS byte lds + 16 l (or 4 l); lds is uniform over the wavefront.
+// The compiler does not see these as LDS writes, so its conservative rule (wait for every
+// direct-to-LDS copy in flight before any LDS access) does not drain a prefetched buffer; the
+// caller waits for the copies with an explicit s_waitcnt vmcnt before the buffer is read, and
+// orders the copies after the reads of the buffer they overwrite (barrier or program order).
+// No VGPR is written by these instructions.
+__device__ __forceinline__ void lds_copy16(const void *gsrc, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy16_nt(const void *gsrc, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void *gsrc, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+// LDS byte address of a shared-memory object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
 // bf16 <-> f32.  Encoding rounds to nearest even on bit 16 (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     uint32_t u = fbits(x);

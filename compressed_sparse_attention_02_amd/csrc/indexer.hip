@@ -27,8 +27,9 @@
 
 namespace v4a {
 
-constexpr int kGroupsPerIter = 4;   // key groups of 16 per load batch (two batches in flight)
-constexpr int kMaxKeysPerWG = 4 * 64 * 16;  // 4 wavefronts x at most 64 groups of 16 keys
+constexpr int kGroupsPerIter = 4;   // key groups of 16 per load batch
+constexpr int kMaxGroupsPerWave = 64;
+constexpr int kStreamMaxKeys = 4096;  // keys per workgroup of the streaming kernel
 struct IndexerParams {
     const uint8_t *kc;   // key codes [B][cap][d/2]
     const uint8_t *ks;   // key scales [B][cap][d/32]
@@ -48,6 +49,7 @@ struct IndexerParams {
     uint32_t *hist;        // [BQ][hist_copies][4096] or NULL
     int hist_copies;
     int groups_per_wave;   // key groups of 16 per wavefront (a multiple of kGroupsPerIter)
+    int stream_kpw;        // streaming kernel: keys per workgroup (a multiple of 64, <= kStreamMaxKeys)
     bool key_rec;          // decode step (one query per sequence, d = 128): the key that the
     CompressParams key;    // query's newest token completes is compressed here (see below)
 };
@@ -77,26 +79,106 @@ __device__ __forceinline__ void lds_barrier() {
 // Adds the workgroup's LDS histogram into copy (blockIdx.x % hist_copies) of the query's
 // global histogram; spreading the copies keeps many workgroups off the same hot bins.  The
 // score stores before it need not have completed.
-__device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint32_t *lhist) {
-    lds_barrier();
+template <int NT>
+__device__ __forceinline__ void flush_hist_nobarrier(const IndexerParams &P, int qi, const uint32_t *lhist) {
     if (!P.hist) return;
     uint32_t *gh = P.hist + ((int64_t)qi * P.hist_copies + (int)(blockIdx.x % (unsigned)P.hist_copies)) * kHistBins;
     // consecutive bins in consecutive lanes, so the few hot bins of a query leave in one wide
     // atomic instruction per cache line; all LDS reads are issued before the first atomic
-    constexpr int kPer = 16;  // bins per thread with 256 threads
-    if (blockDim.x * kPer == kHistBins) {
-        uint32_t c[kPer];
+    static_assert(kHistBins % NT == 0, "whole bins per thread");
+    constexpr int kPer = kHistBins / NT;  // bins per thread
+    uint32_t c[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; i++) c[i] = lhist[threadIdx.x + i * 256];
+    for (int i = 0; i < kPer; i++) c[i] = lhist[threadIdx.x + i * NT];
 #pragma unroll
-        for (int i = 0; i < kPer; i++)
-            if (c[i]) atomicAdd(&gh[threadIdx.x + i * 256], c[i]);
-        return;
+    for (int i = 0; i < kPer; i++)
+        if (c[i]) atomicAdd(&gh[threadIdx.x + i * NT], c[i]);
+}
+
+template <int NT>
+__device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint32_t *lhist) {
+    lds_barrier();
+    flush_hist_nobarrier<NT>(P, qi, lhist);
+}
+
+// A query's MFMA operands: 4 head groups of 16 heads; lane (col, grp) holds head 16g+col's
+// MX block grp and the weights of heads 16g + 4 grp + i.  Heads past H read head H-1 (all loads
+// issued together) and are zeroed: code 0 and weight 0.
+struct QueryOperands {
+    v8i qa[4];
+    int qscale[4];
+    float wt[4][4];
+};
+
+__device__ __forceinline__ QueryOperands load_query(const IndexerParams &P, const QueryPos &QP, int qi, int b, int col,
+                                                    int grp) {
+    QueryOperands o;
+    uint4 qc[4];
+    uint32_t qsb[4];
+    float wr[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        const int h = min(16 * g + col, P.H - 1);
+        const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
+        qc[g] = *(const uint4 *)(P.qc + row * 64 + grp * 16);
+        qsb[g] = P.qs[row * 4 + grp];
+#pragma unroll
+        for (int i = 0; i < 4; i++) wr[g][i] = P.w[(int64_t)qi * P.H + min(16 * g + 4 * grp + i, P.H - 1)];
     }
-    for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
-        uint32_t c = lhist[bin];
-        if (c) atomicAdd(&gh[bin], c);
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        const bool on = 16 * g + col < P.H;
+        o.qa[g] = v8i{on ? (int)qc[g].x : 0, on ? (int)qc[g].y : 0, on ? (int)qc[g].z : 0, on ? (int)qc[g].w : 0,
+                      0, 0, 0, 0};
+        o.qscale[g] = on ? (int)qsb[g] : 127;
+#pragma unroll
+        for (int i = 0; i < 4; i++) o.wt[g][i] = (16 * g + 4 * grp + i < P.H) ? wr[g][i] : 0.0f;
     }
+    return o;
+}
+
+// fma chain grp of key col of a group (codes kdu, the key's four scale bytes kscu)
+__device__ __forceinline__ float key_chain(const QueryOperands &qo, const uint4 &kdu, uint32_t kscu, int grp) {
+    const v8i kb = v8i{(int)kdu.x, (int)kdu.y, (int)kdu.z, (int)kdu.w, 0, 0, 0, 0};
+    const int sc = (int)((kscu >> (8 * grp)) & 0xFFu);
+    v4f acc[4];
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+        acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                                                                  qo.qscale[g], 0, sc);
+    // ReLU on the bit pattern: a finite float is negative (or -0) exactly when its bits read as
+    // a negative int, so max(int bits, 0) gives s for s > 0 and +0 otherwise
+    float cu = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float si = acc[g][i];  // a scalar copy: bit casts read whole objects
+            const float r = __builtin_bit_cast(float, max(__builtin_bit_cast(int, si), 0));
+            cu = fmaf(qo.wt[g][i], r, cu);
+        }
+    }
+    return cu;
+}
+
+// Scores of a batch of four key groups: lane 16 q + col returns the score of key col of group
+// q.  Lane group q holds chain q of key col of every group u; a 4 x 4 transpose across the lane
+// groups (swap the upper half of c0/c1 with the lower half of c2/c3, then the odd rows of those
+// with the even rows) leaves lane group q holding chains 0..3 of key col of group q, so every
+// lane finishes one key with the fixed-order sum.
+static_assert(kGroupsPerIter == 4, "the chain transpose pairs four groups with four lane groups");
+__device__ __forceinline__ float batch_scores(const QueryOperands &qo, const uint4 (&kd)[kGroupsPerIter],
+                                              const uint32_t (&ksc)[kGroupsPerIter], int grp) {
+    uint32_t c[kGroupsPerIter];
+#pragma unroll
+    for (int u = 0; u < kGroupsPerIter; u++) c[u] = fbits(key_chain(qo, kd[u], ksc[u], grp));
+    const auto a02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+    const auto a13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+    const auto t01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+    const auto t23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+    float sc = ((bitsf(t01[0]) + bitsf(t01[1])) + bitsf(t23[0])) + bitsf(t23[1]);
+    if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
+    return sc;
 }
 
 // MXFP4, d = 128 (one 16x16x128 scaled MFMA per 16 heads and 16 keys), H <= 64.
@@ -114,15 +196,17 @@ __device__ __forceinline__ void flush_hist(const IndexerParams &P, int qi, uint3
 // STREAM: the keys are read once per launch (decode: one query per sequence), so they are
 // loaded non-temporally; otherwise (a prefill chunk: every query of the chunk reads the same
 // keys) they are loaded through the caches, which serve the other queries' re-reads.
-template <bool KEYREC, bool STREAM>
-__global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
+template <int NW, int NB, bool KEYREC, bool STREAM>
+__global__ void __launch_bounds__(64 * NW) indexer_mxfp4_kernel(IndexerParams P, QueryPos QP) {
+    constexpr int NT = 64 * NW;
+    static_assert(NB >= 2 && NB <= 4, "load batches in flight");
     __shared__ uint32_t lhist[kHistBins];
-    __shared__ __attribute__((aligned(16))) float sbuf[kMaxKeysPerWG];  // this workgroup's scores
-    __shared__ __attribute__((aligned(16))) uint8_t knew[80];           // the new key's codes + scales
+    __shared__ __attribute__((aligned(16))) float sbuf[NW * kMaxGroupsPerWave * 16];  // this workgroup's scores
+    __shared__ __attribute__((aligned(16))) uint8_t knew[80];  // the new key's codes + scales
     const int qi = blockIdx.y;
     const int b = qi / QP.Q;
     const int64_t n_vis = visible_keys(QP, qi);
-    const int64_t keys_per_wg = (int64_t)4 * P.groups_per_wave * 16;
+    const int64_t keys_per_wg = (int64_t)NW * P.groups_per_wave * 16;
     const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
     if (k0 >= n_vis) return;  // uniform over the workgroup
 
@@ -165,82 +249,23 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
             ksc[u] = *(const uint32_t *)(ks + key * 4u);
         }
     };
-    // the first key batch is requested before the query, so the two latencies overlap
-    uint4 kdA[kGroupsPerIter], kdB[kGroupsPerIter];
-    uint32_t kscA[kGroupsPerIter], kscB[kGroupsPerIter];
-    if (wbase < kend) load_iter(0, kdA, kscA);
-    for (int bin = threadIdx.x; bin < kHistBins; bin += 256) lhist[bin] = 0;
-
-    // query: 4 head groups of 16 heads; lane holds head 16g+col, MX block grp.  Heads past H
-    // read head H-1 (all loads issued together) and are zeroed: code 0 and weight 0.
-    v8i qa[4];
-    int qscale[4];
-    float wt[4][4];  // w of heads 16g + 4*grp + i
-    {
-        uint4 qc[4];
-        uint32_t qsb[4];
-        float wr[4][4];
+    // iterations holding at least one visible key (uniform over the wavefront)
+    const int n_live = wbase >= kend ? 0 : min(n_it, (int)((kend - wbase + kGroupsPerIter * 16 - 1) / (kGroupsPerIter * 16)));
+    // the first NB-1 key batches are requested before the query, so their latencies overlap
+    uint4 kd[NB][kGroupsPerIter];
+    uint32_t ksc[NB][kGroupsPerIter];
+    if (n_live > 0) {
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int h = min(16 * g + col, P.H - 1);
-            const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
-            qc[g] = *(const uint4 *)(P.qc + row * 64 + grp * 16);
-            qsb[g] = P.qs[row * 4 + grp];
-#pragma unroll
-            for (int i = 0; i < 4; i++) wr[g][i] = P.w[(int64_t)qi * P.H + min(16 * g + 4 * grp + i, P.H - 1)];
-        }
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const bool on = 16 * g + col < P.H;
-            qa[g] = v8i{on ? (int)qc[g].x : 0, on ? (int)qc[g].y : 0, on ? (int)qc[g].z : 0, on ? (int)qc[g].w : 0,
-                        0, 0, 0, 0};
-            qscale[g] = on ? (int)qsb[g] : 127;
-#pragma unroll
-            for (int i = 0; i < 4; i++) wt[g][i] = (16 * g + 4 * grp + i < P.H) ? wr[g][i] : 0.0f;
-        }
+        for (int j = 0; j < NB - 1; j++) load_iter(min(j, n_live - 1), kd[j], ksc[j]);
     }
+    for (int bin = threadIdx.x; bin < kHistBins; bin += NT) lhist[bin] = 0;
+
+    const QueryOperands qo = load_query(P, QP, qi, b, col, grp);
     __syncthreads();
 
-    // fma chain grp of key col of a group (codes kdu, the key's four scale bytes kscu)
-    auto key_chain = [&](const uint4 &kdu, uint32_t kscu) -> float {
-        const v8i kb = v8i{(int)kdu.x, (int)kdu.y, (int)kdu.z, (int)kdu.w, 0, 0, 0, 0};
-        const int sc = (int)((kscu >> (8 * grp)) & 0xFFu);
-        v4f acc[4];
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-            acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
-                                                                      qscale[g], 0, sc);
-        // ReLU on the bit pattern: a finite float is negative (or -0) exactly when its bits
-        // read as a negative int, so max(int bits, 0) gives s for s > 0 and +0 otherwise
-        float cu = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float si = acc[g][i];  // a scalar copy: bit casts read whole objects
-                const float r = __builtin_bit_cast(float, max(__builtin_bit_cast(int, si), 0));
-                cu = fmaf(wt[g][i], r, cu);
-            }
-        }
-        return cu;
-    };
-    static_assert(kGroupsPerIter == 4, "the chain transpose below pairs four groups with four lane groups");
     auto compute_iter = [&](int it, const uint4 (&kd)[kGroupsPerIter], const uint32_t (&ksc)[kGroupsPerIter]) {
         const int64_t base = wbase + (int64_t)it * kGroupsPerIter * 16;
-        uint32_t c[kGroupsPerIter];
-#pragma unroll
-        for (int u = 0; u < kGroupsPerIter; u++) c[u] = fbits(key_chain(kd[u], ksc[u]));
-        // Lane group q holds chain q of key col of every group u.  A 4 x 4 transpose across the
-        // lane groups (swap the upper half of c0/c1 with the lower half of c2/c3, then the odd
-        // rows of those with the even rows) leaves lane group q holding chains 0..3 of key col of
-        // group q, so every lane finishes one key with the fixed-order sum.
-        const auto a02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
-        const auto a13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
-        const auto t01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
-        const auto t23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
-        float sc = ((bitsf(t01[0]) + bitsf(t01[1])) + bitsf(t23[0])) + bitsf(t23[1]);
-        if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
-        sbuf[base - k0 + 16 * grp + col] = sc;  // slots past kend are never read
+        sbuf[base - k0 + 16 * grp + col] = batch_scores(qo, kd, ksc, grp);  // slots past kend are never read
     };
     // the new key: merged, encoded (into LDS) and scored right after the first iteration, while
     // the rest of the stream is in flight; its score replaces the stale one after the stream
@@ -251,21 +276,24 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // every key column of the group holds the new key; the chains meet as in compute_iter
-        const float c = key_chain(*(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64));
+        const float c = key_chain(qo, *(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64), grp);
         float sc = ((lane_value(c, 0) + lane_value(c, 16)) + lane_value(c, 32)) + lane_value(c, 48);
         if (sc == 0.0f) sc = 0.0f;  // -0 -> +0
         sc_new = sc;
     };
-    for (int it = 0; it < n_it; it += 2) {
-        if (wbase + (int64_t)it * kGroupsPerIter * 16 >= kend) break;  // uniform over the wavefront
-        const bool more1 = it + 1 < n_it && wbase + (int64_t)(it + 1) * kGroupsPerIter * 16 < kend;
-        if (more1) load_iter(it + 1, kdB, kscB);
-        compute_iter(it, kdA, kscA);
-        if (own && it == 0) new_key();
-        if (!more1) break;
-        const bool more2 = it + 2 < n_it && wbase + (int64_t)(it + 2) * kGroupsPerIter * 16 < kend;
-        if (more2) load_iter(it + 2, kdA, kscA);
-        compute_iter(it + 1, kdB, kscB);
+    // A ring of NB load batches: batch it + NB - 1 is requested before batch it is computed.
+    // Past the wavefront's last iteration the request repeats that iteration (valid addresses,
+    // never computed), so every iteration issues the same loads and each wait leaves the later
+    // batches in flight.
+    for (int it0 = 0; it0 < n_live; it0 += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const int it = it0 + j;
+            if (it >= n_live) break;  // uniform over the wavefront
+            load_iter(min(it + NB - 1, n_live - 1), kd[(j + NB - 1) % NB], ksc[(j + NB - 1) % NB]);
+            compute_iter(it, kd[j], ksc[j]);
+            if (own && it == 0) new_key();
+        }
     }
     if (own) {
         if (lane == 0) sbuf[i_new - k0] = sc_new;
@@ -284,7 +312,7 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
     uint16_t *g_key16 = P.score_keys && P.key16 ? (uint16_t *)P.score_keys + (int64_t)qi * P.key_stride + k0 : nullptr;
     const int hshift = P.key16 ? 4 : 20;  // the top 12 bits of either key
     const bool sc_aligned = ((k0 + (int64_t)qi * P.n_max) & 3) == 0;
-    for (int i0 = 4 * threadIdx.x; i0 < n_here; i0 += 4 * 256) {
+    for (int i0 = 4 * threadIdx.x; i0 < n_here; i0 += 4 * NT) {
         const float4 v = *(const float4 *)(sbuf + i0);
         const float vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t kk[4];
@@ -325,7 +353,234 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerParams P, Que
                 if (i0 + j < n_here) atomicAdd(&lhist[kk[j] >> hshift], 1u);
         }
     }
-    flush_hist(P, qi, lhist);
+    flush_hist<NT>(P, qi, lhist);
+}
+
+// Streaming form of the MXFP4 kernel for a long decode scan (one query per sequence, d = 128,
+// H <= 64): one workgroup of kStreamWaves wavefronts per CU owns kpw consecutive keys of one
+// query, cut into batches of 64 keys (four groups of 16).
+//  - Wavefronts claim batches from an LDS counter (each claim is made one batch before its
+//    loads, so its latency hides behind the arithmetic) and keep two batches in flight: a
+//    batch's key codes and scales are copied straight into the wavefront's LDS stage by
+//    direct-to-LDS loads, so no register waits on them and the only wait is for the older
+//    stage.  A wavefront keeps claiming until the workgroup's keys run out, whichever
+//    wavefronts the hardware favours.
+//  - Each lane ends a batch holding one key's score: its orderable key leaves at once (one
+//    256-byte store per batch) and is counted in the LDS histogram, so nothing remains to do
+//    after the stream but the histogram flush.
+//  - key_rec: wavefront 0 of the workgroup holding the query's new entry requests the entry's
+//    candidate rows before the stream and, after its last batch, merges, encodes and scores
+//    the new key with the same arithmetic; the batch holding that entry leaves its slot to it.
+// Scores, keys and histogram are bitwise those of indexer_mxfp4_kernel.
+constexpr int kStreamWaves = 8;   // wavefronts per workgroup
+constexpr int kStreamStages = 3;  // key batches in flight per wavefront (LDS stages of 5 KB)
+
+template <bool KEYREC>
+__global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel(IndexerParams P, QueryPos QP) {
+    constexpr int NW = kStreamWaves;
+    constexpr int kBatch = kGroupsPerIter * 16;  // keys per batch
+    __shared__ uint32_t lhist[kHistBins];
+    __shared__ uint32_t next_batch;
+    __shared__ __attribute__((aligned(16))) uint8_t knew[80];
+    __shared__ __attribute__((aligned(16))) uint8_t qcodes[4][1024];  // head group g: lane l's 16 code bytes
+    __shared__ __attribute__((aligned(16))) uint32_t qscl[4][64];      // head group g: lane l's head's scale word
+    __shared__ __attribute__((aligned(16))) float qw[64];              // w of head h (h < H; H - 1 past it)
+    // load stages: kStreamStages per wavefront, used round robin
+    __shared__ __attribute__((aligned(16))) uint8_t codes[kStreamStages][NW][kGroupsPerIter * 1024];
+    __shared__ __attribute__((aligned(16))) uint32_t scl[kStreamStages][NW][kGroupsPerIter * 64];
+    const int qi = blockIdx.y;
+    const int b = qi / QP.Q;
+    const int64_t n_vis = visible_keys(QP, qi);
+    const int64_t k0 = (int64_t)blockIdx.x * P.stream_kpw;
+    if (k0 >= n_vis) return;  // uniform over the workgroup
+    const int64_t kend = k0 + P.stream_kpw < n_vis ? k0 + P.stream_kpw : n_vis;
+    const int n_batches = (int)((kend - k0 + kBatch - 1) / kBatch);
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const uint8_t *kc = P.kc + (int64_t)b * P.kcap * 64;
+    const uint8_t *ks = P.ks + (int64_t)b * P.kcap * 4;
+    const uint32_t key_last = (uint32_t)(kend - 1);
+
+    int64_t i_new = -1;
+    if (KEYREC) {
+        const int64_t pos = QP.pos[qi];
+        if ((pos + 1) % P.key.m == 0) i_new = (pos + 1) / P.key.m - 1;
+        if (i_new < k0 || i_new >= kend) i_new = -1;  // not this workgroup's
+    }
+    const bool own = KEYREC && wv == 0 && i_new >= 0;  // uniform over the wavefront
+    KeyPrefetch<2> kp;
+    if (own) key_prefetch<2>(P.key, qi, i_new, (int64_t)P.key.m * (i_new - 1), kp);
+
+    // batch bt into a stage: group u is keys k0 + 64 bt + 16 u + (0..15); lane l copies its 16
+    // code bytes (MX block grp of key col) to byte 1024 u + 16 l and its key's scale word to
+    // word 64 u + l.  Lanes past the end read a clamped, valid key of this query, masked later.
+    auto load_batch = [&](int bt, uint8_t *cst, uint32_t *sst) {
+        const uint32_t kb0 = (uint32_t)k0 + (uint32_t)(bt * kBatch + col);
+#pragma unroll
+        for (int u = 0; u < kGroupsPerIter; u++) {
+            const uint32_t key = min(kb0 + (uint32_t)(16 * u), key_last);
+            lds_copy16_nt(kc + (key * 64u + (uint32_t)grp * 16u), lds_addr(cst + 1024 * u));
+            lds_copy4(ks + key * 4u, lds_addr(sst + 64 * u));
+        }
+    };
+    // The stream's LDS instructions are written out too (the compiler, which cannot tell the
+    // stages' copies apart, would otherwise wait for every copy in flight before each LDS
+    // access); the explicit vmcnt wait before a stage is read covers that stage's copies.
+    auto stage_scores = [&](const uint8_t *cst, const uint32_t *sst, const QueryOperands &qo) {
+        u32x4 c0, c1, c2, c3;
+        uint32_t s0, s1, s2, s3;
+        const uint32_t ca = lds_addr(cst) + 16u * (uint32_t)lane;
+        const uint32_t sa = lds_addr(sst) + 4u * (uint32_t)lane;
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:1024\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:3072\n\t"
+            "ds_read_b32 %4, %9\n\t"
+            "ds_read_b32 %5, %9 offset:256\n\t"
+            "ds_read_b32 %6, %9 offset:512\n\t"
+            "ds_read_b32 %7, %9 offset:768\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c0), "=&v"(c1), "=&v"(c2), "=&v"(c3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+            : "v"(ca), "v"(sa)
+            : "memory");
+        const uint4 kd[kGroupsPerIter] = {make_uint4(c0.x, c0.y, c0.z, c0.w), make_uint4(c1.x, c1.y, c1.z, c1.w),
+                                          make_uint4(c2.x, c2.y, c2.z, c2.w), make_uint4(c3.x, c3.y, c3.z, c3.w)};
+        const uint32_t ksc[kGroupsPerIter] = {s0, s1, s2, s3};
+        return batch_scores(qo, kd, ksc, grp);
+    };
+    uint32_t *g_key = P.score_keys && !P.key16 ? (uint32_t *)P.score_keys + (int64_t)qi * P.key_stride : nullptr;
+    uint16_t *g_key16 = P.score_keys && P.key16 ? (uint16_t *)P.score_keys + (int64_t)qi * P.key_stride : nullptr;
+    float *g_sc = P.scores ? P.scores + (int64_t)qi * P.n_max : nullptr;
+    const int hshift = P.key16 ? 4 : 20;  // the top 12 bits of either key
+    const uint32_t hist_base = lds_addr(lhist);
+    // batch bt's scores leave: one key per lane (the new entry's slot is left to its owner)
+    auto emit = [&](int bt, float sc) {
+        const int64_t i = k0 + (int64_t)bt * kBatch + lane;
+        if (i < kend && i != i_new) {
+            const uint32_t key = P.key16 ? score_key16(sc) : score_key(sc);
+            if (g_key) g_key[i] = key;
+            if (g_key16) g_key16[i] = (uint16_t)key;
+            if (g_sc) g_sc[i] = sc;
+            if (P.hist) asm volatile("ds_add_u32 %0, %1" ::"v"(hist_base + 4u * (key >> hshift)), "v"(1u) : "memory");
+        }
+    };
+
+    // Wavefront 0 copies the query (codes, scales, weights) to LDS before its first batches and
+    // waits only for those copies; every wavefront then reads its operands from LDS, so no
+    // register of the stream waits on a global load the compiler would drain the copies for.
+    for (int bin = threadIdx.x; bin < kHistBins; bin += 64 * NW) lhist[bin] = 0;
+    if (threadIdx.x == 0) next_batch = kStreamStages * NW;
+    if (wv == 0) {
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int h = min(16 * g + col, P.H - 1);
+            const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
+            lds_copy16(P.qc + row * 64 + grp * 16, lds_addr(qcodes[g]));
+            lds_copy4(P.qs + row * 4, lds_addr(qscl[g]));
+        }
+        lds_copy4(P.w + (int64_t)qi * P.H + min(lane, P.H - 1), lds_addr(qw));
+    }
+    // the first kStreamStages batches of every wavefront are fixed (batch j NW + wv for stage j);
+    // the rest are claimed
+    int bq[kStreamStages];  // the batches in stages st, st + 1, ... (mod kStreamStages)
+#pragma unroll
+    for (int j = 0; j < kStreamStages; j++) {
+        bq[j] = j * NW + wv;
+        load_batch(min(bq[j], n_batches - 1), codes[j][wv], scl[j][wv]);
+    }
+    if (wv == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * kStreamStages) : "memory");
+    lds_barrier();
+    QueryOperands qo;
+    {
+        u32x4 c[4], w4[4];
+        uint32_t sc[4];
+        const uint32_t ca = lds_addr(qcodes) + 16u * (uint32_t)lane, sa = lds_addr(qscl) + 4u * (uint32_t)lane;
+        const uint32_t wa = lds_addr(qw) + 16u * (uint32_t)grp;
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:1024\n\t"
+            "ds_read_b128 %2, %12 offset:2048\n\t"
+            "ds_read_b128 %3, %12 offset:3072\n\t"
+            "ds_read_b32 %4, %13\n\t"
+            "ds_read_b32 %5, %13 offset:256\n\t"
+            "ds_read_b32 %6, %13 offset:512\n\t"
+            "ds_read_b32 %7, %13 offset:768\n\t"
+            "ds_read_b128 %8, %14\n\t"
+            "ds_read_b128 %9, %14 offset:64\n\t"
+            "ds_read_b128 %10, %14 offset:128\n\t"
+            "ds_read_b128 %11, %14 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]),
+              "=&v"(sc[3]), "=&v"(w4[0]), "=&v"(w4[1]), "=&v"(w4[2]), "=&v"(w4[3])
+            : "v"(ca), "v"(sa), "v"(wa)
+            : "memory");
+        // as load_query: heads past H get code 0, scale 127 and weight 0
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const bool on = 16 * g + col < P.H;
+            qo.qa[g] = v8i{on ? (int)c[g].x : 0, on ? (int)c[g].y : 0, on ? (int)c[g].z : 0, on ? (int)c[g].w : 0,
+                           0, 0, 0, 0};
+            qo.qscale[g] = on ? (int)((sc[g] >> (8 * grp)) & 0xFFu) : 127;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t wb = w4[g][i];  // a scalar copy: bit casts read whole objects
+                qo.wt[g][i] = (16 * g + 4 * grp + i < P.H) ? __builtin_bit_cast(float, wb) : 0.0f;
+            }
+        }
+    }
+
+    const uint32_t nb_addr = lds_addr(&next_batch);
+    // a claim: lane 0 adds one to the batch counter; the old value, read later by the whole
+    // wavefront, is the claimed batch
+    auto claim_next = [&]() {
+        uint32_t c = 0;
+        if (lane == 0)
+            asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(c) : "v"(nb_addr), "v"(1u)
+                         : "memory");
+        return c;
+    };
+    uint32_t claim = claim_next();
+    // Every step refills the stage it has read (a finished wavefront repeats the last batch:
+    // valid addresses, never computed), so each wait leaves exactly the other stages' copies in
+    // flight: at most (kStreamStages - 1) x 8 newer loads (the key stores in between may still
+    // travel; loads complete in order, so these counts leave the stage read complete).
+    for (int st = 0;;) {
+        if (bq[0] >= n_batches) break;  // uniform over the wavefront
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * (kStreamStages - 1)) : "memory");
+        emit(bq[0], stage_scores(codes[st][wv], scl[st][wv], qo));
+        const int nb = __builtin_amdgcn_readfirstlane(claim);
+        load_batch(min(nb, n_batches - 1), codes[st][wv], scl[st][wv]);
+        claim = claim_next();
+#pragma unroll
+        for (int j = 0; j + 1 < kStreamStages; j++) bq[j] = bq[j + 1];
+        bq[kStreamStages - 1] = nb;
+        st = st + 1 == kStreamStages ? 0 : st + 1;
+    }
+    if (own) {
+        // the new key: merged, encoded (into LDS), scored as the stream's keys are, counted and
+        // stored; then its cache row (64 code bytes, 4 scale bytes) from the LDS copy
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        key_finish<2>(P.key, kp, qi, i_new, knew, false);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float c = key_chain(qo, *(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64), grp);
+        float sn = ((lane_value(c, 0) + lane_value(c, 16)) + lane_value(c, 32)) + lane_value(c, 48);
+        if (sn == 0.0f) sn = 0.0f;  // -0 -> +0
+        if (lane == 0) {
+            const uint32_t key = P.key16 ? score_key16(sn) : score_key(sn);
+            if (g_key) g_key[i_new] = key;
+            if (g_key16) g_key16[i_new] = (uint16_t)key;
+            if (g_sc) g_sc[i_new] = sn;
+            if (P.hist) atomicAdd(&lhist[key >> hshift], 1u);
+        }
+        const int64_t row = P.key.out_row0 + (int64_t)qi * P.key.cap + i_new;
+        if (lane < 16) ((uint32_t *)((uint8_t *)P.key.idx.codes + row * 64))[lane] = ((const uint32_t *)knew)[lane];
+        if (lane == 16) *(uint32_t *)(P.key.idx.scales + row * 4) = *(const uint32_t *)(knew + 64);
+    }
+    lds_barrier();
+    flush_hist_nobarrier<64 * NW>(P, qi, lhist);
 }
 
 // fp32 keys and queries: one thread per key; per head an fma chain over ascending dims.
@@ -352,7 +607,7 @@ __global__ void __launch_bounds__(256) indexer_f32_kernel(IndexerParams P, Query
         }
         emit_score(P, qi, i, ((c[0] + c[1]) + c[2]) + c[3], P.hist ? lhist : nullptr);
     }
-    flush_hist(P, qi, lhist);
+    flush_hist<256>(P, qi, lhist);
 }
 
 // Scores of invisible positions (for the scores-only entry point).
@@ -377,6 +632,14 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
     V4A_LAUNCH("zero_kernel", zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16);
     return hipGetLastError();
 }
+
+// Launch shape of the MXFP4 scoring kernel.
+constexpr int kScoreWaves = 4;      // wavefronts per workgroup
+constexpr int kScoreBatches = 2;    // key load batches in flight per wavefront
+constexpr int kScoreMinWGs = 1024;  // keys per workgroup grow while the grid keeps this many
+// Launch shape of the streaming kernel (one query per sequence, at least kStreamMinKeys keys).
+constexpr int kStreamWGs = 256;     // workgroups aimed at (one per CU)
+constexpr int64_t kStreamMinKeys = (int64_t)kStreamWGs * 1024;
 
 hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t s) {
     IndexerParams P{};
@@ -409,22 +672,38 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     }
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
-    if (mx) {
-        // keys per workgroup: doubled from 512 while the grid keeps at least 1024 workgroups, so
-        // a large scan runs as 512-1024 workgroups (two to four per CU) of up to 4096 keys; it
-        // changes only the work split, never a result.  (At the 1M-context decode, 2048-key
-        // workgroups, two per CU, measured 20-21 us on every device tried; 1024-key ones 19-24.)
-        int gpw = 2 * kGroupsPerIter;  // keys per workgroup = 4 wavefronts * gpw groups * 16 keys
-        while (gpw < 64 && (int64_t)BQ * ((a.n_max + 64 * gpw - 1) / (64 * gpw)) >= 1024) gpw *= 2;
-        P.groups_per_wave = gpw;
-        const int64_t kpw = (int64_t)64 * gpw;
+    if (mx && a.Q == 1 && (int64_t)BQ * a.n_max >= kStreamMinKeys) {
+        // a long decode scan: one streaming workgroup per CU; keys per workgroup the largest of
+        // 1024, 2048, 4096 that still gives kStreamWGs workgroups
+        int kpw = kStreamMaxKeys;
+        while (kpw > 1024 && (int64_t)BQ * ((a.n_max + kpw - 1) / kpw) < kStreamWGs) kpw /= 2;
+        P.stream_kpw = kpw;
         dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
         if (P.key_rec)
-            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<true, true>), grid, dim3(256), 0, s, P, qp);
-        else if (a.Q == 1)
-            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<false, true>), grid, dim3(256), 0, s, P, qp);
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<true>), grid, dim3(64 * kStreamWaves), 0,
+                       s, P, qp);
         else
-            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<false, false>), grid, dim3(256), 0, s, P, qp);
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<false>), grid, dim3(64 * kStreamWaves), 0,
+                       s, P, qp);
+    } else if (mx) {
+        // keys per wavefront: doubled from 128 while the grid keeps at least kScoreMinWGs
+        // workgroups; it changes only the work split, never a result
+        constexpr int NW = kScoreWaves;
+        int gpw = 2 * kGroupsPerIter;
+        while (gpw < kMaxGroupsPerWave && (int64_t)BQ * ((a.n_max + 16 * NW * gpw - 1) / (16 * NW * gpw)) >= kScoreMinWGs)
+            gpw *= 2;
+        P.groups_per_wave = gpw;
+        const int64_t kpw = (int64_t)16 * NW * gpw;
+        dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
+        if (P.key_rec)
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<NW, kScoreBatches, true, true>), grid, dim3(64 * NW), 0,
+                       s, P, qp);
+        else if (a.Q == 1)
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<NW, kScoreBatches, false, true>), grid, dim3(64 * NW),
+                       0, s, P, qp);
+        else
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_kernel<NW, kScoreBatches, false, false>), grid,
+                       dim3(64 * NW), 0, s, P, qp);
     } else {
         dim3 grid((unsigned)((a.n_max + 255) / 256), (unsigned)BQ);
         V4A_LAUNCH("indexer_f32_kernel", indexer_f32_kernel, grid, dim3(256), 0, s, P, qp);

@@ -152,12 +152,10 @@ __device__ __forceinline__ void tiled_chunk(const uint16_t *__restrict__ cur, ui
     if (issue) {
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(wsrc[i] + k_next),
-                                             (gemm_lds_ptr_t)(next + (64 * wv_u + 8 * i) * kTK), 16, 0, 0);
+            lds_copy16(wsrc[i] + k_next, lds_addr(next + (64 * wv_u + 8 * i) * kTK));
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(asrc[i] + k_next),
-                                             (gemm_lds_ptr_t)(next + kStageW + (32 * wv_u + 8 * i) * kTK), 16, 0, 0);
+            lds_copy16(asrc[i] + k_next, lds_addr(next + kStageW + (32 * wv_u + 8 * i) * kTK));
     }
     const uint16_t *__restrict__ sa = cur + kStageW;
 #pragma unroll
@@ -228,12 +226,10 @@ __global__ void __launch_bounds__(256, 1) gemm_tiled_kernel(GemmParams P, TiledM
     for (int c = 0; c < 2 && c < nch; c++) {
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(wsrc[i] + c * kTK),
-                                             (gemm_lds_ptr_t)(smem + c * kStage + (64 * wv_u + 8 * i) * kTK), 16, 0, 0);
+            lds_copy16(wsrc[i] + c * kTK, lds_addr(smem + c * kStage + (64 * wv_u + 8 * i) * kTK));
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)(asrc[i] + c * kTK),
-                                             (gemm_lds_ptr_t)(smem + c * kStage + kStageW + (32 * wv_u + 8 * i) * kTK), 16, 0, 0);
+            lds_copy16(asrc[i] + c * kTK, lds_addr(smem + c * kStage + kStageW + (32 * wv_u + 8 * i) * kTK));
     }
     for (int c = 0; c < nch; c++) {
         // this wavefront's loads of chunk c have landed (chunk c+1's may still travel); after the
@@ -321,7 +317,7 @@ __global__ void __launch_bounds__(256) gemm_gemv_kernel(GemmParams P) {
         uint8_t *next = base + ((c + 2) % 3) * kGvStage;
 #pragma unroll
         for (int i = 0; i < kGvLoads; i++)
-            __builtin_amdgcn_global_load_lds((gemm_glb_ptr_t)src[i], (gemm_lds_ptr_t)(next + 4 * i * kGvRow), 16, 0, 0);
+            lds_copy16(src[i], lds_addr(next + 4 * i * kGvRow));
         if (c + 3 < nch) {  // uniform
 #pragma unroll
             for (int i = 0; i < kGvLoads; i++) src[i] += kGvK;
