@@ -78,6 +78,49 @@ def test_scores_mxfp4_bit_exact():
         assert np.all(got[b, n_vis:] == -np.inf)
 
 
+def test_scores_mxfp4_streaming_ragged():
+    """A long one-query-per-sequence scan (the streaming scoring kernel: B * n_max >= 256K keys)
+    with ragged visible counts that are not multiples of a 64-key batch and one sequence too
+    short to reach most workgroups' ranges: every visible score bit-exact, -inf past it."""
+    B, N, H = 3, 150000, 64
+    keys = normal(105, "keys", (B, N, 128))
+    q = normal(105, "q_idx", (B, H, 128))
+    w = normal(105, "w", (B, 1, H))
+    n_entries = [100003, N, 70001]
+    q_pos = [4 * 100003 - 1, 4 * 149985 + 2, 4 * 1000 + 1]  # visible 100003, 149985, 1000
+    announce("indexer scores MXFP4 streaming, ragged B=3 N=150000")
+    ki, qi = idx_from_f32(keys), idx_from_f32(q)
+    out = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    v4.v4a_indexer_scores(ki, n_entries, 4, qi, f32(w), B, 1, H, q_pos, N, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        kc, ks = oracle.quant_mxfp4(keys[b, :n_entries[b]])
+        qc, qs = oracle.quant_mxfp4(q[b])
+        n_vis = oracle.visible_entries(n_entries[b], 4, q_pos[b])
+        ref, bad = oracle.indexer_scores_mxfp4(qc, qs, w[b, 0], kc, ks, n_vis)
+        assert bad == 0
+        assert np.array_equal(got[b, :n_vis].view(np.uint32), ref.view(np.uint32)), b
+        assert np.all(got[b, n_vis:] == -np.inf)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32_scores", "bf16_scores"])
+def test_topk_streaming_ragged(bf16):
+    """The top-k call over the same ragged long scan (streaming scoring kernel, then the
+    selection), bit-exact against the oracle for every sequence."""
+    B, N, H, k = 3, 150000, 64, 1024
+    keys = normal(106, "keys", (B, N, 128))
+    q = normal(106, "q_idx", (B, H, 128))
+    w = normal(106, "w", (B, 1, H))
+    n_entries = np.array([100003, N, 70001])
+    q_pos = [4 * 100003 - 1, 4 * 149985 + 2, 4 * 1000 + 1]
+    announce(f"topk streaming, ragged B=3 N=150000 bf16={bf16}")
+    got, _, _ = run_topk(keys, q, w, n_entries, q_pos, k, bf16=bf16)
+    ref = oracle_topk(keys, q, w, n_entries, q_pos, k, bf16=bf16)
+    for b in range(B):
+        assert np.array_equal(got[b, 0], ref[b, 0]), (b, np.setdiff1d(got[b, 0], ref[b, 0])[:10])
+
+
 def test_scores_f32_bit_exact():
     w_ = TINY
     N = w_.n_csa
