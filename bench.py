@@ -6,24 +6,24 @@
 
 A step is one CSA decode step of the 1M-context workload (4 sequences at position
 1,048,575, 262,144 compressed entries each, 128 query heads, head dim 512, 64 MXFP4
-indexer heads, top-1024, 128-token window, sink):
-  1. compress the block each sequence's newest token completes into its entry record and
-     its MXFP4 indexer key (two batched compressor launches; the record, read only by
-     attention, is compressed on a second stream while the indexer runs);
-  2. score every entry with the lightning indexer and select the top-1024;
+indexer heads, top-1024, 128-token window, sink), as one v4a_decode_step_csa call on one
+stream (five launches):
+  1. score every entry with the lightning indexer (the kernel also compresses the indexer key
+     of the block each sequence's newest token completes);
+  2. select the top-1024 (threshold scan, then the final selection, whose extra workgroups
+     compress the new entry records and clear the histograms for the next call);
   3. attend over the selected entries plus the window with the sink, then combine the splits.
 Inputs are seeded synthetic data (N(0,1) before quantisation).  Every input set is cloned
 R times in HBM and step i uses set i mod R, so the 256 MB Infinity Cache cannot hold the
-working set; the inputs are resident in HBM when timing starts.  The timed step is one
-v4a_decode_step_csa call, launched directly on one stream.
+working set; the inputs are resident in HBM when timing starts.
 
 One JSON line is printed: throughput (tokens/s = sequences decoded per second), the roofline
-of the dominant launch (the indexer + top-k call, whose MXFP4 scoring kernel streams the
-keys), timed live with HIP events on the stream the kernels run on in a second timed loop of
-the same step composed of the separate entry points (the fused call offers no boundary to
-place events at), the oracle timed on the host cores, a parity check of set 0 against the
-oracle, and secondary figures: the 1M-context HCA decode step and one 4096-token prefill
-chunk per layer kind.
+of the dominant launch (the MXFP4 scoring kernel, timed live with HIP events the library
+records around each of its launches on the step's stream in a second loop of the same
+steps), the step composed of the separate entry points for comparison, the oracle timed on
+the host cores, a parity check of set 0 against the oracle, and secondary figures: the
+1M-context HCA decode step, one 4096-token prefill chunk per layer kind, the 131K CSA decode
+step, the standalone compressors and the grouped output projection.
 
 --copy-probe first runs a plain device copy (an elementwise negation of 1 GiB) five times, so
 that a hardware-counter run of this command can scale FETCH_SIZE / WRITE_SIZE by what the
