@@ -375,22 +375,31 @@ __global__ void __launch_bounds__(64 * NW) indexer_mxfp4_kernel(IndexerParams P,
 constexpr int kStreamWaves = 8;   // wavefronts per workgroup
 constexpr int kStreamStages = 3;  // key batches in flight per wavefront (LDS stages of 5 KB)
 
-template <bool KEYREC>
+template <int QT, bool KEYREC>
 __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel(IndexerParams P, QueryPos QP) {
     constexpr int NW = kStreamWaves;
+    constexpr int NST = QT == 1 ? kStreamStages : 2;  // stages per wavefront (LDS holds QT histograms)
     constexpr int kBatch = kGroupsPerIter * 16;  // keys per batch
-    __shared__ uint32_t lhist[kHistBins];
+    static_assert(QT == 1 || !KEYREC, "the new key is compressed here for one query per sequence only");
+    __shared__ uint32_t lhist[QT][kHistBins];
     __shared__ uint32_t next_batch;
     __shared__ __attribute__((aligned(16))) uint8_t knew[80];
-    __shared__ __attribute__((aligned(16))) uint8_t qcodes[4][1024];  // head group g: lane l's 16 code bytes
-    __shared__ __attribute__((aligned(16))) uint32_t qscl[4][64];      // head group g: lane l's head's scale word
-    __shared__ __attribute__((aligned(16))) float qw[64];              // w of head h (h < H; H - 1 past it)
-    // load stages: kStreamStages per wavefront, used round robin
-    __shared__ __attribute__((aligned(16))) uint8_t codes[kStreamStages][NW][kGroupsPerIter * 1024];
-    __shared__ __attribute__((aligned(16))) uint32_t scl[kStreamStages][NW][kGroupsPerIter * 64];
-    const int qi = blockIdx.y;
-    const int b = qi / QP.Q;
-    const int64_t n_vis = visible_keys(QP, qi);
+    __shared__ __attribute__((aligned(16))) uint8_t qcodes[QT][4][1024];  // head group g: lane l's 16 code bytes
+    __shared__ __attribute__((aligned(16))) uint32_t qscl[QT][4][64];      // head group g: lane l's head's scale word
+    __shared__ __attribute__((aligned(16))) float qw[QT][64];              // w of head h (h < H; H - 1 past it)
+    // load stages: NST per wavefront, used round robin
+    __shared__ __attribute__((aligned(16))) uint8_t codes[NST][NW][kGroupsPerIter * 1024];
+    __shared__ __attribute__((aligned(16))) uint32_t scl[NST][NW][kGroupsPerIter * 64];
+    // queries qi0 .. qi0 + QT - 1: one query, or the QT queries (tokens) of one sequence
+    const int qi0 = (int)blockIdx.y * QT;
+    const int b = qi0 / QP.Q;
+    int64_t nv[QT];
+    int64_t n_vis = 0;  // keys this workgroup streams: the most any of its queries sees
+#pragma unroll
+    for (int j = 0; j < QT; j++) {
+        nv[j] = visible_keys(QP, qi0 + j);
+        n_vis = nv[j] > n_vis ? nv[j] : n_vis;
+    }
     const int64_t k0 = (int64_t)blockIdx.x * P.stream_kpw;
     if (k0 >= n_vis) return;  // uniform over the workgroup
     const int64_t kend = k0 + P.stream_kpw < n_vis ? k0 + P.stream_kpw : n_vis;
@@ -401,6 +410,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
     const uint8_t *ks = P.ks + (int64_t)b * P.kcap * 4;
     const uint32_t key_last = (uint32_t)(kend - 1);
 
+    const int qi = qi0;  // (QT == 1)
     int64_t i_new = -1;
     if (KEYREC) {
         const int64_t pos = QP.pos[qi];
@@ -426,7 +436,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
     // The stream's LDS instructions are written out too (the compiler, which cannot tell the
     // stages' copies apart, would otherwise wait for every copy in flight before each LDS
     // access); the explicit vmcnt wait before a stage is read covers that stage's copies.
-    auto stage_scores = [&](const uint8_t *cst, const uint32_t *sst, const QueryOperands &qo) {
+    auto stage_scores = [&](const uint8_t *cst, const uint32_t *sst, const QueryOperands (&qo)[QT], float (&sc)[QT]) {
         u32x4 c0, c1, c2, c3;
         uint32_t s0, s1, s2, s3;
         const uint32_t ca = lds_addr(cst) + 16u * (uint32_t)lane;
@@ -447,56 +457,65 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
         const uint4 kd[kGroupsPerIter] = {make_uint4(c0.x, c0.y, c0.z, c0.w), make_uint4(c1.x, c1.y, c1.z, c1.w),
                                           make_uint4(c2.x, c2.y, c2.z, c2.w), make_uint4(c3.x, c3.y, c3.z, c3.w)};
         const uint32_t ksc[kGroupsPerIter] = {s0, s1, s2, s3};
-        return batch_scores(qo, kd, ksc, grp);
+#pragma unroll
+        for (int j = 0; j < QT; j++) sc[j] = batch_scores(qo[j], kd, ksc, grp);
     };
-    uint32_t *g_key = P.score_keys && !P.key16 ? (uint32_t *)P.score_keys + (int64_t)qi * P.key_stride : nullptr;
-    uint16_t *g_key16 = P.score_keys && P.key16 ? (uint16_t *)P.score_keys + (int64_t)qi * P.key_stride : nullptr;
-    float *g_sc = P.scores ? P.scores + (int64_t)qi * P.n_max : nullptr;
     const int hshift = P.key16 ? 4 : 20;  // the top 12 bits of either key
-    const uint32_t hist_base = lds_addr(lhist);
-    // batch bt's scores leave: one key per lane (the new entry's slot is left to its owner)
-    auto emit = [&](int bt, float sc) {
+    // batch bt's scores leave: one key per lane and query, for the keys that query sees (the new
+    // entry's slot is left to its owner)
+    auto emit = [&](int bt, const float (&sc)[QT]) {
         const int64_t i = k0 + (int64_t)bt * kBatch + lane;
-        if (i < kend && i != i_new) {
-            const uint32_t key = P.key16 ? score_key16(sc) : score_key(sc);
-            if (g_key) g_key[i] = key;
-            if (g_key16) g_key16[i] = (uint16_t)key;
-            if (g_sc) g_sc[i] = sc;
-            if (P.hist) asm volatile("ds_add_u32 %0, %1" ::"v"(hist_base + 4u * (key >> hshift)), "v"(1u) : "memory");
+#pragma unroll
+        for (int j = 0; j < QT; j++) {
+            if (i < kend && i < nv[j] && i != i_new) {
+                const int64_t row = (int64_t)(qi0 + j);
+                const uint32_t key = P.key16 ? score_key16(sc[j]) : score_key(sc[j]);
+                if (P.score_keys && !P.key16) ((uint32_t *)P.score_keys)[row * P.key_stride + i] = key;
+                if (P.score_keys && P.key16) ((uint16_t *)P.score_keys)[row * P.key_stride + i] = (uint16_t)key;
+                if (P.scores) P.scores[row * P.n_max + i] = sc[j];
+                if (P.hist)
+                    asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(lhist[j]) + 4u * (key >> hshift)), "v"(1u) : "memory");
+            }
         }
     };
 
     // Wavefront 0 copies the query (codes, scales, weights) to LDS before its first batches and
     // waits only for those copies; every wavefront then reads its operands from LDS, so no
     // register of the stream waits on a global load the compiler would drain the copies for.
-    for (int bin = threadIdx.x; bin < kHistBins; bin += 64 * NW) lhist[bin] = 0;
-    if (threadIdx.x == 0) next_batch = kStreamStages * NW;
+#pragma unroll
+    for (int j = 0; j < QT; j++)
+        for (int bin = threadIdx.x; bin < kHistBins; bin += 64 * NW) lhist[j][bin] = 0;
+    if (threadIdx.x == 0) next_batch = NST * NW;
     if (wv == 0) {
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int h = min(16 * g + col, P.H - 1);
-            const int64_t row = (int64_t)b * P.qcap + (int64_t)(qi % QP.Q) * P.H + h;
-            lds_copy16(P.qc + row * 64 + grp * 16, lds_addr(qcodes[g]));
-            lds_copy4(P.qs + row * 4, lds_addr(qscl[g]));
-        }
-        lds_copy4(P.w + (int64_t)qi * P.H + min(lane, P.H - 1), lds_addr(qw));
-    }
-    // the first kStreamStages batches of every wavefront are fixed (batch j NW + wv for stage j);
-    // the rest are claimed
-    int bq[kStreamStages];  // the batches in stages st, st + 1, ... (mod kStreamStages)
+        for (int j = 0; j < QT; j++) {
 #pragma unroll
-    for (int j = 0; j < kStreamStages; j++) {
+            for (int g = 0; g < 4; g++) {
+                const int h = min(16 * g + col, P.H - 1);
+                const int64_t row = (int64_t)b * P.qcap + (int64_t)((qi0 + j) % QP.Q) * P.H + h;
+                lds_copy16(P.qc + row * 64 + grp * 16, lds_addr(qcodes[j][g]));
+                lds_copy4(P.qs + row * 4, lds_addr(qscl[j][g]));
+            }
+            lds_copy4(P.w + (int64_t)(qi0 + j) * P.H + min(lane, P.H - 1), lds_addr(qw[j]));
+        }
+    }
+    // the first NST batches of every wavefront are fixed (batch j NW + wv for stage j); the
+    // rest are claimed
+    int bq[NST];  // the batches in stages st, st + 1, ... (mod NST)
+#pragma unroll
+    for (int j = 0; j < NST; j++) {
         bq[j] = j * NW + wv;
         load_batch(min(bq[j], n_batches - 1), codes[j][wv], scl[j][wv]);
     }
-    if (wv == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * kStreamStages) : "memory");
+    if (wv == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * NST) : "memory");
     lds_barrier();
-    QueryOperands qo;
-    {
+    QueryOperands qo[QT];
+#pragma unroll
+    for (int jq = 0; jq < QT; jq++) {
         u32x4 c[4], w4[4];
         uint32_t sc[4];
-        const uint32_t ca = lds_addr(qcodes) + 16u * (uint32_t)lane, sa = lds_addr(qscl) + 4u * (uint32_t)lane;
-        const uint32_t wa = lds_addr(qw) + 16u * (uint32_t)grp;
+        const uint32_t ca = lds_addr(qcodes[jq]) + 16u * (uint32_t)lane, sa = lds_addr(qscl[jq]) + 4u * (uint32_t)lane;
+        const uint32_t wa = lds_addr(qw[jq]) + 16u * (uint32_t)grp;
         asm volatile(
             "ds_read_b128 %0, %12\n\t"
             "ds_read_b128 %1, %12 offset:1024\n\t"
@@ -519,13 +538,13 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const bool on = 16 * g + col < P.H;
-            qo.qa[g] = v8i{on ? (int)c[g].x : 0, on ? (int)c[g].y : 0, on ? (int)c[g].z : 0, on ? (int)c[g].w : 0,
-                           0, 0, 0, 0};
-            qo.qscale[g] = on ? (int)((sc[g] >> (8 * grp)) & 0xFFu) : 127;
+            qo[jq].qa[g] = v8i{on ? (int)c[g].x : 0, on ? (int)c[g].y : 0, on ? (int)c[g].z : 0,
+                               on ? (int)c[g].w : 0, 0, 0, 0, 0};
+            qo[jq].qscale[g] = on ? (int)((sc[g] >> (8 * grp)) & 0xFFu) : 127;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const uint32_t wb = w4[g][i];  // a scalar copy: bit casts read whole objects
-                qo.wt[g][i] = (16 * g + 4 * grp + i < P.H) ? __builtin_bit_cast(float, wb) : 0.0f;
+                qo[jq].wt[g][i] = (16 * g + 4 * grp + i < P.H) ? __builtin_bit_cast(float, wb) : 0.0f;
             }
         }
     }
@@ -543,19 +562,21 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
     uint32_t claim = claim_next();
     // Every step refills the stage it has read (a finished wavefront repeats the last batch:
     // valid addresses, never computed), so each wait leaves exactly the other stages' copies in
-    // flight: at most (kStreamStages - 1) x 8 newer loads (the key stores in between may still
-    // travel; loads complete in order, so these counts leave the stage read complete).
+    // flight: at most (NST - 1) x 8 newer loads (the key stores in between may still travel;
+    // loads complete in order, so these counts leave the stage read complete).
     for (int st = 0;;) {
         if (bq[0] >= n_batches) break;  // uniform over the wavefront
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * (kStreamStages - 1)) : "memory");
-        emit(bq[0], stage_scores(codes[st][wv], scl[st][wv], qo));
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGroupsPerIter * (NST - 1)) : "memory");
+        float sc[QT];
+        stage_scores(codes[st][wv], scl[st][wv], qo, sc);
+        emit(bq[0], sc);
         const int nb = __builtin_amdgcn_readfirstlane(claim);
         load_batch(min(nb, n_batches - 1), codes[st][wv], scl[st][wv]);
         claim = claim_next();
 #pragma unroll
-        for (int j = 0; j + 1 < kStreamStages; j++) bq[j] = bq[j + 1];
-        bq[kStreamStages - 1] = nb;
-        st = st + 1 == kStreamStages ? 0 : st + 1;
+        for (int j = 0; j + 1 < NST; j++) bq[j] = bq[j + 1];
+        bq[NST - 1] = nb;
+        st = st + 1 == NST ? 0 : st + 1;
     }
     if (own) {
         // the new key: merged, encoded (into LDS), scored as the stream's keys are, counted and
@@ -565,22 +586,23 @@ __global__ void __launch_bounds__(64 * kStreamWaves) indexer_mxfp4_stream_kernel
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const float c = key_chain(qo, *(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64), grp);
+        const float c = key_chain(qo[0], *(const uint4 *)(knew + 16 * grp), *(const uint32_t *)(knew + 64), grp);
         float sn = ((lane_value(c, 0) + lane_value(c, 16)) + lane_value(c, 32)) + lane_value(c, 48);
         if (sn == 0.0f) sn = 0.0f;  // -0 -> +0
         if (lane == 0) {
             const uint32_t key = P.key16 ? score_key16(sn) : score_key(sn);
-            if (g_key) g_key[i_new] = key;
-            if (g_key16) g_key16[i_new] = (uint16_t)key;
-            if (g_sc) g_sc[i_new] = sn;
-            if (P.hist) atomicAdd(&lhist[key >> hshift], 1u);
+            if (P.score_keys && !P.key16) ((uint32_t *)P.score_keys)[(int64_t)qi * P.key_stride + i_new] = key;
+            if (P.score_keys && P.key16) ((uint16_t *)P.score_keys)[(int64_t)qi * P.key_stride + i_new] = (uint16_t)key;
+            if (P.scores) P.scores[(int64_t)qi * P.n_max + i_new] = sn;
+            if (P.hist) atomicAdd(&lhist[0][key >> hshift], 1u);
         }
         const int64_t row = P.key.out_row0 + (int64_t)qi * P.key.cap + i_new;
         if (lane < 16) ((uint32_t *)((uint8_t *)P.key.idx.codes + row * 64))[lane] = ((const uint32_t *)knew)[lane];
         if (lane == 16) *(uint32_t *)(P.key.idx.scales + row * 4) = *(const uint32_t *)(knew + 64);
     }
     lds_barrier();
-    flush_hist_nobarrier<64 * NW>(P, qi, lhist);
+#pragma unroll
+    for (int j = 0; j < QT; j++) flush_hist_nobarrier<64 * NW>(P, qi0 + j, lhist[j]);
 }
 
 // fp32 keys and queries: one thread per key; per head an fma chain over ascending dims.
@@ -672,18 +694,23 @@ hipError_t launch_indexer(const IndexerArgs &a, const QueryPos &qp, hipStream_t 
     }
     const int BQ = a.B * a.Q;
     if (a.n_max == 0 || BQ == 0) return hipSuccess;
-    if (mx && a.Q == 1 && (int64_t)BQ * a.n_max >= kStreamMinKeys) {
-        // a long decode scan: one streaming workgroup per CU; keys per workgroup the largest of
-        // 1024, 2048, 4096 that still gives kStreamWGs workgroups
+    if (mx && (a.Q == 1 || a.Q == 2) && (int64_t)BQ * a.n_max >= kStreamMinKeys && !(a.Q == 2 && P.key_rec)) {
+        // a long decode scan: one streaming workgroup per CU; with two queries per sequence (a
+        // two-token step) both are scored from each batch a workgroup loads.  Keys per workgroup
+        // the largest of 1024, 2048, 4096 that still gives kStreamWGs workgroups.
+        const int rows = a.B;  // workgroup rows: one per sequence (its Q queries)
         int kpw = kStreamMaxKeys;
-        while (kpw > 1024 && (int64_t)BQ * ((a.n_max + kpw - 1) / kpw) < kStreamWGs) kpw /= 2;
+        while (kpw > 1024 && (int64_t)rows * ((a.n_max + kpw - 1) / kpw) < kStreamWGs) kpw /= 2;
         P.stream_kpw = kpw;
-        dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)BQ);
-        if (P.key_rec)
-            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<true>), grid, dim3(64 * kStreamWaves), 0,
+        dim3 grid((unsigned)((a.n_max + kpw - 1) / kpw), (unsigned)rows);
+        if (a.Q == 2)
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<2, false>), grid, dim3(64 * kStreamWaves), 0,
+                       s, P, qp);
+        else if (P.key_rec)
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<1, true>), grid, dim3(64 * kStreamWaves), 0,
                        s, P, qp);
         else
-            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<false>), grid, dim3(64 * kStreamWaves), 0,
+            V4A_LAUNCH("indexer_mxfp4_kernel", (indexer_mxfp4_stream_kernel<1, false>), grid, dim3(64 * kStreamWaves), 0,
                        s, P, qp);
     } else if (mx) {
         // keys per wavefront: doubled from 128 while the grid keeps at least kScoreMinWGs
