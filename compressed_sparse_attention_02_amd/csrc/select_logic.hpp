@@ -56,19 +56,23 @@ __host__ __device__ __forceinline__ uint32_t sel_clamp_count(uint32_t c, uint32_
 // Ordered compaction: walking the listed keys in index order with gt_before keys above the
 // threshold key tkey and eq_before keys equal to it already seen, returns the output slot of a
 // key (keys above tkey are all kept; keys equal to it while fewer than rem have been kept,
-// lowest index first), or -1 if it is not kept; advances the counts.
+// lowest index first), or -1 if it is not kept; advances the counts.  Both counts are read
+// and written back unconditionally: a store through a pointer chosen by the comparison would
+// keep them in memory (scratch on the GPU) instead of registers.
 __host__ __device__ __forceinline__ int sel_place(uint32_t key, uint32_t tkey, uint32_t rem, uint32_t k_eff,
                                                   uint32_t *gt_before, uint32_t *eq_before) {
+    const uint32_t g = *gt_before, e = *eq_before;
+    const bool gt = key > tkey, eq = key == tkey;
     int p = -1;
-    if (key > tkey) {
-        const uint32_t q = *gt_before + (*eq_before < rem ? *eq_before : rem);
+    if (gt) {
+        const uint32_t q = g + (e < rem ? e : rem);
         if (q < k_eff) p = (int)q;
-        (*gt_before)++;
-    } else if (key == tkey) {
-        const uint32_t q = *gt_before + *eq_before;
-        if (*eq_before < rem && q < k_eff) p = (int)q;
-        (*eq_before)++;
+    } else if (eq) {
+        const uint32_t q = g + e;
+        if (e < rem && q < k_eff) p = (int)q;
     }
+    *gt_before = g + (gt ? 1u : 0u);
+    *eq_before = e + (eq ? 1u : 0u);
     return p;
 }
 

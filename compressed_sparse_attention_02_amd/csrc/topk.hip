@@ -34,6 +34,7 @@ constexpr int kMaxSlices = 1024;  // n_max <= 8M keys
 constexpr int kSubBins = 1024;    // 10-bit digits of the low 20 score-key bits
 constexpr int kSelTPS = 16;       // finalize: fewest threads per slice placing its listed keys
 constexpr int kSelSpec = 8;       // finalize: listed keys per thread requested with the counts
+constexpr int kRankMax = 64;      // finalize: keys left in the first digit's bin ranked by one wavefront
 
 int select_slices(int64_t n_max) {
     int64_t s = (n_max + kSelSlice - 1) / kSelSlice;
@@ -221,6 +222,8 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
     __shared__ uint32_t lidx[kLdsList];
     __shared__ uint32_t lkey[kLdsList];
     __shared__ uint32_t soff[kMaxSlices + 1];
+    __shared__ uint32_t cand[kRankMax];
+    __shared__ uint32_t n_cand, r_sub, r_rem;
     const int BQ = (int)gridDim.x - P.n_rec;
     if ((int)blockIdx.x >= BQ) {
         // sequence b, whose QP.Q queries (its new tokens) are queries b*Q .. b*Q+Q-1
@@ -238,10 +241,17 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
             const int64_t pos = query_pos(QP, b * Q + j);
             if ((pos + 1) % m != 0) continue;  // no block completed by this token
             const int64_t i = (pos + 1) / m - 1;
-            if (P.rec.D == 512)
+            if (P.rec.D == 512 && entry_two_phase(P.rec)) {
+                // every candidate row requested at once, then merged and finished bitwise as
+                // compress_entry would: a shorter serial chain for the one wavefront
+                KeyPrefetch<8> kr;
+                key_prefetch<8>(P.rec, b, i, (int64_t)m * (i - 1), kr);
+                prefetched_entry_finish<8>(P.rec, kr, b, i, nullptr, 0);
+            } else if (P.rec.D == 512) {
                 compress_entry<8>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
-            else
+            } else {
                 compress_entry<2>(P.rec, scratch, b, i, (int64_t)m * (i - 1));
+            }
         }
         return;
     }
@@ -253,6 +263,27 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         for (int j = t; j < P.k; j += kSelThreads) out[j] = -1;
         return;
     }
+    // global order of the listed keys: slice offsets, then the keys themselves into LDS
+    const uint32_t *cnts = P.counts + (int64_t)qi * P.slices;
+    const int S = P.slices;
+    const uint32_t *lst = P.list + (int64_t)qi * S * kSelSlice * 2;
+    // Up to 32 slices: tps threads per slice (512 over the slice count rounded up to a power of
+    // two, at least kSelTPS) request its count and its first tps * kSelSpec listed keys at once
+    // (slots past the count lie inside the slice's list region and are dropped), before the
+    // scan's threshold is read, so counts, keys and threshold take one memory round trip
+    const bool few_slices = S <= kSelThreads / kSelTPS;
+    int tps = kSelThreads;
+    while (tps > kSelTPS && tps * S > kSelThreads) tps >>= 1;
+    const int sl = t / tps, p0 = t % tps;
+    const bool live = few_slices && sl < S;
+    const uint32_t c_raw = live ? cnts[sl] : 0u;
+    const uint32_t *ls = lst + (int64_t)(live ? sl : 0) * kSelSlice * 2;
+    uint2 e[kSelSpec];
+#pragma unroll
+    for (int u = 0; u < kSelSpec; u++) {
+        const int pos = p0 + tps * u;  // < kSelSlice: inside the slice's list region
+        e[u] = live ? *(const uint2 *)(ls + 2 * pos) : make_uint2(0, 0);
+    }
     const int T = P.meta[2 * qi];
     const uint32_t above = (uint32_t)P.meta[2 * qi + 1];
     // the scan's result is trusted only if it is consistent (a threshold bin, fewer than k_eff
@@ -262,32 +293,14 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         return;
     }
     const uint32_t need = k_eff - above;  // >= 1: keys still to take from bin T
-    // global order of the listed keys: slice offsets, then the keys themselves into LDS
-    const uint32_t *cnts = P.counts + (int64_t)qi * P.slices;
-    const int S = P.slices;
-    const uint32_t *lst = P.list + (int64_t)qi * S * kSelSlice * 2;
     // the first digit pass: bits 10..19 of the keys in bin T (bits 16..19 of widened 16-bit keys)
     const int shift0 = P.key16 ? 16 : 10;
     const uint32_t dmask0 = P.key16 ? 15u : (uint32_t)(kSubBins - 1);
     bool hist0 = false;  // the first pass's histogram was counted while the keys were placed
     uint32_t L;
-    if (S <= kSelThreads / kSelTPS) {
-        // tps threads per slice (512 over the slice count rounded up to a power of two, at
-        // least kSelTPS) request its count and its first tps * kSelSpec listed keys at once
-        // (slots past the count lie inside the slice's list region and are dropped), so counts
-        // and keys take one memory round trip; one block scan of the counts then places every key
-        int tps = kSelThreads;
-        while (tps > kSelTPS && tps * S > kSelThreads) tps >>= 1;
-        const int sl = t / tps, p0 = t % tps;
-        const bool live = sl < S;
-        const uint32_t c = live ? sel_clamp_count(cnts[sl], (uint32_t)kSelSlice) : 0u;
-        const uint32_t *ls = lst + (int64_t)(live ? sl : 0) * kSelSlice * 2;
-        uint2 e[kSelSpec];
-#pragma unroll
-        for (int u = 0; u < kSelSpec; u++) {
-            const int pos = p0 + tps * u;  // < kSelSlice: inside the slice's list region
-            e[u] = live ? *(const uint2 *)(ls + 2 * pos) : make_uint2(0, 0);
-        }
+    if (few_slices) {
+        // one block scan of the counts requested above places every key
+        const uint32_t c = live ? sel_clamp_count(c_raw, (uint32_t)kSelSlice) : 0u;
         for (int i = t; i < kSubBins; i += kSelThreads) hist[i] = 0;
         uint32_t tot;
         const uint32_t mine = (live && p0 == 0) ? c : 0u;
@@ -403,6 +416,50 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         rem -= ab;
         sub |= (uint32_t)d << shift;
         sub_mask |= dmask << shift;
+        if (p == 0 && n_pass == 2 && hist[d] <= (uint32_t)kRankMax) {
+            // few keys share the first digit (bits 10..19): instead of a second histogram pass
+            // they are gathered and one wavefront ranks them; the rem-th largest of them (with
+            // repeats) is the threshold key, and rem becomes the count of its equals still
+            // needed, as the second pass would leave them
+            const uint32_t nd = hist[d];
+            if (t == 0) {
+                n_cand = 0;
+                r_rem = 0;
+            }
+            __syncthreads();
+            const uint32_t pre = (((uint32_t)T << 20) | sub) >> 10;
+            for (uint32_t j = t; j < L; j += kSelThreads) {
+                uint32_t idx, key;
+                entry(j, &idx, &key);
+                if ((key >> 10) == pre) {
+                    const uint32_t slot = atomicAdd(&n_cand, 1u);
+                    if (slot < (uint32_t)kRankMax) cand[slot] = key;
+                }
+            }
+            __syncthreads();
+            if (t < 64) {
+                const uint32_t n = min(min(n_cand, nd), (uint32_t)kRankMax);
+                const uint32_t x = (uint32_t)t < n ? cand[t] : 0u;
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t q = 0; q < n; q++) {
+                    const uint32_t y = cand[q];
+                    gt += y > x ? 1u : 0u;
+                    ge += y >= x ? 1u : 0u;
+                }
+                if ((uint32_t)t < n && gt < rem && rem <= ge) {  // every such lane holds the same key
+                    r_sub = x & (uint32_t)(kSubBins - 1);
+                    r_rem = rem - gt;
+                }
+            }
+            __syncthreads();
+            if (r_rem == 0) {  // the gathered keys do not hold the rem-th: select nothing (uniform)
+                for (int j = t; j < P.k; j += kSelThreads) out[j] = -1;
+                return;
+            }
+            sub |= r_sub;
+            rem = r_rem;
+            break;
+        }
     }
     const uint32_t tkey = ((uint32_t)T << 20) | sub;  // the k_eff-th best score key
     // ordered compaction: thread t owns a contiguous run of the global order; keys > tkey are
@@ -428,11 +485,20 @@ __global__ void __launch_bounds__(kSelThreads) select_final_kernel(SelParams P, 
         gt_before = block_scan(n_gt, wsum, &t1) - n_gt;
         eq_before = block_scan(n_eq, wsum, &t2) - n_eq;
     }
-    for (uint32_t j = j0; j < j1; j++) {
-        uint32_t idx, key;
-        entry(j, &idx, &key);
-        const int p = sel_place(key, tkey, rem, k_eff, &gt_before, &eq_before);
-        if (p >= 0) out[p] = (int32_t)idx;
+    // the LDS form has a loop of its own: a global read in the loop (the long-list form) would
+    // make every iteration wait for the previous iteration's store as well
+    if (in_lds) {
+        for (uint32_t j = j0; j < j1; j++) {
+            const uint32_t idx = lidx[j], key = lkey[j];
+            const int p = sel_place(key, tkey, rem, k_eff, &gt_before, &eq_before);
+            if (p >= 0) out[p] = (int32_t)idx;
+        }
+    } else {
+        for (uint32_t j = j0; j < j1; j++) {
+            const uint2 e = fetch(j);
+            const int p = sel_place(e.y, tkey, rem, k_eff, &gt_before, &eq_before);
+            if (p >= 0) out[p] = (int32_t)e.x;
+        }
     }
     for (int j = (int)k_eff + t; j < P.k; j += kSelThreads) out[j] = -1;
 }

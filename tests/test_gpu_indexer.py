@@ -184,6 +184,23 @@ def test_topk_adversarial_ties():
     assert np.array_equal(got[1, 0], np.arange(k))
 
 
+def test_topk_small_tie_groups():
+    """Keys drawn from 3000 vectors (about four copies each): equal scores come in small
+    groups, so the few keys sharing the threshold's first 22 bits (ranked by one wavefront
+    instead of a second digit pass) hold repeats, and the lowest indices must win."""
+    B, N, H, k = 2, 12000, 64, 700
+    g = np.random.default_rng(305)
+    base = normal(305, "keys", (3000, 128))
+    keys = base[g.integers(0, 3000, size=(B, N))]
+    q = normal(305, "q_idx", (B, H, 128))
+    w = normal(305, "w", (B, 1, H))
+    announce("topk small tie groups")
+    for bf16 in (False, True):
+        got, _, _ = run_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=bf16)
+        ref = oracle_topk(keys, q, w, np.array([N, N]), [4 * N - 1] * 2, k, bf16=bf16)
+        assert np.array_equal(got, ref), bf16
+
+
 def test_topk_list_longer_than_lds():
     """Every key identical: the threshold bin lists all 30000 keys, more than the final
     selection keeps in LDS, so it reads them from the list in global memory."""
