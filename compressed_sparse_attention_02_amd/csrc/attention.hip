@@ -135,16 +135,15 @@ __device__ __forceinline__ void store_out4(const AttnParams &P, int b, int h, in
 
 // Final output of head h, dims d0 .. d0+3: normalisation with the sink, inverse RoPE on the
 // RoPE dims, cast.  Reached by the whole wavefront; rope_wave says whether any of its lanes
-// holds RoPE dims (uniform), so other wavefronts skip the cos/sin.
-__device__ __forceinline__ void finish4(const AttnParams &P, const SeqInfo &Sq, int b, int h, int d0,
-                                        bool rope_wave, float m2, float l, float (&o)[4]) {
+// holds RoPE dims (uniform), and only then is rl (the cos/sin of the query position, which the
+// caller evaluates while its loads are in flight) read.
+__device__ __forceinline__ void finish4(const AttnParams &P, int b, int h, int d0, bool rope_wave,
+                                        const RopeLanes &rl, float m2, float l, float (&o)[4]) {
     const float f = finish_factor(P, h, m2, l);
 #pragma unroll
     for (int v = 0; v < 4; v++) o[v] *= f;
     const int Dn = P.D - P.R;
     if (P.rope_inv && rope_wave) {
-        RopeLanes rl;
-        rl.eval(P.rt, P.R / 2, (double)sq_pos(Sq, b));
 #pragma unroll
         for (int v = 0; v < 4; v += 2) {
             const float2 cs = rl.get(min(max((d0 + v - Dn) / 2, 0), P.R / 2 - 1));
@@ -666,7 +665,9 @@ __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) attn_mfma_kernel(AttnPa
                 }
         }
         q ^= 1;
-        __syncthreads();      // readers of this tile's buffer are done before it is refilled
+        // No barrier here: the buffer this tile used is refilled (by direct loads, or by
+        // stage_bf16) only after the next iteration's barrier, which every wavefront reaches
+        // after its last read of it.
     }
     if (!wave_on) return;
     // l over the four lane groups of each head
@@ -750,6 +751,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
         m2s[s] = ml.x;
         ls[s] = ml.y;
     }
+    // the cos/sin of the inverse RoPE, while the partials are in flight
+    const bool rope_wave = 16 * dt + 16 > P.D - P.R;
+    RopeLanes rl;
+    if (P.rope_inv && rope_wave) rl.eval(P.rt, P.R / 2, (double)sq_pos(Sq, b));
     float M = P.sink[h] * kLog2e;
 #pragma unroll
     for (int s = 0; s < NS; s++)
@@ -764,7 +769,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(AttnPa
         for (int v = 0; v < 4; v++) o[v] = fmaf(bf16_half(po[s], v), c, o[v]);
     }
     // finish with m2 = M and l as the merged sum (the factor exp2(M - M) is 1)
-    finish4(P, Sq, b, h, d0, 16 * dt + 16 > P.D - P.R, M, l, o);
+    finish4(P, b, h, d0, rope_wave, rl, M, l, o);
 }
 
 // ---------------------------------------------------------------- fp32 kernel -------

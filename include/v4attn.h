@@ -185,6 +185,11 @@ V4A_API v4a_status v4a_indexer_topk(const v4a_idx *keys, const int64_t *n_entrie
                             int32_t H_I, const int64_t *q_pos, int32_t k, int32_t *out_idx,
                             void *ws, size_t ws_bytes, void *stream);
 V4A_API size_t v4a_indexer_topk_workspace(int32_t B, int32_t Q, int64_t n_max, int32_t k);
+/* The workspace holds, per query: its score keys (4 bytes per key up to n_max, padded), two
+ * 4096-bin histograms and a candidate list sized for the worst case, in which every key of an
+ * 8192-key slice ties in the threshold bin (8 bytes per key of every slice).  Examples: 12.7 MB
+ * for 4 sequences over 262,144 entries (B = 4, Q = 1), 1.16 GB for a 4096-query prefill chunk
+ * over 17,408 entries (B = 1, Q = 4096), of which 805 MB is the candidate list. */
 
 /* The same call with the scores held in BF16 for the selection ([cyqw] section 3.4: the
  * index score is kept in BF16 instead of FP32, which halves the selector's score bytes).
